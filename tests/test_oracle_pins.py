@@ -1,0 +1,246 @@
+"""Pins of the CPU oracle to facts outside itself: brute force, closed forms, invariants, and
+special cases that reduce to library routines (torch).  CPU only."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from mixture_experts_layer_20_amd import inputs as I
+
+
+# --------------------------------------------------------------------------------- selection
+
+def brute_topk(row, k):
+    # Python floats: -0.0 == 0.0, so ties (including signed zeros) fall through to the index.
+    return sorted(range(len(row)), key=lambda e: (-float(row[e]), e))[:k]
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+@pytest.mark.parametrize("kind", ["gauss", "integer_ties", "signed_zero"])
+def test_topk_matches_brute_force(k, kind):
+    rng = np.random.default_rng(100 + k)
+    T, E = 64, 8
+    if kind == "gauss":
+        L = rng.standard_normal((T, E)).astype(np.float32)
+    elif kind == "integer_ties":
+        L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)   # many exact ties
+    else:
+        L = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), size=(T, E))
+    got = O.select_topk(L, k)
+    for t in range(T):
+        assert list(got[t]) == brute_topk(L[t], k), (t, L[t])
+
+
+def test_topk_all_permutations_tiny():
+    # Every ordering of 4 logits with one tie, all k.
+    for perm in itertools.permutations([0.5, 2.0, 2.0, -1.0]):
+        L = np.array([perm], np.float32)
+        for k in range(1, 5):
+            assert list(O.select_topk(L, k)[0]) == brute_topk(perm, k)
+
+
+def test_hand_example_ties_and_gates():
+    # Logits [1, 3, 3], top-2: the two 3s, lower index first; equal logits give equal gates.
+    L = np.array([[1.0, 3.0, 3.0]], np.float32)
+    idx = O.select_topk(L, 2)
+    assert idx.tolist() == [[1, 2]]
+    g = O.gate_weights(L, idx)
+    assert g.tolist() == [[0.5, 0.5]]
+
+
+def test_gate_closed_forms():
+    rng = np.random.default_rng(3)
+    L = rng.standard_normal((50, 6)).astype(np.float32)
+    # k = 1: the gate is exactly one.
+    assert np.all(O.gate_weights(L, O.select_topk(L, 1)) == 1.0)
+    # k = 2: the first gate is the logistic function of the logit gap.
+    idx = O.select_topk(L, 2)
+    g = O.gate_weights(L, idx)
+    l0 = L[np.arange(50), idx[:, 0]].astype(np.float64)
+    l1 = L[np.arange(50), idx[:, 1]].astype(np.float64)
+    np.testing.assert_allclose(g[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-14)
+    np.testing.assert_allclose(g[:, 1], 1.0 / (1.0 + np.exp(l0 - l1)), rtol=1e-14)
+    # gates are non-increasing along the chosen order and sum to one.
+    g4 = O.gate_weights(L, O.select_topk(L, 4))
+    assert np.all(np.diff(g4, axis=1) <= 0)
+    np.testing.assert_allclose(g4.sum(1), 1.0, rtol=1e-14)
+    # Renormalised gates equal the full softmax renormalised over the chosen experts (torch).
+    idx4 = O.select_topk(L, 4)
+    p = torch.softmax(torch.from_numpy(L.astype(np.float64)), dim=1).numpy()
+    ps = np.take_along_axis(p, idx4.astype(np.int64), 1)
+    np.testing.assert_allclose(g4, ps / ps.sum(1, keepdims=True), rtol=1e-13)
+    # Without renormalisation: the full softmax probabilities themselves.
+    np.testing.assert_allclose(O.gate_weights(L, idx4, renormalize=False), ps, rtol=1e-13)
+
+
+# --------------------------------------------------------------------------------- logits
+
+def scalar_logits(x, w, b):
+    T, d = x.shape
+    E = w.shape[0]
+    out = np.zeros((T, E), np.float32)
+    for t in range(T):
+        for e in range(E):
+            acc = np.float32(0.0)
+            for i in range(d):
+                acc = np.float32(acc + np.float32(x[t, i] * w[e, i]))
+            if b is not None:
+                acc = np.float32(acc + b[e])
+            out[t, e] = acc
+    return out
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_canonical_logits_match_scalar_loop(bf16, with_bias):
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 37)).astype(np.float32)
+    w = (0.02 * rng.standard_normal((3, 37))).astype(np.float32)
+    b = (1.5 * rng.standard_normal(3)).astype(np.float32) if with_bias else None
+    if bf16:
+        x = I.f32_from_bf16_bits(I.bf16_bits_from_f32(x))
+        w = I.f32_from_bf16_bits(I.bf16_bits_from_f32(w))
+    got = O.canonical_router_logits(x, w, b)
+    ref = scalar_logits(x, w, b)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_canonical_logits_within_summation_bound():
+    # Recursive summation: |fl(sum) - sum| <= (d) u sum|x_i w_i| (+ the final rounding), u = 2^-24.
+    rng = np.random.default_rng(8)
+    T, d, E = 40, 2048, 16
+    x = I.f32_from_bf16_bits(I.bf16_bits_from_f32(rng.standard_normal((T, d)).astype(np.float32)))
+    w = I.f32_from_bf16_bits(I.bf16_bits_from_f32(0.02 * rng.standard_normal((E, d)).astype(np.float32)))
+    got = O.canonical_router_logits(x, w).astype(np.float64)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    bound = (d + 1) * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T)
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_bf16_rounding_is_nearest_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 0.0, -0.0,
+                     3.0e38, 1e-40], np.float32)
+    back = I.f32_from_bf16_bits(I.bf16_bits_from_f32(vals))
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins; 1 + 3*2^-8 rounds up.
+    assert back[1] == 1.0 and back[2] == np.float32(1.0 + 2 ** -6)
+    assert back[3] == 1.0 and back[4] == -2.5
+    assert np.signbit(back[6]) and back[5] == 0.0
+    # bf16 values are fixed points of the rounding.
+    assert np.array_equal(I.bf16_bits_from_f32(back), I.bf16_bits_from_f32(vals))
+
+
+# --------------------------------------------------------------------------------- dispatch
+
+def _routing(T, E, k, seed, skew=0.0):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((T, E)).astype(np.float32) + skew * rng.standard_normal(E).astype(np.float32)
+    return O.select_topk(L, k)
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(1, 1, 1, 0.0), (100, 8, 2, 0.0), (333, 64, 4, 3.0),
+                                        (257, 128, 8, 0.0), (64, 16, 16, 0.0)])
+def test_dispatch_invariants(T, E, k, skew):
+    idx = _routing(T, E, k, T + E, skew)
+    counts, offsets, dest_pos, src_row = O.dispatch_plan(idx, E)
+    flat = idx.reshape(-1)
+    # counts by a direct Python tally
+    tally = [0] * E
+    for e in flat.tolist():
+        tally[e] += 1
+    assert counts.tolist() == tally and counts.sum() == T * k
+    assert offsets[0] == 0 and offsets[-1] == T * k
+    assert np.all(np.diff(offsets) == counts)
+    # bijection: dest_pos is a permutation and src_row its inverse
+    assert np.array_equal(np.sort(dest_pos), np.arange(T * k))
+    assert np.array_equal(src_row[dest_pos], np.arange(T * k))
+    # every row of expert e holds an assignment to e, in ascending assignment order (stable)
+    for e in range(E):
+        rows = src_row[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[rows] == e)
+        assert np.all(np.diff(rows) > 0)
+    # the permuted activations are row copies of the tokens
+    x = np.random.default_rng(1).standard_normal((T, 5)).astype(np.float32)
+    xp = O.permute_rows(x, src_row, k)
+    for p in range(T * k):
+        assert np.array_equal(xp[p], x[src_row[p] // k])
+
+
+# --------------------------------------------------------------------------------- MLP/combine
+
+def _torch_swiglu(x, w1, w3, w2):
+    x, w1, w3, w2 = (torch.from_numpy(np.asarray(a, np.float64)) for a in (x, w1, w3, w2))
+    return (torch.nn.functional.silu(x @ w1.T) * (x @ w3.T)) @ w2.T
+
+
+def _small_params(T, d, E, f, fs, seed):
+    rng = np.random.default_rng(seed)
+    p = dict(x=rng.standard_normal((T, d)),
+             w1=0.3 * rng.standard_normal((E, f, d)), w3=0.3 * rng.standard_normal((E, f, d)),
+             w2=0.3 * rng.standard_normal((E, d, f)), wr=0.3 * rng.standard_normal((E, d)))
+    if fs:
+        p.update(ws1=0.3 * rng.standard_normal((fs, d)), ws3=0.3 * rng.standard_normal((fs, d)),
+                 ws2=0.3 * rng.standard_normal((d, fs)))
+    else:
+        p.update(ws1=None, ws3=None, ws2=None)
+    return p
+
+
+def test_single_expert_top1_is_dense_swiglu():
+    p = _small_params(T=37, d=16, E=1, f=24, fs=12, seed=4)
+    fwd = O.layer_forward(p["x"], p["w1"], p["w3"], p["w2"], 1, w_router=p["wr"],
+                          ws1=p["ws1"], ws3=p["ws3"], ws2=p["ws2"])
+    assert np.all(fwd["gates"] == 1.0)
+    ref = _torch_swiglu(p["x"], p["w1"][0], p["w3"][0], p["w2"][0]) + \
+        _torch_swiglu(p["x"], p["ws1"], p["ws3"], p["ws2"])
+    np.testing.assert_allclose(fwd["out"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_identical_experts_make_output_routing_independent():
+    p = _small_params(T=50, d=12, E=6, f=10, fs=7, seed=5)
+    for key in ("w1", "w3", "w2"):
+        p[key] = np.repeat(p[key][:1], 6, axis=0)
+    fwd = O.layer_forward(p["x"], p["w1"], p["w3"], p["w2"], 3, w_router=p["wr"],
+                          ws1=p["ws1"], ws3=p["ws3"], ws2=p["ws2"])
+    ref = _torch_swiglu(p["x"], p["w1"][0], p["w3"][0], p["w2"][0]) + \
+        _torch_swiglu(p["x"], p["ws1"], p["ws3"], p["ws2"])
+    np.testing.assert_allclose(fwd["out"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_all_experts_chosen_is_dense_soft_mixture():
+    T, d, E, f = 30, 10, 5, 8
+    p = _small_params(T, d, E, f, 0, seed=6)
+    fwd = O.layer_forward(p["x"], p["w1"], p["w3"], p["w2"], E, w_router=p["wr"])
+    L = torch.from_numpy(fwd["logits"].astype(np.float64))
+    prob = torch.softmax(L, dim=1)
+    ref = sum(prob[:, e:e + 1] * _torch_swiglu(p["x"], p["w1"][e], p["w3"][e], p["w2"][e]) for e in range(E))
+    np.testing.assert_allclose(fwd["out"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_combine_of_permuted_identity_is_identity():
+    T, E, k, d = 40, 8, 3, 6
+    idx = _routing(T, E, k, 9)
+    L = np.random.default_rng(2).standard_normal((T, E)).astype(np.float32)
+    g = O.gate_weights(L, idx)
+    counts, offsets, dest_pos, src_row = O.dispatch_plan(idx, E)
+    x = np.random.default_rng(3).standard_normal((T, d))
+    out = O.combine(O.permute_rows(x, src_row, k), g, dest_pos)
+    np.testing.assert_allclose(out, x, rtol=1e-14, atol=1e-14)
+
+
+def test_fp32_oracle_error_is_far_below_tolerances():
+    cfg = I.CONFIGS["tiny_fp32"]
+    vals = I.values(I.make_inputs(cfg))
+    f64, _ = O.run_layer(cfg, vals, dt=np.float64)
+    f32, _ = O.run_layer(cfg, vals, dt=np.float32)
+    assert np.array_equal(f64["topk_idx"], f32["topk_idx"])
+    assert O.max_abs_rel_err(f32["out"], f64["out"]) < 1e-6
+    # a reduced bf16 shape with backward: far below the bf16 tolerance
+    cfgb = I.CONFIGS["tiny64e_learned_skew"].with_(T=256, d=256, E=16, f=128, fs=128)
+    vb = I.values(I.make_inputs(cfgb))
+    fa, ba = O.run_layer(cfgb, vb, dt=np.float64)
+    fb, bb = O.run_layer(cfgb, vb, dt=np.float32)
+    assert O.max_abs_rel_err(fb["out"], fa["out"]) < 1e-5
+    for key in ("dx", "dW1", "dW2", "dW3", "dWr", "dWs1"):
+        assert O.max_abs_rel_err(bb[key], ba[key]) < 1e-4, key

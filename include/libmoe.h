@@ -1,0 +1,223 @@
+/*
+ * libmoe — one GPU's share of the Olmo-core 3 mixture-of-experts block, for AMD MI355X (gfx950).
+ *
+ * The layer: every token picks its top-k routed experts (learned router or random routing) and
+ * also goes through one shared expert; the routed experts are SwiGLU MLPs that stay resident on
+ * the GPU while tokens are moved to them; the output is the gate-weighted sum of the k expert
+ * outputs plus the shared expert's output.  Sources: "Olmo-core DDP MoE examples" README,
+ * section "Production throughput runs" (top-4 routing, one shared expert, learned vs random
+ * routing); "Olmo-core 3 Opens Large MoE Training", "Technical Deep Dive" (experts stay pinned in
+ * local memory, tokens are routed to them); "Scaling Trillion-Parameter Models: The Architecture
+ * of Olmo-core 3", "Code Snippet" (a per-token expert selection step).
+ *
+ * Conventions shared by every call
+ *   Memory      All tensor pointers are DEVICE pointers owned by the caller.  The library keeps
+ *               no pointer after a call returns and allocates no device memory: scratch space is
+ *               the caller's workspace, sized by the matching *_workspace_size function.
+ *   Layout      Row-major, contiguous.  Weights are [out_features, in_features]:
+ *                 w_router [E, d]; w1, w3 [G, f, d]; w2 [G, d, f].
+ *   Types       dt = MOE_F32: every activation and weight is float.  dt = MOE_BF16: activations,
+ *               weights and their gradients are bfloat16 (uint16 bit patterns); router logits,
+ *               gates, gate gradients and the router weight gradient are always float32;
+ *               accumulation is always float32.
+ *   Streams     Every call only enqueues work on `stream` (a hipStream_t; NULL = null stream)
+ *               and returns.  No call synchronises with the host or copies to the host.
+ *   Errors      Arguments are checked on the host before anything is enqueued.  Invalid values
+ *               return MOE_ERR_INVALID_VALUE, valid but unsupported sizes MOE_ERR_UNSUPPORTED,
+ *               a too small workspace MOE_ERR_WORKSPACE, a failed launch MOE_ERR_HIP.  Detail is
+ *               in moe_last_error() (per thread).  Nothing aborts and nothing throws.
+ *   Results     Every output is bitwise deterministic from run to run (no floating-point
+ *               atomics).  Gradients are written, never accumulated into.
+ *   Sizes       1 <= k <= min(E, 8), E <= 256, T*k < 2^31; for the expert MLP calls d and f must
+ *               be multiples of 128.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_VALUE = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+/* ------------------------------------------------------------------------------------------ */
+/* Routing                                                                                     */
+
+/* Router: logits, top-k selection and gate weights.
+ * Source: "Scaling Trillion-Parameter Models ...", "Code Snippet" (one expert choice per token);
+ * "Olmo-core DDP MoE examples", "Production throughput runs" (top-4; learned or random routing).
+ *   x          [T, d]  (dt)            tokens; read only when w_router != NULL
+ *   w_router   [E, d]  (dt) or NULL    learned router.  NULL selects random routing: `logits`
+ *                                       is then an INPUT (caller-drawn scores)
+ *   bias       [E] float or NULL       constant per-expert logit bias (learned routing only)
+ *   logits     [T, E] float            learned: OUTPUT, L[t,e] = x[t,:].w_router[e,:] summed in
+ *                                       index order with one fp32 rounding per product and per
+ *                                       addition, then + bias[e]; random: INPUT
+ *   topk_idx   [T, k] int32  OUTPUT    the k largest logits of each token, largest first; equal
+ *                                       logits ordered by lower expert index (-0 equals +0)
+ *   topk_gate  [T, k] float  OUTPUT    renormalize=1: softmax over the k chosen logits;
+ *                                       renormalize=0: full softmax probability over all E
+ * NaN or infinite logits are not supported (the selection is then unspecified). */
+moe_status_t moe_route(const void* x, const void* w_router, const float* bias, float* logits,
+                       int64_t T, int64_t d, int32_t E, int32_t k, int32_t renormalize,
+                       moe_dtype_t dt, int32_t* topk_idx, float* topk_gate, moe_stream_t stream);
+
+/* Token dispatch: per-expert histogram, exclusive prefix sum, stable permutation and row gather.
+ * Source: "Olmo-core 3 Opens Large MoE Training", "Enhanced Key Takeaways" and "Technical Deep
+ * Dive" (tokens are routed to experts that stay in place).
+ * Assignment a = t*k + j (token t, slot j) belongs to expert topk_idx[a].  Rows are expert-major;
+ * inside an expert they keep ascending a (a stable counting sort).
+ *   topk_idx  [T, k] int32  INPUT, each value in [0, E) (out-of-range values are not checked)
+ *   counts    [E] int32     OUTPUT  rows per expert
+ *   offsets   [E+1] int32   OUTPUT  exclusive prefix sum of counts; offsets[E] = T*k
+ *   dest_pos  [T*k] int32   OUTPUT  row of assignment a
+ *   src_row   [T*k] int32   OUTPUT  assignment held by row p (inverse of dest_pos)
+ *   x_perm    [T*k, d] (dt) OUTPUT or NULL: x_perm[p] = x[src_row[p] / k] (exact copy)
+ *   ws        device workspace of moe_permute_workspace_size(T, E, k) bytes */
+size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k);
+moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E,
+                         int32_t k, moe_dtype_t dt, int32_t* counts, int32_t* offsets,
+                         int32_t* dest_pos, int32_t* src_row, void* x_perm, void* ws,
+                         size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Grouped SwiGLU expert MLP.  G groups (experts) over M rows; group g owns rows                */
+/* [offsets[g], offsets[g+1]) of x_in (offsets is a DEVICE array, non-decreasing, offsets[0]=0,  */
+/* offsets[G]=M).  Group g computes A = X W1[g]^T, B = X W3[g]^T, H = silu(A)*B, Y = H W2[g]^T.  */
+/* The shared expert is the same computation with G = 1 and offsets = {0, T}.                   */
+/* Source: "Olmo-core DDP MoE examples", "Interpreting the eight-layer DDP vs FSDP comparison"   */
+/* (sparse expert kernels; shared-branch mixing) and "Production throughput runs" (one shared    */
+/* expert).  The SwiGLU form is the reading taken where the pages are silent.                    */
+
+/* Workspace for the forward calls (tile schedule only). */
+size_t moe_grouped_mlp_fwd_workspace_size(int64_t M, int32_t G, int64_t d, int64_t f);
+/* Workspace for moe_grouped_mlp_bwd: the tile schedule plus dAB [M, 2f] (dt). */
+size_t moe_grouped_mlp_bwd_workspace_size(int64_t M, int32_t G, int64_t d, int64_t f);
+
+/* Forward: gate/up GEMM with fused SwiGLU, then the down GEMM.
+ *   x_in [M, d]; w1, w3 [G, f, d]; w2 [G, d, f]           INPUT  (dt)
+ *   a_stash, b_stash [M, f]                               OUTPUT (dt) or both NULL (no backward)
+ *   h [M, f]                                              OUTPUT (dt) (also the down GEMM input)
+ *   y [M, d]                                              OUTPUT (dt) */
+moe_status_t moe_grouped_mlp_fwd(const void* x_in, const int32_t* offsets, int32_t G, int64_t M,
+                                 int64_t d, int64_t f, const void* w1, const void* w3,
+                                 const void* w2, moe_dtype_t dt, void* a_stash, void* b_stash,
+                                 void* h, void* y, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Backward of moe_grouped_mlp_fwd (all four steps below, dAB kept in the workspace).
+ *   dy [M, d], x_in [M, d], a, b, h [M, f]                INPUT  (dt)
+ *   dx_in [M, d]                                          OUTPUT (dt)
+ *   dw1, dw3 [G, f, d]; dw2 [G, d, f]                     OUTPUT (dt); a group with no rows
+ *                                                         gets exact zeros */
+moe_status_t moe_grouped_mlp_bwd(const void* dy, const void* x_in, const void* a, const void* b,
+                                 const void* h, const int32_t* offsets, int32_t G, int64_t M,
+                                 int64_t d, int64_t f, const void* w1, const void* w3,
+                                 const void* w2, moe_dtype_t dt, void* dx_in, void* dw1, void* dw3,
+                                 void* dw2, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* The individual GEMM stages of the two calls above, each a single kernel launch, for callers
+ * that schedule or time the stages themselves.  Same argument meanings; ws needs
+ * moe_grouped_mlp_fwd_workspace_size bytes.  dab [M, 2f] (dt) holds dA in columns [0, f) and
+ * dB in columns [f, 2f):
+ *   gate_up_fwd:   A = X W1^T, B = X W3^T; h = silu(A) * B (a_stash/b_stash may be NULL)
+ *   down_fwd:      y = h W2^T
+ *   down_bwd:      dH = dy W2; dA = dH * B * s * (1 + A (1 - s)), s = sigmoid(A); dB = dH*silu(A)
+ *   down_wgrad:    dw2[g] = dy_g^T h_g
+ *   gate_up_dgrad: dx_in = dA W1 + dB W3
+ *   gate_up_wgrad: dw1[g] = dA_g^T x_g, dw3[g] = dB_g^T x_g */
+moe_status_t moe_expert_gate_up_fwd(const void* x_in, const int32_t* offsets, int32_t G,
+                                    int64_t M, int64_t d, int64_t f, const void* w1,
+                                    const void* w3, moe_dtype_t dt, void* a_stash, void* b_stash,
+                                    void* h, void* ws, size_t ws_bytes, moe_stream_t stream);
+moe_status_t moe_expert_down_fwd(const void* h, const int32_t* offsets, int32_t G, int64_t M,
+                                 int64_t d, int64_t f, const void* w2, moe_dtype_t dt, void* y,
+                                 void* ws, size_t ws_bytes, moe_stream_t stream);
+moe_status_t moe_expert_down_bwd(const void* dy, const void* a, const void* b,
+                                 const int32_t* offsets, int32_t G, int64_t M, int64_t d,
+                                 int64_t f, const void* w2, moe_dtype_t dt, void* dab, void* ws,
+                                 size_t ws_bytes, moe_stream_t stream);
+moe_status_t moe_expert_down_wgrad(const void* dy, const void* h, const int32_t* offsets,
+                                   int32_t G, int64_t M, int64_t d, int64_t f, moe_dtype_t dt,
+                                   void* dw2, void* ws, size_t ws_bytes, moe_stream_t stream);
+moe_status_t moe_expert_gate_up_dgrad(const void* dab, const int32_t* offsets, int32_t G,
+                                      int64_t M, int64_t d, int64_t f, const void* w1,
+                                      const void* w3, moe_dtype_t dt, void* dx_in, void* ws,
+                                      size_t ws_bytes, moe_stream_t stream);
+moe_status_t moe_expert_gate_up_wgrad(const void* dab, const void* x_in, const int32_t* offsets,
+                                      int32_t G, int64_t M, int64_t d, int64_t f, moe_dtype_t dt,
+                                      void* dw1, void* dw3, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Combine                                                                                     */
+
+/* Weighted combine / unpermute: out[t] = shared_out[t] + sum_j topk_gate[t,j] * y_perm[dest_pos[t*k+j]],
+ * summed in fp32.  Source: "Olmo-core DDP MoE examples", "Production throughput runs" (top-k
+ * experts plus one shared expert); the shared branch is added with weight 1.
+ *   y_perm [T*k, d] (dt), topk_gate [T, k] float, dest_pos [T*k] int32   INPUT
+ *   shared_out [T, d] (dt) INPUT or NULL;  out [T, d] (dt) OUTPUT */
+moe_status_t moe_combine(const void* y_perm, const float* topk_gate, const int32_t* dest_pos,
+                         const void* shared_out, int64_t T, int64_t d, int32_t k, moe_dtype_t dt,
+                         void* out, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Backward                                                                                    */
+
+/* Backward of moe_combine:
+ *   dy_perm[dest_pos[t*k+j]] = topk_gate[t,j] * dout[t]                 OUTPUT [T*k, d] (dt)
+ *   dgate[t,j] = <dout[t], y_perm[dest_pos[t*k+j]]> (fp32)              OUTPUT [T, k] or NULL
+ * (the shared expert's output gradient is dout itself). */
+moe_status_t moe_combine_bwd(const void* dout, const void* y_perm, const float* topk_gate,
+                             const int32_t* dest_pos, int64_t T, int64_t d, int32_t k,
+                             moe_dtype_t dt, void* dy_perm, float* dgate, moe_stream_t stream);
+
+/* Backward of the row gather plus the other contributions to dx:
+ *   dx[t] = sum_j dx_perm[dest_pos[t*k+j]] + dx_add0[t] + dx_add1[t]   (fp32 sum)
+ *   dx_perm [T*k, d] (dt) INPUT; dx_add0, dx_add1 [T, d] (dt) INPUT or NULL; dx [T, d] OUTPUT */
+moe_status_t moe_permute_bwd(const void* dx_perm, const int32_t* dest_pos, const void* dx_add0,
+                             const void* dx_add1, int64_t T, int64_t d, int32_t k,
+                             moe_dtype_t dt, void* dx, moe_stream_t stream);
+
+/* Router backward (learned routing, renormalize = 1).  With g the gates and dg their gradient,
+ * the logit gradient is dL[t, S_j] = g_j (dg_j - sum_i g_i dg_i) on the chosen experts and 0
+ * elsewhere (the bias, a constant, gets none).  Then
+ *   dw_router = dL^T x   [E, d] float OUTPUT (an expert no token chose gets exact zeros)
+ *   dx_router = dL w_router  [T, d] (dt) OUTPUT
+ * Inputs: dgate, topk_gate [T, k] float; topk_idx [T, k]; offsets [E+1] and src_row [T*k] from
+ * moe_permute; x [T, d]; w_router [E, d].  ws: moe_route_bwd_workspace_size(T, d, E, k) bytes.
+ * Source: "Olmo-core DDP MoE examples", "Production throughput runs" (learned routing is
+ * trained).  renormalize = 0 returns MOE_ERR_UNSUPPORTED. */
+size_t moe_route_bwd_workspace_size(int64_t T, int64_t d, int32_t E, int32_t k);
+moe_status_t moe_route_bwd(const float* dgate, const float* topk_gate, const int32_t* topk_idx,
+                           const int32_t* offsets, const int32_t* src_row, const void* x,
+                           const void* w_router, int64_t T, int64_t d, int32_t E, int32_t k,
+                           int32_t renormalize, moe_dtype_t dt, float* dw_router, void* dx_router,
+                           void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Utilities                                                                                   */
+
+const char* moe_status_string(moe_status_t status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version, e.g. "libmoe 0.1 gfx950". */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

@@ -1,0 +1,356 @@
+// libmoe C-ABI: argument validation, workspace carving and kernel launches.
+// Every entry point checks its arguments on the host before enqueuing anything, never
+// synchronises, never allocates, and reports errors through status codes.
+#include "libmoe.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status_t hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxInt = 0x7fffffff;
+
+#define CHECK(cond, st, ...)                 \
+  do {                                       \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+moe_status_t check_dtype(moe_dtype_t dt) {
+  CHECK(dt == MOE_F32 || dt == MOE_BF16, MOE_ERR_INVALID_VALUE, "dt must be MOE_F32 or MOE_BF16");
+  return MOE_OK;
+}
+
+moe_status_t check_tokens(int64_t T, int64_t d, int32_t E, int32_t k) {
+  CHECK(T >= 0, MOE_ERR_INVALID_VALUE, "T must be >= 0 (got %lld)", (long long)T);
+  CHECK(d > 0, MOE_ERR_INVALID_VALUE, "d must be > 0 (got %lld)", (long long)d);
+  CHECK(E > 0, MOE_ERR_INVALID_VALUE, "E must be > 0 (got %d)", E);
+  CHECK(k > 0 && k <= E, MOE_ERR_INVALID_VALUE, "k must be in [1, E] (got k=%d, E=%d)", k, E);
+  CHECK(E <= 256, MOE_ERR_UNSUPPORTED, "E > 256 is not supported (got %d)", E);
+  CHECK(k <= 8, MOE_ERR_UNSUPPORTED, "k > 8 is not supported (got %d)", k);
+  CHECK(d <= kMaxInt && T <= kMaxInt, MOE_ERR_UNSUPPORTED, "T and d must fit in int32");
+  CHECK(T * k <= kMaxInt - 8, MOE_ERR_UNSUPPORTED, "T*k must be < 2^31");
+  CHECK(T * (int64_t)E <= kMaxInt, MOE_ERR_UNSUPPORTED, "T*E must be < 2^31");
+  return MOE_OK;
+}
+
+moe_status_t check_mlp(int32_t G, int64_t M, int64_t d, int64_t f, moe_dtype_t dt) {
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  CHECK(G > 0, MOE_ERR_INVALID_VALUE, "G must be > 0 (got %d)", G);
+  CHECK(M >= 0, MOE_ERR_INVALID_VALUE, "M must be >= 0 (got %lld)", (long long)M);
+  CHECK(d > 0 && f > 0, MOE_ERR_INVALID_VALUE, "d and f must be > 0");
+  CHECK(d % 128 == 0 && f % 128 == 0, MOE_ERR_UNSUPPORTED,
+        "d and f must be multiples of 128 (got d=%lld, f=%lld)", (long long)d, (long long)f);
+  CHECK(M <= kMaxInt / 2 && d <= 65536 && f <= 65536 && G <= 65536, MOE_ERR_UNSUPPORTED,
+        "sizes out of the supported range");
+  CHECK(((M + 127) / 128 + G) * (2 * f / 64 + d / 64) < kMaxInt, MOE_ERR_UNSUPPORTED, "grid too large");
+  return MOE_OK;
+}
+
+inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+inline size_t esize(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+inline hipStream_t S(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+moe_status_t run_gemm(int mode, const moe::GemmArgs& a, moe_dtype_t dt, moe_stream_t s,
+                      const char* what) {
+  return hip_check(moe::launch_grouped_gemm(mode, a, dt == MOE_BF16, S(s)), what);
+}
+
+moe::GemmArgs base_args(const int32_t* offsets, int32_t G, int64_t M, int64_t d, int64_t f, void* ws) {
+  moe::GemmArgs a{};
+  a.offsets = offsets;
+  a.tile_prefix = reinterpret_cast<int32_t*>(ws);
+  a.G = G;
+  a.M = (int)M;
+  a.d = (int)d;
+  a.f = (int)f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_VALUE: return "MOE_ERR_INVALID_VALUE";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+
+// ---------------------------------------------------------------------------------------------
+
+moe_status_t moe_route(const void* x, const void* w_router, const float* bias, float* logits,
+                       int64_t T, int64_t d, int32_t E, int32_t k, int32_t renormalize,
+                       moe_dtype_t dt, int32_t* topk_idx, float* topk_gate, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, E, k)) != MOE_OK) return st;
+  CHECK(renormalize == 0 || renormalize == 1, MOE_ERR_INVALID_VALUE, "renormalize must be 0 or 1");
+  CHECK(!w_router || x, MOE_ERR_INVALID_VALUE, "x is NULL with a learned router");
+  CHECK(w_router || !bias, MOE_ERR_INVALID_VALUE, "bias given without a learned router");
+  if (T == 0) return MOE_OK;
+  CHECK(logits && topk_idx && topk_gate, MOE_ERR_INVALID_VALUE, "logits/topk_idx/topk_gate is NULL");
+  if (w_router) {
+    st = hip_check(moe::launch_router_logits(x, w_router, bias, logits, (int)T, (int)d, E,
+                                             dt == MOE_BF16, S(stream)),
+                   "router logits");
+    if (st != MOE_OK) return st;
+  }
+  return hip_check(moe::launch_topk_gate(logits, (int)T, E, k, renormalize, topk_idx, topk_gate, S(stream)),
+                   "top-k");
+}
+
+size_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || E <= 0 || k <= 0) return 0;
+  return moe::permute_ws_bytes(T, E, k);
+}
+
+moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E,
+                         int32_t k, moe_dtype_t dt, int32_t* counts, int32_t* offsets,
+                         int32_t* dest_pos, int32_t* src_row, void* x_perm, void* ws,
+                         size_t ws_bytes, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, E, k)) != MOE_OK) return st;
+  CHECK(counts && offsets, MOE_ERR_INVALID_VALUE, "counts/offsets is NULL");
+  CHECK(T == 0 || (topk_idx && dest_pos && src_row), MOE_ERR_INVALID_VALUE,
+        "topk_idx/dest_pos/src_row is NULL");
+  CHECK(!x_perm || x || T == 0, MOE_ERR_INVALID_VALUE, "x is NULL while x_perm is requested");
+  CHECK(!x_perm || d % 8 == 0, MOE_ERR_UNSUPPORTED, "the row gather needs d %% 8 == 0 (got %lld)",
+        (long long)d);
+  const size_t need = moe::permute_ws_bytes(T, E, k);
+  CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+        ws ? ws_bytes : (size_t)0);
+  return hip_check(moe::launch_permute(x, topk_idx, (int)T, (int)d, E, k, dt == MOE_BF16, counts,
+                                       offsets, dest_pos, src_row, x_perm, ws, S(stream)),
+                   "permute");
+}
+
+// ---------------------------------------------------------------------------------------------
+
+size_t moe_grouped_mlp_fwd_workspace_size(int64_t M, int32_t G, int64_t d, int64_t f) {
+  (void)M; (void)d; (void)f;
+  if (G <= 0) return 0;
+  return moe::gemm_ws_bytes(G);
+}
+
+size_t moe_grouped_mlp_bwd_workspace_size(int64_t M, int32_t G, int64_t d, int64_t f) {
+  (void)d;
+  if (G <= 0 || M < 0 || f <= 0) return 0;
+  // dAB is sized for fp32 so one workspace serves both element types.
+  return moe::gemm_ws_bytes(G) + align256((size_t)M * 2 * f * 4);
+}
+
+#define MLP_COMMON_CHECKS(need)                                                              \
+  g_err.clear();                                                                             \
+  moe_status_t st = check_mlp(G, M, d, f, dt);                                               \
+  if (st != MOE_OK) return st;                                                               \
+  CHECK(offsets, MOE_ERR_INVALID_VALUE, "offsets is NULL");                                  \
+  CHECK(ws && ws_bytes >= (need), MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", \
+        (size_t)(need), ws ? ws_bytes : (size_t)0);
+
+moe_status_t moe_expert_gate_up_fwd(const void* x_in, const int32_t* offsets, int32_t G,
+                                    int64_t M, int64_t d, int64_t f, const void* w1,
+                                    const void* w3, moe_dtype_t dt, void* a_stash, void* b_stash,
+                                    void* h, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
+  CHECK(w1 && w3 && (M == 0 || (x_in && h)), MOE_ERR_INVALID_VALUE, "x_in/w1/w3/h is NULL");
+  CHECK((a_stash == nullptr) == (b_stash == nullptr), MOE_ERR_INVALID_VALUE,
+        "a_stash and b_stash must both be given or both be NULL");
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  a.a = x_in; a.b0 = w1; a.b1 = w3; a.out0 = a_stash; a.out1 = b_stash; a.out2 = h;
+  return run_gemm(moe::GEMM_UP_FWD, a, dt, stream, "gate/up GEMM");
+}
+
+moe_status_t moe_expert_down_fwd(const void* h, const int32_t* offsets, int32_t G, int64_t M,
+                                 int64_t d, int64_t f, const void* w2, moe_dtype_t dt, void* y,
+                                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
+  CHECK(w2 && (M == 0 || (h && y)), MOE_ERR_INVALID_VALUE, "h/w2/y is NULL");
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  a.a = h; a.b0 = w2; a.out0 = y;
+  return run_gemm(moe::GEMM_DOWN_FWD, a, dt, stream, "down GEMM");
+}
+
+moe_status_t moe_expert_down_bwd(const void* dy, const void* a_stash, const void* b_stash,
+                                 const int32_t* offsets, int32_t G, int64_t M, int64_t d,
+                                 int64_t f, const void* w2, moe_dtype_t dt, void* dab, void* ws,
+                                 size_t ws_bytes, moe_stream_t stream) {
+  MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
+  CHECK(w2 && (M == 0 || (dy && a_stash && b_stash && dab)), MOE_ERR_INVALID_VALUE,
+        "dy/a/b/w2/dab is NULL");
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  a.a = dy; a.b0 = w2; a.aux0 = a_stash; a.aux1 = b_stash; a.out0 = dab;
+  return run_gemm(moe::GEMM_DOWN_BWD, a, dt, stream, "down dgrad GEMM");
+}
+
+moe_status_t moe_expert_down_wgrad(const void* dy, const void* h, const int32_t* offsets,
+                                   int32_t G, int64_t M, int64_t d, int64_t f, moe_dtype_t dt,
+                                   void* dw2, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
+  CHECK(dw2 && (M == 0 || (dy && h)), MOE_ERR_INVALID_VALUE, "dy/h/dw2 is NULL");
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  a.a = dy; a.b0 = h; a.out0 = dw2;
+  return run_gemm(moe::GEMM_DOWN_WGRAD, a, dt, stream, "down wgrad GEMM");
+}
+
+moe_status_t moe_expert_gate_up_dgrad(const void* dab, const int32_t* offsets, int32_t G,
+                                      int64_t M, int64_t d, int64_t f, const void* w1,
+                                      const void* w3, moe_dtype_t dt, void* dx_in, void* ws,
+                                      size_t ws_bytes, moe_stream_t stream) {
+  MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
+  CHECK(w1 && w3 && (M == 0 || (dab && dx_in)), MOE_ERR_INVALID_VALUE, "dab/w1/w3/dx_in is NULL");
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  a.a = dab; a.b0 = w1; a.b1 = w3; a.out0 = dx_in;
+  return run_gemm(moe::GEMM_UP_DGRAD, a, dt, stream, "gate/up dgrad GEMM");
+}
+
+moe_status_t moe_expert_gate_up_wgrad(const void* dab, const void* x_in, const int32_t* offsets,
+                                      int32_t G, int64_t M, int64_t d, int64_t f, moe_dtype_t dt,
+                                      void* dw1, void* dw3, void* ws, size_t ws_bytes,
+                                      moe_stream_t stream) {
+  MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
+  CHECK(dw1 && dw3 && (M == 0 || (dab && x_in)), MOE_ERR_INVALID_VALUE, "dab/x_in/dw1/dw3 is NULL");
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  a.a = dab; a.b0 = x_in; a.out0 = dw1; a.out1 = dw3;
+  return run_gemm(moe::GEMM_UP_WGRAD, a, dt, stream, "gate/up wgrad GEMM");
+}
+
+moe_status_t moe_grouped_mlp_fwd(const void* x_in, const int32_t* offsets, int32_t G, int64_t M,
+                                 int64_t d, int64_t f, const void* w1, const void* w3,
+                                 const void* w2, moe_dtype_t dt, void* a_stash, void* b_stash,
+                                 void* h, void* y, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = moe_expert_gate_up_fwd(x_in, offsets, G, M, d, f, w1, w3, dt, a_stash, b_stash,
+                                           h, ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_down_fwd(h, offsets, G, M, d, f, w2, dt, y, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_grouped_mlp_bwd(const void* dy, const void* x_in, const void* a, const void* b,
+                                 const void* h, const int32_t* offsets, int32_t G, int64_t M,
+                                 int64_t d, int64_t f, const void* w1, const void* w3,
+                                 const void* w2, moe_dtype_t dt, void* dx_in, void* dw1, void* dw3,
+                                 void* dw2, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  MLP_COMMON_CHECKS(moe_grouped_mlp_bwd_workspace_size(M, G, d, f));
+  CHECK(w1 && w3 && w2 && dw1 && dw3 && dw2, MOE_ERR_INVALID_VALUE, "weight or gradient pointer is NULL");
+  CHECK(M == 0 || (dy && x_in && a && b && h && dx_in), MOE_ERR_INVALID_VALUE,
+        "activation pointer is NULL");
+  void* dab = reinterpret_cast<char*>(ws) + moe::gemm_ws_bytes(G);
+  const size_t gws = moe::gemm_ws_bytes(G);
+  if ((st = moe_expert_down_bwd(dy, a, b, offsets, G, M, d, f, w2, dt, dab, ws, gws, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_expert_down_wgrad(dy, h, offsets, G, M, d, f, dt, dw2, ws, gws, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_expert_gate_up_dgrad(dab, offsets, G, M, d, f, w1, w3, dt, dx_in, ws, gws, stream)) != MOE_OK)
+    return st;
+  return moe_expert_gate_up_wgrad(dab, x_in, offsets, G, M, d, f, dt, dw1, dw3, ws, gws, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+
+moe_status_t moe_combine(const void* y_perm, const float* topk_gate, const int32_t* dest_pos,
+                         const void* shared_out, int64_t T, int64_t d, int32_t k, moe_dtype_t dt,
+                         void* out, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, k, k)) != MOE_OK) return st;
+  CHECK(d % 8 == 0, MOE_ERR_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
+  if (T == 0) return MOE_OK;
+  CHECK(y_perm && topk_gate && dest_pos && out, MOE_ERR_INVALID_VALUE, "y_perm/topk_gate/dest_pos/out is NULL");
+  return hip_check(moe::launch_combine(y_perm, topk_gate, dest_pos, shared_out, (int)T, (int)d, k,
+                                       dt == MOE_BF16, out, S(stream)),
+                   "combine");
+}
+
+moe_status_t moe_combine_bwd(const void* dout, const void* y_perm, const float* topk_gate,
+                             const int32_t* dest_pos, int64_t T, int64_t d, int32_t k,
+                             moe_dtype_t dt, void* dy_perm, float* dgate, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, k, k)) != MOE_OK) return st;
+  CHECK(d % 8 == 0, MOE_ERR_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
+  if (T == 0) return MOE_OK;
+  CHECK(dout && topk_gate && dest_pos && dy_perm, MOE_ERR_INVALID_VALUE, "dout/topk_gate/dest_pos/dy_perm is NULL");
+  CHECK(!dgate || y_perm, MOE_ERR_INVALID_VALUE, "y_perm is NULL while dgate is requested");
+  return hip_check(moe::launch_combine_bwd(dout, y_perm, topk_gate, dest_pos, (int)T, (int)d, k,
+                                           dt == MOE_BF16, dy_perm, dgate, S(stream)),
+                   "combine backward");
+}
+
+moe_status_t moe_permute_bwd(const void* dx_perm, const int32_t* dest_pos, const void* dx_add0,
+                             const void* dx_add1, int64_t T, int64_t d, int32_t k,
+                             moe_dtype_t dt, void* dx, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, k, k)) != MOE_OK) return st;
+  CHECK(d % 8 == 0, MOE_ERR_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
+  if (T == 0) return MOE_OK;
+  CHECK(dx_perm && dest_pos && dx, MOE_ERR_INVALID_VALUE, "dx_perm/dest_pos/dx is NULL");
+  return hip_check(moe::launch_permute_bwd(dx_perm, dest_pos, dx_add0, dx_add1, (int)T, (int)d, k,
+                                           dt == MOE_BF16, dx, S(stream)),
+                   "permute backward");
+}
+
+size_t moe_route_bwd_workspace_size(int64_t T, int64_t d, int32_t E, int32_t k) {
+  if (T < 0 || d <= 0 || E <= 0 || k <= 0) return 0;
+  return moe::route_bwd_ws_bytes(T, d, E, k);
+}
+
+moe_status_t moe_route_bwd(const float* dgate, const float* topk_gate, const int32_t* topk_idx,
+                           const int32_t* offsets, const int32_t* src_row, const void* x,
+                           const void* w_router, int64_t T, int64_t d, int32_t E, int32_t k,
+                           int32_t renormalize, moe_dtype_t dt, float* dw_router, void* dx_router,
+                           void* ws, size_t ws_bytes, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, E, k)) != MOE_OK) return st;
+  CHECK(renormalize == 0 || renormalize == 1, MOE_ERR_INVALID_VALUE, "renormalize must be 0 or 1");
+  CHECK(renormalize == 1, MOE_ERR_UNSUPPORTED, "router backward supports renormalized gates only");
+  CHECK(offsets && w_router && dw_router, MOE_ERR_INVALID_VALUE, "offsets/w_router/dw_router is NULL");
+  CHECK(T == 0 || (dgate && topk_gate && topk_idx && src_row && x && dx_router), MOE_ERR_INVALID_VALUE,
+        "a per-token pointer is NULL");
+  const size_t need = moe::route_bwd_ws_bytes(T, d, E, k);
+  CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+        ws ? ws_bytes : (size_t)0);
+  return hip_check(moe::launch_route_bwd(dgate, topk_gate, topk_idx, offsets, src_row, x, w_router,
+                                         (int)T, (int)d, E, k, dt == MOE_BF16, dw_router, dx_router,
+                                         ws, S(stream)),
+                   "router backward");
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Weighted combine of the MoE layer and its backward.
+//
+// The output of a token is the gate-weighted sum of its k routed experts' outputs plus the shared
+// expert's output ("Olmo-core DDP MoE examples", "Production throughput runs": top-4 routing with
+// one shared expert).  Row gathers are 16-byte vector loads; sums are fp32; one block per token.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <typename T> struct V8;
+template <> struct V8<bf16_t> {
+  __device__ static void load(const bf16_t* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(bf16_t* p, const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct V8<float> {
+  __device__ static void load(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ static void store(float* p, const float (&v)[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// out[t] = shared[t] + sum_j g[t,j] y_perm[dest_pos[t*k+j]]
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* y_perm, const float* gate,
+                                                      const int32_t* dest_pos, const T* shared,
+                                                      int d, int k, T* out) {
+  const int t = blockIdx.x;
+  int rows[8];
+  float g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = j < k ? dest_pos[(size_t)t * k + j] : 0;
+    g[j] = j < k ? gate[(size_t)t * k + j] : 0.0f;
+  }
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        V8<T>::load(y_perm + (size_t)rows[j] * d + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += g[j] * v[i];
+      }
+    }
+    if (shared) {
+      V8<T>::load(shared + (size_t)t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    V8<T>::store(out + (size_t)t * d + c, acc);
+  }
+}
+
+// dy_perm[dest_pos[t*k+j]] = g[t,j] dout[t];  dgate[t,j] = <dout[t], y_perm[dest_pos[t*k+j]]>.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T* y_perm,
+                                                          const float* gate,
+                                                          const int32_t* dest_pos, int d, int k,
+                                                          T* dy_perm, float* dgate) {
+  __shared__ float red[4][8];
+  const int t = blockIdx.x;
+  int rows[8];
+  float g[8], dot[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    rows[j] = j < k ? dest_pos[(size_t)t * k + j] : 0;
+    g[j] = j < k ? gate[(size_t)t * k + j] : 0.0f;
+    dot[j] = 0.0f;
+  }
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float go[8], v[8], o[8];
+    V8<T>::load(dout + (size_t)t * d + c, go);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = g[j] * go[i];
+        V8<T>::store(dy_perm + (size_t)rows[j] * d + c, o);
+        if (dgate) {
+          V8<T>::load(y_perm + (size_t)rows[j] * d + c, v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dot[j] += go[i] * v[i];
+        }
+      }
+    }
+  }
+  if (!dgate) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float s = dot[j];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) red[w][j] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    const int j = threadIdx.x;
+    dgate[(size_t)t * k + j] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y_perm, const float* gate, const int32_t* dest_pos,
+                          const void* shared_out, int T, int d, int k, bool bf16, void* out,
+                          hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
+                       reinterpret_cast<const bf16_t*>(y_perm), gate, dest_pos,
+                       reinterpret_cast<const bf16_t*>(shared_out), d, k, reinterpret_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(y_perm), gate, dest_pos,
+                       reinterpret_cast<const float*>(shared_out), d, k, reinterpret_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dout, const void* y_perm, const float* gate,
+                              const int32_t* dest_pos, int T, int d, int k, bool bf16,
+                              void* dy_perm, float* dgate, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
+                       reinterpret_cast<const bf16_t*>(dout), reinterpret_cast<const bf16_t*>(y_perm),
+                       gate, dest_pos, d, k, reinterpret_cast<bf16_t*>(dy_perm), dgate);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(T), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(dout), reinterpret_cast<const float*>(y_perm), gate,
+                       dest_pos, d, k, reinterpret_cast<float*>(dy_perm), dgate);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,268 @@
+// Token dispatch of the MoE layer: per-expert histogram, exclusive prefix sum, stable
+// permutation to an expert-major layout and the row gather; plus the gather's backward.
+//
+// Tokens are moved to experts that stay in place ("Olmo-core 3 Opens Large MoE Training",
+// "Enhanced Key Takeaways" and "Technical Deep Dive").  The permutation is a stable counting sort
+// of the (token, slot) assignments by expert, so within an expert rows keep ascending token
+// order.  Ranks come from wavefront ballots and a scan, never from atomic slot claims, so every
+// output is deterministic.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int CH_THREADS = 256;
+constexpr int CH_PER_THREAD = 16;
+constexpr int CHUNK = CH_THREADS * CH_PER_THREAD;  // assignments per chunk (4096)
+
+// Pass 1.  Each block ranks the assignments of one chunk among equal experts, in assignment
+// order.  Wave w takes the contiguous quarter [w*1024, (w+1)*1024) of the chunk in 16 steps of
+// 64; inside a step the rank of a lane is the number of lower lanes with the same expert, found
+// from ballots of the expert id's bits.  Afterwards the per-wave counts are prefix-summed so the
+// rank is the chunk-local stable rank.  Writes local_rank[a] and chunk_counts[chunk][E].
+__global__ __launch_bounds__(CH_THREADS) void local_rank_kernel(const int32_t* topk_idx, int Tk,
+                                                                int E, int nbits,
+                                                                int32_t* local_rank,
+                                                                int32_t* chunk_counts) {
+  __shared__ int cnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < 4 * 256; i += CH_THREADS) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * CHUNK + w * (CHUNK / 4);
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int ev[CH_PER_THREAD], rk[CH_PER_THREAD];
+#pragma unroll
+  for (int it = 0; it < CH_PER_THREAD; ++it) {
+    const int a = base + it * 64 + lane;
+    const bool valid = a < Tk;
+    const int e = valid ? topk_idx[a] : 0;
+    unsigned long long peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int before = __popcll(peers & lt);
+    int r = 0;
+    if (valid) r = cnt[w][e] + before;
+    // The highest lane of each group of equal experts advances the wave's counter.
+    const bool leader = valid && ((peers >> lane) == 1ull);
+    __builtin_amdgcn_wave_barrier();
+    if (leader) cnt[w][e] = r + 1;
+    __builtin_amdgcn_wave_barrier();
+    ev[it] = valid ? e : -1;
+    rk[it] = r;
+  }
+  __syncthreads();
+  // Exclusive prefix over the four waves, per expert; chunk totals.
+  for (int e = tid; e < E; e += CH_THREADS) {
+    int run = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = cnt[q][e];
+      cnt[q][e] = run;
+      run += c;
+    }
+    chunk_counts[(size_t)blockIdx.x * E + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < CH_PER_THREAD; ++it) {
+    const int a = base + it * 64 + lane;
+    if (ev[it] >= 0) local_rank[a] = rk[it] + cnt[w][ev[it]];
+  }
+}
+
+// Pass 2.  One block: counts, offsets, and the first row of every (chunk, expert) pair.
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t* chunk_counts, int nch, int E,
+                                                   int Tk, int32_t* counts, int32_t* offsets,
+                                                   int32_t* chunk_base) {
+  __shared__ int s[256];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nch; ++c) {
+      const int v = chunk_counts[(size_t)c * E + e];
+      chunk_base[(size_t)c * E + e] = total;
+      total += v;
+    }
+  }
+  s[e] = total;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = e >= off ? s[e - off] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  const int excl = s[e] - total;
+  if (e < E) {
+    counts[e] = total;
+    offsets[e] = excl;
+    for (int c = 0; c < nch; ++c) chunk_base[(size_t)c * E + e] += excl;
+  }
+  if (e == 0) offsets[E] = Tk;
+}
+
+// Pass 3.  dest_pos, src_row, and (optionally) the row copy x_perm[dest] = x[a / k].
+// One block handles 8 assignments; rows are copied 16 bytes per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void scatter_gather_kernel(const T* x, const int32_t* topk_idx,
+                                                             const int32_t* local_rank,
+                                                             const int32_t* chunk_base, int Tk,
+                                                             int d, int E, int k,
+                                                             int32_t* dest_pos, int32_t* src_row,
+                                                             T* x_perm) {
+  __shared__ int dst_s[8];
+  __shared__ int tok_s[8];
+  const int a0 = blockIdx.x * 8;
+  if (threadIdx.x < 8) {
+    const int a = a0 + threadIdx.x;
+    int dst = -1;
+    if (a < Tk) {
+      const int e = topk_idx[a];
+      dst = chunk_base[(size_t)(a / CHUNK) * E + e] + local_rank[a];
+      dest_pos[a] = dst;
+      src_row[dst] = a;
+    }
+    dst_s[threadIdx.x] = dst;
+    tok_s[threadIdx.x] = a / k;
+  }
+  if (x_perm == nullptr) return;
+  __syncthreads();
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
+  const int nv = d / V;
+  for (int i = 0; i < 8; ++i) {
+    const int dst = dst_s[i];
+    if (dst < 0) break;
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tok_s[i] * d);
+    uint4* out = reinterpret_cast<uint4*>(x_perm + (size_t)dst * d);
+    for (int c = threadIdx.x; c < nv; c += 256) out[c] = src[c];
+  }
+}
+
+// 8 consecutive elements as fp32.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  __device__ static void load(const bf16_t* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(bf16_t* p, const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Vec8<float> {
+  __device__ static void load(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ static void store(float* p, const float (&v)[8]) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// dx[t] = sum_j dx_perm[dest_pos[t*k+j]] + add0[t] + add1[t], fp32 sums, one block per token.
+template <typename T>
+__global__ __launch_bounds__(256) void permute_bwd_kernel(const T* dx_perm, const int32_t* dest_pos,
+                                                          const T* add0, const T* add1, int d,
+                                                          int k, T* dx) {
+  const int t = blockIdx.x;
+  int rows[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rows[j] = j < k ? dest_pos[(size_t)t * k + j] : 0;
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        Vec8<T>::load(dx_perm + (size_t)rows[j] * d + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
+    }
+    if (add0) {
+      Vec8<T>::load(add0 + (size_t)t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (add1) {
+      Vec8<T>::load(add1 + (size_t)t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    Vec8<T>::store(dx + (size_t)t * d + c, acc);
+  }
+}
+
+inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t permute_ws_bytes(long long T, int E, int k) {
+  const long long Tk = T * k;
+  const long long nch = (Tk + CHUNK - 1) / CHUNK;
+  return 2 * align256((size_t)nch * E * sizeof(int32_t)) + align256((size_t)Tk * sizeof(int32_t));
+}
+
+hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,
+                          bool bf16, int32_t* counts, int32_t* offsets, int32_t* dest_pos,
+                          int32_t* src_row, void* x_perm, void* ws, hipStream_t s) {
+  const int Tk = T * k;
+  const int nch = ceil_div(Tk, CHUNK);
+  char* p = reinterpret_cast<char*>(ws);
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)nch * E * sizeof(int32_t));
+  int32_t* chunk_base = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)nch * E * sizeof(int32_t));
+  int32_t* local_rank = reinterpret_cast<int32_t*>(p);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (Tk > 0)
+    hipLaunchKernelGGL(local_rank_kernel, dim3(nch), dim3(CH_THREADS), 0, s, topk_idx, Tk, E, nbits,
+                       local_rank, chunk_counts);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, Tk, counts, offsets,
+                     chunk_base);
+  if (Tk > 0) {
+    if (bf16)
+      hipLaunchKernelGGL(scatter_gather_kernel<bf16_t>, dim3(ceil_div(Tk, 8)), dim3(256), 0, s,
+                         reinterpret_cast<const bf16_t*>(x), topk_idx, local_rank, chunk_base, Tk, d,
+                         E, k, dest_pos, src_row, reinterpret_cast<bf16_t*>(x_perm));
+    else
+      hipLaunchKernelGGL(scatter_gather_kernel<float>, dim3(ceil_div(Tk, 8)), dim3(256), 0, s,
+                         reinterpret_cast<const float*>(x), topk_idx, local_rank, chunk_base, Tk, d,
+                         E, k, dest_pos, src_row, reinterpret_cast<float*>(x_perm));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_bwd(const void* dx_perm, const int32_t* dest_pos, const void* add0,
+                              const void* add1, int T, int d, int k, bool bf16, void* dx,
+                              hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(permute_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
+                       reinterpret_cast<const bf16_t*>(dx_perm), dest_pos,
+                       reinterpret_cast<const bf16_t*>(add0), reinterpret_cast<const bf16_t*>(add1), d,
+                       k, reinterpret_cast<bf16_t*>(dx));
+  else
+    hipLaunchKernelGGL(permute_bwd_kernel<float>, dim3(T), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(dx_perm), dest_pos,
+                       reinterpret_cast<const float*>(add0), reinterpret_cast<const float*>(add1), d, k,
+                       reinterpret_cast<float*>(dx));
+  return hipGetLastError();
+}
+
+}  // namespace moe

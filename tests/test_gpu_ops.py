@@ -1,0 +1,302 @@
+"""Per-call parity of libmoe's HIP kernels against the CPU oracle (GPU).
+
+Integer, index and copy results must match bit for bit; floating-point results must be within a
+max-abs-relative error of 1e-5 (fp32) or 2e-2 (bf16 storage, fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_20_amd import inputs as I
+from mixture_experts_layer_20_amd import libmoe as L
+from oracle import moe_oracle as O
+from tests.gpu_helpers import DEV, TOL, as_dtype_values, assert_close, dev_tensor, log, tnp
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": L.MOE_F32, "bf16": L.MOE_BF16}
+
+
+def i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+
+
+def f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
+
+
+def empty(shape, dtype):
+    return torch.empty(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device=DEV)
+
+
+# ------------------------------------------------------------------------------------------ route
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,k,bias", [(333, 256, 8, 2, False), (200, 96, 64, 4, True),
+                                           (70, 2048, 128, 4, False), (65, 40, 256, 8, True),
+                                           (17, 64, 3, 3, True), (5, 16, 1, 1, False)])
+def test_learned_route_bit_exact(dtype, T, d, E, k, bias):
+    log(f"route learned {dtype} T={T} d={d} E={E} k={k} bias={bias}")
+    rng = np.random.default_rng(T + E)
+    x = as_dtype_values(rng.standard_normal((T, d)), dtype)
+    w = as_dtype_values(0.02 * rng.standard_normal((E, d)), dtype)
+    b = (1.5 * rng.standard_normal(E)).astype(np.float32) if bias else None
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    L.moe_route(dev_tensor(x, dtype), dev_tensor(w, dtype), f32(b) if bias else None, logits, T, d, E, k, 1,
+                DT[dtype], idx, gate)
+    torch.cuda.synchronize()
+    ref_logits = O.canonical_router_logits(x, w, b)
+    assert np.array_equal(tnp(logits).view(np.uint32), ref_logits.view(np.uint32)), "logits not bit-exact"
+    ref_idx = O.select_topk(ref_logits, k)
+    assert np.array_equal(tnp(idx), ref_idx)
+    assert_close("gates", tnp(gate), O.gate_weights(ref_logits, ref_idx), 1e-6)
+
+
+@pytest.mark.parametrize("renormalize", [1, 0])
+@pytest.mark.parametrize("kind", ["gauss", "integer_ties", "signed_zero"])
+@pytest.mark.parametrize("E,k", [(64, 4), (256, 8), (8, 8), (130, 3)])
+def test_random_route_ties(renormalize, kind, E, k):
+    log(f"route random {kind} E={E} k={k} renorm={renormalize}")
+    T = 1000
+    rng = np.random.default_rng(E * 10 + k)
+    if kind == "gauss":
+        Lg = rng.standard_normal((T, E)).astype(np.float32)
+    elif kind == "integer_ties":
+        Lg = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    else:
+        Lg = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), size=(T, E))
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    L.moe_route(None, None, None, f32(Lg), T, 64, E, k, renormalize, L.MOE_BF16, idx, gate)
+    torch.cuda.synchronize()
+    ref_idx = O.select_topk(Lg, k)
+    assert np.array_equal(tnp(idx), ref_idx)
+    assert_close("gates", tnp(gate), O.gate_weights(Lg, ref_idx, renormalize=bool(renormalize)), 1e-6)
+
+
+# ---------------------------------------------------------------------------------------- permute
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,k,skew", [(1, 8, 1, 1, 0.0), (1000, 256, 16, 4, 0.0),
+                                           (4097, 64, 64, 4, 3.0), (3000, 128, 256, 8, 0.0),
+                                           (8192, 2048, 64, 4, 0.0), (2500, 16, 5, 2, 10.0)])
+def test_permute_bit_exact(dtype, T, d, E, k, skew):
+    log(f"permute {dtype} T={T} d={d} E={E} k={k} skew={skew}")
+    rng = np.random.default_rng(T)
+    Lg = rng.standard_normal((T, E)).astype(np.float32) + skew * rng.standard_normal(E).astype(np.float32)
+    idx = O.select_topk(Lg, k)
+    x = as_dtype_values(rng.standard_normal((T, d)), dtype)
+    Tk = T * k
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    dest = torch.empty(Tk, dtype=torch.int32, device=DEV)
+    src = torch.empty(Tk, dtype=torch.int32, device=DEV)
+    xp = empty((Tk, d), dtype)
+    wsn = L.moe_permute_workspace_size(T, E, k)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    L.moe_permute(dev_tensor(x, dtype), i32(idx), T, d, E, k, DT[dtype], counts, offsets, dest, src, xp, ws, wsn)
+    torch.cuda.synchronize()
+    rc, ro, rd, rs = O.dispatch_plan(idx, E)
+    assert np.array_equal(tnp(counts), rc)
+    assert np.array_equal(tnp(offsets), ro)
+    assert np.array_equal(tnp(dest), rd)
+    assert np.array_equal(tnp(src), rs)
+    got = tnp(xp)
+    ref = O.permute_rows(x, rs, k)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------ grouped MLP
+
+def ragged_offsets(M, G, rng, empty_groups=()):
+    """Random non-decreasing group boundaries over M rows, with the listed groups empty."""
+    w = rng.random(G) + 0.05
+    for g in empty_groups:
+        w[g] = 0.0
+    cuts = np.floor(np.cumsum(w) / w.sum() * M).astype(np.int64)
+    cuts[-1] = M
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = cuts
+    for g in empty_groups:
+        off[g + 1] = off[g]
+    off = np.maximum.accumulate(off)
+    off[-1] = M
+    return off
+
+
+MLP_SHAPES = [
+    # (M, G, d, f, empty groups)
+    (1000, 8, 256, 256, (3,)),
+    (517, 5, 128, 384, (0, 4)),
+    (64, 3, 384, 128, ()),
+    (2048, 16, 256, 128, (1, 2, 15)),
+    (1, 1, 128, 128, ()),
+    (300, 1, 512, 256, ()),
+]
+
+
+def mlp_problem(M, G, d, f, dtype, seed):
+    rng = np.random.default_rng(seed)
+    v = lambda *s, std=1.0: as_dtype_values(std * rng.standard_normal(s), dtype)
+    return dict(X=v(M, d), w1=v(G, f, d, std=0.05), w3=v(G, f, d, std=0.05), w2=v(G, d, f, std=0.05),
+                dY=v(M, d))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", MLP_SHAPES)
+def test_grouped_mlp_fwd_bwd(dtype, shape):
+    M, G, d, f, empties = shape
+    log(f"grouped mlp {dtype} M={M} G={G} d={d} f={f} empty={empties}")
+    rng = np.random.default_rng(M + G)
+    off = ragged_offsets(M, G, rng, empties)
+    P = mlp_problem(M, G, d, f, dtype, M * 7 + d)
+    dtc = DT[dtype]
+    dev = {k: dev_tensor(v, dtype) for k, v in P.items()}
+    offs = i32(off)
+    a, b, h = empty((M, f), dtype), empty((M, f), dtype), empty((M, f), dtype)
+    y = empty((M, d), dtype)
+    wsn = L.moe_grouped_mlp_fwd_workspace_size(M, G, d, f)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    L.moe_grouped_mlp_fwd(dev["X"], offs, G, M, d, f, dev["w1"], dev["w3"], dev["w2"], dtc, a, b, h, y, ws, wsn)
+    dx = empty((M, d), dtype)
+    dw1, dw3, dw2 = empty((G, f, d), dtype), empty((G, f, d), dtype), empty((G, d, f), dtype)
+    bwsn = L.moe_grouped_mlp_bwd_workspace_size(M, G, d, f)
+    bws = torch.empty(bwsn, dtype=torch.uint8, device=DEV)
+    L.moe_grouped_mlp_bwd(dev["dY"], dev["X"], a, b, h, offs, G, M, d, f, dev["w1"], dev["w3"], dev["w2"], dtc,
+                          dx, dw1, dw3, dw2, bws, bwsn)
+    torch.cuda.synchronize()
+    A, B, H, Y = O.grouped_swiglu_forward(P["X"], off, P["w1"], P["w3"], P["w2"])
+    rdx, rdw1, rdw3, rdw2, rdA, rdB = O.grouped_swiglu_backward(P["dY"], P["X"], A, B, H, off, P["w1"],
+                                                                P["w3"], P["w2"])
+    tol = TOL[dtype]
+    assert_close("A", tnp(a), A, tol)
+    assert_close("B", tnp(b), B, tol)
+    assert_close("H", tnp(h), H, tol)
+    assert_close("Y", tnp(y), Y, tol)
+    assert_close("dX", tnp(dx), rdx, tol)
+    assert_close("dW1", tnp(dw1), rdw1, tol)
+    assert_close("dW3", tnp(dw3), rdw3, tol)
+    assert_close("dW2", tnp(dw2), rdw2, tol)
+    for g in empties:   # no rows: exact zeros
+        assert np.all(tnp(dw1)[g] == 0) and np.all(tnp(dw3)[g] == 0) and np.all(tnp(dw2)[g] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stage_calls_equal_combined_calls(dtype):
+    M, G, d, f = 700, 6, 256, 256
+    log(f"stage vs combined {dtype}")
+    rng = np.random.default_rng(5)
+    off = ragged_offsets(M, G, rng, (2,))
+    P = mlp_problem(M, G, d, f, dtype, 9)
+    dtc = DT[dtype]
+    dev = {k: dev_tensor(v, dtype) for k, v in P.items()}
+    offs = i32(off)
+    wsn = L.moe_grouped_mlp_bwd_workspace_size(M, G, d, f)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    outs = []
+    for staged in (False, True):
+        a, b, h, y = empty((M, f), dtype), empty((M, f), dtype), empty((M, f), dtype), empty((M, d), dtype)
+        dx, dab = empty((M, d), dtype), empty((M, 2 * f), dtype)
+        dw1, dw3, dw2 = empty((G, f, d), dtype), empty((G, f, d), dtype), empty((G, d, f), dtype)
+        if staged:
+            L.moe_expert_gate_up_fwd(dev["X"], offs, G, M, d, f, dev["w1"], dev["w3"], dtc, a, b, h, ws, wsn)
+            L.moe_expert_down_fwd(h, offs, G, M, d, f, dev["w2"], dtc, y, ws, wsn)
+            L.moe_expert_down_bwd(dev["dY"], a, b, offs, G, M, d, f, dev["w2"], dtc, dab, ws, wsn)
+            L.moe_expert_down_wgrad(dev["dY"], h, offs, G, M, d, f, dtc, dw2, ws, wsn)
+            L.moe_expert_gate_up_dgrad(dab, offs, G, M, d, f, dev["w1"], dev["w3"], dtc, dx, ws, wsn)
+            L.moe_expert_gate_up_wgrad(dab, dev["X"], offs, G, M, d, f, dtc, dw1, dw3, ws, wsn)
+        else:
+            L.moe_grouped_mlp_fwd(dev["X"], offs, G, M, d, f, dev["w1"], dev["w3"], dev["w2"], dtc, a, b, h, y,
+                                  ws, wsn)
+            L.moe_grouped_mlp_bwd(dev["dY"], dev["X"], a, b, h, offs, G, M, d, f, dev["w1"], dev["w3"],
+                                  dev["w2"], dtc, dx, dw1, dw3, dw2, ws, wsn)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (a, b, h, y, dx, dw1, dw3, dw2)])
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
+
+
+def test_forward_without_stash():
+    M, G, d, f = 400, 4, 128, 128
+    rng = np.random.default_rng(3)
+    off = ragged_offsets(M, G, rng)
+    P = mlp_problem(M, G, d, f, "bf16", 4)
+    dev = {k: dev_tensor(v, "bf16") for k, v in P.items()}
+    h, y = empty((M, f), "bf16"), empty((M, d), "bf16")
+    wsn = L.moe_grouped_mlp_fwd_workspace_size(M, G, d, f)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    L.moe_grouped_mlp_fwd(dev["X"], i32(off), G, M, d, f, dev["w1"], dev["w3"], dev["w2"], L.MOE_BF16, None,
+                          None, h, y, ws, wsn)
+    torch.cuda.synchronize()
+    _, _, H, Y = O.grouped_swiglu_forward(P["X"], off, P["w1"], P["w3"], P["w2"])
+    assert_close("Y", tnp(y), Y, 2e-2)
+
+
+# ---------------------------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,k,shared", [(500, 256, 16, 4, True), (33, 4096, 8, 2, False),
+                                             (1, 8, 1, 1, True), (300, 2048, 256, 8, True)])
+def test_combine_and_backward(dtype, T, d, E, k, shared):
+    log(f"combine {dtype} T={T} d={d} E={E} k={k} shared={shared}")
+    rng = np.random.default_rng(T * 3 + d)
+    Lg = rng.standard_normal((T, E)).astype(np.float32)
+    idx = O.select_topk(Lg, k)
+    gates = O.gate_weights(Lg, idx).astype(np.float32)
+    _, _, dest, _ = O.dispatch_plan(idx, E)
+    Y = as_dtype_values(rng.standard_normal((T * k, d)), dtype)
+    S = as_dtype_values(rng.standard_normal((T, d)), dtype) if shared else None
+    dout = as_dtype_values(rng.standard_normal((T, d)), dtype)
+    out = empty((T, d), dtype)
+    L.moe_combine(dev_tensor(Y, dtype), f32(gates), i32(dest), dev_tensor(S, dtype) if shared else None, T, d, k,
+                  DT[dtype], out)
+    dY = empty((T * k, d), dtype)
+    dg = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    L.moe_combine_bwd(dev_tensor(dout, dtype), dev_tensor(Y, dtype), f32(gates), i32(dest), T, d, k, DT[dtype],
+                      dY, dg)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert_close("out", tnp(out), O.combine(Y, gates, dest, S), tol)
+    rdY, rdg = O.combine_backward(dout, Y, gates, dest)
+    assert_close("dY", tnp(dY), rdY, tol)
+    assert_close("dgate", tnp(dg), rdg, 1e-5)
+    # permute backward with both addends
+    dXp = as_dtype_values(rng.standard_normal((T * k, d)), dtype)
+    a0 = as_dtype_values(rng.standard_normal((T, d)), dtype)
+    a1 = as_dtype_values(rng.standard_normal((T, d)), dtype)
+    dx = empty((T, d), dtype)
+    L.moe_permute_bwd(dev_tensor(dXp, dtype), i32(dest), dev_tensor(a0, dtype), dev_tensor(a1, dtype), T, d, k,
+                      DT[dtype], dx)
+    torch.cuda.synchronize()
+    assert_close("dx", tnp(dx), O.permute_backward(dXp, dest, k, (a0, a1)), tol)
+
+
+# ------------------------------------------------------------------------------------ router bwd
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,k,skew", [(600, 256, 16, 4, 0.0), (2000, 128, 64, 4, 4.0),
+                                           (40, 384, 256, 8, 0.0), (9, 16, 4, 1, 0.0)])
+def test_route_backward(dtype, T, d, E, k, skew):
+    log(f"route bwd {dtype} T={T} d={d} E={E} k={k}")
+    rng = np.random.default_rng(T + d)
+    x = as_dtype_values(rng.standard_normal((T, d)), dtype)
+    w = as_dtype_values(0.02 * rng.standard_normal((E, d)), dtype)
+    Lg = (rng.standard_normal((T, E)) + skew * rng.standard_normal(E)).astype(np.float32)
+    idx = O.select_topk(Lg, k)
+    gates = O.gate_weights(Lg, idx).astype(np.float32)
+    counts, off, dest, src = O.dispatch_plan(idx, E)
+    dg = rng.standard_normal((T, k)).astype(np.float32)
+    dw = torch.empty((E, d), dtype=torch.float32, device=DEV)
+    dxr = empty((T, d), dtype)
+    wsn = L.moe_route_bwd_workspace_size(T, d, E, k)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    L.moe_route_bwd(f32(dg), f32(gates), i32(idx), i32(off), i32(src), dev_tensor(x, dtype), dev_tensor(w, dtype),
+                    T, d, E, k, 1, DT[dtype], dw, dxr, ws, wsn)
+    torch.cuda.synchronize()
+    dL = O.router_logit_grad(dg, gates, idx, E)
+    rdw, rdx = O.router_backward(dL, x, w)
+    assert_close("dWr", tnp(dw), rdw, 1e-5)
+    assert_close("dx_router", tnp(dxr), rdx, TOL[dtype])
+    for e in np.nonzero(counts == 0)[0]:
+        assert np.all(tnp(dw)[e] == 0)

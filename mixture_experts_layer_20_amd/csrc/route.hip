@@ -166,15 +166,26 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int
 // ------------------------------------------------------------------------------------------
 // Router backward (gates = softmax over the chosen logits).
 
-// dl[t*k+j] = g_j (dg_j - sum_i g_i dg_i): the logit gradient of the chosen experts.
+// dl[t*k+j] = g_j (dg_j - sum_i g_i dg_i): the logit gradient of the chosen experts.  Evaluated
+// as g_j * sum_i g_i (dg_j - dg_i), equal because the gates sum to one; this form has no
+// cancellation between large terms when one gate is close to 1 and the others are tiny.
 __global__ void route_dl_kernel(const float* dgate, const float* gate, int T, int k, float* dl) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
-  float s = 0.0f;
-  for (int j = 0; j < k; ++j) s += gate[(size_t)t * k + j] * dgate[(size_t)t * k + j];
-  for (int j = 0; j < k; ++j) {
-    const size_t a = (size_t)t * k + j;
-    dl[a] = gate[a] * (dgate[a] - s);
+  float g[8], dg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    g[j] = j < k ? gate[(size_t)t * k + j] : 0.0f;
+    dg[j] = j < k ? dgate[(size_t)t * k + j] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < k) s += g[i] * (dg[j] - dg[i]);
+    dl[(size_t)t * k + j] = g[j] * s;
   }
 }
 

@@ -93,6 +93,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="tiny64e_random")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 counters), if present")
     a = ap.parse_args(argv)
@@ -115,6 +117,12 @@ def main(argv=None) -> int:
     inp = I.make_inputs(cfg)
     dev = torch.device("cuda:0")
     lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev))
+    if a.copy_probe_mb > 0:
+        src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
         lay.step()

@@ -61,7 +61,7 @@ moe_status_t check_mlp(int32_t G, int64_t M, int64_t d, int64_t f, moe_dtype_t d
   CHECK(d > 0 && f > 0, MOE_ERR_INVALID_VALUE, "d and f must be > 0");
   CHECK(d % 128 == 0 && f % 128 == 0, MOE_ERR_UNSUPPORTED,
         "d and f must be multiples of 128 (got d=%lld, f=%lld)", (long long)d, (long long)f);
-  CHECK(M <= kMaxInt / 2 && d <= 65536 && f <= 65536 && G <= 65536, MOE_ERR_UNSUPPORTED,
+  CHECK(M <= kMaxInt / 2 && d <= 65536 && f <= 65536 && G <= 1024, MOE_ERR_UNSUPPORTED,
         "sizes out of the supported range");
   CHECK(((M + 127) / 128 + G) * (2 * f / 64 + d / 64) < kMaxInt, MOE_ERR_UNSUPPORTED, "grid too large");
   return MOE_OK;
@@ -76,10 +76,12 @@ moe_status_t run_gemm(int mode, const moe::GemmArgs& a, moe_dtype_t dt, moe_stre
   return hip_check(moe::launch_grouped_gemm(mode, a, dt == MOE_BF16, S(s)), what);
 }
 
-moe::GemmArgs base_args(const int32_t* offsets, int32_t G, int64_t M, int64_t d, int64_t f, void* ws) {
+moe::GemmArgs base_args(const int32_t* offsets, int32_t G, int64_t M, int64_t d, int64_t f, void* ws,
+                        size_t ws_bytes) {
   moe::GemmArgs a{};
   a.offsets = offsets;
   a.tile_prefix = reinterpret_cast<int32_t*>(ws);
+  a.ws_bytes = ws_bytes;
   a.G = G;
   a.M = (int)M;
   a.d = (int)d;
@@ -166,10 +168,11 @@ size_t moe_grouped_mlp_fwd_workspace_size(int64_t M, int32_t G, int64_t d, int64
 }
 
 size_t moe_grouped_mlp_bwd_workspace_size(int64_t M, int32_t G, int64_t d, int64_t f) {
-  (void)d;
-  if (G <= 0 || M < 0 || f <= 0) return 0;
-  // dAB is sized for fp32 so one workspace serves both element types.
-  return moe::gemm_ws_bytes(G) + align256((size_t)M * 2 * f * 4);
+  if (G <= 0 || M < 0 || f <= 0 || d <= 0) return 0;
+  // Tile prefix and split-K partials first, dAB (sized for fp32 so one workspace serves both
+  // element types) at the end.
+  return moe::gemm_ws_bytes(G) + align256(moe::gemm_partial_bytes(G, M, (int)d, (int)f)) +
+         align256((size_t)M * 2 * f * 4);
 }
 
 #define MLP_COMMON_CHECKS(need)                                                              \
@@ -188,7 +191,7 @@ moe_status_t moe_expert_gate_up_fwd(const void* x_in, const int32_t* offsets, in
   CHECK(w1 && w3 && (M == 0 || (x_in && h)), MOE_ERR_INVALID_VALUE, "x_in/w1/w3/h is NULL");
   CHECK((a_stash == nullptr) == (b_stash == nullptr), MOE_ERR_INVALID_VALUE,
         "a_stash and b_stash must both be given or both be NULL");
-  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws, ws_bytes);
   a.a = x_in; a.b0 = w1; a.b1 = w3; a.out0 = a_stash; a.out1 = b_stash; a.out2 = h;
   return run_gemm(moe::GEMM_UP_FWD, a, dt, stream, "gate/up GEMM");
 }
@@ -198,7 +201,7 @@ moe_status_t moe_expert_down_fwd(const void* h, const int32_t* offsets, int32_t 
                                  void* ws, size_t ws_bytes, moe_stream_t stream) {
   MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
   CHECK(w2 && (M == 0 || (h && y)), MOE_ERR_INVALID_VALUE, "h/w2/y is NULL");
-  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws, ws_bytes);
   a.a = h; a.b0 = w2; a.out0 = y;
   return run_gemm(moe::GEMM_DOWN_FWD, a, dt, stream, "down GEMM");
 }
@@ -210,7 +213,7 @@ moe_status_t moe_expert_down_bwd(const void* dy, const void* a_stash, const void
   MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
   CHECK(w2 && (M == 0 || (dy && a_stash && b_stash && dab)), MOE_ERR_INVALID_VALUE,
         "dy/a/b/w2/dab is NULL");
-  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws, ws_bytes);
   a.a = dy; a.b0 = w2; a.aux0 = a_stash; a.aux1 = b_stash; a.out0 = dab;
   return run_gemm(moe::GEMM_DOWN_BWD, a, dt, stream, "down dgrad GEMM");
 }
@@ -220,7 +223,7 @@ moe_status_t moe_expert_down_wgrad(const void* dy, const void* h, const int32_t*
                                    void* dw2, void* ws, size_t ws_bytes, moe_stream_t stream) {
   MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
   CHECK(dw2 && (M == 0 || (dy && h)), MOE_ERR_INVALID_VALUE, "dy/h/dw2 is NULL");
-  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws, ws_bytes);
   a.a = dy; a.b0 = h; a.out0 = dw2;
   return run_gemm(moe::GEMM_DOWN_WGRAD, a, dt, stream, "down wgrad GEMM");
 }
@@ -231,7 +234,7 @@ moe_status_t moe_expert_gate_up_dgrad(const void* dab, const int32_t* offsets, i
                                       size_t ws_bytes, moe_stream_t stream) {
   MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
   CHECK(w1 && w3 && (M == 0 || (dab && dx_in)), MOE_ERR_INVALID_VALUE, "dab/w1/w3/dx_in is NULL");
-  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws, ws_bytes);
   a.a = dab; a.b0 = w1; a.b1 = w3; a.out0 = dx_in;
   return run_gemm(moe::GEMM_UP_DGRAD, a, dt, stream, "gate/up dgrad GEMM");
 }
@@ -242,7 +245,7 @@ moe_status_t moe_expert_gate_up_wgrad(const void* dab, const void* x_in, const i
                                       moe_stream_t stream) {
   MLP_COMMON_CHECKS(moe::gemm_ws_bytes(G));
   CHECK(dw1 && dw3 && (M == 0 || (dab && x_in)), MOE_ERR_INVALID_VALUE, "dab/x_in/dw1/dw3 is NULL");
-  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws);
+  moe::GemmArgs a = base_args(offsets, G, M, d, f, ws, ws_bytes);
   a.a = dab; a.b0 = x_in; a.out0 = dw1; a.out1 = dw3;
   return run_gemm(moe::GEMM_UP_WGRAD, a, dt, stream, "gate/up wgrad GEMM");
 }
@@ -266,8 +269,9 @@ moe_status_t moe_grouped_mlp_bwd(const void* dy, const void* x_in, const void* a
   CHECK(w1 && w3 && w2 && dw1 && dw3 && dw2, MOE_ERR_INVALID_VALUE, "weight or gradient pointer is NULL");
   CHECK(M == 0 || (dy && x_in && a && b && h && dx_in), MOE_ERR_INVALID_VALUE,
         "activation pointer is NULL");
-  void* dab = reinterpret_cast<char*>(ws) + moe::gemm_ws_bytes(G);
-  const size_t gws = moe::gemm_ws_bytes(G);
+  const size_t dab_bytes = align256((size_t)M * 2 * f * 4);
+  const size_t gws = moe_grouped_mlp_bwd_workspace_size(M, G, d, f) - dab_bytes;
+  void* dab = reinterpret_cast<char*>(ws) + gws;
   if ((st = moe_expert_down_bwd(dy, a, b, offsets, G, M, d, f, w2, dt, dab, ws, gws, stream)) != MOE_OK)
     return st;
   if ((st = moe_expert_down_wgrad(dy, h, offsets, G, M, d, f, dt, dw2, ws, gws, stream)) != MOE_OK)

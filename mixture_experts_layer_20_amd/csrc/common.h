@@ -83,11 +83,14 @@ struct GemmArgs {
   void* out1;
   void* out2;
   const int32_t* offsets;     // [G+1] row offsets of the groups
-  int32_t* tile_prefix;       // [G+1] workspace: M-tiles before each group (ragged-M modes)
+  int32_t* tile_prefix;       // workspace start: [G+1] M-tiles before each group, then split-K partials
+  size_t ws_bytes;            // bytes of that workspace
   int G, M, d, f;
 };
 
 size_t gemm_ws_bytes(int G);
+// Workspace bytes for the fp32 partial sums of the split weight-gradient reductions.
+size_t gemm_partial_bytes(int G, long long M, int d, int f);
 hipError_t launch_grouped_gemm(int mode, const GemmArgs& args, bool bf16, hipStream_t s);
 
 }  // namespace moe

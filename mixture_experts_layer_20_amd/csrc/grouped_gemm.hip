@@ -14,6 +14,10 @@
 // fp32 path: a plain LDS-tiled FMA kernel with the same tile schedule and epilogues.
 #include "common.h"
 
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+
 namespace moe {
 namespace {
 
@@ -213,10 +217,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, int g, int m, int n,
 // --------------------------------------------------------------------------------------------
 // bf16 MFMA kernel
 
-constexpr int BM = 128, BN = 128, BK = 64, NTHREADS = 256;
+constexpr int BK = 64, NTHREADS = 256, MAXG = 1024;
 
-// LDS element offset of (row, 16-byte chunk) in a [rows][64] bf16 tile, chunk XOR-swizzled by row.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// LDS element offset of (row, 16-byte chunk) in a [rows][64] bf16 tile (128-byte rows).  The
+// chunk is XOR-swizzled with (row & 7) ^ ((row >> 3) & 1): 16 consecutive rows read at the same
+// logical chunk (one MFMA operand load of 16 lanes) then hit 16 distinct 16-byte bank groups of
+// gfx950's 64-bank LDS, and any 8 consecutive rows hit 8 distinct chunks.
+__host__ __device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__host__ __device__ __forceinline__ int lds_off(int row, int chunk) { return row * BK + ((chunk ^ lds_swz(row)) << 3); }
 
 __device__ __forceinline__ uint2 pack_lo(uint32_t a, uint32_t b, uint32_t c, uint32_t e) {
   return make_uint2((a & 0xffffu) | (b << 16), (c & 0xffffu) | (e << 16));
@@ -227,7 +235,7 @@ __device__ __forceinline__ uint2 pack_hi(uint32_t a, uint32_t b, uint32_t c, uin
 
 // Write 4 k-rows x 8 columns (r[0..3], each 8 consecutive columns) into a K-contiguous LDS tile
 // as 8 rows x 4 k: tile row = col0 + i, k offset = kq*4.
-__device__ __forceinline__ void store_transposed(bf16_t* tile, const uint4 (&r)[4], int col0, int kq) {
+__device__ __forceinline__ void store_transposed(bf16_t* tile, const uint4* r, int col0, int kq) {
   const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
   const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
   const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
@@ -238,7 +246,7 @@ __device__ __forceinline__ void store_transposed(bf16_t* tile, const uint4 (&r)[
     for (int h = 0; h < 2; ++h) {
       const int row = col0 + 2 * w + h;
       const uint2 v = h == 0 ? pack_lo(w0[w], w1[w], w2[w], w3[w]) : pack_hi(w0[w], w1[w], w2[w], w3[w]);
-      const int off = row * BK + ((((kq >> 1) ^ (row & 7))) << 3) + ((kq & 1) << 2);
+      const int off = lds_off(row, kq >> 1) + ((kq & 1) << 2);
       *reinterpret_cast<uint2*>(tile + off) = v;
     }
   }
@@ -254,158 +262,302 @@ __device__ __forceinline__ uint4 gload16(const void* ptr) {
 #endif
 }
 
-// Global -> registers for the K step starting at k0.
-template <int MODE>
+// Tile configuration: BM x BN output tile, 64-deep K steps, a WGM x WGN grid of waves, each wave
+// owning a (BM/WGM) x (BN/WGN) block built from 32x32x16 MFMAs.
+template <int BM_, int BN_, int WGM_, int WGN_> struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int NTH = 64 * WGM * WGN;           // threads
+  static constexpr int MI = BM / (32 * WGM);           // 32-row MFMA blocks per wave
+  static constexpr int NI = BN / (32 * WGN);           // 32-column MFMA blocks per wave
+  static constexpr int KC_ROWS = NTH / 8;              // rows per pass of a K-contiguous load
+  static constexpr int MC_COLS = NTH / 2;              // columns per pass of a K-strided load
+  static constexpr int LDS = 2 * (BM + BN) * BK * 2;   // double-buffered stages, bytes
+  // 16-byte staging registers per thread for an R-row operand: K-contiguous loads spread the
+  // R*64 elements over all threads; K-strided loads give each thread 4 k-rows x 8 columns per
+  // pass of MC_COLS columns (a tile narrower than one pass leaves the remaining threads idle).
+  static constexpr int nregs(bool kcontig, int R) {
+    return kcontig ? R * BK / 8 / NTH : 4 * (R >= MC_COLS ? R / MC_COLS : 1);
+  }
+  static_assert(BM * BK / 8 % NTH == 0 && BN * BK / 8 % NTH == 0, "tile too small for the thread count");
+};
+
+// Global -> registers for one K step starting at k0.  K-contiguous operands: 8 threads per
+// 128-byte row segment.  K-strided operands: each thread reads 4 consecutive k-rows x 8 columns.
+template <int MODE, class C>
 __device__ __forceinline__ void load_tiles(const GemmArgs& p, int g, int m0, int m_end, int nt, int k0,
-                                           int k_end, int tid, uint4 (&ra)[4], uint4 (&rb)[4]) {
+                                           int k_end, int tid,
+                                           uint4 (&ra)[C::nregs(Traits<MODE>::a_kcontig, C::BM)],
+                                           uint4 (&rb)[C::nregs(Traits<MODE>::b_kcontig, C::BN)]) {
   typedef Traits<MODE> TR;
+  constexpr int NA = C::nregs(TR::a_kcontig, C::BM), NB = C::nregs(TR::b_kcontig, C::BN);
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   if constexpr (TR::a_kcontig) {
     const int c = tid & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + i * 32 + (tid >> 3);
+    for (int i = 0; i < NA; ++i) {
+      const int m = m0 + i * C::KC_ROWS + (tid >> 3);
       ra[i] = m < m_end ? gload16(a_ptr_kc<MODE, bf16_t>(p, m, k0 + c * 8)) : zero4;
     }
   } else {
     const int q = tid & 15, c = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + q * 4 + i;
-      ra[i] = k < k_end ? gload16(a_ptr_mc<MODE, bf16_t>(p, k, m0 + c * 8)) : zero4;
-    }
+    for (int ps = 0; ps < NA / 4; ++ps)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = k0 + q * 4 + i;
+        const int col = ps * C::MC_COLS + c * 8;
+        ra[ps * 4 + i] = (k < k_end && col < C::BM) ? gload16(a_ptr_mc<MODE, bf16_t>(p, k, m0 + col)) : zero4;
+      }
   }
   if constexpr (TR::b_kcontig) {
     const int c = tid & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = i * 32 + (tid >> 3);
-      rb[i] = gload16(b_ptr_kc<MODE, bf16_t, BN>(p, g, nt, r, k0 + c * 8));
+    for (int i = 0; i < NB; ++i) {
+      const int r = i * C::KC_ROWS + (tid >> 3);
+      rb[i] = gload16(b_ptr_kc<MODE, bf16_t, C::BN>(p, g, nt, r, k0 + c * 8));
     }
   } else {
     const int q = tid & 15, c = tid >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + q * 4 + i;
-      rb[i] = k < k_end ? gload16(b_ptr_mc<MODE, bf16_t>(p, g, k, nt * BN + c * 8)) : zero4;
-    }
+    for (int ps = 0; ps < NB / 4; ++ps)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = k0 + q * 4 + i;
+        const int col = ps * C::MC_COLS + c * 8;
+        rb[ps * 4 + i] = (k < k_end && col < C::BN) ? gload16(b_ptr_mc<MODE, bf16_t>(p, g, k, nt * C::BN + col)) : zero4;
+      }
   }
 }
 
-// Registers -> one LDS buffer (A tile, B tile).
-template <int MODE>
-__device__ __forceinline__ void store_tiles(bf16_t* As, bf16_t* Bs, int tid, const uint4 (&ra)[4],
-                                            const uint4 (&rb)[4]) {
+// Registers -> one LDS stage (A tile [BM][64], then B tile [BN][64]).
+template <int MODE, class C>
+__device__ __forceinline__ void store_tiles(bf16_t* As, bf16_t* Bs, int tid,
+                                            const uint4 (&ra)[C::nregs(Traits<MODE>::a_kcontig, C::BM)],
+                                            const uint4 (&rb)[C::nregs(Traits<MODE>::b_kcontig, C::BN)]) {
   typedef Traits<MODE> TR;
+  constexpr int NA = C::nregs(TR::a_kcontig, C::BM), NB = C::nregs(TR::b_kcontig, C::BN);
   if constexpr (TR::a_kcontig) {
     const int c = tid & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(As + lds_off(i * 32 + (tid >> 3), c)) = ra[i];
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(As + lds_off(i * C::KC_ROWS + (tid >> 3), c)) = ra[i];
   } else {
-    store_transposed(As, ra, (tid >> 4) * 8, tid & 15);
+#pragma unroll
+    for (int ps = 0; ps < NA / 4; ++ps) {
+      const int col = ps * C::MC_COLS + (tid >> 4) * 8;
+      if (col < C::BM) store_transposed(As, &ra[ps * 4], col, tid & 15);
+    }
   }
   if constexpr (TR::b_kcontig) {
     const int c = tid & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(Bs + lds_off(i * 32 + (tid >> 3), c)) = rb[i];
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<uint4*>(Bs + lds_off(i * C::KC_ROWS + (tid >> 3), c)) = rb[i];
   } else {
-    store_transposed(Bs, rb, (tid >> 4) * 8, tid & 15);
+#pragma unroll
+    for (int ps = 0; ps < NB / 4; ++ps) {
+      const int col = ps * C::MC_COLS + (tid >> 4) * 8;
+      if (col < C::BN) store_transposed(Bs, &rb[ps * 4], col, tid & 15);
+    }
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16(GemmArgs p, int NT, int MT) {
+// Tile row of the wave's ni-th 32-column block.  The gate/up GEMM's B tile holds BN/2 W1 rows
+// then the same BN/2 W3 rows; blocks ni and ni + NI/2 cover the same output columns, so a lane
+// holds the gate and the up value of one output element.
+template <int MODE, class C>
+__device__ __forceinline__ int wave_nrow(int wn, int ni) {
+  if constexpr (MODE == GEMM_UP_FWD) {
+    constexpr int H = C::BN / (2 * C::WGN);   // W1 columns per wave
+    return (ni < C::NI / 2) ? wn * H + 32 * ni : C::BN / 2 + wn * H + 32 * (ni - C::NI / 2);
+  } else {
+    return wn * (C::BN / C::WGN) + 32 * ni;
+  }
+}
+
+// Per-group tile prefix in LDS (ragged-M modes): pref[g] = M-tiles of the groups before g.
+template <int BMv, int NTH>
+__device__ void block_tile_prefix(const GemmArgs& p, int* pref, int* scratch) {
+  const int tid = threadIdx.x;
+  if (tid == 0) scratch[NTH] = 0;
+  __syncthreads();
+  for (int base = 0; base < p.G; base += NTH) {
+    const int g = base + tid;
+    int c = 0;
+    if (g < p.G) {
+      int lo, hi;
+      group_rows(p.offsets, g, p.M, lo, hi);
+      c = (hi - lo + BMv - 1) / BMv;
+    }
+    scratch[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < NTH; off <<= 1) {
+      const int v = tid >= off ? scratch[tid - off] : 0;
+      __syncthreads();
+      scratch[tid] += v;
+      __syncthreads();
+    }
+    const int carry = scratch[NTH];
+    if (g < p.G) pref[g] = carry + scratch[tid] - c;
+    __syncthreads();
+    if (tid == NTH - 1) scratch[NTH] = carry + scratch[NTH - 1];
+    __syncthreads();
+  }
+  if (tid == 0) pref[p.G] = scratch[NTH];
+  __syncthreads();
+}
+
+// Persistent grouped GEMM.  Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on
+// XCD b % 8); each XCD gets one contiguous run of logical tiles so that neighbouring tiles (same
+// expert rows, next columns; then the next rows of the same expert) share operands in that XCD's
+// L2.  Weight-gradient modes may split the reduction over the expert's rows into `ksplit` parts
+// written as fp32 partials (summed in order afterwards).
+template <int MODE, class C>
+__global__ __launch_bounds__(C::NTH, 1) void grouped_gemm_bf16(GemmArgs p, int NT, int MT, int ksplit,
+                                                               float* partial) {
   typedef Traits<MODE> TR;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][2][BM * BK];
+  constexpr int BMv = C::BM, BNv = C::BN, MI = C::MI, NI = C::NI;
+  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+  __shared__ int pref[MAXG + 1];
+  __shared__ int scan_scratch[C::NTH + 1];
 
   const int tid = threadIdx.x;
-  int g, m0, m_end, nt, k_begin, k_end;
-  if constexpr (!TR::raggedK) {
-    if (!decode_ragged_m<BM>(p, NT, true, g, m0, m_end, nt)) return;
-    k_begin = 0;
-    k_end = mode_K(MODE, p.d, p.f);
-  } else {
-    const int L = blockIdx.x;
-    nt = L % NT;
-    const int r = L / NT;
-    const int mt = r % MT;
-    g = r / MT;
-    m0 = mt * BM;
-    m_end = m0 + BM;
-    group_rows(p.offsets, g, p.M, k_begin, k_end);
-  }
-  const int nk = (k_end - k_begin + BK - 1) / BK;
-
-  uint4 ra[4], rb[4];
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
-  // Tile rows of the wave's two 32-column blocks.  The gate/up GEMM pairs W1 column block
-  // (rows [0, 64) of the B tile) with the same W3 block (rows [64, 128)), so one lane holds
-  // A and B of the same output element.
-  const int nb0 = MODE == GEMM_UP_FWD ? wn * 32 : wn * 64;
-  const int nb1 = MODE == GEMM_UP_FWD ? 64 + wn * 32 : wn * 64 + 32;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
 
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  if (nk > 0) {
-    load_tiles<MODE>(p, g, m0, m_end, nt, k_begin, k_end, tid, ra, rb);
-    store_tiles<MODE>(lds[0][0], lds[0][1], tid, ra, rb);
-    __syncthreads();
+  int total;
+  if constexpr (!TR::raggedK) {
+    block_tile_prefix<BMv, C::NTH>(p, pref, scan_scratch);
+    total = pref[p.G] * NT;
+  } else {
+    total = p.G * ksplit * MT * NT;
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tiles<MODE>(p, g, m0, m_end, nt, k_begin + (kt + 1) * BK, k_end, tid, ra, rb);
-    const bf16_t* As = lds[buf][0];
-    const bf16_t* Bs = lds[buf][1];
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int chunk = s * 2 + (lane >> 5);
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int row = wm * 64 + mi * 32 + (lane & 31);
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(row, chunk));
+  const int per = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int nbx = gridDim.x >> 3;
+  const int L_end = min(total, (xcd + 1) * per);
+
+  for (int L = xcd * per + (blockIdx.x >> 3); L < L_end; L += nbx) {
+    int g, m0, m_end, nt, k_begin, k_end, split = 0;
+    if constexpr (!TR::raggedK) {
+      const int mt = L / NT;
+      nt = L - mt * NT;
+      int lo = 0, hi = p.G;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pref[mid] <= mt) lo = mid; else hi = mid;
       }
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int row = (ni == 0 ? nb0 : nb1) + (lane & 31);
-        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(row, chunk));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      g = lo;
+      int r0, r1;
+      group_rows(p.offsets, g, p.M, r0, r1);
+      m0 = r0 + (mt - pref[g]) * BMv;
+      m_end = r1;
+      k_begin = 0;
+      k_end = mode_K(MODE, p.d, p.f);
+    } else {
+      nt = L % NT;
+      int r = L / NT;
+      const int mt = r % MT;
+      r /= MT;
+      split = r % ksplit;
+      g = r / ksplit;
+      m0 = mt * BMv;
+      m_end = m0 + BMv;
+      int r0, r1;
+      group_rows(p.offsets, g, p.M, r0, r1);
+      // Split s covers a contiguous, BK-aligned share of the expert's rows.
+      const int chunk = ((r1 - r0 + ksplit - 1) / ksplit + BK - 1) / BK * BK;
+      k_begin = min(r1, r0 + split * chunk);
+      k_end = min(r1, k_begin + chunk);
     }
-    if (kt + 1 < nk) store_tiles<MODE>(lds[buf ^ 1][0], lds[buf ^ 1][1], tid, ra, rb);
-    __syncthreads();
-  }
+    const int nk = (k_end - k_begin + BK - 1) / BK;
 
-  // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31) and, for element v,
-  // row 8*(v/4) + 4*(lane/32) + v%4.
+    uint4 ra[C::nregs(TR::a_kcontig, BMv)], rb[C::nregs(TR::b_kcontig, BNv)];
+    f32x16_t acc[MI][NI];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (m >= m_end) continue;
-      if constexpr (MODE == GEMM_UP_FWD) {
-        const int n = nt * (BN / 2) + wn * 32 + (lane & 31);
-        epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][0][v], acc[mi][1][v]);
-      } else {
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const int n = nt * BN + (ni == 0 ? nb0 : nb1) + (lane & 31);
-          epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][ni][v], 0.0f);
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    if (nk > 0) {
+      load_tiles<MODE, C>(p, g, m0, m_end, nt, k_begin, k_end, tid, ra, rb);
+      store_tiles<MODE, C>(lds, lds + BMv * BK, tid, ra, rb);
+      __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) load_tiles<MODE, C>(p, g, m0, m_end, nt, k_begin + (kt + 1) * BK, k_end, tid, ra, rb);
+      const bf16_t* As = lds + buf * (BMv + BNv) * BK;
+      const bf16_t* Bs = As + BMv * BK;
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        const int chunk = s * 2 + (lane >> 5);
+        bf16x8_t af[MI], bfr[NI];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          af[mi] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(wm * (BMv / C::WGM) + mi * 32 + (lane & 31), chunk));
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          bfr[ni] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(wave_nrow<MODE, C>(wn, ni) + (lane & 31), chunk));
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+      }
+      if (kt + 1 < nk) {
+        bf16_t* Ns = lds + (buf ^ 1) * (BMv + BNv) * BK;
+        store_tiles<MODE, C>(Ns, Ns + BMv * BK, tid, ra, rb);
+      }
+      __syncthreads();
+    }
+
+    // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31) and, for element v,
+    // row 8*(v/4) + 4*(lane/32) + v%4.
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * (BMv / C::WGM) + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m >= m_end) continue;
+        if constexpr (MODE == GEMM_UP_FWD) {
+#pragma unroll
+          for (int ni = 0; ni < NI / 2; ++ni) {
+            const int n = nt * (BNv / 2) + wave_nrow<MODE, C>(wn, ni) + (lane & 31);
+            epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][ni][v], acc[mi][ni + NI / 2][v]);
+          }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const int n = nt * BNv + wave_nrow<MODE, C>(wn, ni) + (lane & 31);
+            if constexpr (TR::raggedK) {
+              if (ksplit > 1) {
+                const int Mw = mode_Mw(MODE, p.d, p.f), Nw = mode_N(MODE, p.d, p.f);
+                partial[(((size_t)split * p.G + g) * Mw + m) * Nw + n] = acc[mi][ni][v];
+                continue;
+              }
+            }
+            epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][ni][v], 0.0f);
+          }
         }
       }
     }
+  }
+}
+
+// Sum of the split-K partials in split order, written through the weight-gradient epilogue.
+template <int MODE>
+__global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p, const float* partial, int ksplit) {
+  const int Mw = mode_Mw(MODE, p.d, p.f), Nw = mode_N(MODE, p.d, p.f);
+  const size_t per_split = (size_t)p.G * Mw * Nw;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < per_split; i += (size_t)gridDim.x * 256) {
+    float s = 0.0f;
+    for (int k = 0; k < ksplit; ++k) s += partial[(size_t)k * per_split + i];
+    const int n = (int)(i % Nw);
+    const size_t r = i / Nw;
+    const int m = (int)(r % Mw);
+    const int g = (int)(r / Mw);
+    epilogue<MODE, bf16_t>(p, g, m, n, s, 0.0f);
   }
 }
 
@@ -506,26 +658,118 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs p, int NT, int 
   }
 }
 
-template <int MODE>
-hipError_t launch_mode(const GemmArgs& p, bool bf16, hipStream_t s) {
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Split of the weight-gradient reduction: only when there are too few output tiles to fill the
+// chip, and only as far as the workspace holds the fp32 partials.
+int choose_ksplit(int tiles, int G, int M, int Mw, int Nw, size_t partial_bytes) {
+  const int cus = num_cus();
+  if (tiles >= 2 * cus) return 1;
+  int ks = (2 * cus + tiles - 1) / tiles;
+  const int rows_per_group = G > 0 ? M / G : 0;
+  ks = std::min(ks, std::max(1, rows_per_group / 512));
+  ks = std::min(ks, 8);
+  while (ks > 1 && (size_t)ks * G * Mw * Nw * sizeof(float) > partial_bytes) --ks;
+  return std::max(ks, 1);
+}
+
+template <int MODE, class C>
+hipError_t launch_bf16(const GemmArgs& p, size_t partial_bytes, float* partial, hipStream_t s) {
   typedef Traits<MODE> TR;
-  const int bm = bf16 ? BM : FBM, bn = bf16 ? BN : FBN;
-  const int NT = mode_N(MODE, p.d, p.f) / bn;
+  auto kern = grouped_gemm_bf16<MODE, C>;
+  static int blocks_per_cu = 0;
+  if (blocks_per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, C::NTH, C::LDS);
+    if (e != hipSuccess) return e;
+    blocks_per_cu = nb > 0 ? nb : 1;
+  }
+  const int NT = mode_N(MODE, p.d, p.f) / C::BN;
+  int MT = 0, ksplit = 1;
+  long long tiles;
+  if constexpr (!TR::raggedK) {
+    if (p.M == 0) return hipSuccess;
+    if (p.G > MAXG) return hipErrorInvalidValue;
+    tiles = ((long long)ceil_div(p.M, C::BM) + p.G) * NT;
+  } else {
+    MT = mode_Mw(MODE, p.d, p.f) / C::BM;
+    tiles = (long long)p.G * MT * NT;
+    ksplit = choose_ksplit((int)tiles, p.G, p.M, mode_Mw(MODE, p.d, p.f), NT * C::BN, partial_bytes);
+    tiles *= ksplit;
+  }
+  long long grid = std::min<long long>(tiles, (long long)num_cus() * blocks_per_cu);
+  grid = (grid + 7) / 8 * 8;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NTH), C::LDS, s, p, NT, MT, ksplit, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (TR::raggedK) {
+    if (ksplit > 1) {
+      const size_t n = (size_t)p.G * mode_Mw(MODE, p.d, p.f) * mode_N(MODE, p.d, p.f);
+      const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+      hipLaunchKernelGGL(splitk_reduce<MODE>, dim3(blocks), dim3(256), 0, s, p, partial, ksplit);
+      e = hipGetLastError();
+    }
+  }
+  return e;
+}
+
+typedef Cfg<128, 128, 2, 2> T128x128;   // 4 waves of 64x64
+typedef Cfg<128, 256, 2, 4> T128x256;   // 8 waves of 64x64
+typedef Cfg<256, 128, 4, 2> T256x128;   // 8 waves of 64x64
+typedef Cfg<256, 256, 2, 4> T256x256;   // 8 waves of 128x64
+
+template <int MODE>
+hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float* partial, hipStream_t s) {
+  typedef Traits<MODE> TR;
+  if (bf16) {
+    // Tile shape (LIBMOE_TILE=<BM>x<BN> overrides it for tuning sweeps; a shape that does not
+    // divide the problem falls back to the default).
+    const int N = mode_N(MODE, p.d, p.f);
+    const int Mw = TR::raggedK ? mode_Mw(MODE, p.d, p.f) : 256;
+    // Default: 256x256 (8 waves of 128x64) where it divides; groups averaging under 384 rows
+    // use 128x128 (4 waves, two workgroups per CU) to bound the ragged-tail waste.
+    int bm = 128, bn = 128;
+    if (N % 256 == 0 && Mw % 256 == 0 && (TR::raggedK || (p.G > 0 && p.M / p.G >= 384))) bm = bn = 256;
+    static const char* ov = getenv("LIBMOE_TILE");
+    if (ov) {
+      int obm = 0, obn = 0;
+      if (sscanf(ov, "%dx%d", &obm, &obn) == 2 && (obm == 128 || obm == 256) && (obn == 128 || obn == 256) &&
+          N % obn == 0 && Mw % obm == 0) {
+        bm = obm;
+        bn = obn;
+      }
+    }
+    if (bm == 256 && bn == 256) return launch_bf16<MODE, T256x256>(p, partial_bytes, partial, s);
+    if (bm == 256) return launch_bf16<MODE, T256x128>(p, partial_bytes, partial, s);
+    if (bn == 256) return launch_bf16<MODE, T128x256>(p, partial_bytes, partial, s);
+    return launch_bf16<MODE, T128x128>(p, partial_bytes, partial, s);
+  }
+  const int NT = mode_N(MODE, p.d, p.f) / FBN;
   int grid, MT = 0;
   if constexpr (!TR::raggedK) {
     if (p.M == 0) return hipSuccess;
-    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(256), 0, s, p.offsets, p.G, p.M, bm,
-                       p.tile_prefix);
-    long long tiles = ((long long)ceil_div(p.M, bm) + p.G) * NT;
-    tiles = (tiles + 7) / 8 * 8;
-    grid = (int)tiles;
+    hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(256), 0, s, p.offsets, p.G, p.M, FBM, p.tile_prefix);
+    grid = (int)(((long long)ceil_div(p.M, FBM) + p.G) * NT);
   } else {
-    MT = mode_Mw(MODE, p.d, p.f) / bm;
+    MT = mode_Mw(MODE, p.d, p.f) / FBM;
     grid = p.G * MT * NT;
   }
   if (grid <= 0) return hipSuccess;
-  if (bf16) hipLaunchKernelGGL(grouped_gemm_bf16<MODE>, dim3(grid), dim3(NTHREADS), 0, s, p, NT, MT);
-  else hipLaunchKernelGGL(grouped_gemm_f32<MODE>, dim3(grid), dim3(256), 0, s, p, NT, MT);
+  hipLaunchKernelGGL(grouped_gemm_f32<MODE>, dim3(grid), dim3(256), 0, s, p, NT, MT);
   return hipGetLastError();
 }
 
@@ -533,14 +777,31 @@ hipError_t launch_mode(const GemmArgs& p, bool bf16, hipStream_t s) {
 
 size_t gemm_ws_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) / 256 * 256; }
 
+size_t gemm_partial_bytes(int G, long long M, int d, int f) {
+  size_t best = 0;
+  for (int mode : {GEMM_DOWN_WGRAD, GEMM_UP_WGRAD}) {
+    const int Mw = mode_Mw(mode, d, f), N = mode_N(mode, d, f);
+    // smallest tile count over the shapes the launcher may pick (128x128 is the fallback)
+    const int tiles = G * (Mw / 256 > 0 ? Mw / 256 : 1) * (N / 256 > 0 ? N / 256 : 1);
+    const int ks = choose_ksplit(tiles, G, (int)M, Mw, N, (size_t)-1);
+    if (ks > 1) best = std::max(best, (size_t)ks * G * Mw * N * sizeof(float));
+  }
+  return best;
+}
+
 hipError_t launch_grouped_gemm(int mode, const GemmArgs& p, bool bf16, hipStream_t s) {
+  // Split-K partials live in the workspace after the tile prefix.
+  float* partial = p.ws_bytes > gemm_ws_bytes(p.G)
+                       ? reinterpret_cast<float*>(reinterpret_cast<char*>(p.tile_prefix) + gemm_ws_bytes(p.G))
+                       : nullptr;
+  const size_t pb = partial ? p.ws_bytes - gemm_ws_bytes(p.G) : 0;
   switch (mode) {
-    case GEMM_UP_FWD: return launch_mode<GEMM_UP_FWD>(p, bf16, s);
-    case GEMM_DOWN_FWD: return launch_mode<GEMM_DOWN_FWD>(p, bf16, s);
-    case GEMM_DOWN_BWD: return launch_mode<GEMM_DOWN_BWD>(p, bf16, s);
-    case GEMM_UP_DGRAD: return launch_mode<GEMM_UP_DGRAD>(p, bf16, s);
-    case GEMM_DOWN_WGRAD: return launch_mode<GEMM_DOWN_WGRAD>(p, bf16, s);
-    case GEMM_UP_WGRAD: return launch_mode<GEMM_UP_WGRAD>(p, bf16, s);
+    case GEMM_UP_FWD: return launch_mode<GEMM_UP_FWD>(p, bf16, pb, partial, s);
+    case GEMM_DOWN_FWD: return launch_mode<GEMM_DOWN_FWD>(p, bf16, pb, partial, s);
+    case GEMM_DOWN_BWD: return launch_mode<GEMM_DOWN_BWD>(p, bf16, pb, partial, s);
+    case GEMM_UP_DGRAD: return launch_mode<GEMM_UP_DGRAD>(p, bf16, pb, partial, s);
+    case GEMM_DOWN_WGRAD: return launch_mode<GEMM_DOWN_WGRAD>(p, bf16, pb, partial, s);
+    case GEMM_UP_WGRAD: return launch_mode<GEMM_UP_WGRAD>(p, bf16, pb, partial, s);
     default: return hipErrorInvalidValue;
   }
 }

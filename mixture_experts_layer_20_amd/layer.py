@@ -70,6 +70,9 @@ class Buffers:
             b["hs"] = e(T, fs)
             b["s"] = e(T, d)
         if cfg.backward:
+            # Backward GEMM workspace: tile prefix plus room for split weight-gradient partials.
+            b["ws_bwd"] = u8(max(L.moe_grouped_mlp_bwd_workspace_size(Tk, E, d, f),
+                                 L.moe_grouped_mlp_bwd_workspace_size(T, 1, d, max(fs, 128))))
             b["dy"] = e(Tk, d)
             b["dgate"] = f32(T, k)
             b["dab"] = e(Tk, 2 * f)
@@ -162,7 +165,7 @@ class MoELayer:
                         b["src_row"], p["x"], p["w_router"], T, d, E, k, self.renorm, dt, b["dwr"],
                         b["dx_router"], b["ws_route"], b["ws_route"].numel())
             dx_router = b["dx_router"]
-        ws, wsn = b["ws_fwd"], b["ws_fwd"].numel()
+        ws, wsn = b["ws_bwd"], b["ws_bwd"].numel()
         self._stage("down_bwd", L.moe_expert_down_bwd, b["dy"], b["a"], b["b"], b["offsets"], E, Tk, d, f,
                     p["w2"], dt, b["dab"], ws, wsn)
         self._stage("down_wgrad", L.moe_expert_down_wgrad, b["dy"], b["h"], b["offsets"], E, Tk, d, f, dt,

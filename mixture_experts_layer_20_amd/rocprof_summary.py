@@ -1,0 +1,142 @@
+"""Summarise rocprofv3 output of bench.py runs into the text kept under profiles/.
+
+Inputs (all written by rocprofv3 with --output-format csv):
+  <trace dir>/run_kernel_stats.csv, run_kernel_trace.csv   from  --kernel-trace --stats
+  <pmc dir>/run_counter_collection.csv                      from  --pmc FETCH_SIZE  (one pass)
+  <pmc dir>/run_counter_collection.csv                      from  --pmc WRITE_SIZE  (one pass)
+The bench run must include `--copy-probe-mb N`: one plain device copy of N MiB whose counter
+readings calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) to bytes.
+
+Each grouped-GEMM kernel runs twice per layer step (routed experts, then the shared expert, in the
+same stage order), so the i-th dispatch of a kernel within a step is labelled by that order.
+
+Usage:
+  python -m mixture_experts_layer_20_amd.rocprof_summary --trace T --fetch F --write W \
+      --workload tiny64e_random --copy-mb 256 --command "<the rocprofv3 commands>" \
+      --out profiles/<name>.md [--traffic-json profiles/traffic.json]
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+
+MODES = ["gate_up_fwd", "down_fwd", "down_bwd", "gate_up_dgrad", "down_wgrad", "gate_up_wgrad"]
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    h.update(open(os.path.join(PKG, "csrc", "grouped_gemm.hip"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"grouped_gemm_bf16<(\d), [^>]*Cfg<(\d+), (\d+), (\d), (\d)>", name)
+    if m:
+        return f"grouped_gemm_bf16[{MODES[int(m.group(1))]}, {m.group(2)}x{m.group(3)}, {int(m.group(4)) * int(m.group(5))} waves]"
+    n = re.sub(r"void |moe::|\(anonymous namespace\)::", "", name)
+    n = re.sub(r"\(.*", "", n)
+    return n.strip()
+
+
+def gemm_mode(name: str) -> str | None:
+    m = re.search(r"grouped_gemm_bf16<(\d),", name)
+    return MODES[int(m.group(1))] if m else None
+
+
+def labelled_dispatches(rows, name_key, id_key):
+    """Label GEMM dispatches 'routed'/'shared' by their order within a step."""
+    seen = collections.Counter()
+    out = []
+    for r in sorted(rows, key=lambda r: int(r[id_key])):
+        n = r[name_key]
+        mode = gemm_mode(n)
+        label = None
+        if mode:
+            label = ("routed", "shared")[seen[n] % 2]
+            seen[n] += 1
+        out.append((r, mode, label))
+    return out
+
+
+def copy_scale(pmc_csv: str, counter: str, copy_mb: int) -> float | None:
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(pmc_csv))
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) > 4096]
+    if not vals:
+        return None
+    return copy_mb * 1024.0 / (sum(vals) / len(vals))
+
+
+def per_stage_counter(pmc_csv: str, counter: str):
+    rows = [r for r in csv.DictReader(open(pmc_csv)) if r["Counter_Name"] == counter]
+    acc = collections.defaultdict(list)
+    for r, mode, label in labelled_dispatches(rows, "Kernel_Name", "Dispatch_Id"):
+        if mode:
+            acc[(mode, label)].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--copy-mb", type=int, required=True)
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--traffic-json")
+    a = ap.parse_args(argv)
+
+    stats = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_trace.csv"))))
+    # per-stage durations from the trace
+    durs = collections.defaultdict(list)
+    for r, mode, label in labelled_dispatches(trace, "Kernel_Name", "Dispatch_Id"):
+        if mode:
+            durs[(mode, label)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    fcsv = os.path.join(a.fetch, "run_counter_collection.csv")
+    wcsv = os.path.join(a.write, "run_counter_collection.csv")
+    fs = copy_scale(fcsv, "FETCH_SIZE", a.copy_mb)
+    ws = copy_scale(wcsv, "WRITE_SIZE", a.copy_mb)
+    fetch = per_stage_counter(fcsv, "FETCH_SIZE")
+    write = per_stage_counter(wcsv, "WRITE_SIZE")
+
+    lines = [f"# rocprofv3 summary: grouped GEMM and other kernels, workload {a.workload}", "",
+             "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", "",
+             f"grouped_gemm.hip sha256[:16] = {kernel_source_sha()}", "",
+             "## Kernel statistics (--kernel-trace --stats)", "",
+             "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    lines += ["", "## Grouped GEMM stages: duration and HBM traffic per launch", "",
+              f"Counter calibration with a plain {a.copy_mb} MiB device copy: FETCH_SIZE x{fs:.3f}, "
+              f"WRITE_SIZE x{ws:.3f} (KiB per dispatch -> bytes = KiB x 1024 x factor).", "",
+              "| stage | expert set | avg us (trace) | HBM read MB | HBM write MB |",
+              "|---|---|---:|---:|---:|"]
+    traffic = {}
+    for key in sorted(durs, key=lambda k: (MODES.index(k[0]), k[1])):
+        d = sum(durs[key]) / len(durs[key])
+        rd = fetch.get(key, float("nan")) * 1024 * (fs or 1)
+        wr = write.get(key, float("nan")) * 1024 * (ws or 1)
+        lines.append(f"| {key[0]} | {key[1]} | {d:.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
+        stage = key[0] if key[1] == "routed" else "shared_" + key[0]
+        traffic[stage] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                          "avg_us_trace": d, "kernel_source_sha": kernel_source_sha()}
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    if a.traffic_json:
+        allt = json.load(open(a.traffic_json)) if os.path.exists(a.traffic_json) else {}
+        allt[a.workload] = traffic
+        json.dump(allt, open(a.traffic_json, "w"), indent=1, sort_keys=True)
+    print("\n".join(lines))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

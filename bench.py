@@ -196,11 +196,8 @@ def main(argv=None) -> int:
 
 
 def _kernel_source_sha() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    p = os.path.join(ROOT, "mixture_experts_layer_20_amd", "csrc", "grouped_gemm.hip")
-    h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
+    from mixture_experts_layer_20_amd.rocprof_summary import kernel_source_sha
+    return kernel_source_sha()
 
 
 if __name__ == "__main__":

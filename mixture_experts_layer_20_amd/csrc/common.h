@@ -92,5 +92,10 @@ size_t gemm_ws_bytes(int G);
 // Workspace bytes for the fp32 partial sums of the split weight-gradient reductions.
 size_t gemm_partial_bytes(int G, long long M, int d, int f);
 hipError_t launch_grouped_gemm(int mode, const GemmArgs& args, bool bf16, hipStream_t s);
+// Pipelined bf16 kernel (256x256 tiles, direct-to-LDS ring): whether it covers this problem, and
+// its launcher (ksplit/partial: split weight-gradient reduction, as in launch_grouped_gemm).
+bool pipe_supports(int mode, const GemmArgs& args);
+hipError_t launch_grouped_gemm_pipe(int mode, const GemmArgs& args, int ksplit, float* partial, hipStream_t s,
+                                    int num_cus);
 
 }  // namespace moe

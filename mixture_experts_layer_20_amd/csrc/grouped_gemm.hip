@@ -13,6 +13,7 @@
 // activations in wgrad) are transposed in registers on their way into LDS.
 // fp32 path: a plain LDS-tiled FMA kernel with the same tile schedule and epilogues.
 #include "common.h"
+#include "gemm_common.h"
 
 #include <algorithm>
 #include <cstdio>
@@ -21,49 +22,7 @@
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-template <int MODE> struct Traits {
-  static constexpr bool raggedK = (MODE == GEMM_DOWN_WGRAD || MODE == GEMM_UP_WGRAD);
-  static constexpr bool a_kcontig = !raggedK;
-  static constexpr bool b_kcontig = (MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD);
-};
-
-// Reduction length of the ragged-M modes.
-__host__ __device__ inline int mode_K(int mode, int d, int f) {
-  switch (mode) {
-    case GEMM_UP_FWD: return d;
-    case GEMM_DOWN_FWD: return f;
-    case GEMM_DOWN_BWD: return d;
-    case GEMM_UP_DGRAD: return 2 * f;
-    default: return 0;
-  }
-}
-// Output columns (in tile space: the gate/up GEMM packs W1 and W3 columns side by side).
-__host__ __device__ inline int mode_N(int mode, int d, int f) {
-  switch (mode) {
-    case GEMM_UP_FWD: return 2 * f;
-    case GEMM_DOWN_FWD: return d;
-    case GEMM_DOWN_BWD: return f;
-    case GEMM_UP_DGRAD: return d;
-    case GEMM_DOWN_WGRAD: return f;
-    case GEMM_UP_WGRAD: return d;
-    default: return 0;
-  }
-}
-// Output rows of the weight-gradient modes.
-__host__ __device__ inline int mode_Mw(int mode, int d, int f) {
-  return mode == GEMM_DOWN_WGRAD ? d : 2 * f;
-}
-
-__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-
-// Group row range, clamped into [0, M] (the same clamping the tile-prefix kernel uses).
-__device__ __forceinline__ void group_rows(const int32_t* offsets, int g, int M, int& lo, int& hi) {
-  lo = clampi(offsets[g], 0, M);
-  hi = clampi(offsets[g + 1], lo, M);
-}
+using namespace gemm;
 
 // M-tiles per group, exclusive prefix over groups, one block.
 __global__ void tile_prefix_kernel(const int32_t* offsets, int G, int M, int bm, int32_t* prefix) {
@@ -129,89 +88,6 @@ __device__ __forceinline__ bool decode_ragged_m(const GemmArgs& p, int NT, bool 
   m0 = r0 + (mt - p.tile_prefix[g]) * BMv;
   m_end = r1;
   return true;
-}
-
-// --------------------------------------------------------------------------------------------
-// Operand addressing.  "A" rows are output rows (tokens, or weight-gradient rows), "B" rows are
-// output columns.  K-contiguous operands are addressed by (row, k); K-strided ones by (k, col)
-// with the 8 consecutive columns read together.
-
-// Pointer to A(row m, k) for the ragged-M modes: A is [M, K] row-major.
-template <int MODE, typename T>
-__device__ __forceinline__ const T* a_ptr_kc(const GemmArgs& p, int m, int k) {
-  const int K = mode_K(MODE, p.d, p.f);
-  return reinterpret_cast<const T*>(p.a) + (size_t)m * K + k;
-}
-
-// Pointer to B(row r of the tile, k) for the K-contiguous weight operands.
-template <int MODE, typename T, int BNv>
-__device__ __forceinline__ const T* b_ptr_kc(const GemmArgs& p, int g, int nt, int r, int k) {
-  if constexpr (MODE == GEMM_UP_FWD) {
-    constexpr int H = BNv / 2;
-    const int n = nt * H + (r < H ? r : r - H);
-    const T* w = reinterpret_cast<const T*>(r < H ? p.b0 : p.b1);
-    return w + ((size_t)g * p.f + n) * p.d + k;
-  } else {  // GEMM_DOWN_FWD: W2[g] is [d, f]
-    const int n = nt * BNv + r;
-    return reinterpret_cast<const T*>(p.b0) + ((size_t)g * p.d + n) * p.f + k;
-  }
-}
-
-// Pointer to B(k, column n) for the K-strided operands (column n contiguous).
-template <int MODE, typename T>
-__device__ __forceinline__ const T* b_ptr_mc(const GemmArgs& p, int g, int k, int n) {
-  if constexpr (MODE == GEMM_DOWN_BWD) {  // W2[g] viewed as [d(k), f(n)]
-    return reinterpret_cast<const T*>(p.b0) + ((size_t)g * p.d + k) * p.f + n;
-  } else if constexpr (MODE == GEMM_UP_DGRAD) {  // [W1[g]; W3[g]] viewed as [2f(k), d(n)]
-    const T* w = reinterpret_cast<const T*>(k < p.f ? p.b0 : p.b1);
-    const int kk = k < p.f ? k : k - p.f;
-    return w + ((size_t)g * p.f + kk) * p.d + n;
-  } else if constexpr (MODE == GEMM_DOWN_WGRAD) {  // h rows
-    return reinterpret_cast<const T*>(p.b0) + (size_t)k * p.f + n;
-  } else {  // GEMM_UP_WGRAD: x rows
-    return reinterpret_cast<const T*>(p.b0) + (size_t)k * p.d + n;
-  }
-}
-
-// Pointer to A(k, row m) for the weight-gradient modes (row m contiguous).
-template <int MODE, typename T>
-__device__ __forceinline__ const T* a_ptr_mc(const GemmArgs& p, int k, int m) {
-  if constexpr (MODE == GEMM_DOWN_WGRAD) {  // dy rows [M, d]
-    return reinterpret_cast<const T*>(p.a) + (size_t)k * p.d + m;
-  } else {  // dAB rows [M, 2f]
-    return reinterpret_cast<const T*>(p.a) + (size_t)k * (2 * p.f) + m;
-  }
-}
-
-// --------------------------------------------------------------------------------------------
-// Epilogue: one output element (v1 is the up-projection value of the gate/up GEMM).
-template <int MODE, typename T>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, int g, int m, int n, float v0, float v1) {
-  if constexpr (MODE == GEMM_UP_FWD) {
-    const size_t i = (size_t)m * p.f + n;
-    const float h = v0 * sigmoid_f32(v0) * v1;
-    if (p.out0) reinterpret_cast<T*>(p.out0)[i] = from_f32<T>(v0);
-    if (p.out1) reinterpret_cast<T*>(p.out1)[i] = from_f32<T>(v1);
-    reinterpret_cast<T*>(p.out2)[i] = from_f32<T>(h);
-  } else if constexpr (MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD) {
-    reinterpret_cast<T*>(p.out0)[(size_t)m * p.d + n] = from_f32<T>(v0);
-  } else if constexpr (MODE == GEMM_DOWN_BWD) {
-    const size_t i = (size_t)m * p.f + n;
-    const float a = to_f32<T>(reinterpret_cast<const T*>(p.aux0)[i]);
-    const float b = to_f32<T>(reinterpret_cast<const T*>(p.aux1)[i]);
-    const float s = sigmoid_f32(a);
-    const float da = v0 * b * s * (1.0f + a * (1.0f - s));
-    const float db = v0 * a * s;
-    T* dab = reinterpret_cast<T*>(p.out0) + (size_t)m * (2 * p.f);
-    dab[n] = from_f32<T>(da);
-    dab[p.f + n] = from_f32<T>(db);
-  } else if constexpr (MODE == GEMM_DOWN_WGRAD) {
-    reinterpret_cast<T*>(p.out0)[((size_t)g * p.d + m) * p.f + n] = from_f32<T>(v0);
-  } else {  // GEMM_UP_WGRAD: rows [0, f) -> dW1, [f, 2f) -> dW3
-    T* out = reinterpret_cast<T*>(m < p.f ? p.out0 : p.out1);
-    const int mm = m < p.f ? m : m - p.f;
-    out[((size_t)g * p.f + mm) * p.d + n] = from_f32<T>(v0);
-  }
 }
 
 // --------------------------------------------------------------------------------------------
@@ -545,6 +421,233 @@ __global__ __launch_bounds__(C::NTH, 1) void grouped_gemm_bf16(GemmArgs p, int N
   }
 }
 
+// --------------------------------------------------------------------------------------------
+// Pipelined kernel for the modes whose two operands are K-contiguous (gate/up and down forward).
+//
+// 256x256 output tiles, 8 waves of 128x64, K consumed 32 at a time through a ring of four LDS
+// stages that the global loads fill directly (global_load_lds_dwordx4: lane l's 16 bytes land at
+// M0 + 16*l), so three stages of loads are in flight while one is multiplied and no registers are
+// spent on staging.  Each stage is its own LDS object and the loop is unrolled over the ring, so
+// the compiler's wait tracking sees which stage an LDS read touches; waits are explicit
+// s_waitcnt with a barrier (no fence: a fence would drain every load in flight).
+
+namespace dmak {
+constexpr int BM = 256, BN = 256, BKS = 32, S = 4, NTH = 512;
+constexpr int ROWB = BKS * 2;              // bytes per LDS row (32 bf16)
+constexpr int STAGE = (BM + BN) * ROWB;    // 32 KiB per stage
+typedef Cfg<256, 256, 2, 4> Geo;           // wave geometry: 2 x 4 waves, MI = 4, NI = 2
+}  // namespace dmak
+
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+// 16-byte chunk swizzle for 64-byte LDS rows: 16 consecutive rows read at one logical chunk hit 16
+// distinct 16-byte bank groups of the 64-bank LDS.
+__host__ __device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
+
+// s_waitcnt with lgkmcnt = 0, expcnt untouched, vmcnt = N (N < 16).
+#define MOE_WAIT_VM_LGKM0(N) __builtin_amdgcn_s_waitcnt(0x0070 | (N))
+
+// Issue one stage: A and B tiles, 1024 16-byte slots each, two instructions per wave per operand.
+// Slot q of a tile is (row q/4, physical chunk q%4); the lane fetches the logical chunk that the
+// swizzle places there.  A rows past the expert's end re-read its last row (never stored).
+template <int MODE>
+__device__ __forceinline__ void dma_issue(const GemmArgs& p, char* st, int g, int m0, int m_end, int nt,
+                                          int k0, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = (wave * 2 + j) * 64 + lane;
+    const int row = q >> 2, logical = (q & 3) ^ swz64(row);
+    const int m = min(m0 + row, m_end - 1);
+    __builtin_amdgcn_global_load_lds((gvoid_t*)a_ptr_kc<MODE, bf16_t>(p, m, k0 + logical * 8),
+                                     (lvoid_t*)(st + (wave * 2 + j) * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = (wave * 2 + j) * 64 + lane;
+    const int row = q >> 2, logical = (q & 3) ^ swz64(row);
+    __builtin_amdgcn_global_load_lds((gvoid_t*)b_ptr_kc<MODE, bf16_t, dmak::BN>(p, g, nt, row, k0 + logical * 8),
+                                     (lvoid_t*)(st + dmak::BM * dmak::ROWB + (wave * 2 + j) * 1024), 16, 0, 0);
+  }
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)ptr);
+}
+
+// 16-byte LDS read issued as inline assembly.  The compiler's own wait insertion would otherwise
+// drain every direct-to-LDS load in flight before the read (it cannot tell which stage a read
+// touches), so these reads are invisible to it and are fenced by lds_wait below instead.
+__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) {
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
+// Wait for all LDS reads of this wave; the fragments are in-out operands so that no use of them
+// can be scheduled before the wait.
+__device__ __forceinline__ void lds_wait(bf16x8_t (&af)[4], bf16x8_t (&bf)[2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]));
+}
+
+// Per-lane LDS byte offsets (within a stage) of the fragments of the two 16-deep substeps.
+struct DmaFragOffsets {
+  uint32_t a[2][4];   // [substep][mi]
+  uint32_t b[2][2];   // [substep][ni]
+};
+
+template <int MODE>
+__device__ __forceinline__ DmaFragOffsets dma_frag_offsets(int wm, int wn, int lane) {
+  using namespace dmak;
+  DmaFragOffsets o;
+#pragma unroll
+  for (int s = 0; s < BKS / 16; ++s) {
+    const int chunk = s * 2 + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < Geo::MI; ++mi) {
+      const int row = wm * (BM / Geo::WGM) + mi * 32 + (lane & 31);
+      o.a[s][mi] = row * ROWB + ((chunk ^ swz64(row)) << 4);
+    }
+#pragma unroll
+    for (int ni = 0; ni < Geo::NI; ++ni) {
+      const int row = wave_nrow<MODE, Geo>(wn, ni) + (lane & 31);
+      o.b[s][ni] = BM * ROWB + row * ROWB + ((chunk ^ swz64(row)) << 4);
+    }
+  }
+  return o;
+}
+
+// One stage of MFMAs: two 16-deep substeps, 4 A and 2 B fragments each; the reads of the second
+// substep are issued before the first substep's MFMAs.
+__device__ __forceinline__ void dma_compute(uint32_t base, const DmaFragOffsets& o,
+                                            f32x16_t (&acc)[dmak::Geo::MI][dmak::Geo::NI]) {
+  using namespace dmak;
+  bf16x8_t af[2][4], bfr[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) af[0][mi] = lds_read16(base + o.a[0][mi]);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) bfr[0][ni] = lds_read16(base + o.b[0][ni]);
+  lds_wait(af[0], bfr[0]);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) af[1][mi] = lds_read16(base + o.a[1][mi]);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) bfr[1][ni] = lds_read16(base + o.b[1][ni]);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][mi], bfr[0][ni], acc[mi][ni], 0, 0, 0);
+  lds_wait(af[1], bfr[1]);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][mi], bfr[1][ni], acc[mi][ni], 0, 0, 0);
+}
+
+// Wait until stage k has landed (this wave's loads; the barrier makes every wave's visible and
+// certifies that all waves finished the stage that is about to be refilled).
+__device__ __forceinline__ void dma_wait_stage(int k, int nk) {
+  const int later = nk - 1 - k;     // stages issued after k that may stay in flight (4 loads each)
+  if (later >= 2) MOE_WAIT_VM_LGKM0(8);
+  else if (later == 1) MOE_WAIT_VM_LGKM0(4);
+  else MOE_WAIT_VM_LGKM0(0);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(dmak::NTH, 1) void grouped_gemm_bf16_dma(GemmArgs p, int NT) {
+  using namespace dmak;
+  typedef Geo C;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[STAGE];
+  __shared__ __attribute__((aligned(16))) char st3[STAGE];
+  __shared__ int pref[MAXG + 1];
+  __shared__ int scan_scratch[NTH + 1];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
+
+  block_tile_prefix<BM, NTH>(p, pref, scan_scratch);
+  const int total = pref[p.G] * NT;
+  const int per = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int nbx = gridDim.x >> 3;
+  const int L_end = min(total, (xcd + 1) * per);
+  const int nk = mode_K(MODE, p.d, p.f) / BKS;
+  const DmaFragOffsets fo = dma_frag_offsets<MODE>(wm, wn, lane);
+  const uint32_t sb0 = lds_addr(st0), sb1 = lds_addr(st1), sb2 = lds_addr(st2), sb3 = lds_addr(st3);
+
+  for (int L = xcd * per + (blockIdx.x >> 3); L < L_end; L += nbx) {
+    const int mt = L / NT;
+    const int nt = L - mt * NT;
+    int lo = 0, hi = p.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pref[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    int r0, r1;
+    group_rows(p.offsets, g, p.M, r0, r1);
+    const int m0 = r0 + (mt - pref[g]) * BM;
+    const int m_end = r1;
+
+    f32x16_t acc[C::MI][C::NI];
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    MOE_WAIT_VM_LGKM0(0);   // the previous tile's stores count in vmcnt too
+    dma_issue<MODE>(p, st0, g, m0, m_end, nt, 0, wave, lane);
+    if (nk > 1) dma_issue<MODE>(p, st1, g, m0, m_end, nt, BKS, wave, lane);
+    if (nk > 2) dma_issue<MODE>(p, st2, g, m0, m_end, nt, 2 * BKS, wave, lane);
+    for (int kt = 0; kt < nk; kt += S) {
+#define MOE_DMA_STEP(I, CUR, NXT)                                                     \
+      if (kt + I < nk) {                                                                \
+        dma_wait_stage(kt + I, nk);                                                     \
+        if (kt + I + 3 < nk) dma_issue<MODE>(p, NXT, g, m0, m_end, nt, (kt + I + 3) * BKS, wave, lane); \
+        dma_compute(CUR, fo, acc);                                                      \
+      }
+      MOE_DMA_STEP(0, sb0, st3)
+      MOE_DMA_STEP(1, sb1, st0)
+      MOE_DMA_STEP(2, sb2, st1)
+      MOE_DMA_STEP(3, sb3, st2)
+#undef MOE_DMA_STEP
+    }
+    MOE_WAIT_VM_LGKM0(0);
+    asm volatile("s_barrier" ::: "memory");   // every wave is done with the ring before it refills
+
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * (BM / C::WGM) + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m >= m_end) continue;
+        if constexpr (MODE == GEMM_UP_FWD) {
+#pragma unroll
+          for (int ni = 0; ni < C::NI / 2; ++ni) {
+            const int n = nt * (BN / 2) + wave_nrow<MODE, C>(wn, ni) + (lane & 31);
+            epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][ni][v], acc[mi][ni + C::NI / 2][v]);
+          }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < C::NI; ++ni) {
+            const int n = nt * BN + wave_nrow<MODE, C>(wn, ni) + (lane & 31);
+            epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][ni][v], 0.0f);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Sum of the split-K partials in split order, written through the weight-gradient epilogue.
 template <int MODE>
 __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p, const float* partial, int ksplit) {
@@ -727,6 +830,26 @@ hipError_t launch_bf16(const GemmArgs& p, size_t partial_bytes, float* partial, 
   return e;
 }
 
+template <int MODE>
+hipError_t launch_bf16_dma(const GemmArgs& p, hipStream_t s) {
+  auto kern = grouped_gemm_bf16_dma<MODE>;
+  static int blocks_per_cu = 0;
+  if (blocks_per_cu == 0) {
+    int nb = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, dmak::NTH, 0);
+    if (e != hipSuccess) return e;
+    blocks_per_cu = nb > 0 ? nb : 1;
+  }
+  if (p.M == 0) return hipSuccess;
+  if (p.G > MAXG) return hipErrorInvalidValue;
+  const int NT = mode_N(MODE, p.d, p.f) / dmak::BN;
+  const long long tiles = ((long long)ceil_div(p.M, dmak::BM) + p.G) * NT;
+  long long grid = std::min<long long>(tiles, (long long)num_cus() * blocks_per_cu);
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(dmak::NTH), 0, s, p, NT);
+  return hipGetLastError();
+}
+
 typedef Cfg<128, 128, 2, 2> T128x128;   // 4 waves of 64x64
 typedef Cfg<128, 256, 2, 4> T128x256;   // 8 waves of 64x64
 typedef Cfg<256, 128, 4, 2> T256x128;   // 8 waves of 64x64
@@ -736,6 +859,23 @@ template <int MODE>
 hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float* partial, hipStream_t s) {
   typedef Traits<MODE> TR;
   if (bf16) {
+    // The pipelined 256x256 kernel wherever it applies: weight gradients, and ragged-M stages
+    // whose groups average at least 384 rows (LIBMOE_PIPE=0 disables it).
+    static const char* pipe_env = getenv("LIBMOE_PIPE");
+    const bool pipe_on = !(pipe_env && pipe_env[0] == '0');
+    if (pipe_on && pipe_supports(MODE, p) && (TR::raggedK || (p.G > 0 && p.M / p.G >= 384))) {
+      int ksplit = 1;
+      if constexpr (TR::raggedK) {
+        const int Mw = mode_Mw(MODE, p.d, p.f), N = mode_N(MODE, p.d, p.f);
+        ksplit = choose_ksplit(p.G * (Mw / 256) * (N / 256), p.G, p.M, Mw, N, partial_bytes);
+      }
+      hipError_t e = launch_grouped_gemm_pipe(MODE, p, ksplit, partial, s, num_cus());
+      if (e != hipSuccess || ksplit <= 1) return e;
+      const size_t n = (size_t)p.G * mode_Mw(MODE, p.d, p.f) * mode_N(MODE, p.d, p.f);
+      hipLaunchKernelGGL(splitk_reduce<MODE>, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                         s, p, partial, ksplit);
+      return hipGetLastError();
+    }
     // Tile shape (LIBMOE_TILE=<BM>x<BN> overrides it for tuning sweeps; a shape that does not
     // divide the problem falls back to the default).
     const int N = mode_N(MODE, p.d, p.f);
@@ -752,6 +892,12 @@ hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float
         bm = obm;
         bn = obn;
       }
+    }
+    if constexpr (MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD) {
+      // Both operands K-contiguous: the direct-to-LDS pipelined kernel (LIBMOE_DMA=0 disables it).
+      static const char* dma = getenv("LIBMOE_DMA");
+      if (bm == 256 && bn == 256 && mode_K(MODE, p.d, p.f) % dmak::BKS == 0 && !(dma && dma[0] == '0'))
+        return launch_bf16_dma<MODE>(p, s);
     }
     if (bm == 256 && bn == 256) return launch_bf16<MODE, T256x256>(p, partial_bytes, partial, s);
     if (bm == 256) return launch_bf16<MODE, T256x128>(p, partial_bytes, partial, s);

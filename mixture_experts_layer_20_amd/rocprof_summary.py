@@ -29,9 +29,14 @@ MODES = ["gate_up_fwd", "down_fwd", "down_bwd", "gate_up_dgrad", "down_wgrad", "
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+GEMM_SOURCES = ("common.h", "gemm_common.h", "grouped_gemm.hip", "grouped_gemm_pipe.hip")
+
+
 def kernel_source_sha() -> str:
+    """Hash of the grouped-GEMM sources: counter readings are valid only for the code they came from."""
     h = hashlib.sha256()
-    h.update(open(os.path.join(PKG, "csrc", "grouped_gemm.hip"), "rb").read())
+    for name in GEMM_SOURCES:
+        h.update(open(os.path.join(PKG, "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -39,13 +44,16 @@ def short_name(name: str) -> str:
     m = re.search(r"grouped_gemm_bf16<(\d), [^>]*Cfg<(\d+), (\d+), (\d), (\d)>", name)
     if m:
         return f"grouped_gemm_bf16[{MODES[int(m.group(1))]}, {m.group(2)}x{m.group(3)}, {int(m.group(4)) * int(m.group(5))} waves]"
+    m = re.search(r"(grouped_gemm_pipe|grouped_gemm_bf16_dma|splitk_reduce)<(\d)>", name)
+    if m:
+        return f"{m.group(1)}[{MODES[int(m.group(2))]}]"
     n = re.sub(r"void |moe::|\(anonymous namespace\)::", "", name)
     n = re.sub(r"\(.*", "", n)
     return n.strip()
 
 
 def gemm_mode(name: str) -> str | None:
-    m = re.search(r"grouped_gemm_bf16<(\d),", name)
+    m = re.search(r"grouped_gemm_(?:bf16|bf16_dma|pipe|f32)<(\d)[,>]", name)
     return MODES[int(m.group(1))] if m else None
 
 
@@ -109,7 +117,7 @@ def main(argv=None) -> int:
 
     lines = [f"# rocprofv3 summary: grouped GEMM and other kernels, workload {a.workload}", "",
              "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", "",
-             f"grouped_gemm.hip sha256[:16] = {kernel_source_sha()}", "",
+             f"grouped-GEMM sources ({', '.join(GEMM_SOURCES)}) sha256[:16] = {kernel_source_sha()}", "",
              "## Kernel statistics (--kernel-trace --stats)", "",
              "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
     for r in stats:

@@ -133,6 +133,9 @@ MLP_SHAPES = [
     (2048, 16, 256, 128, (1, 2, 15)),
     (1, 1, 128, 128, ()),
     (300, 1, 512, 256, ()),
+    # groups large enough for the pipelined 256x256 kernel on every stage
+    (4000, 6, 512, 256, (2,)),
+    (3000, 1, 256, 512, ()),
 ]
 
 

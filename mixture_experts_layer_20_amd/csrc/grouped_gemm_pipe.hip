@@ -5,21 +5,26 @@
 // "Technical Deep Dive"); each expert's rows form one ragged group of the grouped GEMM.
 //
 // Design (one workgroup = 256x256 output tile, 4 waves in a 2x2 grid, 128x128 per wave):
-//  * K is consumed 32 at a time through a ring of four 32 KiB LDS stages that global loads fill
-//    directly (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l).  Three stages are
-//    in flight while one is multiplied; no registers are spent on staging.
+//  * K is consumed 32 at a time ("K step") through a ring of four 32 KiB LDS stages that global
+//    loads fill directly (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l).  The
+//    loads form one continuous stream over all tiles of the workgroup: the stage four steps
+//    ahead is issued as soon as a slot frees up, also across tile boundaries, so the next tile's
+//    first stages are in flight during the current tile's epilogue.
 //  * An operand that is K-contiguous in memory is kept [row][32 k] in LDS (64-byte rows, 16-byte
 //    chunks XOR-swizzled) and read with ds_read_b128.  An operand that is K-strided (weights in
 //    dgrad, activations in wgrad) is kept [32 k][256 rows] (512-byte rows, 64-byte windows
 //    XOR-swizzled by k) and read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k
 //    of one column: two such reads form a 32x32x16 MFMA operand.  No transposition pass.
-//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators (256 per lane).
-//  * LDS reads are inline assembly with explicit lgkmcnt waits; the ring is governed by explicit
-//    vmcnt waits and a plain s_barrier.  (The compiler's own waits would drain every load in
-//    flight before each LDS read, and a fenced barrier drains them too.)
-//  * Epilogue: the accumulators go through LDS in fp32, are read back as rows of 8 consecutive
-//    columns, get the mode's elementwise math (SwiGLU, SwiGLU backward) and are written with
-//    16-byte stores.
+//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators (256 per lane, in AGPRs).
+//  * One wave per SIMD, so the wave's own instruction order decides how well the matrix core is
+//    fed: each K step is two phases of 16 MFMAs, and every LDS fragment read and every global
+//    load is placed between two MFMAs (scheduling barriers pin the order).  One s_barrier per K
+//    step, between the phases.  LDS reads are inline assembly with explicit lgkmcnt waits and the
+//    ring is governed by explicit vmcnt waits (the compiler's own waits would drain every load in
+//    flight before each LDS access).
+//  * Epilogue straight from the accumulators: 4x4 DPP quad transposes give each lane 4
+//    consecutive columns of one row, the mode's elementwise math (SwiGLU, SwiGLU backward) is
+//    applied and 8-byte bf16 stores go out.
 //  * Persistent grid, per-expert tile prefix computed in-kernel, tiles dealt so each XCD walks one
 //    contiguous run (workgroup b runs on XCD b % 8).
 #include "common.h"
@@ -52,6 +57,14 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* ptr) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)ptr);
 }
 
+// One 32-bit LDS load, waited for.  Written out because a compiler-generated LDS access would be
+// preceded by a wait for every direct-to-LDS load in flight.
+__device__ __forceinline__ int lds_load_i32(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
 // ---- K-contiguous operand: [256 rows][32 k], 64-byte rows; chunk swizzle (row >> 2) & 3 makes
 // 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int kc_swz(int row) { return (row >> 2) & 3; }
@@ -61,46 +74,174 @@ __device__ __forceinline__ int kc_swz(int row) { return (row >> 2) & 3; }
 // distinct bank groups.
 __device__ __forceinline__ int mc_phys_chunk(int k, int chunk) { return chunk ^ ((k & 3) << 2); }
 
-// Direct loads of one operand tile for the K step starting at k0 (4 instructions per wave).
-// KC: slot q = (row q/4, physical chunk q%4).  MC: slot q = (k q/32, physical chunk q%32).
-template <int MODE, bool A_OP>
-__device__ __forceinline__ void issue_operand(const GemmArgs& p, char* dst, int g, int m0, int m_end, int nt,
-                                              int k0, int k_end, int wave, int lane) {
-  constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = (wave * 4 + j) * 64 + lane;
-    const bf16_t* src;
-    if constexpr (kc) {
-      const int row = q >> 2;
-      const int kk = k0 + (((q & 3) ^ kc_swz(row)) << 3);
-      if constexpr (A_OP) {
-        src = a_ptr_kc<MODE, bf16_t>(p, min(m0 + row, m_end - 1), kk);
-      } else {
-        src = b_ptr_kc<MODE, bf16_t, BN>(p, g, nt, row, kk);
-      }
-    } else {
-      const int kr = q >> 5;
-      const int col = ((q & 31) ^ ((kr & 3) << 2)) << 3;   // logical column of this physical chunk
-      const int k = k0 + kr;
-      if (k < k_end) {
-        if constexpr (A_OP) src = a_ptr_mc<MODE, bf16_t>(p, k, m0 + col);
-        else src = b_ptr_mc<MODE, bf16_t>(p, g, k, nt * BN + col);
-      } else {
-        src = reinterpret_cast<const bf16_t*>(g_zero_rows);
-      }
-    }
-    __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(dst + (wave * 4 + j) * 1024), 16, 0, 0);
-  }
+// ---- Tiles -------------------------------------------------------------------------------
+// Output tile: group g, rows [m0, min(m0 + 256, m_end)), tile column nt, K range [k_begin, k_end)
+// in nk steps of 32 (split: K chunk index of a split weight gradient).
+struct Tile {
+  int g, m0, m_end, nt, k_begin, k_end, nk, split;
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Group row range from the clamped offsets kept in LDS (the clamping of group_rows).
+__device__ __forceinline__ void group_rows_lds(uint32_t offs, int g, int& lo, int& hi) {
+  lo = uniform(lds_load_i32(offs + 4 * g));
+  hi = max(lo, uniform(lds_load_i32(offs + 4 * (g + 1))));
 }
 
 template <int MODE>
-__device__ __forceinline__ void issue_stage(const GemmArgs& p, char* st, int g, int m0, int m_end, int nt, int k0,
-                                            int k_end, int wave, int lane) {
-  issue_operand<MODE, true>(p, st, g, m0, m_end, nt, k0, k_end, wave, lane);
-  issue_operand<MODE, false>(p, st + OPB, g, m0, m_end, nt, k0, k_end, wave, lane);
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, uint32_t pref, uint32_t offs, int L, int NT, int MT,
+                                            int ksplit) {
+  Tile t;
+  t.split = 0;
+  if constexpr (!Traits<MODE>::raggedK) {
+    const int mt = L / NT;
+    t.nt = L - mt * NT;
+    int lo = 0, hi = p.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (uniform(lds_load_i32(pref + 4 * mid)) <= mt) lo = mid; else hi = mid;
+    }
+    t.g = lo;
+    int r0, r1;
+    group_rows_lds(offs, t.g, r0, r1);
+    t.m0 = r0 + (mt - uniform(lds_load_i32(pref + 4 * t.g))) * BM;
+    t.m_end = r1;
+    t.k_begin = 0;
+    t.k_end = mode_K(MODE, p.d, p.f);
+  } else {
+    t.nt = L % NT;
+    int r = L / NT;
+    const int mt = r % MT;
+    r /= MT;
+    t.split = r % ksplit;
+    t.g = r / ksplit;
+    t.m0 = mt * BM;
+    t.m_end = t.m0 + BM;
+    int r0, r1;
+    group_rows_lds(offs, t.g, r0, r1);
+    const int chunk = ((r1 - r0 + ksplit - 1) / ksplit + BKS - 1) / BKS * BKS;
+    t.k_begin = min(r1, r0 + t.split * chunk);
+    t.k_end = min(r1, t.k_begin + chunk);
+  }
+  t.nk = (t.k_end - t.k_begin + BKS - 1) / BKS;
+  return t;
 }
 
+// ---- Direct loads ------------------------------------------------------------------------
+// Load IDX (0..3: operand A, 4..7: operand B) of the stage starting at k0 of tile t: 16 bytes per
+// lane into LDS slot q = (wave * 4 + j) * 64 + lane of the operand tile.
+// KC: slot q = (row q/4, physical chunk q%4).  MC: slot q = (k q/32, physical chunk q%32).
+template <int MODE, int IDX>
+__device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const Tile& t, int k0, int wave, int lane) {
+  constexpr bool A_OP = IDX < 4;
+  constexpr int j = IDX & 3;
+  constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
+  const int q = (wave * 4 + j) * 64 + lane;
+  const bf16_t* src;
+  if constexpr (kc) {
+    const int row = q >> 2;
+    const int kk = k0 + (((q & 3) ^ kc_swz(row)) << 3);
+    if constexpr (A_OP) {
+      src = a_ptr_kc<MODE, bf16_t>(p, min(t.m0 + row, t.m_end - 1), kk);
+    } else {
+      src = b_ptr_kc<MODE, bf16_t, BN>(p, t.g, t.nt, row, kk);
+    }
+  } else {
+    const int kr = q >> 5;
+    const int col = ((q & 31) ^ ((kr & 3) << 2)) << 3;   // logical column of this physical chunk
+    const int k = k0 + kr;
+    if (k < t.k_end) {
+      if constexpr (A_OP) src = a_ptr_mc<MODE, bf16_t>(p, k, t.m0 + col);
+      else src = b_ptr_mc<MODE, bf16_t>(p, t.g, k, t.nt * BN + col);
+    } else {
+      src = reinterpret_cast<const bf16_t*>(g_zero_rows);
+    }
+  }
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * 4 + j) * 1024), 16,
+                                   0, 0);
+}
+
+// Loads inside the K loop: source = wave-uniform stage base + per-lane 32-bit byte offset.  The
+// offsets depend on the tile only through the row clamp of the K-contiguous A operand; the bases
+// carry k0 and the tile position.
+template <int MODE>
+__device__ __forceinline__ uint32_t load_offset(const GemmArgs& p, const Tile& t, int idx, int wave, int lane) {
+  const bool a_op = idx < 4;
+  const int q = (wave * 4 + (idx & 3)) * 64 + lane;
+  const bool kc = a_op ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
+  if (kc) {
+    const int row = q >> 2;
+    const uint32_t c16 = (uint32_t)(((q & 3) ^ kc_swz(row)) << 4);
+    if (a_op) {
+      const int K = mode_K(MODE, p.d, p.f);
+      return (uint32_t)(min(t.m0 + row, t.m_end - 1) - t.m0) * (uint32_t)K * 2u + c16;
+    }
+    if constexpr (MODE == GEMM_UP_FWD) return (uint32_t)(row & (BN / 2 - 1)) * (uint32_t)p.d * 2u + c16;
+    return (uint32_t)row * (uint32_t)p.f * 2u + c16;   // GEMM_DOWN_FWD: W2 rows of length f
+  }
+  const int kr = q >> 5;
+  const uint32_t col = (uint32_t)(((q & 31) ^ ((kr & 3) << 2)) << 3);
+  uint32_t stride;   // elements per K row of the operand
+  if (a_op) stride = MODE == GEMM_DOWN_WGRAD ? p.d : 2 * p.f;
+  else if constexpr (MODE == GEMM_DOWN_BWD || MODE == GEMM_DOWN_WGRAD) stride = p.f;
+  else stride = p.d;
+  return ((uint32_t)kr * stride + col) * 2u;
+}
+
+// Wave-uniform byte bases of operands A and B for the stage starting at k0.
+template <int MODE>
+__device__ __forceinline__ void stage_bases(const GemmArgs& p, const Tile& t, int k0, int wave, const char*& sa,
+                                            const char*& sb) {
+  const char* a = reinterpret_cast<const char*>(p.a);
+  const char* b0 = reinterpret_cast<const char*>(p.b0);
+  const size_t d = p.d, f = p.f, g = t.g;
+  if constexpr (MODE == GEMM_UP_FWD) {
+    sa = a + ((size_t)t.m0 * d + k0) * 2;
+    sb = reinterpret_cast<const char*>(wave < 2 ? p.b0 : p.b1) + ((g * f + (size_t)t.nt * (BN / 2)) * d + k0) * 2;
+  } else if constexpr (MODE == GEMM_DOWN_FWD) {
+    sa = a + ((size_t)t.m0 * f + k0) * 2;
+    sb = b0 + ((g * d + (size_t)t.nt * BN) * f + k0) * 2;
+  } else if constexpr (MODE == GEMM_DOWN_BWD) {
+    sa = a + ((size_t)t.m0 * d + k0) * 2;
+    sb = b0 + ((g * d + k0) * f + (size_t)t.nt * BN) * 2;
+  } else if constexpr (MODE == GEMM_UP_DGRAD) {
+    sa = a + ((size_t)t.m0 * 2 * f + k0) * 2;
+    const bool up = k0 >= p.f;
+    sb = reinterpret_cast<const char*>(up ? p.b1 : p.b0) + ((g * f + (size_t)(up ? k0 - p.f : k0)) * d +
+                                                            (size_t)t.nt * BN) * 2;
+  } else if constexpr (MODE == GEMM_DOWN_WGRAD) {
+    sa = a + ((size_t)k0 * d + t.m0) * 2;
+    sb = b0 + ((size_t)k0 * f + (size_t)t.nt * BN) * 2;
+  } else {
+    sa = a + ((size_t)k0 * 2 * f + t.m0) * 2;
+    sb = b0 + ((size_t)k0 * d + (size_t)t.nt * BN) * 2;
+  }
+}
+
+template <int MODE, int IDX>
+__device__ __forceinline__ void issue_fast(char* stage, const char* sa, const char* sb, const uint32_t (&voff)[8],
+                                           int k_left, int wave, int lane) {
+  constexpr bool A_OP = IDX < 4;
+  const char* src = (A_OP ? sa : sb) + voff[IDX];
+  if constexpr (Traits<MODE>::raggedK) {
+    // K-strided operands: lane reads K row (wave * 4 + j) * 2 + lane / 32 of the stage; rows past
+    // the group's end read zeros.
+    const int kr = (wave * 4 + (IDX & 3)) * 2 + (lane >> 5);
+    if (kr >= k_left) src = reinterpret_cast<const char*>(g_zero_rows);
+  }
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * 4 + (IDX & 3)) * 1024),
+                                   16, 0, 0);
+}
+
+// The next stage to load: operand bases and the number of its K rows inside the tile's K range.
+struct StageSrc {
+  const char* sa;
+  const char* sb;
+  int k_left;
+};
+
+// ---- Fragments ---------------------------------------------------------------------------
 // Row (A) / column (B) of the wave's MFMA block i inside the 256-wide operand tile.
 template <int MODE, bool A_OP>
 __device__ __forceinline__ int block_row(int wm, int wn, int i) {
@@ -146,100 +287,119 @@ constexpr int kc_block_off(int i) {
               : (MODE == GEMM_UP_FWD ? (i < 2 ? 2048 * i : 8192 + 2048 * (i - 2)) : 2048 * i);
 }
 
-#define MOE_DS_READ_B128(OUT, ADDR, OFF) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(OUT) : "v"(ADDR), "i"(OFF))
-#define MOE_DS_READ_TR(OUT, ADDR, OFF) asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(OUT) : "v"(ADDR), "i"(OFF))
-
-// Fragments of one 16-deep substep.  For MC operands the two 64-bit halves are kept apart until
-// the wait, then packed (4 k from the first read, 4 from the second).
+// Fragments of one 16-deep substep, read one instruction at a time (IDX).  KC: 4 reads, one per
+// block.  MC: 8 reads, two per block (4 k each), kept apart until packed for the MFMA.
 template <bool KC>
 struct Frag;
 template <>
 struct Frag<true> {
+  static constexpr int NREADS = 4;
   bf16x8_t v[4];
-  template <int MODE, bool A_OP>
-  __device__ __forceinline__ void read(uint32_t addr) {
-    MOE_DS_READ_B128(v[0], addr, (kc_block_off<MODE, A_OP>(0)));
-    MOE_DS_READ_B128(v[1], addr, (kc_block_off<MODE, A_OP>(1)));
-    MOE_DS_READ_B128(v[2], addr, (kc_block_off<MODE, A_OP>(2)));
-    MOE_DS_READ_B128(v[3], addr, (kc_block_off<MODE, A_OP>(3)));
+  template <int MODE, bool A_OP, int IDX>
+  __device__ __forceinline__ void read_one(uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[IDX]) : "v"(addr), "i"(kc_block_off<MODE, A_OP>(IDX)));
   }
   __device__ __forceinline__ bf16x8_t get(int i) const { return v[i]; }
 };
 template <>
 struct Frag<false> {
+  static constexpr int NREADS = 8;
   u32x2_t h[2][4];
-  template <int MODE, bool A_OP>
-  __device__ __forceinline__ void read(uint32_t addr) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t ai = addr ^ (uint32_t)(i << 6);
-      MOE_DS_READ_TR(h[0][i], ai, 0);
-      MOE_DS_READ_TR(h[1][i], ai, 2048);
-    }
+  template <int MODE, bool A_OP, int IDX>
+  __device__ __forceinline__ void read_one(uint32_t addr) {
+    constexpr int i = IDX >> 1, r = IDX & 1;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(h[r][i]) : "v"(addr ^ (uint32_t)(i << 6)), "i"(r * 2048));
   }
   __device__ __forceinline__ bf16x8_t get(int i) const {
     const u32x4_t u = {h[0][i].x, h[0][i].y, h[1][i].x, h[1][i].y};
     return __builtin_bit_cast(bf16x8_t, u);
   }
 };
-#undef MOE_DS_READ_B128
-#undef MOE_DS_READ_TR
 
-// Wait until at most N LDS reads are outstanding (the reads issued after fa/fb); fa and fb are
-// in-out operands so no use of them can be scheduled before the wait.  lgkmcnt is 4 bits wide:
-// N is clamped to 15, which is conservative (it also waits for the oldest of the newer reads).
-#define MOE_LGKM_ASM(NSTR, ...) asm volatile("s_waitcnt lgkmcnt(" NSTR ")" : __VA_ARGS__)
-#define MOE_LGKM_SWITCH(N, ...)                       \
-  do {                                                 \
-    if constexpr ((N) == 0) MOE_LGKM_ASM("0", __VA_ARGS__);   \
-    else if constexpr ((N) == 8) MOE_LGKM_ASM("8", __VA_ARGS__); \
-    else if constexpr ((N) == 12) MOE_LGKM_ASM("12", __VA_ARGS__); \
-    else MOE_LGKM_ASM("15", __VA_ARGS__);              \
-  } while (0)
-
-template <int N>
+// Wait until every LDS read is done; the fragments are in-out operands so no use of them can be
+// scheduled before the wait.
 __device__ __forceinline__ void frag_wait(Frag<true>& a, Frag<true>& b) {
-  MOE_LGKM_SWITCH(N, "+v"(a.v[0]), "+v"(a.v[1]), "+v"(a.v[2]), "+v"(a.v[3]), "+v"(b.v[0]), "+v"(b.v[1]),
-                  "+v"(b.v[2]), "+v"(b.v[3]));
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.v[0]), "+v"(a.v[1]), "+v"(a.v[2]), "+v"(a.v[3]), "+v"(b.v[0]),
+               "+v"(b.v[1]), "+v"(b.v[2]), "+v"(b.v[3]));
 }
-template <int N>
 __device__ __forceinline__ void frag_wait(Frag<true>& a, Frag<false>& b) {
-  MOE_LGKM_SWITCH(N, "+v"(a.v[0]), "+v"(a.v[1]), "+v"(a.v[2]), "+v"(a.v[3]), "+v"(b.h[0][0]), "+v"(b.h[0][1]),
-                  "+v"(b.h[0][2]), "+v"(b.h[0][3]), "+v"(b.h[1][0]), "+v"(b.h[1][1]), "+v"(b.h[1][2]),
-                  "+v"(b.h[1][3]));
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.v[0]), "+v"(a.v[1]), "+v"(a.v[2]), "+v"(a.v[3]), "+v"(b.h[0][0]),
+               "+v"(b.h[0][1]), "+v"(b.h[0][2]), "+v"(b.h[0][3]), "+v"(b.h[1][0]), "+v"(b.h[1][1]),
+               "+v"(b.h[1][2]), "+v"(b.h[1][3]));
 }
-template <int N>
 __device__ __forceinline__ void frag_wait(Frag<false>& a, Frag<false>& b) {
-  MOE_LGKM_SWITCH(N, "+v"(a.h[0][0]), "+v"(a.h[0][1]), "+v"(a.h[0][2]), "+v"(a.h[0][3]), "+v"(a.h[1][0]),
-                  "+v"(a.h[1][1]), "+v"(a.h[1][2]), "+v"(a.h[1][3]), "+v"(b.h[0][0]), "+v"(b.h[0][1]),
-                  "+v"(b.h[0][2]), "+v"(b.h[0][3]), "+v"(b.h[1][0]), "+v"(b.h[1][1]), "+v"(b.h[1][2]),
-                  "+v"(b.h[1][3]));
-}
-#undef MOE_LGKM_SWITCH
-#undef MOE_LGKM_ASM
-
-// Number of LDS read instructions of one substep's fragments, and the wait count that lets one
-// substep's worth of newer reads stay in flight.
-template <bool KC> constexpr int nreads() { return KC ? 4 : 8; }
-template <bool KA, bool KB> constexpr int newer_reads() {
-  return nreads<KA>() + nreads<KB>() > 15 ? 15 : nreads<KA>() + nreads<KB>();
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.h[0][0]), "+v"(a.h[0][1]), "+v"(a.h[0][2]), "+v"(a.h[0][3]),
+               "+v"(a.h[1][0]), "+v"(a.h[1][1]), "+v"(a.h[1][2]), "+v"(a.h[1][3]), "+v"(b.h[0][0]),
+               "+v"(b.h[0][1]), "+v"(b.h[0][2]), "+v"(b.h[0][3]), "+v"(b.h[1][0]), "+v"(b.h[1][1]),
+               "+v"(b.h[1][2]), "+v"(b.h[1][3]));
 }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0), N a multiple of 8 below 64.
-__device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4070);   // vmcnt 16 = low bits 0, high bits 1
-  else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0070 | 8);
-  else __builtin_amdgcn_s_waitcnt(0x0070);
-}
-
+// ---- K step phases -------------------------------------------------------------------------
+// Slot Q of a phase: MFMA Q (block row Q/4, block column Q%4), then the memory instructions that
+// belong to the slot.  The scheduling barriers keep this order: the matrix core always has the
+// next MFMA queued while the wave issues a read or a load.
 template <int MODE>
-__device__ __forceinline__ void mma_substep(const Frag<Traits<MODE>::a_kcontig>& fa,
-                                            const Frag<Traits<MODE>::b_kcontig>& fb, f32x16_t (&acc)[MI][NI]) {
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const bf16x8_t a = fa.get(i);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, fb.get(j), acc[i][j], 0, 0, 0);
+using FragA = Frag<Traits<MODE>::a_kcontig>;
+template <int MODE>
+using FragB = Frag<Traits<MODE>::b_kcontig>;
+
+template <int MODE, int Q>
+__device__ __forceinline__ void mfma_slot(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a, const FragB<MODE>& b) {
+  constexpr int i = Q >> 2, j = Q & 3;
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.get(i), b.get(j), acc[i][j], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Fragment read R of a substep (A's reads first, then B's).
+template <int MODE, int R>
+__device__ __forceinline__ void read_slot(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
+  constexpr int NRA = FragA<MODE>::NREADS, NRB = FragB<MODE>::NREADS;
+  if constexpr (R < NRA) a.template read_one<MODE, true, R>(ra);
+  else if constexpr (R < NRA + NRB) b.template read_one<MODE, false, R - NRA>(rb);
+}
+
+// Phase 0 of a K step: MFMAs on substep 0 (a0, b0); reads of substep 1 (a1, b1) of the same
+// stage at ra/rb.
+template <int MODE, int Q>
+__device__ __forceinline__ void phase0(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a0, const FragB<MODE>& b0,
+                                       FragA<MODE>& a1, FragB<MODE>& b1, uint32_t ra, uint32_t rb) {
+  if constexpr (Q < 16) {
+    mfma_slot<MODE, Q>(acc, a0, b0);
+    read_slot<MODE, Q>(a1, b1, ra, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    phase0<MODE, Q + 1>(acc, a0, b0, a1, b1, ra, rb);
+  }
+}
+
+// Phase 1: MFMAs on substep 1 (a1, b1); reads of substep 0 (a0, b0) of the next stage at ra/rb;
+// the 8 loads of the stage four steps ahead into this step's slot (slots 8..15).
+template <int MODE, int Q>
+__device__ __forceinline__ void phase1(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a1, const FragB<MODE>& b1,
+                                       FragA<MODE>& a0, FragB<MODE>& b0, uint32_t ra, uint32_t rb, char* stage,
+                                       const StageSrc& ss, const uint32_t (&voff)[8], int wave, int lane) {
+  if constexpr (Q < 16) {
+    mfma_slot<MODE, Q>(acc, a1, b1);
+    read_slot<MODE, Q>(a0, b0, ra, rb);
+    if constexpr (Q >= 8) issue_fast<MODE, Q - 8>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    phase1<MODE, Q + 1>(acc, a1, b1, a0, b0, ra, rb, stage, ss, voff, wave, lane);
+  }
+}
+
+// All reads of one substep's fragments (prologue).
+template <int MODE, int R>
+__device__ __forceinline__ void read_all(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
+  if constexpr (R < FragA<MODE>::NREADS + FragB<MODE>::NREADS) {
+    read_slot<MODE, R>(a, b, ra, rb);
+    read_all<MODE, R + 1>(a, b, ra, rb);
+  }
+}
+
+template <int MODE, int IDX>
+__device__ __forceinline__ void issue_all(const GemmArgs& p, char* stage, const Tile& t, int k0, int wave, int lane) {
+  if constexpr (IDX < 8) {
+    issue_load<MODE, IDX>(p, stage, t, k0, wave, lane);
+    issue_all<MODE, IDX + 1>(p, stage, t, k0, wave, lane);
   }
 }
 
@@ -261,12 +421,14 @@ __device__ __forceinline__ u32x2_t pack4_bf16(const float (&x)[4]) {
 __device__ __forceinline__ void st8(void* base, size_t elem, const float (&x)[4]) {
   *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(base) + elem) = pack4_bf16(x);
 }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Store 4 consecutive outputs (row m, columns n..n+3) of the mode; u holds the up-projection values
-// of the gate/up GEMM.
+// of the gate/up GEMM, au/bu the stashed pre-activations of the down-projection dgrad.
 template <int MODE>
 __device__ __forceinline__ void store4(const GemmArgs& p, int g, int m, int n, const float (&v)[4], const float (&u)[4],
-                                       int split, int ksplit, float* partial) {
+                                       u32x2_t au, u32x2_t bu, int split, int ksplit, float* partial) {
   if constexpr (MODE == GEMM_UP_FWD) {
     float h[4];
 #pragma unroll
@@ -278,15 +440,12 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int g, int m, int n, c
   } else if constexpr (MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD) {
     st8(p.out0, (size_t)m * p.d + n, v);
   } else if constexpr (MODE == GEMM_DOWN_BWD) {
-    const size_t idx = (size_t)m * p.f + n;
-    const u32x2_t au = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(p.aux0) + idx);
-    const u32x2_t bu = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(p.aux1) + idx);
-    const uint32_t aw[2] = {au.x, au.y}, bw[2] = {bu.x, bu.y};
+    const float a4[4] = {bf16_lo(au.x), bf16_hi(au.x), bf16_lo(au.y), bf16_hi(au.y)};
+    const float b4[4] = {bf16_lo(bu.x), bf16_hi(bu.x), bf16_lo(bu.y), bf16_hi(bu.y)};
     float da[4], db[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float a = __uint_as_float(i & 1 ? (aw[i >> 1] & 0xffff0000u) : (aw[i >> 1] << 16));
-      const float b = __uint_as_float(i & 1 ? (bw[i >> 1] & 0xffff0000u) : (bw[i >> 1] << 16));
+      const float a = a4[i], b = b4[i];
       const float s = fast_sigmoid(a);
       da[i] = v[i] * b * s * (1.0f + a * (1.0f - s));
       db[i] = v[i] * a * s;
@@ -346,6 +505,16 @@ template <int MODE>
 __device__ __forceinline__ void epilogue_block(const GemmArgs& p, const f32x16_t& c, const f32x16_t& cu, int g,
                                                int row, int m_end, int n, int lane, int split, int ksplit,
                                                float* partial) {
+  u32x2_t au[4] = {}, bu[4] = {};
+  if constexpr (MODE == GEMM_DOWN_BWD) {
+    // All stashed pre-activations of the block first (rows clamped into the group), then the math.
+#pragma unroll
+    for (int vg = 0; vg < 4; ++vg) {
+      const size_t idx = (size_t)min(row + 8 * vg, m_end - 1) * p.f + n;
+      au[vg] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(p.aux0) + idx);
+      bu[vg] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(p.aux1) + idx);
+    }
+  }
 #pragma unroll
   for (int vg = 0; vg < 4; ++vg) {
     const int m = row + 8 * vg;
@@ -356,7 +525,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& p, const f32x16_t
       MOE_AGPR_READ4(cu, 4 * vg, u);
       quad_transpose(u, lane);
     }
-    if (m < m_end) store4<MODE>(p, g, m, n, v, u, split, ksplit, partial);
+    if (m < m_end) store4<MODE>(p, g, m, n, v, u, au[vg], bu[vg], split, ksplit, partial);
   }
 }
 
@@ -376,16 +545,38 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const f32x16_t 
 }
 
 template <int MODE>
-__device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], int g, int row0,
-                                              int m_end, int col0, int lane, int split, int ksplit, float* partial) {
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], const Tile& t,
+                                              int wm, int wn, int lane, int ksplit, float* partial) {
   // The accumulator reads are opaque to the hazard checker: leave the last MFMA's write-back
   // (at most 18 wait states) behind before the first of them.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-  epilogue_from<MODE, 0>(p, acc, g, row0, m_end, col0, lane, split, ksplit, partial);
+  const int row0 = t.m0 + wm * 128;
+  const int col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 64 : t.nt * BN + wn * 128;
+  epilogue_from<MODE, 0>(p, acc, t.g, row0, t.m_end, col0, lane, t.split, ksplit, partial);
 }
 
-// Per-group tile prefix (ragged-M modes): pref[g] = 256-row tiles of the groups before g.
-__device__ __forceinline__ void tile_prefix_lds(const GemmArgs& p, int* pref, int* scratch) {
+// Output of a tile with an empty K range (a weight gradient of an expert without tokens): zeros.
+template <int MODE>
+__device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int wm, int wn, int lane, int ksplit,
+                                          float* partial) {
+  const float z[4] = {0.f, 0.f, 0.f, 0.f};
+  const u32x2_t zw = {0u, 0u};
+  const int row0 = t.m0 + wm * 128, col0 = t.nt * BN + wn * 128;
+#pragma unroll 1
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll 1
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int m = row0 + mi * 32 + 8 * vg + 4 * (lane >> 5) + (lane & 3);
+        const int n = col0 + ni * 32 + 4 * ((lane & 31) >> 2);
+        if (m < t.m_end) store4<MODE>(p, t.g, m, n, z, z, zw, zw, t.split, ksplit, partial);
+      }
+}
+
+// Per-group tile prefix (ragged-M modes): pref[g] = 256-row tiles of the groups before g, from
+// the clamped offsets in offs.
+__device__ __forceinline__ void tile_prefix_lds(const GemmArgs& p, const int* offs, int* pref, int* scratch) {
   const int tid = threadIdx.x;
   if (tid == 0) scratch[NTH] = 0;
   __syncthreads();
@@ -393,8 +584,7 @@ __device__ __forceinline__ void tile_prefix_lds(const GemmArgs& p, int* pref, in
     const int g = base + tid;
     int c = 0;
     if (g < p.G) {
-      int lo, hi;
-      group_rows(p.offsets, g, p.M, lo, hi);
+      const int lo = offs[g], hi = max(lo, offs[g + 1]);
       c = (hi - lo + BM - 1) / BM;
     }
     scratch[tid] = c;
@@ -415,26 +605,80 @@ __device__ __forceinline__ void tile_prefix_lds(const GemmArgs& p, int* pref, in
   __syncthreads();
 }
 
+// s_waitcnt vmcnt(N) (lgkmcnt(0) too): everything but the N newest loads or stores is done.
+__device__ __forceinline__ void wait_vm16() { __builtin_amdgcn_s_waitcnt(0x4070); }
+__device__ __forceinline__ void wait_vm24() { __builtin_amdgcn_s_waitcnt(0x4078); }
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Producer of the load stream: the tile and K step of the next stage to load.  Once the stream
+// runs out it keeps reloading the last stage (valid memory, into slots nobody reads again), so
+// every K step issues exactly 8 loads per wave and the vmcnt arithmetic stays fixed.
+struct Producer {
+  Tile t;
+  int L, k;
+  uint32_t voff[8];
+};
+
+template <int MODE>
+__device__ __forceinline__ void set_offsets(Producer& pr, const GemmArgs& p, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pr.voff[i] = load_offset<MODE>(p, pr.t, i, wave, lane);
+}
+
+template <int MODE>
+__device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs& p, int wave) {
+  StageSrc ss;
+  const int k0 = pr.t.k_begin + pr.k * BKS;
+  ss.k_left = pr.t.k_end - k0;
+  stage_bases<MODE>(p, pr.t, k0, wave, ss.sa, ss.sb);
+  return ss;
+}
+
+template <int MODE>
+__device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, uint32_t pref, uint32_t offs, int nbx,
+                                        int L_end, int NT, int MT, int ksplit, int wave, int lane) {
+  if (pr.k + 1 < pr.t.nk) {
+    ++pr.k;
+    return;
+  }
+  for (int L = pr.L + nbx; L < L_end; L += nbx) {
+    const Tile t = decode_tile<MODE>(p, pref, offs, L, NT, MT, ksplit);
+    if (t.nk > 0) {
+      pr.t = t;
+      pr.L = L;
+      pr.k = 0;
+      set_offsets<MODE>(pr, p, wave, lane);
+      return;
+    }
+  }
+  pr.L = L_end;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, int MT, int ksplit, float* partial) {
   typedef Traits<MODE> TR;
-  constexpr bool AKC = TR::a_kcontig, BKC = TR::b_kcontig;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
-  __shared__ int pref[PMAXG + 1];
+  __shared__ int pref_s[PMAXG + 1];
+  __shared__ int offs_s[PMAXG + 1];
   __shared__ int scan_scratch[NTH + 1];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = uniform(tid >> 6), lane = tid & 63;
   const int wm = wave % WGM, wn = wave / WGM;
   const uint32_t lds0 = lds_addr_of(lds);
+  const uint32_t pref = lds_addr_of(pref_s), offs = lds_addr_of(offs_s);
 
   const uint32_t fa0 = lds0 + frag_base<MODE, true>(0, wm, wn, lane), fa1 = lds0 + frag_base<MODE, true>(1, wm, wn, lane);
   const uint32_t fb0 = lds0 + frag_base<MODE, false>(0, wm, wn, lane), fb1 = lds0 + frag_base<MODE, false>(1, wm, wn, lane);
 
+  // Clamped group offsets (the clamping of group_rows) and, for ragged M, the tile prefix.
+  for (int g = tid; g <= p.G; g += NTH) offs_s[g] = clampi(p.offsets[g], 0, p.M);
+  __syncthreads();
   int total;
   if constexpr (!TR::raggedK) {
-    tile_prefix_lds(p, pref, scan_scratch);
-    total = pref[p.G] * NT;
+    tile_prefix_lds(p, offs_s, pref_s, scan_scratch);
+    total = pref_s[p.G] * NT;
   } else {
     total = p.G * ksplit * MT * NT;
   }
@@ -443,113 +687,73 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
   const int nbx = gridDim.x >> 3;
   const int L_end = min(total, (xcd + 1) * per);
 
-  // Tile decode: group, row range and K range of logical tile L.
-  struct Tile {
-    int g, m0, m_end, nt, k_begin, k_end, split, nk;
-  };
-  auto decode = [&](int L) {
-    Tile t;
-    t.split = 0;
-    if constexpr (!TR::raggedK) {
-      const int mt = L / NT;
-      t.nt = L - mt * NT;
-      int lo = 0, hi = p.G;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pref[mid] <= mt) lo = mid; else hi = mid;
-      }
-      t.g = lo;
-      int r0, r1;
-      group_rows(p.offsets, t.g, p.M, r0, r1);
-      t.m0 = r0 + (mt - pref[t.g]) * BM;
-      t.m_end = r1;
-      t.k_begin = 0;
-      t.k_end = mode_K(MODE, p.d, p.f);
-    } else {
-      t.nt = L % NT;
-      int r = L / NT;
-      const int mt = r % MT;
-      r /= MT;
-      t.split = r % ksplit;
-      t.g = r / ksplit;
-      t.m0 = mt * BM;
-      t.m_end = t.m0 + BM;
-      int r0, r1;
-      group_rows(p.offsets, t.g, p.M, r0, r1);
-      const int chunk = ((r1 - r0 + ksplit - 1) / ksplit + BKS - 1) / BKS * BKS;
-      t.k_begin = min(r1, r0 + t.split * chunk);
-      t.k_end = min(r1, t.k_begin + chunk);
-    }
-    t.nk = (t.k_end - t.k_begin + BKS - 1) / BKS;
-    return t;
-  };
-  // First three K stages of a tile into ring slots 0..2.
-  auto prefetch = [&](const Tile& t) {
-    for (int s = 0; s < 3 && s < t.nk; ++s)
-      issue_stage<MODE>(p, lds + s * STAGE, t.g, t.m0, t.m_end, t.nt, t.k_begin + s * BKS, t.k_end, wave, lane);
-  };
-
-  int L = xcd * per + (blockIdx.x >> 3);
-  Tile cur;
-  if (L < L_end) {
-    cur = decode(L);
-    prefetch(cur);
+  // Consumer: the tile being multiplied (the first one with work; empty ones get zeros).
+  int Lc = xcd * per + (blockIdx.x >> 3);
+  Tile ct;
+  for (;; Lc += nbx) {
+    if (Lc >= L_end) return;
+    ct = decode_tile<MODE>(p, pref, offs, Lc, NT, MT, ksplit);
+    if (ct.nk > 0) break;
+    zero_tile<MODE>(p, ct, wm, wn, lane, ksplit, partial);
   }
-  for (; L < L_end; L += nbx) {
-    const int g = cur.g, m0 = cur.m0, m_end = cur.m_end, nt = cur.nt, k_begin = cur.k_begin, k_end = cur.k_end;
-    const int nk = cur.nk, split = cur.split;
 
+  // Prologue: stages 0..3 into slots 0..3, wait for stage 0, read substep 0 of stage 0.
+  Producer pr;
+  pr.t = ct;
+  pr.L = Lc;
+  pr.k = 0;
+  set_offsets<MODE>(pr, p, wave, lane);
+#pragma unroll 1
+  for (int s = 0; s < NSTAGE; ++s) {
+    issue_all<MODE, 0>(p, lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
+    advance<MODE>(pr, p, pref, offs, nbx, L_end, NT, MT, ksplit, wave, lane);
+  }
+  wait_vm24();
+  barrier();
+  FragA<MODE> a0, a1;
+  FragB<MODE> b0, b1;
+  read_all<MODE, 0>(a0, b0, fa0, fb0);
+  frag_wait(a0, b0);
+
+  int j = 0;
+  for (;;) {
     f32x16_t acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < NI; ++j)
+      for (int jj = 0; jj < NI; ++jj)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    if (nk > 0) {
-      // Everything older than stage 0's loads (the previous tile's stores) is also waited for;
-      // stages 1 and 2 stay in flight.
-      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): stores of the previous tile may be younger
-      asm volatile("s_barrier" ::: "memory");
-      Frag<AKC> a0, a1;
-      Frag<BKC> b0, b1;
-      a0.template read<MODE, true>(fa0);
-      b0.template read<MODE, false>(fb0);
-      for (int kt = 0; kt < nk; ++kt) {
-        const uint32_t sb = (kt & 3) * STAGE;
-        a1.template read<MODE, true>(fa1 + sb);
-        b1.template read<MODE, false>(fb1 + sb);
-        frag_wait<newer_reads<AKC, BKC>()>(a0, b0);
-        mma_substep<MODE>(a0, b0, acc);
-        if (kt + 1 < nk) {
-          wait_vm(kt + 2 < nk ? 8 : 0);
-          asm volatile("s_barrier" ::: "memory");
-          if (kt + 3 < nk)
-            issue_stage<MODE>(p, lds + ((kt + 3) & 3) * STAGE, g, m0, m_end, nt, k_begin + (kt + 3) * BKS, k_end,
-                              wave, lane);
-          const uint32_t sn = ((kt + 1) & 3) * STAGE;
-          a0.template read<MODE, true>(fa0 + sn);
-          b0.template read<MODE, false>(fb0 + sn);
-          frag_wait<newer_reads<AKC, BKC>()>(a1, b1);
-        } else {
-          frag_wait<0>(a1, b1);
-        }
-        mma_substep<MODE>(a1, b1, acc);
+        for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
+    for (int kc = 0; kc < ct.nk; ++kc, ++j) {
+      // Phase 0: substep 0 of stage j; read substep 1.
+      const uint32_t sb = (j & 3) * STAGE;
+      phase0<MODE, 0>(acc, a0, b0, a1, b1, fa1 + sb, fb1 + sb);
+      frag_wait(a1, b1);
+      // Stage j+1 has landed once only the loads of stages j+2, j+3 (and any stores issued after
+      // them) are outstanding; the barrier makes every wave's part visible and frees slot j & 3.
+      wait_vm16();
+      barrier();
+      // Phase 1: substep 1 of stage j; read substep 0 of stage j+1; load stage j+4 into slot j & 3.
+      const uint32_t sn = ((j + 1) & 3) * STAGE;
+      const StageSrc ss = stage_src<MODE>(pr, p, wave);
+      phase1<MODE, 0>(acc, a1, b1, a0, b0, fa0 + sn, fb0 + sn, lds + sb, ss, pr.voff, wave, lane);
+      advance<MODE>(pr, p, pref, offs, nbx, L_end, NT, MT, ksplit, wave, lane);
+      frag_wait(a0, b0);
+    }
+    epilogue_tile<MODE>(p, acc, ct, wm, wn, lane, ksplit, partial);
+    bool more = false;
+    for (Lc += nbx; Lc < L_end; Lc += nbx) {
+      ct = decode_tile<MODE>(p, pref, offs, Lc, NT, MT, ksplit);
+      if (ct.nk > 0) {
+        more = true;
+        break;
       }
+      zero_tile<MODE>(p, ct, wm, wn, lane, ksplit, partial);
     }
-    // The ring is free once every wave has finished its reads: start the next tile's loads now so
-    // they overlap this tile's epilogue.
-    asm volatile("s_barrier" ::: "memory");
-    if (L + nbx < L_end) {
-      cur = decode(L + nbx);
-      prefetch(cur);
-    }
-
-    const int row0 = m0 + wm * 128;
-    const int col0 = (MODE == GEMM_UP_FWD) ? nt * (BN / 2) + wn * 64 : nt * BN + wn * 128;
-    epilogue_tile<MODE>(p, acc, g, row0, m_end, col0, lane, split, ksplit, partial);
+    if (!more) break;
   }
+  // No direct-to-LDS load may still be writing when the workgroup's LDS is released.
+  wait_vm0();
 }
 
 template <int MODE>

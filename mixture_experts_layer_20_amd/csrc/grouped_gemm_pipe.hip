@@ -418,27 +418,81 @@ __device__ __forceinline__ u32x2_t pack4_bf16(const float (&x)[4]) {
   w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b16x2_t));
   return w;
 }
-__device__ __forceinline__ void st8(void* base, size_t elem, const float (&x)[4]) {
-  *reinterpret_cast<u32x2_t*>(reinterpret_cast<bf16_t*>(base) + elem) = pack4_bf16(x);
-}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Store 4 consecutive outputs (row m, columns n..n+3) of the mode; u holds the up-projection values
-// of the gate/up GEMM, au/bu the stashed pre-activations of the down-projection dgrad.
+// Output window of one wave: the tensor region that starts at the wave's first output row and
+// column, as a buffer resource whose size ends with the last row inside the group.  Stores to
+// rows past it are dropped by the hardware, so no store is branched around and every epilogue
+// issues a fixed number of memory instructions (the K loop's vmcnt arithmetic relies on it).
+struct OutWin {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t row_bytes;
+};
+__device__ __forceinline__ OutWin out_win(const void* base, size_t elem_off, int rows, int row_elems, int esize) {
+  OutWin w;
+  w.row_bytes = (uint32_t)(row_elems * esize);
+  char* b = const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * esize;
+  w.r = __builtin_amdgcn_make_buffer_rsrc(b, 0, max(rows, 0) * (int)w.row_bytes, 0x00020000);
+  return w;
+}
+__device__ __forceinline__ void st_bf16x4(const OutWin& w, int r, int c, const float (&x)[4]) {
+  __builtin_amdgcn_raw_buffer_store_b64(pack4_bf16(x), w.r, (int)(r * w.row_bytes) + c * 2, 0, 0);
+}
+__device__ __forceinline__ void st_f32x4(const OutWin& w, int r, int c, const float (&x)[4]) {
+  const u32x4_t v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(v, w.r, (int)(r * w.row_bytes) + c * 4, 0, 0);
+}
+
+// The output windows of one wave's 128x128 block of a tile.
+struct OutWins {
+  OutWin w[3];
+};
+
 template <int MODE>
-__device__ __forceinline__ void store4(const GemmArgs& p, int g, int m, int n, const float (&v)[4], const float (&u)[4],
-                                       u32x2_t au, u32x2_t bu, int split, int ksplit, float* partial) {
+__device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, int row0, int col0, int ksplit,
+                                            float* partial) {
+  OutWins o;
+  const int rows = min(128, t.m_end - row0);
+  const size_t d = p.d, f = p.f;
+  if constexpr (MODE == GEMM_UP_FWD) {
+    const size_t e = (size_t)row0 * f + col0;
+    o.w[0] = out_win(p.out0, e, rows, p.f, 2);
+    o.w[1] = out_win(p.out1, e, rows, p.f, 2);
+    o.w[2] = out_win(p.out2, e, rows, p.f, 2);
+  } else if constexpr (MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD) {
+    o.w[0] = out_win(p.out0, (size_t)row0 * d + col0, rows, p.d, 2);
+  } else if constexpr (MODE == GEMM_DOWN_BWD) {
+    o.w[0] = out_win(p.out0, (size_t)row0 * 2 * f + col0, rows, 2 * p.f, 2);
+  } else {
+    const int Mw = mode_Mw(MODE, p.d, p.f), Nw = mode_N(MODE, p.d, p.f);
+    if (ksplit > 1) {
+      o.w[0] = out_win(partial, (((size_t)t.split * p.G + t.g) * Mw + row0) * Nw + col0, 128, Nw, 4);
+    } else if constexpr (MODE == GEMM_DOWN_WGRAD) {
+      o.w[0] = out_win(p.out0, ((size_t)t.g * d + row0) * f + col0, 128, p.f, 2);
+    } else {  // rows [0, f) of the gradient go to dW1, [f, 2f) to dW3; a wave's 128 rows lie in one
+      const bool up = row0 >= p.f;
+      o.w[0] = out_win(up ? p.out1 : p.out0, ((size_t)t.g * f + (up ? row0 - p.f : row0)) * d + col0, 128, p.d, 2);
+    }
+  }
+  return o;
+}
+
+// Store 4 consecutive outputs (window row r, columns c..c+3) of the mode; u holds the
+// up-projection values of the gate/up GEMM, au/bu the stashed pre-activations of the
+// down-projection dgrad.
+template <int MODE>
+__device__ __forceinline__ void store4(const GemmArgs& p, const OutWins& o, int r, int c, const float (&v)[4],
+                                       const float (&u)[4], u32x2_t au, u32x2_t bu, int ksplit) {
   if constexpr (MODE == GEMM_UP_FWD) {
     float h[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) h[i] = v[i] * fast_sigmoid(v[i]) * u[i];
-    const size_t idx = (size_t)m * p.f + n;
-    if (p.out0) st8(p.out0, idx, v);
-    if (p.out1) st8(p.out1, idx, u);
-    st8(p.out2, idx, h);
+    if (p.out0) st_bf16x4(o.w[0], r, c, v);
+    if (p.out1) st_bf16x4(o.w[1], r, c, u);
+    st_bf16x4(o.w[2], r, c, h);
   } else if constexpr (MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD) {
-    st8(p.out0, (size_t)m * p.d + n, v);
+    st_bf16x4(o.w[0], r, c, v);
   } else if constexpr (MODE == GEMM_DOWN_BWD) {
     const float a4[4] = {bf16_lo(au.x), bf16_hi(au.x), bf16_lo(au.y), bf16_hi(au.y)};
     const float b4[4] = {bf16_lo(bu.x), bf16_hi(bu.x), bf16_lo(bu.y), bf16_hi(bu.y)};
@@ -450,22 +504,19 @@ __device__ __forceinline__ void store4(const GemmArgs& p, int g, int m, int n, c
       da[i] = v[i] * b * s * (1.0f + a * (1.0f - s));
       db[i] = v[i] * a * s;
     }
-    const size_t row = (size_t)m * (2 * p.f);
-    st8(p.out0, row + n, da);
-    st8(p.out0, row + p.f + n, db);
-  } else {  // weight gradients: m is the gradient row, n its column
-    const int Mw = mode_Mw(MODE, p.d, p.f), Nw = mode_N(MODE, p.d, p.f);
-    if (ksplit > 1) {
-      float* dst = partial + (((size_t)split * p.G + g) * Mw + m) * Nw + n;
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-    } else if constexpr (MODE == GEMM_DOWN_WGRAD) {
-      st8(p.out0, ((size_t)g * p.d + m) * p.f + n, v);
-    } else {
-      void* out = m < p.f ? p.out0 : p.out1;
-      const int mm = m < p.f ? m : m - p.f;
-      st8(out, ((size_t)g * p.f + mm) * p.d + n, v);
-    }
+    st_bf16x4(o.w[0], r, c, da);
+    st_bf16x4(o.w[0], r, p.f + c, db);
+  } else {  // weight gradients
+    if (ksplit > 1) st_f32x4(o.w[0], r, c, v);
+    else st_bf16x4(o.w[0], r, c, v);
   }
+}
+
+// Store instructions every epilogue issues at least (per wave; the optional pre-activation
+// stashes of the gate/up GEMM not counted).
+template <int MODE>
+constexpr int epilogue_stores() {
+  return MODE == GEMM_UP_FWD ? 32 : (MODE == GEMM_DOWN_BWD ? 128 : 64);
 }
 
 // 4x4 transpose inside each quad of lanes (DPP quad permutes): on entry lane j of a quad holds
@@ -498,26 +549,41 @@ __device__ __forceinline__ void quad_transpose(float (&x)[4], int lane) {
       : "=v"(X[0]), "=v"(X[1]), "=v"(X[2]), "=v"(X[3])                                            \
       : "a"(C[(E0)]), "a"(C[(E0) + 1]), "a"(C[(E0) + 2]), "a"(C[(E0) + 3]))
 
+// Stashed pre-activations (a, b) of one accumulator block for the down-projection dgrad: rows
+// row + 8*vg (clamped into the group), columns n..n+3.  Loaded with inline assembly and waited for
+// explicitly: a compiler-tracked load would be preceded and followed by waits that drain the
+// load stream of the next tile.
+struct AuxBlock {
+  u32x2_t a[4], b[4];
+};
+__device__ __forceinline__ void load_aux(const GemmArgs& p, int row, int m_end, int n, AuxBlock& x) {
+#pragma unroll
+  for (int vg = 0; vg < 4; ++vg) {
+    const size_t idx = (size_t)min(row + 8 * vg, m_end - 1) * p.f + n;
+    const bf16_t* pa = reinterpret_cast<const bf16_t*>(p.aux0) + idx;
+    const bf16_t* pb = reinterpret_cast<const bf16_t*>(p.aux1) + idx;
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(x.a[vg]) : "v"(pa) : "memory");
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(x.b[vg]) : "v"(pb) : "memory");
+  }
+}
+template <int N>
+__device__ __forceinline__ void wait_aux(AuxBlock& x) {
+  asm volatile("s_waitcnt vmcnt(%8)"
+               : "+v"(x.a[0]), "+v"(x.a[1]), "+v"(x.a[2]), "+v"(x.a[3]), "+v"(x.b[0]), "+v"(x.b[1]), "+v"(x.b[2]),
+                 "+v"(x.b[3])
+               : "n"(N)
+               : "memory");
+}
+
 // Epilogue straight from the accumulators.  In the 32x32 accumulator layout lane l holds column
 // l % 32 and, for element v, row 8*(v/4) + 4*(l/32) + v%4; after the quad transpose of elements
 // 4g..4g+3 lane l holds row 8g + 4*(l/32) + l%4 and columns 4*((l%32)/4) .. +3.
 template <int MODE>
-__device__ __forceinline__ void epilogue_block(const GemmArgs& p, const f32x16_t& c, const f32x16_t& cu, int g,
-                                               int row, int m_end, int n, int lane, int split, int ksplit,
-                                               float* partial) {
-  u32x2_t au[4] = {}, bu[4] = {};
-  if constexpr (MODE == GEMM_DOWN_BWD) {
-    // All stashed pre-activations of the block first (rows clamped into the group), then the math.
-#pragma unroll
-    for (int vg = 0; vg < 4; ++vg) {
-      const size_t idx = (size_t)min(row + 8 * vg, m_end - 1) * p.f + n;
-      au[vg] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(p.aux0) + idx);
-      bu[vg] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const bf16_t*>(p.aux1) + idx);
-    }
-  }
+__device__ __forceinline__ void epilogue_block(const GemmArgs& p, const OutWins& o, const f32x16_t& c,
+                                               const f32x16_t& cu, int r, int cc, int lane, const AuxBlock& x,
+                                               int ksplit) {
 #pragma unroll
   for (int vg = 0; vg < 4; ++vg) {
-    const int m = row + 8 * vg;
     float v[4], u[4];
     MOE_AGPR_READ4(c, 4 * vg, v);
     quad_transpose(v, lane);
@@ -525,22 +591,50 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& p, const f32x16_t
       MOE_AGPR_READ4(cu, 4 * vg, u);
       quad_transpose(u, lane);
     }
-    if (m < m_end) store4<MODE>(p, g, m, n, v, u, au[vg], bu[vg], split, ksplit, partial);
+    store4<MODE>(p, o, r + 8 * vg, cc, v, u, x.a[vg], x.b[vg], ksplit);
   }
+}
+
+// Window row and column of lane's first element of accumulator block IDX.
+template <int MODE, int IDX>
+__device__ __forceinline__ int block_r(int lane) {
+  constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
+  return (IDX / NJ) * 32 + 4 * (lane >> 5) + (lane & 3);
+}
+template <int MODE, int IDX>
+__device__ __forceinline__ int block_c(int lane) {
+  constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
+  return (IDX % NJ) * 32 + 4 * ((lane & 31) >> 2);
+}
+
+// Memory instructions issued after the pre-activation loads of block IDX and before the wait for
+// them: the stores of block IDX-1 and the loads of block IDX+1.
+template <int IDX, int NB>
+constexpr int aux_younger() {
+  return (IDX >= 1 ? 8 : 0) + (IDX + 1 < NB ? 8 : 0);
 }
 
 // Blocks IDX.. of the wave's accumulators, unrolled at compile time (the loop unroller gives up on
 // the larger epilogues, and a run-time block index would put the accumulators in scratch memory).
+// The down-projection dgrad keeps the pre-activation loads one block ahead of their use.
 template <int MODE, int IDX>
-__device__ __forceinline__ void epilogue_from(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], int g, int row0,
-                                              int m_end, int col0, int lane, int split, int ksplit, float* partial) {
+__device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& o, const f32x16_t (&acc)[MI][NI],
+                                              int row0, int col0, int m_end, int lane, AuxBlock (&aux)[2],
+                                              int ksplit) {
   constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
-  if constexpr (IDX < MI * NJ) {
+  constexpr int NB = MI * NJ;
+  if constexpr (IDX < NB) {
+    if constexpr (MODE == GEMM_DOWN_BWD) {
+      if constexpr (IDX + 1 < NB)
+        load_aux(p, row0 + block_r<MODE, IDX + 1>(lane), m_end, col0 + block_c<MODE, IDX + 1>(lane),
+                 aux[(IDX + 1) % 2]);
+      wait_aux<aux_younger<IDX, NB>()>(aux[IDX % 2]);
+    }
     constexpr int mi = IDX / NJ, ni = IDX % NJ;
     constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NI / 2 : ni;
-    epilogue_block<MODE>(p, acc[mi][ni], acc[mi][nu], g, row0 + mi * 32 + 4 * (lane >> 5) + (lane & 3), m_end,
-                         col0 + ni * 32 + 4 * ((lane & 31) >> 2), lane, split, ksplit, partial);
-    epilogue_from<MODE, IDX + 1>(p, acc, g, row0, m_end, col0, lane, split, ksplit, partial);
+    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, IDX>(lane), block_c<MODE, IDX>(lane), lane,
+                         aux[IDX % 2], ksplit);
+    epilogue_from<MODE, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
   }
 }
 
@@ -552,7 +646,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
   const int row0 = t.m0 + wm * 128;
   const int col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 64 : t.nt * BN + wn * 128;
-  epilogue_from<MODE, 0>(p, acc, t.g, row0, t.m_end, col0, lane, t.split, ksplit, partial);
+  const OutWins o = out_wins<MODE>(p, t, row0, col0, ksplit, partial);
+  AuxBlock aux[2];
+  if constexpr (MODE == GEMM_DOWN_BWD)
+    load_aux(p, row0 + block_r<MODE, 0>(lane), t.m_end, col0 + block_c<MODE, 0>(lane), aux[0]);
+  epilogue_from<MODE, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
 }
 
 // Output of a tile with an empty K range (a weight gradient of an expert without tokens): zeros.
@@ -562,16 +660,15 @@ __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int 
   const float z[4] = {0.f, 0.f, 0.f, 0.f};
   const u32x2_t zw = {0u, 0u};
   const int row0 = t.m0 + wm * 128, col0 = t.nt * BN + wn * 128;
+  const OutWins o = out_wins<MODE>(p, t, row0, col0, ksplit, partial);
 #pragma unroll 1
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll 1
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg) {
-        const int m = row0 + mi * 32 + 8 * vg + 4 * (lane >> 5) + (lane & 3);
-        const int n = col0 + ni * 32 + 4 * ((lane & 31) >> 2);
-        if (m < t.m_end) store4<MODE>(p, t.g, m, n, z, z, zw, zw, t.split, ksplit, partial);
-      }
+      for (int vg = 0; vg < 4; ++vg)
+        store4<MODE>(p, o, mi * 32 + 8 * vg + 4 * (lane >> 5) + (lane & 3), ni * 32 + 4 * ((lane & 31) >> 2), z, z,
+                     zw, zw, ksplit);
 }
 
 // Per-group tile prefix (ragged-M modes): pref[g] = 256-row tiles of the groups before g, from
@@ -605,10 +702,13 @@ __device__ __forceinline__ void tile_prefix_lds(const GemmArgs& p, const int* of
   __syncthreads();
 }
 
-// s_waitcnt vmcnt(N) (lgkmcnt(0) too): everything but the N newest loads or stores is done.
-__device__ __forceinline__ void wait_vm16() { __builtin_amdgcn_s_waitcnt(0x4070); }
-__device__ __forceinline__ void wait_vm24() { __builtin_amdgcn_s_waitcnt(0x4078); }
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// s_waitcnt vmcnt(N) lgkmcnt(0): everything but the N newest loads or stores is done.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
+}
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Producer of the load stream: the tile and K step of the next stage to load.  Once the stream
@@ -708,14 +808,18 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
     issue_all<MODE, 0>(p, lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
     advance<MODE>(pr, p, pref, offs, nbx, L_end, NT, MT, ksplit, wave, lane);
   }
-  wait_vm24();
+  wait_vm<24>();
   barrier();
   FragA<MODE> a0, a1;
   FragB<MODE> b0, b1;
   read_all<MODE, 0>(a0, b0, fa0, fb0);
   frag_wait(a0, b0);
 
-  int j = 0;
+  // K steps since the last epilogue.  Its stores are younger than the stage each of the next three
+  // K steps waits for, and at least epilogue_stores() of them were issued, so those steps may
+  // leave that many more operations outstanding.
+  constexpr int VM_AFTER_EPI = 16 + epilogue_stores<MODE>() < 62 ? 16 + epilogue_stores<MODE>() : 62;
+  int j = 0, since_epi = 3;
   for (;;) {
     f32x16_t acc[MI][NI];
 #pragma unroll
@@ -731,7 +835,8 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
       frag_wait(a1, b1);
       // Stage j+1 has landed once only the loads of stages j+2, j+3 (and any stores issued after
       // them) are outstanding; the barrier makes every wave's part visible and frees slot j & 3.
-      wait_vm16();
+      if (since_epi < 3) wait_vm<VM_AFTER_EPI>();
+      else wait_vm<16>();
       barrier();
       // Phase 1: substep 1 of stage j; read substep 0 of stage j+1; load stage j+4 into slot j & 3.
       const uint32_t sn = ((j + 1) & 3) * STAGE;
@@ -739,8 +844,10 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
       phase1<MODE, 0>(acc, a1, b1, a0, b0, fa0 + sn, fb0 + sn, lds + sb, ss, pr.voff, wave, lane);
       advance<MODE>(pr, p, pref, offs, nbx, L_end, NT, MT, ksplit, wave, lane);
       frag_wait(a0, b0);
+      ++since_epi;
     }
     epilogue_tile<MODE>(p, acc, ct, wm, wn, lane, ksplit, partial);
+    since_epi = 0;
     bool more = false;
     for (Lc += nbx; Lc < L_end; Lc += nbx) {
       ct = decode_tile<MODE>(p, pref, offs, Lc, NT, MT, ksplit);
@@ -753,7 +860,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
     if (!more) break;
   }
   // No direct-to-LDS load may still be writing when the workgroup's LDS is released.
-  wait_vm0();
+  wait_vm<0>();
 }
 
 template <int MODE>

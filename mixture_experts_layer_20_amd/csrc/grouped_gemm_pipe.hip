@@ -343,10 +343,12 @@ using FragA = Frag<Traits<MODE>::a_kcontig>;
 template <int MODE>
 using FragB = Frag<Traits<MODE>::b_kcontig>;
 
+// The B fragment goes in as the MFMA's first operand: the accumulator block is then the
+// transpose of the output block, so each lane ends up with consecutive output columns of one row.
 template <int MODE, int Q>
 __device__ __forceinline__ void mfma_slot(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a, const FragB<MODE>& b) {
   constexpr int i = Q >> 2, j = Q & 3;
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.get(i), b.get(j), acc[i][j], 0, 0, 0);
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b.get(j), a.get(i), acc[i][j], 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -436,12 +438,22 @@ __device__ __forceinline__ OutWin out_win(const void* base, size_t elem_off, int
   w.r = __builtin_amdgcn_make_buffer_rsrc(b, 0, max(rows, 0) * (int)w.row_bytes, 0x00020000);
   return w;
 }
-__device__ __forceinline__ void st_bf16x4(const OutWin& w, int r, int c, const float (&x)[4]) {
-  __builtin_amdgcn_raw_buffer_store_b64(pack4_bf16(x), w.r, (int)(r * w.row_bytes) + c * 2, 0, 0);
+// 8 fp32 values to packed bf16 (16 bytes).
+__device__ __forceinline__ u32x4_t pack8_bf16(const float (&x)[8]) {
+  const float lo[4] = {x[0], x[1], x[2], x[3]}, hi[4] = {x[4], x[5], x[6], x[7]};
+  const u32x2_t a = pack4_bf16(lo), b = pack4_bf16(hi);
+  const u32x4_t w = {a.x, a.y, b.x, b.y};
+  return w;
 }
-__device__ __forceinline__ void st_f32x4(const OutWin& w, int r, int c, const float (&x)[4]) {
-  const u32x4_t v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-  __builtin_amdgcn_raw_buffer_store_b128(v, w.r, (int)(r * w.row_bytes) + c * 4, 0, 0);
+__device__ __forceinline__ void st_bf16x8(const OutWin& w, int r, int c, const float (&x)[8]) {
+  __builtin_amdgcn_raw_buffer_store_b128(pack8_bf16(x), w.r, (int)(r * w.row_bytes) + c * 2, 0, 0);
+}
+__device__ __forceinline__ void st_f32x8(const OutWin& w, int r, int c, const float (&x)[8]) {
+  const u32x4_t lo = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+  const u32x4_t hi = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
+  const int off = (int)(r * w.row_bytes) + c * 4;
+  __builtin_amdgcn_raw_buffer_store_b128(lo, w.r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(hi, w.r, off + 16, 0, 0);
 }
 
 // The output windows of one wave's 128x128 block of a tile.
@@ -478,37 +490,42 @@ __device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, in
   return o;
 }
 
-// Store 4 consecutive outputs (window row r, columns c..c+3) of the mode; u holds the
-// up-projection values of the gate/up GEMM, au/bu the stashed pre-activations of the
-// down-projection dgrad.
+// Stashed pre-activations (a, b) of the down-projection dgrad for 8 consecutive columns.
+struct Aux8 {
+  u32x4_t a, b;
+};
+
+// Store 8 consecutive outputs (window row r, columns c..c+7) of the mode; u holds the
+// up-projection values of the gate/up GEMM, x the stashed pre-activations of the down-projection
+// dgrad.
 template <int MODE>
-__device__ __forceinline__ void store4(const GemmArgs& p, const OutWins& o, int r, int c, const float (&v)[4],
-                                       const float (&u)[4], u32x2_t au, u32x2_t bu, int ksplit) {
+__device__ __forceinline__ void store8(const GemmArgs& p, const OutWins& o, int r, int c, const float (&v)[8],
+                                       const float (&u)[8], const Aux8& x, int ksplit) {
   if constexpr (MODE == GEMM_UP_FWD) {
-    float h[4];
+    float h[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = v[i] * fast_sigmoid(v[i]) * u[i];
-    if (p.out0) st_bf16x4(o.w[0], r, c, v);
-    if (p.out1) st_bf16x4(o.w[1], r, c, u);
-    st_bf16x4(o.w[2], r, c, h);
+    for (int i = 0; i < 8; ++i) h[i] = v[i] * fast_sigmoid(v[i]) * u[i];
+    if (p.out0) st_bf16x8(o.w[0], r, c, v);
+    if (p.out1) st_bf16x8(o.w[1], r, c, u);
+    st_bf16x8(o.w[2], r, c, h);
   } else if constexpr (MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD) {
-    st_bf16x4(o.w[0], r, c, v);
+    st_bf16x8(o.w[0], r, c, v);
   } else if constexpr (MODE == GEMM_DOWN_BWD) {
-    const float a4[4] = {bf16_lo(au.x), bf16_hi(au.x), bf16_lo(au.y), bf16_hi(au.y)};
-    const float b4[4] = {bf16_lo(bu.x), bf16_hi(bu.x), bf16_lo(bu.y), bf16_hi(bu.y)};
-    float da[4], db[4];
+    const uint32_t aw[4] = {x.a.x, x.a.y, x.a.z, x.a.w}, bw[4] = {x.b.x, x.b.y, x.b.z, x.b.w};
+    float da[8], db[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = a4[i], b = b4[i];
+    for (int i = 0; i < 8; ++i) {
+      const float a = (i & 1) ? bf16_hi(aw[i >> 1]) : bf16_lo(aw[i >> 1]);
+      const float b = (i & 1) ? bf16_hi(bw[i >> 1]) : bf16_lo(bw[i >> 1]);
       const float s = fast_sigmoid(a);
       da[i] = v[i] * b * s * (1.0f + a * (1.0f - s));
       db[i] = v[i] * a * s;
     }
-    st_bf16x4(o.w[0], r, c, da);
-    st_bf16x4(o.w[0], r, p.f + c, db);
+    st_bf16x8(o.w[0], r, c, da);
+    st_bf16x8(o.w[0], r, p.f + c, db);
   } else {  // weight gradients
-    if (ksplit > 1) st_f32x4(o.w[0], r, c, v);
-    else st_bf16x4(o.w[0], r, c, v);
+    if (ksplit > 1) st_f32x8(o.w[0], r, c, v);
+    else st_bf16x8(o.w[0], r, c, v);
   }
 }
 
@@ -516,32 +533,13 @@ __device__ __forceinline__ void store4(const GemmArgs& p, const OutWins& o, int 
 // stashes of the gate/up GEMM not counted).
 template <int MODE>
 constexpr int epilogue_stores() {
-  return MODE == GEMM_UP_FWD ? 32 : (MODE == GEMM_DOWN_BWD ? 128 : 64);
-}
-
-// 4x4 transpose inside each quad of lanes (DPP quad permutes): on entry lane j of a quad holds
-// x[e] = M[j][e]; on exit it holds x[e] = M[e][j].
-__device__ __forceinline__ float dpp_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
-}
-__device__ __forceinline__ float dpp_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
-}
-__device__ __forceinline__ void quad_transpose(float (&x)[4], int lane) {
-  const bool hi = lane & 2, odd = lane & 1;
-  const float u0 = dpp_xor2(x[0]), u1 = dpp_xor2(x[1]), u2 = dpp_xor2(x[2]), u3 = dpp_xor2(x[3]);
-  const float n0 = hi ? u2 : x[0], n1 = hi ? u3 : x[1], n2 = hi ? x[2] : u0, n3 = hi ? x[3] : u1;
-  const float w0 = dpp_xor1(n0), w1 = dpp_xor1(n1), w2 = dpp_xor1(n2), w3 = dpp_xor1(n3);
-  x[0] = odd ? w1 : n0;
-  x[1] = odd ? n1 : w0;
-  x[2] = odd ? w3 : n2;
-  x[3] = odd ? n3 : w2;
+  return MODE == GEMM_UP_FWD ? 16 : (MODE == GEMM_DOWN_BWD ? 64 : 32);
 }
 
 // Copies of four accumulator registers to VGPRs.  Written out so that each value leaves its AGPR
 // only where it is used: left to itself the compiler moves the whole accumulator set to VGPRs at
-// the end of the K loop and spills.  The hazard checker does not look into inline asm, so the
-// two wait states a DPP read of a freshly written VGPR needs are added here.
+// the end of the K loop and spills.  The hazard checker does not look into inline asm, so two
+// wait states for a cross-lane read of a freshly written VGPR are added here.
 #define MOE_AGPR_READ4(C, E0, X)                                                                  \
   asm volatile(                                                                                   \
       "v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\tv_accvgpr_read_b32 %2, %6\n\t"     \
@@ -549,69 +547,75 @@ __device__ __forceinline__ void quad_transpose(float (&x)[4], int lane) {
       : "=v"(X[0]), "=v"(X[1]), "=v"(X[2]), "=v"(X[3])                                            \
       : "a"(C[(E0)]), "a"(C[(E0) + 1]), "a"(C[(E0) + 2]), "a"(C[(E0) + 3]))
 
-// Stashed pre-activations (a, b) of one accumulator block for the down-projection dgrad: rows
-// row + 8*vg (clamped into the group), columns n..n+3.  Loaded with inline assembly and waited for
-// explicitly: a compiler-tracked load would be preceded and followed by waits that drain the
-// load stream of the next tile.
-struct AuxBlock {
-  u32x2_t a[4], b[4];
-};
-__device__ __forceinline__ void load_aux(const GemmArgs& p, int row, int m_end, int n, AuxBlock& x) {
+// Half H of an accumulator block as 8 consecutive output columns.  With the transposed MFMA, lane
+// l holds output row l % 32 and, for element v, column 8*(v/4) + 4*(l/32) + v%4 of the block.
+// Swapping the upper lanes of group 2H with the lower lanes of group 2H+1 (v_permlane32_swap)
+// leaves lane l with columns 16H + 8*(l/32) + 0..7.
+__device__ __forceinline__ void block_half(const f32x16_t& c, int h, float (&x)[8]) {
+  float lo[4], hi[4];
+  MOE_AGPR_READ4(c, 8 * h, lo);
+  MOE_AGPR_READ4(c, 8 * h + 4, hi);
 #pragma unroll
-  for (int vg = 0; vg < 4; ++vg) {
-    const size_t idx = (size_t)min(row + 8 * vg, m_end - 1) * p.f + n;
-    const bf16_t* pa = reinterpret_cast<const bf16_t*>(p.aux0) + idx;
-    const bf16_t* pb = reinterpret_cast<const bf16_t*>(p.aux1) + idx;
-    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(x.a[vg]) : "v"(pa) : "memory");
-    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(x.b[vg]) : "v"(pb) : "memory");
+  for (int e = 0; e < 4; ++e) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo[e]), __float_as_uint(hi[e]), false, false);
+    x[e] = __uint_as_float(r[0]);
+    x[4 + e] = __uint_as_float(r[1]);
+  }
+}
+
+// Pre-activations of block rows/columns for the down-projection dgrad, loaded with inline assembly
+// and waited for explicitly: a compiler-tracked load would be preceded and followed by waits that
+// drain the load stream of the next tile.  Row clamped into the group.
+struct AuxBlock {
+  Aux8 h[2];
+};
+__device__ __forceinline__ void load_aux(const GemmArgs& p, int row, int m_end, int col, AuxBlock& x) {
+  const size_t base = (size_t)min(row, m_end - 1) * p.f + col;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16_t* pa = reinterpret_cast<const bf16_t*>(p.aux0) + base + 16 * h;
+    const bf16_t* pb = reinterpret_cast<const bf16_t*>(p.aux1) + base + 16 * h;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.h[h].a) : "v"(pa) : "memory");
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.h[h].b) : "v"(pb) : "memory");
   }
 }
 template <int N>
 __device__ __forceinline__ void wait_aux(AuxBlock& x) {
-  asm volatile("s_waitcnt vmcnt(%8)"
-               : "+v"(x.a[0]), "+v"(x.a[1]), "+v"(x.a[2]), "+v"(x.a[3]), "+v"(x.b[0]), "+v"(x.b[1]), "+v"(x.b[2]),
-                 "+v"(x.b[3])
+  asm volatile("s_waitcnt vmcnt(%4)"
+               : "+v"(x.h[0].a), "+v"(x.h[0].b), "+v"(x.h[1].a), "+v"(x.h[1].b)
                : "n"(N)
                : "memory");
 }
 
-// Epilogue straight from the accumulators.  In the 32x32 accumulator layout lane l holds column
-// l % 32 and, for element v, row 8*(v/4) + 4*(l/32) + v%4; after the quad transpose of elements
-// 4g..4g+3 lane l holds row 8g + 4*(l/32) + l%4 and columns 4*((l%32)/4) .. +3.
-template <int MODE>
-__device__ __forceinline__ void epilogue_block(const GemmArgs& p, const OutWins& o, const f32x16_t& c,
-                                               const f32x16_t& cu, int r, int cc, int lane, const AuxBlock& x,
-                                               int ksplit) {
-#pragma unroll
-  for (int vg = 0; vg < 4; ++vg) {
-    float v[4], u[4];
-    MOE_AGPR_READ4(c, 4 * vg, v);
-    quad_transpose(v, lane);
-    if constexpr (MODE == GEMM_UP_FWD) {
-      MOE_AGPR_READ4(cu, 4 * vg, u);
-      quad_transpose(u, lane);
-    }
-    store4<MODE>(p, o, r + 8 * vg, cc, v, u, x.a[vg], x.b[vg], ksplit);
-  }
-}
-
-// Window row and column of lane's first element of accumulator block IDX.
+// Window row and column of lane's first output of accumulator block IDX.
 template <int MODE, int IDX>
 __device__ __forceinline__ int block_r(int lane) {
   constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
-  return (IDX / NJ) * 32 + 4 * (lane >> 5) + (lane & 3);
+  return (IDX / NJ) * 32 + (lane & 31);
 }
 template <int MODE, int IDX>
 __device__ __forceinline__ int block_c(int lane) {
   constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
-  return (IDX % NJ) * 32 + 4 * ((lane & 31) >> 2);
+  return (IDX % NJ) * 32 + 8 * (lane >> 5);
+}
+
+template <int MODE>
+__device__ __forceinline__ void epilogue_block(const GemmArgs& p, const OutWins& o, const f32x16_t& c,
+                                               const f32x16_t& cu, int r, int cc, const AuxBlock& x, int ksplit) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float v[8], u[8];
+    block_half(c, h, v);
+    if constexpr (MODE == GEMM_UP_FWD) block_half(cu, h, u);
+    store8<MODE>(p, o, r, cc + 16 * h, v, u, x.h[h], ksplit);
+  }
 }
 
 // Memory instructions issued after the pre-activation loads of block IDX and before the wait for
-// them: the stores of block IDX-1 and the loads of block IDX+1.
+// them: the stores of block IDX-1 and the loads of block IDX+1 (4 each).
 template <int IDX, int NB>
 constexpr int aux_younger() {
-  return (IDX >= 1 ? 8 : 0) + (IDX + 1 < NB ? 8 : 0);
+  return (IDX >= 1 ? 4 : 0) + (IDX + 1 < NB ? 4 : 0);
 }
 
 // Blocks IDX.. of the wave's accumulators, unrolled at compile time (the loop unroller gives up on
@@ -632,7 +636,7 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& 
     }
     constexpr int mi = IDX / NJ, ni = IDX % NJ;
     constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NI / 2 : ni;
-    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, IDX>(lane), block_c<MODE, IDX>(lane), lane,
+    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, IDX>(lane), block_c<MODE, IDX>(lane),
                          aux[IDX % 2], ksplit);
     epilogue_from<MODE, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
   }
@@ -657,8 +661,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
 template <int MODE>
 __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int wm, int wn, int lane, int ksplit,
                                           float* partial) {
-  const float z[4] = {0.f, 0.f, 0.f, 0.f};
-  const u32x2_t zw = {0u, 0u};
+  const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const Aux8 zx = {};
   const int row0 = t.m0 + wm * 128, col0 = t.nt * BN + wn * 128;
   const OutWins o = out_wins<MODE>(p, t, row0, col0, ksplit, partial);
 #pragma unroll 1
@@ -666,9 +670,8 @@ __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int 
 #pragma unroll 1
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-      for (int vg = 0; vg < 4; ++vg)
-        store4<MODE>(p, o, mi * 32 + 8 * vg + 4 * (lane >> 5) + (lane & 3), ni * 32 + 4 * ((lane & 31) >> 2), z, z,
-                     zw, zw, ksplit);
+      for (int h = 0; h < 2; ++h)
+        store8<MODE>(p, o, mi * 32 + (lane & 31), ni * 32 + 8 * (lane >> 5) + 16 * h, z, z, zx, ksplit);
 }
 
 // Per-group tile prefix (ragged-M modes): pref[g] = 256-row tiles of the groups before g, from

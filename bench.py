@@ -27,20 +27,19 @@ PEAK_HBM_GBS = 8000.0
 GEMM_STAGES = ("gate_up_fwd", "down_fwd", "down_bwd", "down_wgrad", "gate_up_dgrad", "gate_up_wgrad")
 
 
-def stage_flops(cfg):
-    """Algorithmic FLOPs of each library call of one step (2 per multiply-add, no padding)."""
+def stage_flops(cfg, merged=True):
+    """Algorithmic FLOPs of each GEMM stage call of one step (2 per multiply-add, no padding).
+    Merged: each stage runs the routed experts and the shared expert in one call."""
     Tk, T, d, f, fs = cfg.T * cfg.k, cfg.T, cfg.d, cfg.f, cfg.fs
-    fl = {
-        "gate_up_fwd": 4.0 * Tk * d * f, "down_fwd": 2.0 * Tk * d * f,
-        "down_bwd": 2.0 * Tk * d * f, "down_wgrad": 2.0 * Tk * d * f,
-        "gate_up_dgrad": 4.0 * Tk * d * f, "gate_up_wgrad": 4.0 * Tk * d * f,
-    }
-    if fs:
-        fl["shared_fwd"] = 6.0 * T * d * fs
-        fl.update({"shared_down_bwd": 2.0 * T * d * fs, "shared_down_wgrad": 2.0 * T * d * fs,
-                   "shared_gate_up_dgrad": 4.0 * T * d * fs, "shared_gate_up_wgrad": 4.0 * T * d * fs})
-    if not cfg.backward:
-        fl = {k: v for k, v in fl.items() if k in ("gate_up_fwd", "down_fwd", "shared_fwd")}
+    per_row = {"gate_up_fwd": 4.0, "down_fwd": 2.0, "down_bwd": 2.0, "down_wgrad": 2.0,
+               "gate_up_dgrad": 4.0, "gate_up_wgrad": 4.0}
+    stages = GEMM_STAGES if cfg.backward else ("gate_up_fwd", "down_fwd")
+    fl = {}
+    for s in stages:
+        fl[s] = per_row[s] * Tk * d * f
+        if fs:
+            key = s if merged else "shared_" + s
+            fl[key] = fl.get(key, 0.0) + per_row[s] * T * d * fs
     return fl
 
 
@@ -96,6 +95,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="tiny64e_random")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="one GEMM call per expert set instead of routed + shared in one call")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -119,7 +120,7 @@ def main(argv=None) -> int:
     print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = I.make_inputs(cfg)
     dev = torch.device("cuda:0")
-    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev))
+    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not a.no_merge)
     if a.copy_probe_mb > 0:
         src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -145,7 +146,7 @@ def main(argv=None) -> int:
     for name, pairs in lay.events.items():
         ms = [s.elapsed_time(e) for s, e in pairs]
         stages[name] = sum(ms) / len(ms)
-    flops = stage_flops(cfg)
+    flops = stage_flops(cfg, merged=not a.no_merge)
     gemm_ms = sum(stages[s] for s in flops if s in stages)
     gemm_flop = sum(flops.values())
     stage_tflops = {s: flops[s] / (stages[s] * 1e-3) / 1e12 for s in flops if s in stages}

@@ -161,6 +161,58 @@ moe_status_t moe_expert_gate_up_wgrad(const void* dab, const void* x_in, const i
                                       void* dw1, void* dw3, void* ws, size_t ws_bytes,
                                       moe_stream_t stream);
 
+/* The same GEMM stages over two sets of experts in one call: the routed experts and the shared
+ * expert (the pages' block has top-k routed experts plus one shared expert on every token:
+ * "Olmo-core DDP MoE examples", "Production throughput runs").  The shared expert is a set with
+ * G = 1, offsets = {0, T} and x = the layer input.  Where the pipelined kernel takes both sets
+ * the stage is one launch, whose tiles fill the CUs that a lone one-group GEMM would leave idle;
+ * otherwise the sets run one after the other.  Results are identical either way.
+ * Each stage reads the members listed above for its single-set call:
+ *   GATE_UP_FWD:   x, w1, w3 -> a, b (both NULL or both given), h
+ *   DOWN_FWD:      h, w2 -> y
+ *   DOWN_BWD:      dy, w2, a, b -> dab
+ *   GATE_UP_DGRAD: dab, w1, w3 -> dx
+ *   DOWN_WGRAD:    dy, h -> dw2
+ *   GATE_UP_WGRAD: dab, x -> dw1, dw3
+ * Unused members may be NULL.  Every set needs d common; f may differ between sets. */
+typedef struct {
+  const int32_t* offsets; /* [G+1] device, as for the single-set calls */
+  int32_t G;
+  int64_t M;              /* rows of this set */
+  int64_t f;              /* hidden width of this set's experts */
+  const void* x;          /* [M, d] */
+  const void* w1;         /* [G, f, d] */
+  const void* w3;         /* [G, f, d] */
+  const void* w2;         /* [G, d, f] */
+  void* a;                /* [M, f] */
+  void* b;                /* [M, f] */
+  void* h;                /* [M, f] */
+  void* y;                /* [M, d] */
+  const void* dy;         /* [M, d] */
+  void* dab;              /* [M, 2f] */
+  void* dx;               /* [M, d] */
+  void* dw1;              /* [G, f, d] */
+  void* dw3;              /* [G, f, d] */
+  void* dw2;              /* [G, d, f] */
+} moe_expert_set_t;
+
+typedef enum {
+  MOE_STAGE_GATE_UP_FWD = 0,
+  MOE_STAGE_DOWN_FWD = 1,
+  MOE_STAGE_DOWN_BWD = 2,
+  MOE_STAGE_GATE_UP_DGRAD = 3,
+  MOE_STAGE_DOWN_WGRAD = 4,
+  MOE_STAGE_GATE_UP_WGRAD = 5
+} moe_stage_t;
+
+/* Workspace bytes for moe_expert_stage over these sets (nsets = 1 or 2). */
+size_t moe_expert_stage_workspace_size(const moe_expert_set_t* sets, int32_t nsets, int64_t d);
+/* One GEMM stage over nsets (1 or 2) expert sets; sets is a HOST array, the tensors it points to
+ * are device memory.  Errors as for the single-set calls; MOE_ERR_INVALID_VALUE for a bad stage or
+ * nsets. */
+moe_status_t moe_expert_stage(moe_stage_t stage, const moe_expert_set_t* sets, int32_t nsets, int64_t d,
+                              moe_dtype_t dt, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* ------------------------------------------------------------------------------------------ */
 /* Combine                                                                                     */
 

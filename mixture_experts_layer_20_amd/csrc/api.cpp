@@ -250,6 +250,85 @@ moe_status_t moe_expert_gate_up_wgrad(const void* dab, const void* x_in, const i
   return run_gemm(moe::GEMM_UP_WGRAD, a, dt, stream, "gate/up wgrad GEMM");
 }
 
+size_t moe_expert_stage_workspace_size(const moe_expert_set_t* sets, int32_t nsets, int64_t d) {
+  if (!sets || nsets < 1 || nsets > 2 || d <= 0) return 0;
+  size_t need = 0;
+  for (int i = 0; i < nsets; ++i) {
+    const moe_expert_set_t& e = sets[i];
+    if (e.G <= 0 || e.M < 0 || e.f <= 0) return 0;
+    need = std::max(need, moe::gemm_ws_bytes(e.G) + align256(moe::gemm_partial_bytes(e.G, e.M, (int)d, (int)e.f)));
+  }
+  return need;
+}
+
+namespace {
+
+// The GEMM operands of one expert set for a stage, or an error when a member the stage needs is
+// missing.
+moe_status_t stage_operands(moe_stage_t stage, const moe_expert_set_t& e, moe::GemmArgs& a) {
+  const bool rows = e.M > 0;
+  switch (stage) {
+    case MOE_STAGE_GATE_UP_FWD:
+      CHECK(e.w1 && e.w3 && (!rows || (e.x && e.h)), MOE_ERR_INVALID_VALUE, "x/w1/w3/h is NULL");
+      CHECK((e.a == nullptr) == (e.b == nullptr), MOE_ERR_INVALID_VALUE,
+            "a and b must both be given or both be NULL");
+      a.a = e.x; a.b0 = e.w1; a.b1 = e.w3; a.out0 = e.a; a.out1 = e.b; a.out2 = e.h;
+      return MOE_OK;
+    case MOE_STAGE_DOWN_FWD:
+      CHECK(e.w2 && (!rows || (e.h && e.y)), MOE_ERR_INVALID_VALUE, "h/w2/y is NULL");
+      a.a = e.h; a.b0 = e.w2; a.out0 = e.y;
+      return MOE_OK;
+    case MOE_STAGE_DOWN_BWD:
+      CHECK(e.w2 && (!rows || (e.dy && e.a && e.b && e.dab)), MOE_ERR_INVALID_VALUE, "dy/a/b/w2/dab is NULL");
+      a.a = e.dy; a.b0 = e.w2; a.aux0 = e.a; a.aux1 = e.b; a.out0 = e.dab;
+      return MOE_OK;
+    case MOE_STAGE_GATE_UP_DGRAD:
+      CHECK(e.w1 && e.w3 && (!rows || (e.dab && e.dx)), MOE_ERR_INVALID_VALUE, "dab/w1/w3/dx is NULL");
+      a.a = e.dab; a.b0 = e.w1; a.b1 = e.w3; a.out0 = e.dx;
+      return MOE_OK;
+    case MOE_STAGE_DOWN_WGRAD:
+      CHECK(e.dw2 && (!rows || (e.dy && e.h)), MOE_ERR_INVALID_VALUE, "dy/h/dw2 is NULL");
+      a.a = e.dy; a.b0 = e.h; a.out0 = e.dw2;
+      return MOE_OK;
+    case MOE_STAGE_GATE_UP_WGRAD:
+      CHECK(e.dw1 && e.dw3 && (!rows || (e.dab && e.x)), MOE_ERR_INVALID_VALUE, "dab/x/dw1/dw3 is NULL");
+      a.a = e.dab; a.b0 = e.x; a.out0 = e.dw1; a.out1 = e.dw3;
+      return MOE_OK;
+  }
+  return fail(MOE_ERR_INVALID_VALUE, "unknown stage %d", (int)stage);
+}
+
+}  // namespace
+
+moe_status_t moe_expert_stage(moe_stage_t stage, const moe_expert_set_t* sets, int32_t nsets, int64_t d,
+                              moe_dtype_t dt, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  g_err.clear();
+  CHECK(sets && (nsets == 1 || nsets == 2), MOE_ERR_INVALID_VALUE, "nsets must be 1 or 2 (got %d)", (int)nsets);
+  CHECK((int)stage >= 0 && (int)stage <= 5, MOE_ERR_INVALID_VALUE, "unknown stage %d", (int)stage);
+  size_t need = 0;
+  moe::GemmArgs a{};
+  for (int i = 0; i < nsets; ++i) {
+    const moe_expert_set_t& e = sets[i];
+    moe_status_t st = check_mlp(e.G, e.M, d, e.f, dt);
+    if (st != MOE_OK) return st;
+    CHECK(e.offsets, MOE_ERR_INVALID_VALUE, "offsets of set %d is NULL", i);
+    need = std::max(need, moe::gemm_ws_bytes(e.G));
+    moe::GemmArgs s = base_args(e.offsets, e.G, e.M, d, e.f, ws, ws_bytes);
+    if ((st = stage_operands(stage, e, s)) != MOE_OK) return st;
+    if (i == 0) {
+      a = s;
+    } else {
+      a.nseg = 2;
+      a.s1 = moe::GemmSeg{s.a, s.b0, s.b1, s.aux0, s.aux1, s.out0, s.out1, s.out2, s.offsets, s.G, s.M, s.f};
+    }
+  }
+  CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+        ws ? ws_bytes : (size_t)0);
+  static const char* names[6] = {"gate/up GEMM", "down GEMM", "down dgrad GEMM", "gate/up dgrad GEMM",
+                                 "down wgrad GEMM", "gate/up wgrad GEMM"};
+  return run_gemm((int)stage, a, dt, stream, names[(int)stage]);
+}
+
 moe_status_t moe_grouped_mlp_fwd(const void* x_in, const int32_t* offsets, int32_t G, int64_t M,
                                  int64_t d, int64_t f, const void* w1, const void* w3,
                                  const void* w2, moe_dtype_t dt, void* a_stash, void* b_stash,

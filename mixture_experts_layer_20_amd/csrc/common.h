@@ -73,6 +73,21 @@ enum GemmMode {
   GEMM_UP_WGRAD = 5,   // dW1 = dA^T x, dW3 = dB^T x
 };
 
+// A second set of groups of the same stage (the shared expert next to the routed experts): its own
+// tensors, group offsets, group count, rows and hidden width; d is common.
+struct GemmSeg {
+  const void* a;
+  const void* b0;
+  const void* b1;
+  const void* aux0;
+  const void* aux1;
+  void* out0;
+  void* out1;
+  void* out2;
+  const int32_t* offsets;
+  int G, M, f;
+};
+
 struct GemmArgs {
   const void* a;      // activation operand
   const void* b0;     // weight (or second activation operand for wgrad)
@@ -86,14 +101,17 @@ struct GemmArgs {
   int32_t* tile_prefix;       // workspace start: [G+1] M-tiles before each group, then split-K partials
   size_t ws_bytes;            // bytes of that workspace
   int G, M, d, f;
+  int nseg;                   // 2: s1 is a second set of groups in the same launch (pipelined kernel only)
+  GemmSeg s1;
 };
 
 size_t gemm_ws_bytes(int G);
 // Workspace bytes for the fp32 partial sums of the split weight-gradient reductions.
 size_t gemm_partial_bytes(int G, long long M, int d, int f);
 hipError_t launch_grouped_gemm(int mode, const GemmArgs& args, bool bf16, hipStream_t s);
-// Pipelined bf16 kernel (256x256 tiles, direct-to-LDS ring): whether it covers this problem, and
-// its launcher (ksplit/partial: split weight-gradient reduction, as in launch_grouped_gemm).
+// Pipelined bf16 kernel (256x256 tiles, direct-to-LDS ring): whether it covers this problem (both
+// sets when nseg == 2), and its launcher (ksplit/partial: split weight-gradient reduction, as in
+// launch_grouped_gemm; one set only).
 bool pipe_supports(int mode, const GemmArgs& args);
 hipError_t launch_grouped_gemm_pipe(int mode, const GemmArgs& args, int ksplit, float* partial, hipStream_t s,
                                     int num_cus);

@@ -935,7 +935,57 @@ size_t gemm_partial_bytes(int G, long long M, int d, int f) {
   return best;
 }
 
+namespace {
+
+// Whether the two sets of p go into one launch of the pipelined kernel: it must cover both, and
+// each must be a shape the single-set launcher would give it.
+bool merge_sets(int mode, const GemmArgs& p) {
+  static const char* pipe_env = getenv("LIBMOE_PIPE");
+  if (pipe_env && pipe_env[0] == '0') return false;
+  if (!pipe_supports(mode, p)) return false;
+  // LIBMOE_MERGE=0: never merge; =2: merge whenever the kernel takes both sets (tests, sweeps).
+  const char* m = getenv("LIBMOE_MERGE");
+  if (m && m[0] == '0') return false;
+  if (m && m[0] == '2') return true;
+  // Weight gradients stay one launch per set: a set's tiles reduce over its rows per group, so
+  // the shared expert's tiles (all T rows) would run many times longer than the routed ones and
+  // the static tile deal would leave most CUs idle behind them.
+  if (mode == GEMM_DOWN_WGRAD || mode == GEMM_UP_WGRAD) return false;
+  return p.G > 0 && p.M / p.G >= 384 && p.s1.G > 0 && p.s1.M / p.s1.G >= 384;
+}
+
+// Set 1 of p as a single-set problem.
+GemmArgs second_set(const GemmArgs& p) {
+  GemmArgs q = p;
+  q.nseg = 0;
+  q.a = p.s1.a;
+  q.b0 = p.s1.b0;
+  q.b1 = p.s1.b1;
+  q.aux0 = p.s1.aux0;
+  q.aux1 = p.s1.aux1;
+  q.out0 = p.s1.out0;
+  q.out1 = p.s1.out1;
+  q.out2 = p.s1.out2;
+  q.offsets = p.s1.offsets;
+  q.G = p.s1.G;
+  q.M = p.s1.M;
+  q.f = p.s1.f;
+  return q;
+}
+
+}  // namespace
+
 hipError_t launch_grouped_gemm(int mode, const GemmArgs& p, bool bf16, hipStream_t s) {
+  if (p.nseg == 2) {
+    // Two sets (routed experts and the shared expert): one launch when the pipelined kernel can
+    // take both, else one launch per set (same results).
+    if (bf16 && merge_sets(mode, p)) return launch_grouped_gemm_pipe(mode, p, 1, nullptr, s, num_cus());
+    GemmArgs p0 = p;
+    p0.nseg = 0;
+    const hipError_t e = launch_grouped_gemm(mode, p0, bf16, s);
+    if (e != hipSuccess) return e;
+    return launch_grouped_gemm(mode, second_set(p), bf16, s);
+  }
   // Split-K partials live in the workspace after the tile prefix.
   float* partial = p.ws_bytes > gemm_ws_bytes(p.G)
                        ? reinterpret_cast<float*>(reinterpret_cast<char*>(p.tile_prefix) + gemm_ws_bytes(p.G))

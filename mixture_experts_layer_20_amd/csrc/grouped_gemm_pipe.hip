@@ -41,7 +41,8 @@ constexpr int BM = 256, BN = 256, BKS = 32, NSTAGE = 4, NTH = 256, WGM = 2, WGN 
 constexpr int OPB = 256 * BKS * 2;         // one operand tile of one stage: 16 KiB
 constexpr int STAGE = 2 * OPB;             // 32 KiB
 constexpr int LDS_BYTES = NSTAGE * STAGE;  // 128 KiB
-constexpr int PMAXG = 1024;
+constexpr int PMAXG = 1024;   // groups of the first set
+constexpr int PMAXG1 = 64;    // groups of the second set (the shared expert: 1)
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -75,10 +76,37 @@ __device__ __forceinline__ int kc_swz(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int mc_phys_chunk(int k, int chunk) { return chunk ^ ((k & 3) << 2); }
 
 // ---- Tiles -------------------------------------------------------------------------------
-// Output tile: group g, rows [m0, min(m0 + 256, m_end)), tile column nt, K range [k_begin, k_end)
-// in nk steps of 32 (split: K chunk index of a split weight gradient).
+// Output tile: set seg, group g, rows [m0, min(m0 + 256, m_end)), tile column nt, K range
+// [k_begin, k_end) in nk steps of 32 (split: K chunk index of a split weight gradient).
 struct Tile {
-  int g, m0, m_end, nt, k_begin, k_end, nk, split;
+  int seg, g, m0, m_end, nt, k_begin, k_end, nk, split;
+};
+
+// The arguments of one set of groups (set 1: the second set of a merged launch), in the layout
+// the addressing helpers read.
+__device__ __forceinline__ GemmArgs seg_args(const GemmArgs& p, int seg) {
+  GemmArgs q = p;
+  const bool s1 = seg != 0;
+  q.a = s1 ? p.s1.a : p.a;
+  q.b0 = s1 ? p.s1.b0 : p.b0;
+  q.b1 = s1 ? p.s1.b1 : p.b1;
+  q.aux0 = s1 ? p.s1.aux0 : p.aux0;
+  q.aux1 = s1 ? p.s1.aux1 : p.aux1;
+  q.out0 = s1 ? p.s1.out0 : p.out0;
+  q.out1 = s1 ? p.s1.out1 : p.out1;
+  q.out2 = s1 ? p.s1.out2 : p.out2;
+  q.offsets = s1 ? p.s1.offsets : p.offsets;
+  q.G = s1 ? p.s1.G : p.G;
+  q.M = s1 ? p.s1.M : p.M;
+  q.f = s1 ? p.s1.f : p.f;
+  return q;
+}
+
+// Tile geometry of one set: tile columns, weight-gradient row tiles, tiles, and the LDS tables
+// (clamped group offsets, per-group tile prefix).
+struct SegGeo {
+  int NT, MT, total;
+  uint32_t offs, pref;
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -90,9 +118,13 @@ __device__ __forceinline__ void group_rows_lds(uint32_t offs, int g, int& lo, in
 }
 
 template <int MODE>
-__device__ __forceinline__ Tile decode_tile(const GemmArgs& p, uint32_t pref, uint32_t offs, int L, int NT, int MT,
-                                            int ksplit) {
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&geo)[2], int L, int ksplit) {
   Tile t;
+  t.seg = L >= geo[0].total;
+  if (t.seg) L -= geo[0].total;
+  const GemmArgs p = seg_args(p0, t.seg);
+  const int NT = t.seg ? geo[1].NT : geo[0].NT, MT = t.seg ? geo[1].MT : geo[0].MT;
+  const uint32_t pref = t.seg ? geo[1].pref : geo[0].pref, offs = t.seg ? geo[1].offs : geo[0].offs;
   t.split = 0;
   if constexpr (!Traits<MODE>::raggedK) {
     const int mt = L / NT;
@@ -676,14 +708,14 @@ __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int 
 
 // Per-group tile prefix (ragged-M modes): pref[g] = 256-row tiles of the groups before g, from
 // the clamped offsets in offs.
-__device__ __forceinline__ void tile_prefix_lds(const GemmArgs& p, const int* offs, int* pref, int* scratch) {
+__device__ __forceinline__ void tile_prefix_lds(int G, const int* offs, int* pref, int* scratch) {
   const int tid = threadIdx.x;
   if (tid == 0) scratch[NTH] = 0;
   __syncthreads();
-  for (int base = 0; base < p.G; base += NTH) {
+  for (int base = 0; base < G; base += NTH) {
     const int g = base + tid;
     int c = 0;
-    if (g < p.G) {
+    if (g < G) {
       const int lo = offs[g], hi = max(lo, offs[g + 1]);
       c = (hi - lo + BM - 1) / BM;
     }
@@ -696,12 +728,12 @@ __device__ __forceinline__ void tile_prefix_lds(const GemmArgs& p, const int* of
       __syncthreads();
     }
     const int carry = scratch[NTH];
-    if (g < p.G) pref[g] = carry + scratch[tid] - c;
+    if (g < G) pref[g] = carry + scratch[tid] - c;
     __syncthreads();
     if (tid == NTH - 1) scratch[NTH] = carry + scratch[NTH - 1];
     __syncthreads();
   }
-  if (tid == 0) pref[p.G] = scratch[NTH];
+  if (tid == 0) pref[G] = scratch[NTH];
   __syncthreads();
 }
 
@@ -725,8 +757,9 @@ struct Producer {
 
 template <int MODE>
 __device__ __forceinline__ void set_offsets(Producer& pr, const GemmArgs& p, int wave, int lane) {
+  const GemmArgs q = seg_args(p, pr.t.seg);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pr.voff[i] = load_offset<MODE>(p, pr.t, i, wave, lane);
+  for (int i = 0; i < 8; ++i) pr.voff[i] = load_offset<MODE>(q, pr.t, i, wave, lane);
 }
 
 template <int MODE>
@@ -734,19 +767,19 @@ __device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs
   StageSrc ss;
   const int k0 = pr.t.k_begin + pr.k * BKS;
   ss.k_left = pr.t.k_end - k0;
-  stage_bases<MODE>(p, pr.t, k0, wave, ss.sa, ss.sb);
+  stage_bases<MODE>(seg_args(p, pr.t.seg), pr.t, k0, wave, ss.sa, ss.sb);
   return ss;
 }
 
 template <int MODE>
-__device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, uint32_t pref, uint32_t offs, int nbx,
-                                        int L_end, int NT, int MT, int ksplit, int wave, int lane) {
+__device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const SegGeo (&geo)[2], int nbx, int L_end,
+                                        int ksplit, int wave, int lane) {
   if (pr.k + 1 < pr.t.nk) {
     ++pr.k;
     return;
   }
   for (int L = pr.L + nbx; L < L_end; L += nbx) {
-    const Tile t = decode_tile<MODE>(p, pref, offs, L, NT, MT, ksplit);
+    const Tile t = decode_tile<MODE>(p, geo, L, ksplit);
     if (t.nk > 0) {
       pr.t = t;
       pr.L = L;
@@ -759,32 +792,52 @@ __device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, uint32_
 }
 
 template <int MODE>
-__global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, int MT, int ksplit, float* partial) {
+__global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int ksplit, float* partial) {
   typedef Traits<MODE> TR;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   __shared__ int pref_s[PMAXG + 1];
   __shared__ int offs_s[PMAXG + 1];
+  __shared__ int pref1_s[PMAXG1 + 1];
+  __shared__ int offs1_s[PMAXG1 + 1];
   __shared__ int scan_scratch[NTH + 1];
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6), lane = tid & 63;
   const int wm = wave % WGM, wn = wave / WGM;
   const uint32_t lds0 = lds_addr_of(lds);
-  const uint32_t pref = lds_addr_of(pref_s), offs = lds_addr_of(offs_s);
 
   const uint32_t fa0 = lds0 + frag_base<MODE, true>(0, wm, wn, lane), fa1 = lds0 + frag_base<MODE, true>(1, wm, wn, lane);
   const uint32_t fb0 = lds0 + frag_base<MODE, false>(0, wm, wn, lane), fb1 = lds0 + frag_base<MODE, false>(1, wm, wn, lane);
 
-  // Clamped group offsets (the clamping of group_rows) and, for ragged M, the tile prefix.
+  // Per set: clamped group offsets (the clamping of group_rows), tile geometry and, for ragged M,
+  // the per-group tile prefix.  Set 1 (if any) follows set 0 in the tile order.
+  const bool two = p.nseg == 2;
   for (int g = tid; g <= p.G; g += NTH) offs_s[g] = clampi(p.offsets[g], 0, p.M);
+  if (two)
+    for (int g = tid; g <= p.s1.G; g += NTH) offs1_s[g] = clampi(p.s1.offsets[g], 0, p.s1.M);
   __syncthreads();
-  int total;
-  if constexpr (!TR::raggedK) {
-    tile_prefix_lds(p, offs_s, pref_s, scan_scratch);
-    total = pref_s[p.G] * NT;
-  } else {
-    total = p.G * ksplit * MT * NT;
+  SegGeo geo[2];
+  geo[0].offs = lds_addr_of(offs_s);
+  geo[0].pref = lds_addr_of(pref_s);
+  geo[1].offs = lds_addr_of(offs1_s);
+  geo[1].pref = lds_addr_of(pref1_s);
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int f = sg ? p.s1.f : p.f, G = sg ? p.s1.G : p.G;
+    geo[sg].NT = mode_N(MODE, p.d, f) / BN;
+    geo[sg].MT = TR::raggedK ? mode_Mw(MODE, p.d, f) / BM : 0;
+    if (sg == 1 && !two) {
+      geo[sg].total = 0;
+    } else if constexpr (!TR::raggedK) {
+      int* offs_tab = sg ? offs1_s : offs_s;
+      int* pref_tab = sg ? pref1_s : pref_s;
+      tile_prefix_lds(G, offs_tab, pref_tab, scan_scratch);
+      geo[sg].total = pref_tab[G] * geo[sg].NT;
+    } else {
+      geo[sg].total = G * ksplit * geo[sg].MT * geo[sg].NT;
+    }
   }
+  const int total = geo[0].total + geo[1].total;
   const int per = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7;
   const int nbx = gridDim.x >> 3;
@@ -795,9 +848,9 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
   Tile ct;
   for (;; Lc += nbx) {
     if (Lc >= L_end) return;
-    ct = decode_tile<MODE>(p, pref, offs, Lc, NT, MT, ksplit);
+    ct = decode_tile<MODE>(p, geo, Lc, ksplit);
     if (ct.nk > 0) break;
-    zero_tile<MODE>(p, ct, wm, wn, lane, ksplit, partial);
+    zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, ksplit, partial);
   }
 
   // Prologue: stages 0..3 into slots 0..3, wait for stage 0, read substep 0 of stage 0.
@@ -808,8 +861,8 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
   set_offsets<MODE>(pr, p, wave, lane);
 #pragma unroll 1
   for (int s = 0; s < NSTAGE; ++s) {
-    issue_all<MODE, 0>(p, lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
-    advance<MODE>(pr, p, pref, offs, nbx, L_end, NT, MT, ksplit, wave, lane);
+    issue_all<MODE, 0>(seg_args(p, pr.t.seg), lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
+    advance<MODE>(pr, p, geo, nbx, L_end, ksplit, wave, lane);
   }
   wait_vm<24>();
   barrier();
@@ -845,20 +898,20 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
       const uint32_t sn = ((j + 1) & 3) * STAGE;
       const StageSrc ss = stage_src<MODE>(pr, p, wave);
       phase1<MODE, 0>(acc, a1, b1, a0, b0, fa0 + sn, fb0 + sn, lds + sb, ss, pr.voff, wave, lane);
-      advance<MODE>(pr, p, pref, offs, nbx, L_end, NT, MT, ksplit, wave, lane);
+      advance<MODE>(pr, p, geo, nbx, L_end, ksplit, wave, lane);
       frag_wait(a0, b0);
       ++since_epi;
     }
-    epilogue_tile<MODE>(p, acc, ct, wm, wn, lane, ksplit, partial);
+    epilogue_tile<MODE>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, ksplit, partial);
     since_epi = 0;
     bool more = false;
     for (Lc += nbx; Lc < L_end; Lc += nbx) {
-      ct = decode_tile<MODE>(p, pref, offs, Lc, NT, MT, ksplit);
+      ct = decode_tile<MODE>(p, geo, Lc, ksplit);
       if (ct.nk > 0) {
         more = true;
         break;
       }
-      zero_tile<MODE>(p, ct, wm, wn, lane, ksplit, partial);
+      zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, ksplit, partial);
     }
     if (!more) break;
   }
@@ -866,34 +919,37 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int NT, 
   wait_vm<0>();
 }
 
+// Upper bound of the tiles of one set (ragged M: every group may add a partial tile).
+template <int MODE>
+long long set_tiles(int G, int M, int d, int f, int ksplit) {
+  const long long NT = mode_N(MODE, d, f) / BN;
+  if constexpr (!Traits<MODE>::raggedK) return M > 0 ? ((long long)ceil_div(M, BM) + G) * NT : 0;
+  else return (long long)G * (mode_Mw(MODE, d, f) / BM) * NT * ksplit;
+}
+
 template <int MODE>
 hipError_t launch_pipe(const GemmArgs& p, int ksplit, float* partial, hipStream_t s, int num_cus) {
-  typedef Traits<MODE> TR;
-  const int NT = mode_N(MODE, p.d, p.f) / BN;
-  int MT = 0;
-  long long tiles;
-  if constexpr (!TR::raggedK) {
-    if (p.M == 0) return hipSuccess;
-    tiles = ((long long)ceil_div(p.M, BM) + p.G) * NT;
-  } else {
-    MT = mode_Mw(MODE, p.d, p.f) / BM;
-    tiles = (long long)p.G * MT * NT * ksplit;
-  }
+  long long tiles = set_tiles<MODE>(p.G, p.M, p.d, p.f, ksplit);
+  if (p.nseg == 2) tiles += set_tiles<MODE>(p.s1.G, p.s1.M, p.d, p.s1.f, ksplit);
   long long grid = std::min<long long>(tiles, (long long)num_cus);
   grid = (grid + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_pipe<MODE>, dim3((unsigned)grid), dim3(NTH), 0, s, p, NT, MT, ksplit, partial);
+  hipLaunchKernelGGL(grouped_gemm_pipe<MODE>, dim3((unsigned)grid), dim3(NTH), 0, s, p, ksplit, partial);
   return hipGetLastError();
 }
 
 }  // namespace
 
+static bool pipe_supports_set(int mode, int G, int d, int f, int gmax) {
+  if (G > gmax) return false;
+  if (gemm::mode_N(mode, d, f) % BN) return false;
+  if (mode == GEMM_DOWN_WGRAD || mode == GEMM_UP_WGRAD) return gemm::mode_Mw(mode, d, f) % BM == 0;
+  return gemm::mode_K(mode, d, f) % BKS == 0;
+}
+
 bool pipe_supports(int mode, const GemmArgs& p) {
-  if (p.G > PMAXG) return false;
-  const int N = gemm::mode_N(mode, p.d, p.f);
-  if (N % BN) return false;
-  if (mode == GEMM_DOWN_WGRAD || mode == GEMM_UP_WGRAD) return gemm::mode_Mw(mode, p.d, p.f) % BM == 0;
-  return gemm::mode_K(mode, p.d, p.f) % BKS == 0;
+  if (!pipe_supports_set(mode, p.G, p.d, p.f, PMAXG)) return false;
+  return p.nseg != 2 || pipe_supports_set(mode, p.s1.G, p.d, p.s1.f, PMAXG1);
 }
 
 hipError_t launch_grouped_gemm_pipe(int mode, const GemmArgs& p, int ksplit, float* partial, hipStream_t s,

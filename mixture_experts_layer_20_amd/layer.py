@@ -60,9 +60,8 @@ class Buffers:
         b["y"] = e(Tk, d)
         b["out"] = e(T, d)
         b["ws_perm"] = u8(L.moe_permute_workspace_size(T, E, k))
-        gws = max(L.moe_grouped_mlp_fwd_workspace_size(Tk, E, d, f),
-                  L.moe_grouped_mlp_fwd_workspace_size(T, 1, d, max(fs, 128)))
-        b["ws_fwd"] = u8(gws)
+        sizing = [L.expert_set(None, E, Tk, f)] + ([L.expert_set(None, 1, T, fs)] if fs > 0 else [])
+        b["ws_fwd"] = u8(L.moe_expert_stage_workspace_size(sizing, d))
         if fs > 0:
             b["shared_offsets"] = torch.tensor([0, T], dtype=torch.int32, device=device)
             b["as"] = e(T, fs)
@@ -71,8 +70,7 @@ class Buffers:
             b["s"] = e(T, d)
         if cfg.backward:
             # Backward GEMM workspace: tile prefix plus room for split weight-gradient partials.
-            b["ws_bwd"] = u8(max(L.moe_grouped_mlp_bwd_workspace_size(Tk, E, d, f),
-                                 L.moe_grouped_mlp_bwd_workspace_size(T, 1, d, max(fs, 128))))
+            b["ws_bwd"] = u8(L.moe_expert_stage_workspace_size(sizing, d))
             b["dy"] = e(Tk, d)
             b["dgate"] = f32(T, k)
             b["dab"] = e(Tk, 2 * f)
@@ -104,15 +102,47 @@ class MoELayer:
     ws1, ws3, ws2 (shared expert, may be None), dout (backward).
     ``events``: if given a dict, a (start, end) pair of CUDA events is recorded on the current
     stream around every library call, keyed by stage name.
+    ``merge_shared``: run each GEMM stage of the routed experts and the shared expert as one
+    two-set call (one launch where the kernel allows); False makes one call per set.
     """
 
-    def __init__(self, cfg: MoEConfig, params: dict, bufs: Buffers | None = None, renormalize: int = 1):
+    def __init__(self, cfg: MoEConfig, params: dict, bufs: Buffers | None = None, renormalize: int = 1,
+                 merge_shared: bool = True):
         self.cfg = cfg
         self.p = params
         self.bufs = bufs or Buffers.allocate(cfg, params["x"].device)
         self.renorm = renormalize
+        self.merge = merge_shared
         self.dt = L.MOE_BF16 if cfg.dtype == "bf16" else L.MOE_F32
         self.events: dict | None = None
+
+    def _sets(self, dout=None):
+        """The routed experts and (if any) the shared expert as expert sets."""
+        c, p, b = self.cfg, self.p, self.bufs
+        T, E, k, f, fs = c.T, c.E, c.k, c.f, c.fs
+        bw = c.backward
+        g = lambda name: b.t.get(name)
+        routed = L.expert_set(b["offsets"], E, T * k, f, x=b["x_perm"], w1=p["w1"], w3=p["w3"], w2=p["w2"],
+                              a=b["a"] if bw else None, b=b["b"] if bw else None, h=b["h"], y=b["y"],
+                              dy=g("dy"), dab=g("dab"), dx=g("dx_perm"), dw1=g("dw1"), dw3=g("dw3"),
+                              dw2=g("dw2"))
+        if fs == 0:
+            return [routed]
+        shared = L.expert_set(b["shared_offsets"], 1, T, fs, x=p["x"], w1=p["ws1"], w3=p["ws3"], w2=p["ws2"],
+                              a=b["as"] if bw else None, b=b["bs"] if bw else None, h=b["hs"], y=b["s"],
+                              dy=dout, dab=g("dabs"), dx=g("dx_shared"), dw1=g("dws1"), dw3=g("dws3"),
+                              dw2=g("dws2"))
+        return [routed, shared]
+
+    def _gemm(self, name, stage, sets, ws):
+        """One GEMM stage over the expert sets: a single call, or one call per set."""
+        d, dt = self.cfg.d, self.dt
+        if self.merge or len(sets) == 1:
+            self._stage(name, L.moe_expert_stage, stage, sets, d, dt, ws, ws.numel())
+        else:
+            for i, s in enumerate(sets):
+                self._stage(name if i == 0 else "shared_" + name, L.moe_expert_stage, stage, [s], d, dt, ws,
+                            ws.numel())
 
     def _stage(self, name, fn, *args):
         if self.events is None:
@@ -136,18 +166,10 @@ class MoELayer:
         self._stage("permute", L.moe_permute, p["x"], b["topk_idx"], T, d, E, k, dt, b["counts"],
                     b["offsets"], b["dest_pos"], b["src_row"], b["x_perm"], b["ws_perm"],
                     b["ws_perm"].numel())
-        stash_a = b["a"] if c.backward else None
-        stash_b = b["b"] if c.backward else None
-        self._stage("gate_up_fwd", L.moe_expert_gate_up_fwd, b["x_perm"], b["offsets"], E, Tk, d, f,
-                    p["w1"], p["w3"], dt, stash_a, stash_b, b["h"], b["ws_fwd"], b["ws_fwd"].numel())
-        self._stage("down_fwd", L.moe_expert_down_fwd, b["h"], b["offsets"], E, Tk, d, f, p["w2"], dt,
-                    b["y"], b["ws_fwd"], b["ws_fwd"].numel())
-        shared = None
-        if fs > 0:
-            self._stage("shared_fwd", L.moe_grouped_mlp_fwd, p["x"], b["shared_offsets"], 1, T, d, fs,
-                        p["ws1"], p["ws3"], p["ws2"], dt, b["as"] if c.backward else None,
-                        b["bs"] if c.backward else None, b["hs"], b["s"], b["ws_fwd"], b["ws_fwd"].numel())
-            shared = b["s"]
+        sets = self._sets()
+        self._gemm("gate_up_fwd", L.MOE_STAGE_GATE_UP_FWD, sets, b["ws_fwd"])
+        self._gemm("down_fwd", L.MOE_STAGE_DOWN_FWD, sets, b["ws_fwd"])
+        shared = b["s"] if fs > 0 else None
         self._stage("combine", L.moe_combine, b["y"], b["gate"], b["dest_pos"], shared, T, d, k, dt, b["out"])
         return b["out"]
 
@@ -165,27 +187,13 @@ class MoELayer:
                         b["src_row"], p["x"], p["w_router"], T, d, E, k, self.renorm, dt, b["dwr"],
                         b["dx_router"], b["ws_route"], b["ws_route"].numel())
             dx_router = b["dx_router"]
-        ws, wsn = b["ws_bwd"], b["ws_bwd"].numel()
-        self._stage("down_bwd", L.moe_expert_down_bwd, b["dy"], b["a"], b["b"], b["offsets"], E, Tk, d, f,
-                    p["w2"], dt, b["dab"], ws, wsn)
-        self._stage("down_wgrad", L.moe_expert_down_wgrad, b["dy"], b["h"], b["offsets"], E, Tk, d, f, dt,
-                    b["dw2"], ws, wsn)
-        self._stage("gate_up_dgrad", L.moe_expert_gate_up_dgrad, b["dab"], b["offsets"], E, Tk, d, f,
-                    p["w1"], p["w3"], dt, b["dx_perm"], ws, wsn)
-        self._stage("gate_up_wgrad", L.moe_expert_gate_up_wgrad, b["dab"], b["x_perm"], b["offsets"], E, Tk,
-                    d, f, dt, b["dw1"], b["dw3"], ws, wsn)
-        dx_shared = None
-        if fs > 0:
-            so = b["shared_offsets"]
-            self._stage("shared_down_bwd", L.moe_expert_down_bwd, dout, b["as"], b["bs"], so, 1, T, d, fs,
-                        p["ws2"], dt, b["dabs"], ws, wsn)
-            self._stage("shared_down_wgrad", L.moe_expert_down_wgrad, dout, b["hs"], so, 1, T, d, fs, dt,
-                        b["dws2"], ws, wsn)
-            self._stage("shared_gate_up_dgrad", L.moe_expert_gate_up_dgrad, b["dabs"], so, 1, T, d, fs,
-                        p["ws1"], p["ws3"], dt, b["dx_shared"], ws, wsn)
-            self._stage("shared_gate_up_wgrad", L.moe_expert_gate_up_wgrad, b["dabs"], p["x"], so, 1, T, d, fs,
-                        dt, b["dws1"], b["dws3"], ws, wsn)
-            dx_shared = b["dx_shared"]
+        ws = b["ws_bwd"]
+        sets = self._sets(dout)
+        self._gemm("down_bwd", L.MOE_STAGE_DOWN_BWD, sets, ws)
+        self._gemm("down_wgrad", L.MOE_STAGE_DOWN_WGRAD, sets, ws)
+        self._gemm("gate_up_dgrad", L.MOE_STAGE_GATE_UP_DGRAD, sets, ws)
+        self._gemm("gate_up_wgrad", L.MOE_STAGE_GATE_UP_WGRAD, sets, ws)
+        dx_shared = b["dx_shared"] if fs > 0 else None
         self._stage("permute_bwd", L.moe_permute_bwd, b["dx_perm"], b["dest_pos"], dx_shared, dx_router, T, d,
                     k, dt, b["dx"])
         return b["dx"]

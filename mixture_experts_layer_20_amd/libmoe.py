@@ -20,6 +20,13 @@ MOE_ERR_HIP = 4
 MOE_F32 = 0
 MOE_BF16 = 1
 
+MOE_STAGE_GATE_UP_FWD = 0
+MOE_STAGE_DOWN_FWD = 1
+MOE_STAGE_DOWN_BWD = 2
+MOE_STAGE_GATE_UP_DGRAD = 3
+MOE_STAGE_DOWN_WGRAD = 4
+MOE_STAGE_GATE_UP_WGRAD = 5
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libmoe.so")
 
 _c = ctypes
@@ -27,6 +34,16 @@ _P = _c.c_void_p
 _I64 = _c.c_int64
 _I32 = _c.c_int32
 _SZ = _c.c_size_t
+
+
+
+class ExpertSet(ctypes.Structure):
+    """moe_expert_set_t: one set of experts of a multi-set GEMM stage."""
+    _fields_ = [("offsets", ctypes.c_void_p), ("G", ctypes.c_int32), ("M", ctypes.c_int64),
+                ("f", ctypes.c_int64)] + [(n, ctypes.c_void_p) for n in
+                                          ("x", "w1", "w3", "w2", "a", "b", "h", "y", "dy", "dab", "dx", "dw1",
+                                           "dw3", "dw2")]
+
 
 # name -> (restype, argtypes); mirrors include/libmoe.h
 _SIGS = {
@@ -46,6 +63,8 @@ _SIGS = {
     "moe_expert_down_wgrad": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _SZ, _P]),
     "moe_expert_gate_up_dgrad": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
     "moe_expert_gate_up_wgrad": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _SZ, _P]),
+    "moe_expert_stage_workspace_size": (_SZ, [_P, _I32, _I64]),
+    "moe_expert_stage": (_I32, [_I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
     "moe_combine": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_combine_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P]),
     "moe_permute_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
@@ -191,6 +210,31 @@ def moe_expert_gate_up_dgrad(dab, offsets, G, M, d, f, w1, w3, dt, dx_in, ws, ws
 def moe_expert_gate_up_wgrad(dab, x_in, offsets, G, M, d, f, dt, dw1, dw3, ws, ws_bytes, stream=None):
     _call("moe_expert_gate_up_wgrad", _ptr(dab), _ptr(x_in), _ptr(offsets), G, M, d, f, dt, _ptr(dw1),
           _ptr(dw3), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def expert_set(offsets, G, M, f, **tensors) -> ExpertSet:
+    """An ExpertSet from tensors (members not given are NULL)."""
+    e = ExpertSet()
+    e.offsets = _ptr(offsets)
+    e.G, e.M, e.f = G, M, f
+    for name, t in tensors.items():
+        setattr(e, name, _ptr(t))
+    return e
+
+
+def _set_array(sets):
+    arr = (ExpertSet * len(sets))(*sets)
+    return arr, len(sets)
+
+
+def moe_expert_stage_workspace_size(sets, d) -> int:
+    arr, n = _set_array(sets)
+    return lib().moe_expert_stage_workspace_size(ctypes.cast(arr, _P), n, d)
+
+
+def moe_expert_stage(stage, sets, d, dt, ws, ws_bytes, stream=None):
+    arr, n = _set_array(sets)
+    _call("moe_expert_stage", stage, ctypes.cast(arr, _P), n, d, dt, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def moe_combine(y_perm, topk_gate, dest_pos, shared_out, T, d, k, dt, out, stream=None):

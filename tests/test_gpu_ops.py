@@ -220,6 +220,62 @@ def test_stage_calls_equal_combined_calls(dtype):
         assert torch.equal(u, v)
 
 
+def _set_tensors(P, off, M, G, d, f, dtype):
+    dev = {k: dev_tensor(v, dtype) for k, v in P.items()}
+    T = dict(offsets=i32(off), x=dev["X"], w1=dev["w1"], w3=dev["w3"], w2=dev["w2"], dy=dev["dY"],
+             a=empty((M, f), dtype), b=empty((M, f), dtype), h=empty((M, f), dtype), y=empty((M, d), dtype),
+             dab=empty((M, 2 * f), dtype), dx=empty((M, d), dtype), dw1=empty((G, f, d), dtype),
+             dw3=empty((G, f, d), dtype), dw2=empty((G, d, f), dtype))
+    return T
+
+
+def _run_stages(tensor_sets, shapes, d, dtype, merged):
+    """All six stages over the sets, in one call per stage (merged) or one call per set."""
+    sets = [L.expert_set(T["offsets"], G, M, f, **{k: v for k, v in T.items() if k != "offsets"})
+            for T, (M, G, f) in zip(tensor_sets, shapes)]
+    wsn = L.moe_expert_stage_workspace_size(sets, d)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    for stage in (L.MOE_STAGE_GATE_UP_FWD, L.MOE_STAGE_DOWN_FWD, L.MOE_STAGE_DOWN_BWD, L.MOE_STAGE_DOWN_WGRAD,
+                  L.MOE_STAGE_GATE_UP_DGRAD, L.MOE_STAGE_GATE_UP_WGRAD):
+        if merged:
+            L.moe_expert_stage(stage, sets, d, DT[dtype], ws, wsn)
+        else:
+            for s in sets:
+                L.moe_expert_stage(stage, [s], d, DT[dtype], ws, wsn)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("merge", ["2", "1", "0"])
+def test_two_expert_sets(dtype, merge, monkeypatch):
+    """Routed experts and a shared expert (own rows, weights and hidden width) in one call per
+    stage: each set's results match the oracle, and (forward and dgrad stages) equal the
+    one-set-per-call results bit for bit.  LIBMOE_MERGE=2 forces the single-launch path."""
+    monkeypatch.setenv("LIBMOE_MERGE", merge)
+    d = 512
+    shapes = [(4096, 8, 256), (1000, 1, 512)]   # (M, G, f): routed, shared
+    log(f"two expert sets {dtype} merge={merge}")
+    rng = np.random.default_rng(11)
+    offs = [ragged_offsets(4096, 8, rng, (5,)), np.array([0, 1000], np.int32)]
+    probs = [mlp_problem(M, G, d, f, dtype, 20 + i) for i, (M, G, f) in enumerate(shapes)]
+    results = []
+    for merged in (True, False):
+        ts = [_set_tensors(P, off, M, G, d, f, dtype) for P, off, (M, G, f) in zip(probs, offs, shapes)]
+        _run_stages(ts, shapes, d, dtype, merged)
+        results.append(ts)
+    tol = TOL[dtype]
+    for i, (P, off, (M, G, f)) in enumerate(zip(probs, offs, shapes)):
+        A, B, H, Y = O.grouped_swiglu_forward(P["X"], off, P["w1"], P["w3"], P["w2"])
+        rdx, rdw1, rdw3, rdw2, _, _ = O.grouped_swiglu_backward(P["dY"], P["X"], A, B, H, off, P["w1"], P["w3"],
+                                                                P["w2"])
+        got = results[0][i]
+        for name, ref in (("a", A), ("b", B), ("h", H), ("y", Y), ("dx", rdx), ("dw1", rdw1), ("dw3", rdw3),
+                          ("dw2", rdw2)):
+            assert_close(f"set{i}.{name}", tnp(got[name]), ref, tol)
+        for name in ("a", "b", "h", "y", "dab", "dx"):
+            assert torch.equal(got[name], results[1][i][name]), f"set{i}.{name}: merged != per-set"
+
+
 def test_forward_without_stash():
     M, G, d, f = 400, 4, 128, 128
     rng = np.random.default_rng(3)

@@ -258,6 +258,10 @@ size_t moe_expert_stage_workspace_size(const moe_expert_set_t* sets, int32_t nse
     if (e.G <= 0 || e.M < 0 || e.f <= 0) return 0;
     need = std::max(need, moe::gemm_ws_bytes(e.G) + align256(moe::gemm_partial_bytes(e.G, e.M, (int)d, (int)e.f)));
   }
+  if (nsets == 2)
+    need = std::max(need, moe::gemm_ws_bytes(sets[0].G) +
+                              align256(moe::gemm_sets_partial_bytes(sets[0].G, sets[0].M, sets[1].G, sets[1].M,
+                                                                    (int)d, (int)sets[1].f)));
   return need;
 }
 

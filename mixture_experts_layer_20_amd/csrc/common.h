@@ -86,6 +86,7 @@ struct GemmSeg {
   void* out2;
   const int32_t* offsets;
   int G, M, f;
+  int ksplit;   // weight gradients: row-reduction split of this set (fp32 partials; 0 or 1: none)
 };
 
 struct GemmArgs {
@@ -108,6 +109,8 @@ struct GemmArgs {
 size_t gemm_ws_bytes(int G);
 // Workspace bytes for the fp32 partial sums of the split weight-gradient reductions.
 size_t gemm_partial_bytes(int G, long long M, int d, int f);
+// The same for the second set of a two-set weight-gradient launch (its split reduction).
+size_t gemm_sets_partial_bytes(int G0, long long M0, int G1, long long M1, int d, int f1);
 hipError_t launch_grouped_gemm(int mode, const GemmArgs& args, bool bf16, hipStream_t s);
 // Pipelined bf16 kernel (256x256 tiles, direct-to-LDS ring): whether it covers this problem (both
 // sets when nseg == 2), and its launcher (ksplit/partial: split weight-gradient reduction, as in

@@ -923,6 +923,22 @@ hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float
 
 size_t gemm_ws_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) / 256 * 256; }
 
+// Split of the second set's row reduction in a two-set weight-gradient launch: chunks about as
+// long as a group of the first set (at least 256 rows), at most 8.
+static int sets_split(int G0, long long M0, int G1, long long M1) {
+  const long long rows0 = std::max<long long>(256, G0 > 0 ? M0 / G0 : 0);
+  return (int)std::min<long long>(8, std::max<long long>(1, (M1 / std::max(1, G1) + rows0 - 1) / rows0));
+}
+
+size_t gemm_sets_partial_bytes(int G0, long long M0, int G1, long long M1, int d, int f1) {
+  const int ks = sets_split(G0, M0, G1, M1);
+  if (ks <= 1) return 0;
+  size_t best = 0;
+  for (int mode : {GEMM_DOWN_WGRAD, GEMM_UP_WGRAD})
+    best = std::max(best, (size_t)ks * G1 * mode_Mw(mode, d, f1) * mode_N(mode, d, f1) * sizeof(float));
+  return best;
+}
+
 size_t gemm_partial_bytes(int G, long long M, int d, int f) {
   size_t best = 0;
   for (int mode : {GEMM_DOWN_WGRAD, GEMM_UP_WGRAD}) {
@@ -947,10 +963,10 @@ bool merge_sets(int mode, const GemmArgs& p) {
   const char* m = getenv("LIBMOE_MERGE");
   if (m && m[0] == '0') return false;
   if (m && m[0] == '2') return true;
-  // Weight gradients stay one launch per set: a set's tiles reduce over its rows per group, so
-  // the shared expert's tiles (all T rows) would run many times longer than the routed ones and
-  // the static tile deal would leave most CUs idle behind them.
-  if (mode == GEMM_DOWN_WGRAD || mode == GEMM_UP_WGRAD) return false;
+  // Weight gradients: set 0 must fill the chip without a split; set 1's row reduction is split so
+  // its tiles are about as long as set 0's (see launch_wgrad_sets).
+  if (mode == GEMM_DOWN_WGRAD || mode == GEMM_UP_WGRAD)
+    return (long long)p.G * (mode_Mw(mode, p.d, p.f) / 256) * (mode_N(mode, p.d, p.f) / 256) >= 2LL * num_cus();
   return p.G > 0 && p.M / p.G >= 384 && p.s1.G > 0 && p.s1.M / p.s1.G >= 384;
 }
 
@@ -973,13 +989,42 @@ GemmArgs second_set(const GemmArgs& p) {
   return q;
 }
 
+// Weight gradients of two sets in one launch.  A set's tiles reduce over its groups' rows, so the
+// shared expert (all T rows in one group) would give tiles many times longer than the routed
+// ones and leave most CUs idle behind them: its reduction is split into chunks about as long as a
+// routed group (fp32 partials in the workspace, summed in chunk order by splitk_reduce
+// afterwards, as for a split single set).
+template <int MODE>
+hipError_t launch_wgrad_sets(const GemmArgs& p, hipStream_t s) {
+  float* partial = p.ws_bytes > gemm_ws_bytes(p.G)
+                       ? reinterpret_cast<float*>(reinterpret_cast<char*>(p.tile_prefix) + gemm_ws_bytes(p.G))
+                       : nullptr;
+  const size_t pb = partial ? p.ws_bytes - gemm_ws_bytes(p.G) : 0;
+  const int Mw = mode_Mw(MODE, p.d, p.s1.f), N = mode_N(MODE, p.d, p.s1.f);
+  int ks = sets_split(p.G, p.M, p.s1.G, p.s1.M);
+  while (ks > 1 && (size_t)ks * p.s1.G * Mw * N * sizeof(float) > pb) --ks;
+  GemmArgs q = p;
+  q.s1.ksplit = ks;
+  hipError_t e = launch_grouped_gemm_pipe(MODE, q, 1, partial, s, num_cus());
+  if (e != hipSuccess || ks <= 1) return e;
+  const GemmArgs p1 = second_set(p);
+  const size_t n = (size_t)p1.G * Mw * N;
+  hipLaunchKernelGGL(splitk_reduce<MODE>, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0, s,
+                     p1, partial, ks);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(int mode, const GemmArgs& p, bool bf16, hipStream_t s) {
   if (p.nseg == 2) {
     // Two sets (routed experts and the shared expert): one launch when the pipelined kernel can
     // take both, else one launch per set (same results).
-    if (bf16 && merge_sets(mode, p)) return launch_grouped_gemm_pipe(mode, p, 1, nullptr, s, num_cus());
+    if (bf16 && merge_sets(mode, p)) {
+      if (mode == GEMM_DOWN_WGRAD) return launch_wgrad_sets<GEMM_DOWN_WGRAD>(p, s);
+      if (mode == GEMM_UP_WGRAD) return launch_wgrad_sets<GEMM_UP_WGRAD>(p, s);
+      return launch_grouped_gemm_pipe(mode, p, 1, nullptr, s, num_cus());
+    }
     GemmArgs p0 = p;
     p0.nseg = 0;
     const hipError_t e = launch_grouped_gemm(mode, p0, bf16, s);

@@ -79,7 +79,7 @@ __device__ __forceinline__ int mc_phys_chunk(int k, int chunk) { return chunk ^ 
 // Output tile: set seg, group g, rows [m0, min(m0 + 256, m_end)), tile column nt, K range
 // [k_begin, k_end) in nk steps of 32 (split: K chunk index of a split weight gradient).
 struct Tile {
-  int seg, g, m0, m_end, nt, k_begin, k_end, nk, split;
+  int seg, g, m0, m_end, nt, k_begin, k_end, nk, split, ks;
 };
 
 // The arguments of one set of groups (set 1: the second set of a merged launch), in the layout
@@ -102,12 +102,21 @@ __device__ __forceinline__ GemmArgs seg_args(const GemmArgs& p, int seg) {
   return q;
 }
 
-// Tile geometry of one set: tile columns, weight-gradient row tiles, tiles, and the LDS tables
-// (clamped group offsets, per-group tile prefix).
+// Tile geometry of one set: tile columns, weight-gradient row tiles, split, tiles, and the LDS
+// tables (clamped group offsets, per-group tile prefix).
 struct SegGeo {
-  int NT, MT, total;
+  int NT, MT, ks, total;
   uint32_t offs, pref;
 };
+
+// The tiles of one XCD: n of them; list position i < n1 is tile total0 + lo1 + i (set 1), the
+// others are lo0 + (i - n1) (set 0 numbering, which set 1 continues).
+struct Deal {
+  int n, n1, lo0, lo1, total0;
+};
+__device__ __forceinline__ int tile_at(const Deal& dl, int i) {
+  return i < dl.n1 ? dl.total0 + dl.lo1 + i : dl.lo0 + (i - dl.n1);
+}
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -118,12 +127,14 @@ __device__ __forceinline__ void group_rows_lds(uint32_t offs, int g, int& lo, in
 }
 
 template <int MODE>
-__device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&geo)[2], int L, int ksplit) {
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&geo)[2], int L) {
   Tile t;
   t.seg = L >= geo[0].total;
   if (t.seg) L -= geo[0].total;
   const GemmArgs p = seg_args(p0, t.seg);
   const int NT = t.seg ? geo[1].NT : geo[0].NT, MT = t.seg ? geo[1].MT : geo[0].MT;
+  const int ksplit = t.seg ? geo[1].ks : geo[0].ks;
+  t.ks = ksplit;
   const uint32_t pref = t.seg ? geo[1].pref : geo[0].pref, offs = t.seg ? geo[1].offs : geo[0].offs;
   t.split = 0;
   if constexpr (!Traits<MODE>::raggedK) {
@@ -494,8 +505,7 @@ struct OutWins {
 };
 
 template <int MODE>
-__device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, int row0, int col0, int ksplit,
-                                            float* partial) {
+__device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, int row0, int col0, float* partial) {
   OutWins o;
   const int rows = min(128, t.m_end - row0);
   const size_t d = p.d, f = p.f;
@@ -510,7 +520,7 @@ __device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, in
     o.w[0] = out_win(p.out0, (size_t)row0 * 2 * f + col0, rows, 2 * p.f, 2);
   } else {
     const int Mw = mode_Mw(MODE, p.d, p.f), Nw = mode_N(MODE, p.d, p.f);
-    if (ksplit > 1) {
+    if (t.ks > 1) {
       o.w[0] = out_win(partial, (((size_t)t.split * p.G + t.g) * Mw + row0) * Nw + col0, 128, Nw, 4);
     } else if constexpr (MODE == GEMM_DOWN_WGRAD) {
       o.w[0] = out_win(p.out0, ((size_t)t.g * d + row0) * f + col0, 128, p.f, 2);
@@ -676,13 +686,14 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& 
 
 template <int MODE>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], const Tile& t,
-                                              int wm, int wn, int lane, int ksplit, float* partial) {
+                                              int wm, int wn, int lane, float* partial) {
   // The accumulator reads are opaque to the hazard checker: leave the last MFMA's write-back
   // (at most 18 wait states) behind before the first of them.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
   const int row0 = t.m0 + wm * 128;
   const int col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 64 : t.nt * BN + wn * 128;
-  const OutWins o = out_wins<MODE>(p, t, row0, col0, ksplit, partial);
+  const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
+  const int ksplit = t.ks;
   AuxBlock aux[2];
   if constexpr (MODE == GEMM_DOWN_BWD)
     load_aux(p, row0 + block_r<MODE, 0>(lane), t.m_end, col0 + block_c<MODE, 0>(lane), aux[0]);
@@ -691,12 +702,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
 
 // Output of a tile with an empty K range (a weight gradient of an expert without tokens): zeros.
 template <int MODE>
-__device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int wm, int wn, int lane, int ksplit,
+__device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int wm, int wn, int lane,
                                           float* partial) {
   const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const Aux8 zx = {};
   const int row0 = t.m0 + wm * 128, col0 = t.nt * BN + wn * 128;
-  const OutWins o = out_wins<MODE>(p, t, row0, col0, ksplit, partial);
+  const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
+  const int ksplit = t.ks;
 #pragma unroll 1
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll 1
@@ -751,7 +763,7 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // every K step issues exactly 8 loads per wave and the vmcnt arithmetic stays fixed.
 struct Producer {
   Tile t;
-  int L, k;
+  int i, k;   // this XCD's tile list position, K step
   uint32_t voff[8];
 };
 
@@ -772,23 +784,23 @@ __device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs
 }
 
 template <int MODE>
-__device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const SegGeo (&geo)[2], int nbx, int L_end,
-                                        int ksplit, int wave, int lane) {
+__device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const SegGeo (&geo)[2], const Deal& dl,
+                                        int nbx, int wave, int lane) {
   if (pr.k + 1 < pr.t.nk) {
     ++pr.k;
     return;
   }
-  for (int L = pr.L + nbx; L < L_end; L += nbx) {
-    const Tile t = decode_tile<MODE>(p, geo, L, ksplit);
+  for (int i = pr.i + nbx; i < dl.n; i += nbx) {
+    const Tile t = decode_tile<MODE>(p, geo, tile_at(dl, i));
     if (t.nk > 0) {
       pr.t = t;
-      pr.L = L;
+      pr.i = i;
       pr.k = 0;
       set_offsets<MODE>(pr, p, wave, lane);
       return;
     }
   }
-  pr.L = L_end;
+  pr.i = dl.n;
 }
 
 template <int MODE>
@@ -826,6 +838,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     const int f = sg ? p.s1.f : p.f, G = sg ? p.s1.G : p.G;
     geo[sg].NT = mode_N(MODE, p.d, f) / BN;
     geo[sg].MT = TR::raggedK ? mode_Mw(MODE, p.d, f) / BM : 0;
+    geo[sg].ks = sg ? max(1, p.s1.ksplit) : ksplit;
     if (sg == 1 && !two) {
       geo[sg].total = 0;
     } else if constexpr (!TR::raggedK) {
@@ -834,35 +847,50 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
       tile_prefix_lds(G, offs_tab, pref_tab, scan_scratch);
       geo[sg].total = pref_tab[G] * geo[sg].NT;
     } else {
-      geo[sg].total = G * ksplit * geo[sg].MT * geo[sg].NT;
+      geo[sg].total = G * geo[sg].ks * geo[sg].MT * geo[sg].NT;
     }
   }
-  const int total = geo[0].total + geo[1].total;
-  const int per = (total + 7) >> 3;
+  // Tiles are dealt so each XCD (workgroup b runs on XCD b % 8) walks one contiguous run of the
+  // tile order.  Weight gradients of two sets: each XCD gets a run of each set, the longer set-1
+  // tiles (split shared-expert reductions) first.
   const int xcd = blockIdx.x & 7;
   const int nbx = gridDim.x >> 3;
-  const int L_end = min(total, (xcd + 1) * per);
+  Deal dl;
+  dl.total0 = geo[0].total;
+  if (TR::raggedK && two) {
+    const int per0 = (geo[0].total + 7) >> 3, per1 = (geo[1].total + 7) >> 3;
+    dl.lo0 = min(geo[0].total, xcd * per0);
+    dl.lo1 = min(geo[1].total, xcd * per1);
+    dl.n1 = min(geo[1].total, (xcd + 1) * per1) - dl.lo1;
+    dl.n = dl.n1 + min(geo[0].total, (xcd + 1) * per0) - dl.lo0;
+  } else {
+    const int total = geo[0].total + geo[1].total, per = (total + 7) >> 3;
+    dl.lo0 = min(total, xcd * per);
+    dl.lo1 = 0;
+    dl.n1 = 0;
+    dl.n = min(total, (xcd + 1) * per) - dl.lo0;
+  }
 
   // Consumer: the tile being multiplied (the first one with work; empty ones get zeros).
-  int Lc = xcd * per + (blockIdx.x >> 3);
+  int ic = blockIdx.x >> 3;
   Tile ct;
-  for (;; Lc += nbx) {
-    if (Lc >= L_end) return;
-    ct = decode_tile<MODE>(p, geo, Lc, ksplit);
+  for (;; ic += nbx) {
+    if (ic >= dl.n) return;
+    ct = decode_tile<MODE>(p, geo, tile_at(dl, ic));
     if (ct.nk > 0) break;
-    zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, ksplit, partial);
+    zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
   }
 
   // Prologue: stages 0..3 into slots 0..3, wait for stage 0, read substep 0 of stage 0.
   Producer pr;
   pr.t = ct;
-  pr.L = Lc;
+  pr.i = ic;
   pr.k = 0;
   set_offsets<MODE>(pr, p, wave, lane);
 #pragma unroll 1
   for (int s = 0; s < NSTAGE; ++s) {
     issue_all<MODE, 0>(seg_args(p, pr.t.seg), lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
-    advance<MODE>(pr, p, geo, nbx, L_end, ksplit, wave, lane);
+    advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
   }
   wait_vm<24>();
   barrier();
@@ -898,20 +926,20 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
       const uint32_t sn = ((j + 1) & 3) * STAGE;
       const StageSrc ss = stage_src<MODE>(pr, p, wave);
       phase1<MODE, 0>(acc, a1, b1, a0, b0, fa0 + sn, fb0 + sn, lds + sb, ss, pr.voff, wave, lane);
-      advance<MODE>(pr, p, geo, nbx, L_end, ksplit, wave, lane);
+      advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
       frag_wait(a0, b0);
       ++since_epi;
     }
-    epilogue_tile<MODE>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, ksplit, partial);
+    epilogue_tile<MODE>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
     since_epi = 0;
     bool more = false;
-    for (Lc += nbx; Lc < L_end; Lc += nbx) {
-      ct = decode_tile<MODE>(p, geo, Lc, ksplit);
+    for (ic += nbx; ic < dl.n; ic += nbx) {
+      ct = decode_tile<MODE>(p, geo, tile_at(dl, ic));
       if (ct.nk > 0) {
         more = true;
         break;
       }
-      zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, ksplit, partial);
+      zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
     }
     if (!more) break;
   }
@@ -930,7 +958,7 @@ long long set_tiles(int G, int M, int d, int f, int ksplit) {
 template <int MODE>
 hipError_t launch_pipe(const GemmArgs& p, int ksplit, float* partial, hipStream_t s, int num_cus) {
   long long tiles = set_tiles<MODE>(p.G, p.M, p.d, p.f, ksplit);
-  if (p.nseg == 2) tiles += set_tiles<MODE>(p.s1.G, p.s1.M, p.d, p.s1.f, ksplit);
+  if (p.nseg == 2) tiles += set_tiles<MODE>(p.s1.G, p.s1.M, p.d, p.s1.f, std::max(1, p.s1.ksplit));
   long long grid = std::min<long long>(tiles, (long long)num_cus);
   grid = (grid + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;

@@ -12,12 +12,11 @@ namespace moe {
 namespace {
 
 constexpr int CH_THREADS = 256;
-constexpr int CH_PER_THREAD = 16;
-constexpr int CHUNK = CH_THREADS * CH_PER_THREAD;  // assignments per chunk (4096)
+constexpr int CH_PER_THREAD = 4;
+constexpr int CHUNK = CH_THREADS * CH_PER_THREAD;  // assignments per chunk (1024)
 
 // Pass 1.  Each block ranks the assignments of one chunk among equal experts, in assignment
-// order.  Wave w takes the contiguous quarter [w*1024, (w+1)*1024) of the chunk in 16 steps of
-// 64; inside a step the rank of a lane is the number of lower lanes with the same expert, found
+// order.  Wave w takes the contiguous quarter [w*256, (w+1)*256) of the chunk in 4 steps of 64; inside a step the rank of a lane is the number of lower lanes with the same expert, found
 // from ballots of the expert id's bits.  Afterwards the per-wave counts are prefix-summed so the
 // rank is the chunk-local stable rank.  Writes local_rank[a] and chunk_counts[chunk][E].
 __global__ __launch_bounds__(CH_THREADS) void local_rank_kernel(const int32_t* topk_idx, int Tk,
@@ -81,6 +80,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* chunk_counts, 
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) {
       const int v = chunk_counts[(size_t)c * E + e];
       chunk_base[(size_t)c * E + e] = total;

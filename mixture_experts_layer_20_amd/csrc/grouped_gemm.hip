@@ -648,19 +648,35 @@ __global__ __launch_bounds__(dmak::NTH, 1) void grouped_gemm_bf16_dma(GemmArgs p
   }
 }
 
-// Sum of the split-K partials in split order, written through the weight-gradient epilogue.
+// Sum of the split-K partials in split order, written as bf16 weight gradients (dW2, or dW1/dW3
+// by gradient row).  Each thread sums 8 consecutive columns (16-byte loads, one 16-byte store).
 template <int MODE>
 __global__ __launch_bounds__(256) void splitk_reduce(GemmArgs p, const float* partial, int ksplit) {
   const int Mw = mode_Mw(MODE, p.d, p.f), Nw = mode_N(MODE, p.d, p.f);
   const size_t per_split = (size_t)p.G * Mw * Nw;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < per_split; i += (size_t)gridDim.x * 256) {
-    float s = 0.0f;
-    for (int k = 0; k < ksplit; ++k) s += partial[(size_t)k * per_split + i];
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; i < per_split; i += (size_t)gridDim.x * 256 * 8) {
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < ksplit; ++k) {
+      const float4* src = reinterpret_cast<const float4*>(partial + (size_t)k * per_split + i);
+      const float4 a = src[0], b = src[1];
+      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+      s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+    }
     const int n = (int)(i % Nw);
     const size_t r = i / Nw;
     const int m = (int)(r % Mw);
     const int g = (int)(r / Mw);
-    epilogue<MODE, bf16_t>(p, g, m, n, s, 0.0f);
+    bf16_t* dst;
+    if constexpr (MODE == GEMM_DOWN_WGRAD) {
+      dst = reinterpret_cast<bf16_t*>(p.out0) + ((size_t)g * p.d + m) * p.f + n;
+    } else {
+      const bool up = m >= p.f;
+      dst = reinterpret_cast<bf16_t*>(up ? p.out1 : p.out0) + ((size_t)g * p.f + (up ? m - p.f : m)) * p.d + n;
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f32_to_bf16(s[2 * j]) | ((uint32_t)f32_to_bf16(s[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -822,7 +838,7 @@ hipError_t launch_bf16(const GemmArgs& p, size_t partial_bytes, float* partial, 
   if constexpr (TR::raggedK) {
     if (ksplit > 1) {
       const size_t n = (size_t)p.G * mode_Mw(MODE, p.d, p.f) * mode_N(MODE, p.d, p.f);
-      const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+      const unsigned blocks = (unsigned)std::min<size_t>((n / 8 + 255) / 256, 4096);
       hipLaunchKernelGGL(splitk_reduce<MODE>, dim3(blocks), dim3(256), 0, s, p, partial, ksplit);
       e = hipGetLastError();
     }
@@ -872,7 +888,7 @@ hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float
       hipError_t e = launch_grouped_gemm_pipe(MODE, p, ksplit, partial, s, num_cus());
       if (e != hipSuccess || ksplit <= 1) return e;
       const size_t n = (size_t)p.G * mode_Mw(MODE, p.d, p.f) * mode_N(MODE, p.d, p.f);
-      hipLaunchKernelGGL(splitk_reduce<MODE>, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0,
+      hipLaunchKernelGGL(splitk_reduce<MODE>, dim3((unsigned)std::min<size_t>((n / 8 + 255) / 256, 4096)), dim3(256), 0,
                          s, p, partial, ksplit);
       return hipGetLastError();
     }
@@ -924,9 +940,10 @@ hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float
 size_t gemm_ws_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) / 256 * 256; }
 
 // Split of the second set's row reduction in a two-set weight-gradient launch: chunks about as
-// long as a group of the first set (at least 256 rows), at most 8.
+// long as two groups of the first set (at least 512 rows; the partials cost HBM traffic), at
+// most 8.
 static int sets_split(int G0, long long M0, int G1, long long M1) {
-  const long long rows0 = std::max<long long>(256, G0 > 0 ? M0 / G0 : 0);
+  const long long rows0 = std::max<long long>(512, G0 > 0 ? 2 * (M0 / G0) : 0);
   return (int)std::min<long long>(8, std::max<long long>(1, (M1 / std::max(1, G1) + rows0 - 1) / rows0));
 }
 
@@ -1009,7 +1026,7 @@ hipError_t launch_wgrad_sets(const GemmArgs& p, hipStream_t s) {
   if (e != hipSuccess || ks <= 1) return e;
   const GemmArgs p1 = second_set(p);
   const size_t n = (size_t)p1.G * Mw * N;
-  hipLaunchKernelGGL(splitk_reduce<MODE>, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0, s,
+  hipLaunchKernelGGL(splitk_reduce<MODE>, dim3((unsigned)std::min<size_t>((n / 8 + 255) / 256, 4096)), dim3(256), 0, s,
                      p1, partial, ks);
   return hipGetLastError();
 }

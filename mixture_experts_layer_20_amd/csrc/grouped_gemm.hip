@@ -939,20 +939,23 @@ hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float
 
 size_t gemm_ws_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) / 256 * 256; }
 
-// Split of the second set's row reduction in a two-set weight-gradient launch: chunks about as
-// long as two groups of the first set (at least 512 rows; the partials cost HBM traffic), at
-// most 8.
-static int sets_split(int G0, long long M0, int G1, long long M1) {
-  const long long rows0 = std::max<long long>(512, G0 > 0 ? 2 * (M0 / G0) : 0);
-  return (int)std::min<long long>(8, std::max<long long>(1, (M1 / std::max(1, G1) + rows0 - 1) / rows0));
+// Split of the second set's row reduction in a two-set weight-gradient launch: enough chunks for
+// its tiles to give every CU one (they are dealt first), chunks of at least 512 rows, at most 8.
+static int sets_split(int mode, int G1, long long M1, int d, int f1) {
+  const long long tiles = (long long)G1 * (mode_Mw(mode, d, f1) / 256) * (mode_N(mode, d, f1) / 256);
+  if (tiles <= 0) return 1;
+  long long ks = (num_cus() + tiles - 1) / tiles;
+  ks = std::min<long long>(ks, M1 / std::max(1, G1) / 512);
+  return (int)std::max<long long>(1, std::min<long long>(ks, 8));
 }
 
 size_t gemm_sets_partial_bytes(int G0, long long M0, int G1, long long M1, int d, int f1) {
-  const int ks = sets_split(G0, M0, G1, M1);
-  if (ks <= 1) return 0;
+  (void)G0; (void)M0;
   size_t best = 0;
-  for (int mode : {GEMM_DOWN_WGRAD, GEMM_UP_WGRAD})
-    best = std::max(best, (size_t)ks * G1 * mode_Mw(mode, d, f1) * mode_N(mode, d, f1) * sizeof(float));
+  for (int mode : {GEMM_DOWN_WGRAD, GEMM_UP_WGRAD}) {
+    const int ks = sets_split(mode, G1, M1, d, f1);
+    if (ks > 1) best = std::max(best, (size_t)ks * G1 * mode_Mw(mode, d, f1) * mode_N(mode, d, f1) * sizeof(float));
+  }
   return best;
 }
 
@@ -1018,7 +1021,7 @@ hipError_t launch_wgrad_sets(const GemmArgs& p, hipStream_t s) {
                        : nullptr;
   const size_t pb = partial ? p.ws_bytes - gemm_ws_bytes(p.G) : 0;
   const int Mw = mode_Mw(MODE, p.d, p.s1.f), N = mode_N(MODE, p.d, p.s1.f);
-  int ks = sets_split(p.G, p.M, p.s1.G, p.s1.M);
+  int ks = sets_split(MODE, p.s1.G, p.s1.M, p.d, p.s1.f);
   while (ks > 1 && (size_t)ks * p.s1.G * Mw * N * sizeof(float) > pb) --ks;
   GemmArgs q = p;
   q.s1.ksplit = ks;

@@ -77,9 +77,11 @@ __device__ __forceinline__ int mc_phys_chunk(int k, int chunk) { return chunk ^ 
 
 // ---- Tiles -------------------------------------------------------------------------------
 // Output tile: set seg, group g, rows [m0, min(m0 + 256, m_end)), tile column nt, K range
-// [k_begin, k_end) in nk steps of 32 (split: K chunk index of a split weight gradient).
+// [k_begin, k_end) in nk steps of 32 (split: K chunk index of a split weight gradient; ks: the
+// split count).  half: at most 128 rows remain (ragged M only), multiplied as a 128x256 tile.
 struct Tile {
   int seg, g, m0, m_end, nt, k_begin, k_end, nk, split, ks;
+  bool half;
 };
 
 // The arguments of one set of groups (set 1: the second set of a merged launch), in the layout
@@ -137,6 +139,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
   t.ks = ksplit;
   const uint32_t pref = t.seg ? geo[1].pref : geo[0].pref, offs = t.seg ? geo[1].offs : geo[0].offs;
   t.split = 0;
+  t.half = false;
   if constexpr (!Traits<MODE>::raggedK) {
     const int mt = L / NT;
     t.nt = L - mt * NT;
@@ -150,6 +153,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
     group_rows_lds(offs, t.g, r0, r1);
     t.m0 = r0 + (mt - uniform(lds_load_i32(pref + 4 * t.g))) * BM;
     t.m_end = r1;
+    t.half = r1 - t.m0 <= BM / 2;
     t.k_begin = 0;
     t.k_end = mode_K(MODE, p.d, p.f);
   } else {
@@ -285,11 +289,21 @@ struct StageSrc {
 };
 
 // ---- Fragments ---------------------------------------------------------------------------
+// Tile shapes.  Full tiles: 256x256, waves in a 2x2 grid of 128x128 (4x4 MFMA blocks each).  Half
+// tiles (the last rows of a group when at most 128 remain): 128x256, waves side by side, 128x64
+// each (4x2 blocks); the load stream is the same, the MFMA work halves.  Wave w = wm + 2*wn.
+template <bool HALF> constexpr int nblk_b() { return HALF ? 2 : 4; }
+
 // Row (A) / column (B) of the wave's MFMA block i inside the 256-wide operand tile.
-template <int MODE, bool A_OP>
+template <int MODE, bool A_OP, bool HALF>
 __device__ __forceinline__ int block_row(int wm, int wn, int i) {
   if constexpr (A_OP) {
-    return wm * 128 + 32 * i;
+    return (HALF ? 0 : wm * 128) + 32 * i;
+  } else if constexpr (HALF) {
+    const int w = wm + WGM * wn;
+    // gate/up: the wave's 32 gate (W1) columns in block 0, the same up (W3) columns in block 1
+    if constexpr (MODE == GEMM_UP_FWD) return i == 0 ? w * 32 : 128 + w * 32;
+    else return w * 64 + 32 * i;
   } else if constexpr (MODE == GEMM_UP_FWD) {
     // gate (W1) columns in blocks 0,1 and the same up (W3) columns in blocks 2,3
     return (i < 2) ? wn * 64 + 32 * i : 128 + wn * 64 + 32 * (i - 2);
@@ -304,11 +318,11 @@ __device__ __forceinline__ int block_row(int wm, int wn, int i) {
 //      rows further; the swizzle repeats every 16 rows), applied as the instruction's offset field.
 //  MC: block i is 32 columns = 4 chunks further; with the window swizzle that is an XOR of i into
 //      address bits 6-7.  The second transposed read of a block is 4 k-rows = 2048 bytes further.
-template <int MODE, bool A_OP>
+template <int MODE, bool A_OP, bool HALF>
 __device__ __forceinline__ uint32_t frag_base(int s, int wm, int wn, int lane) {
   constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
   const uint32_t base = A_OP ? 0 : OPB;
-  const int rb = block_row<MODE, A_OP>(wm, wn, 0);
+  const int rb = block_row<MODE, A_OP, HALF>(wm, wn, 0);
   if constexpr (kc) {
     const int row = rb + (lane & 31);
     const int chunk = s * 2 + (lane >> 5);
@@ -324,31 +338,34 @@ __device__ __forceinline__ uint32_t frag_base(int s, int wm, int wn, int lane) {
 }
 
 // Offset of block i relative to block 0 (KC operands), in bytes.
-template <int MODE, bool A_OP>
+template <int MODE, bool A_OP, bool HALF>
 constexpr int kc_block_off(int i) {
-  return A_OP ? 2048 * i
-              : (MODE == GEMM_UP_FWD ? (i < 2 ? 2048 * i : 8192 + 2048 * (i - 2)) : 2048 * i);
+  if (A_OP) return 2048 * i;
+  if (MODE == GEMM_UP_FWD) return HALF ? 8192 * i : (i < 2 ? 2048 * i : 8192 + 2048 * (i - 2));
+  return 2048 * i;
 }
 
-// Fragments of one 16-deep substep, read one instruction at a time (IDX).  KC: 4 reads, one per
-// block.  MC: 8 reads, two per block (4 k each), kept apart until packed for the MFMA.
+// Fragments of one 16-deep substep, read one instruction at a time (IDX).  KC: one read per
+// block.  MC: two reads per block (4 k each), kept apart until packed for the MFMA.
 template <bool KC>
 struct Frag;
 template <>
 struct Frag<true> {
-  static constexpr int NREADS = 4;
+  static constexpr int PER_BLOCK = 1;
   bf16x8_t v[4];
-  template <int MODE, bool A_OP, int IDX>
+  template <int MODE, bool A_OP, bool HALF, int IDX>
   __device__ __forceinline__ void read_one(uint32_t addr) {
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[IDX]) : "v"(addr), "i"(kc_block_off<MODE, A_OP>(IDX)));
+    asm volatile("ds_read_b128 %0, %1 offset:%2"
+                 : "=v"(v[IDX])
+                 : "v"(addr), "i"(kc_block_off<MODE, A_OP, HALF>(IDX)));
   }
   __device__ __forceinline__ bf16x8_t get(int i) const { return v[i]; }
 };
 template <>
 struct Frag<false> {
-  static constexpr int NREADS = 8;
+  static constexpr int PER_BLOCK = 2;
   u32x2_t h[2][4];
-  template <int MODE, bool A_OP, int IDX>
+  template <int MODE, bool A_OP, bool HALF, int IDX>
   __device__ __forceinline__ void read_one(uint32_t addr) {
     constexpr int i = IDX >> 1, r = IDX & 1;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(h[r][i]) : "v"(addr ^ (uint32_t)(i << 6)), "i"(r * 2048));
@@ -378,7 +395,7 @@ __device__ __forceinline__ void frag_wait(Frag<false>& a, Frag<false>& b) {
 }
 
 // ---- K step phases -------------------------------------------------------------------------
-// Slot Q of a phase: MFMA Q (block row Q/4, block column Q%4), then the memory instructions that
+// Slot Q of a phase: MFMA Q (block row Q/NB, block column Q%NB), then the memory instructions that
 // belong to the slot.  The scheduling barriers keep this order: the matrix core always has the
 // next MFMA queued while the wave issues a read or a load.
 template <int MODE>
@@ -386,57 +403,70 @@ using FragA = Frag<Traits<MODE>::a_kcontig>;
 template <int MODE>
 using FragB = Frag<Traits<MODE>::b_kcontig>;
 
+// MFMAs per phase and fragment reads per substep of a shape.
+template <bool HALF> constexpr int nslots() { return MI * nblk_b<HALF>(); }
+template <int MODE, bool HALF>
+constexpr int nreads_a() { return MI * FragA<MODE>::PER_BLOCK; }
+template <int MODE, bool HALF>
+constexpr int nreads_b() { return nblk_b<HALF>() * FragB<MODE>::PER_BLOCK; }
+
 // The B fragment goes in as the MFMA's first operand: the accumulator block is then the
 // transpose of the output block, so each lane ends up with consecutive output columns of one row.
-template <int MODE, int Q>
+template <int MODE, bool HALF, int Q>
 __device__ __forceinline__ void mfma_slot(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a, const FragB<MODE>& b) {
-  constexpr int i = Q >> 2, j = Q & 3;
+  constexpr int NB = nblk_b<HALF>();
+  constexpr int i = Q / NB, j = Q % NB;
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b.get(j), a.get(i), acc[i][j], 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Fragment read R of a substep (A's reads first, then B's).
-template <int MODE, int R>
+template <int MODE, bool HALF, int R>
 __device__ __forceinline__ void read_slot(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
-  constexpr int NRA = FragA<MODE>::NREADS, NRB = FragB<MODE>::NREADS;
-  if constexpr (R < NRA) a.template read_one<MODE, true, R>(ra);
-  else if constexpr (R < NRA + NRB) b.template read_one<MODE, false, R - NRA>(rb);
+  constexpr int NRA = nreads_a<MODE, HALF>(), NRB = nreads_b<MODE, HALF>();
+  if constexpr (R < NRA) a.template read_one<MODE, true, HALF, R>(ra);
+  else if constexpr (R < NRA + NRB) b.template read_one<MODE, false, HALF, R - NRA>(rb);
 }
 
 // Phase 0 of a K step: MFMAs on substep 0 (a0, b0); reads of substep 1 (a1, b1) of the same
 // stage at ra/rb.
-template <int MODE, int Q>
+template <int MODE, bool HALF, int Q>
 __device__ __forceinline__ void phase0(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a0, const FragB<MODE>& b0,
                                        FragA<MODE>& a1, FragB<MODE>& b1, uint32_t ra, uint32_t rb) {
-  if constexpr (Q < 16) {
-    mfma_slot<MODE, Q>(acc, a0, b0);
-    read_slot<MODE, Q>(a1, b1, ra, rb);
+  constexpr int NS = nslots<HALF>(), NR = nreads_a<MODE, HALF>() + nreads_b<MODE, HALF>();
+  if constexpr (Q < NS) {
+    mfma_slot<MODE, HALF, Q>(acc, a0, b0);
+    // reads spread over the slots (two per slot where there are more reads than slots)
+    read_slot<MODE, HALF, Q>(a1, b1, ra, rb);
+    if constexpr (NR > NS) read_slot<MODE, HALF, Q + NS>(a1, b1, ra, rb);
     __builtin_amdgcn_sched_barrier(0);
-    phase0<MODE, Q + 1>(acc, a0, b0, a1, b1, ra, rb);
+    phase0<MODE, HALF, Q + 1>(acc, a0, b0, a1, b1, ra, rb);
   }
 }
 
 // Phase 1: MFMAs on substep 1 (a1, b1); reads of substep 0 (a0, b0) of the next stage at ra/rb;
-// the 8 loads of the stage four steps ahead into this step's slot (slots 8..15).
-template <int MODE, int Q>
+// the 8 loads of the stage four steps ahead into this step's slot (the last 8 slots).
+template <int MODE, bool HALF, int Q>
 __device__ __forceinline__ void phase1(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a1, const FragB<MODE>& b1,
                                        FragA<MODE>& a0, FragB<MODE>& b0, uint32_t ra, uint32_t rb, char* stage,
                                        const StageSrc& ss, const uint32_t (&voff)[8], int wave, int lane) {
-  if constexpr (Q < 16) {
-    mfma_slot<MODE, Q>(acc, a1, b1);
-    read_slot<MODE, Q>(a0, b0, ra, rb);
-    if constexpr (Q >= 8) issue_fast<MODE, Q - 8>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
+  constexpr int NS = nslots<HALF>(), NR = nreads_a<MODE, HALF>() + nreads_b<MODE, HALF>();
+  if constexpr (Q < NS) {
+    mfma_slot<MODE, HALF, Q>(acc, a1, b1);
+    read_slot<MODE, HALF, Q>(a0, b0, ra, rb);
+    if constexpr (NR > NS) read_slot<MODE, HALF, Q + NS>(a0, b0, ra, rb);
+    if constexpr (Q >= NS - 8) issue_fast<MODE, Q - (NS - 8)>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
-    phase1<MODE, Q + 1>(acc, a1, b1, a0, b0, ra, rb, stage, ss, voff, wave, lane);
+    phase1<MODE, HALF, Q + 1>(acc, a1, b1, a0, b0, ra, rb, stage, ss, voff, wave, lane);
   }
 }
 
-// All reads of one substep's fragments (prologue).
-template <int MODE, int R>
+// All reads of one substep's fragments (prologue, start of a tile).
+template <int MODE, bool HALF, int R>
 __device__ __forceinline__ void read_all(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
-  if constexpr (R < FragA<MODE>::NREADS + FragB<MODE>::NREADS) {
-    read_slot<MODE, R>(a, b, ra, rb);
-    read_all<MODE, R + 1>(a, b, ra, rb);
+  if constexpr (R < nreads_a<MODE, HALF>() + nreads_b<MODE, HALF>()) {
+    read_slot<MODE, HALF, R>(a, b, ra, rb);
+    read_all<MODE, HALF, R + 1>(a, b, ra, rb);
   }
 }
 
@@ -571,11 +601,11 @@ __device__ __forceinline__ void store8(const GemmArgs& p, const OutWins& o, int 
   }
 }
 
-// Store instructions every epilogue issues at least (per wave; the optional pre-activation
-// stashes of the gate/up GEMM not counted).
+// Store instructions every epilogue issues at least (per wave, half tiles; the optional
+// pre-activation stashes of the gate/up GEMM not counted).
 template <int MODE>
 constexpr int epilogue_stores() {
-  return MODE == GEMM_UP_FWD ? 16 : (MODE == GEMM_DOWN_BWD ? 64 : 32);
+  return MODE == GEMM_UP_FWD ? 8 : (MODE == GEMM_DOWN_BWD ? 32 : 16);
 }
 
 // Copies of four accumulator registers to VGPRs.  Written out so that each value leaves its AGPR
@@ -629,16 +659,18 @@ __device__ __forceinline__ void wait_aux(AuxBlock& x) {
                : "memory");
 }
 
+// Output blocks per wave row of a shape (the gate/up GEMM pairs a gate block with an up block).
+template <int MODE, bool HALF>
+constexpr int out_nj() { return MODE == GEMM_UP_FWD ? nblk_b<HALF>() / 2 : nblk_b<HALF>(); }
+
 // Window row and column of lane's first output of accumulator block IDX.
-template <int MODE, int IDX>
+template <int MODE, bool HALF, int IDX>
 __device__ __forceinline__ int block_r(int lane) {
-  constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
-  return (IDX / NJ) * 32 + (lane & 31);
+  return (IDX / out_nj<MODE, HALF>()) * 32 + (lane & 31);
 }
-template <int MODE, int IDX>
+template <int MODE, bool HALF, int IDX>
 __device__ __forceinline__ int block_c(int lane) {
-  constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
-  return (IDX % NJ) * 32 + 8 * (lane >> 5);
+  return (IDX % out_nj<MODE, HALF>()) * 32 + 8 * (lane >> 5);
 }
 
 template <int MODE>
@@ -663,41 +695,44 @@ constexpr int aux_younger() {
 // Blocks IDX.. of the wave's accumulators, unrolled at compile time (the loop unroller gives up on
 // the larger epilogues, and a run-time block index would put the accumulators in scratch memory).
 // The down-projection dgrad keeps the pre-activation loads one block ahead of their use.
-template <int MODE, int IDX>
+template <int MODE, bool HALF, int IDX>
 __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& o, const f32x16_t (&acc)[MI][NI],
                                               int row0, int col0, int m_end, int lane, AuxBlock (&aux)[2],
                                               int ksplit) {
-  constexpr int NJ = (MODE == GEMM_UP_FWD) ? NI / 2 : NI;
+  constexpr int NJ = out_nj<MODE, HALF>();
   constexpr int NB = MI * NJ;
   if constexpr (IDX < NB) {
     if constexpr (MODE == GEMM_DOWN_BWD) {
       if constexpr (IDX + 1 < NB)
-        load_aux(p, row0 + block_r<MODE, IDX + 1>(lane), m_end, col0 + block_c<MODE, IDX + 1>(lane),
+        load_aux(p, row0 + block_r<MODE, HALF, IDX + 1>(lane), m_end, col0 + block_c<MODE, HALF, IDX + 1>(lane),
                  aux[(IDX + 1) % 2]);
       wait_aux<aux_younger<IDX, NB>()>(aux[IDX % 2]);
     }
     constexpr int mi = IDX / NJ, ni = IDX % NJ;
-    constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NI / 2 : ni;
-    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, IDX>(lane), block_c<MODE, IDX>(lane),
-                         aux[IDX % 2], ksplit);
-    epilogue_from<MODE, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
+    constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NJ : ni;
+    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, HALF, IDX>(lane),
+                         block_c<MODE, HALF, IDX>(lane), aux[IDX % 2], ksplit);
+    epilogue_from<MODE, HALF, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
   }
 }
 
-template <int MODE>
+template <int MODE, bool HALF>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], const Tile& t,
                                               int wm, int wn, int lane, float* partial) {
   // The accumulator reads are opaque to the hazard checker: leave the last MFMA's write-back
   // (at most 18 wait states) behind before the first of them.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-  const int row0 = t.m0 + wm * 128;
-  const int col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 64 : t.nt * BN + wn * 128;
+  const int w = wm + WGM * wn;
+  const int row0 = t.m0 + (HALF ? 0 : wm * 128);
+  int col0;
+  if constexpr (HALF) col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + w * 32 : t.nt * BN + w * 64;
+  else col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 64 : t.nt * BN + wn * 128;
   const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
   const int ksplit = t.ks;
   AuxBlock aux[2];
   if constexpr (MODE == GEMM_DOWN_BWD)
-    load_aux(p, row0 + block_r<MODE, 0>(lane), t.m_end, col0 + block_c<MODE, 0>(lane), aux[0]);
-  epilogue_from<MODE, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
+    load_aux(p, row0 + block_r<MODE, HALF, 0>(lane), t.m_end, col0 + block_c<MODE, HALF, 0>(lane), aux[0]);
+  epilogue_from<MODE, HALF, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
 }
 
 // Output of a tile with an empty K range (a weight gradient of an expert without tokens): zeros.
@@ -803,6 +838,61 @@ __device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const S
   pr.i = dl.n;
 }
 
+// Per-lane fragment read bases of one tile shape (substeps 0 and 1, both operands).
+struct FragBases {
+  uint32_t a0, a1, b0, b1;
+};
+template <int MODE, bool HALF>
+__device__ __forceinline__ FragBases frag_bases(uint32_t lds0, int wm, int wn, int lane) {
+  FragBases f;
+  f.a0 = lds0 + frag_base<MODE, true, HALF>(0, wm, wn, lane);
+  f.a1 = lds0 + frag_base<MODE, true, HALF>(1, wm, wn, lane);
+  f.b0 = lds0 + frag_base<MODE, false, HALF>(0, wm, wn, lane);
+  f.b1 = lds0 + frag_base<MODE, false, HALF>(1, wm, wn, lane);
+  return f;
+}
+
+// One output tile of shape HALF: its K steps j, j+1, ... and its epilogue.  On entry a0/b0 hold
+// substep 0 of stage j read for this shape; on return, substep 0 of the next stage (the next
+// tile's first) read for this shape.
+template <int MODE, bool HALF>
+__device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& ct, const FragBases& fb, FragA<MODE>& a0,
+                                         FragB<MODE>& b0, FragA<MODE>& a1, FragB<MODE>& b1, int& j,
+                                         int& since_epi, Producer& pr, const SegGeo (&geo)[2], const Deal& dl,
+                                         int nbx, int wm, int wn, int wave, int lane, char* lds, float* partial) {
+  // K steps since the last epilogue.  Its stores are younger than the stage each of the next three
+  // K steps waits for, and at least epilogue_stores() of them were issued, so those steps may
+  // leave that many more operations outstanding.
+  constexpr int VM_AFTER_EPI = 16 + epilogue_stores<MODE>() < 62 ? 16 + epilogue_stores<MODE>() : 62;
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < nblk_b<HALF>(); ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
+  for (int kc = 0; kc < ct.nk; ++kc, ++j) {
+    // Phase 0: substep 0 of stage j; read substep 1.
+    const uint32_t sb = (j & 3) * STAGE;
+    phase0<MODE, HALF, 0>(acc, a0, b0, a1, b1, fb.a1 + sb, fb.b1 + sb);
+    frag_wait(a1, b1);
+    // Stage j+1 has landed once only the loads of stages j+2, j+3 (and any stores issued after
+    // them) are outstanding; the barrier makes every wave's part visible and frees slot j & 3.
+    if (since_epi < 3) wait_vm<VM_AFTER_EPI>();
+    else wait_vm<16>();
+    barrier();
+    // Phase 1: substep 1 of stage j; read substep 0 of stage j+1; load stage j+4 into slot j & 3.
+    const uint32_t sn = ((j + 1) & 3) * STAGE;
+    const StageSrc ss = stage_src<MODE>(pr, p, wave);
+    phase1<MODE, HALF, 0>(acc, a1, b1, a0, b0, fb.a0 + sn, fb.b0 + sn, lds + sb, ss, pr.voff, wave, lane);
+    advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
+    frag_wait(a0, b0);
+    ++since_epi;
+  }
+  epilogue_tile<MODE, HALF>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
+  since_epi = 0;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int ksplit, float* partial) {
   typedef Traits<MODE> TR;
@@ -818,8 +908,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
   const int wm = wave % WGM, wn = wave / WGM;
   const uint32_t lds0 = lds_addr_of(lds);
 
-  const uint32_t fa0 = lds0 + frag_base<MODE, true>(0, wm, wn, lane), fa1 = lds0 + frag_base<MODE, true>(1, wm, wn, lane);
-  const uint32_t fb0 = lds0 + frag_base<MODE, false>(0, wm, wn, lane), fb1 = lds0 + frag_base<MODE, false>(1, wm, wn, lane);
+  const FragBases full = frag_bases<MODE, false>(lds0, wm, wn, lane);
 
   // Per set: clamped group offsets (the clamping of group_rows), tile geometry and, for ragged M,
   // the per-group tile prefix.  Set 1 (if any) follows set 0 in the tile order.
@@ -896,42 +985,38 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
   barrier();
   FragA<MODE> a0, a1;
   FragB<MODE> b0, b1;
-  read_all<MODE, 0>(a0, b0, fa0, fb0);
-  frag_wait(a0, b0);
-
-  // K steps since the last epilogue.  Its stores are younger than the stage each of the next three
-  // K steps waits for, and at least epilogue_stores() of them were issued, so those steps may
-  // leave that many more operations outstanding.
-  constexpr int VM_AFTER_EPI = 16 + epilogue_stores<MODE>() < 62 ? 16 + epilogue_stores<MODE>() : 62;
   int j = 0, since_epi = 3;
+  if constexpr (TR::raggedK) {
+    read_all<MODE, false, 0>(a0, b0, full.a0, full.b0);
+    frag_wait(a0, b0);
+  }
+  // Ragged M: half tiles have their own fragment bases; after a tile, the substep-0 fragments of
+  // the next stage were read for that tile's shape and are read again when the shape changes.
+  const FragBases hb = frag_bases<MODE, true>(lds0, wm, wn, lane);
+  bool fr_half = !ct.half;
   for (;;) {
-    f32x16_t acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int jj = 0; jj < NI; ++jj)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
-    for (int kc = 0; kc < ct.nk; ++kc, ++j) {
-      // Phase 0: substep 0 of stage j; read substep 1.
-      const uint32_t sb = (j & 3) * STAGE;
-      phase0<MODE, 0>(acc, a0, b0, a1, b1, fa1 + sb, fb1 + sb);
-      frag_wait(a1, b1);
-      // Stage j+1 has landed once only the loads of stages j+2, j+3 (and any stores issued after
-      // them) are outstanding; the barrier makes every wave's part visible and frees slot j & 3.
-      if (since_epi < 3) wait_vm<VM_AFTER_EPI>();
-      else wait_vm<16>();
-      barrier();
-      // Phase 1: substep 1 of stage j; read substep 0 of stage j+1; load stage j+4 into slot j & 3.
-      const uint32_t sn = ((j + 1) & 3) * STAGE;
-      const StageSrc ss = stage_src<MODE>(pr, p, wave);
-      phase1<MODE, 0>(acc, a1, b1, a0, b0, fa0 + sn, fb0 + sn, lds + sb, ss, pr.voff, wave, lane);
-      advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
-      frag_wait(a0, b0);
-      ++since_epi;
+    if constexpr (TR::raggedK) {
+      run_tile<MODE, false>(p, ct, full, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
+                            partial);
+    } else if (ct.half) {
+      if (!fr_half) {
+        const uint32_t sb = (j & 3) * STAGE;
+        read_all<MODE, true, 0>(a0, b0, hb.a0 + sb, hb.b0 + sb);
+        frag_wait(a0, b0);
+      }
+      run_tile<MODE, true>(p, ct, hb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
+                           partial);
+      fr_half = true;
+    } else {
+      if (fr_half) {
+        const uint32_t sb = (j & 3) * STAGE;
+        read_all<MODE, false, 0>(a0, b0, full.a0 + sb, full.b0 + sb);
+        frag_wait(a0, b0);
+      }
+      run_tile<MODE, false>(p, ct, full, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
+                            partial);
+      fr_half = false;
     }
-    epilogue_tile<MODE>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
-    since_epi = 0;
     bool more = false;
     for (ic += nbx; ic < dl.n; ic += nbx) {
       ct = decode_tile<MODE>(p, geo, tile_at(dl, ic));

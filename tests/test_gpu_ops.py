@@ -153,7 +153,24 @@ def test_grouped_mlp_fwd_bwd(dtype, shape):
     log(f"grouped mlp {dtype} M={M} G={G} d={d} f={f} empty={empties}")
     rng = np.random.default_rng(M + G)
     off = ragged_offsets(M, G, rng, empties)
-    P = mlp_problem(M, G, d, f, dtype, M * 7 + d)
+    check_grouped_mlp(dtype, off, d, f, empties, M * 7 + d)
+
+
+# Group sizes whose last row tiles hold 128 rows or fewer (multiplied as 128-row tiles) next to
+# groups whose last tiles are longer, exactly one tile, a single row, and empty.
+TAIL_SIZES = [512, 513, 768, 1, 640, 0, 385, 1000, 384, 129]
+
+
+@pytest.mark.parametrize("f", [256, 512])
+def test_grouped_mlp_tile_tails(f):
+    off = np.concatenate([[0], np.cumsum(TAIL_SIZES)]).astype(np.int32)
+    log(f"grouped mlp tile tails bf16 sizes={TAIL_SIZES} f={f}")
+    check_grouped_mlp("bf16", off, 256, f, (5,), 11)
+
+
+def check_grouped_mlp(dtype, off, d, f, empties, seed):
+    G, M = len(off) - 1, int(off[-1])
+    P = mlp_problem(M, G, d, f, dtype, seed)
     dtc = DT[dtype]
     dev = {k: dev_tensor(v, dtype) for k, v in P.items()}
     offs = i32(off)

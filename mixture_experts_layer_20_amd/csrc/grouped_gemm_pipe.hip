@@ -104,10 +104,10 @@ __device__ __forceinline__ GemmArgs seg_args(const GemmArgs& p, int seg) {
   return q;
 }
 
-// Tile geometry of one set: tile columns, weight-gradient row tiles, split, tiles, and the LDS
-// tables (clamped group offsets, per-group tile prefix).
+// Tile geometry of one set: tile columns, weight-gradient row tiles, split, tiles, the row-tile
+// band of the tile order, and the LDS tables (clamped group offsets, per-group tile prefix).
 struct SegGeo {
-  int NT, MT, ks, total;
+  int NT, MT, ks, total, band;
   uint32_t offs, pref;
 };
 
@@ -141,17 +141,27 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
   t.split = 0;
   t.half = false;
   if constexpr (!Traits<MODE>::raggedK) {
-    const int mt = L / NT;
-    t.nt = L - mt * NT;
+    // Tile order: group by group; inside a group, bands of `band` row tiles, and inside a band
+    // column by column.  A band spans about as many tiles as an XCD runs at once, so the tiles
+    // that read one weight tile run together, and a band cut by that window re-reads activation
+    // rows rather than a whole expert's weights.
     int lo = 0, hi = p.G;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (uniform(lds_load_i32(pref + 4 * mid)) <= mt) lo = mid; else hi = mid;
+      if (uniform(lds_load_i32(pref + 4 * mid)) * NT <= L) lo = mid; else hi = mid;
     }
     t.g = lo;
+    const int p0 = uniform(lds_load_i32(pref + 4 * t.g)), p1 = uniform(lds_load_i32(pref + 4 * (t.g + 1)));
+    const int MB = t.seg ? geo[1].band : geo[0].band;
+    const int l = L - p0 * NT;
+    const int b = l / (MB * NT);
+    const int mb = min(MB, p1 - p0 - b * MB);
+    const int r = l - b * MB * NT;
+    t.nt = r / mb;
+    const int mt = b * MB + (r - t.nt * mb);
     int r0, r1;
     group_rows_lds(offs, t.g, r0, r1);
-    t.m0 = r0 + (mt - uniform(lds_load_i32(pref + 4 * t.g))) * BM;
+    t.m0 = r0 + mt * BM;
     t.m_end = r1;
     t.half = r1 - t.m0 <= BM / 2;
     t.k_begin = 0;
@@ -445,7 +455,7 @@ __device__ __forceinline__ void phase0(f32x16_t (&acc)[MI][NI], const FragA<MODE
 }
 
 // Phase 1: MFMAs on substep 1 (a1, b1); reads of substep 0 (a0, b0) of the next stage at ra/rb;
-// the 8 loads of the stage four steps ahead into this step's slot (the last 8 slots).
+// the 8 loads of the stage four steps ahead into this step's slot, spread over the phase.
 template <int MODE, bool HALF, int Q>
 __device__ __forceinline__ void phase1(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a1, const FragB<MODE>& b1,
                                        FragA<MODE>& a0, FragB<MODE>& b0, uint32_t ra, uint32_t rb, char* stage,
@@ -455,7 +465,8 @@ __device__ __forceinline__ void phase1(f32x16_t (&acc)[MI][NI], const FragA<MODE
     mfma_slot<MODE, HALF, Q>(acc, a1, b1);
     read_slot<MODE, HALF, Q>(a0, b0, ra, rb);
     if constexpr (NR > NS) read_slot<MODE, HALF, Q + NS>(a0, b0, ra, rb);
-    if constexpr (Q >= NS - 8) issue_fast<MODE, Q - (NS - 8)>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
+    // one load every NS/8 slots: a burst of direct loads stalls the issuing wave
+    if constexpr (Q % (NS / 8) == 0) issue_fast<MODE, Q / (NS / 8)>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     phase1<MODE, HALF, Q + 1>(acc, a1, b1, a0, b0, ra, rb, stage, ss, voff, wave, lane);
   }
@@ -518,17 +529,6 @@ __device__ __forceinline__ u32x4_t pack8_bf16(const float (&x)[8]) {
   const u32x4_t w = {a.x, a.y, b.x, b.y};
   return w;
 }
-__device__ __forceinline__ void st_bf16x8(const OutWin& w, int r, int c, const float (&x)[8]) {
-  __builtin_amdgcn_raw_buffer_store_b128(pack8_bf16(x), w.r, (int)(r * w.row_bytes) + c * 2, 0, 0);
-}
-__device__ __forceinline__ void st_f32x8(const OutWin& w, int r, int c, const float (&x)[8]) {
-  const u32x4_t lo = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-  const u32x4_t hi = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
-  const int off = (int)(r * w.row_bytes) + c * 4;
-  __builtin_amdgcn_raw_buffer_store_b128(lo, w.r, off, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b128(hi, w.r, off + 16, 0, 0);
-}
-
 // The output windows of one wave's 128x128 block of a tile.
 struct OutWins {
   OutWin w[3];
@@ -562,42 +562,100 @@ __device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, in
   return o;
 }
 
-// Stashed pre-activations (a, b) of the down-projection dgrad for 8 consecutive columns.
-struct Aux8 {
-  u32x4_t a, b;
+// Output layout of a 32x32 accumulator block after block_half: lane l holds row l % 32, and for
+// half H the 8 columns 16H + 8*(l/32) + 0..7, so a store of 16 bytes per lane covers 32 rows with
+// 32 contiguous bytes each, which the CU's store path takes at a quarter of its rate for rows of
+// 64 bytes or more.  Exchanging lane groups (v_permlane16_swap, one per dword) between the two
+// 16-byte pieces a, b of each lane turns them into r0, covering rows 0..15, and r1, rows 16..31,
+// four lanes and 64 contiguous bytes per row: lane l then holds row l % 16 (+16 in r1), piece
+// (l/16) % 2 of lane (l % 16) + 32*(l/32).  The exchange is its own inverse.
+__device__ __forceinline__ void swap16(const u32x4_t& a, const u32x4_t& b, u32x4_t& r0, u32x4_t& r1) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a[e], b[e], false, false);
+    r0[e] = r[0];
+    r1[e] = r[1];
+  }
+}
+// Column offset (elements) of lane's 16 bytes in the exchanged layout: bf16 pieces are the two
+// halves of the block (8 columns each), fp32 pieces the two quarters of one half (4 columns).
+__device__ __forceinline__ int xcol_bf16(int lane) { return 16 * ((lane >> 4) & 1) + 8 * (lane >> 5); }
+__device__ __forceinline__ int xcol_f32(int lane) { return 4 * ((lane >> 4) & 1) + 8 * (lane >> 5); }
+
+// Store two packed pieces (the lane's halves H = 0, 1 of a block) as rows rl and rl + 16 at
+// column cl of the exchanged layout.
+__device__ __forceinline__ void st_pair(const OutWin& w, int rl, int cl, int esize, const u32x4_t& a,
+                                        const u32x4_t& b) {
+  u32x4_t r0, r1;
+  swap16(a, b, r0, r1);
+  const int off = (int)(rl * w.row_bytes) + cl * esize;
+  __builtin_amdgcn_raw_buffer_store_b128(r0, w.r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(r1, w.r, off + 16 * (int)w.row_bytes, 0, 0);
+}
+__device__ __forceinline__ void st_pair_bf16(const OutWin& w, int rl, int cl, const float (&x)[2][8]) {
+  st_pair(w, rl, cl, 2, pack8_bf16(x[0]), pack8_bf16(x[1]));
+}
+__device__ __forceinline__ u32x4_t bits4(float a, float b, float c, float d) {
+  const u32x4_t r = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+  return r;
+}
+
+// Stashed pre-activations (a, b) of the down-projection dgrad for one block, as loaded: rows 0..15
+// (a0, b0) and 16..31 (a1, b1) of the exchanged layout.
+struct AuxBlock {
+  u32x4_t a0, a1, b0, b1;
 };
 
-// Store 8 consecutive outputs (window row r, columns c..c+7) of the mode; u holds the
-// up-projection values of the gate/up GEMM, x the stashed pre-activations of the down-projection
-// dgrad.
+// Store one 32x32 output block (rows br.., columns bc.. of the wave's window) of the mode: v holds
+// the lane's two halves of the accumulator block, u the up-projection halves of the gate/up GEMM,
+// x the stashed pre-activations of the down-projection dgrad.
 template <int MODE>
-__device__ __forceinline__ void store8(const GemmArgs& p, const OutWins& o, int r, int c, const float (&v)[8],
-                                       const float (&u)[8], const Aux8& x, int ksplit) {
+__device__ __forceinline__ void store_block(const GemmArgs& p, const OutWins& o, int br, int bc, const float (&v)[2][8],
+                                            const float (&u)[2][8], const AuxBlock& x, int ksplit, int lane) {
+  const int rl = br + (lane & 15);
+  const int cl = bc + xcol_bf16(lane);
   if constexpr (MODE == GEMM_UP_FWD) {
-    float h[8];
+    float h[2][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = v[i] * fast_sigmoid(v[i]) * u[i];
-    if (p.out0) st_bf16x8(o.w[0], r, c, v);
-    if (p.out1) st_bf16x8(o.w[1], r, c, u);
-    st_bf16x8(o.w[2], r, c, h);
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[hh][i] = v[hh][i] * fast_sigmoid(v[hh][i]) * u[hh][i];
+    if (p.out0) st_pair_bf16(o.w[0], rl, cl, v);
+    if (p.out1) st_pair_bf16(o.w[1], rl, cl, u);
+    st_pair_bf16(o.w[2], rl, cl, h);
   } else if constexpr (MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD) {
-    st_bf16x8(o.w[0], r, c, v);
+    st_pair_bf16(o.w[0], rl, cl, v);
   } else if constexpr (MODE == GEMM_DOWN_BWD) {
-    const uint32_t aw[4] = {x.a.x, x.a.y, x.a.z, x.a.w}, bw[4] = {x.b.x, x.b.y, x.b.z, x.b.w};
-    float da[8], db[8];
+    // back to the accumulator layout: halves 0 and 1 of a and b
+    u32x4_t ah[2], bh[2];
+    swap16(x.a0, x.a1, ah[0], ah[1]);
+    swap16(x.b0, x.b1, bh[0], bh[1]);
+    u32x4_t pa[2], pb[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a = (i & 1) ? bf16_hi(aw[i >> 1]) : bf16_lo(aw[i >> 1]);
-      const float b = (i & 1) ? bf16_hi(bw[i >> 1]) : bf16_lo(bw[i >> 1]);
-      const float s = fast_sigmoid(a);
-      da[i] = v[i] * b * s * (1.0f + a * (1.0f - s));
-      db[i] = v[i] * a * s;
+    for (int hh = 0; hh < 2; ++hh) {
+      float da[8], db[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float a = (i & 1) ? bf16_hi(ah[hh][i >> 1]) : bf16_lo(ah[hh][i >> 1]);
+        const float b = (i & 1) ? bf16_hi(bh[hh][i >> 1]) : bf16_lo(bh[hh][i >> 1]);
+        const float s = fast_sigmoid(a);
+        da[i] = v[hh][i] * b * s * (1.0f + a * (1.0f - s));
+        db[i] = v[hh][i] * a * s;
+      }
+      pa[hh] = pack8_bf16(da);
+      pb[hh] = pack8_bf16(db);
     }
-    st_bf16x8(o.w[0], r, c, da);
-    st_bf16x8(o.w[0], r, p.f + c, db);
+    st_pair(o.w[0], rl, cl, 2, pa[0], pa[1]);
+    st_pair(o.w[0], rl, p.f + cl, 2, pb[0], pb[1]);
   } else {  // weight gradients
-    if (ksplit > 1) st_f32x8(o.w[0], r, c, v);
-    else st_bf16x8(o.w[0], r, c, v);
+    if (ksplit > 1) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        st_pair(o.w[0], rl, bc + 16 * hh + xcol_f32(lane), 4, bits4(v[hh][0], v[hh][1], v[hh][2], v[hh][3]),
+                bits4(v[hh][4], v[hh][5], v[hh][6], v[hh][7]));
+    } else {
+      st_pair_bf16(o.w[0], rl, cl, v);
+    }
   }
 }
 
@@ -635,54 +693,47 @@ __device__ __forceinline__ void block_half(const f32x16_t& c, int h, float (&x)[
   }
 }
 
-// Pre-activations of block rows/columns for the down-projection dgrad, loaded with inline assembly
-// and waited for explicitly: a compiler-tracked load would be preceded and followed by waits that
-// drain the load stream of the next tile.  Row clamped into the group.
-struct AuxBlock {
-  Aux8 h[2];
-};
-__device__ __forceinline__ void load_aux(const GemmArgs& p, int row, int m_end, int col, AuxBlock& x) {
-  const size_t base = (size_t)min(row, m_end - 1) * p.f + col;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const bf16_t* pa = reinterpret_cast<const bf16_t*>(p.aux0) + base + 16 * h;
-    const bf16_t* pb = reinterpret_cast<const bf16_t*>(p.aux1) + base + 16 * h;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.h[h].a) : "v"(pa) : "memory");
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.h[h].b) : "v"(pb) : "memory");
-  }
+// Pre-activations of one block for the down-projection dgrad, loaded in the exchanged layout
+// (64 contiguous bytes per row) with inline assembly and waited for explicitly: a compiler-tracked
+// load would be preceded and followed by waits that drain the load stream of the next tile.  Rows
+// clamped into the group.
+__device__ __forceinline__ void load_aux(const GemmArgs& p, int row, int m_end, int col, AuxBlock& x, int lane) {
+  const int rl = row + (lane & 15), cl = col + xcol_bf16(lane);
+  const size_t e0 = (size_t)min(rl, m_end - 1) * p.f + cl, e1 = (size_t)min(rl + 16, m_end - 1) * p.f + cl;
+  const bf16_t* a = reinterpret_cast<const bf16_t*>(p.aux0);
+  const bf16_t* b = reinterpret_cast<const bf16_t*>(p.aux1);
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.a0) : "v"(a + e0) : "memory");
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.a1) : "v"(a + e1) : "memory");
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.b0) : "v"(b + e0) : "memory");
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x.b1) : "v"(b + e1) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_aux(AuxBlock& x) {
-  asm volatile("s_waitcnt vmcnt(%4)"
-               : "+v"(x.h[0].a), "+v"(x.h[0].b), "+v"(x.h[1].a), "+v"(x.h[1].b)
-               : "n"(N)
-               : "memory");
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(x.a0), "+v"(x.a1), "+v"(x.b0), "+v"(x.b1) : "n"(N) : "memory");
 }
 
 // Output blocks per wave row of a shape (the gate/up GEMM pairs a gate block with an up block).
 template <int MODE, bool HALF>
 constexpr int out_nj() { return MODE == GEMM_UP_FWD ? nblk_b<HALF>() / 2 : nblk_b<HALF>(); }
 
-// Window row and column of lane's first output of accumulator block IDX.
+// Window row and column of accumulator block IDX.
 template <int MODE, bool HALF, int IDX>
-__device__ __forceinline__ int block_r(int lane) {
-  return (IDX / out_nj<MODE, HALF>()) * 32 + (lane & 31);
-}
+constexpr int block_r() { return (IDX / out_nj<MODE, HALF>()) * 32; }
 template <int MODE, bool HALF, int IDX>
-__device__ __forceinline__ int block_c(int lane) {
-  return (IDX % out_nj<MODE, HALF>()) * 32 + 8 * (lane >> 5);
-}
+constexpr int block_c() { return (IDX % out_nj<MODE, HALF>()) * 32; }
 
 template <int MODE>
 __device__ __forceinline__ void epilogue_block(const GemmArgs& p, const OutWins& o, const f32x16_t& c,
-                                               const f32x16_t& cu, int r, int cc, const AuxBlock& x, int ksplit) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float v[8], u[8];
-    block_half(c, h, v);
-    if constexpr (MODE == GEMM_UP_FWD) block_half(cu, h, u);
-    store8<MODE>(p, o, r, cc + 16 * h, v, u, x.h[h], ksplit);
+                                               const f32x16_t& cu, int br, int bc, const AuxBlock& x, int ksplit,
+                                               int lane) {
+  float v[2][8], u[2][8];
+  block_half(c, 0, v[0]);
+  block_half(c, 1, v[1]);
+  if constexpr (MODE == GEMM_UP_FWD) {
+    block_half(cu, 0, u[0]);
+    block_half(cu, 1, u[1]);
   }
+  store_block<MODE>(p, o, br, bc, v, u, x, ksplit, lane);
 }
 
 // Memory instructions issued after the pre-activation loads of block IDX and before the wait for
@@ -704,14 +755,14 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& 
   if constexpr (IDX < NB) {
     if constexpr (MODE == GEMM_DOWN_BWD) {
       if constexpr (IDX + 1 < NB)
-        load_aux(p, row0 + block_r<MODE, HALF, IDX + 1>(lane), m_end, col0 + block_c<MODE, HALF, IDX + 1>(lane),
-                 aux[(IDX + 1) % 2]);
+        load_aux(p, row0 + block_r<MODE, HALF, IDX + 1>(), m_end, col0 + block_c<MODE, HALF, IDX + 1>(),
+                 aux[(IDX + 1) % 2], lane);
       wait_aux<aux_younger<IDX, NB>()>(aux[IDX % 2]);
     }
     constexpr int mi = IDX / NJ, ni = IDX % NJ;
     constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NJ : ni;
-    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, HALF, IDX>(lane),
-                         block_c<MODE, HALF, IDX>(lane), aux[IDX % 2], ksplit);
+    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, HALF, IDX>(), block_c<MODE, HALF, IDX>(),
+                         aux[IDX % 2], ksplit, lane);
     epilogue_from<MODE, HALF, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
   }
 }
@@ -731,7 +782,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
   const int ksplit = t.ks;
   AuxBlock aux[2];
   if constexpr (MODE == GEMM_DOWN_BWD)
-    load_aux(p, row0 + block_r<MODE, HALF, 0>(lane), t.m_end, col0 + block_c<MODE, HALF, 0>(lane), aux[0]);
+    load_aux(p, row0 + block_r<MODE, HALF, 0>(), t.m_end, col0 + block_c<MODE, HALF, 0>(), aux[0], lane);
   epilogue_from<MODE, HALF, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
 }
 
@@ -739,18 +790,15 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
 template <int MODE>
 __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int wm, int wn, int lane,
                                           float* partial) {
-  const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const Aux8 zx = {};
+  const float z[2][8] = {};
+  const AuxBlock zx = {};
   const int row0 = t.m0 + wm * 128, col0 = t.nt * BN + wn * 128;
   const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
   const int ksplit = t.ks;
 #pragma unroll 1
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll 1
-    for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        store8<MODE>(p, o, mi * 32 + (lane & 31), ni * 32 + 8 * (lane >> 5) + 16 * h, z, z, zx, ksplit);
+    for (int ni = 0; ni < NI; ++ni) store_block<MODE>(p, o, mi * 32, ni * 32, z, z, zx, ksplit, lane);
 }
 
 // Per-group tile prefix (ragged-M modes): pref[g] = 256-row tiles of the groups before g, from
@@ -928,6 +976,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     geo[sg].NT = mode_N(MODE, p.d, f) / BN;
     geo[sg].MT = TR::raggedK ? mode_Mw(MODE, p.d, f) / BM : 0;
     geo[sg].ks = sg ? max(1, p.s1.ksplit) : ksplit;
+    geo[sg].band = max(1, (int)(gridDim.x >> 3) / geo[sg].NT);
     if (sg == 1 && !two) {
       geo[sg].total = 0;
     } else if constexpr (!TR::raggedK) {

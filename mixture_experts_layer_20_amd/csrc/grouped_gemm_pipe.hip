@@ -121,6 +121,15 @@ __device__ __forceinline__ int tile_at(const Deal& dl, int i) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A pointer that is the same in every lane, kept in scalar registers (the compiler cannot always
+// tell, and then addresses it per lane or loops over the lanes for a buffer resource).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (T*)(uintptr_t)((hi << 32) | lo);
+}
 
 // Group row range from the clamped offsets kept in LDS (the clamping of group_rows).
 __device__ __forceinline__ void group_rows_lds(uint32_t offs, int g, int& lo, int& hi) {
@@ -517,9 +526,9 @@ struct OutWin {
 };
 __device__ __forceinline__ OutWin out_win(const void* base, size_t elem_off, int rows, int row_elems, int esize) {
   OutWin w;
-  w.row_bytes = (uint32_t)(row_elems * esize);
-  char* b = const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * esize;
-  w.r = __builtin_amdgcn_make_buffer_rsrc(b, 0, max(rows, 0) * (int)w.row_bytes, 0x00020000);
+  w.row_bytes = (uint32_t)uniform(row_elems * esize);
+  char* b = uniform_ptr(const_cast<char*>(reinterpret_cast<const char*>(base)) + elem_off * esize);
+  w.r = __builtin_amdgcn_make_buffer_rsrc(b, 0, uniform(max(rows, 0) * (int)w.row_bytes), 0x00020000);
   return w;
 }
 // 8 fp32 values to packed bf16 (16 bytes).
@@ -863,6 +872,8 @@ __device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs
   const int k0 = pr.t.k_begin + pr.k * BKS;
   ss.k_left = pr.t.k_end - k0;
   stage_bases<MODE>(seg_args(p, pr.t.seg), pr.t, k0, wave, ss.sa, ss.sb);
+  ss.sa = uniform_ptr(ss.sa);
+  ss.sb = uniform_ptr(ss.sb);
   return ss;
 }
 

@@ -72,7 +72,47 @@ __global__ __launch_bounds__(CH_THREADS) void local_rank_kernel(const int32_t* t
   }
 }
 
-// Pass 2.  One block: counts, offsets, and the first row of every (chunk, expert) pair.
+// Pass 2.  One block: counts, offsets, and the first row of every (chunk, expert) pair.  The
+// chunk counts are staged in LDS ([chunk][expert]), each expert's column is prefix-summed by one
+// thread, the expert totals by the block, and the results go back out in one coalesced pass.
+constexpr int SCAN_THREADS = 1024;
+constexpr int SCAN_LDS = 12288;   // staged counts (ints); larger problems take the plain scan
+__global__ __launch_bounds__(SCAN_THREADS) void scan_lds_kernel(const int32_t* chunk_counts, int nch, int E,
+                                                                 int Tk, int32_t* counts, int32_t* offsets,
+                                                                 int32_t* chunk_base) {
+  __shared__ int cc[SCAN_LDS];
+  __shared__ int tot[SCAN_THREADS];
+  const int tid = threadIdx.x, n = nch * E;
+  for (int i = tid; i < n; i += SCAN_THREADS) cc[i] = chunk_counts[i];
+  __syncthreads();
+  int total = 0;
+  if (tid < E) {
+    for (int c = 0; c < nch; ++c) {
+      const int v = cc[c * E + tid];
+      cc[c * E + tid] = total;
+      total += v;
+    }
+  }
+  tot[tid] = total;
+  __syncthreads();
+  for (int off = 1; off < SCAN_THREADS; off <<= 1) {
+    const int v = tid >= off ? tot[tid - off] : 0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = tot[tid] - total;
+  }
+  if (tid == 0) offsets[E] = Tk;
+  for (int i = tid; i < n; i += SCAN_THREADS) {
+    const int e = i % E;
+    chunk_base[i] = cc[i] + (e > 0 ? tot[e - 1] : 0);
+  }
+}
+
+// The same for any size, with the counts left in global memory.
 __global__ __launch_bounds__(256) void scan_kernel(const int32_t* chunk_counts, int nch, int E,
                                                    int Tk, int32_t* counts, int32_t* offsets,
                                                    int32_t* chunk_base) {
@@ -233,8 +273,12 @@ hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int d, 
   if (Tk > 0)
     hipLaunchKernelGGL(local_rank_kernel, dim3(nch), dim3(CH_THREADS), 0, s, topk_idx, Tk, E, nbits,
                        local_rank, chunk_counts);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, Tk, counts, offsets,
-                     chunk_base);
+  if ((long long)nch * E <= SCAN_LDS && E <= SCAN_THREADS)
+    hipLaunchKernelGGL(scan_lds_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, chunk_counts, nch, E, Tk, counts,
+                       offsets, chunk_base);
+  else
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, Tk, counts, offsets,
+                       chunk_base);
   if (Tk > 0) {
     if (bf16)
       hipLaunchKernelGGL(scatter_gather_kernel<bf16_t>, dim3(ceil_div(Tk, 8)), dim3(256), 0, s,

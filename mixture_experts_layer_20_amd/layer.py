@@ -189,13 +189,16 @@ class MoELayer:
             dx_router = b["dx_router"]
         ws = b["ws_bwd"]
         sets = self._sets(dout)
+        # Each activation gradient is consumed right after it is produced, while it still sits in
+        # the last-level cache (dA/dB by the gate/up dgrad, dX_perm by the permute backward); the
+        # weight gradients, which nothing downstream reads, go last.
         self._gemm("down_bwd", L.MOE_STAGE_DOWN_BWD, sets, ws)
-        self._gemm("down_wgrad", L.MOE_STAGE_DOWN_WGRAD, sets, ws)
         self._gemm("gate_up_dgrad", L.MOE_STAGE_GATE_UP_DGRAD, sets, ws)
-        self._gemm("gate_up_wgrad", L.MOE_STAGE_GATE_UP_WGRAD, sets, ws)
         dx_shared = b["dx_shared"] if fs > 0 else None
         self._stage("permute_bwd", L.moe_permute_bwd, b["dx_perm"], b["dest_pos"], dx_shared, dx_router, T, d,
                     k, dt, b["dx"])
+        self._gemm("down_wgrad", L.MOE_STAGE_DOWN_WGRAD, sets, ws)
+        self._gemm("gate_up_wgrad", L.MOE_STAGE_GATE_UP_WGRAD, sets, ws)
         return b["dx"]
 
     def step(self):

@@ -7,8 +7,9 @@ Inputs (all written by rocprofv3 with --output-format csv):
 The bench run must include `--copy-probe-mb N`: one plain device copy of N MiB whose counter
 readings calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) to bytes.
 
-Each grouped-GEMM kernel runs twice per layer step (routed experts, then the shared expert, in the
-same stage order), so the i-th dispatch of a kernel within a step is labelled by that order.
+Each GEMM stage of a layer step is one launch covering the routed experts and the shared expert
+(--sets-per-stage 1, the default), or two launches, routed then shared (--sets-per-stage 2, a
+bench run with --no-merge); dispatches are labelled by that order.
 
 Usage:
   python -m mixture_experts_layer_20_amd.rocprof_summary --trace T --fetch F --write W \
@@ -57,8 +58,9 @@ def gemm_mode(name: str) -> str | None:
     return MODES[int(m.group(1))] if m else None
 
 
-def labelled_dispatches(rows, name_key, id_key):
-    """Label GEMM dispatches 'routed'/'shared' by their order within a step."""
+def labelled_dispatches(rows, name_key, id_key, sets_per_stage=1):
+    """Label GEMM dispatches by expert set: 'routed+shared' (one launch per stage) or
+    'routed'/'shared' by their order within a step."""
     seen = collections.Counter()
     out = []
     for r in sorted(rows, key=lambda r: int(r[id_key])):
@@ -66,7 +68,7 @@ def labelled_dispatches(rows, name_key, id_key):
         mode = gemm_mode(n)
         label = None
         if mode:
-            label = ("routed", "shared")[seen[n] % 2]
+            label = "routed+shared" if sets_per_stage == 1 else ("routed", "shared")[seen[n] % 2]
             seen[n] += 1
         out.append((r, mode, label))
     return out
@@ -80,10 +82,10 @@ def copy_scale(pmc_csv: str, counter: str, copy_mb: int) -> float | None:
     return copy_mb * 1024.0 / (sum(vals) / len(vals))
 
 
-def per_stage_counter(pmc_csv: str, counter: str):
+def per_stage_counter(pmc_csv: str, counter: str, sets_per_stage: int):
     rows = [r for r in csv.DictReader(open(pmc_csv)) if r["Counter_Name"] == counter]
     acc = collections.defaultdict(list)
-    for r, mode, label in labelled_dispatches(rows, "Kernel_Name", "Dispatch_Id"):
+    for r, mode, label in labelled_dispatches(rows, "Kernel_Name", "Dispatch_Id", sets_per_stage):
         if mode:
             acc[(mode, label)].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
@@ -99,21 +101,22 @@ def main(argv=None) -> int:
     ap.add_argument("--command", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json")
+    ap.add_argument("--sets-per-stage", type=int, choices=(1, 2), default=1)
     a = ap.parse_args(argv)
 
     stats = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_stats.csv"))))
     trace = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_trace.csv"))))
     # per-stage durations from the trace
     durs = collections.defaultdict(list)
-    for r, mode, label in labelled_dispatches(trace, "Kernel_Name", "Dispatch_Id"):
+    for r, mode, label in labelled_dispatches(trace, "Kernel_Name", "Dispatch_Id", a.sets_per_stage):
         if mode:
             durs[(mode, label)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     fcsv = os.path.join(a.fetch, "run_counter_collection.csv")
     wcsv = os.path.join(a.write, "run_counter_collection.csv")
     fs = copy_scale(fcsv, "FETCH_SIZE", a.copy_mb)
     ws = copy_scale(wcsv, "WRITE_SIZE", a.copy_mb)
-    fetch = per_stage_counter(fcsv, "FETCH_SIZE")
-    write = per_stage_counter(wcsv, "WRITE_SIZE")
+    fetch = per_stage_counter(fcsv, "FETCH_SIZE", a.sets_per_stage)
+    write = per_stage_counter(wcsv, "WRITE_SIZE", a.sets_per_stage)
 
     lines = [f"# rocprofv3 summary: grouped GEMM and other kernels, workload {a.workload}", "",
              "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", "",
@@ -134,7 +137,7 @@ def main(argv=None) -> int:
         rd = fetch.get(key, float("nan")) * 1024 * (fs or 1)
         wr = write.get(key, float("nan")) * 1024 * (ws or 1)
         lines.append(f"| {key[0]} | {key[1]} | {d:.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
-        stage = key[0] if key[1] == "routed" else "shared_" + key[0]
+        stage = "shared_" + key[0] if key[1] == "shared" else key[0]
         traffic[stage] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
                           "avg_us_trace": d, "kernel_source_sha": kernel_source_sha()}
     open(a.out, "w").write("\n".join(lines) + "\n")

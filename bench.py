@@ -27,9 +27,10 @@ PEAK_HBM_GBS = 8000.0
 GEMM_STAGES = ("gate_up_fwd", "down_fwd", "down_bwd", "down_wgrad", "gate_up_dgrad", "gate_up_wgrad")
 
 
-def stage_flops(cfg, merged=True):
+def stage_flops(cfg, merged=True, recompute=False):
     """Algorithmic FLOPs of each GEMM stage call of one step (2 per multiply-add, no padding).
-    Merged: each stage runs the routed experts and the shared expert in one call."""
+    Merged: each stage runs the routed experts and the shared expert in one call.  Recompute: the
+    backward repeats the gate/up GEMM (the recompute variant's extra work)."""
     Tk, T, d, f, fs = cfg.T * cfg.k, cfg.T, cfg.d, cfg.f, cfg.fs
     per_row = {"gate_up_fwd": 4.0, "down_fwd": 2.0, "down_bwd": 2.0, "down_wgrad": 2.0,
                "gate_up_dgrad": 4.0, "gate_up_wgrad": 4.0}
@@ -40,6 +41,11 @@ def stage_flops(cfg, merged=True):
         if fs:
             key = s if merged else "shared_" + s
             fl[key] = fl.get(key, 0.0) + per_row[s] * T * d * fs
+    if recompute and cfg.backward:
+        fl["gate_up_recompute"] = per_row["gate_up_fwd"] * Tk * d * f
+        if fs:
+            key = "gate_up_recompute" if merged else "shared_gate_up_recompute"
+            fl[key] = fl.get(key, 0.0) + per_row["gate_up_fwd"] * T * d * fs
     return fl
 
 
@@ -95,6 +101,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="tiny64e_random")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="per-layer recompute variant: no A/B stash in the forward, gate/up GEMM rerun in "
+                         "the backward")
     ap.add_argument("--no-merge", action="store_true",
                     help="one GEMM call per expert set instead of routed + shared in one call")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -120,7 +129,7 @@ def main(argv=None) -> int:
     print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = I.make_inputs(cfg)
     dev = torch.device("cuda:0")
-    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not a.no_merge)
+    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not a.no_merge, recompute=a.recompute)
     if a.copy_probe_mb > 0:
         src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -146,7 +155,7 @@ def main(argv=None) -> int:
     for name, pairs in lay.events.items():
         ms = [s.elapsed_time(e) for s, e in pairs]
         stages[name] = sum(ms) / len(ms)
-    flops = stage_flops(cfg, merged=not a.no_merge)
+    flops = stage_flops(cfg, merged=not a.no_merge, recompute=a.recompute)
     gemm_ms = sum(stages[s] for s in flops if s in stages)
     gemm_flop = sum(flops.values())
     stage_tflops = {s: flops[s] / (stages[s] * 1e-3) / 1e12 for s in flops if s in stages}
@@ -179,7 +188,7 @@ def main(argv=None) -> int:
         if cfg.routing == "random" else "synthetic (seeded Gaussian inputs and weights, learned router)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "expert_d_ff": cfg.f, "shared_d_ff": cfg.fs, "routing": cfg.routing,
-                   "backward": cfg.backward},
+                   "backward": cfg.backward, "recompute": a.recompute},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
         "grouped_gemm": {"tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12,

@@ -104,23 +104,30 @@ class MoELayer:
     stream around every library call, keyed by stage name.
     ``merge_shared``: run each GEMM stage of the routed experts and the shared expert as one
     two-set call (one launch where the kernel allows); False makes one call per set.
+    ``recompute``: the per-layer recompute variant of the Ultra runs ("Olmo-core 3 Opens Large MoE
+    Training", "Technical Deep Dive"): the forward keeps no SwiGLU pre-activation stash (it writes
+    H only), and the backward runs the gate/up GEMM again to regenerate A, B and H before the
+    down-projection dgrad.  The kernels are deterministic, so the results are bitwise those of the
+    stashing pass.
     """
 
     def __init__(self, cfg: MoEConfig, params: dict, bufs: Buffers | None = None, renormalize: int = 1,
-                 merge_shared: bool = True):
+                 merge_shared: bool = True, recompute: bool = False):
         self.cfg = cfg
         self.p = params
         self.bufs = bufs or Buffers.allocate(cfg, params["x"].device)
         self.renorm = renormalize
         self.merge = merge_shared
+        self.recompute = recompute
         self.dt = L.MOE_BF16 if cfg.dtype == "bf16" else L.MOE_F32
         self.events: dict | None = None
 
-    def _sets(self, dout=None):
-        """The routed experts and (if any) the shared expert as expert sets."""
+    def _sets(self, dout=None, stash=True):
+        """The routed experts and (if any) the shared expert as expert sets; stash=False leaves out
+        the pre-activation outputs A and B."""
         c, p, b = self.cfg, self.p, self.bufs
         T, E, k, f, fs = c.T, c.E, c.k, c.f, c.fs
-        bw = c.backward
+        bw = c.backward and stash
         g = lambda name: b.t.get(name)
         routed = L.expert_set(b["offsets"], E, T * k, f, x=b["x_perm"], w1=p["w1"], w3=p["w3"], w2=p["w2"],
                               a=b["a"] if bw else None, b=b["b"] if bw else None, h=b["h"], y=b["y"],
@@ -166,7 +173,7 @@ class MoELayer:
         self._stage("permute", L.moe_permute, p["x"], b["topk_idx"], T, d, E, k, dt, b["counts"],
                     b["offsets"], b["dest_pos"], b["src_row"], b["x_perm"], b["ws_perm"],
                     b["ws_perm"].numel())
-        sets = self._sets()
+        sets = self._sets(stash=not self.recompute)
         self._gemm("gate_up_fwd", L.MOE_STAGE_GATE_UP_FWD, sets, b["ws_fwd"])
         self._gemm("down_fwd", L.MOE_STAGE_DOWN_FWD, sets, b["ws_fwd"])
         shared = b["s"] if fs > 0 else None
@@ -189,6 +196,8 @@ class MoELayer:
             dx_router = b["dx_router"]
         ws = b["ws_bwd"]
         sets = self._sets(dout)
+        if self.recompute:
+            self._gemm("gate_up_recompute", L.MOE_STAGE_GATE_UP_FWD, sets, b["ws_fwd"])
         # Each activation gradient is consumed right after it is produced, while it still sits in
         # the last-level cache (dA/dB by the gate/up dgrad, dX_perm by the permute backward); the
         # weight gradients, which nothing downstream reads, go last.

@@ -42,9 +42,9 @@ def as_dtype_values(a: np.ndarray, dtype: str) -> np.ndarray:
     return I.f32_from_bf16_bits(I.bf16_bits_from_f32(a)) if dtype == "bf16" else a
 
 
-def run_layer_gpu(cfg, inp, renormalize=1):
+def run_layer_gpu(cfg, inp, renormalize=1, recompute=False):
     params = LY.upload_inputs(inp, DEV)
-    lay = LY.MoELayer(cfg, params, renormalize=renormalize)
+    lay = LY.MoELayer(cfg, params, renormalize=renormalize, recompute=recompute)
     lay.step()
     torch.cuda.synchronize()
     return lay

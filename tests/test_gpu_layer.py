@@ -75,6 +75,33 @@ def test_layer_is_bitwise_deterministic():
             assert torch.equal(v, lay.bufs[k]), k
 
 
+@pytest.mark.parametrize("name", ["fp32_fwd_bwd_learned_bias", "bf16_random_ragged", "bf16_learned_skew"])
+def test_recompute_layer_matches_oracle(name):
+    """Per-layer recompute variant (no A/B stash in the forward, gate/up GEMM rerun in the backward)
+    against the oracle, which keeps the stash."""
+    cfg = SMALL[name]
+    log(f"layer {name} with recompute: {cfg}")
+    inp = I.make_inputs(cfg)
+    lay = run_layer_gpu(cfg, inp, recompute=True)
+    fwd, bwd = O.run_layer(cfg, I.values(inp))
+    compare_layer(cfg, lay, fwd, bwd)
+
+
+def test_recompute_is_bitwise_the_stashing_pass():
+    """At the benchmark's shape and launch configuration the recompute variant reproduces every
+    output of the stashing pass bit for bit (the kernels are deterministic)."""
+    cfg = I.CONFIGS["tiny64e_random"]
+    log(f"recompute vs stash, full size: {cfg}")
+    inp = I.make_inputs(cfg)
+    ref = run_layer_gpu(cfg, inp)
+    keep = {k: ref.bufs[k].clone() for k in ("out", "dx", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2", "a", "b", "h")}
+    del ref
+    torch.cuda.empty_cache()
+    lay = run_layer_gpu(cfg, inp, recompute=True)
+    for k, v in keep.items():
+        assert torch.equal(v, lay.bufs[k]), k
+
+
 FULL = ["tiny64e_random", "tiny64e_learned_skew", "e128_2seq", "e32_2seq", "e8_2seq", "large_e128"]
 
 

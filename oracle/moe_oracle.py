@@ -25,7 +25,9 @@ is the plain definition, with numpy matmul, sort and exp as the only library ste
 Pins (tests/test_oracle_*.py): brute-force top-k with forced ties and signed zeros; a scalar
 fp32 loop for the logits; bijection/stability/count invariants of the permutation; E=1,k=1 equal
 to torch's dense SwiGLU; identical experts; k=E equal to a dense soft mixture; central finite
-differences; torch fp64 autograd on a dense masked formulation.
+differences; torch fp64 autograd on a dense masked formulation; for the load-balancing loss, the
+balanced-routing and single-expert closed forms, zero row sums of its gradient, finite differences
+and autograd.
 """
 from __future__ import annotations
 
@@ -266,6 +268,39 @@ def router_logit_grad(dgates, gates, topk_idx, E, renormalize=True, logits=None,
     return p * (dp - (p * dp).sum(axis=1, keepdims=True))
 
 
+def load_balancing_loss(logits, counts, k, weight, dt=np.float64):
+    """Auxiliary load-balancing loss of the router and the router statistics it is built from.
+
+    The pages name only the loss weights of their runs, 0.02 to 0.50 (Olmo-core DDP MoE examples,
+    "Other experiments in the report"), not the formula.  Reading taken: the loss is
+        weight * E * sum_e f_e P_e,
+    f_e = count_e / (T k), the fraction of the T k assignments routed to expert e, and P_e the mean
+    over the tokens of the softmax over all E logits.  f comes from the selection, which is
+    piecewise constant, so only P carries a gradient.  Returns (loss, P, f).
+    """
+    L = np.asarray(logits, dt)
+    T, E = L.shape
+    m = L.max(axis=1, keepdims=True)
+    p = np.exp(L - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    P = p.mean(axis=0)
+    f = np.asarray(counts, dt) / (T * k)
+    return weight * E * (f * P).sum(), P, f
+
+
+def load_balancing_loss_grad(logits, f, weight, dt=np.float64):
+    """dloss/dlogits [T, E] of load_balancing_loss at fixed f: the softmax Jacobian applied to
+    c f with c = weight E / T, G[t, j] = c p[t, j] (f_j - sum_e f_e p[t, e])."""
+    L = np.asarray(logits, dt)
+    T, E = L.shape
+    m = L.max(axis=1, keepdims=True)
+    p = np.exp(L - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    f = np.asarray(f, dt)
+    c = weight * E / T
+    return c * p * (f[None, :] - (p * f[None, :]).sum(axis=1, keepdims=True))
+
+
 def router_backward(dL, x, w_router, dt=np.float64):
     """dW_router = dL^T x  ([E, d]);  dx_router = dL W_router  ([T, d])."""
     x = np.asarray(x, dt)
@@ -278,12 +313,13 @@ def router_backward(dL, x, w_router, dt=np.float64):
 
 
 def layer_forward(x, w1, w3, w2, k, *, logits=None, w_router=None, bias=None, ws1=None, ws3=None,
-                  ws2=None, renormalize=True, dt=np.float64, logits_mode="canonical_fp32"):
+                  ws2=None, renormalize=True, dt=np.float64, logits_mode="canonical_fp32", lbl_weight=0.0):
     """Forward pass of the MoE layer. Returns a dict of every intermediate.
 
     Routing: random routing passes ``logits``; learned routing passes ``w_router`` (and optional
     ``bias``) and the logits are computed here: in the canonical fp32 order by default, or by a
-    ``dt`` matmul when ``logits_mode="dense"`` (finite-difference checks only).
+    ``dt`` matmul when ``logits_mode="dense"`` (finite-difference checks only).  With learned
+    routing and lbl_weight > 0 the load-balancing loss and its statistics are added (lbl, P, f).
     """
     x = np.asarray(x)
     T, d = x.shape
@@ -305,9 +341,12 @@ def layer_forward(x, w1, w3, w2, k, *, logits=None, w_router=None, bias=None, ws
     else:
         As = Bs = Hs = S = None
     out = combine(Y, gates, dest_pos, S, dt)
-    return dict(logits=logits, topk_idx=topk_idx, gates=gates, counts=counts, offsets=offsets,
-                dest_pos=dest_pos, src_row=src_row, X_perm=X_perm, A=A, B=B, H=H, Y=Y,
-                As=As, Bs=Bs, Hs=Hs, S=S, out=out)
+    res = dict(logits=logits, topk_idx=topk_idx, gates=gates, counts=counts, offsets=offsets,
+               dest_pos=dest_pos, src_row=src_row, X_perm=X_perm, A=A, B=B, H=H, Y=Y,
+               As=As, Bs=Bs, Hs=Hs, S=S, out=out, lbl_weight=lbl_weight)
+    if w_router is not None and lbl_weight > 0:
+        res["lbl"], res["P"], res["f"] = load_balancing_loss(logits, counts, k, lbl_weight, dt)
+    return res
 
 
 def layer_backward(fwd, dout, x, w1, w3, w2, k, *, w_router=None, ws1=None, ws3=None, ws2=None,
@@ -332,6 +371,8 @@ def layer_backward(fwd, dout, x, w1, w3, w2, k, *, w_router=None, ws1=None, ws3=
     if w_router is not None:
         dL = router_logit_grad(dgates, fwd["gates"], fwd["topk_idx"], E, renormalize,
                                fwd["logits"], dt)
+        if fwd.get("lbl_weight", 0.0) > 0:
+            dL = dL + load_balancing_loss_grad(fwd["logits"], fwd["f"], fwd["lbl_weight"], dt)
         dWr, dx_router = router_backward(dL, x, w_router, dt)
         res.update(dlogits=dL, dWr=dWr, dx_router=dx_router)
         addends.append(dx_router)
@@ -339,11 +380,12 @@ def layer_backward(fwd, dout, x, w1, w3, w2, k, *, w_router=None, ws1=None, ws3=
     return res
 
 
-def run_layer(cfg, vals: dict, dt=np.float64, renormalize=True):
+def run_layer(cfg, vals: dict, dt=np.float64, renormalize=True, lbl_weight=0.0):
     """Forward (and backward, when the workload has one) on the value dict of the inputs module."""
     fwd = layer_forward(vals["x"], vals["w1"], vals["w3"], vals["w2"], cfg.k, logits=vals["logits"],
                         w_router=vals["w_router"], bias=vals["bias"], ws1=vals["ws1"],
-                        ws3=vals["ws3"], ws2=vals["ws2"], renormalize=renormalize, dt=dt)
+                        ws3=vals["ws3"], ws2=vals["ws2"], renormalize=renormalize, dt=dt,
+                        lbl_weight=lbl_weight)
     bwd = None
     if cfg.backward:
         bwd = layer_backward(fwd, vals["dout"], vals["x"], vals["w1"], vals["w3"], vals["w2"], cfg.k,

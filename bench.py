@@ -101,6 +101,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="tiny64e_random")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lbl", type=float, default=0.0,
+                    help="weight of the router's load-balancing loss (learned-routing workloads; 0: off)")
     ap.add_argument("--recompute", action="store_true",
                     help="per-layer recompute variant: no A/B stash in the forward, gate/up GEMM rerun in "
                          "the backward")
@@ -129,7 +131,8 @@ def main(argv=None) -> int:
     print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = I.make_inputs(cfg)
     dev = torch.device("cuda:0")
-    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not a.no_merge, recompute=a.recompute)
+    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not a.no_merge, recompute=a.recompute,
+                      lbl_weight=a.lbl)
     if a.copy_probe_mb > 0:
         src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -188,7 +191,8 @@ def main(argv=None) -> int:
         if cfg.routing == "random" else "synthetic (seeded Gaussian inputs and weights, learned router)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "expert_d_ff": cfg.f, "shared_d_ff": cfg.fs, "routing": cfg.routing,
-                   "backward": cfg.backward, "recompute": a.recompute},
+                   "backward": cfg.backward, "recompute": a.recompute,
+                   "lbl_weight": a.lbl if cfg.routing == "learned" else 0.0},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
         "grouped_gemm": {"tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12,

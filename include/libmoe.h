@@ -260,6 +260,34 @@ moe_status_t moe_route_bwd(const float* dgate, const float* topk_gate, const int
                            void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* Router statistics and the auxiliary load-balancing loss (learned routing)                   */
+/* The pages run load-balancing experiments at loss weights 0.02 to 0.50 ("Olmo-core DDP MoE
+ * examples", "Other experiments in the report") without stating the loss.  Implemented reading:
+ *   loss = weight * E * sum_e f_e P_e,  f_e = counts[e] / (T k),  P_e = mean_t softmax(logits[t])_e
+ * (softmax over all E logits).  f comes from the selection and carries no gradient.            */
+
+/* Forward: prob_mean [E] float OUTPUT (P), load_frac [E] float OUTPUT (f), loss [1] float OUTPUT.
+ *   logits [T, E] float INPUT (the router logits; NULL allowed when T = 0); counts [E] int32 INPUT
+ *   (from moe_permute).  All device pointers.  ws: moe_router_aux_workspace_size(T, E) bytes.
+ *   Sums in fixed orders (bitwise reproducible).  Errors: NULL output, bad sizes, small workspace. */
+size_t moe_router_aux_workspace_size(int64_t T, int32_t E);
+moe_status_t moe_router_aux(const float* logits, const int32_t* counts, int64_t T, int32_t E, int32_t k,
+                            float weight, float* loss, float* prob_mean, float* load_frac, void* ws,
+                            size_t ws_bytes, moe_stream_t stream);
+
+/* Backward: with G[t, j] = (weight E / T) p[t, j] (f_j - sum_e f_e p[t, e]) the gradient of the
+ * loss with respect to the logits, ADDS
+ *   G^T x        to dw_router [E, d] float (IN/OUT),
+ *   G w_router   to dx_router [T, d] (dt) (IN/OUT; the sum is rounded once to dt),
+ * so it runs after moe_route_bwd on the same buffers.  Inputs: logits [T, E] float, load_frac [E]
+ * float (from moe_router_aux), x [T, d] (dt), w_router [E, d] (dt).  d must be a multiple of 8.
+ * ws: moe_router_aux_bwd_workspace_size(T, d, E) bytes.  Fixed summation orders. */
+size_t moe_router_aux_bwd_workspace_size(int64_t T, int64_t d, int32_t E);
+moe_status_t moe_router_aux_bwd(const float* logits, const float* load_frac, const void* x, const void* w_router,
+                                int64_t T, int64_t d, int32_t E, float weight, moe_dtype_t dt, float* dw_router,
+                                void* dx_router, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
 /* Utilities                                                                                   */
 
 const char* moe_status_string(moe_status_t status);

@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe.so")
 
-SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "combine.hip", "grouped_gemm.hip", "grouped_gemm_pipe.hip"]
+SOURCES = ["api.cpp", "route.hip", "router_aux.hip", "dispatch.hip", "combine.hip", "grouped_gemm.hip",
+           "grouped_gemm_pipe.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions stay off: plain scalar fp32 code only.

@@ -440,4 +440,48 @@ moe_status_t moe_route_bwd(const float* dgate, const float* topk_gate, const int
                    "router backward");
 }
 
+size_t moe_router_aux_workspace_size(int64_t T, int32_t E) {
+  if (T < 0 || E <= 0) return 0;
+  return moe::router_aux_ws_bytes(T, E);
+}
+
+moe_status_t moe_router_aux(const float* logits, const int32_t* counts, int64_t T, int32_t E, int32_t k,
+                            float weight, float* loss, float* prob_mean, float* load_frac, void* ws,
+                            size_t ws_bytes, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_tokens(T, 1, E, k);
+  if (st != MOE_OK) return st;
+  CHECK(counts && loss && prob_mean && load_frac, MOE_ERR_INVALID_VALUE, "counts/loss/prob_mean/load_frac is NULL");
+  CHECK(T == 0 || logits, MOE_ERR_INVALID_VALUE, "logits is NULL");
+  const size_t need = moe::router_aux_ws_bytes(T, E);
+  CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+        ws ? ws_bytes : (size_t)0);
+  return hip_check(moe::launch_router_aux(logits, counts, (int)T, E, k, weight, loss, prob_mean, load_frac, ws,
+                                          S(stream)),
+                   "router statistics");
+}
+
+size_t moe_router_aux_bwd_workspace_size(int64_t T, int64_t d, int32_t E) {
+  if (T < 0 || d <= 0 || E <= 0) return 0;
+  return moe::router_aux_bwd_ws_bytes(T, d, E);
+}
+
+moe_status_t moe_router_aux_bwd(const float* logits, const float* load_frac, const void* x, const void* w_router,
+                                int64_t T, int64_t d, int32_t E, float weight, moe_dtype_t dt, float* dw_router,
+                                void* dx_router, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, E, 1)) != MOE_OK) return st;
+  CHECK(d % 8 == 0, MOE_ERR_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
+  CHECK(load_frac && w_router && dw_router, MOE_ERR_INVALID_VALUE, "load_frac/w_router/dw_router is NULL");
+  CHECK(T == 0 || (logits && x && dx_router), MOE_ERR_INVALID_VALUE, "logits/x/dx_router is NULL");
+  const size_t need = moe::router_aux_bwd_ws_bytes(T, d, E);
+  CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+        ws ? ws_bytes : (size_t)0);
+  return hip_check(moe::launch_router_aux_bwd(logits, load_frac, x, w_router, (int)T, (int)d, E, weight,
+                                              dt == MOE_BF16, dw_router, dx_router, ws, S(stream)),
+                   "router load-balancing backward");
+}
+
 }  // extern "C"

@@ -46,6 +46,15 @@ hipError_t launch_route_bwd(const float* dgate, const float* gate, const int32_t
                             const void* w, int T, int d, int E, int k, bool bf16, float* dw,
                             void* dx_router, void* ws, hipStream_t s);
 
+// Router statistics and the load-balancing loss
+size_t router_aux_ws_bytes(long long T, int E);
+hipError_t launch_router_aux(const float* logits, const int32_t* counts, int T, int E, int k, float weight,
+                             float* loss, float* prob_mean, float* load_frac, void* ws, hipStream_t s);
+size_t router_aux_bwd_ws_bytes(long long T, long long d, int E);
+hipError_t launch_router_aux_bwd(const float* logits, const float* load_frac, const void* x, const void* w,
+                                 int T, int d, int E, float weight, bool bf16, float* dw, void* dx, void* ws,
+                                 hipStream_t s);
+
 // Dispatch
 size_t permute_ws_bytes(long long T, int E, int k);
 hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int d, int E, int k,

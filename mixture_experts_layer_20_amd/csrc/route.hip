@@ -10,26 +10,90 @@
 // specified bitwise, so this runs on the vector ALUs.
 #include "common.h"
 
+#include <type_traits>
+
 #pragma clang fp contract(off)
 
 namespace moe {
 namespace {
 
-constexpr int RT = 64;   // tokens per block
+constexpr int RT = 32;   // tokens per block
 constexpr int RE = 64;   // experts per block
 constexpr int RK = 32;   // features per LDS step
+constexpr int RTH = 128; // threads per block: 8 x 16, each 4 tokens x 4 experts
+
+// 8 consecutive elements k0.. of a row as fp32 (0 past n; a 16-byte load when the row is aligned and
+// all 8 are in range).
+template <bool BF16>
+__device__ __forceinline__ void row8(const void* base, size_t row_off, int k0, int n, bool valid, float (&v)[8]) {
+  if (BF16) {
+    const bf16_t* r = reinterpret_cast<const bf16_t*>(base) + row_off;
+    if (valid && k0 + 8 <= n && ((row_off + k0) & 7) == 0) {
+      const uint4 u = *reinterpret_cast<const uint4*>(r + k0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (valid && k0 + i < n) ? bf16_to_f32(r[k0 + i]) : 0.0f;
+    }
+  } else {
+    const float* r = reinterpret_cast<const float*>(base) + row_off;
+    if (valid && k0 + 8 <= n && ((row_off + k0) & 3) == 0) {
+      const float4 a = *reinterpret_cast<const float4*>(r + k0), b = *reinterpret_cast<const float4*>(r + k0 + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (valid && k0 + i < n) ? r[k0 + i] : 0.0f;
+    }
+  }
+}
+
+// One feature of the 4x4 block: products in the canonical order (see router_logits_kernel).
+template <bool BF16>
+__device__ __forceinline__ void logits_step(const float* xrow, const float* wrow, int tx, int ty, float (&acc)[4][4]) {
+  const float4 av = *reinterpret_cast<const float4*>(xrow + ty * 4);
+  const float4 bv = *reinterpret_cast<const float4*>(wrow + tx * 4);
+  const float a[4] = {av.x, av.y, av.z, av.w}, b[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (BF16) {
+        acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+      } else {
+        const float prod = a[i] * b[j];
+        acc[i][j] = acc[i][j] + prod;
+      }
+    }
+}
 
 // Logits: one thread owns 4 tokens x 4 experts and walks the features in increasing order.
 // bf16 inputs: the product of two bf16 values is exact in fp32, so a fused multiply-add rounds
-// exactly like the separate product and sum.  fp32 inputs: separate multiply and add.
+// exactly like the separate product and sum.  fp32 inputs: separate multiply and add.  The next
+// 32-feature tile is loaded into registers while the current one is multiplied.
 template <bool BF16>
-__global__ __launch_bounds__(256) void router_logits_kernel(const void* xv, const void* wv,
+__global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, const void* wv,
                                                             const float* bias, float* logits,
                                                             int T, int d, int E) {
-  __shared__ float xs[RK][RT + 1];
-  __shared__ float ws[RK][RE + 1];
+  __shared__ __attribute__((aligned(16))) float xs[RK][RT];
+  __shared__ __attribute__((aligned(16))) float ws[RK][RE];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
+  // staging: thread q loads 8 features (chunk q % 4) of token row q / 4 and of expert rows q / 4
+  // and q / 4 + 32
+  const int sr = tid >> 2, sk = (tid & 3) * 8;
+  const bool xok = t0 + sr < T, w0ok = e0 + sr < E, w1ok = e0 + sr + 32 < E;
+  const size_t xoff = (size_t)(xok ? t0 + sr : 0) * d, w0off = (size_t)(w0ok ? e0 + sr : 0) * d,
+               w1off = (size_t)(w1ok ? e0 + sr + 32 : 0) * d;
+  float xr[8], wr0[8], wr1[8];
+  row8<BF16>(xv, xoff, sk, d, xok, xr);
+  row8<BF16>(wv, w0off, sk, d, w0ok, wr0);
+  row8<BF16>(wv, w1off, sk, d, w1ok, wr1);
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -38,41 +102,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* xv, cons
 
   for (int k0 = 0; k0 < d; k0 += RK) {
 #pragma unroll
-    for (int i = 0; i < (RT * RK) / 256; ++i) {
-      const int e = tid + i * 256;
-      const int r = e / RK, kk = e % RK;
-      const int t = t0 + r, ex = e0 + r, k = k0 + kk;
-      float xval = 0.0f, wval = 0.0f;
-      if (t < T && k < d) {
-        xval = BF16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(xv)[(size_t)t * d + k])
-                    : reinterpret_cast<const float*>(xv)[(size_t)t * d + k];
-      }
-      if (ex < E && k < d) {
-        wval = BF16 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(wv)[(size_t)ex * d + k])
-                    : reinterpret_cast<const float*>(wv)[(size_t)ex * d + k];
-      }
-      xs[kk][r] = xval;
-      ws[kk][r] = wval;
+    for (int i = 0; i < 8; ++i) {
+      xs[sk + i][sr] = xr[i];
+      ws[sk + i][sr] = wr0[i];
+      ws[sk + i][sr + 32] = wr1[i];
     }
     __syncthreads();
+    if (k0 + RK < d) {
+      row8<BF16>(xv, xoff, k0 + RK + sk, d, xok, xr);
+      row8<BF16>(wv, w0off, k0 + RK + sk, d, w0ok, wr0);
+      row8<BF16>(wv, w1off, k0 + RK + sk, d, w1ok, wr1);
+    }
     const int kn = d - k0 < RK ? d - k0 : RK;
-    for (int kk = 0; kk < kn; ++kk) {
-      float a[4], b[4];
+    if (kn == RK) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (BF16) {
-            acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-          } else {
-            const float prod = a[i] * b[j];
-            acc[i][j] = acc[i][j] + prod;
-          }
-        }
+      for (int kk = 0; kk < RK; ++kk) logits_step<BF16>(xs[kk], ws[kk], tx, ty, acc);
+    } else {
+      for (int kk = 0; kk < kn; ++kk) logits_step<BF16>(xs[kk], ws[kk], tx, ty, acc);
     }
     __syncthreads();
   }
@@ -204,8 +250,9 @@ __global__ __launch_bounds__(256) void route_dx_kernel(const float* dl, const in
   }
 }
 
-constexpr int SEG = 256;     // permuted rows per partial sum of the router weight gradient
-constexpr int DWCOLS = 1024; // columns per block
+constexpr int SEG = 64;      // permuted rows per partial sum of the router weight gradient
+constexpr int DWCOLS = 1024; // columns per block (any d)
+constexpr int DWCOLS8 = 2048; // columns per block, 8 per thread (d a multiple of 8)
 
 // Segment prefix: number of SEG-row segments before each expert.
 __global__ void seg_prefix_kernel(const int32_t* offsets, int E, int Tk, int32_t* prefix) {
@@ -303,6 +350,66 @@ __global__ __launch_bounds__(256) void route_dw_partial_kernel(const float* dl, 
   }
 }
 
+// The same with 8 consecutive columns per thread and 16-byte loads of the token rows (d a
+// multiple of 8); rows are accumulated in the same order.
+template <typename T>
+__global__ __launch_bounds__(256) void route_dw_partial8_kernel(const float* dl, const int32_t* src_row,
+                                                                const int32_t* offsets,
+                                                                const int32_t* seg_prefix,
+                                                                const T* x, int E, int Tk, int d,
+                                                                int k, float* partial) {
+  const int seg = blockIdx.x;
+  if (seg >= seg_prefix[E]) return;
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (seg_prefix[mid] <= seg) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  int r0 = offsets[e], r1 = offsets[e + 1];
+  r0 = r0 < 0 ? 0 : (r0 > Tk ? Tk : r0);
+  r1 = r1 < r0 ? r0 : (r1 > Tk ? Tk : r1);
+  const int p0 = r0 + (seg - seg_prefix[e]) * SEG;
+  const int p1 = p0 + SEG < r1 ? p0 + SEG : r1;
+  __shared__ int tok_s[SEG];
+  __shared__ float w_s[SEG];
+  const int n = p1 - p0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int a = src_row[p0 + i];
+    tok_s[i] = a / k;
+    w_s[i] = dl[a];
+  }
+  __syncthreads();
+  const int c = blockIdx.y * DWCOLS8 + threadIdx.x * 8;
+  if (c >= d) return;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  for (int rr = 0; rr < n; rr += 8) {
+    float xv[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (rr + u < n) {
+        row8<std::is_same<T, bf16_t>::value>(x, (size_t)tok_s[rr + u] * d, c, d, true, xv[u]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xv[u][q] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (rr + u < n) {
+        const float w = w_s[rr + u];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += w * xv[u][q];
+      }
+    }
+  }
+  float* out = partial + (size_t)seg * d + c;
+  reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
 // dW_router[e] = sum of the expert's segment partials, in segment order (zeros if none).
 __global__ __launch_bounds__(256) void route_dw_reduce_kernel(const float* partial,
                                                               const int32_t* seg_prefix, int d,
@@ -311,7 +418,8 @@ __global__ __launch_bounds__(256) void route_dw_reduce_kernel(const float* parti
   const int s0 = seg_prefix[e], s1 = seg_prefix[e + 1];
   for (int c = blockIdx.y * DWCOLS + threadIdx.x; c < d && c < (blockIdx.y + 1) * DWCOLS; c += 256) {
     float acc = 0.0f;
-    for (int s = s0; s < s1; ++s) acc += partial[(size_t)s * d + c];
+#pragma unroll 16
+    for (int s = s0; s < s1; ++s) acc += partial[(size_t)s * d + c];   // in order; loads overlap
     dw[(size_t)e * d + c] = acc;
   }
 }
@@ -324,8 +432,8 @@ hipError_t launch_router_logits(const void* x, const void* w, const float* bias,
                                 int T, int d, int E, bool bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid(ceil_div(T, RT), ceil_div(E, RE));
-  if (bf16) hipLaunchKernelGGL(router_logits_kernel<true>, grid, dim3(256), 0, s, x, w, bias, logits, T, d, E);
-  else hipLaunchKernelGGL(router_logits_kernel<false>, grid, dim3(256), 0, s, x, w, bias, logits, T, d, E);
+  if (bf16) hipLaunchKernelGGL(router_logits_kernel<true>, grid, dim3(RTH), 0, s, x, w, bias, logits, T, d, E);
+  else hipLaunchKernelGGL(router_logits_kernel<false>, grid, dim3(RTH), 0, s, x, w, bias, logits, T, d, E);
   return hipGetLastError();
 }
 
@@ -369,14 +477,23 @@ hipError_t launch_route_bwd(const float* dgate, const float* gate, const int32_t
   hipLaunchKernelGGL(seg_prefix_kernel, dim3(1), dim3(256), 0, s, offsets, E, Tk, seg_prefix);
   const int ncb = ceil_div(d, DWCOLS);
   const long long nseg = max_segments(Tk, E);
-  if (bf16)
+  if (d % 8 == 0) {
+    const dim3 g((unsigned)nseg, ceil_div(d, DWCOLS8));
+    if (bf16)
+      hipLaunchKernelGGL(route_dw_partial8_kernel<bf16_t>, g, dim3(256), 0, s, dl, src_row, offsets, seg_prefix,
+                         reinterpret_cast<const bf16_t*>(x), E, Tk, d, k, partial);
+    else
+      hipLaunchKernelGGL(route_dw_partial8_kernel<float>, g, dim3(256), 0, s, dl, src_row, offsets, seg_prefix,
+                         reinterpret_cast<const float*>(x), E, Tk, d, k, partial);
+  } else if (bf16) {
     hipLaunchKernelGGL(route_dw_partial_kernel<bf16_t>, dim3((unsigned)nseg, ncb), dim3(256), 0, s, dl,
                        src_row, offsets, seg_prefix, reinterpret_cast<const bf16_t*>(x), E, Tk, d, k,
                        partial);
-  else
+  } else {
     hipLaunchKernelGGL(route_dw_partial_kernel<float>, dim3((unsigned)nseg, ncb), dim3(256), 0, s, dl,
                        src_row, offsets, seg_prefix, reinterpret_cast<const float*>(x), E, Tk, d, k,
                        partial);
+  }
   hipLaunchKernelGGL(route_dw_reduce_kernel, dim3(E, ncb), dim3(256), 0, s, partial, seg_prefix, d, dw);
   return hipGetLastError();
 }

@@ -112,13 +112,26 @@ class MoELayer:
     """
 
     def __init__(self, cfg: MoEConfig, params: dict, bufs: Buffers | None = None, renormalize: int = 1,
-                 merge_shared: bool = True, recompute: bool = False):
+                 merge_shared: bool = True, recompute: bool = False, lbl_weight: float = 0.0):
         self.cfg = cfg
         self.p = params
         self.bufs = bufs or Buffers.allocate(cfg, params["x"].device)
         self.renorm = renormalize
         self.merge = merge_shared
         self.recompute = recompute
+        # Auxiliary load-balancing loss of the learned router (weight 0: off): its statistics and
+        # loss in the forward, its gradient added to the router gradients in the backward.
+        self.lbl = float(lbl_weight) if cfg.routing == "learned" else 0.0
+        if self.lbl > 0:
+            dev, t = params["x"].device, self.bufs.t
+            t["lbl_loss"] = torch.empty(1, dtype=torch.float32, device=dev)
+            t["prob_mean"] = torch.empty(cfg.E, dtype=torch.float32, device=dev)
+            t["load_frac"] = torch.empty(cfg.E, dtype=torch.float32, device=dev)
+            t["ws_aux"] = torch.empty(max(1, L.moe_router_aux_workspace_size(cfg.T, cfg.E)), dtype=torch.uint8,
+                                      device=dev)
+            if cfg.backward:
+                t["ws_aux_bwd"] = torch.empty(max(1, L.moe_router_aux_bwd_workspace_size(cfg.T, cfg.d, cfg.E)),
+                                              dtype=torch.uint8, device=dev)
         self.dt = L.MOE_BF16 if cfg.dtype == "bf16" else L.MOE_F32
         self.events: dict | None = None
 
@@ -173,6 +186,9 @@ class MoELayer:
         self._stage("permute", L.moe_permute, p["x"], b["topk_idx"], T, d, E, k, dt, b["counts"],
                     b["offsets"], b["dest_pos"], b["src_row"], b["x_perm"], b["ws_perm"],
                     b["ws_perm"].numel())
+        if self.lbl > 0:
+            self._stage("router_aux", L.moe_router_aux, logits, b["counts"], T, E, k, self.lbl, b["lbl_loss"],
+                        b["prob_mean"], b["load_frac"], b["ws_aux"], b["ws_aux"].numel())
         sets = self._sets(stash=not self.recompute)
         self._gemm("gate_up_fwd", L.MOE_STAGE_GATE_UP_FWD, sets, b["ws_fwd"])
         self._gemm("down_fwd", L.MOE_STAGE_DOWN_FWD, sets, b["ws_fwd"])
@@ -194,6 +210,10 @@ class MoELayer:
                         b["src_row"], p["x"], p["w_router"], T, d, E, k, self.renorm, dt, b["dwr"],
                         b["dx_router"], b["ws_route"], b["ws_route"].numel())
             dx_router = b["dx_router"]
+            if self.lbl > 0:
+                self._stage("router_aux_bwd", L.moe_router_aux_bwd, b["logits"], b["load_frac"], p["x"],
+                            p["w_router"], T, d, E, self.lbl, dt, b["dwr"], b["dx_router"], b["ws_aux_bwd"],
+                            b["ws_aux_bwd"].numel())
         ws = b["ws_bwd"]
         sets = self._sets(dout)
         if self.recompute:

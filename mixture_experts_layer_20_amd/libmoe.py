@@ -69,6 +69,10 @@ _SIGS = {
     "moe_combine_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P, _P]),
     "moe_permute_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "moe_route_bwd_workspace_size": (_SZ, [_I64, _I64, _I32, _I32]),
+    "moe_router_aux_workspace_size": (_SZ, [_I64, _I32]),
+    "moe_router_aux": (_I32, [_P, _P, _I64, _I32, _I32, _c.c_float, _P, _P, _P, _P, _SZ, _P]),
+    "moe_router_aux_bwd_workspace_size": (_SZ, [_I64, _I64, _I32]),
+    "moe_router_aux_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _c.c_float, _I32, _P, _P, _P, _SZ, _P]),
     "moe_route_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P,
                              _P, _SZ, _P]),
     "moe_status_string": (_c.c_char_p, [_I32]),
@@ -261,3 +265,22 @@ def moe_route_bwd(dgate, topk_gate, topk_idx, offsets, src_row, x, w_router, T, 
     _call("moe_route_bwd", _ptr(dgate), _ptr(topk_gate), _ptr(topk_idx), _ptr(offsets), _ptr(src_row),
           _ptr(x), _ptr(w_router), T, d, E, k, renormalize, dt, _ptr(dw_router), _ptr(dx_router), _ptr(ws),
           ws_bytes, _stream(stream))
+
+
+def moe_router_aux_workspace_size(T, E) -> int:
+    return lib().moe_router_aux_workspace_size(T, E)
+
+
+def moe_router_aux(logits, counts, T, E, k, weight, loss, prob_mean, load_frac, ws, ws_bytes, stream=None):
+    _call("moe_router_aux", _ptr(logits), _ptr(counts), T, E, k, weight, _ptr(loss), _ptr(prob_mean),
+          _ptr(load_frac), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_router_aux_bwd_workspace_size(T, d, E) -> int:
+    return lib().moe_router_aux_bwd_workspace_size(T, d, E)
+
+
+def moe_router_aux_bwd(logits, load_frac, x, w_router, T, d, E, weight, dt, dw_router, dx_router, ws, ws_bytes,
+                       stream=None):
+    _call("moe_router_aux_bwd", _ptr(logits), _ptr(load_frac), _ptr(x), _ptr(w_router), T, d, E, weight, dt,
+          _ptr(dw_router), _ptr(dx_router), _ptr(ws), ws_bytes, _stream(stream))

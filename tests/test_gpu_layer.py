@@ -8,7 +8,8 @@ import torch
 
 from mixture_experts_layer_20_amd import inputs as I
 from oracle import moe_oracle as O
-from tests.gpu_helpers import (TOL, assert_close, expert_weight_grads, full_routing, log, run_layer_gpu,
+from mixture_experts_layer_20_amd import layer as LY
+from tests.gpu_helpers import (DEV, TOL, assert_close, expert_weight_grads, full_routing, log, run_layer_gpu,
                                sampled_token_oracle, tnp)
 
 pytestmark = pytest.mark.gpu
@@ -100,6 +101,23 @@ def test_recompute_is_bitwise_the_stashing_pass():
     lay = run_layer_gpu(cfg, inp, recompute=True)
     for k, v in keep.items():
         assert torch.equal(v, lay.bufs[k]), k
+
+
+@pytest.mark.parametrize("name", ["fp32_fwd_bwd_learned_bias", "bf16_learned_skew", "bf16_all_to_few_experts"])
+def test_layer_with_load_balancing_loss_matches_oracle(name):
+    cfg = SMALL[name]
+    w = 0.05
+    log(f"layer {name} with load-balancing loss {w}: {cfg}")
+    inp = I.make_inputs(cfg)
+    params = LY.upload_inputs(inp, DEV)
+    lay = LY.MoELayer(cfg, params, lbl_weight=w)
+    lay.step()
+    torch.cuda.synchronize()
+    fwd, bwd = O.run_layer(cfg, I.values(inp), lbl_weight=w)
+    compare_layer(cfg, lay, fwd, bwd)
+    assert_close("P", tnp(lay.bufs["prob_mean"]), fwd["P"], 1e-5)
+    assert_close("f", tnp(lay.bufs["load_frac"]), fwd["f"], 1e-6)
+    assert abs(tnp(lay.bufs["lbl_loss"])[0] - fwd["lbl"]) <= 1e-5 * abs(fwd["lbl"])
 
 
 FULL = ["tiny64e_random", "tiny64e_learned_skew", "e128_2seq", "e32_2seq", "e8_2seq", "large_e128"]

@@ -376,3 +376,63 @@ def test_route_backward(dtype, T, d, E, k, skew):
     assert_close("dx_router", tnp(dxr), rdx, TOL[dtype])
     for e in np.nonzero(counts == 0)[0]:
         assert np.all(tnp(dw)[e] == 0)
+
+
+# ------------------------------------------------------------------- router load-balancing loss
+
+AUX_SHAPES = [(333, 64, 8, 2), (8192, 256, 64, 4), (1, 16, 1, 1), (129, 40, 37, 3), (600, 8, 256, 8),
+              (0, 64, 16, 2)]
+
+
+@pytest.mark.parametrize("T,d,E,k", AUX_SHAPES)
+@pytest.mark.parametrize("skew", [0.0, 3.0])
+def test_router_aux_statistics_and_loss(T, d, E, k, skew):
+    log(f"router aux fwd T={T} E={E} k={k} skew={skew}")
+    rng = np.random.default_rng(T + E)
+    Lg = (rng.standard_normal((T, E)) + skew * rng.standard_normal(E)).astype(np.float32)
+    idx = O.select_topk(Lg, k) if T else np.zeros((0, k), np.int64)
+    counts = np.bincount(idx.reshape(-1), minlength=E).astype(np.int32)
+    w = 0.05
+    loss = torch.full((1,), float("nan"), device=DEV)
+    P = torch.empty(E, dtype=torch.float32, device=DEV)
+    f = torch.empty(E, dtype=torch.float32, device=DEV)
+    wsn = L.moe_router_aux_workspace_size(T, E)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    L.moe_router_aux(f32(Lg), i32(counts), T, E, k, w, loss, P, f, ws, wsn)
+    torch.cuda.synchronize()
+    if T == 0:
+        assert tnp(loss)[0] == 0 and np.all(tnp(P) == 0) and np.all(tnp(f) == 0)
+        return
+    rl, rP, rf = O.load_balancing_loss(Lg, counts, k, w)
+    assert_close("P", tnp(P), rP, 1e-5)
+    assert_close("f", tnp(f), rf, 1e-6)
+    assert abs(tnp(loss)[0] - rl) <= 1e-5 * abs(rl)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,d,E,k", [s for s in AUX_SHAPES if s[0] > 0])
+def test_router_aux_backward_adds_its_gradient(dtype, T, d, E, k):
+    log(f"router aux bwd {dtype} T={T} d={d} E={E}")
+    rng = np.random.default_rng(T * 3 + d)
+    x = as_dtype_values(rng.standard_normal((T, d)), dtype)
+    wr = as_dtype_values(0.02 * rng.standard_normal((E, d)), dtype)
+    Lg = rng.standard_normal((T, E)).astype(np.float32)
+    f = (rng.random(E) / E).astype(np.float32)
+    w = 0.5
+    G = O.load_balancing_loss_grad(Lg, f, w)
+    rdw, rdx = O.router_backward(G, x, wr)
+    # what the call adds to: values of the same magnitude as what it adds, so that the check sees
+    # the added part
+    dw0 = (np.abs(rdw).max() * rng.standard_normal((E, d))).astype(np.float32)
+    dx0 = as_dtype_values(max(np.abs(rdx).max(), 1e-30) * rng.standard_normal((T, d)), dtype)
+    dw = f32(dw0)
+    dx = dev_tensor(dx0, dtype)
+    wsn = L.moe_router_aux_bwd_workspace_size(T, d, E)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    L.moe_router_aux_bwd(f32(Lg), f32(f), dev_tensor(x, dtype), dev_tensor(wr, dtype), T, d, E, w, DT[dtype], dw, dx,
+                         ws, wsn)
+    torch.cuda.synchronize()
+    # fp32 sums for dW; dx rounded once to dtype
+    assert_close("dWr", tnp(dw), dw0 + rdw, 1e-5)
+    assert_close("dx_router", tnp(dx), dx0 + rdx, TOL[dtype])
+

@@ -855,16 +855,11 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // every K step issues exactly 8 loads per wave and the vmcnt arithmetic stays fixed.
 struct Producer {
   Tile t;
-  int i, k;   // this XCD's tile list position, K step
+  int i, k;        // this XCD's tile list position, K step
   uint32_t voff[8];
+  StageSrc ss;     // sources of stage k
+  long long da, db;  // byte step of the sources from one K step to the next
 };
-
-template <int MODE>
-__device__ __forceinline__ void set_offsets(Producer& pr, const GemmArgs& p, int wave, int lane) {
-  const GemmArgs q = seg_args(p, pr.t.seg);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) pr.voff[i] = load_offset<MODE>(q, pr.t, i, wave, lane);
-}
 
 template <int MODE>
 __device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs& p, int wave) {
@@ -877,11 +872,34 @@ __device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs
   return ss;
 }
 
+// A new tile for the producer: per-lane load offsets, the sources of its first stage and the
+// per-step source strides (K-contiguous operands move 32 elements, K-strided ones 32 rows).
+template <int MODE>
+__device__ __forceinline__ void set_offsets(Producer& pr, const GemmArgs& p, int wave, int lane) {
+  const GemmArgs q = seg_args(p, pr.t.seg);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pr.voff[i] = load_offset<MODE>(q, pr.t, i, wave, lane);
+  pr.ss = stage_src<MODE>(pr, p, wave);
+  const long long d = q.d, f = q.f, kc = 2 * BKS;
+  if constexpr (MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD) { pr.da = kc; pr.db = kc; }
+  else if constexpr (MODE == GEMM_DOWN_BWD) { pr.da = kc; pr.db = kc * f; }
+  else if constexpr (MODE == GEMM_UP_DGRAD) { pr.da = kc; pr.db = kc * d; }
+  else if constexpr (MODE == GEMM_DOWN_WGRAD) { pr.da = kc * d; pr.db = kc * f; }
+  else { pr.da = kc * 2 * f; pr.db = kc * d; }
+}
+
 template <int MODE>
 __device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const SegGeo (&geo)[2], const Deal& dl,
                                         int nbx, int wave, int lane) {
   if (pr.k + 1 < pr.t.nk) {
     ++pr.k;
+    if (MODE == GEMM_UP_DGRAD && pr.t.k_begin + pr.k * BKS == (pr.t.seg ? p.s1.f : p.f)) {
+      pr.ss = stage_src<MODE>(pr, p, wave);   // K moves from the gate half (W1) to the up half (W3)
+    } else {
+      pr.ss.sa += pr.da;
+      pr.ss.sb += pr.db;
+      pr.ss.k_left -= BKS;
+    }
     return;
   }
   for (int i = pr.i + nbx; i < dl.n; i += nbx) {
@@ -942,8 +960,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& ct, cons
     barrier();
     // Phase 1: substep 1 of stage j; read substep 0 of stage j+1; load stage j+4 into slot j & 3.
     const uint32_t sn = ((j + 1) & 3) * STAGE;
-    const StageSrc ss = stage_src<MODE>(pr, p, wave);
-    phase1<MODE, HALF, 0>(acc, a1, b1, a0, b0, fb.a0 + sn, fb.b0 + sn, lds + sb, ss, pr.voff, wave, lane);
+    phase1<MODE, HALF, 0>(acc, a1, b1, a0, b0, fb.a0 + sn, fb.b0 + sn, lds + sb, pr.ss, pr.voff, wave, lane);
     advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
     frag_wait(a0, b0);
     ++since_epi;

@@ -145,7 +145,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* chunk_counts, 
 }
 
 // Pass 3.  dest_pos, src_row, and (optionally) the row copy x_perm[dest] = x[a / k].
-// One block handles 8 assignments; rows are copied 16 bytes per thread.
+// One block per token: its k destinations first, then the row is read once (16 bytes per thread)
+// and written to each destination.
 template <typename T>
 __global__ __launch_bounds__(256) void scatter_gather_kernel(const T* x, const int32_t* topk_idx,
                                                              const int32_t* local_rank,
@@ -154,30 +155,23 @@ __global__ __launch_bounds__(256) void scatter_gather_kernel(const T* x, const i
                                                              int32_t* dest_pos, int32_t* src_row,
                                                              T* x_perm) {
   __shared__ int dst_s[8];
-  __shared__ int tok_s[8];
-  const int a0 = blockIdx.x * 8;
-  if (threadIdx.x < 8) {
-    const int a = a0 + threadIdx.x;
-    int dst = -1;
-    if (a < Tk) {
-      const int e = topk_idx[a];
-      dst = chunk_base[(size_t)(a / CHUNK) * E + e] + local_rank[a];
-      dest_pos[a] = dst;
-      src_row[dst] = a;
-    }
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) {
+    const int a = t * k + threadIdx.x;
+    const int e = topk_idx[a];
+    const int dst = chunk_base[(size_t)(a / CHUNK) * E + e] + local_rank[a];
+    dest_pos[a] = dst;
+    src_row[dst] = a;
     dst_s[threadIdx.x] = dst;
-    tok_s[threadIdx.x] = a / k;
   }
   if (x_perm == nullptr) return;
   __syncthreads();
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
   const int nv = d / V;
-  for (int i = 0; i < 8; ++i) {
-    const int dst = dst_s[i];
-    if (dst < 0) break;
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tok_s[i] * d);
-    uint4* out = reinterpret_cast<uint4*>(x_perm + (size_t)dst * d);
-    for (int c = threadIdx.x; c < nv; c += 256) out[c] = src[c];
+  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * d);
+  for (int c = threadIdx.x; c < nv; c += 256) {
+    const uint4 v = src[c];
+    for (int j = 0; j < k; ++j) reinterpret_cast<uint4*>(x_perm + (size_t)dst_s[j] * d)[c] = v;
   }
 }
 
@@ -281,11 +275,11 @@ hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int d, 
                        chunk_base);
   if (Tk > 0) {
     if (bf16)
-      hipLaunchKernelGGL(scatter_gather_kernel<bf16_t>, dim3(ceil_div(Tk, 8)), dim3(256), 0, s,
+      hipLaunchKernelGGL(scatter_gather_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
                          reinterpret_cast<const bf16_t*>(x), topk_idx, local_rank, chunk_base, Tk, d,
                          E, k, dest_pos, src_row, reinterpret_cast<bf16_t*>(x_perm));
     else
-      hipLaunchKernelGGL(scatter_gather_kernel<float>, dim3(ceil_div(Tk, 8)), dim3(256), 0, s,
+      hipLaunchKernelGGL(scatter_gather_kernel<float>, dim3(T), dim3(256), 0, s,
                          reinterpret_cast<const float*>(x), topk_idx, local_rank, chunk_base, Tk, d,
                          E, k, dest_pos, src_row, reinterpret_cast<float*>(x_perm));
   }

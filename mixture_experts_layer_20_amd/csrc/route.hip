@@ -20,7 +20,7 @@ namespace {
 constexpr int RT = 32;   // tokens per block
 constexpr int RE = 64;   // experts per block
 constexpr int RK = 32;   // features per LDS step
-constexpr int RTH = 128; // threads per block: 8 x 16, each 4 tokens x 4 experts
+constexpr int RTH = 256; // threads per block: 16 x 16, each 2 tokens x 4 experts (4 waves per CU)
 
 // 8 consecutive elements k0.. of a row as fp32 (0 past n; a 16-byte load when the row is aligned and
 // all 8 are in range).
@@ -53,14 +53,14 @@ __device__ __forceinline__ void row8(const void* base, size_t row_off, int k0, i
   }
 }
 
-// One feature of the 4x4 block: products in the canonical order (see router_logits_kernel).
+// One feature of the 2x4 block: products in the canonical order (see router_logits_kernel).
 template <bool BF16>
-__device__ __forceinline__ void logits_step(const float* xrow, const float* wrow, int tx, int ty, float (&acc)[4][4]) {
-  const float4 av = *reinterpret_cast<const float4*>(xrow + ty * 4);
+__device__ __forceinline__ void logits_step(const float* xrow, const float* wrow, int tx, int ty, float (&acc)[2][4]) {
+  const float2 av = *reinterpret_cast<const float2*>(xrow + ty * 2);
   const float4 bv = *reinterpret_cast<const float4*>(wrow + tx * 4);
-  const float a[4] = {av.x, av.y, av.z, av.w}, b[4] = {bv.x, bv.y, bv.z, bv.w};
+  const float a[2] = {av.x, av.y}, b[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (BF16) {
@@ -72,7 +72,7 @@ __device__ __forceinline__ void logits_step(const float* xrow, const float* wrow
     }
 }
 
-// Logits: one thread owns 4 tokens x 4 experts and walks the features in increasing order.
+// Logits: one thread owns 2 tokens x 4 experts and walks the features in increasing order.
 // bf16 inputs: the product of two bf16 values is exact in fp32, so a fused multiply-add rounds
 // exactly like the separate product and sum.  fp32 inputs: separate multiply and add.  The next
 // 32-feature tile is loaded into registers while the current one is multiplied.
@@ -84,34 +84,31 @@ __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, cons
   __shared__ __attribute__((aligned(16))) float ws[RK][RE];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
-  // staging: thread q loads 8 features (chunk q % 4) of token row q / 4 and of expert rows q / 4
-  // and q / 4 + 32
+  // staging: thread q loads 8 features (chunk q % 4) of expert row q / 4, and threads q < 128 the
+  // same of token row q / 4
   const int sr = tid >> 2, sk = (tid & 3) * 8;
-  const bool xok = t0 + sr < T, w0ok = e0 + sr < E, w1ok = e0 + sr + 32 < E;
-  const size_t xoff = (size_t)(xok ? t0 + sr : 0) * d, w0off = (size_t)(w0ok ? e0 + sr : 0) * d,
-               w1off = (size_t)(w1ok ? e0 + sr + 32 : 0) * d;
-  float xr[8], wr0[8], wr1[8];
+  const bool xload = tid < 128;
+  const bool xok = xload && t0 + sr < T, wok = e0 + sr < E;
+  const size_t xoff = (size_t)(xok ? t0 + sr : 0) * d, woff = (size_t)(wok ? e0 + sr : 0) * d;
+  float xr[8], wr[8];
   row8<BF16>(xv, xoff, sk, d, xok, xr);
-  row8<BF16>(wv, w0off, sk, d, w0ok, wr0);
-  row8<BF16>(wv, w1off, sk, d, w1ok, wr1);
-  float acc[4][4];
+  row8<BF16>(wv, woff, sk, d, wok, wr);
+  float acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
   for (int k0 = 0; k0 < d; k0 += RK) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      xs[sk + i][sr] = xr[i];
-      ws[sk + i][sr] = wr0[i];
-      ws[sk + i][sr + 32] = wr1[i];
+      if (xload) xs[sk + i][sr] = xr[i];
+      ws[sk + i][sr] = wr[i];
     }
     __syncthreads();
     if (k0 + RK < d) {
       row8<BF16>(xv, xoff, k0 + RK + sk, d, xok, xr);
-      row8<BF16>(wv, w0off, k0 + RK + sk, d, w0ok, wr0);
-      row8<BF16>(wv, w1off, k0 + RK + sk, d, w1ok, wr1);
+      row8<BF16>(wv, woff, k0 + RK + sk, d, wok, wr);
     }
     const int kn = d - k0 < RK ? d - k0 : RK;
     if (kn == RK) {
@@ -123,8 +120,8 @@ __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, cons
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + ty * 2 + i;
     if (t >= T) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -745,34 +745,49 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& p, const OutWins&
   store_block<MODE>(p, o, br, bc, v, u, x, ksplit, lane);
 }
 
+// Blocks whose pre-activations are in flight ahead of the block being stored.
+constexpr int AUX_AHEAD = 2;
+
 // Memory instructions issued after the pre-activation loads of block IDX and before the wait for
-// them: the stores of block IDX-1 and the loads of block IDX+1 (4 each).
+// them: the stores of the AUX_AHEAD blocks before it and the loads of the AUX_AHEAD blocks after
+// it (4 each; block j's loads are issued before the wait of block j - AUX_AHEAD).
 template <int IDX, int NB>
 constexpr int aux_younger() {
-  return (IDX >= 1 ? 4 : 0) + (IDX + 1 < NB ? 4 : 0);
+  return 4 * (IDX < AUX_AHEAD ? IDX : AUX_AHEAD) + 4 * (NB - 1 - IDX < AUX_AHEAD ? NB - 1 - IDX : AUX_AHEAD);
 }
 
 // Blocks IDX.. of the wave's accumulators, unrolled at compile time (the loop unroller gives up on
 // the larger epilogues, and a run-time block index would put the accumulators in scratch memory).
-// The down-projection dgrad keeps the pre-activation loads one block ahead of their use.
+// The down-projection dgrad keeps the pre-activation loads AUX_AHEAD blocks ahead of their use.
 template <int MODE, bool HALF, int IDX>
 __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& o, const f32x16_t (&acc)[MI][NI],
-                                              int row0, int col0, int m_end, int lane, AuxBlock (&aux)[2],
-                                              int ksplit) {
+                                              int row0, int col0, int m_end, int lane,
+                                              AuxBlock (&aux)[AUX_AHEAD + 1], int ksplit) {
   constexpr int NJ = out_nj<MODE, HALF>();
   constexpr int NB = MI * NJ;
+  constexpr int NA = AUX_AHEAD + 1;
   if constexpr (IDX < NB) {
     if constexpr (MODE == GEMM_DOWN_BWD) {
-      if constexpr (IDX + 1 < NB)
-        load_aux(p, row0 + block_r<MODE, HALF, IDX + 1>(), m_end, col0 + block_c<MODE, HALF, IDX + 1>(),
-                 aux[(IDX + 1) % 2], lane);
-      wait_aux<aux_younger<IDX, NB>()>(aux[IDX % 2]);
+      if constexpr (IDX + AUX_AHEAD < NB)
+        load_aux(p, row0 + block_r<MODE, HALF, IDX + AUX_AHEAD>(), m_end,
+                 col0 + block_c<MODE, HALF, IDX + AUX_AHEAD>(), aux[(IDX + AUX_AHEAD) % NA], lane);
+      wait_aux<aux_younger<IDX, NB>()>(aux[IDX % NA]);
     }
     constexpr int mi = IDX / NJ, ni = IDX % NJ;
     constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NJ : ni;
     epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, HALF, IDX>(), block_c<MODE, HALF, IDX>(),
-                         aux[IDX % 2], ksplit, lane);
+                         aux[IDX % NA], ksplit, lane);
     epilogue_from<MODE, HALF, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
+  }
+}
+
+// Pre-activation loads of blocks IDX..AUX_AHEAD-1, issued in block order before the first store.
+template <int MODE, bool HALF, int IDX>
+__device__ __forceinline__ void aux_prologue(const GemmArgs& p, int row0, int col0, int m_end,
+                                             AuxBlock (&aux)[AUX_AHEAD + 1], int lane) {
+  if constexpr (IDX < AUX_AHEAD && IDX < MI * out_nj<MODE, HALF>()) {
+    load_aux(p, row0 + block_r<MODE, HALF, IDX>(), m_end, col0 + block_c<MODE, HALF, IDX>(), aux[IDX], lane);
+    aux_prologue<MODE, HALF, IDX + 1>(p, row0, col0, m_end, aux, lane);
   }
 }
 
@@ -789,9 +804,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
   else col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 64 : t.nt * BN + wn * 128;
   const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
   const int ksplit = t.ks;
-  AuxBlock aux[2];
-  if constexpr (MODE == GEMM_DOWN_BWD)
-    load_aux(p, row0 + block_r<MODE, HALF, 0>(), t.m_end, col0 + block_c<MODE, HALF, 0>(), aux[0], lane);
+  AuxBlock aux[AUX_AHEAD + 1];
+  if constexpr (MODE == GEMM_DOWN_BWD) aux_prologue<MODE, HALF, 0>(p, row0, col0, t.m_end, aux, lane);
   epilogue_from<MODE, HALF, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
 }
 

@@ -288,6 +288,79 @@ moe_status_t moe_router_aux_bwd(const float* logits, const float* load_frac, con
                                 void* dx_router, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
+/* MXFP8 grouped GEMMs                                                                          */
+/* The pages train their largest operating points with an MXFP8 recipe ("Olmo-core DDP MoE
+ * examples", "Production throughput runs", operating-point table; "Other experiments in the
+ * report", MXFP8 ablation of the MLP) without defining the format.  Reading implemented: OCP
+ * Microscaling (MX) v1.0 MXFP8 -- E4M3 elements (bias 7, largest magnitude 448, no infinities)
+ * and one E8M0 scale byte s (value 2^(s - 127)) per 32 consecutive elements of the CONTRACTION
+ * axis.  Quantizing a block: shared exponent = floor(log2(max |v|)) - 8 clamped to [-127, 127]
+ * (-127 for an all-zero block); each element becomes E4M3(v / 2^shared), rounded to nearest with
+ * ties to even, magnitudes above 448 saturated to 448.  Codes and scales are exact (bitwise equal
+ * to that definition).  A product of MX operands is the product of the dequantized matrices; it is
+ * accumulated in fp32 and stored as bf16.  Inputs of the quantizers are bf16; NaN/Inf unsupported. */
+
+/* Quantize x [R, K] (bf16, row stride ldx elements) along its rows:
+ *   codes  [R, K] uint8 OUTPUT (E4M3), scales [R, K/32] uint8 OUTPUT (E8M0).
+ * K must be a multiple of 32, ldx a multiple of 8 and >= K.  R = 0 is a no-op. */
+moe_status_t moe_mx_quantize_rows(const void* x, int64_t R, int64_t K, int64_t ldx, uint8_t* codes,
+                                  uint8_t* scales, moe_stream_t stream);
+
+/* Minimum row stride (bytes) of moe_mx_quantize_cols' output for R rows in G groups padded to kpad. */
+int64_t moe_mx_quantize_cols_ld(int64_t R, int32_t G, int32_t kpad);
+
+/* Quantize x [R, N] (bf16, row stride ldx elements) along its COLUMNS, one row range per group,
+ * and store it transposed (contraction axis last), for the weight gradients whose contraction
+ * runs over the rows an expert received:
+ *   group g = rows offsets[g]..offsets[g+1]-1 (offsets [G+1] int32 device, clamped to [0, R]) or,
+ *   when offsets is NULL, rows g*group_rows..(g+1)*group_rows-1 (then R must equal G*group_rows);
+ *   each group is padded with zero rows to a multiple of kpad (a multiple of 128);
+ *   kbase  [G+1] int32 OUTPUT: first column of each group (kbase[G] = total padded length);
+ *   codes  [N, ldc] uint8 OUTPUT, group g at columns kbase[g]..kbase[g+1]-1, columns past
+ *          kbase[G] hold zero codes; scales [N, ldc/32] uint8 OUTPUT alike.
+ * ldc must be a multiple of 128 and >= moe_mx_quantize_cols_ld(R, G, kpad) (offsets given) or
+ * G * round_up(group_rows, kpad) (offsets NULL).  N and ldx must be even; G <= 1024. */
+moe_status_t moe_mx_quantize_cols(const void* x, int64_t R, int64_t N, int64_t ldx, const int32_t* offsets,
+                                  int32_t G, int64_t group_rows, int32_t kpad, uint8_t* codes, uint8_t* scales,
+                                  int64_t ldc, int32_t* kbase, moe_stream_t stream);
+
+typedef enum {
+  MOE_MX_EPI_STORE = 0,      /* out0 [M, N] bf16 = C */
+  MOE_MX_EPI_SWIGLU = 1,     /* B holds 2N rows per group (rows 0..N-1: gate W1, N..2N-1: up W3);
+                                G1 = A B_gate^T, G3 = A B_up^T; out2 [M, N] = silu(G1) * G3,
+                                out0 / out1 [M, N] = G1 / G3 (each may be NULL) */
+  MOE_MX_EPI_SWIGLU_BWD = 2  /* C = dH; aux0, aux1 [M, N] bf16 = the stashed G1, G3;
+                                out0 [M, 2N] = [dH * G3 * s (1 + G1 (1 - s)) | dH * G1 * s],
+                                s = sigmoid(G1) */
+} moe_mx_epilogue_t;
+
+/* Grouped product over ragged ROW ranges (forward and data-gradient GEMMs):
+ *   C[m, n] = sum_k A[m, k] B_g[n, k] for rows m of group g = offsets[g]..offsets[g+1]-1
+ *   a_codes [M, K], a_scales [M, K/32] (from moe_mx_quantize_rows);
+ *   B_g row n at b_codes + g*b_group_stride + n*b_row_stride, its scales at
+ *   b_scales + (g*b_group_stride + n*b_row_stride)/32 (B has N rows, 2N for MOE_MX_EPI_SWIGLU);
+ *   offsets [G+1] int32 device (clamped to [0, M]; rows outside every group are not written).
+ * K must be a multiple of 128, N of 128 (64 for MOE_MX_EPI_SWIGLU), both strides multiples of 128.
+ * ws: moe_mx_gemm_workspace_size(G) bytes. */
+size_t moe_mx_gemm_workspace_size(int32_t G);
+moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                              const uint8_t* b_scales, int64_t b_row_stride, int64_t b_group_stride,
+                              const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
+                              void* out0, void* out1, void* out2, const void* aux0, const void* aux1, void* ws,
+                              size_t ws_bytes, moe_stream_t stream);
+
+/* Grouped product over ragged CONTRACTION ranges (weight gradients):
+ *   C_g[m, n] = sum_{k in [kbase[g], kbase[g+1])} A[m, k] B[n, k]
+ *   a_codes [M, lda], b_codes [N, ldb] (from moe_mx_quantize_cols, same kbase), scales alike /32;
+ *   rows m < split go to out0 [G, split, N], rows m >= split to out1 [G, M - split, N] (bf16);
+ *   a group with no rows gets exact zeros.  kbase is device data the call cannot check: it must be
+ *   non-decreasing with kbase[G] <= min(lda, ldb) (moe_mx_quantize_cols writes such a kbase).
+ * M and N must be multiples of 128, lda and ldb multiples of 128, kbase multiples of 128. */
+moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int64_t lda, const uint8_t* b_codes,
+                           const uint8_t* b_scales, int64_t ldb, const int32_t* kbase, int32_t G, int64_t M,
+                           int64_t N, int64_t split, void* out0, void* out1, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
 /* Utilities                                                                                   */
 
 const char* moe_status_string(moe_status_t status);

@@ -20,7 +20,7 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe.so")
 
 SOURCES = ["api.cpp", "route.hip", "router_aux.hip", "dispatch.hip", "combine.hip", "grouped_gemm.hip",
-           "grouped_gemm_pipe.hip"]
+           "grouped_gemm_pipe.hip", "mxfp8.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions stay off: plain scalar fp32 code only.

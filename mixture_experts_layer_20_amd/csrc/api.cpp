@@ -3,6 +3,7 @@
 // synchronises, never allocates, and reports errors through status codes.
 #include "libmoe.h"
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -482,6 +483,140 @@ moe_status_t moe_router_aux_bwd(const float* logits, const float* load_frac, con
   return hip_check(moe::launch_router_aux_bwd(logits, load_frac, x, w_router, (int)T, (int)d, E, weight,
                                               dt == MOE_BF16, dw_router, dx_router, ws, S(stream)),
                    "router load-balancing backward");
+}
+
+// ---------------------------------------------------------------------------------------------
+// MXFP8
+
+moe_status_t moe_mx_quantize_rows(const void* x, int64_t R, int64_t K, int64_t ldx, uint8_t* codes,
+                                  uint8_t* scales, moe_stream_t stream) {
+  g_err.clear();
+  CHECK(R >= 0 && K > 0, MOE_ERR_INVALID_VALUE, "R must be >= 0 and K > 0 (got R=%lld, K=%lld)", (long long)R,
+        (long long)K);
+  CHECK(K % 32 == 0, MOE_ERR_UNSUPPORTED, "K must be a multiple of 32 (got %lld)", (long long)K);
+  CHECK(ldx >= K && ldx % 8 == 0, MOE_ERR_INVALID_VALUE, "ldx must be >= K and a multiple of 8 (got %lld)",
+        (long long)ldx);
+  CHECK(K <= kMaxInt && R <= kMaxInt, MOE_ERR_UNSUPPORTED, "R and K must fit in int32");
+  if (R == 0) return MOE_OK;
+  CHECK(x && codes && scales, MOE_ERR_INVALID_VALUE, "x/codes/scales is NULL");
+  return hip_check(moe::launch_mx_quant_rows(x, R, (int)K, ldx, codes, scales, S(stream)), "MXFP8 row quantization");
+}
+
+int64_t moe_mx_quantize_cols_ld(int64_t R, int32_t G, int32_t kpad) {
+  if (R < 0 || G <= 0 || kpad <= 0) return 0;
+  // Only a non-empty group adds padding, at most kpad - 1 rows.
+  return (R + std::min<int64_t>(G, R) * (kpad - 1)) / kpad * kpad;
+}
+
+moe_status_t moe_mx_quantize_cols(const void* x, int64_t R, int64_t N, int64_t ldx, const int32_t* offsets,
+                                  int32_t G, int64_t group_rows, int32_t kpad, uint8_t* codes, uint8_t* scales,
+                                  int64_t ldc, int32_t* kbase, moe_stream_t stream) {
+  g_err.clear();
+  CHECK(R >= 0 && N > 0, MOE_ERR_INVALID_VALUE, "R must be >= 0 and N > 0");
+  CHECK(N % 2 == 0 && ldx >= N && ldx % 2 == 0, MOE_ERR_UNSUPPORTED, "N and ldx must be even, ldx >= N");
+  CHECK(G > 0 && G <= 1024, MOE_ERR_INVALID_VALUE, "G must be in [1, 1024] (got %d)", G);
+  CHECK(kpad > 0 && kpad % 128 == 0, MOE_ERR_UNSUPPORTED, "kpad must be a positive multiple of 128 (got %d)",
+        kpad);
+  CHECK(ldc % 128 == 0 && ldc >= 0, MOE_ERR_INVALID_VALUE, "ldc must be a multiple of 128 (got %lld)",
+        (long long)ldc);
+  CHECK(R <= kMaxInt && N <= kMaxInt && ldc <= kMaxInt, MOE_ERR_UNSUPPORTED, "sizes must fit in int32");
+  int64_t need;
+  if (offsets) {
+    need = moe_mx_quantize_cols_ld(R, G, kpad);
+  } else {
+    CHECK(group_rows >= 0 && R == (int64_t)G * group_rows, MOE_ERR_INVALID_VALUE,
+          "without offsets R must equal G * group_rows (got R=%lld, G=%d, group_rows=%lld)", (long long)R, G,
+          (long long)group_rows);
+    need = (int64_t)G * ((group_rows + kpad - 1) / kpad * kpad);
+  }
+  CHECK(ldc >= need, MOE_ERR_INVALID_VALUE, "ldc must be >= %lld (got %lld)", (long long)need, (long long)ldc);
+  CHECK(kbase && (ldc == 0 || (codes && scales)), MOE_ERR_INVALID_VALUE, "kbase/codes/scales is NULL");
+  CHECK(R == 0 || x, MOE_ERR_INVALID_VALUE, "x is NULL");
+  return hip_check(moe::launch_mx_quant_cols(x, R, (int)N, ldx, offsets, G, group_rows, kpad, codes, scales, ldc,
+                                             kbase, S(stream)),
+                   "MXFP8 column quantization");
+}
+
+size_t moe_mx_gemm_workspace_size(int32_t G) {
+  if (G <= 0) return 0;
+  return align256((size_t)(G + 1) * sizeof(int32_t));
+}
+
+moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                              const uint8_t* b_scales, int64_t b_row_stride, int64_t b_group_stride,
+                              const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
+                              void* out0, void* out1, void* out2, const void* aux0, const void* aux1, void* ws,
+                              size_t ws_bytes, moe_stream_t stream) {
+  g_err.clear();
+  CHECK(epilogue >= MOE_MX_EPI_STORE && epilogue <= MOE_MX_EPI_SWIGLU_BWD, MOE_ERR_INVALID_VALUE,
+        "unknown epilogue %d", epilogue);
+  CHECK(G > 0 && G <= 1024, MOE_ERR_INVALID_VALUE, "G must be in [1, 1024] (got %d)", G);
+  CHECK(M >= 0 && N > 0 && K > 0, MOE_ERR_INVALID_VALUE, "M must be >= 0, N and K > 0");
+  const int oc = epilogue == MOE_MX_EPI_SWIGLU ? 64 : 128;
+  CHECK(K % 128 == 0 && N % oc == 0, MOE_ERR_UNSUPPORTED, "K must be a multiple of 128 and N of %d", oc);
+  CHECK(b_row_stride >= K && b_row_stride % 128 == 0 && b_group_stride >= 0 && b_group_stride % 128 == 0,
+        MOE_ERR_INVALID_VALUE, "B strides must be multiples of 128, the row stride >= K");
+  CHECK(M <= kMaxInt && N <= kMaxInt / 2 && K <= kMaxInt, MOE_ERR_UNSUPPORTED, "sizes must fit in int32");
+  CHECK(((M + 127) / 128 + G) * (N / oc) < kMaxInt, MOE_ERR_UNSUPPORTED, "grid too large");
+  CHECK(a_codes && a_scales && b_codes && b_scales && offsets, MOE_ERR_INVALID_VALUE, "an operand pointer is NULL");
+  if (epilogue == MOE_MX_EPI_STORE) CHECK(out0, MOE_ERR_INVALID_VALUE, "out0 is NULL");
+  if (epilogue == MOE_MX_EPI_SWIGLU) CHECK(out2, MOE_ERR_INVALID_VALUE, "out2 is NULL");
+  if (epilogue == MOE_MX_EPI_SWIGLU_BWD) CHECK(out0 && aux0 && aux1, MOE_ERR_INVALID_VALUE, "out0/aux0/aux1 is NULL");
+  const size_t need = moe_mx_gemm_workspace_size(G);
+  CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+        ws ? ws_bytes : (size_t)0);
+  if (M == 0) return MOE_OK;
+  moe::MxGemmArgs a{};
+  a.a = a_codes;
+  a.as = a_scales;
+  a.lda = K;
+  a.b = b_codes;
+  a.bs = b_scales;
+  a.ldb = b_row_stride;
+  a.b_gstride = b_group_stride;
+  a.offsets = offsets;
+  a.tile_prefix = reinterpret_cast<int32_t*>(ws);
+  a.G = G;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.out0 = out0;
+  a.out1 = out1;
+  a.out2 = out2;
+  a.aux0 = aux0;
+  a.aux1 = aux1;
+  return hip_check(moe::launch_mx_gemm(epilogue, false, a, S(stream)), "MXFP8 grouped GEMM (rows)");
+}
+
+moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int64_t lda, const uint8_t* b_codes,
+                           const uint8_t* b_scales, int64_t ldb, const int32_t* kbase, int32_t G, int64_t M,
+                           int64_t N, int64_t split, void* out0, void* out1, moe_stream_t stream) {
+  g_err.clear();
+  CHECK(G > 0 && G <= 1024, MOE_ERR_INVALID_VALUE, "G must be in [1, 1024] (got %d)", G);
+  CHECK(M > 0 && N > 0 && split >= 0 && split <= M, MOE_ERR_INVALID_VALUE, "M, N must be > 0, split in [0, M]");
+  CHECK(M % 128 == 0 && N % 128 == 0, MOE_ERR_UNSUPPORTED, "M and N must be multiples of 128");
+  CHECK(lda > 0 && ldb > 0 && lda % 128 == 0 && ldb % 128 == 0, MOE_ERR_INVALID_VALUE,
+        "lda and ldb must be positive multiples of 128");
+  CHECK(M <= kMaxInt && N <= kMaxInt && lda <= kMaxInt && ldb <= kMaxInt, MOE_ERR_UNSUPPORTED,
+        "sizes must fit in int32");
+  CHECK((int64_t)G * (M / 128) * (N / 128) < kMaxInt, MOE_ERR_UNSUPPORTED, "grid too large");
+  CHECK(a_codes && a_scales && b_codes && b_scales && kbase, MOE_ERR_INVALID_VALUE, "an operand pointer is NULL");
+  CHECK((split == 0 || out0) && (split == M || out1), MOE_ERR_INVALID_VALUE, "out0/out1 is NULL");
+  moe::MxGemmArgs a{};
+  a.a = a_codes;
+  a.as = a_scales;
+  a.lda = lda;
+  a.b = b_codes;
+  a.bs = b_scales;
+  a.ldb = ldb;
+  a.offsets = kbase;
+  a.G = G;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.out0 = out0;
+  a.out1 = out1;
+  a.split = (int)split;
+  return hip_check(moe::launch_mx_gemm(MOE_MX_EPI_STORE, true, a, S(stream)), "MXFP8 grouped GEMM (K)");
 }
 
 }  // extern "C"

@@ -1,0 +1,530 @@
+// MXFP8 quantization and grouped GEMMs on gfx950's block-scaled FP8 matrix instruction.
+//
+// The pages run their largest operating points with an MXFP8 recipe (Olmo-core DDP MoE examples,
+// "Production throughput runs", operating-point table, and "Other experiments in the report") but
+// do not define the format.  Reading taken: the OCP Microscaling (MX) v1.0 MXFP8 format with E4M3
+// elements, one E8M0 scale (a power of two 2^(byte - 127)) per 32 consecutive elements of the
+// contraction axis; shared exponent floor(log2(block max)) - 8, clamped to [-127, 127] (-127 for an
+// all-zero block); elements rounded to nearest, ties to even, magnitudes past 448 saturated to 448.
+//
+// Quantization works on the bit patterns (integer shifts with round-to-nearest-even), so every code
+// and every scale byte is exact.  The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4: lane i + 32h of
+// an operand holds row i, bytes 0..15 in the first 32-element block of the 64-wide K step (k =
+// 16h..16h+15) and bytes 16..31 in the second (k = 32+16h..); the scale of block b of row i comes
+// from lane i + 32b.  Products of E4M3 values and power-of-two scales are exact in fp32, and are
+// accumulated in fp32.
+//
+// GEMM design: one workgroup = one 128x128 output tile (4 waves, 2x2, 64x64 each), K consumed 128
+// bytes (= 128 elements) per step through a double-buffered LDS tile (16 KiB per operand and
+// buffer) with 128-byte row segments, 16-byte chunks XOR-swizzled by (row >> 1) & 7 so a
+// ds_read_b128 over 16 rows hits 16 distinct bank groups.  The B operand is the instruction's first
+// operand, so each lane's accumulators hold 4 consecutive output columns of one row.
+#include "common.h"
+
+#include <algorithm>
+
+namespace moe {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+// Native vectors: HIP's uint4 is a class, which keeps arrays of it out of registers.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---- E4M3 / E8M0 --------------------------------------------------------------------------
+
+// floor(log2(v)) of a positive finite fp32 magnitude given by its bits.
+__device__ __forceinline__ int floor_log2_bits(uint32_t a) {
+  const int ex = (int)(a >> 23);
+  return ex ? ex - 127 : (31 - __clz(a)) - 149;
+}
+
+// Shared exponent of a block from the bits of its largest magnitude.
+__device__ __forceinline__ int mx_shared_exp(uint32_t amax) {
+  if (amax == 0) return -127;
+  const int e = floor_log2_bits(amax) - 8;   // 8: exponent of E4M3's largest binade (448 = 1.75 * 2^8)
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// x / 2^s rounded to nearest, ties to even (1 <= s <= 31).
+__device__ __forceinline__ uint32_t rne_shr(uint32_t x, int s) {
+  const uint32_t q = x >> s, rem = x & ((1u << s) - 1u), half = 1u << (s - 1);
+  return q + (uint32_t)((rem > half) | ((rem == half) & (q & 1u)));
+}
+
+// E4M3 code of v / 2^e (v given by its fp32 bits).
+__device__ __forceinline__ uint32_t e4m3_code(uint32_t bits, int e) {
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t a = bits & 0x7fffffffu;
+  if (a == 0) return sign;
+  uint32_t sig;
+  int lg;
+  if (a >> 23) {
+    sig = (a & 0x7fffffu) | 0x800000u;
+    lg = (int)(a >> 23) - 127;
+  } else {  // fp32 subnormal: normalise the significand
+    const int lz = __clz(a) - 8;
+    sig = a << lz;
+    lg = -126 - lz;
+  }
+  const int ey = lg - e;  // binade of the scaled value
+  uint32_t code;
+  if (ey >= -6) {  // normal E4M3: keep 3 fraction bits
+    if (ey > 8) return sign | 0x7eu;
+    uint32_t r = rne_shr(sig, 20);  // 8..16
+    int eb = ey + 7;
+    if (r == 16) {
+      r = 8;
+      ++eb;
+    }
+    code = ((uint32_t)eb << 3) | (r - 8);
+    if (code > 0x7eu) code = 0x7eu;  // 480 and up saturate to 448
+  } else {  // subnormal E4M3: multiples of 2^-9 (a result of 8 is the smallest normal, code 8)
+    const int s = 14 - ey;
+    code = s >= 25 ? 0u : rne_shr(sig, s);
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ uint32_t bf16_bits_f32(uint32_t h) { return h << 16; }
+
+// ---- Row quantization: 8 elements per lane, 4 lanes per block ---------------------------------
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16_t* __restrict__ x, long long R, int K,
+                                                            long long ldx, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const int nch = K >> 3;
+  const long long total = R * nch;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const long long r = i / nch;
+    const int c = (int)(i - r * nch);
+    const uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + (long long)c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = max(amax, (w[j] & 0x7fffu) << 16);
+      amax = max(amax, (w[j] >> 16 & 0x7fffu) << 16);
+    }
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+    const int e = mx_shared_exp(amax);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lo |= e4m3_code(bf16_bits_f32(w[j] & 0xffffu), e) << (16 * j);
+      lo |= e4m3_code(bf16_bits_f32(w[j] >> 16), e) << (16 * j + 8);
+      hi |= e4m3_code(bf16_bits_f32(w[j + 2] & 0xffffu), e) << (16 * j);
+      hi |= e4m3_code(bf16_bits_f32(w[j + 2] >> 16), e) << (16 * j + 8);
+    }
+    *reinterpret_cast<uint2*>(codes + r * K + (long long)c * 8) = make_uint2(lo, hi);
+    if ((c & 3) == 0) scales[r * (K >> 5) + (c >> 2)] = (uint8_t)(e + 127);
+  }
+}
+
+// ---- Group prefixes -------------------------------------------------------------------------
+// out[g] = mult * sum_{j<g} ceil(len_j / unit), len_j the clamped row count of group j (offsets, or
+// group_rows each when offsets is null).  One workgroup of 1024 threads, G <= 1024.
+__global__ __launch_bounds__(1024) void mx_prefix_kernel(const int32_t* __restrict__ offsets, int G,
+                                                         long long group_rows, long long R, int unit, int mult,
+                                                         int32_t* __restrict__ out) {
+  __shared__ int buf[1024];
+  const int t = threadIdx.x;
+  int v = 0;
+  if (t < G) {
+    long long len;
+    if (offsets) {
+      const long long lo = min(max((long long)offsets[t], 0LL), R);
+      const long long hi = min(max((long long)offsets[t + 1], lo), R);
+      len = hi - lo;
+    } else {
+      len = group_rows;
+    }
+    v = (int)((len + unit - 1) / unit);
+  }
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int add = t >= o ? buf[t - o] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  if (t < G) out[t + 1] = buf[t] * mult;
+  if (t == 0) out[0] = 0;
+}
+
+// ---- Column quantization: a 32-row block of one group x 512 columns per workgroup ------------
+__global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __restrict__ x, long long R, int N,
+                                                            long long ldx, const int32_t* __restrict__ offsets,
+                                                            int G, long long group_rows,
+                                                            const int32_t* __restrict__ kbase,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales, long long ldc) {
+  const long long k0 = (long long)blockIdx.x * 32;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 2;
+  const long long ktot = kbase[G];
+  long long r0 = 0, rhi = 0;  // source rows of this block: [r0, min(r0 + 32, rhi))
+  if (k0 < ktot) {
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (kbase[mid] <= k0) lo = mid; else hi = mid;
+    }
+    long long glo, ghi;
+    if (offsets) {
+      glo = min(max((long long)offsets[lo], 0LL), R);
+      ghi = min(max((long long)offsets[lo + 1], glo), R);
+    } else {
+      glo = (long long)lo * group_rows;
+      ghi = glo + group_rows;
+    }
+    r0 = glo + (k0 - kbase[lo]);
+    rhi = ghi;
+  }
+  if (n >= N) return;
+  uint32_t v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    v[j] = r0 + j < rhi ? *reinterpret_cast<const uint32_t*>(x + (r0 + j) * ldx + n) : 0u;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = max(amax, ((v[j] >> (16 * c)) & 0x7fffu) << 16);
+    const int e = mx_shared_exp(amax);
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      w[q] = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        w[q] |= e4m3_code(bf16_bits_f32((v[4 * q + b] >> (16 * c)) & 0xffffu), e) << (8 * b);
+    }
+    uint8_t* dst = codes + (long long)(n + c) * ldc + k0;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[(long long)(n + c) * (ldc >> 5) + blockIdx.x] = (uint8_t)(e + 127);
+  }
+}
+
+// ---- Grouped GEMM ---------------------------------------------------------------------------
+constexpr int TB = 128;               // tile rows = tile columns = K step (bytes)
+constexpr int OPBYTES = TB * TB;      // one operand tile of one buffer: 16 KiB
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ uint32_t bf16pack(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Operand fragment of a 32-row block for K step half s: row i = lane & 31, chunks 4s + h and
+// 4s + 2 + h (h = lane >> 5) of the 128-byte row.
+__device__ __forceinline__ i32x8_t read_frag(const uint8_t* tile, int row, int s, int h) {
+  const uint8_t* base = tile + row * TB;
+  const int sw = swz(row);
+  const u32x4_t p = *reinterpret_cast<const u32x4_t*>(base + 16 * ((4 * s + h) ^ sw));
+  const u32x4_t q = *reinterpret_cast<const u32x4_t*>(base + 16 * ((4 * s + 2 + h) ^ sw));
+  i32x8_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = (int)p[j];
+    r[4 + j] = (int)q[j];
+  }
+  return r;
+}
+
+template <int EPI, bool RK>
+__global__ __launch_bounds__(256, 2) void mx_gemm_kernel(MxGemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][OPBYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, li = lane & 31, h = lane >> 5;
+  // Output columns per tile: the SwiGLU tile multiplies 64 gate and 64 up columns.
+  constexpr int OC = EPI == MX_EPI_SWIGLU ? 64 : 128;
+  const int NT = p.N / OC;
+
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD one contiguous run of tiles.
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int per = nb >> 3;
+  int Lt;
+  {
+    const int xcd = b & 7, idx = b >> 3;
+    const int rem = nb & 7;  // the first `rem` XCDs get one more
+    const int start = xcd * per + min(xcd, rem);
+    Lt = start + idx;
+  }
+  const int nt = Lt % NT;
+  int g, m0, m_end;
+  long long kb0, kb1;
+  if constexpr (!RK) {
+    const int mt = Lt / NT;
+    if (mt >= p.tile_prefix[p.G]) return;
+    int lo = 0, hi = p.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tile_prefix[mid] <= mt) lo = mid; else hi = mid;
+    }
+    g = lo;
+    const int r0 = min(max(p.offsets[g], 0), p.M);
+    const int r1 = min(max(p.offsets[g + 1], r0), p.M);
+    m0 = r0 + (mt - p.tile_prefix[g]) * TB;
+    m_end = r1;
+    kb0 = 0;
+    kb1 = p.K;
+  } else {
+    const int MT = p.M / TB;
+    const int r = Lt / NT;
+    if (r >= p.G * MT) return;
+    g = r / MT;
+    m0 = (r - g * MT) * TB;
+    m_end = p.M;
+    kb0 = p.offsets[g];
+    kb1 = p.offsets[g + 1];
+  }
+  const int nk = (int)((kb1 - kb0) / TB);
+
+  // Global load slots: thread loads rows (tid >> 3) + 32j, 16-byte chunk tid & 7, of both operands.
+  const int lrow = tid >> 3, lch = tid & 7;
+  const uint8_t* ga[4];
+  const uint8_t* gb[4];
+  const uint8_t* bbase = p.b + (RK ? 0 : (long long)g * p.b_gstride);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = lrow + 32 * j;
+    const int ar = RK ? m0 + r : min(m0 + r, m_end - 1);
+    ga[j] = p.a + (long long)ar * p.lda + kb0 + 16 * lch;
+    int br;
+    if constexpr (EPI == MX_EPI_SWIGLU) {
+      // tile row r: wave column r >> 6, block (r >> 5) & 1 (0: gate rows, 1: up rows), column r & 31
+      br = ((r >> 5) & 1) * p.N + nt * 64 + (r >> 6) * 32 + (r & 31);
+    } else {
+      br = nt * TB + r;
+    }
+    gb[j] = bbase + (long long)br * p.ldb + kb0 + 16 * lch;
+  }
+  const int lofs = lrow * TB + 16 * (lch ^ swz(lrow));  // + 32 * TB * j
+
+  // Scale words (4 blocks of one K step) of this lane's fragment rows, shifted by 8h so that byte 0
+  // (step half 0) and byte 2 (step half 1) are this lane's blocks.
+  const uint8_t* sa_p[2];
+  const uint8_t* sb_p[2];
+  const long long lda_s = p.lda >> 5, ldb_s = p.ldb >> 5;
+  const uint8_t* bsbase = p.bs + (RK ? 0 : (long long)g * (p.b_gstride >> 5));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = wm * 64 + q * 32 + li;
+    const int ar = RK ? m0 + r : min(m0 + r, m_end - 1);
+    sa_p[q] = p.as + (long long)ar * lda_s + (kb0 >> 5);
+    const int c = wn * 64 + q * 32 + li;
+    int br;
+    if constexpr (EPI == MX_EPI_SWIGLU) br = q * p.N + nt * 64 + wn * 32 + li;
+    else br = nt * TB + c;
+    sb_p[q] = bsbase + (long long)br * ldb_s + (kb0 >> 5);
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  u32x4_t ra[4], rb[4];
+  uint32_t sa_c[2], sb_c[2], sa_n[2] = {0, 0}, sb_n[2] = {0, 0};
+  if (nk > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = *reinterpret_cast<const u32x4_t*>(ga[j]);
+      rb[j] = *reinterpret_cast<const u32x4_t*>(gb[j]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      sa_c[q] = *reinterpret_cast<const uint32_t*>(sa_p[q]) >> (8 * h);
+      sb_c[q] = *reinterpret_cast<const uint32_t*>(sb_p[q]) >> (8 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4_t*>(&lds[0][0][lofs + 32 * TB * j]) = ra[j];
+      *reinterpret_cast<u32x4_t*>(&lds[0][1][lofs + 32 * TB * j]) = rb[j];
+    }
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const long long off = (long long)(kt + 1) * TB;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ra[j] = *reinterpret_cast<const u32x4_t*>(ga[j] + off);
+        rb[j] = *reinterpret_cast<const u32x4_t*>(gb[j] + off);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        sa_n[q] = *reinterpret_cast<const uint32_t*>(sa_p[q] + 4 * (kt + 1)) >> (8 * h);
+        sb_n[q] = *reinterpret_cast<const uint32_t*>(sb_p[q] + 4 * (kt + 1)) >> (8 * h);
+      }
+    }
+    const uint8_t* ta = lds[cur][0];
+    const uint8_t* tb = lds[cur][1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      i32x8_t fa[2], fb[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        fa[q] = read_frag(ta, wm * 64 + q * 32 + li, s, h);
+        fb[q] = read_frag(tb, wn * 64 + q * 32 + li, s, h);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (s == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0,
+                                                                        (int)sb_c[j], 0, (int)sa_c[i]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 2,
+                                                                        (int)sb_c[j], 2, (int)sa_c[i]);
+        }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<u32x4_t*>(&lds[cur ^ 1][0][lofs + 32 * TB * j]) = ra[j];
+        *reinterpret_cast<u32x4_t*>(&lds[cur ^ 1][1][lofs + 32 * TB * j]) = rb[j];
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        sa_c[q] = sa_n[q];
+        sb_c[q] = sb_n[q];
+      }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds row li of each 32-row block, columns 8*(r/4) + 4h + (r%4).
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + wm * 64 + i * 32 + li;
+    if (!RK && row >= m_end) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (EPI == MX_EPI_SWIGLU) {
+        const int col = nt * 64 + wn * 32 + 8 * q + 4 * h;
+        float hv[4];
+        const long long o = (long long)row * p.N + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = acc[i][0][4 * q + r], bb = acc[i][1][4 * q + r];
+          hv[r] = a * sigmoid_f32(a) * bb;
+        }
+        if (p.out0)
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + o) =
+              make_uint2(bf16pack(acc[i][0][4 * q], acc[i][0][4 * q + 1]),
+                         bf16pack(acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]));
+        if (p.out1)
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out1) + o) =
+              make_uint2(bf16pack(acc[i][1][4 * q], acc[i][1][4 * q + 1]),
+                         bf16pack(acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]));
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out2) + o) =
+            make_uint2(bf16pack(hv[0], hv[1]), bf16pack(hv[2], hv[3]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = nt * TB + wn * 64 + j * 32 + 8 * q + 4 * h;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+          if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
+            const long long o = (long long)row * p.N + col;
+            const uint2 av = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.aux0) + o);
+            const uint2 bv = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.aux1) + o);
+            const uint32_t aw[2] = {av.x, av.y}, bw[2] = {bv.x, bv.y};
+            float da[4], db[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float a = bf16_to_f32((bf16_t)(aw[r >> 1] >> (16 * (r & 1))));
+              const float bb = bf16_to_f32((bf16_t)(bw[r >> 1] >> (16 * (r & 1))));
+              const float sg = sigmoid_f32(a);
+              da[r] = v[r] * bb * sg * (1.0f + a * (1.0f - sg));
+              db[r] = v[r] * a * sg;
+            }
+            bf16_t* dab = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * (2 * p.N);
+            *reinterpret_cast<uint2*>(dab + col) = make_uint2(bf16pack(da[0], da[1]), bf16pack(da[2], da[3]));
+            *reinterpret_cast<uint2*>(dab + p.N + col) =
+                make_uint2(bf16pack(db[0], db[1]), bf16pack(db[2], db[3]));
+          } else {
+            bf16_t* dst;
+            if constexpr (RK) {
+              dst = row < p.split
+                        ? reinterpret_cast<bf16_t*>(p.out0) + ((long long)g * p.split + row) * p.N + col
+                        : reinterpret_cast<bf16_t*>(p.out1) +
+                              ((long long)g * (p.M - p.split) + (row - p.split)) * p.N + col;
+            } else {
+              dst = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * p.N + col;
+            }
+            *reinterpret_cast<uint2*>(dst) = make_uint2(bf16pack(v[0], v[1]), bf16pack(v[2], v[3]));
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, bool RK>
+hipError_t launch_mx(const MxGemmArgs& a, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL((mx_gemm_kernel<EPI, RK>), dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant_rows(const void* x, long long R, int K, long long ldx, uint8_t* codes,
+                                uint8_t* scales, hipStream_t s) {
+  const long long total = R * (K / 8);
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)std::min<long long>((total + 255) / 256, 256LL * 16);
+  hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(x), R,
+                     K, ldx, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_cols(const void* x, long long R, int N, long long ldx, const int32_t* offsets,
+                                int G, long long group_rows, int kpad, uint8_t* codes, uint8_t* scales,
+                                long long ldc, int32_t* kbase, hipStream_t s) {
+  hipLaunchKernelGGL(mx_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, G, group_rows, R, kpad, kpad, kbase);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ldc == 0 || N == 0) return e;
+  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3((unsigned)(ldc / 32), (unsigned)((N + 511) / 512)), dim3(256), 0,
+                     s, reinterpret_cast<const bf16_t*>(x), R, N, ldx, offsets, G, group_rows, kbase, codes,
+                     scales, ldc);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream_t s) {
+  const int OC = epi == MX_EPI_SWIGLU ? 64 : TB;
+  const long long NT = a.N / OC;
+  long long tiles;
+  if (!ragged_k) {
+    hipLaunchKernelGGL(mx_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.G, 0LL, (long long)a.M, TB, 1,
+                       a.tile_prefix);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    tiles = ((long long)(a.M + TB - 1) / TB + a.G) * NT;
+  } else {
+    tiles = (long long)a.G * (a.M / TB) * NT;
+  }
+  if (tiles == 0) return hipSuccess;
+  const int blocks = (int)tiles;
+  if (ragged_k) return launch_mx<MX_EPI_STORE, true>(a, blocks, s);
+  switch (epi) {
+    case MX_EPI_SWIGLU: return launch_mx<MX_EPI_SWIGLU, false>(a, blocks, s);
+    case MX_EPI_SWIGLU_BWD: return launch_mx<MX_EPI_SWIGLU_BWD, false>(a, blocks, s);
+    default: return launch_mx<MX_EPI_STORE, false>(a, blocks, s);
+  }
+}
+
+}  // namespace moe

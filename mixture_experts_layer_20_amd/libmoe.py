@@ -27,6 +27,10 @@ MOE_STAGE_GATE_UP_DGRAD = 3
 MOE_STAGE_DOWN_WGRAD = 4
 MOE_STAGE_GATE_UP_WGRAD = 5
 
+MOE_MX_EPI_STORE = 0
+MOE_MX_EPI_SWIGLU = 1
+MOE_MX_EPI_SWIGLU_BWD = 2
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libmoe.so")
 
 _c = ctypes
@@ -75,6 +79,13 @@ _SIGS = {
     "moe_router_aux_bwd": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _c.c_float, _I32, _P, _P, _P, _SZ, _P]),
     "moe_route_bwd": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P,
                              _P, _SZ, _P]),
+    "moe_mx_quantize_rows": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "moe_mx_quantize_cols_ld": (_I64, [_I64, _I32, _I32]),
+    "moe_mx_quantize_cols": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _I64, _I32, _P, _P, _I64, _P, _P]),
+    "moe_mx_gemm_workspace_size": (_SZ, [_I32]),
+    "moe_mx_gemm_rows": (_I32, [_P, _P, _P, _P, _I64, _I64, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P,
+                                _P, _SZ, _P]),
+    "moe_mx_gemm_k": (_I32, [_P, _P, _I64, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _P, _P, _P]),
     "moe_status_string": (_c.c_char_p, [_I32]),
     "moe_last_error": (_c.c_char_p, []),
     "moe_version": (_c.c_char_p, []),
@@ -284,3 +295,33 @@ def moe_router_aux_bwd(logits, load_frac, x, w_router, T, d, E, weight, dt, dw_r
                        stream=None):
     _call("moe_router_aux_bwd", _ptr(logits), _ptr(load_frac), _ptr(x), _ptr(w_router), T, d, E, weight, dt,
           _ptr(dw_router), _ptr(dx_router), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_mx_quantize_rows(x, R, K, ldx, codes, scales, stream=None):
+    _call("moe_mx_quantize_rows", _ptr(x), R, K, ldx, _ptr(codes), _ptr(scales), _stream(stream))
+
+
+def moe_mx_quantize_cols_ld(R, G, kpad) -> int:
+    return lib().moe_mx_quantize_cols_ld(R, G, kpad)
+
+
+def moe_mx_quantize_cols(x, R, N, ldx, offsets, G, group_rows, kpad, codes, scales, ldc, kbase, stream=None):
+    _call("moe_mx_quantize_cols", _ptr(x), R, N, ldx, _ptr(offsets), G, group_rows, kpad, _ptr(codes),
+          _ptr(scales), ldc, _ptr(kbase), _stream(stream))
+
+
+def moe_mx_gemm_workspace_size(G) -> int:
+    return lib().moe_mx_gemm_workspace_size(G)
+
+
+def moe_mx_gemm_rows(a_codes, a_scales, b_codes, b_scales, b_row_stride, b_group_stride, offsets, G, M, N, K,
+                     epilogue, out0, out1, out2, aux0, aux1, ws, ws_bytes, stream=None):
+    _call("moe_mx_gemm_rows", _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), b_row_stride,
+          b_group_stride, _ptr(offsets), G, M, N, K, epilogue, _ptr(out0), _ptr(out1), _ptr(out2), _ptr(aux0),
+          _ptr(aux1), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_mx_gemm_k(a_codes, a_scales, lda, b_codes, b_scales, ldb, kbase, G, M, N, split, out0, out1,
+                  stream=None):
+    _call("moe_mx_gemm_k", _ptr(a_codes), _ptr(a_scales), lda, _ptr(b_codes), _ptr(b_scales), ldb, _ptr(kbase),
+          G, M, N, split, _ptr(out0), _ptr(out1), _stream(stream))

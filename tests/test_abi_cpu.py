@@ -116,3 +116,38 @@ def test_combine_and_backward_argument_checks(lib):
             L.MOE_BF16, FAKE, FAKE, FAKE, rws)
     _expect(L.MOE_ERR_WORKSPACE, L.moe_route_bwd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 16, 4, 2, 1,
             L.MOE_BF16, FAKE, FAKE, FAKE, rws - 1)
+
+
+def test_mxfp8_argument_checks(lib):
+    q = L.moe_mx_quantize_rows
+    _expect(L.MOE_ERR_UNSUPPORTED, q, FAKE, 4, 48, 48, FAKE, FAKE)          # K not a multiple of 32
+    _expect(L.MOE_ERR_INVALID_VALUE, q, FAKE, 4, 64, 60, FAKE, FAKE)        # ldx < K
+    _expect(L.MOE_ERR_INVALID_VALUE, q, None, 4, 64, 64, FAKE, FAKE)
+    q(None, 0, 64, 64, None, None)                                           # no rows: OK, nothing launched
+    assert L.moe_mx_quantize_cols_ld(1000, 8, 128) == (1000 + 8 * 127) // 128 * 128
+    assert L.moe_mx_quantize_cols_ld(3, 8, 128) == 3 * 128   # three one-row groups
+    assert L.moe_mx_quantize_cols_ld(0, 8, 128) == 0
+    qc = L.moe_mx_quantize_cols
+    ld = L.moe_mx_quantize_cols_ld(1000, 8, 128)
+    _expect(L.MOE_ERR_INVALID_VALUE, qc, FAKE, 1000, 64, 64, FAKE, 8, 0, 128, FAKE, FAKE, ld - 128, FAKE)
+    _expect(L.MOE_ERR_UNSUPPORTED, qc, FAKE, 1000, 64, 64, FAKE, 8, 0, 96, FAKE, FAKE, ld, FAKE)
+    _expect(L.MOE_ERR_INVALID_VALUE, qc, FAKE, 1000, 64, 64, FAKE, 0, 0, 128, FAKE, FAKE, ld, FAKE)
+    _expect(L.MOE_ERR_INVALID_VALUE, qc, FAKE, 1000, 64, 64, None, 8, 100, 128, FAKE, FAKE, ld, FAKE)
+    _expect(L.MOE_ERR_INVALID_VALUE, qc, FAKE, 1000, 64, 64, FAKE, 8, 0, 128, FAKE, FAKE, ld, None)
+    ws = L.moe_mx_gemm_workspace_size(8)
+    assert ws >= 9 * 4
+    g = L.moe_mx_gemm_rows
+    base = lambda N, K, epi, w: (FAKE, FAKE, FAKE, FAKE, K, N * K, FAKE, 8, 512, N, K, epi, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, w)
+    _expect(L.MOE_ERR_UNSUPPORTED, g, *base(256, 192, L.MOE_MX_EPI_STORE, ws))
+    _expect(L.MOE_ERR_UNSUPPORTED, g, *base(192, 256, L.MOE_MX_EPI_STORE, ws))
+    _expect(L.MOE_ERR_INVALID_VALUE, g, *base(256, 256, 7, ws))
+    _expect(L.MOE_ERR_WORKSPACE, g, *base(256, 256, L.MOE_MX_EPI_STORE, ws - 1))
+    args = list(base(192, 256, L.MOE_MX_EPI_SWIGLU, ws))
+    args[14] = None   # out2 (H) is required
+    _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
+    gk = L.moe_mx_gemm_k
+    _expect(L.MOE_ERR_UNSUPPORTED, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 192, 256, 0, None, FAKE)
+    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 256, 256, 300, FAKE, FAKE)
+    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 500, FAKE, FAKE, 512, FAKE, 8, 256, 256, 0, None, FAKE)
+    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 256, 256, 128, None, FAKE)

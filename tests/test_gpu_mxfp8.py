@@ -1,0 +1,210 @@
+"""MXFP8 quantization and grouped GEMMs of libmoe against the CPU oracle (GPU).
+
+Codes, scale bytes and group column offsets must match the oracle bit for bit.  Products: the
+oracle multiplies the dequantized operands in float64; the device accumulates exact products in
+fp32 and rounds the result to bf16 once, so the max-abs-relative error is bounded by bf16's half
+ulp (2^-9) plus the fp32 accumulation error; the tests allow 4e-3."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_20_amd import libmoe as L
+from oracle import mxfp8 as MX
+from tests.gpu_helpers import DEV, as_dtype_values, assert_close, dev_tensor, log, tnp
+
+pytestmark = pytest.mark.gpu
+
+TOL = 4e-3
+
+
+def i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+
+
+def u8(t):
+    return t.cpu().numpy().astype(np.uint8)
+
+
+def awkward_blocks(rng, R, K):
+    """bf16 values with per-block magnitudes spread over 2^-30..2^30, all-zero blocks, saturating
+    blocks (a block maximum just under a power of two) and exact rounding ties."""
+    x = rng.standard_normal((R, K))
+    nb = K // 32
+    scale = np.exp2(rng.integers(-30, 31, size=(R, nb)))
+    x = (x.reshape(R, nb, 32) * scale[:, :, None]).reshape(R, K)
+    z = rng.random((R, nb)) < 0.05
+    x.reshape(R, nb, 32)[z] = 0.0
+    sat = rng.random((R, nb)) < 0.05
+    blk = x.reshape(R, nb, 32)
+    blk[sat, 0] = 500.0 * np.sign(blk[sat, 0] + 0.5)       # rounds past 448: saturates
+    tie = rng.random((R, nb)) < 0.05
+    blk[tie, 1] = 2.0 ** 8 * 1.0625                        # halfway between two E4M3 values at scale 1
+    blk[tie, 2] = 2.0 ** 8 * (1.0 + 3 / 16)                # the other parity
+    return as_dtype_values(x, "bf16")
+
+
+@pytest.mark.parametrize("R,K,pad", [(333, 2048, 0), (1, 32, 0), (1000, 96, 64), (64, 1024, 8)])
+def test_quantize_rows_bit_exact(R, K, pad):
+    log(f"mx quantize rows R={R} K={K} pad={pad}")
+    rng = np.random.default_rng(R + K)
+    x = awkward_blocks(rng, R, K)
+    ldx = K + pad
+    xs = np.zeros((R, ldx), np.float32)
+    xs[:, :K] = x
+    codes = torch.empty((R, K), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=DEV)
+    L.moe_mx_quantize_rows(dev_tensor(xs, "bf16"), R, K, ldx, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = MX.mx_quantize_rows(x)
+    assert np.array_equal(u8(scales), rs), "scale bytes differ"
+    assert np.array_equal(u8(codes), rc), "E4M3 codes differ"
+
+
+@pytest.mark.parametrize("R,N,G,kpad,uniform", [(1000, 256, 8, 128, False), (2048, 128, 4, 128, True),
+                                                (77, 64, 5, 256, False)])
+def test_quantize_cols_bit_exact(R, N, G, kpad, uniform):
+    log(f"mx quantize cols R={R} N={N} G={G} kpad={kpad} uniform={uniform}")
+    rng = np.random.default_rng(R + N + G)
+    x = awkward_blocks(rng, N, -(-R // 32) * 32)[:, :R].T.copy()     # blocks run along the rows
+    if uniform:
+        offsets = np.arange(G + 1) * (R // G)
+        ldc = G * (-(-(R // G) // kpad) * kpad)
+    else:
+        cuts = np.sort(rng.integers(0, R + 1, size=G - 1))
+        cuts[1] = cuts[0]                      # an empty group
+        offsets = np.concatenate([[0], cuts, [R]])
+        ldc = L.moe_mx_quantize_cols_ld(R, G, kpad)
+    codes = torch.full((N, ldc), 0x55, dtype=torch.uint8, device=DEV)
+    scales = torch.full((N, ldc // 32), 0x55, dtype=torch.uint8, device=DEV)
+    kbase = torch.empty(G + 1, dtype=torch.int32, device=DEV)
+    L.moe_mx_quantize_cols(dev_tensor(x, "bf16"), R, N, N, None if uniform else i32(offsets), G, R // G, kpad,
+                           codes, scales, ldc, kbase)
+    torch.cuda.synchronize()
+    rc, rs, rk = MX.mx_quantize_grouped_cols(x, offsets, kpad)
+    kt = int(rk[-1])
+    assert np.array_equal(tnp(kbase), rk), "group column offsets differ"
+    assert np.array_equal(u8(codes)[:, :kt], rc), "E4M3 codes differ"
+    assert np.array_equal(u8(scales)[:, :kt // 32], rs), "scale bytes differ"
+    assert not u8(codes)[:, kt:].any() and not u8(scales)[:, kt // 32:].any(), "tail not cleared"
+
+
+def ragged_offsets(rng, M, G):
+    cuts = np.sort(rng.integers(0, M + 1, size=G - 1))
+    if G > 3:
+        cuts[2] = cuts[1]                      # an empty group
+    return np.concatenate([[0], cuts, [M]]).astype(np.int64)
+
+
+def quantize_rows_gpu(x):
+    R, K = x.shape
+    codes = torch.empty((R, K), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=DEV)
+    L.moe_mx_quantize_rows(dev_tensor(x, "bf16"), R, K, K, codes, scales)
+    return codes, scales
+
+
+@pytest.mark.parametrize("M,N,K,G", [(700, 256, 384, 6), (129, 128, 128, 1), (2000, 384, 1024, 9)])
+def test_gemm_rows_store(M, N, K, G):
+    log(f"mx gemm rows store M={M} N={N} K={K} G={G}")
+    rng = np.random.default_rng(M + N + K)
+    a = as_dtype_values(rng.standard_normal((M, K)), "bf16")
+    b = as_dtype_values(0.02 * rng.standard_normal((G, N, K)), "bf16")
+    offs = ragged_offsets(rng, M, G)
+    ac, as_ = quantize_rows_gpu(a)
+    bc, bs = quantize_rows_gpu(b.reshape(G * N, K))
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(L.moe_mx_gemm_workspace_size(G), dtype=torch.uint8, device=DEV)
+    L.moe_mx_gemm_rows(ac, as_, bc, bs, K, N * K, i32(offs), G, M, N, K, L.MOE_MX_EPI_STORE, out, None, None, None,
+                       None, ws, ws.numel())
+    torch.cuda.synchronize()
+    qa = MX.mx_quantize_rows(a)
+    qb = [MX.mx_quantize_rows(b[g]) for g in range(G)]
+    ref = MX.mx_grouped_gemm_rows(qa[0], qa[1], np.stack([q[0] for q in qb]), np.stack([q[1] for q in qb]), offs)
+    assert_close("C", tnp(out), ref, TOL)
+
+
+def test_gemm_rows_swiglu_and_backward():
+    M, f, d, G = 900, 256, 256, 5
+    log(f"mx gemm rows swiglu fwd/bwd M={M} f={f} d={d} G={G}")
+    rng = np.random.default_rng(7)
+    x = as_dtype_values(rng.standard_normal((M, d)), "bf16")
+    w1 = as_dtype_values(0.02 * rng.standard_normal((G, f, d)), "bf16")
+    w3 = as_dtype_values(0.02 * rng.standard_normal((G, f, d)), "bf16")
+    offs = ragged_offsets(rng, M, G)
+    w13 = np.concatenate([w1, w3], axis=1)                       # [G, 2f, d]: gate rows, then up rows
+    xc, xs = quantize_rows_gpu(x)
+    wc, wsc = quantize_rows_gpu(w13.reshape(G * 2 * f, d))
+    A = torch.empty((M, f), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty_like(A)
+    H = torch.empty_like(A)
+    ws = torch.empty(L.moe_mx_gemm_workspace_size(G), dtype=torch.uint8, device=DEV)
+    L.moe_mx_gemm_rows(xc, xs, wc, wsc, d, 2 * f * d, i32(offs), G, M, f, d, L.MOE_MX_EPI_SWIGLU, A, B, H, None,
+                       None, ws, ws.numel())
+    torch.cuda.synchronize()
+    qx = MX.mx_quantize_rows(x)
+    q1 = [MX.mx_quantize_rows(w1[g]) for g in range(G)]
+    q3 = [MX.mx_quantize_rows(w3[g]) for g in range(G)]
+    G1 = MX.mx_grouped_gemm_rows(*qx, np.stack([q[0] for q in q1]), np.stack([q[1] for q in q1]), offs)
+    G3 = MX.mx_grouped_gemm_rows(*qx, np.stack([q[0] for q in q3]), np.stack([q[1] for q in q3]), offs)
+    Href = G1 / (1.0 + np.exp(-G1)) * G3
+    assert_close("A", tnp(A), G1, TOL)
+    assert_close("B", tnp(B), G3, TOL)
+    assert_close("H", tnp(H), Href, TOL)
+
+    # Backward through the down projection: dH = dY W2 (contraction over d), SwiGLU backward
+    # against the stashed A and B.
+    dy = as_dtype_values(rng.standard_normal((M, d)), "bf16")
+    w2t = as_dtype_values(0.02 * rng.standard_normal((G, f, d)), "bf16")   # W2^T per group: [f, d]
+    dyc, dys = quantize_rows_gpu(dy)
+    w2c, w2s = quantize_rows_gpu(w2t.reshape(G * f, d))
+    a_in = as_dtype_values(2.0 * rng.standard_normal((M, f)), "bf16")     # stashed gate/up values
+    b_in = as_dtype_values(rng.standard_normal((M, f)), "bf16")
+    dab = torch.empty((M, 2 * f), dtype=torch.bfloat16, device=DEV)
+    L.moe_mx_gemm_rows(dyc, dys, w2c, w2s, d, f * d, i32(offs), G, M, f, d, L.MOE_MX_EPI_SWIGLU_BWD, dab, None,
+                       None, dev_tensor(a_in, "bf16"), dev_tensor(b_in, "bf16"), ws, ws.numel())
+    torch.cuda.synchronize()
+    qdy = MX.mx_quantize_rows(dy)
+    q2 = [MX.mx_quantize_rows(w2t[g]) for g in range(G)]
+    dH = MX.mx_grouped_gemm_rows(*qdy, np.stack([q[0] for q in q2]), np.stack([q[1] for q in q2]), offs)
+    a, b = a_in.astype(np.float64), b_in.astype(np.float64)
+    s = 1.0 / (1.0 + np.exp(-a))
+    dA = dH * b * s * (1.0 + a * (1.0 - s))
+    dB = dH * a * s
+    got = tnp(dab)
+    assert_close("dA", got[:, :f], dA, TOL)
+    assert_close("dB", got[:, f:], dB, TOL)
+
+
+@pytest.mark.parametrize("R,Mw,N,G,split", [(1000, 256, 128, 7, 128), (300, 128, 256, 3, 128),
+                                            (4096, 384, 128, 2, 384)])
+def test_gemm_k(R, Mw, N, G, split):
+    log(f"mx gemm k R={R} Mw={Mw} N={N} G={G} split={split}")
+    rng = np.random.default_rng(R + Mw + N)
+    a = as_dtype_values(rng.standard_normal((R, Mw)), "bf16")     # e.g. dY rows of the experts' tokens
+    b = as_dtype_values(rng.standard_normal((R, N)), "bf16")      # e.g. H rows
+    offs = ragged_offsets(rng, R, G)
+    kpad = 128
+    ld = L.moe_mx_quantize_cols_ld(R, G, kpad)
+    ac = torch.empty((Mw, ld), dtype=torch.uint8, device=DEV)
+    as_ = torch.empty((Mw, ld // 32), dtype=torch.uint8, device=DEV)
+    bc = torch.empty((N, ld), dtype=torch.uint8, device=DEV)
+    bs = torch.empty((N, ld // 32), dtype=torch.uint8, device=DEV)
+    kb = torch.empty(G + 1, dtype=torch.int32, device=DEV)
+    kb2 = torch.empty(G + 1, dtype=torch.int32, device=DEV)
+    L.moe_mx_quantize_cols(dev_tensor(a, "bf16"), R, Mw, Mw, i32(offs), G, 0, kpad, ac, as_, ld, kb)
+    L.moe_mx_quantize_cols(dev_tensor(b, "bf16"), R, N, N, i32(offs), G, 0, kpad, bc, bs, ld, kb2)
+    out0 = torch.full((G, split, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out1 = torch.full((G, Mw - split, N), float("nan"), dtype=torch.bfloat16, device=DEV) if split < Mw else None
+    L.moe_mx_gemm_k(ac, as_, ld, bc, bs, ld, kb, G, Mw, N, split, out0, out1)
+    torch.cuda.synchronize()
+    qa = MX.mx_quantize_grouped_cols(a, offs, kpad)
+    qb = MX.mx_quantize_grouped_cols(b, offs, kpad)
+    ref = MX.mx_grouped_gemm_k(qa[0], qa[1], qb[0], qb[1], qa[2])
+    got = tnp(out0)
+    if out1 is not None:
+        got = np.concatenate([got, tnp(out1)], axis=1)
+    for g in range(G):
+        if offs[g + 1] == offs[g]:
+            assert np.all(got[g] == 0), f"empty group {g} not exact zeros"
+        else:
+            assert_close(f"C[{g}]", got[g], ref[g], TOL)

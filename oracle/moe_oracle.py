@@ -200,6 +200,14 @@ def grouped_swiglu_backward(dY, X_perm, A, B, H, offsets, W1, W3, W2, dt=np.floa
     return dX, dW1, dW3, dW2, dA, dB
 
 
+class PlainExperts:
+    """The expert MLP arithmetic of the layer: exact SwiGLU in the oracle's precision."""
+    grouped_forward = staticmethod(grouped_swiglu_forward)
+    forward = staticmethod(swiglu_forward)
+    grouped_backward = staticmethod(grouped_swiglu_backward)
+    backward = staticmethod(swiglu_backward)
+
+
 # ---------------------------------------------------------------------------------------------
 # Combine and its backward
 
@@ -313,13 +321,16 @@ def router_backward(dL, x, w_router, dt=np.float64):
 
 
 def layer_forward(x, w1, w3, w2, k, *, logits=None, w_router=None, bias=None, ws1=None, ws3=None,
-                  ws2=None, renormalize=True, dt=np.float64, logits_mode="canonical_fp32", lbl_weight=0.0):
+                  ws2=None, renormalize=True, dt=np.float64, logits_mode="canonical_fp32", lbl_weight=0.0,
+                  experts=None):
     """Forward pass of the MoE layer. Returns a dict of every intermediate.
 
     Routing: random routing passes ``logits``; learned routing passes ``w_router`` (and optional
     ``bias``) and the logits are computed here: in the canonical fp32 order by default, or by a
     ``dt`` matmul when ``logits_mode="dense"`` (finite-difference checks only).  With learned
     routing and lbl_weight > 0 the load-balancing loss and its statistics are added (lbl, P, f).
+    ``experts``: an object with the expert MLP's arithmetic (grouped_forward, forward,
+    grouped_backward, backward, e.g. the MXFP8 variant); default: the plain SwiGLU above.
     """
     x = np.asarray(x)
     T, d = x.shape
@@ -335,9 +346,10 @@ def layer_forward(x, w1, w3, w2, k, *, logits=None, w_router=None, bias=None, ws
     gates = gate_weights(logits, topk_idx, renormalize, dt)
     counts, offsets, dest_pos, src_row = dispatch_plan(topk_idx, E)
     X_perm = permute_rows(x, src_row, k).astype(dt)
-    A, B, H, Y = grouped_swiglu_forward(X_perm, offsets, w1, w3, w2, dt)
+    ex = experts or PlainExperts
+    A, B, H, Y = ex.grouped_forward(X_perm, offsets, w1, w3, w2, dt)
     if ws1 is not None:
-        As, Bs, Hs, S = swiglu_forward(x, ws1, ws3, ws2, dt)
+        As, Bs, Hs, S = ex.forward(x, ws1, ws3, ws2, dt)
     else:
         As = Bs = Hs = S = None
     out = combine(Y, gates, dest_pos, S, dt)
@@ -350,7 +362,7 @@ def layer_forward(x, w1, w3, w2, k, *, logits=None, w_router=None, bias=None, ws
 
 
 def layer_backward(fwd, dout, x, w1, w3, w2, k, *, w_router=None, ws1=None, ws3=None, ws2=None,
-                   renormalize=True, dt=np.float64):
+                   renormalize=True, dt=np.float64, experts=None):
     """Backward pass given the forward dict and dL/dout.
 
     Random routing (w_router is None): the logits are data, so no router gradient and no
@@ -359,12 +371,13 @@ def layer_backward(fwd, dout, x, w1, w3, w2, k, *, w_router=None, ws1=None, ws3=
     T, d = np.asarray(x).shape
     E = np.asarray(w1).shape[0]
     dY, dgates = combine_backward(dout, fwd["Y"], fwd["gates"], fwd["dest_pos"], dt)
-    dX_perm, dW1, dW3, dW2, dA, dB = grouped_swiglu_backward(
+    ex = experts or PlainExperts
+    dX_perm, dW1, dW3, dW2, dA, dB = ex.grouped_backward(
         dY, fwd["X_perm"], fwd["A"], fwd["B"], fwd["H"], fwd["offsets"], w1, w3, w2, dt)
     res = dict(dY=dY, dgates=dgates, dX_perm=dX_perm, dW1=dW1, dW3=dW3, dW2=dW2, dA=dA, dB=dB)
     addends = []
     if ws1 is not None:
-        dxs, dWs1, dWs3, dWs2, dAs, dBs = swiglu_backward(
+        dxs, dWs1, dWs3, dWs2, dAs, dBs = ex.backward(
             dout, x, fwd["As"], fwd["Bs"], fwd["Hs"], ws1, ws3, ws2, dt)
         res.update(dx_shared=dxs, dWs1=dWs1, dWs3=dWs3, dWs2=dWs2)
         addends.append(dxs)
@@ -380,17 +393,17 @@ def layer_backward(fwd, dout, x, w1, w3, w2, k, *, w_router=None, ws1=None, ws3=
     return res
 
 
-def run_layer(cfg, vals: dict, dt=np.float64, renormalize=True, lbl_weight=0.0):
+def run_layer(cfg, vals: dict, dt=np.float64, renormalize=True, lbl_weight=0.0, experts=None):
     """Forward (and backward, when the workload has one) on the value dict of the inputs module."""
     fwd = layer_forward(vals["x"], vals["w1"], vals["w3"], vals["w2"], cfg.k, logits=vals["logits"],
                         w_router=vals["w_router"], bias=vals["bias"], ws1=vals["ws1"],
                         ws3=vals["ws3"], ws2=vals["ws2"], renormalize=renormalize, dt=dt,
-                        lbl_weight=lbl_weight)
+                        lbl_weight=lbl_weight, experts=experts)
     bwd = None
     if cfg.backward:
         bwd = layer_backward(fwd, vals["dout"], vals["x"], vals["w1"], vals["w3"], vals["w2"], cfg.k,
                              w_router=vals["w_router"], ws1=vals["ws1"], ws3=vals["ws3"],
-                             ws2=vals["ws2"], renormalize=renormalize, dt=dt)
+                             ws2=vals["ws2"], renormalize=renormalize, dt=dt, experts=experts)
     return fwd, bwd
 
 

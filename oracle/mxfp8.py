@@ -185,3 +185,98 @@ def mx_grouped_gemm_k(a_codes, a_scales, b_codes, b_scales, kbase) -> np.ndarray
         lo, hi = int(kbase[g]), int(kbase[g + 1])
         C[g] = A[:, lo:hi] @ B[:, lo:hi].T
     return C
+
+
+# ---------------------------------------------------------------------------------------------
+# The expert MLP with MXFP8 products (forward and backward)
+#
+# Every product of the SwiGLU expert is taken on MX operands quantized along its own contraction
+# axis (the recipe's reading: activations and weights are quantized afresh for each product, along
+# the axis it sums over).  Inputs of a quantization are the values the layer stores: x, weights and
+# the upstream gradient are bf16 data; H, dY and [dA | dB] are stored as bf16 before they are
+# quantized; the SwiGLU backward reads the bf16 stash of A and B.  Quantization decides codes, so it
+# runs on those bf16 values; the products are float64.  A weight gradient's contraction runs over
+# the rows one expert received, whose 32-row blocks start at the expert's first row.
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of each element (via float32; ties to even at both steps)."""
+    f = np.ascontiguousarray(np.asarray(a, np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+class MXExperts:
+    """Expert arithmetic for moe_oracle.layer_forward / layer_backward (argument ``experts``).
+
+    quantize=False and store_bf16=False turn every quantization and every bf16 storage rounding into
+    the identity: the result is then the plain SwiGLU expert (the structural pin of this class)."""
+
+    def __init__(self, quantize: bool = True, store_bf16: bool = True):
+        self.quantize = quantize
+        self.store_bf16 = store_bf16
+
+    def mx(self, m: np.ndarray) -> np.ndarray:
+        """Values of m after MXFP8 quantization along its last axis."""
+        m = np.asarray(m, np.float64)
+        if not self.quantize or m.size == 0:
+            return m
+        c, s = mx_quantize_rows(m.reshape(-1, m.shape[-1]))
+        return mx_dequantize_rows(c, s)[:, :m.shape[-1]].reshape(m.shape)
+
+    def st(self, m: np.ndarray) -> np.ndarray:
+        """Values of m as the layer stores them (bf16)."""
+        return bf16_round(m) if self.store_bf16 else np.asarray(m, np.float64)
+
+    def forward(self, X, w1, w3, w2, dt=np.float64):
+        """A = X W1^T, B = X W3^T (contraction over d), H = silu(A) B, Y = H W2^T (over f)."""
+        Xq = self.mx(X)
+        A = Xq @ self.mx(w1).T
+        B = Xq @ self.mx(w3).T
+        H = A / (1.0 + np.exp(-A)) * B
+        Y = self.mx(self.st(H)) @ self.mx(w2).T
+        return A, B, H, Y
+
+    def backward(self, dY, X, A, B, H, w1, w3, w2, dt=np.float64):
+        """dH = dY W2 (over d); SwiGLU backward on the stored A, B; dX = [dA | dB] [W1; W3] (over 2f);
+        dW2 = dY^T H, dW1 = dA^T X, dW3 = dB^T X (over the rows)."""
+        w1, w3, w2 = (np.asarray(w, np.float64) for w in (w1, w3, w2))
+        dYs = self.st(dY)
+        dH = self.mx(dYs) @ self.mx(w2.T).T
+        a, b = self.st(A), self.st(B)
+        s = 1.0 / (1.0 + np.exp(-a))
+        dA = dH * b * s * (1.0 + a * (1.0 - s))
+        dB = dH * a * s
+        dAB = self.st(np.concatenate([dA, dB], axis=1))
+        dX = self.mx(dAB) @ self.mx(np.concatenate([w1.T, w3.T], axis=1)).T
+        Hs, Xs = self.st(H), np.asarray(X, np.float64)
+        dYq, Hq, ABq, Xq = (self.mx(m.T) for m in (dYs, Hs, dAB, Xs))
+        dW2 = dYq @ Hq.T
+        f = w1.shape[0]
+        dW1 = ABq[:f] @ Xq.T
+        dW3 = ABq[f:] @ Xq.T
+        return dX, dW1, dW3, dW2, dA, dB
+
+    def grouped_forward(self, X_perm, offsets, W1, W3, W2, dt=np.float64):
+        M = X_perm.shape[0]
+        E, f, d = np.asarray(W1).shape
+        A, B, H, Y = np.zeros((M, f)), np.zeros((M, f)), np.zeros((M, f)), np.zeros((M, d))
+        for e in range(E):
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 > r0:
+                A[r0:r1], B[r0:r1], H[r0:r1], Y[r0:r1] = self.forward(X_perm[r0:r1], W1[e], W3[e], W2[e])
+        return A, B, H, Y
+
+    def grouped_backward(self, dY, X_perm, A, B, H, offsets, W1, W3, W2, dt=np.float64):
+        M = X_perm.shape[0]
+        E, f, d = np.asarray(W1).shape
+        dX, dA, dB = np.zeros((M, d)), np.zeros((M, f)), np.zeros((M, f))
+        dW1, dW3, dW2 = np.zeros((E, f, d)), np.zeros((E, f, d)), np.zeros((E, d, f))
+        for e in range(E):
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 > r0:
+                sl = slice(r0, r1)
+                dX[sl], dW1[e], dW3[e], dW2[e], dA[sl], dB[sl] = self.backward(
+                    dY[sl], X_perm[sl], A[sl], B[sl], H[sl], W1[e], W3[e], W2[e])
+        return dX, dW1, dW3, dW2, dA, dB

@@ -1,0 +1,51 @@
+"""Pins of the MXFP8 expert MLP of the layer oracle (CPU).
+
+The MXFP8 layer is the plain layer with every expert product taken on MX-quantized operands and the
+stored intermediates rounded to bf16.  With both turned off it must reduce to the plain oracle, which
+fixes its structure (operands, transposes, contraction axes of all six products); with them on it must
+differ from the plain layer by the size of E4M3 roundings (3 fraction bits: a few percent per
+product, compounded over the four products of a gradient), not more."""
+import numpy as np
+import pytest
+
+from mixture_experts_layer_20_amd import inputs as I
+from oracle import moe_oracle as O
+from oracle import mxfp8 as MX
+
+
+def small_cfg(routing="learned"):
+    base = I.CONFIGS["tiny64e_learned_skew" if routing == "learned" else "tiny64e_random"]
+    return base.with_(name="mx_small", T=96, d=128, E=6, k=2, f=128, fs=128, bias_std=0.5)
+
+
+@pytest.mark.parametrize("routing", ["learned", "random"])
+def test_identity_quantizer_reduces_to_the_plain_layer(routing):
+    cfg = small_cfg(routing)
+    vals = I.values(I.make_inputs(cfg))
+    fwd, bwd = O.run_layer(cfg, vals)
+    mfwd, mbwd = O.run_layer(cfg, vals, experts=MX.MXExperts(quantize=False, store_bf16=False))
+    for key in ("out",):
+        assert O.max_abs_rel_err(mfwd[key], fwd[key]) < 1e-12, key
+    for key in ("dx", "dW1", "dW3", "dW2", "dWs1", "dWs3", "dWs2") + (("dWr",) if routing == "learned" else ()):
+        assert O.max_abs_rel_err(mbwd[key], bwd[key]) < 1e-12, key
+
+
+def test_quantized_layer_differs_by_an_e4m3_rounding():
+    cfg = small_cfg()
+    vals = I.values(I.make_inputs(cfg))
+    fwd, bwd = O.run_layer(cfg, vals)
+    mfwd, mbwd = O.run_layer(cfg, vals, experts=MX.MXExperts())
+    assert np.array_equal(mfwd["topk_idx"], fwd["topk_idx"])     # routing is not quantized
+    for got, ref, name in [(mfwd["out"], fwd["out"], "out"), (mbwd["dx"], bwd["dx"], "dx"),
+                           (mbwd["dW1"], bwd["dW1"], "dW1"), (mbwd["dW2"], bwd["dW2"], "dW2"),
+                           (mbwd["dWs3"], bwd["dWs3"], "dWs3")]:
+        e = O.max_abs_rel_err(got, ref)
+        assert 1e-4 < e < 0.2, f"{name}: {e:.2e}"
+
+
+def test_bf16_round_matches_the_format():
+    v = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -3.14159, 65504.0, 2.0 ** -130, 0.0])
+    r = MX.bf16_round(v)
+    assert r[0] == 1.0 and r[1] == 1.0 and r[2] == 1.0 + 2.0 ** -6     # ties to even
+    assert r[3] == -3.140625 and r[4] == 65536.0 and r[6] == 0.0
+    assert r[5] == 2.0 ** -130                                       # subnormal kept

@@ -22,6 +22,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s fwd+bwd on 1 GPU; grouped-GEMM TFLOP/s (% bf16 MFMA peak)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 GEMM_STAGES = ("gate_up_fwd", "down_fwd", "down_bwd", "down_wgrad", "gate_up_dgrad", "gate_up_wgrad")
@@ -106,6 +107,8 @@ def main(argv=None) -> int:
     ap.add_argument("--recompute", action="store_true",
                     help="per-layer recompute variant: no A/B stash in the forward, gate/up GEMM rerun in "
                          "the backward")
+    ap.add_argument("--precision", choices=("bf16", "mxfp8"), default="bf16",
+                    help="expert products in bf16, or in MXFP8 (E4M3 with one E8M0 scale per 32 elements)")
     ap.add_argument("--no-merge", action="store_true",
                     help="one GEMM call per expert set instead of routed + shared in one call")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -131,8 +134,9 @@ def main(argv=None) -> int:
     print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = I.make_inputs(cfg)
     dev = torch.device("cuda:0")
-    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not a.no_merge, recompute=a.recompute,
-                      lbl_weight=a.lbl)
+    mx = a.precision == "mxfp8"
+    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not (a.no_merge or mx), recompute=a.recompute,
+                      lbl_weight=a.lbl, precision=a.precision)
     if a.copy_probe_mb > 0:
         src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -158,20 +162,21 @@ def main(argv=None) -> int:
     for name, pairs in lay.events.items():
         ms = [s.elapsed_time(e) for s, e in pairs]
         stages[name] = sum(ms) / len(ms)
-    flops = stage_flops(cfg, merged=not a.no_merge, recompute=a.recompute)
+    flops = stage_flops(cfg, merged=not (a.no_merge or mx), recompute=a.recompute)
+    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     gemm_ms = sum(stages[s] for s in flops if s in stages)
     gemm_flop = sum(flops.values())
     stage_tflops = {s: flops[s] / (stages[s] * 1e-3) / 1e12 for s in flops if s in stages}
     # The dominant GEMM kernel: the longest stage that is one kernel launch (a weight-gradient
     # stage is the GEMM plus its split-reduction pass).
-    dom = max((s for s in GEMM_STAGES if s in stages and "wgrad" not in s), key=lambda s: stages[s])
+    dom = max((s for s in GEMM_STAGES if s in stages and (mx or "wgrad" not in s)), key=lambda s: stages[s])
     achieved = stage_tflops[dom]
     traffic = None
     if os.path.exists(a.traffic_json):
         try:
             tj = json.load(open(a.traffic_json))
             ent = tj.get(cfg.name, {}).get(dom)
-            if ent and ent.get("kernel_source_sha") == _kernel_source_sha():
+            if ent and not mx and ent.get("kernel_source_sha") == _kernel_source_sha():
                 traffic = ent["bytes_per_launch"]
         except Exception:
             traffic = None
@@ -186,17 +191,17 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "mxfp8-e4m3 products, bf16 storage" if mx else cfg.dtype,
         "data": "synthetic (seeded Gaussian inputs and weights; random routing logits drawn per token)"
         if cfg.routing == "random" else "synthetic (seeded Gaussian inputs and weights, learned router)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "expert_d_ff": cfg.f, "shared_d_ff": cfg.fs, "routing": cfg.routing,
-                   "backward": cfg.backward, "recompute": a.recompute,
+                   "backward": cfg.backward, "recompute": a.recompute, "precision": a.precision,
                    "lbl_weight": a.lbl if cfg.routing == "learned" else 0.0},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "grouped_gemm": {"tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12,
-                         "frac_peak": gemm_flop / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "frac_peak": gemm_flop / (gemm_ms * 1e-3) / 1e12 / peak,
                          "ms": gemm_ms, "per_stage_tflops": stage_tflops},
         "stages_ms": stages,
         "hbm_bound_stages": {s: {"gbs": by / (stages[s] * 1e-3) / 1e9,
@@ -204,6 +209,10 @@ def main(argv=None) -> int:
                                  "bytes": by}
                              for s, by in stage_bytes(cfg).items() if s in stages},
     }
+    if mx:
+        # MXFP8 quantization passes (activations each product, weights in both orientations).
+        qs = {k: v for k, v in stages.items() if k.startswith("q_") or k.startswith("shared_q_")}
+        line["mxfp8_quantize_ms"] = sum(qs.values())
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, inp, a.cpu_sample_tokens)

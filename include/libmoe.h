@@ -326,8 +326,8 @@ moe_status_t moe_mx_quantize_cols(const void* x, int64_t R, int64_t N, int64_t l
 
 typedef enum {
   MOE_MX_EPI_STORE = 0,      /* out0 [M, N] bf16 = C */
-  MOE_MX_EPI_SWIGLU = 1,     /* B holds 2N rows per group (rows 0..N-1: gate W1, N..2N-1: up W3);
-                                G1 = A B_gate^T, G3 = A B_up^T; out2 [M, N] = silu(G1) * G3,
+  MOE_MX_EPI_SWIGLU = 1,     /* B = gate rows (W1), B2 = up rows (W3), N rows each per group;
+                                G1 = A B^T, G3 = A B2^T; out2 [M, N] = silu(G1) * G3,
                                 out0 / out1 [M, N] = G1 / G3 (each may be NULL) */
   MOE_MX_EPI_SWIGLU_BWD = 2  /* C = dH; aux0, aux1 [M, N] bf16 = the stashed G1, G3;
                                 out0 [M, 2N] = [dH * G3 * s (1 + G1 (1 - s)) | dH * G1 * s],
@@ -338,14 +338,18 @@ typedef enum {
  *   C[m, n] = sum_k A[m, k] B_g[n, k] for rows m of group g = offsets[g]..offsets[g+1]-1
  *   a_codes [M, K], a_scales [M, K/32] (from moe_mx_quantize_rows);
  *   B_g row n at b_codes + g*b_group_stride + n*b_row_stride, its scales at
- *   b_scales + (g*b_group_stride + n*b_row_stride)/32 (B has N rows, 2N for MOE_MX_EPI_SWIGLU);
+ *   b_scales + (g*b_group_stride + n*b_row_stride)/32 (N rows per group);
+ *   b2_codes / b2_scales: a second B source with the same strides, NULL or given together.  With
+ *   MOE_MX_EPI_SWIGLU it holds the up-projection rows (required).  Otherwise, if given, columns
+ *   k >= b2_k of B come from it, at column k - b2_k (b2_k a multiple of 128 in (0, K)): the gate/up
+ *   data gradient contracts [dA | dB] with W1 and W3 stacked along K;
  *   offsets [G+1] int32 device (clamped to [0, M]; rows outside every group are not written).
  * K must be a multiple of 128, N of 128 (64 for MOE_MX_EPI_SWIGLU), both strides multiples of 128.
  * ws: moe_mx_gemm_workspace_size(G) bytes. */
 size_t moe_mx_gemm_workspace_size(int32_t G);
 moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                               const uint8_t* b_scales, int64_t b_row_stride, int64_t b_group_stride,
-                              const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
+                              const uint8_t* b2_codes, const uint8_t* b2_scales, int64_t b2_k, const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
                               void* out0, void* out1, void* out2, const void* aux0, const void* aux1, void* ws,
                               size_t ws_bytes, moe_stream_t stream);
 

@@ -544,7 +544,7 @@ size_t moe_mx_gemm_workspace_size(int32_t G) {
 
 moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                               const uint8_t* b_scales, int64_t b_row_stride, int64_t b_group_stride,
-                              const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
+                              const uint8_t* b2_codes, const uint8_t* b2_scales, int64_t b2_k, const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
                               void* out0, void* out1, void* out2, const void* aux0, const void* aux1, void* ws,
                               size_t ws_bytes, moe_stream_t stream) {
   g_err.clear();
@@ -554,11 +554,21 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
   CHECK(M >= 0 && N > 0 && K > 0, MOE_ERR_INVALID_VALUE, "M must be >= 0, N and K > 0");
   const int oc = epilogue == MOE_MX_EPI_SWIGLU ? 64 : 128;
   CHECK(K % 128 == 0 && N % oc == 0, MOE_ERR_UNSUPPORTED, "K must be a multiple of 128 and N of %d", oc);
-  CHECK(b_row_stride >= K && b_row_stride % 128 == 0 && b_group_stride >= 0 && b_group_stride % 128 == 0,
-        MOE_ERR_INVALID_VALUE, "B strides must be multiples of 128, the row stride >= K");
+  // Columns one source holds: all K, or the two parts of a K split.
+  const int64_t span = (b2_codes && epilogue != MOE_MX_EPI_SWIGLU) ? std::max<int64_t>(b2_k, K - b2_k) : K;
+  CHECK(b_row_stride >= span && b_row_stride % 128 == 0 && b_group_stride >= 0 && b_group_stride % 128 == 0,
+        MOE_ERR_INVALID_VALUE, "B strides must be multiples of 128, the row stride >= the columns of a source");
   CHECK(M <= kMaxInt && N <= kMaxInt / 2 && K <= kMaxInt, MOE_ERR_UNSUPPORTED, "sizes must fit in int32");
   CHECK(((M + 127) / 128 + G) * (N / oc) < kMaxInt, MOE_ERR_UNSUPPORTED, "grid too large");
   CHECK(a_codes && a_scales && b_codes && b_scales && offsets, MOE_ERR_INVALID_VALUE, "an operand pointer is NULL");
+  CHECK((b2_codes == nullptr) == (b2_scales == nullptr), MOE_ERR_INVALID_VALUE,
+        "b2_codes and b2_scales must both be given or both be NULL");
+  if (epilogue == MOE_MX_EPI_SWIGLU) {
+    CHECK(b2_codes, MOE_ERR_INVALID_VALUE, "the SwiGLU epilogue needs the up-projection rows in b2");
+  } else if (b2_codes) {
+    CHECK(b2_k > 0 && b2_k < K && b2_k % 128 == 0, MOE_ERR_INVALID_VALUE,
+          "b2_k must be a multiple of 128 in (0, K) (got %lld)", (long long)b2_k);
+  }
   if (epilogue == MOE_MX_EPI_STORE) CHECK(out0, MOE_ERR_INVALID_VALUE, "out0 is NULL");
   if (epilogue == MOE_MX_EPI_SWIGLU) CHECK(out2, MOE_ERR_INVALID_VALUE, "out2 is NULL");
   if (epilogue == MOE_MX_EPI_SWIGLU_BWD) CHECK(out0 && aux0 && aux1, MOE_ERR_INVALID_VALUE, "out0/aux0/aux1 is NULL");
@@ -574,6 +584,9 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
   a.bs = b_scales;
   a.ldb = b_row_stride;
   a.b_gstride = b_group_stride;
+  a.b2 = b2_codes;
+  a.bs2 = b2_scales;
+  a.ksplit = (epilogue != MOE_MX_EPI_SWIGLU && b2_codes) ? (int)b2_k : 0;
   a.offsets = offsets;
   a.tile_prefix = reinterpret_cast<int32_t*>(ws);
   a.G = G;

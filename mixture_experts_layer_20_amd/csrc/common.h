@@ -155,6 +155,9 @@ struct MxGemmArgs {
   const uint8_t* b;       // B codes (group g at b + g*b_gstride), row stride ldb; scales alike /32
   const uint8_t* bs;
   long long ldb, b_gstride;
+  const uint8_t* b2;      // second B source (same strides): SwiGLU up rows; else K columns >= ksplit
+  const uint8_t* bs2;
+  int ksplit;
   const int32_t* offsets; // ragged rows: [G+1] row offsets; ragged K: [G+1] column offsets (kbase)
   int32_t* tile_prefix;   // ragged rows: [G+1] workspace
   int G, M, N, K;         // ragged rows: M rows, K fixed; ragged K: M rows of A (per group output rows)

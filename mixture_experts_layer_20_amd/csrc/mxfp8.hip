@@ -288,20 +288,24 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(MxGemmArgs p) {
   const int lrow = tid >> 3, lch = tid & 7;
   const uint8_t* ga[4];
   const uint8_t* gb[4];
-  const uint8_t* bbase = p.b + (RK ? 0 : (long long)g * p.b_gstride);
+  const uint8_t* gb2[4];   // K columns >= ksplit (store / SwiGLU backward with a second source)
+  const long long gofs = RK ? 0 : (long long)g * p.b_gstride;
+  const bool split = EPI != MX_EPI_SWIGLU && p.b2 != nullptr;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = lrow + 32 * j;
     const int ar = RK ? m0 + r : min(m0 + r, m_end - 1);
     ga[j] = p.a + (long long)ar * p.lda + kb0 + 16 * lch;
-    int br;
     if constexpr (EPI == MX_EPI_SWIGLU) {
-      // tile row r: wave column r >> 6, block (r >> 5) & 1 (0: gate rows, 1: up rows), column r & 31
-      br = ((r >> 5) & 1) * p.N + nt * 64 + (r >> 6) * 32 + (r & 31);
+      // tile row r: wave column r >> 6, block (r >> 5) & 1 (0: gate rows of b, 1: up rows of b2)
+      const int br = nt * 64 + (r >> 6) * 32 + (r & 31);
+      gb[j] = (((r >> 5) & 1) ? p.b2 : p.b) + gofs + (long long)br * p.ldb + kb0 + 16 * lch;
+      gb2[j] = gb[j];
     } else {
-      br = nt * TB + r;
+      const int br = nt * TB + r;
+      gb[j] = p.b + gofs + (long long)br * p.ldb + kb0 + 16 * lch;
+      gb2[j] = (split ? p.b2 : p.b) + gofs + (long long)br * p.ldb + 16 * lch - p.ksplit;
     }
-    gb[j] = bbase + (long long)br * p.ldb + kb0 + 16 * lch;
   }
   const int lofs = lrow * TB + 16 * (lch ^ swz(lrow));  // + 32 * TB * j
 
@@ -309,19 +313,25 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(MxGemmArgs p) {
   // (step half 0) and byte 2 (step half 1) are this lane's blocks.
   const uint8_t* sa_p[2];
   const uint8_t* sb_p[2];
+  const uint8_t* sb2_p[2];
   const long long lda_s = p.lda >> 5, ldb_s = p.ldb >> 5;
-  const uint8_t* bsbase = p.bs + (RK ? 0 : (long long)g * (p.b_gstride >> 5));
+  const long long gofs_s = gofs >> 5;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = wm * 64 + q * 32 + li;
     const int ar = RK ? m0 + r : min(m0 + r, m_end - 1);
     sa_p[q] = p.as + (long long)ar * lda_s + (kb0 >> 5);
-    const int c = wn * 64 + q * 32 + li;
-    int br;
-    if constexpr (EPI == MX_EPI_SWIGLU) br = q * p.N + nt * 64 + wn * 32 + li;
-    else br = nt * TB + c;
-    sb_p[q] = bsbase + (long long)br * ldb_s + (kb0 >> 5);
+    if constexpr (EPI == MX_EPI_SWIGLU) {
+      const int br = nt * 64 + wn * 32 + li;
+      sb_p[q] = (q ? p.bs2 : p.bs) + gofs_s + (long long)br * ldb_s + (kb0 >> 5);
+      sb2_p[q] = sb_p[q];
+    } else {
+      const int br = nt * TB + wn * 64 + q * 32 + li;
+      sb_p[q] = p.bs + gofs_s + (long long)br * ldb_s + (kb0 >> 5);
+      sb2_p[q] = (split ? p.bs2 : p.bs) + gofs_s + (long long)br * ldb_s - (p.ksplit >> 5);
+    }
   }
+  const int ks = split ? p.ksplit : 0x7fffffff;   // K columns from the second source start here
 
   f32x16_t acc[2][2];
 #pragma unroll
@@ -337,12 +347,12 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(MxGemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ra[j] = *reinterpret_cast<const u32x4_t*>(ga[j]);
-      rb[j] = *reinterpret_cast<const u32x4_t*>(gb[j]);
+      rb[j] = *reinterpret_cast<const u32x4_t*>(ks <= 0 ? gb2[j] : gb[j]);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       sa_c[q] = *reinterpret_cast<const uint32_t*>(sa_p[q]) >> (8 * h);
-      sb_c[q] = *reinterpret_cast<const uint32_t*>(sb_p[q]) >> (8 * h);
+      sb_c[q] = *reinterpret_cast<const uint32_t*>(ks <= 0 ? sb2_p[q] : sb_p[q]) >> (8 * h);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -357,15 +367,17 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(MxGemmArgs p) {
     const bool more = kt + 1 < nk;
     if (more) {
       const long long off = (long long)(kt + 1) * TB;
+      const bool second = kb0 + off >= ks;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ra[j] = *reinterpret_cast<const u32x4_t*>(ga[j] + off);
-        rb[j] = *reinterpret_cast<const u32x4_t*>(gb[j] + off);
+        rb[j] = *reinterpret_cast<const u32x4_t*>((second ? gb2[j] + kb0 : gb[j]) + off);
       }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         sa_n[q] = *reinterpret_cast<const uint32_t*>(sa_p[q] + 4 * (kt + 1)) >> (8 * h);
-        sb_n[q] = *reinterpret_cast<const uint32_t*>(sb_p[q] + 4 * (kt + 1)) >> (8 * h);
+        sb_n[q] = *reinterpret_cast<const uint32_t*>((second ? sb2_p[q] + (kb0 >> 5) : sb_p[q]) + 4 * (kt + 1)) >>
+                  (8 * h);
       }
     }
     const uint8_t* ta = lds[cur][0];
@@ -474,6 +486,310 @@ __global__ __launch_bounds__(256, 2) void mx_gemm_kernel(MxGemmArgs p) {
   }
 }
 
+// ---- Pipelined grouped GEMM: 256x256 tiles ----------------------------------------------------
+// 8 waves (2 per SIMD): wave w covers rows 128*(w & 1) .. +128 and columns 64*(w >> 1) .. +64 of
+// the tile (4 x 2 blocks of 32x32).  K step = 64 bytes.  Codes stream through a ring of four
+// 32 KiB LDS stages filled by direct loads (global_load_lds_dwordx4: lane l's 16 bytes land at
+// M0 + 16 l); the stage three steps ahead is issued right after the barrier that publishes the
+// current one, so three stages (96 KiB) are in flight per CU.  Scale bytes: one dword per row
+// covers two K steps (4 blocks); the 512 dwords of a tile's two steps land in a three-slot LDS
+// ring.  LDS reads are inline assembly that waits for its own results; the ring is governed by
+// explicit vmcnt waits (a compiler-generated LDS read would first wait for every direct load in
+// flight).  K-contiguous rows of 64 bytes are stored with 16-byte chunk c at c ^ ((row >> 2) & 3).
+constexpr int PB = 256;                 // tile rows / columns
+constexpr int PK = 64;                  // K step (bytes = elements)
+constexpr int PSTAGE = 2 * PB * PK;     // 32 KiB: A then B
+constexpr int PNST = 4;
+constexpr int PSC = 2048;               // scale slot: 256 A dwords, then 256 B dwords
+constexpr int PNSC = 3;
+constexpr int P_LDS = PNST * PSTAGE + PNSC * PSC;
+
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+__device__ __forceinline__ uint32_t lds_off(const void* ptr) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)ptr);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | (0xf << 8));
+}
+__device__ __forceinline__ void pbarrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Fragments and scales of one K step, read from LDS with the wait inside the same block.  Outputs
+// are early-clobber: a result may land while later reads of the block still need their addresses.
+struct PFrag {
+  u32x4_t a[4][2];
+  u32x4_t b[2][2];
+  uint32_t sa[4], sb[2];
+};
+
+__device__ __forceinline__ void read_step(PFrag& f, uint32_t a0, uint32_t a2, uint32_t b0, uint32_t b2, uint32_t sa,
+                                          uint32_t sb) {
+  asm volatile(
+      "ds_read_b128 %0, %18\n\t"
+      "ds_read_b128 %1, %19\n\t"
+      "ds_read_b128 %2, %18 offset:2048\n\t"
+      "ds_read_b128 %3, %19 offset:2048\n\t"
+      "ds_read_b128 %4, %18 offset:4096\n\t"
+      "ds_read_b128 %5, %19 offset:4096\n\t"
+      "ds_read_b128 %6, %18 offset:6144\n\t"
+      "ds_read_b128 %7, %19 offset:6144\n\t"
+      "ds_read_b128 %8, %20\n\t"
+      "ds_read_b128 %9, %21\n\t"
+      "ds_read_b128 %10, %20 offset:2048\n\t"
+      "ds_read_b128 %11, %21 offset:2048\n\t"
+      "ds_read_u8 %12, %22\n\t"
+      "ds_read_u8 %13, %22 offset:128\n\t"
+      "ds_read_u8 %14, %22 offset:256\n\t"
+      "ds_read_u8 %15, %22 offset:384\n\t"
+      "ds_read_u8 %16, %23\n\t"
+      "ds_read_u8 %17, %23 offset:128\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]), "=&v"(f.a[2][0]), "=&v"(f.a[2][1]),
+        "=&v"(f.a[3][0]), "=&v"(f.a[3][1]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1]),
+        "=&v"(f.sa[0]), "=&v"(f.sa[1]), "=&v"(f.sa[2]), "=&v"(f.sa[3]), "=&v"(f.sb[0]), "=&v"(f.sb[1])
+      : "v"(a0), "v"(a2), "v"(b0), "v"(b2), "v"(sa), "v"(sb)
+      : "memory");
+}
+
+__device__ __forceinline__ i32x8_t frag8(const u32x4_t& lo, const u32x4_t& hi) {
+  i32x8_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j] = (int)lo[j];
+    r[4 + j] = (int)hi[j];
+  }
+  return r;
+}
+
+template <int EPI, bool RK>
+__global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char plds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1, li = lane & 31, h = lane >> 5;
+  constexpr int OC = EPI == MX_EPI_SWIGLU ? 128 : PB;   // output columns per tile
+  const int NT = p.N / OC;
+
+  const int nb = gridDim.x, b = blockIdx.x;
+  int Lt;
+  {
+    const int per = nb >> 3, rem = nb & 7, xcd = b & 7;
+    Lt = xcd * per + min(xcd, rem) + (b >> 3);
+  }
+  const int nt = Lt % NT;
+  int g, m0, m_end;
+  long long kb0, kb1;
+  if constexpr (!RK) {
+    const int mt = Lt / NT;
+    if (mt >= p.tile_prefix[p.G]) return;
+    int lo = 0, hi = p.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tile_prefix[mid] <= mt) lo = mid; else hi = mid;
+    }
+    g = lo;
+    const int r0 = min(max(p.offsets[g], 0), p.M);
+    const int r1 = min(max(p.offsets[g + 1], r0), p.M);
+    m0 = r0 + (mt - p.tile_prefix[g]) * PB;
+    m_end = r1;
+    kb0 = 0;
+    kb1 = p.K;
+  } else {
+    const int MT = p.M / PB;
+    const int r = Lt / NT;
+    if (r >= p.G * MT) return;
+    g = r / MT;
+    m0 = (r - g * MT) * PB;
+    m_end = p.M;
+    kb0 = p.offsets[g];
+    kb1 = p.offsets[g + 1];
+  }
+  const int nk = (int)((kb1 - kb0) / PK);
+  const long long lda_s = p.lda >> 5, ldb_s = p.ldb >> 5;
+  const long long gofs = RK ? 0 : (long long)g * p.b_gstride;
+  const bool split = EPI != MX_EPI_SWIGLU && p.b2 != nullptr;
+  const int ks = split ? p.ksplit : 0x7fffffff;   // K columns from the second source start here
+
+  // B tile row r: its source (first or second) and row.  The SwiGLU tile holds gate rows (first
+  // source) and up rows (second source) of 128 output columns.
+  auto bsrc2 = [&](int r) -> bool { return EPI == MX_EPI_SWIGLU && ((r >> 5) & 1); };
+  auto brow = [&](int r) -> int {
+    if constexpr (EPI == MX_EPI_SWIGLU) return nt * 128 + (r >> 6) * 32 + (r & 31);
+    else return nt * PB + r;
+  };
+  auto arow = [&](int r) -> int { return RK ? m0 + r : min(m0 + r, m_end - 1); };
+
+  // This lane's code loads: instruction j (0, 1) of each operand fills slot q = (2 wave + j) 64 + lane
+  // = row q >> 2, physical chunk q & 3.  gb2: the same rows in the second source, K column 0.
+  const uint8_t* ga[2];
+  const uint8_t* gb[2];
+  const uint8_t* gb2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = (2 * wave + j) * 64 + lane;
+    const int row = q >> 2;
+    const int c = (q & 3) ^ ((row >> 2) & 3);
+    ga[j] = p.a + (long long)arow(row) * p.lda + kb0 + 16 * c;
+    const long long bo = gofs + (long long)brow(row) * p.ldb + 16 * c;
+    gb[j] = (bsrc2(row) ? p.b2 : p.b) + bo + kb0;
+    gb2[j] = (split ? p.b2 : p.b) + bo;
+  }
+  // Scale dword load: wave w < 4 loads A rows 64 w + lane, wave w >= 4 B rows 64 (w - 4) + lane.
+  const uint8_t* gs;
+  const uint8_t* gs2;
+  {
+    const int r = (wave & 3) * 64 + lane;
+    const long long bo = (gofs >> 5) + (long long)brow(r) * ldb_s;
+    gs = wave < 4 ? p.as + (long long)arow(r) * lda_s + (kb0 >> 5) : (bsrc2(r) ? p.bs2 : p.bs) + bo + (kb0 >> 5);
+    gs2 = wave < 4 ? gs : (split ? p.bs2 : p.bs) + bo;
+  }
+
+  char* ring = plds;
+  char* sring = plds + PNST * PSTAGE;
+  auto issue = [&](int s) {
+    char* st = ring + (s & 3) * PSTAGE;
+    const long long off = (long long)s * PK;
+    const bool second = kb0 + off >= ks;   // B columns of this stage come from the second source
+    if ((s & 1) == 0) {
+      const uint8_t* src = (second && wave >= 4) ? gs2 + ((kb0 + off - ks) >> 5) : gs + 2 * s;
+      __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(sring + ((s >> 1) % PNSC) * PSC + wave * 256), 4, 0,
+                                       0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(ga[j] + off), (lvoid_t*)(st + (2 * wave + j) * 1024), 16, 0, 0);
+      const uint8_t* bs = second ? gb2[j] + (kb0 + off - ks) : gb[j] + off;
+      __builtin_amdgcn_global_load_lds((gvoid_t*)bs, (lvoid_t*)(st + PB * PK + (2 * wave + j) * 1024), 16, 0, 0);
+    }
+  };
+
+  // LDS read offsets of this lane: A rows 128 wm + 32 i + li, B rows 64 wn + 32 j + li; chunks h, 2 + h.
+  const int sw = (li >> 2) & 3;
+  const uint32_t ring0 = lds_off(ring), sring0 = lds_off(sring);
+  const uint32_t oa0 = (uint32_t)((wm * 128 + li) * PK + 16 * (h ^ sw));
+  const uint32_t oa2 = (uint32_t)((wm * 128 + li) * PK + 16 * ((2 + h) ^ sw));
+  const uint32_t ob0 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * (h ^ sw));
+  const uint32_t ob2 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * ((2 + h) ^ sw));
+  const uint32_t osa = (uint32_t)((wm * 128 + li) * 4 + h);
+  const uint32_t osb = (uint32_t)(1024 + (wn * 64 + li) * 4 + h);
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  for (int s = 0; s < 3 && s < nk; ++s) issue(s);
+  for (int j = 0; j < nk; ++j) {
+    // Stage j complete for this wave: at most the loads of the (up to two) later stages in flight.
+    const int later = min(nk - 1 - j, 2);
+    if (later >= 2) wait_vm<8>();
+    else if (later == 1) wait_vm<4>();
+    else wait_vm<0>();
+    pbarrier();
+    if (j + 3 < nk) issue(j + 3);
+    PFrag f;
+    const uint32_t sb = ring0 + (uint32_t)((j & 3) * PSTAGE);
+    const uint32_t ss = sring0 + (uint32_t)(((j >> 1) % PNSC) * PSC + 2 * (j & 1));
+    read_step(f, sb + oa0, sb + oa2, sb + ob0, sb + ob2, ss + osa, ss + osb);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const i32x8_t fa = frag8(f.a[i][0], f.a[i][1]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        acc[i][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag8(f.b[c][0], f.b[c][1]), fa, acc[i][c], 0, 0,
+                                                                    0, (int)f.sb[c], 0, (int)f.sa[i]);
+    }
+  }
+
+  // Epilogue: lane holds row li of each 32-row block, columns 8 (r / 4) + 4 h + (r % 4).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + wm * 128 + i * 32 + li;
+    if (!RK && row >= m_end) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (EPI == MX_EPI_SWIGLU) {
+        const int col = nt * 128 + wn * 32 + 8 * q + 4 * h;
+        float hv[4];
+        const long long o = (long long)row * p.N + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = acc[i][0][4 * q + r], bb = acc[i][1][4 * q + r];
+          hv[r] = a * sigmoid_f32(a) * bb;
+        }
+        if (p.out0)
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + o) =
+              make_uint2(bf16pack(acc[i][0][4 * q], acc[i][0][4 * q + 1]),
+                         bf16pack(acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]));
+        if (p.out1)
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out1) + o) =
+              make_uint2(bf16pack(acc[i][1][4 * q], acc[i][1][4 * q + 1]),
+                         bf16pack(acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]));
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out2) + o) =
+            make_uint2(bf16pack(hv[0], hv[1]), bf16pack(hv[2], hv[3]));
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int col = nt * PB + wn * 64 + c * 32 + 8 * q + 4 * h;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][c][4 * q + r];
+          if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
+            const long long o = (long long)row * p.N + col;
+            const uint2 av = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.aux0) + o);
+            const uint2 bv = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.aux1) + o);
+            const uint32_t aw[2] = {av.x, av.y}, bw[2] = {bv.x, bv.y};
+            float da[4], db[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float a = bf16_to_f32((bf16_t)(aw[r >> 1] >> (16 * (r & 1))));
+              const float bb = bf16_to_f32((bf16_t)(bw[r >> 1] >> (16 * (r & 1))));
+              const float sg = sigmoid_f32(a);
+              da[r] = v[r] * bb * sg * (1.0f + a * (1.0f - sg));
+              db[r] = v[r] * a * sg;
+            }
+            bf16_t* dab = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * (2 * p.N);
+            *reinterpret_cast<uint2*>(dab + col) = make_uint2(bf16pack(da[0], da[1]), bf16pack(da[2], da[3]));
+            *reinterpret_cast<uint2*>(dab + p.N + col) =
+                make_uint2(bf16pack(db[0], db[1]), bf16pack(db[2], db[3]));
+          } else {
+            bf16_t* dst;
+            if constexpr (RK) {
+              dst = row < p.split
+                        ? reinterpret_cast<bf16_t*>(p.out0) + ((long long)g * p.split + row) * p.N + col
+                        : reinterpret_cast<bf16_t*>(p.out1) +
+                              ((long long)g * (p.M - p.split) + (row - p.split)) * p.N + col;
+            } else {
+              dst = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * p.N + col;
+            }
+            *reinterpret_cast<uint2*>(dst) = make_uint2(bf16pack(v[0], v[1]), bf16pack(v[2], v[3]));
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, bool RK>
+hipError_t launch_mx_pipe(const MxGemmArgs& a, int blocks, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_pipe_kernel<EPI, RK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, P_LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((mx_gemm_pipe_kernel<EPI, RK>), dim3(blocks), dim3(512), P_LDS, s, a);
+  return hipGetLastError();
+}
+
 template <int EPI, bool RK>
 hipError_t launch_mx(const MxGemmArgs& a, int blocks, hipStream_t s) {
   hipLaunchKernelGGL((mx_gemm_kernel<EPI, RK>), dim3(blocks), dim3(256), 0, s, a);
@@ -505,20 +821,32 @@ hipError_t launch_mx_quant_cols(const void* x, long long R, int N, long long ldx
 }
 
 hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream_t s) {
-  const int OC = epi == MX_EPI_SWIGLU ? 64 : TB;
+  // The pipelined 256x256 kernel covers output widths that are multiples of its tile (128 columns
+  // for SwiGLU) and, for weight gradients, output heights that are multiples of 256.
+  const bool pipe = (epi == MX_EPI_SWIGLU ? a.N % 128 == 0 : a.N % PB == 0) && (!ragged_k || a.M % PB == 0);
+  const int TM = pipe ? PB : TB;
+  const int OC = epi == MX_EPI_SWIGLU ? TM / 2 : TM;
   const long long NT = a.N / OC;
   long long tiles;
   if (!ragged_k) {
-    hipLaunchKernelGGL(mx_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.G, 0LL, (long long)a.M, TB, 1,
+    hipLaunchKernelGGL(mx_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.G, 0LL, (long long)a.M, TM, 1,
                        a.tile_prefix);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    tiles = ((long long)(a.M + TB - 1) / TB + a.G) * NT;
+    tiles = ((long long)(a.M + TM - 1) / TM + a.G) * NT;
   } else {
-    tiles = (long long)a.G * (a.M / TB) * NT;
+    tiles = (long long)a.G * (a.M / TM) * NT;
   }
   if (tiles == 0) return hipSuccess;
   const int blocks = (int)tiles;
+  if (pipe) {
+    if (ragged_k) return launch_mx_pipe<MX_EPI_STORE, true>(a, blocks, s);
+    switch (epi) {
+      case MX_EPI_SWIGLU: return launch_mx_pipe<MX_EPI_SWIGLU, false>(a, blocks, s);
+      case MX_EPI_SWIGLU_BWD: return launch_mx_pipe<MX_EPI_SWIGLU_BWD, false>(a, blocks, s);
+      default: return launch_mx_pipe<MX_EPI_STORE, false>(a, blocks, s);
+    }
+  }
   if (ragged_k) return launch_mx<MX_EPI_STORE, true>(a, blocks, s);
   switch (epi) {
     case MX_EPI_SWIGLU: return launch_mx<MX_EPI_SWIGLU, false>(a, blocks, s);

@@ -95,6 +95,34 @@ class Buffers:
         return self.t[k]
 
 
+class MxSet:
+    """Buffers and calls of one expert set (routed experts, or the shared expert as one group) in
+    MXFP8: every product quantizes both operands along its contraction axis (E4M3 codes, one E8M0
+    scale per 32 elements) and multiplies them on the block-scaled matrix instruction.  Weights are
+    quantized once per pass in each orientation the products need."""
+
+    KPAD = 128   # weight gradients: each group's rows padded to a multiple of this
+
+    def __init__(self, offsets, G, M, d, f, device, backward):
+        self.offsets, self.G, self.M, self.d, self.f = offsets, G, M, d, f
+        u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device=device)
+        q = lambda R, K: (u8(max(R, 1), K), u8(max(R, 1), K // 32))
+        self.xq = q(M, d)
+        self.w1q, self.w3q, self.w2q = q(G * f, d), q(G * f, d), q(G * d, f)
+        self.hq = q(M, f)
+        self.ws = u8(max(L.moe_mx_gemm_workspace_size(G), 256))
+        if backward:
+            self.dyq = q(M, d)
+            self.dabq = q(M, 2 * f)
+            self.w2t = q(f, G * d)          # W2 along d: [f, G d]
+            self.w1t, self.w3t = q(d, G * f), q(d, G * f)   # W1, W3 along f: [d, G f]
+            self.ld = max(int(L.moe_mx_quantize_cols_ld(M, G, self.KPAD)), self.KPAD)
+            self.dyc, self.hc = q(d, self.ld), q(f, self.ld)
+            self.abc, self.xc = q(2 * f, self.ld), q(d, self.ld)
+            self.kbase = torch.empty(G + 1, dtype=torch.int32, device=device)
+            self.kbase_w = torch.empty(G + 1, dtype=torch.int32, device=device)
+
+
 class MoELayer:
     """One GPU's MoE layer pass over device-resident inputs.
 
@@ -109,10 +137,14 @@ class MoELayer:
     H only), and the backward runs the gate/up GEMM again to regenerate A, B and H before the
     down-projection dgrad.  The kernels are deterministic, so the results are bitwise those of the
     stashing pass.
+    ``precision``: "bf16" (bf16 MFMA products) or "mxfp8" (the MXFP8 recipe of the Ultra runs, "Olmo-core
+    DDP MoE examples", "Production throughput runs": every expert product on MX-quantized E4M3
+    operands with fp32 accumulation; stored activations and gradients stay bf16).
     """
 
     def __init__(self, cfg: MoEConfig, params: dict, bufs: Buffers | None = None, renormalize: int = 1,
-                 merge_shared: bool = True, recompute: bool = False, lbl_weight: float = 0.0):
+                 merge_shared: bool = True, recompute: bool = False, lbl_weight: float = 0.0,
+                 precision: str = "bf16"):
         self.cfg = cfg
         self.p = params
         self.bufs = bufs or Buffers.allocate(cfg, params["x"].device)
@@ -134,6 +166,17 @@ class MoELayer:
                                               dtype=torch.uint8, device=dev)
         self.dt = L.MOE_BF16 if cfg.dtype == "bf16" else L.MOE_F32
         self.events: dict | None = None
+        if precision not in ("bf16", "mxfp8"):
+            raise ValueError(f"unknown precision {precision!r}")
+        self.precision = precision
+        self.mx = None
+        if precision == "mxfp8":
+            if cfg.dtype != "bf16" or recompute:
+                raise ValueError("the MXFP8 expert path takes bf16 workloads without recompute")
+            dev, b = params["x"].device, self.bufs
+            self.mx = [MxSet(b["offsets"], cfg.E, cfg.T * cfg.k, cfg.d, cfg.f, dev, cfg.backward)]
+            if cfg.fs > 0:
+                self.mx.append(MxSet(b["shared_offsets"], 1, cfg.T, cfg.d, cfg.fs, dev, cfg.backward))
 
     def _sets(self, dout=None, stash=True):
         """The routed experts and (if any) the shared expert as expert sets; stash=False leaves out
@@ -189,9 +232,12 @@ class MoELayer:
         if self.lbl > 0:
             self._stage("router_aux", L.moe_router_aux, logits, b["counts"], T, E, k, self.lbl, b["lbl_loss"],
                         b["prob_mean"], b["load_frac"], b["ws_aux"], b["ws_aux"].numel())
-        sets = self._sets(stash=not self.recompute)
-        self._gemm("gate_up_fwd", L.MOE_STAGE_GATE_UP_FWD, sets, b["ws_fwd"])
-        self._gemm("down_fwd", L.MOE_STAGE_DOWN_FWD, sets, b["ws_fwd"])
+        if self.mx is not None:
+            self._mx_forward()
+        else:
+            sets = self._sets(stash=not self.recompute)
+            self._gemm("gate_up_fwd", L.MOE_STAGE_GATE_UP_FWD, sets, b["ws_fwd"])
+            self._gemm("down_fwd", L.MOE_STAGE_DOWN_FWD, sets, b["ws_fwd"])
         shared = b["s"] if fs > 0 else None
         self._stage("combine", L.moe_combine, b["y"], b["gate"], b["dest_pos"], shared, T, d, k, dt, b["out"])
         return b["out"]
@@ -214,6 +260,13 @@ class MoELayer:
                 self._stage("router_aux_bwd", L.moe_router_aux_bwd, b["logits"], b["load_frac"], p["x"],
                             p["w_router"], T, d, E, self.lbl, dt, b["dwr"], b["dx_router"], b["ws_aux_bwd"],
                             b["ws_aux_bwd"].numel())
+        dx_shared = b["dx_shared"] if fs > 0 else None
+        if self.mx is not None:
+            self._mx_dgrad(dout)
+            self._stage("permute_bwd", L.moe_permute_bwd, b["dx_perm"], b["dest_pos"], dx_shared, dx_router, T,
+                        d, k, dt, b["dx"])
+            self._mx_wgrad(dout)
+            return b["dx"]
         ws = b["ws_bwd"]
         sets = self._sets(dout)
         if self.recompute:
@@ -223,12 +276,81 @@ class MoELayer:
         # weight gradients, which nothing downstream reads, go last.
         self._gemm("down_bwd", L.MOE_STAGE_DOWN_BWD, sets, ws)
         self._gemm("gate_up_dgrad", L.MOE_STAGE_GATE_UP_DGRAD, sets, ws)
-        dx_shared = b["dx_shared"] if fs > 0 else None
         self._stage("permute_bwd", L.moe_permute_bwd, b["dx_perm"], b["dest_pos"], dx_shared, dx_router, T, d,
                     k, dt, b["dx"])
         self._gemm("down_wgrad", L.MOE_STAGE_DOWN_WGRAD, sets, ws)
         self._gemm("gate_up_wgrad", L.MOE_STAGE_GATE_UP_WGRAD, sets, ws)
         return b["dx"]
+
+    # ---- MXFP8 expert products -------------------------------------------------------------
+    def _mx_tensors(self, i, dout=None):
+        """Input, weights, stash and gradient buffers of expert set i (0: routed, 1: shared)."""
+        p, b, t = self.p, self.bufs, self.bufs.t
+        if i == 0:
+            return dict(x=b["x_perm"], w1=p["w1"], w3=p["w3"], w2=p["w2"], a=t.get("a"), b=t.get("b"), h=b["h"],
+                        y=b["y"], dy=t.get("dy"), dab=t.get("dab"), dx=t.get("dx_perm"), dw1=t.get("dw1"),
+                        dw3=t.get("dw3"), dw2=t.get("dw2"))
+        return dict(x=p["x"], w1=p["ws1"], w3=p["ws3"], w2=p["ws2"], a=t.get("as"), b=t.get("bs"), h=b["hs"],
+                    y=b["s"], dy=dout, dab=t.get("dabs"), dx=t.get("dx_shared"), dw1=t.get("dws1"),
+                    dw3=t.get("dws3"), dw2=t.get("dws2"))
+
+    @staticmethod
+    def _pfx(i, name):
+        return name if i == 0 else "shared_" + name
+
+    def _mx_forward(self):
+        d, bw = self.cfg.d, self.cfg.backward
+        for i, m in enumerate(self.mx):
+            t, G, M, f = self._mx_tensors(i), m.G, m.M, m.f
+            q = lambda name, x, R, K, out: self._stage(self._pfx(i, name), L.moe_mx_quantize_rows, x, R, K, K,
+                                                       out[0], out[1])
+            q("q_w1", t["w1"], G * f, d, m.w1q)
+            q("q_w3", t["w3"], G * f, d, m.w3q)
+            q("q_w2", t["w2"], G * d, f, m.w2q)
+            q("q_x", t["x"], M, d, m.xq)
+            self._stage(self._pfx(i, "gate_up_fwd"), L.moe_mx_gemm_rows, m.xq[0], m.xq[1], m.w1q[0], m.w1q[1], d,
+                        f * d, m.w3q[0], m.w3q[1], 0, m.offsets, G, M, f, d, L.MOE_MX_EPI_SWIGLU,
+                        t["a"] if bw else None, t["b"] if bw else None, t["h"], None, None, m.ws, m.ws.numel())
+            q("q_h", t["h"], M, f, m.hq)
+            self._stage(self._pfx(i, "down_fwd"), L.moe_mx_gemm_rows, m.hq[0], m.hq[1], m.w2q[0], m.w2q[1], f,
+                        d * f, None, None, 0, m.offsets, G, M, d, f, L.MOE_MX_EPI_STORE, t["y"], None, None, None,
+                        None, m.ws, m.ws.numel())
+
+    def _mx_dgrad(self, dout):
+        d = self.cfg.d
+        for i, m in enumerate(self.mx):
+            t, G, M, f = self._mx_tensors(i, dout), m.G, m.M, m.f
+            q = lambda name, x, R, K, out: self._stage(self._pfx(i, name), L.moe_mx_quantize_rows, x, R, K, K,
+                                                       out[0], out[1])
+            qt = lambda name, x, R, N, rows, out, ld: self._stage(
+                self._pfx(i, name), L.moe_mx_quantize_cols, x, R, N, N, None, G, rows, m.KPAD, out[0], out[1], ld,
+                m.kbase_w)
+            q("q_dy", t["dy"], M, d, m.dyq)
+            qt("q_w2t", t["w2"], G * d, f, d, m.w2t, G * d)
+            self._stage(self._pfx(i, "down_bwd"), L.moe_mx_gemm_rows, m.dyq[0], m.dyq[1], m.w2t[0], m.w2t[1], G * d,
+                        d, None, None, 0, m.offsets, G, M, f, d, L.MOE_MX_EPI_SWIGLU_BWD, t["dab"], None, None,
+                        t["a"], t["b"], m.ws, m.ws.numel())
+            q("q_dab", t["dab"], M, 2 * f, m.dabq)
+            qt("q_w1t", t["w1"], G * f, d, f, m.w1t, G * f)
+            qt("q_w3t", t["w3"], G * f, d, f, m.w3t, G * f)
+            self._stage(self._pfx(i, "gate_up_dgrad"), L.moe_mx_gemm_rows, m.dabq[0], m.dabq[1], m.w1t[0],
+                        m.w1t[1], G * f, f, m.w3t[0], m.w3t[1], f, m.offsets, G, M, d, 2 * f, L.MOE_MX_EPI_STORE,
+                        t["dx"], None, None, None, None, m.ws, m.ws.numel())
+
+    def _mx_wgrad(self, dout):
+        d = self.cfg.d
+        for i, m in enumerate(self.mx):
+            t, G, M, f = self._mx_tensors(i, dout), m.G, m.M, m.f
+            qc = lambda name, x, N, out: self._stage(self._pfx(i, name), L.moe_mx_quantize_cols, x, M, N, N,
+                                                     m.offsets, G, 0, m.KPAD, out[0], out[1], m.ld, m.kbase)
+            qc("q_dy_cols", t["dy"], d, m.dyc)
+            qc("q_h_cols", t["h"], f, m.hc)
+            self._stage(self._pfx(i, "down_wgrad"), L.moe_mx_gemm_k, m.dyc[0], m.dyc[1], m.ld, m.hc[0], m.hc[1],
+                        m.ld, m.kbase, G, d, f, d, t["dw2"], None)
+            qc("q_dab_cols", t["dab"], 2 * f, m.abc)
+            qc("q_x_cols", t["x"], d, m.xc)
+            self._stage(self._pfx(i, "gate_up_wgrad"), L.moe_mx_gemm_k, m.abc[0], m.abc[1], m.ld, m.xc[0],
+                        m.xc[1], m.ld, m.kbase, G, 2 * f, d, f, t["dw1"], t["dw3"])
 
     def step(self):
         """One pass of the whole path: forward, then backward when the workload has one."""

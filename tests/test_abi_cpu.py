@@ -137,14 +137,25 @@ def test_mxfp8_argument_checks(lib):
     ws = L.moe_mx_gemm_workspace_size(8)
     assert ws >= 9 * 4
     g = L.moe_mx_gemm_rows
-    base = lambda N, K, epi, w: (FAKE, FAKE, FAKE, FAKE, K, N * K, FAKE, 8, 512, N, K, epi, FAKE, FAKE, FAKE, FAKE,
-                                 FAKE, FAKE, w)
+    up = lambda epi: FAKE if epi == L.MOE_MX_EPI_SWIGLU else None    # second B source: SwiGLU up rows
+    base = lambda N, K, epi, w: (FAKE, FAKE, FAKE, FAKE, K, N * K, up(epi), up(epi), 0, FAKE, 8, 512, N, K, epi, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, w)
     _expect(L.MOE_ERR_UNSUPPORTED, g, *base(256, 192, L.MOE_MX_EPI_STORE, ws))
     _expect(L.MOE_ERR_UNSUPPORTED, g, *base(192, 256, L.MOE_MX_EPI_STORE, ws))
     _expect(L.MOE_ERR_INVALID_VALUE, g, *base(256, 256, 7, ws))
     _expect(L.MOE_ERR_WORKSPACE, g, *base(256, 256, L.MOE_MX_EPI_STORE, ws - 1))
     args = list(base(192, 256, L.MOE_MX_EPI_SWIGLU, ws))
-    args[14] = None   # out2 (H) is required
+    args[17] = None   # out2 (H) is required
+    _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
+    args = list(base(192, 256, L.MOE_MX_EPI_SWIGLU, ws))
+    args[6] = args[7] = None   # the up rows are required
+    _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
+    args = list(base(256, 256, L.MOE_MX_EPI_STORE, ws))
+    args[6] = args[7] = FAKE
+    args[8] = 64               # the K split must be a multiple of 128 inside (0, K)
+    _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
+    args[8] = 128
+    args[7] = None             # codes without scales
     _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
     gk = L.moe_mx_gemm_k
     _expect(L.MOE_ERR_UNSUPPORTED, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 192, 256, 0, None, FAKE)

@@ -7,8 +7,9 @@
 // contraction axis; shared exponent floor(log2(block max)) - 8, clamped to [-127, 127] (-127 for an
 // all-zero block); elements rounded to nearest, ties to even, magnitudes past 448 saturated to 448.
 //
-// Quantization works on the bit patterns (integer shifts with round-to-nearest-even), so every code
-// and every scale byte is exact.  The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4: lane i + 32h of
+// The shared exponent comes from the bit pattern of the block maximum; elements are scaled by an exact
+// power of two, clamped to +-448 and converted by the hardware's round-to-nearest-even E4M3
+// conversion, so every code and every scale byte is exact.  The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4: lane i + 32h of
 // an operand holds row i, bytes 0..15 in the first 32-element block of the 64-wide K step (k =
 // 16h..16h+15) and bytes 16..31 in the second (k = 32+16h..); the scale of block b of row i comes
 // from lane i + 32b.  Products of E4M3 values and power-of-two scales are exact in fp32, and are
@@ -46,47 +47,24 @@ __device__ __forceinline__ int mx_shared_exp(uint32_t amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// x / 2^s rounded to nearest, ties to even (1 <= s <= 31).
-__device__ __forceinline__ uint32_t rne_shr(uint32_t x, int s) {
-  const uint32_t q = x >> s, rem = x & ((1u << s) - 1u), half = 1u << (s - 1);
-  return q + (uint32_t)((rem > half) | ((rem == half) & (q & 1u)));
+// E4M3 codes of v / 2^e: the power-of-two scaling is exact (ldexp), the clamp to +-448 makes the
+// saturation explicit, and the hardware conversion rounds to nearest with ties to even (for bf16
+// inputs this equals the bit-level definition for every finite value and every shared exponent in
+// [-127, 119]; the device tests compare every code with the oracle).  a -> byte 0, b -> byte 1 of
+// the half-word selected by HI.
+__device__ __forceinline__ float mx_scaled(uint32_t bits, int e) {
+  return fminf(fmaxf(ldexpf(__uint_as_float(bits), -e), -448.0f), 448.0f);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pack2(uint32_t old, uint32_t a, uint32_t b, int e) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(a, e), mx_scaled(b, e), (int)old, HI);
+}
+// Four bf16 values (two dwords of bf16 pairs) -> four codes in one dword, in order.
+__device__ __forceinline__ uint32_t e4m3_pack4(uint32_t w0, uint32_t w1, int e) {
+  const uint32_t lo = e4m3_pack2<false>(0u, w0 << 16, w0 & 0xffff0000u, e);
+  return e4m3_pack2<true>(lo, w1 << 16, w1 & 0xffff0000u, e);
 }
 
-// E4M3 code of v / 2^e (v given by its fp32 bits).
-__device__ __forceinline__ uint32_t e4m3_code(uint32_t bits, int e) {
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t a = bits & 0x7fffffffu;
-  if (a == 0) return sign;
-  uint32_t sig;
-  int lg;
-  if (a >> 23) {
-    sig = (a & 0x7fffffu) | 0x800000u;
-    lg = (int)(a >> 23) - 127;
-  } else {  // fp32 subnormal: normalise the significand
-    const int lz = __clz(a) - 8;
-    sig = a << lz;
-    lg = -126 - lz;
-  }
-  const int ey = lg - e;  // binade of the scaled value
-  uint32_t code;
-  if (ey >= -6) {  // normal E4M3: keep 3 fraction bits
-    if (ey > 8) return sign | 0x7eu;
-    uint32_t r = rne_shr(sig, 20);  // 8..16
-    int eb = ey + 7;
-    if (r == 16) {
-      r = 8;
-      ++eb;
-    }
-    code = ((uint32_t)eb << 3) | (r - 8);
-    if (code > 0x7eu) code = 0x7eu;  // 480 and up saturate to 448
-  } else {  // subnormal E4M3: multiples of 2^-9 (a result of 8 is the smallest normal, code 8)
-    const int s = 14 - ey;
-    code = s >= 25 ? 0u : rne_shr(sig, s);
-  }
-  return sign | code;
-}
-
-__device__ __forceinline__ uint32_t bf16_bits_f32(uint32_t h) { return h << 16; }
 
 // ---- Row quantization: 8 elements per lane, 4 lanes per block ---------------------------------
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16_t* __restrict__ x, long long R, int K,
@@ -109,15 +87,8 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const bf16_t* __rest
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
     const int e = mx_shared_exp(amax);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lo |= e4m3_code(bf16_bits_f32(w[j] & 0xffffu), e) << (16 * j);
-      lo |= e4m3_code(bf16_bits_f32(w[j] >> 16), e) << (16 * j + 8);
-      hi |= e4m3_code(bf16_bits_f32(w[j + 2] & 0xffffu), e) << (16 * j);
-      hi |= e4m3_code(bf16_bits_f32(w[j + 2] >> 16), e) << (16 * j + 8);
-    }
-    *reinterpret_cast<uint2*>(codes + r * K + (long long)c * 8) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(codes + r * K + (long long)c * 8) =
+        make_uint2(e4m3_pack4(w[0], w[1], e), e4m3_pack4(w[2], w[3], e));
     if ((c & 3) == 0) scales[r * (K >> 5) + (c >> 2)] = (uint8_t)(e + 127);
   }
 }
@@ -154,17 +125,20 @@ __global__ __launch_bounds__(1024) void mx_prefix_kernel(const int32_t* __restri
   if (t == 0) out[0] = 0;
 }
 
-// ---- Column quantization: a 32-row block of one group x 512 columns per workgroup ------------
+// ---- Column quantization: 128 padded rows of one group x 512 columns per workgroup ----------
+// Each thread quantizes two columns over four 32-row blocks and writes each column's 128 codes as
+// one 128-byte run and its four scale bytes as one dword.  Groups are padded to a multiple of 128
+// rows, so a 128-row chunk never spans two groups.
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __restrict__ x, long long R, int N,
                                                             long long ldx, const int32_t* __restrict__ offsets,
                                                             int G, long long group_rows,
                                                             const int32_t* __restrict__ kbase,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales, long long ldc) {
-  const long long k0 = (long long)blockIdx.x * 32;
+  const long long k0 = (long long)blockIdx.x * 128;
   const int n = (blockIdx.y * 256 + threadIdx.x) * 2;
   const long long ktot = kbase[G];
-  long long r0 = 0, rhi = 0;  // source rows of this block: [r0, min(r0 + 32, rhi))
+  long long r0 = 0, rhi = 0;  // source rows of this chunk: [r0, min(r0 + 128, rhi))
   if (k0 < ktot) {
     int lo = 0, hi = G;
     while (hi - lo > 1) {
@@ -183,28 +157,39 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __rest
     rhi = ghi;
   }
   if (n >= N) return;
-  uint32_t v[32];
+  u32x4_t out[2][8];
+  uint32_t sc[2] = {0u, 0u};
 #pragma unroll
-  for (int j = 0; j < 32; ++j)
-    v[j] = r0 + j < rhi ? *reinterpret_cast<const uint32_t*>(x + (r0 + j) * ldx + n) : 0u;
+  for (int blk = 0; blk < 4; ++blk) {
+    uint32_t v[32];
+    const long long rb = r0 + 32 * blk;
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      v[j] = rb + j < rhi ? *reinterpret_cast<const uint32_t*>(x + (rb + j) * ldx + n) : 0u;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t amax = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = max(amax, ((v[j] >> (16 * c)) & 0x7fffu) << 16);
+      const int e = mx_shared_exp(amax);
+      sc[c] |= (uint32_t)(e + 127) << (8 * blk);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        // column c of rows 4q .. 4q+3 of the block, as bf16 bit patterns in the upper halves
+        const uint32_t x0 = c ? (v[4 * q] & 0xffff0000u) : (v[4 * q] << 16);
+        const uint32_t x1 = c ? (v[4 * q + 1] & 0xffff0000u) : (v[4 * q + 1] << 16);
+        const uint32_t x2 = c ? (v[4 * q + 2] & 0xffff0000u) : (v[4 * q + 2] << 16);
+        const uint32_t x3 = c ? (v[4 * q + 3] & 0xffff0000u) : (v[4 * q + 3] << 16);
+        out[c][2 * blk + (q >> 2)][q & 3] = e4m3_pack2<true>(e4m3_pack2<false>(0u, x0, x1, e), x2, x3, e);
+      }
+    }
+  }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    uint32_t amax = 0;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + (long long)(n + c) * ldc + k0);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) amax = max(amax, ((v[j] >> (16 * c)) & 0x7fffu) << 16);
-    const int e = mx_shared_exp(amax);
-    uint32_t w[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      w[q] = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        w[q] |= e4m3_code(bf16_bits_f32((v[4 * q + b] >> (16 * c)) & 0xffffu), e) << (8 * b);
-    }
-    uint8_t* dst = codes + (long long)(n + c) * ldc + k0;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-    scales[(long long)(n + c) * (ldc >> 5) + blockIdx.x] = (uint8_t)(e + 127);
+    for (int q = 0; q < 8; ++q) dst[q] = out[c][q];
+    *reinterpret_cast<uint32_t*>(scales + (long long)(n + c) * (ldc >> 5) + (k0 >> 5)) = sc[c];
   }
 }
 
@@ -814,7 +799,7 @@ hipError_t launch_mx_quant_cols(const void* x, long long R, int N, long long ldx
   hipLaunchKernelGGL(mx_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, G, group_rows, R, kpad, kpad, kbase);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ldc == 0 || N == 0) return e;
-  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3((unsigned)(ldc / 32), (unsigned)((N + 511) / 512)), dim3(256), 0,
+  hipLaunchKernelGGL(mx_quant_cols_kernel, dim3((unsigned)(ldc / 128), (unsigned)((N + 511) / 512)), dim3(256), 0,
                      s, reinterpret_cast<const bf16_t*>(x), R, N, ldx, offsets, G, group_rows, kbase, codes,
                      scales, ldc);
   return hipGetLastError();

@@ -60,6 +60,36 @@ def test_quantize_rows_bit_exact(R, K, pad):
     assert np.array_equal(u8(codes), rc), "E4M3 codes differ"
 
 
+def every_finite_bf16_blocks():
+    """Every finite bf16 value, twice: once in blocks of 32 values of similar magnitude (sorted, so a
+    block's maximum sits just above its elements) and once in blocks led by a power of two far larger
+    than the rest (so small elements land in E4M3's subnormal range or round to signed zero)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]                         # drop Inf / NaN
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    srt = vals[np.argsort(np.abs(vals), kind="stable")]
+    n = len(srt) // 31 * 31
+    lead = np.exp2(np.floor(np.log2(np.maximum(np.abs(srt[:n:31]), 2.0 ** -126))) + 12)
+    lead = np.minimum(lead, 2.0 ** 127)
+    blocks = np.concatenate([lead[:, None], srt[:n].reshape(-1, 31)], axis=1)
+    both = np.concatenate([np.resize(srt, (len(srt) + 31) // 32 * 32), blocks.ravel()])
+    both = np.resize(both, (len(both) + 1023) // 1024 * 1024)
+    return both.reshape(-1, 1024)
+
+
+def test_quantize_rows_every_bf16_value():
+    x = every_finite_bf16_blocks()
+    R, K = x.shape
+    log(f"mx quantize rows, every finite bf16 value: R={R} K={K}")
+    codes = torch.empty((R, K), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=DEV)
+    L.moe_mx_quantize_rows(dev_tensor(x, "bf16"), R, K, K, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = MX.mx_quantize_rows(x)
+    assert np.array_equal(u8(scales), rs), "scale bytes differ"
+    assert np.array_equal(u8(codes), rc), "E4M3 codes differ"
+
+
 @pytest.mark.parametrize("R,N,G,kpad,uniform", [(1000, 256, 8, 128, False), (2048, 128, 4, 128, True),
                                                 (77, 64, 5, 256, False)])
 def test_quantize_cols_bit_exact(R, N, G, kpad, uniform):

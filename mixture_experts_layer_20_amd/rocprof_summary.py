@@ -45,6 +45,10 @@ def short_name(name: str) -> str:
     m = re.search(r"grouped_gemm_bf16<(\d), [^>]*Cfg<(\d+), (\d+), (\d), (\d)>", name)
     if m:
         return f"grouped_gemm_bf16[{MODES[int(m.group(1))]}, {m.group(2)}x{m.group(3)}, {int(m.group(4)) * int(m.group(5))} waves]"
+    m = re.search(r"(mx_gemm_pipe_kernel|mx_gemm_kernel)<(\d), (true|false)>", name)
+    if m:
+        epi = "wgrad" if m.group(3) == "true" else ("store", "swiglu", "swiglu_bwd")[int(m.group(2))]
+        return f"{m.group(1).replace('_kernel', '')}[{epi}]"
     m = re.search(r"(grouped_gemm_pipe|grouped_gemm_bf16_dma|splitk_reduce)<(\d)>", name)
     if m:
         return f"{m.group(1)}[{MODES[int(m.group(2))]}]"
@@ -94,10 +98,10 @@ def per_stage_counter(pmc_csv: str, counter: str, sets_per_stage: int):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch", help="FETCH_SIZE pass (omit both counter passes for a trace-only summary)")
+    ap.add_argument("--write")
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--copy-mb", type=int, required=True)
+    ap.add_argument("--copy-mb", type=int, default=0)
     ap.add_argument("--command", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json")
@@ -111,6 +115,17 @@ def main(argv=None) -> int:
     for r, mode, label in labelled_dispatches(trace, "Kernel_Name", "Dispatch_Id", a.sets_per_stage):
         if mode:
             durs[(mode, label)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if not (a.fetch and a.write):
+        lines = [f"# rocprofv3 summary: kernels of one layer step, workload {a.workload}", "",
+                 "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", "",
+                 "## Kernel statistics (--kernel-trace --stats)", "",
+                 "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+        for r in stats:
+            lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        open(a.out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return 0
     fcsv = os.path.join(a.fetch, "run_counter_collection.csv")
     wcsv = os.path.join(a.write, "run_counter_collection.csv")
     fs = copy_scale(fcsv, "FETCH_SIZE", a.copy_mb)

@@ -306,3 +306,43 @@ def test_mx_layer_matches_oracle(case):
     # device's fp32-versus-float64 difference; single products are held to 4e-3 above.
     for name, (got, ref) in checks.items():
         assert_close(name, tnp(got), ref, 5e-2)
+
+
+@pytest.mark.parametrize("name", ["tiny64e_random", "tiny64e_learned_skew"])
+def test_mx_layer_full_size_sampled_experts(name):
+    """The MXFP8 layer at the full Tiny-64E shape (the bench's launch configuration).  Routing and
+    dispatch are bit-exact over the whole batch; an expert's products depend only on its own rows,
+    so the oracle runs the MXFP8 expert on the busiest and the least busy non-empty expert and the
+    device's Y rows, dX_perm rows and weight gradients of those experts are compared."""
+    from mixture_experts_layer_20_amd import inputs as I
+    from mixture_experts_layer_20_amd import layer as LY
+    from tests.gpu_helpers import full_routing
+    cfg = I.CONFIGS[name]
+    log(f"mx full-size layer {name}")
+    inp = I.make_inputs(cfg)
+    vals = I.values(inp)
+    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, DEV), precision="mxfp8")
+    lay.step()
+    torch.cuda.synchronize()
+    b = lay.bufs
+    R = full_routing(cfg, vals)
+    for key in ("topk_idx", "offsets", "dest_pos", "src_row"):
+        assert np.array_equal(tnp(b[key]).reshape(-1), np.asarray(R[key]).reshape(-1)), key
+    counts, offs, src = R["counts"], R["offsets"], np.asarray(R["src_row"], np.int64)
+    nz = np.nonzero(counts)[0]
+    ex = MX.MXExperts()
+    for e in sorted({int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])}):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        tok, slot = src[r0:r1] // cfg.k, src[r0:r1] % cfg.k
+        X = vals["x"][tok].astype(np.float64)
+        dY = R["gates"][tok, slot][:, None] * vals["dout"][tok].astype(np.float64)
+        A, B, H, Y = ex.forward(X, vals["w1"][e], vals["w3"][e], vals["w2"][e])
+        dX, dW1, dW3, dW2, _, _ = ex.backward(dY, X, A, B, H, vals["w1"][e], vals["w3"][e], vals["w2"][e])
+        log(f"  expert {e}: {r1 - r0} rows")
+        assert_close(f"y[{e}]", tnp(b["y"][r0:r1]), Y, 5e-2)
+        assert_close(f"dx_perm[{e}]", tnp(b["dx_perm"][r0:r1]), dX, 5e-2)
+        assert_close(f"dw1[{e}]", tnp(b["dw1"][e]), dW1, 5e-2)
+        assert_close(f"dw3[{e}]", tnp(b["dw3"][e]), dW3, 5e-2)
+        assert_close(f"dw2[{e}]", tnp(b["dw2"][e]), dW2, 5e-2)
+    for e in np.nonzero(counts == 0)[0]:
+        assert bool((b["dw2"][int(e)] == 0).all()), f"empty expert {e} has a nonzero gradient"

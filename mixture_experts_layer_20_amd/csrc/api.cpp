@@ -9,6 +9,7 @@
 #include <string>
 
 #include "common.h"
+#include "mxfp8.h"
 
 namespace {
 

@@ -8,31 +8,40 @@
 namespace moe {
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 8-element row segments.  NT: a stream nothing later in the layer pass reads again (a
+// nontemporal access, which does not displace reused data from the caches).
 template <typename T> struct V8;
 template <> struct V8<bf16_t> {
+  template <bool NT = false>
   __device__ static void load(const bf16_t* p, float (&v)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t w = NT ? __builtin_nontemporal_load(q) : *q;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  template <bool NT = false>
   __device__ static void store(bf16_t* p, const float (&v)[8]) {
-    uint32_t w[4];
+    u32x4_t w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    if (NT) __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    else *reinterpret_cast<u32x4_t*>(p) = w;
   }
 };
 template <> struct V8<float> {
+  template <bool NT = false>
   __device__ static void load(const float* p, float (&v)[8]) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
     const float4 b = reinterpret_cast<const float4*>(p)[1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
+  template <bool NT = false>
   __device__ static void store(float* p, const float (&v)[8]) {
     reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
     reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -58,17 +67,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* y_perm, const flo
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < k) {
-        V8<T>::load(y_perm + (size_t)rows[j] * d + c, v);
+        V8<T>::template load<true>(y_perm + (size_t)rows[j] * d + c, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += g[j] * v[i];
       }
     }
     if (shared) {
-      V8<T>::load(shared + (size_t)t * d + c, v);
+      V8<T>::template load<true>(shared + (size_t)t * d + c, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
-    V8<T>::store(out + (size_t)t * d + c, acc);
+    V8<T>::template store<true>(out + (size_t)t * d + c, acc);
   }
 }
 
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const T* dout, const T
         for (int i = 0; i < 8; ++i) o[i] = g[j] * go[i];
         V8<T>::store(dy_perm + (size_t)rows[j] * d + c, o);
         if (dgate) {
-          V8<T>::load(y_perm + (size_t)rows[j] * d + c, v);
+          V8<T>::template load<true>(y_perm + (size_t)rows[j] * d + c, v);
 #pragma unroll
           for (int i = 0; i < 8; ++i) dot[j] += go[i] * v[i];
         }

@@ -21,6 +21,7 @@
 // ds_read_b128 over 16 rows hits 16 distinct bank groups.  The B operand is the instruction's first
 // operand, so each lane's accumulators hold 4 consecutive output columns of one row.
 #include "common.h"
+#include "mxfp8.h"
 
 #include <algorithm>
 

@@ -19,7 +19,7 @@ namespace {
 
 constexpr int RT = 32;   // tokens per block
 constexpr int RE = 64;   // experts per block
-constexpr int RK = 32;   // features per LDS step
+constexpr int RK = 128;  // features per LDS step (long enough to cover the next step's global loads)
 constexpr int RTH = 256; // threads per block: 16 x 16, each 2 tokens x 4 experts (4 waves per CU)
 
 // 8 consecutive elements k0.. of a row as fp32 (0 past n; a 16-byte load when the row is aligned and
@@ -75,7 +75,7 @@ __device__ __forceinline__ void logits_step(const float* xrow, const float* wrow
 // Logits: one thread owns 2 tokens x 4 experts and walks the features in increasing order.
 // bf16 inputs: the product of two bf16 values is exact in fp32, so a fused multiply-add rounds
 // exactly like the separate product and sum.  fp32 inputs: separate multiply and add.  The next
-// 32-feature tile is loaded into registers while the current one is multiplied.
+// 128-feature tile is loaded into registers while the current one is multiplied.
 template <bool BF16>
 __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, const void* wv,
                                                             const float* bias, float* logits,
@@ -84,15 +84,20 @@ __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, cons
   __shared__ __attribute__((aligned(16))) float ws[RK][RE];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
-  // staging: thread q loads 8 features (chunk q % 4) of expert row q / 4, and threads q < 128 the
-  // same of token row q / 4
-  const int sr = tid >> 2, sk = (tid & 3) * 8;
-  const bool xload = tid < 128;
-  const bool xok = xload && t0 + sr < T, wok = e0 + sr < E;
-  const size_t xoff = (size_t)(xok ? t0 + sr : 0) * d, woff = (size_t)(wok ? e0 + sr : 0) * d;
-  float xr[8], wr[8];
-  row8<BF16>(xv, xoff, sk, d, xok, xr);
-  row8<BF16>(wv, woff, sk, d, wok, wr);
+  // staging: thread q loads features (q % 8) * 16 .. + 16 of token row q / 8, and features
+  // (q % 4) * 32 .. + 32 of expert row q / 4
+  const int xr_row = tid >> 3, xk = (tid & 7) * 16;
+  const int wr_row = tid >> 2, wk = (tid & 3) * 32;
+  const bool xok = t0 + xr_row < T, wok = e0 + wr_row < E;
+  const size_t xoff = (size_t)(xok ? t0 + xr_row : 0) * d, woff = (size_t)(wok ? e0 + wr_row : 0) * d;
+  float xr[2][8], wr[4][8];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) row8<BF16>(xv, xoff, k0 + xk + 8 * c, d, xok, xr[c]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) row8<BF16>(wv, woff, k0 + wk + 8 * c, d, wok, wr[c]);
+  };
+  fetch(0);
   float acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -101,15 +106,15 @@ __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, cons
 
   for (int k0 = 0; k0 < d; k0 += RK) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (xload) xs[sk + i][sr] = xr[i];
-      ws[sk + i][sr] = wr[i];
-    }
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xs[xk + 8 * c + i][xr_row] = xr[c][i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ws[wk + 8 * c + i][wr_row] = wr[c][i];
     __syncthreads();
-    if (k0 + RK < d) {
-      row8<BF16>(xv, xoff, k0 + RK + sk, d, xok, xr);
-      row8<BF16>(wv, woff, k0 + RK + sk, d, wok, wr);
-    }
+    if (k0 + RK < d) fetch(k0 + RK);
     const int kn = d - k0 < RK ? d - k0 : RK;
     if (kn == RK) {
 #pragma unroll

@@ -109,6 +109,9 @@ def main(argv=None) -> int:
                          "the backward")
     ap.add_argument("--precision", choices=("bf16", "mxfp8"), default="bf16",
                     help="expert products in bf16, or in MXFP8 (E4M3 with one E8M0 scale per 32 elements)")
+    ap.add_argument("--mx-cached-weights", action="store_true",
+                    help="MXFP8: quantize the expert weights once before the timed steps (the optimizer-step "
+                         "cadence, with several micro-batches per weight update) instead of in every pass")
     ap.add_argument("--no-merge", action="store_true",
                     help="one GEMM call per expert set instead of routed + shared in one call")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -136,7 +139,7 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     mx = a.precision == "mxfp8"
     lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not (a.no_merge or mx), recompute=a.recompute,
-                      lbl_weight=a.lbl, precision=a.precision)
+                      lbl_weight=a.lbl, precision=a.precision, mx_cached_weights=a.mx_cached_weights)
     if a.copy_probe_mb > 0:
         src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -197,6 +200,8 @@ def main(argv=None) -> int:
         "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k,
                    "expert_d_ff": cfg.f, "shared_d_ff": cfg.fs, "routing": cfg.routing,
                    "backward": cfg.backward, "recompute": a.recompute, "precision": a.precision,
+                   "mx_weights": ("quantized once (optimizer-step cadence)" if a.mx_cached_weights
+                                  else "quantized every pass") if mx else None,
                    "lbl_weight": a.lbl if cfg.routing == "learned" else 0.0},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},

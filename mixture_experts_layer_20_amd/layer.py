@@ -140,11 +140,15 @@ class MoELayer:
     ``precision``: "bf16" (bf16 MFMA products) or "mxfp8" (the MXFP8 recipe of the Ultra runs, "Olmo-core
     DDP MoE examples", "Production throughput runs": every expert product on MX-quantized E4M3
     operands with fp32 accumulation; stored activations and gradients stay bf16).
+    ``mx_cached_weights``: quantize the expert weights (both orientations) on the first pass and
+    reuse them until ``refresh_mx_weights()`` is called, as when the weights change once per
+    optimizer step and several micro-batches pass through the layer in between; otherwise every
+    pass quantizes them.
     """
 
     def __init__(self, cfg: MoEConfig, params: dict, bufs: Buffers | None = None, renormalize: int = 1,
                  merge_shared: bool = True, recompute: bool = False, lbl_weight: float = 0.0,
-                 precision: str = "bf16"):
+                 precision: str = "bf16", mx_cached_weights: bool = False):
         self.cfg = cfg
         self.p = params
         self.bufs = bufs or Buffers.allocate(cfg, params["x"].device)
@@ -170,6 +174,8 @@ class MoELayer:
             raise ValueError(f"unknown precision {precision!r}")
         self.precision = precision
         self.mx = None
+        self.mx_cached = bool(mx_cached_weights)
+        self._mx_w_fresh = False   # quantized weights valid (cached mode)
         if precision == "mxfp8":
             if cfg.dtype != "bf16" or recompute:
                 raise ValueError("the MXFP8 expert path takes bf16 workloads without recompute")
@@ -298,15 +304,38 @@ class MoELayer:
     def _pfx(i, name):
         return name if i == 0 else "shared_" + name
 
-    def _mx_forward(self):
-        d, bw = self.cfg.d, self.cfg.backward
+    def refresh_mx_weights(self):
+        """Cached mode: the weights changed; the next pass quantizes them again."""
+        self._mx_w_fresh = False
+
+    def _mx_quantize_weights(self):
+        """Expert weights of both sets in MXFP8: along d / f (forward), and transposed along f / d
+        (data gradients, when the layer has a backward)."""
+        d = self.cfg.d
         for i, m in enumerate(self.mx):
-            t, G, M, f = self._mx_tensors(i), m.G, m.M, m.f
+            t, G, f = self._mx_tensors(i), m.G, m.f
             q = lambda name, x, R, K, out: self._stage(self._pfx(i, name), L.moe_mx_quantize_rows, x, R, K, K,
                                                        out[0], out[1])
             q("q_w1", t["w1"], G * f, d, m.w1q)
             q("q_w3", t["w3"], G * f, d, m.w3q)
             q("q_w2", t["w2"], G * d, f, m.w2q)
+            if self.cfg.backward:
+                qt = lambda name, x, R, N, rows, out, ld: self._stage(
+                    self._pfx(i, name), L.moe_mx_quantize_cols, x, R, N, N, None, G, rows, m.KPAD, out[0], out[1],
+                    ld, m.kbase_w)
+                qt("q_w2t", t["w2"], G * d, f, d, m.w2t, G * d)
+                qt("q_w1t", t["w1"], G * f, d, f, m.w1t, G * f)
+                qt("q_w3t", t["w3"], G * f, d, f, m.w3t, G * f)
+        self._mx_w_fresh = True
+
+    def _mx_forward(self):
+        d, bw = self.cfg.d, self.cfg.backward
+        if not (self.mx_cached and self._mx_w_fresh):
+            self._mx_quantize_weights()
+        for i, m in enumerate(self.mx):
+            t, G, M, f = self._mx_tensors(i), m.G, m.M, m.f
+            q = lambda name, x, R, K, out: self._stage(self._pfx(i, name), L.moe_mx_quantize_rows, x, R, K, K,
+                                                       out[0], out[1])
             q("q_x", t["x"], M, d, m.xq)
             self._stage(self._pfx(i, "gate_up_fwd"), L.moe_mx_gemm_rows, m.xq[0], m.xq[1], m.w1q[0], m.w1q[1], d,
                         f * d, m.w3q[0], m.w3q[1], 0, m.offsets, G, M, f, d, L.MOE_MX_EPI_SWIGLU,
@@ -322,17 +351,11 @@ class MoELayer:
             t, G, M, f = self._mx_tensors(i, dout), m.G, m.M, m.f
             q = lambda name, x, R, K, out: self._stage(self._pfx(i, name), L.moe_mx_quantize_rows, x, R, K, K,
                                                        out[0], out[1])
-            qt = lambda name, x, R, N, rows, out, ld: self._stage(
-                self._pfx(i, name), L.moe_mx_quantize_cols, x, R, N, N, None, G, rows, m.KPAD, out[0], out[1], ld,
-                m.kbase_w)
             q("q_dy", t["dy"], M, d, m.dyq)
-            qt("q_w2t", t["w2"], G * d, f, d, m.w2t, G * d)
             self._stage(self._pfx(i, "down_bwd"), L.moe_mx_gemm_rows, m.dyq[0], m.dyq[1], m.w2t[0], m.w2t[1], G * d,
                         d, None, None, 0, m.offsets, G, M, f, d, L.MOE_MX_EPI_SWIGLU_BWD, t["dab"], None, None,
                         t["a"], t["b"], m.ws, m.ws.numel())
             q("q_dab", t["dab"], M, 2 * f, m.dabq)
-            qt("q_w1t", t["w1"], G * f, d, f, m.w1t, G * f)
-            qt("q_w3t", t["w3"], G * f, d, f, m.w3t, G * f)
             self._stage(self._pfx(i, "gate_up_dgrad"), L.moe_mx_gemm_rows, m.dabq[0], m.dabq[1], m.w1t[0],
                         m.w1t[1], G * f, f, m.w3t[0], m.w3t[1], f, m.offsets, G, M, d, 2 * f, L.MOE_MX_EPI_STORE,
                         t["dx"], None, None, None, None, m.ws, m.ws.numel())

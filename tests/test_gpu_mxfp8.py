@@ -346,3 +346,34 @@ def test_mx_layer_full_size_sampled_experts(name):
         assert_close(f"dw2[{e}]", tnp(b["dw2"][e]), dW2, 5e-2)
     for e in np.nonzero(counts == 0)[0]:
         assert bool((b["dw2"][int(e)] == 0).all()), f"empty expert {e} has a nonzero gradient"
+
+
+def test_mx_cached_weights_match_per_pass_quantization():
+    """Cached MXFP8 weights give bitwise the results of quantizing them in every pass, until the
+    weights change; refresh_mx_weights() makes the next pass see the new weights."""
+    from mixture_experts_layer_20_amd import inputs as I
+    from mixture_experts_layer_20_amd import layer as LY
+    cfg = I.CONFIGS["tiny64e_random"].with_(name="mx_cache", T=256, d=256, E=8, k=2, f=256, fs=256)
+    log("mx cached weights")
+    inp = I.make_inputs(cfg)
+    pa, pb = LY.upload_inputs(inp, DEV), LY.upload_inputs(inp, DEV)
+    every = LY.MoELayer(cfg, pa, precision="mxfp8")
+    cached = LY.MoELayer(cfg, pb, precision="mxfp8", mx_cached_weights=True)
+    keys = ("out", "dx", "dw1", "dw3", "dw2", "dws1")
+    same = lambda: all(torch.equal(every.bufs[k], cached.bufs[k]) for k in keys)
+    for _ in range(2):
+        every.step()
+        cached.step()
+    torch.cuda.synchronize()
+    assert same(), "cached weights differ from per-pass quantization"
+    for p in (pa, pb):
+        p["w1"].mul_(2.0)                       # a weight update (exact in bf16)
+    every.step()
+    cached.step()
+    torch.cuda.synchronize()
+    assert not torch.equal(every.bufs["out"], cached.bufs["out"]), "a stale cache should not see the update"
+    cached.refresh_mx_weights()
+    every.step()
+    cached.step()
+    torch.cuda.synchronize()
+    assert same(), "after refresh_mx_weights() the results differ"

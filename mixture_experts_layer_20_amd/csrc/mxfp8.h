@@ -40,6 +40,7 @@ struct MxGemmArgs {
   const void* aux0;
   const void* aux1;
   int split;              // ragged K: output rows [0, split) -> out0, [split, M) -> out1
+  int tiles;              // tile indices of the launch (set by the launcher)
 };
 hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream_t s);
 

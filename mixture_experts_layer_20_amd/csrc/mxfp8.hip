@@ -552,148 +552,115 @@ __device__ __forceinline__ i32x8_t frag8(const u32x4_t& lo, const u32x4_t& hi) {
   return r;
 }
 
-template <int EPI, bool RK>
-__global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) char plds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1, li = lane & 31, h = lane >> 5;
-  constexpr int OC = EPI == MX_EPI_SWIGLU ? 128 : PB;   // output columns per tile
-  const int NT = p.N / OC;
+// One output tile of the pipelined kernel.
+struct PTile {
+  int g, m0, m_end, nt, nk;
+  long long kb0;
+};
 
-  const int nb = gridDim.x, b = blockIdx.x;
-  int Lt;
-  {
-    const int per = nb >> 3, rem = nb & 7, xcd = b & 7;
-    Lt = xcd * per + min(xcd, rem) + (b >> 3);
-  }
-  const int nt = Lt % NT;
-  int g, m0, m_end;
-  long long kb0, kb1;
+__device__ __forceinline__ int ufirst(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Tile Lt of the launch (tile order: group by group, row tiles, column tiles fastest); false past the
+// last tile.
+template <bool RK>
+__device__ __forceinline__ bool pipe_tile(const MxGemmArgs& p, int Lt, int NT, PTile& t) {
+  t.nt = Lt % NT;
   if constexpr (!RK) {
     const int mt = Lt / NT;
-    if (mt >= p.tile_prefix[p.G]) return;
+    if (mt >= ufirst(p.tile_prefix[p.G])) return false;
     int lo = 0, hi = p.G;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (p.tile_prefix[mid] <= mt) lo = mid; else hi = mid;
+      if (ufirst(p.tile_prefix[mid]) <= mt) lo = mid; else hi = mid;
     }
-    g = lo;
-    const int r0 = min(max(p.offsets[g], 0), p.M);
-    const int r1 = min(max(p.offsets[g + 1], r0), p.M);
-    m0 = r0 + (mt - p.tile_prefix[g]) * PB;
-    m_end = r1;
-    kb0 = 0;
-    kb1 = p.K;
+    t.g = lo;
+    const int r0 = min(max(ufirst(p.offsets[lo]), 0), p.M);
+    const int r1 = min(max(ufirst(p.offsets[lo + 1]), r0), p.M);
+    t.m0 = r0 + (mt - ufirst(p.tile_prefix[lo])) * PB;
+    t.m_end = r1;
+    t.kb0 = 0;
+    t.nk = p.K / PK;
   } else {
     const int MT = p.M / PB;
     const int r = Lt / NT;
-    if (r >= p.G * MT) return;
-    g = r / MT;
-    m0 = (r - g * MT) * PB;
-    m_end = p.M;
-    kb0 = p.offsets[g];
-    kb1 = p.offsets[g + 1];
+    if (r >= p.G * MT) return false;
+    t.g = r / MT;
+    t.m0 = (r - t.g * MT) * PB;
+    t.m_end = p.M;
+    const int k0 = ufirst(p.offsets[t.g]), k1 = ufirst(p.offsets[t.g + 1]);
+    t.kb0 = k0;
+    t.nk = (k1 - k0) / PK;
   }
-  const int nk = (int)((kb1 - kb0) / PK);
-  const long long lda_s = p.lda >> 5, ldb_s = p.ldb >> 5;
-  const long long gofs = RK ? 0 : (long long)g * p.b_gstride;
-  const bool split = EPI != MX_EPI_SWIGLU && p.b2 != nullptr;
-  const int ks = split ? p.ksplit : 0x7fffffff;   // K columns from the second source start here
+  return true;
+}
 
+// This lane's load sources for one tile: code loads (instruction j of each operand fills slot
+// q = (2 wave + j) 64 + lane = row q >> 2, physical chunk q & 3; gb2: the same rows in the second
+// source at K column 0) and the scale dword (wave w < 4: A row 64 w + lane; else B row 64 (w - 4) +
+// lane).
+struct PLoad {
+  const uint8_t* ga[2];
+  const uint8_t* gb[2];
+  const uint8_t* gb2[2];
+  const uint8_t* gs;
+  const uint8_t* gs2;
+};
+
+template <int EPI, bool RK>
+__device__ __forceinline__ void pipe_sources(const MxGemmArgs& p, const PTile& t, bool split, int wave, int lane,
+                                             PLoad& L) {
+  const long long lda_s = p.lda >> 5, ldb_s = p.ldb >> 5;
+  const long long gofs = RK ? 0 : (long long)t.g * p.b_gstride;
   // B tile row r: its source (first or second) and row.  The SwiGLU tile holds gate rows (first
   // source) and up rows (second source) of 128 output columns.
   auto bsrc2 = [&](int r) -> bool { return EPI == MX_EPI_SWIGLU && ((r >> 5) & 1); };
   auto brow = [&](int r) -> int {
-    if constexpr (EPI == MX_EPI_SWIGLU) return nt * 128 + (r >> 6) * 32 + (r & 31);
-    else return nt * PB + r;
+    if constexpr (EPI == MX_EPI_SWIGLU) return t.nt * 128 + (r >> 6) * 32 + (r & 31);
+    else return t.nt * PB + r;
   };
-  auto arow = [&](int r) -> int { return RK ? m0 + r : min(m0 + r, m_end - 1); };
-
-  // This lane's code loads: instruction j (0, 1) of each operand fills slot q = (2 wave + j) 64 + lane
-  // = row q >> 2, physical chunk q & 3.  gb2: the same rows in the second source, K column 0.
-  const uint8_t* ga[2];
-  const uint8_t* gb[2];
-  const uint8_t* gb2[2];
+  auto arow = [&](int r) -> int { return RK ? t.m0 + r : min(t.m0 + r, t.m_end - 1); };
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int q = (2 * wave + j) * 64 + lane;
     const int row = q >> 2;
     const int c = (q & 3) ^ ((row >> 2) & 3);
-    ga[j] = p.a + (long long)arow(row) * p.lda + kb0 + 16 * c;
+    L.ga[j] = p.a + (long long)arow(row) * p.lda + t.kb0 + 16 * c;
     const long long bo = gofs + (long long)brow(row) * p.ldb + 16 * c;
-    gb[j] = (bsrc2(row) ? p.b2 : p.b) + bo + kb0;
-    gb2[j] = (split ? p.b2 : p.b) + bo;
+    L.gb[j] = (bsrc2(row) ? p.b2 : p.b) + bo + t.kb0;
+    L.gb2[j] = (split ? p.b2 : p.b) + bo;
   }
-  // Scale dword load: wave w < 4 loads A rows 64 w + lane, wave w >= 4 B rows 64 (w - 4) + lane.
-  const uint8_t* gs;
-  const uint8_t* gs2;
-  {
-    const int r = (wave & 3) * 64 + lane;
-    const long long bo = (gofs >> 5) + (long long)brow(r) * ldb_s;
-    gs = wave < 4 ? p.as + (long long)arow(r) * lda_s + (kb0 >> 5) : (bsrc2(r) ? p.bs2 : p.bs) + bo + (kb0 >> 5);
-    gs2 = wave < 4 ? gs : (split ? p.bs2 : p.bs) + bo;
+  const int r = (wave & 3) * 64 + lane;
+  const long long bo = (gofs >> 5) + (long long)brow(r) * ldb_s;
+  L.gs = wave < 4 ? p.as + (long long)arow(r) * lda_s + (t.kb0 >> 5)
+                  : (bsrc2(r) ? p.bs2 : p.bs) + bo + (t.kb0 >> 5);
+  L.gs2 = wave < 4 ? L.gs : (split ? p.bs2 : p.bs) + bo;
+}
+
+// Stage s of the load stream = step j of tile t: codes into ring slot s & 3, and on even steps the
+// scale dwords of steps j, j + 1 into scale slot (s >> 1) % 3 (tiles have an even number of steps,
+// so s and j have the same parity).
+__device__ __forceinline__ void pipe_issue(const PLoad& L, long long kb0, int j, int s, int ks, char* ring,
+                                           char* sring, int wave) {
+  char* st = ring + (s & 3) * PSTAGE;
+  const long long off = (long long)j * PK;
+  const bool second = kb0 + off >= ks;   // B columns of this stage come from the second source
+  if ((j & 1) == 0) {
+    const uint8_t* src = (second && wave >= 4) ? L.gs2 + ((kb0 + off - ks) >> 5) : L.gs + 2 * j;
+    __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(sring + ((s >> 1) % PNSC) * PSC + wave * 256), 4, 0,
+                                     0);
   }
-
-  char* ring = plds;
-  char* sring = plds + PNST * PSTAGE;
-  auto issue = [&](int s) {
-    char* st = ring + (s & 3) * PSTAGE;
-    const long long off = (long long)s * PK;
-    const bool second = kb0 + off >= ks;   // B columns of this stage come from the second source
-    if ((s & 1) == 0) {
-      const uint8_t* src = (second && wave >= 4) ? gs2 + ((kb0 + off - ks) >> 5) : gs + 2 * s;
-      __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(sring + ((s >> 1) % PNSC) * PSC + wave * 256), 4, 0,
-                                       0);
-    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(ga[j] + off), (lvoid_t*)(st + (2 * wave + j) * 1024), 16, 0, 0);
-      const uint8_t* bs = second ? gb2[j] + (kb0 + off - ks) : gb[j] + off;
-      __builtin_amdgcn_global_load_lds((gvoid_t*)bs, (lvoid_t*)(st + PB * PK + (2 * wave + j) * 1024), 16, 0, 0);
-    }
-  };
-
-  // LDS read offsets of this lane: A rows 128 wm + 32 i + li, B rows 64 wn + 32 j + li; chunks h, 2 + h.
-  const int sw = (li >> 2) & 3;
-  const uint32_t ring0 = lds_off(ring), sring0 = lds_off(sring);
-  const uint32_t oa0 = (uint32_t)((wm * 128 + li) * PK + 16 * (h ^ sw));
-  const uint32_t oa2 = (uint32_t)((wm * 128 + li) * PK + 16 * ((2 + h) ^ sw));
-  const uint32_t ob0 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * (h ^ sw));
-  const uint32_t ob2 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * ((2 + h) ^ sw));
-  const uint32_t osa = (uint32_t)((wm * 128 + li) * 4 + h);
-  const uint32_t osb = (uint32_t)(1024 + (wn * 64 + li) * 4 + h);
-
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  for (int s = 0; s < 3 && s < nk; ++s) issue(s);
-  for (int j = 0; j < nk; ++j) {
-    // Stage j complete for this wave: at most the loads of the (up to two) later stages in flight.
-    const int later = min(nk - 1 - j, 2);
-    if (later >= 2) wait_vm<8>();
-    else if (later == 1) wait_vm<4>();
-    else wait_vm<0>();
-    pbarrier();
-    if (j + 3 < nk) issue(j + 3);
-    PFrag f;
-    const uint32_t sb = ring0 + (uint32_t)((j & 3) * PSTAGE);
-    const uint32_t ss = sring0 + (uint32_t)(((j >> 1) % PNSC) * PSC + 2 * (j & 1));
-    read_step(f, sb + oa0, sb + oa2, sb + ob0, sb + ob2, ss + osa, ss + osb);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const i32x8_t fa = frag8(f.a[i][0], f.a[i][1]);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        acc[i][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag8(f.b[c][0], f.b[c][1]), fa, acc[i][c], 0, 0,
-                                                                    0, (int)f.sb[c], 0, (int)f.sa[i]);
-    }
+  for (int q = 0; q < 2; ++q) {
+    __builtin_amdgcn_global_load_lds((gvoid_t*)(L.ga[q] + off), (lvoid_t*)(st + (2 * wave + q) * 1024), 16, 0, 0);
+    const uint8_t* bs = second ? L.gb2[q] + (kb0 + off - ks) : L.gb[q] + off;
+    __builtin_amdgcn_global_load_lds((gvoid_t*)bs, (lvoid_t*)(st + PB * PK + (2 * wave + q) * 1024), 16, 0, 0);
   }
+}
 
+template <int EPI, bool RK>
+__device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& t, const f32x16_t (&acc)[4][2],
+                                              int wm, int wn, int li, int h) {
+  const int g = t.g, m0 = t.m0, m_end = t.m_end, nt = t.nt;
   // Epilogue: lane holds row li of each 32-row block, columns 8 (r / 4) + 4 h + (r % 4).
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -763,8 +730,139 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
   }
 }
 
+// Persistent: one workgroup per CU walks its list of tiles; the load stream runs across tile
+// boundaries, so the next tile's first stages are in flight during a tile's epilogue.  The tile
+// list: each XCD (workgroup b runs on XCD b % 8) takes one contiguous eighth of the tiles, dealt
+// round-robin to its workgroups.
 template <int EPI, bool RK>
-hipError_t launch_mx_pipe(const MxGemmArgs& a, int blocks, hipStream_t s) {
+__global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char plds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1, li = lane & 31, h = lane >> 5;
+  constexpr int OC = EPI == MX_EPI_SWIGLU ? 128 : PB;   // output columns per tile
+  const int NT = p.N / OC;
+  // Tiles to share out: ragged rows count the row tiles the groups really have (the launch size
+  // assumes the worst case; an even split of that would leave the XCDs at its end idle).
+  const int U = RK ? p.tiles : ufirst(p.tile_prefix[p.G]) * NT;
+
+  const int nb = gridDim.x, b = blockIdx.x;
+  int first, stride, last;   // this workgroup's tiles: first, first + stride, ... < last
+  if (nb < 8) {
+    first = b;
+    stride = nb;
+    last = U;
+  } else {
+    const int xcd = b & 7;
+    const int nwx = nb / 8 + (xcd < nb % 8 ? 1 : 0);
+    const int per = U / 8, rem = U % 8;
+    const int c0 = xcd * per + min(xcd, rem);
+    first = c0 + (b >> 3);
+    stride = nwx;
+    last = c0 + per + (xcd < rem ? 1 : 0);
+  }
+
+  const bool split = EPI != MX_EPI_SWIGLU && p.b2 != nullptr;
+  const int ks = split ? p.ksplit : 0x7fffffff;   // K columns from the second source start here
+  char* ring = plds;
+  char* sring = plds + PNST * PSTAGE;
+
+  // Producer: the next stage to load (tile position pl, step pj).
+  int pl = first, pj = 0;
+  bool pvalid = false;
+  PTile pt;
+  PLoad L;
+  auto pseek = [&]() {   // move to the first tile at or after pl with steps to load
+    pvalid = false;
+    while (pl < last) {
+      if (!pipe_tile<RK>(p, pl, NT, pt)) { pl = last; break; }
+      if (pt.nk > 0) {
+        pipe_sources<EPI, RK>(p, pt, split, wave, lane, L);
+        pvalid = true;
+        break;
+      }
+      pl += stride;
+    }
+  };
+  int issued = 0;   // stages issued so far
+  auto produce = [&]() {
+    if (!pvalid) return;
+    pipe_issue(L, pt.kb0, pj, issued, ks, ring, sring, wave);
+    ++issued;
+    if (++pj == pt.nk) {
+      pj = 0;
+      pl += stride;
+      pseek();
+    }
+  };
+  pseek();
+  for (int q = 0; q < 3; ++q) produce();
+
+  // LDS read offsets of this lane: A rows 128 wm + 32 i + li, B rows 64 wn + 32 j + li; chunks h, 2 + h.
+  const int sw = (li >> 2) & 3;
+  const uint32_t ring0 = lds_off(ring), sring0 = lds_off(sring);
+  const uint32_t oa0 = (uint32_t)((wm * 128 + li) * PK + 16 * (h ^ sw));
+  const uint32_t oa2 = (uint32_t)((wm * 128 + li) * PK + 16 * ((2 + h) ^ sw));
+  const uint32_t ob0 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * (h ^ sw));
+  const uint32_t ob2 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * ((2 + h) ^ sw));
+  const uint32_t osa = (uint32_t)((wm * 128 + li) * 4 + h);
+  const uint32_t osb = (uint32_t)(1024 + (wn * 64 + li) * 4 + h);
+
+  int c = 0;            // consumer: next stage to multiply
+  bool after_epi = false;
+  for (int Lt = first; Lt < last; Lt += stride) {
+    PTile t;
+    if (!pipe_tile<RK>(p, Lt, NT, t)) break;
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < t.nk; ++j, ++c) {
+      // Stage c complete for this wave.  After an epilogue its stores follow the later stages'
+      // loads in the counter, so wait for everything; otherwise at most the loads of the (up to two)
+      // later stages may still be in flight.
+      const int later = issued - 1 - c;
+      if (after_epi || later <= 0) wait_vm<0>();
+      else if (later == 1) wait_vm<4>();
+      else wait_vm<8>();
+      after_epi = false;
+      pbarrier();
+      produce();
+      PFrag f;
+      const uint32_t sb = ring0 + (uint32_t)((c & 3) * PSTAGE);
+      const uint32_t ss = sring0 + (uint32_t)(((c >> 1) % PNSC) * PSC + 2 * (c & 1));
+      read_step(f, sb + oa0, sb + oa2, sb + ob0, sb + ob2, ss + osa, ss + osb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x8_t fa = frag8(f.a[i][0], f.a[i][1]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(frag8(f.b[q][0], f.b[q][1]), fa, acc[i][q], 0,
+                                                                      0, 0, (int)f.sb[q], 0, (int)f.sa[i]);
+      }
+    }
+    pipe_epilogue<EPI, RK>(p, t, acc, wm, wn, li, h);
+    after_epi = true;
+  }
+}
+
+// Compute units of the current device (one persistent workgroup each).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int EPI, bool RK>
+hipError_t launch_mx_pipe(const MxGemmArgs& a, int tiles, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_pipe_kernel<EPI, RK>,
@@ -772,7 +870,10 @@ hipError_t launch_mx_pipe(const MxGemmArgs& a, int blocks, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((mx_gemm_pipe_kernel<EPI, RK>), dim3(blocks), dim3(512), P_LDS, s, a);
+  MxGemmArgs q = a;
+  q.tiles = tiles;
+  const int blocks = std::min(tiles, device_cus());
+  hipLaunchKernelGGL((mx_gemm_pipe_kernel<EPI, RK>), dim3(blocks), dim3(512), P_LDS, s, q);
   return hipGetLastError();
 }
 

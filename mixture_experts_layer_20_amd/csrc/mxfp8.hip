@@ -657,72 +657,106 @@ __device__ __forceinline__ void pipe_issue(const PLoad& L, long long kb0, int j,
   }
 }
 
+// Accumulator block exchange for wide stores.  After the transposed MFMA, lane l holds row l % 32 and,
+// for element v, column 8 (v / 4) + 4 (l / 32) + v % 4 of the 32x32 block: a store covers 32 rows
+// with 16 bytes each.  v_permlane32_swap of the 4-column pieces of each 16-column half gives lane l
+// 8 consecutive columns 16 H + 8 (l / 32) of its row; v_permlane16_swap of the two halves then
+// leaves x0 = row l % 16 and x1 = row 16 + l % 16, both at columns 16 ((l / 16) % 2) + 8 (l / 32):
+// each 16-byte store covers 16 rows with 64 contiguous bytes.
+__device__ __forceinline__ int xcol(int lane) { return 16 * ((lane >> 4) & 1) + 8 * (lane >> 5); }
+
+__device__ __forceinline__ void xchg_block(const f32x16_t& c, float (&x0)[8], float (&x1)[8]) {
+  float hv[2][8];
+#pragma unroll
+  for (int H = 0; H < 2; ++H)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[8 * H + e]), __float_as_uint(c[8 * H + 4 + e]),
+                                                      false, false);
+      hv[H][e] = __uint_as_float(r[0]);
+      hv[H][4 + e] = __uint_as_float(r[1]);
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(hv[0][e]), __float_as_uint(hv[1][e]), false, false);
+    x0[e] = __uint_as_float(r[0]);
+    x1[e] = __uint_as_float(r[1]);
+  }
+}
+
+__device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
+  u32x4_t w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = bf16pack(v[2 * e], v[2 * e + 1]);
+  return w;
+}
+__device__ __forceinline__ void unpack8(const u32x4_t& w, float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+
 template <int EPI, bool RK>
 __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& t, const f32x16_t (&acc)[4][2],
-                                              int wm, int wn, int li, int h) {
-  const int g = t.g, m0 = t.m0, m_end = t.m_end, nt = t.nt;
-  // Epilogue: lane holds row li of each 32-row block, columns 8 (r / 4) + 4 h + (r % 4).
+                                              int wm, int wn, int lane) {
+  const int cl = xcol(lane), rl = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = m0 + wm * 128 + i * 32 + li;
-    if (!RK && row >= m_end) continue;
+    const int rbase = t.m0 + wm * 128 + i * 32 + rl;   // + 16 for the second piece
+    if constexpr (EPI == MX_EPI_SWIGLU) {
+      float g[2][8], u[2][8];
+      xchg_block(acc[i][0], g[0], g[1]);
+      xchg_block(acc[i][1], u[0], u[1]);
+      const int col = t.nt * 128 + wn * 32 + cl;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (EPI == MX_EPI_SWIGLU) {
-        const int col = nt * 128 + wn * 32 + 8 * q + 4 * h;
-        float hv[4];
+      for (int pc = 0; pc < 2; ++pc) {
+        const int row = rbase + 16 * pc;
+        if (row >= t.m_end) continue;
+        float hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = g[pc][e] * sigmoid_f32(g[pc][e]) * u[pc][e];
         const long long o = (long long)row * p.N + col;
+        if (p.out0) *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(p.out0) + o) = pack8(g[pc]);
+        if (p.out1) *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(p.out1) + o) = pack8(u[pc]);
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(p.out2) + o) = pack8(hv);
+      }
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = acc[i][0][4 * q + r], bb = acc[i][1][4 * q + r];
-          hv[r] = a * sigmoid_f32(a) * bb;
-        }
-        if (p.out0)
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out0) + o) =
-              make_uint2(bf16pack(acc[i][0][4 * q], acc[i][0][4 * q + 1]),
-                         bf16pack(acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]));
-        if (p.out1)
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out1) + o) =
-              make_uint2(bf16pack(acc[i][1][4 * q], acc[i][1][4 * q + 1]),
-                         bf16pack(acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]));
-        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.out2) + o) =
-            make_uint2(bf16pack(hv[0], hv[1]), bf16pack(hv[2], hv[3]));
-      } else {
+      for (int c = 0; c < 2; ++c) {
+        float x[2][8];
+        xchg_block(acc[i][c], x[0], x[1]);
+        const int col = t.nt * PB + wn * 64 + c * 32 + cl;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int col = nt * PB + wn * 64 + c * 32 + 8 * q + 4 * h;
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][c][4 * q + r];
+        for (int pc = 0; pc < 2; ++pc) {
+          const int row = rbase + 16 * pc;
+          if (!RK && row >= t.m_end) continue;
           if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
             const long long o = (long long)row * p.N + col;
-            const uint2 av = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.aux0) + o);
-            const uint2 bv = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.aux1) + o);
-            const uint32_t aw[2] = {av.x, av.y}, bw[2] = {bv.x, bv.y};
-            float da[4], db[4];
+            float a[8], bb[8], da[8], db[8];
+            unpack8(*reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(p.aux0) + o), a);
+            unpack8(*reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(p.aux1) + o), bb);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float a = bf16_to_f32((bf16_t)(aw[r >> 1] >> (16 * (r & 1))));
-              const float bb = bf16_to_f32((bf16_t)(bw[r >> 1] >> (16 * (r & 1))));
-              const float sg = sigmoid_f32(a);
-              da[r] = v[r] * bb * sg * (1.0f + a * (1.0f - sg));
-              db[r] = v[r] * a * sg;
+            for (int e = 0; e < 8; ++e) {
+              const float sg = sigmoid_f32(a[e]);
+              da[e] = x[pc][e] * bb[e] * sg * (1.0f + a[e] * (1.0f - sg));
+              db[e] = x[pc][e] * a[e] * sg;
             }
             bf16_t* dab = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * (2 * p.N);
-            *reinterpret_cast<uint2*>(dab + col) = make_uint2(bf16pack(da[0], da[1]), bf16pack(da[2], da[3]));
-            *reinterpret_cast<uint2*>(dab + p.N + col) =
-                make_uint2(bf16pack(db[0], db[1]), bf16pack(db[2], db[3]));
+            *reinterpret_cast<u32x4_t*>(dab + col) = pack8(da);
+            *reinterpret_cast<u32x4_t*>(dab + p.N + col) = pack8(db);
           } else {
             bf16_t* dst;
             if constexpr (RK) {
               dst = row < p.split
-                        ? reinterpret_cast<bf16_t*>(p.out0) + ((long long)g * p.split + row) * p.N + col
+                        ? reinterpret_cast<bf16_t*>(p.out0) + ((long long)t.g * p.split + row) * p.N + col
                         : reinterpret_cast<bf16_t*>(p.out1) +
-                              ((long long)g * (p.M - p.split) + (row - p.split)) * p.N + col;
+                              ((long long)t.g * (p.M - p.split) + (row - p.split)) * p.N + col;
             } else {
               dst = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * p.N + col;
             }
-            *reinterpret_cast<uint2*>(dst) = make_uint2(bf16pack(v[0], v[1]), bf16pack(v[2], v[3]));
+            *reinterpret_cast<u32x4_t*>(dst) = pack8(x[pc]);
           }
         }
       }
@@ -843,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
                                                                       0, 0, (int)f.sb[q], 0, (int)f.sa[i]);
       }
     }
-    pipe_epilogue<EPI, RK>(p, t, acc, wm, wn, li, h);
+    pipe_epilogue<EPI, RK>(p, t, acc, wm, wn, lane);
     after_epi = true;
   }
 }

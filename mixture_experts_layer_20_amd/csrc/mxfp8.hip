@@ -486,9 +486,15 @@ constexpr int PB = 256;                 // tile rows / columns
 constexpr int PK = 64;                  // K step (bytes = elements)
 constexpr int PSTAGE = 2 * PB * PK;     // 32 KiB: A then B
 constexpr int PNST = 4;
-constexpr int PSC = 2048;               // scale slot: 256 A dwords, then 256 B dwords
-constexpr int PNSC = 3;
-constexpr int P_LDS = PNST * PSTAGE + PNSC * PSC;
+// Scale ring: each row's scale bytes arrive SW at a time (SW = 4: two K steps per dword; SW = 16: eight
+// K steps per 16-byte load, four times fewer scattered requests, when K and the group strides allow).
+// A slot holds 256 A rows, then 256 B rows, SW bytes each.
+template <int SW> struct ScaleRing {
+  static constexpr int STEPS = SW / 2;               // K steps per load
+  static constexpr int SLOT = 2 * PB * SW;
+  static constexpr int SLOTS = SW == 4 ? 3 : 2;      // a slot is reloaded only after its last read
+  static constexpr int LDS = PNST * PSTAGE + SLOTS * SLOT;
+};
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -513,6 +519,7 @@ struct PFrag {
   uint32_t sa[4], sb[2];
 };
 
+template <int SW>
 __device__ __forceinline__ void read_step(PFrag& f, uint32_t a0, uint32_t a2, uint32_t b0, uint32_t b2, uint32_t sa,
                                           uint32_t sb) {
   asm volatile(
@@ -529,16 +536,16 @@ __device__ __forceinline__ void read_step(PFrag& f, uint32_t a0, uint32_t a2, ui
       "ds_read_b128 %10, %20 offset:2048\n\t"
       "ds_read_b128 %11, %21 offset:2048\n\t"
       "ds_read_u8 %12, %22\n\t"
-      "ds_read_u8 %13, %22 offset:128\n\t"
-      "ds_read_u8 %14, %22 offset:256\n\t"
-      "ds_read_u8 %15, %22 offset:384\n\t"
+      "ds_read_u8 %13, %22 offset:%24\n\t"
+      "ds_read_u8 %14, %22 offset:%25\n\t"
+      "ds_read_u8 %15, %22 offset:%26\n\t"
       "ds_read_u8 %16, %23\n\t"
-      "ds_read_u8 %17, %23 offset:128\n\t"
+      "ds_read_u8 %17, %23 offset:%24\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[1][0]), "=&v"(f.a[1][1]), "=&v"(f.a[2][0]), "=&v"(f.a[2][1]),
         "=&v"(f.a[3][0]), "=&v"(f.a[3][1]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]), "=&v"(f.b[1][0]), "=&v"(f.b[1][1]),
         "=&v"(f.sa[0]), "=&v"(f.sa[1]), "=&v"(f.sa[2]), "=&v"(f.sa[3]), "=&v"(f.sb[0]), "=&v"(f.sb[1])
-      : "v"(a0), "v"(a2), "v"(b0), "v"(b2), "v"(sa), "v"(sb)
+      : "v"(a0), "v"(a2), "v"(b0), "v"(b2), "v"(sa), "v"(sb), "i"(32 * SW), "i"(64 * SW), "i"(96 * SW)
       : "memory");
 }
 
@@ -636,18 +643,21 @@ __device__ __forceinline__ void pipe_sources(const MxGemmArgs& p, const PTile& t
   L.gs2 = wave < 4 ? L.gs : (split ? p.bs2 : p.bs) + bo;
 }
 
-// Stage s of the load stream = step j of tile t: codes into ring slot s & 3, and on even steps the
-// scale dwords of steps j, j + 1 into scale slot (s >> 1) % 3 (tiles have an even number of steps,
-// so s and j have the same parity).
+// Stage s of the load stream = step j of tile t: codes into ring slot s & 3, and every STEPS steps the
+// scale bytes of the next STEPS steps into scale slot (s / STEPS) % SLOTS (a tile's step count is a
+// multiple of STEPS, so s and j agree modulo STEPS).
+template <int SW>
 __device__ __forceinline__ void pipe_issue(const PLoad& L, long long kb0, int j, int s, int ks, char* ring,
                                            char* sring, int wave) {
+  using SR = ScaleRing<SW>;
   char* st = ring + (s & 3) * PSTAGE;
   const long long off = (long long)j * PK;
   const bool second = kb0 + off >= ks;   // B columns of this stage come from the second source
-  if ((j & 1) == 0) {
+  if (j % SR::STEPS == 0) {
     const uint8_t* src = (second && wave >= 4) ? L.gs2 + ((kb0 + off - ks) >> 5) : L.gs + 2 * j;
-    __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(sring + ((s >> 1) % PNSC) * PSC + wave * 256), 4, 0,
-                                     0);
+    lvoid_t* dst = (lvoid_t*)(sring + ((s / SR::STEPS) % SR::SLOTS) * SR::SLOT + wave * 64 * SW);
+    if constexpr (SW == 16) __builtin_amdgcn_global_load_lds((gvoid_t*)src, dst, 16, 0, 0);
+    else __builtin_amdgcn_global_load_lds((gvoid_t*)src, dst, 4, 0, 0);
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -768,8 +778,9 @@ __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& 
 // boundaries, so the next tile's first stages are in flight during a tile's epilogue.  The tile
 // list: each XCD (workgroup b runs on XCD b % 8) takes one contiguous eighth of the tiles, dealt
 // round-robin to its workgroups.
-template <int EPI, bool RK>
+template <int EPI, bool RK, int SW>
 __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
+  using SR = ScaleRing<SW>;
   extern __shared__ __attribute__((aligned(16))) char plds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1, li = lane & 31, h = lane >> 5;
@@ -820,7 +831,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
   int issued = 0;   // stages issued so far
   auto produce = [&]() {
     if (!pvalid) return;
-    pipe_issue(L, pt.kb0, pj, issued, ks, ring, sring, wave);
+    pipe_issue<SW>(L, pt.kb0, pj, issued, ks, ring, sring, wave);
     ++issued;
     if (++pj == pt.nk) {
       pj = 0;
@@ -838,8 +849,8 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
   const uint32_t oa2 = (uint32_t)((wm * 128 + li) * PK + 16 * ((2 + h) ^ sw));
   const uint32_t ob0 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * (h ^ sw));
   const uint32_t ob2 = (uint32_t)(PB * PK + (wn * 64 + li) * PK + 16 * ((2 + h) ^ sw));
-  const uint32_t osa = (uint32_t)((wm * 128 + li) * 4 + h);
-  const uint32_t osb = (uint32_t)(1024 + (wn * 64 + li) * 4 + h);
+  const uint32_t osa = (uint32_t)((wm * 128 + li) * SW + h);
+  const uint32_t osb = (uint32_t)(PB * SW + (wn * 64 + li) * SW + h);
 
   int c = 0;            // consumer: next stage to multiply
   bool after_epi = false;
@@ -866,8 +877,8 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
       produce();
       PFrag f;
       const uint32_t sb = ring0 + (uint32_t)((c & 3) * PSTAGE);
-      const uint32_t ss = sring0 + (uint32_t)(((c >> 1) % PNSC) * PSC + 2 * (c & 1));
-      read_step(f, sb + oa0, sb + oa2, sb + ob0, sb + ob2, ss + osa, ss + osb);
+      const uint32_t ss = sring0 + (uint32_t)(((c / SR::STEPS) % SR::SLOTS) * SR::SLOT + 2 * (c % SR::STEPS));
+      read_step<SW>(f, sb + oa0, sb + oa2, sb + ob0, sb + ob2, ss + osa, ss + osb);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const i32x8_t fa = frag8(f.a[i][0], f.a[i][1]);
@@ -895,20 +906,34 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int EPI, bool RK>
-hipError_t launch_mx_pipe(const MxGemmArgs& a, int tiles, hipStream_t s) {
+template <int EPI, bool RK, int SW>
+hipError_t launch_mx_pipe_sw(const MxGemmArgs& a, int tiles, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_pipe_kernel<EPI, RK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, P_LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_pipe_kernel<EPI, RK, SW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, ScaleRing<SW>::LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
   MxGemmArgs q = a;
   q.tiles = tiles;
   const int blocks = std::min(tiles, device_cus());
-  hipLaunchKernelGGL((mx_gemm_pipe_kernel<EPI, RK>), dim3(blocks), dim3(512), P_LDS, s, q);
+  hipLaunchKernelGGL((mx_gemm_pipe_kernel<EPI, RK, SW>), dim3(blocks), dim3(512), ScaleRing<SW>::LDS, s, q);
   return hipGetLastError();
+}
+
+// 16-byte scale loads need every row's scale run, group offset and K split on 16-byte boundaries of
+// the scale arrays (K, row strides, group stride and split multiples of 512 elements), and no K offset.
+inline bool wide_scales(const MxGemmArgs& a, bool ragged_k) {
+  auto al = [](const void* ptr) { return ptr == nullptr || ((uintptr_t)ptr & 15) == 0; };
+  return !ragged_k && a.K % 512 == 0 && a.lda % 512 == 0 && a.ldb % 512 == 0 && a.b_gstride % 512 == 0 &&
+         (a.ksplit == 0 || a.ksplit % 512 == 0) && al(a.as) && al(a.bs) && al(a.bs2);
+}
+
+template <int EPI, bool RK>
+hipError_t launch_mx_pipe(const MxGemmArgs& a, int tiles, hipStream_t s) {
+  if (wide_scales(a, RK)) return launch_mx_pipe_sw<EPI, RK, 16>(a, tiles, s);
+  return launch_mx_pipe_sw<EPI, RK, 4>(a, tiles, s);
 }
 
 template <int EPI, bool RK>

@@ -359,10 +359,15 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
  *   rows m < split go to out0 [G, split, N], rows m >= split to out1 [G, M - split, N] (bf16);
  *   a group with no rows gets exact zeros.  kbase is device data the call cannot check: it must be
  *   non-decreasing with kbase[G] <= min(lda, ldb) (moe_mx_quantize_cols writes such a kbase).
- * M and N must be multiples of 128, lda and ldb multiples of 128, kbase multiples of 128. */
+ * M and N must be multiples of 128, lda and ldb multiples of 128, kbase multiples of 128.
+ * ws: moe_mx_gemm_k_workspace_size(G, M, N) bytes (NULL allowed when that is 0).  When the product
+ * has fewer 256x256 output tiles than the GPU has compute units, each group's K range is split and
+ * the fp32 partial sums are added in split order before the single rounding to bf16 (deterministic). */
+size_t moe_mx_gemm_k_workspace_size(int32_t G, int64_t M, int64_t N);
 moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int64_t lda, const uint8_t* b_codes,
                            const uint8_t* b_scales, int64_t ldb, const int32_t* kbase, int32_t G, int64_t M,
-                           int64_t N, int64_t split, void* out0, void* out1, moe_stream_t stream);
+                           int64_t N, int64_t split, void* out0, void* out1, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
 /* Utilities                                                                                   */

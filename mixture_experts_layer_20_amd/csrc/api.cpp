@@ -588,6 +588,7 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
   a.b2 = b2_codes;
   a.bs2 = b2_scales;
   a.ksplit = (epilogue != MOE_MX_EPI_SWIGLU && b2_codes) ? (int)b2_k : 0;
+  a.kparts = 1;
   a.offsets = offsets;
   a.tile_prefix = reinterpret_cast<int32_t*>(ws);
   a.G = G;
@@ -602,9 +603,15 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
   return hip_check(moe::launch_mx_gemm(epilogue, false, a, S(stream)), "MXFP8 grouped GEMM (rows)");
 }
 
+size_t moe_mx_gemm_k_workspace_size(int32_t G, int64_t M, int64_t N) {
+  if (G <= 0 || M <= 0 || N <= 0 || M > kMaxInt || N > kMaxInt || G > 1024) return 0;
+  return moe::mx_k_workspace_bytes(G, (int)M, (int)N);
+}
+
 moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int64_t lda, const uint8_t* b_codes,
                            const uint8_t* b_scales, int64_t ldb, const int32_t* kbase, int32_t G, int64_t M,
-                           int64_t N, int64_t split, void* out0, void* out1, moe_stream_t stream) {
+                           int64_t N, int64_t split, void* out0, void* out1, void* ws, size_t ws_bytes,
+                           moe_stream_t stream) {
   g_err.clear();
   CHECK(G > 0 && G <= 1024, MOE_ERR_INVALID_VALUE, "G must be in [1, 1024] (got %d)", G);
   CHECK(M > 0 && N > 0 && split >= 0 && split <= M, MOE_ERR_INVALID_VALUE, "M, N must be > 0, split in [0, M]");
@@ -616,6 +623,9 @@ moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int6
   CHECK((int64_t)G * (M / 128) * (N / 128) < kMaxInt, MOE_ERR_UNSUPPORTED, "grid too large");
   CHECK(a_codes && a_scales && b_codes && b_scales && kbase, MOE_ERR_INVALID_VALUE, "an operand pointer is NULL");
   CHECK((split == 0 || out0) && (split == M || out1), MOE_ERR_INVALID_VALUE, "out0/out1 is NULL");
+  const size_t need = moe::mx_k_workspace_bytes(G, (int)M, (int)N);
+  CHECK(need == 0 || (ws && ws_bytes >= need), MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+        ws ? ws_bytes : (size_t)0);
   moe::MxGemmArgs a{};
   a.a = a_codes;
   a.as = a_scales;
@@ -630,6 +640,8 @@ moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int6
   a.out0 = out0;
   a.out1 = out1;
   a.split = (int)split;
+  a.kparts = moe::mx_k_parts(G, (int)M, (int)N);
+  a.partial = reinterpret_cast<float*>(ws);
   return hip_check(moe::launch_mx_gemm(MOE_MX_EPI_STORE, true, a, S(stream)), "MXFP8 grouped GEMM (K)");
 }
 

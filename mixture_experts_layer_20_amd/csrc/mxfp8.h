@@ -41,7 +41,12 @@ struct MxGemmArgs {
   const void* aux1;
   int split;              // ragged K: output rows [0, split) -> out0, [split, M) -> out1
   int tiles;              // tile indices of the launch (set by the launcher)
+  int kparts;             // ragged K: splits of each group's K range (fp32 partials, then a reduction)
+  float* partial;         // [kparts, G, M, N] fp32 when kparts > 1
 };
 hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream_t s);
+// Ragged K: the K split the launcher uses for G groups of M x N outputs, and its workspace bytes.
+int mx_k_parts(int G, int M, int N);
+size_t mx_k_workspace_bytes(int G, int M, int N);
 
 }  // namespace moe

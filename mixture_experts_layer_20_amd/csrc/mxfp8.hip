@@ -561,7 +561,7 @@ __device__ __forceinline__ i32x8_t frag8(const u32x4_t& lo, const u32x4_t& hi) {
 
 // One output tile of the pipelined kernel.
 struct PTile {
-  int g, m0, m_end, nt, nk;
+  int g, m0, m_end, nt, nk, part;
   long long kb0;
 };
 
@@ -588,15 +588,23 @@ __device__ __forceinline__ bool pipe_tile(const MxGemmArgs& p, int Lt, int NT, P
     t.kb0 = 0;
     t.nk = p.K / PK;
   } else {
-    const int MT = p.M / PB;
-    const int r = Lt / NT;
-    if (r >= p.G * MT) return false;
-    t.g = r / MT;
-    t.m0 = (r - t.g * MT) * PB;
+    // Tile order: column tiles fastest, then row tiles, then K parts, then groups.  Part q of a
+    // group covers [q c, (q + 1) c) of its K range, c = its length / kparts rounded up to 128.
+    const int MT = p.M / PB, S = p.kparts;
+    int r = Lt / NT;
+    if (r >= p.G * S * MT) return false;
+    const int mt = r % MT;
+    r /= MT;
+    t.part = r % S;
+    t.g = r / S;
+    t.m0 = mt * PB;
     t.m_end = p.M;
     const int k0 = ufirst(p.offsets[t.g]), k1 = ufirst(p.offsets[t.g + 1]);
-    t.kb0 = k0;
-    t.nk = (k1 - k0) / PK;
+    const int len = k1 - k0;
+    const int chunk = ((len + S - 1) / S + 127) / 128 * 128;
+    const int a = min(len, t.part * chunk), e = min(len, (t.part + 1) * chunk);
+    t.kb0 = k0 + a;
+    t.nk = (e - a) / PK;
   }
   return true;
 }
@@ -757,6 +765,20 @@ __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& 
             *reinterpret_cast<u32x4_t*>(dab + col) = pack8(da);
             *reinterpret_cast<u32x4_t*>(dab + p.N + col) = pack8(db);
           } else {
+            if constexpr (RK) {
+              if (p.kparts > 1) {   // fp32 partial of K part t.part
+                float* dst = p.partial + (((long long)t.part * p.G + t.g) * p.M + row) * p.N + col;
+                u32x4_t w0, w1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  w0[e] = __float_as_uint(x[pc][e]);
+                  w1[e] = __float_as_uint(x[pc][4 + e]);
+                }
+                reinterpret_cast<u32x4_t*>(dst)[0] = w0;
+                reinterpret_cast<u32x4_t*>(dst)[1] = w1;
+                continue;
+              }
+            }
             bf16_t* dst;
             if constexpr (RK) {
               dst = row < p.split
@@ -936,6 +958,34 @@ hipError_t launch_mx_pipe(const MxGemmArgs& a, int tiles, hipStream_t s) {
   return launch_mx_pipe_sw<EPI, RK, 4>(a, tiles, s);
 }
 
+// Sum of the K parts of a weight-gradient product, in part order, rounded once to bf16; rows
+// [0, split) of each group to out0, the others to out1.  8 consecutive elements per thread.
+__global__ __launch_bounds__(256) void mx_k_reduce_kernel(const float* __restrict__ partial, int S, int G, int M,
+                                                          int N, int split, bf16_t* __restrict__ out0,
+                                                          bf16_t* __restrict__ out1) {
+  const long long per = (long long)M * N;
+  const long long total = (long long)G * per / 8;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const long long e0 = i * 8;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int q = 0; q < S; ++q) {
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(partial + (long long)q * G * per + e0);
+      const u32x4_t a = src[0], b = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] += __uint_as_float(a[e]);
+        v[4 + e] += __uint_as_float(b[e]);
+      }
+    }
+    const long long g = e0 / per, rem = e0 - g * per;
+    const int row = (int)(rem / N), col = (int)(rem - (long long)row * N);
+    bf16_t* dst = row < split ? out0 + ((long long)g * split + row) * N + col
+                              : out1 + ((long long)g * (M - split) + (row - split)) * N + col;
+    *reinterpret_cast<u32x4_t*>(dst) = pack8(v);
+  }
+}
+
 template <int EPI, bool RK>
 hipError_t launch_mx(const MxGemmArgs& a, int blocks, hipStream_t s) {
   hipLaunchKernelGGL((mx_gemm_kernel<EPI, RK>), dim3(blocks), dim3(256), 0, s, a);
@@ -966,6 +1016,19 @@ hipError_t launch_mx_quant_cols(const void* x, long long R, int N, long long ldx
   return hipGetLastError();
 }
 
+int mx_k_parts(int G, int M, int N) {
+  if (M % PB != 0 || N % PB != 0) return 1;   // the 128x128 kernel does not split
+  const long long tiles = (long long)G * (M / PB) * (N / PB);
+  const int cus = device_cus();
+  if (tiles >= cus) return 1;
+  return (int)std::min<long long>(16, (cus + tiles - 1) / tiles);
+}
+
+size_t mx_k_workspace_bytes(int G, int M, int N) {
+  const int S = mx_k_parts(G, M, N);
+  return S > 1 ? (size_t)S * G * M * N * sizeof(float) : 0;
+}
+
 hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream_t s) {
   // The pipelined 256x256 kernel covers output widths that are multiples of its tile (128 columns
   // for SwiGLU) and, for weight gradients, output heights that are multiples of 256.
@@ -986,7 +1049,16 @@ hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream
   if (tiles == 0) return hipSuccess;
   const int blocks = (int)tiles;
   if (pipe) {
-    if (ragged_k) return launch_mx_pipe<MX_EPI_STORE, true>(a, blocks, s);
+    if (ragged_k) {
+      if (a.kparts <= 1) return launch_mx_pipe<MX_EPI_STORE, true>(a, blocks, s);
+      hipError_t e = launch_mx_pipe<MX_EPI_STORE, true>(a, blocks * a.kparts, s);
+      if (e != hipSuccess) return e;
+      const long long n8 = (long long)a.G * a.M * a.N / 8;
+      const int rb = (int)std::min<long long>((n8 + 255) / 256, 4096);
+      hipLaunchKernelGGL(mx_k_reduce_kernel, dim3(rb), dim3(256), 0, s, a.partial, a.kparts, a.G, a.M, a.N, a.split,
+                         reinterpret_cast<bf16_t*>(a.out0), reinterpret_cast<bf16_t*>(a.out1));
+      return hipGetLastError();
+    }
     switch (epi) {
       case MX_EPI_SWIGLU: return launch_mx_pipe<MX_EPI_SWIGLU, false>(a, blocks, s);
       case MX_EPI_SWIGLU_BWD: return launch_mx_pipe<MX_EPI_SWIGLU_BWD, false>(a, blocks, s);

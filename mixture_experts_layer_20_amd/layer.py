@@ -121,6 +121,9 @@ class MxSet:
             self.abc, self.xc = q(2 * f, self.ld), q(d, self.ld)
             self.kbase = torch.empty(G + 1, dtype=torch.int32, device=device)
             self.kbase_w = torch.empty(G + 1, dtype=torch.int32, device=device)
+            # weight gradients: split-K partials when the product has few output tiles
+            nws = max(L.moe_mx_gemm_k_workspace_size(G, d, f), L.moe_mx_gemm_k_workspace_size(G, 2 * f, d))
+            self.ws_k = u8(max(nws, 256))
 
 
 class MoELayer:
@@ -369,11 +372,12 @@ class MoELayer:
             qc("q_dy_cols", t["dy"], d, m.dyc)
             qc("q_h_cols", t["h"], f, m.hc)
             self._stage(self._pfx(i, "down_wgrad"), L.moe_mx_gemm_k, m.dyc[0], m.dyc[1], m.ld, m.hc[0], m.hc[1],
-                        m.ld, m.kbase, G, d, f, d, t["dw2"], None)
+                        m.ld, m.kbase, G, d, f, d, t["dw2"], None, m.ws_k, m.ws_k.numel())
             qc("q_dab_cols", t["dab"], 2 * f, m.abc)
             qc("q_x_cols", t["x"], d, m.xc)
             self._stage(self._pfx(i, "gate_up_wgrad"), L.moe_mx_gemm_k, m.abc[0], m.abc[1], m.ld, m.xc[0],
-                        m.xc[1], m.ld, m.kbase, G, 2 * f, d, f, t["dw1"], t["dw3"])
+                        m.xc[1], m.ld, m.kbase, G, 2 * f, d, f, t["dw1"], t["dw3"], m.ws_k,
+                        m.ws_k.numel())
 
     def step(self):
         """One pass of the whole path: forward, then backward when the workload has one."""

@@ -85,7 +85,8 @@ _SIGS = {
     "moe_mx_gemm_workspace_size": (_SZ, [_I32]),
     "moe_mx_gemm_rows": (_I32, [_P, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _I32, _P, _P,
                                 _P, _P, _P, _P, _SZ, _P]),
-    "moe_mx_gemm_k": (_I32, [_P, _P, _I64, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _P, _P, _P]),
+    "moe_mx_gemm_k_workspace_size": (_SZ, [_I32, _I64, _I64]),
+    "moe_mx_gemm_k": (_I32, [_P, _P, _I64, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "moe_status_string": (_c.c_char_p, [_I32]),
     "moe_last_error": (_c.c_char_p, []),
     "moe_version": (_c.c_char_p, []),
@@ -321,7 +322,11 @@ def moe_mx_gemm_rows(a_codes, a_scales, b_codes, b_scales, b_row_stride, b_group
           _ptr(out1), _ptr(out2), _ptr(aux0), _ptr(aux1), _ptr(ws), ws_bytes, _stream(stream))
 
 
-def moe_mx_gemm_k(a_codes, a_scales, lda, b_codes, b_scales, ldb, kbase, G, M, N, split, out0, out1,
+def moe_mx_gemm_k_workspace_size(G, M, N) -> int:
+    return lib().moe_mx_gemm_k_workspace_size(G, M, N)
+
+
+def moe_mx_gemm_k(a_codes, a_scales, lda, b_codes, b_scales, ldb, kbase, G, M, N, split, out0, out1, ws, ws_bytes,
                   stream=None):
     _call("moe_mx_gemm_k", _ptr(a_codes), _ptr(a_scales), lda, _ptr(b_codes), _ptr(b_scales), ldb, _ptr(kbase),
-          G, M, N, split, _ptr(out0), _ptr(out1), _stream(stream))
+          G, M, N, split, _ptr(out0), _ptr(out1), _ptr(ws), ws_bytes, _stream(stream))

@@ -158,7 +158,12 @@ def test_mxfp8_argument_checks(lib):
     args[7] = None             # codes without scales
     _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
     gk = L.moe_mx_gemm_k
-    _expect(L.MOE_ERR_UNSUPPORTED, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 192, 256, 0, None, FAKE)
-    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 256, 256, 300, FAKE, FAKE)
-    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 500, FAKE, FAKE, 512, FAKE, 8, 256, 256, 0, None, FAKE)
-    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 256, 256, 128, None, FAKE)
+    W = 1 << 30   # a large enough workspace size
+    _expect(L.MOE_ERR_UNSUPPORTED, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 192, 256, 0, None, FAKE, FAKE, W)
+    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 256, 256, 300, FAKE, FAKE, FAKE, W)
+    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 500, FAKE, FAKE, 512, FAKE, 8, 256, 256, 0, None, FAKE, FAKE, W)
+    _expect(L.MOE_ERR_INVALID_VALUE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 8, 256, 256, 128, None, FAKE, FAKE, W)
+    need = L.moe_mx_gemm_k_workspace_size(1, 256, 256)      # one tile: its K range is split
+    assert need > 0 and L.moe_mx_gemm_k_workspace_size(1024, 2048, 2048) == 0
+    _expect(L.MOE_ERR_WORKSPACE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 1, 256, 256, 256, FAKE, None, FAKE,
+            need - 1)

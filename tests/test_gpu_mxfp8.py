@@ -211,9 +211,11 @@ def test_gemm_rows_swiglu_and_backward():
 
 @pytest.mark.parametrize("R,Mw,N,G,split", [(1000, 256, 128, 7, 128), (300, 128, 256, 3, 128),
                                             (4096, 384, 128, 2, 384), (2000, 512, 256, 9, 256),
-                                            (700, 256, 512, 4, 0)])
+                                            (700, 256, 512, 4, 0), (8192, 256, 256, 1, 256)])
 def test_gemm_k(R, Mw, N, G, split):
-    log(f"mx gemm k R={R} Mw={Mw} N={N} G={G} split={split}")
+    """Weight-gradient form.  With few 256x256 output tiles the K ranges are split (fp32 partials
+    summed in split order): the last three cases, including parts with no rows."""
+    log(f"mx gemm k R={R} Mw={Mw} N={N} G={G} split={split} parts={L.moe_mx_gemm_k_workspace_size(G, Mw, N) > 0}")
     rng = np.random.default_rng(R + Mw + N)
     a = as_dtype_values(rng.standard_normal((R, Mw)), "bf16")     # e.g. dY rows of the experts' tokens
     b = as_dtype_values(rng.standard_normal((R, N)), "bf16")      # e.g. H rows
@@ -230,7 +232,9 @@ def test_gemm_k(R, Mw, N, G, split):
     L.moe_mx_quantize_cols(dev_tensor(b, "bf16"), R, N, N, i32(offs), G, 0, kpad, bc, bs, ld, kb2)
     out0 = torch.full((G, split, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     out1 = torch.full((G, Mw - split, N), float("nan"), dtype=torch.bfloat16, device=DEV) if split < Mw else None
-    L.moe_mx_gemm_k(ac, as_, ld, bc, bs, ld, kb, G, Mw, N, split, out0, out1)
+    nws = L.moe_mx_gemm_k_workspace_size(G, Mw, N)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+    L.moe_mx_gemm_k(ac, as_, ld, bc, bs, ld, kb, G, Mw, N, split, out0, out1, ws, nws)
     torch.cuda.synchronize()
     qa = MX.mx_quantize_grouped_cols(a, offs, kpad)
     qb = MX.mx_quantize_grouped_cols(b, offs, kpad)

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(1024) void mx_prefix_kernel(const int32_t* __restri
 
 // ---- Column quantization: 128 padded rows of one group x 512 columns per workgroup ----------
 // Each thread quantizes two columns over four 32-row blocks and writes each column's 128 codes as
-// one 128-byte run and its four scale bytes as one dword.  Groups are padded to a multiple of 128
+// one 128-byte run and its four scale bytes as one dword.  A thread only reads and writes its own
+// LDS rows, so no barrier is needed.  Groups are padded to a multiple of 128
 // rows, so a 128-row chunk never spans two groups.
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __restrict__ x, long long R, int N,
                                                             long long ldx, const int32_t* __restrict__ offsets,
@@ -157,16 +158,18 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __rest
     r0 = glo + (k0 - kbase[lo]);
     rhi = ghi;
   }
-  if (n >= N) return;
-  u32x4_t out[2][8];
+  // Codes of this thread's two columns, block by block, staged in LDS ([column][128 codes]) so that
+  // only one block's loads are live at a time; each column's 128 codes then go out as one run.
+  __shared__ __attribute__((aligned(16))) uint8_t stage[512][128];
+  const int lc = threadIdx.x * 2;
+  const bool active = n < N;
   uint32_t sc[2] = {0u, 0u};
-#pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
     uint32_t v[32];
     const long long rb = r0 + 32 * blk;
 #pragma unroll
     for (int j = 0; j < 32; ++j)
-      v[j] = rb + j < rhi ? *reinterpret_cast<const uint32_t*>(x + (rb + j) * ldx + n) : 0u;
+      v[j] = active && rb + j < rhi ? *reinterpret_cast<const uint32_t*>(x + (rb + j) * ldx + n) : 0u;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       uint32_t amax = 0;
@@ -174,6 +177,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __rest
       for (int j = 0; j < 32; ++j) amax = max(amax, ((v[j] >> (16 * c)) & 0x7fffu) << 16);
       const int e = mx_shared_exp(amax);
       sc[c] |= (uint32_t)(e + 127) << (8 * blk);
+      u32x4_t w[2];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         // column c of rows 4q .. 4q+3 of the block, as bf16 bit patterns in the upper halves
@@ -181,15 +185,20 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __rest
         const uint32_t x1 = c ? (v[4 * q + 1] & 0xffff0000u) : (v[4 * q + 1] << 16);
         const uint32_t x2 = c ? (v[4 * q + 2] & 0xffff0000u) : (v[4 * q + 2] << 16);
         const uint32_t x3 = c ? (v[4 * q + 3] & 0xffff0000u) : (v[4 * q + 3] << 16);
-        out[c][2 * blk + (q >> 2)][q & 3] = e4m3_pack2<true>(e4m3_pack2<false>(0u, x0, x1, e), x2, x3, e);
+        w[q >> 2][q & 3] = e4m3_pack2<true>(e4m3_pack2<false>(0u, x0, x1, e), x2, x3, e);
       }
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(&stage[lc + c][32 * blk]);
+      dst[0] = w[0];
+      dst[1] = w[1];
     }
   }
+  if (!active) return;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(&stage[lc + c][0]);
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + (long long)(n + c) * ldc + k0);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dst[q] = out[c][q];
+    for (int q = 0; q < 8; ++q) dst[q] = src[q];
     *reinterpret_cast<uint32_t*>(scales + (long long)(n + c) * (ldc >> 5) + (k0 >> 5)) = sc[c];
   }
 }

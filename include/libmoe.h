@@ -360,7 +360,8 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
  *   a group with no rows gets exact zeros.  kbase is device data the call cannot check: it must be
  *   non-decreasing with kbase[G] <= min(lda, ldb) (moe_mx_quantize_cols writes such a kbase).
  * M and N must be multiples of 128, lda and ldb multiples of 128, kbase multiples of 128.
- * ws: moe_mx_gemm_k_workspace_size(G, M, N) bytes (NULL allowed when that is 0).  When the product
+ * ws: moe_mx_gemm_k_workspace_size(G, M, N) bytes (NULL allowed when that is 0; the size depends
+ * on the compute units of the current device, so query it with the same device current).  When the product
  * has fewer 256x256 output tiles than the GPU has compute units, each group's K range is split and
  * the fp32 partial sums are added in split order before the single rounding to bf16 (deterministic). */
 size_t moe_mx_gemm_k_workspace_size(int32_t G, int64_t M, int64_t N);

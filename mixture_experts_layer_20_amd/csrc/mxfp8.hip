@@ -939,12 +939,16 @@ int device_cus() {
 
 template <int EPI, bool RK, int SW>
 hipError_t launch_mx_pipe_sw(const MxGemmArgs& a, int tiles, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
+  // The dynamic LDS limit above 64 KiB is a per-device attribute of the kernel: set it once per
+  // device (bit d of the mask; devices past 63 set it on every launch).
+  static unsigned long long attr_set = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 64 || !((attr_set >> dev) & 1ull)) {
     hipError_t e = hipFuncSetAttribute((const void*)mx_gemm_pipe_kernel<EPI, RK, SW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, ScaleRing<SW>::LDS);
     if (e != hipSuccess) return e;
-    attr = true;
+    if (dev < 64) attr_set |= 1ull << dev;
   }
   MxGemmArgs q = a;
   q.tiles = tiles;

@@ -344,14 +344,18 @@ typedef enum {
  *   k >= b2_k of B come from it, at column k - b2_k (b2_k a multiple of 128 in (0, K)): the gate/up
  *   data gradient contracts [dA | dB] with W1 and W3 stacked along K;
  *   offsets [G+1] int32 device (clamped to [0, M]; rows outside every group are not written).
+ *   q_codes / q_scales (NULL or given together; SwiGLU epilogues only): also write the MXFP8 of the
+ *   bf16 rows just stored, along the rows (as moe_mx_quantize_rows would): H [M, N] for
+ *   MOE_MX_EPI_SWIGLU, [dA | dB] [M, 2N] for MOE_MX_EPI_SWIGLU_BWD; codes [M, N or 2N], scales /32.
  * K must be a multiple of 128, N of 128 (64 for MOE_MX_EPI_SWIGLU), both strides multiples of 128.
  * ws: moe_mx_gemm_workspace_size(G) bytes. */
 size_t moe_mx_gemm_workspace_size(int32_t G);
 moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                               const uint8_t* b_scales, int64_t b_row_stride, int64_t b_group_stride,
-                              const uint8_t* b2_codes, const uint8_t* b2_scales, int64_t b2_k, const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
-                              void* out0, void* out1, void* out2, const void* aux0, const void* aux1, void* ws,
-                              size_t ws_bytes, moe_stream_t stream);
+                              const uint8_t* b2_codes, const uint8_t* b2_scales, int64_t b2_k, const int32_t* offsets,
+                              int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue, void* out0, void* out1,
+                              void* out2, const void* aux0, const void* aux1, uint8_t* q_codes, uint8_t* q_scales,
+                              void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Grouped product over ragged CONTRACTION ranges (weight gradients):
  *   C_g[m, n] = sum_{k in [kbase[g], kbase[g+1])} A[m, k] B[n, k]

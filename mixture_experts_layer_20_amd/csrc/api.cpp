@@ -545,9 +545,10 @@ size_t moe_mx_gemm_workspace_size(int32_t G) {
 
 moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                               const uint8_t* b_scales, int64_t b_row_stride, int64_t b_group_stride,
-                              const uint8_t* b2_codes, const uint8_t* b2_scales, int64_t b2_k, const int32_t* offsets, int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue,
-                              void* out0, void* out1, void* out2, const void* aux0, const void* aux1, void* ws,
-                              size_t ws_bytes, moe_stream_t stream) {
+                              const uint8_t* b2_codes, const uint8_t* b2_scales, int64_t b2_k, const int32_t* offsets,
+                              int32_t G, int64_t M, int64_t N, int64_t K, int32_t epilogue, void* out0, void* out1,
+                              void* out2, const void* aux0, const void* aux1, uint8_t* q_codes, uint8_t* q_scales,
+                              void* ws, size_t ws_bytes, moe_stream_t stream) {
   g_err.clear();
   CHECK(epilogue >= MOE_MX_EPI_STORE && epilogue <= MOE_MX_EPI_SWIGLU_BWD, MOE_ERR_INVALID_VALUE,
         "unknown epilogue %d", epilogue);
@@ -573,6 +574,10 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
   if (epilogue == MOE_MX_EPI_STORE) CHECK(out0, MOE_ERR_INVALID_VALUE, "out0 is NULL");
   if (epilogue == MOE_MX_EPI_SWIGLU) CHECK(out2, MOE_ERR_INVALID_VALUE, "out2 is NULL");
   if (epilogue == MOE_MX_EPI_SWIGLU_BWD) CHECK(out0 && aux0 && aux1, MOE_ERR_INVALID_VALUE, "out0/aux0/aux1 is NULL");
+  CHECK((q_codes == nullptr) == (q_scales == nullptr), MOE_ERR_INVALID_VALUE,
+        "q_codes and q_scales must both be given or both be NULL");
+  CHECK(!q_codes || epilogue != MOE_MX_EPI_STORE, MOE_ERR_INVALID_VALUE,
+        "quantized outputs are produced by the SwiGLU epilogues only");
   const size_t need = moe_mx_gemm_workspace_size(G);
   CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
         ws ? ws_bytes : (size_t)0);
@@ -600,6 +605,8 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
   a.out2 = out2;
   a.aux0 = aux0;
   a.aux1 = aux1;
+  a.qc = q_codes;
+  a.qs = q_scales;
   return hip_check(moe::launch_mx_gemm(epilogue, false, a, S(stream)), "MXFP8 grouped GEMM (rows)");
 }
 

@@ -41,6 +41,8 @@ struct MxGemmArgs {
   const void* aux1;
   int split;              // ragged K: output rows [0, split) -> out0, [split, M) -> out1
   int tiles;              // tile indices of the launch (set by the launcher)
+  uint8_t* qc;            // SwiGLU / SwiGLU backward: MXFP8 of the bf16 output rows (codes, scales), or null
+  uint8_t* qs;
   int kparts;             // ragged K: splits of each group's K range (fp32 partials, then a reduction)
   float* partial;         // [kparts, G, M, N] fp32 when kparts > 1
 };

@@ -725,6 +725,20 @@ __device__ __forceinline__ void unpack8(const u32x4_t& w, float (&v)[8]) {
   }
 }
 
+// MXFP8 of 8 consecutive bf16 values of a row (packed in w) whose 32-column block is spread over
+// lanes l, l ^ 16, l ^ 32, l ^ 48 (the exchanged layout): codes to dst (8 bytes), the scale byte by
+// the lane holding the block's first columns.
+__device__ __forceinline__ void quant8_xchg(const u32x4_t& w, uint8_t* dst, uint8_t* scale, bool first) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) am = max(am, max((w[e] & 0x7fffu) << 16, ((w[e] >> 16) & 0x7fffu) << 16));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+  const int e = mx_shared_exp(am);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(e4m3_pack4(w[0], w[1], e), e4m3_pack4(w[2], w[3], e));
+  if (first) *scale = (uint8_t)(e + 127);
+}
+
 template <int EPI, bool RK>
 __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& t, const f32x16_t (&acc)[4][2],
                                               int wm, int wn, int lane) {
@@ -747,7 +761,9 @@ __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& 
         const long long o = (long long)row * p.N + col;
         if (p.out0) *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(p.out0) + o) = pack8(g[pc]);
         if (p.out1) *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(p.out1) + o) = pack8(u[pc]);
-        *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(p.out2) + o) = pack8(hv);
+        const u32x4_t hw = pack8(hv);
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(p.out2) + o) = hw;
+        if (p.qc) quant8_xchg(hw, p.qc + o, p.qs + (long long)row * (p.N >> 5) + (col >> 5), cl == 0);
       }
     } else {
 #pragma unroll
@@ -771,8 +787,15 @@ __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& 
               db[e] = x[pc][e] * a[e] * sg;
             }
             bf16_t* dab = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * (2 * p.N);
-            *reinterpret_cast<u32x4_t*>(dab + col) = pack8(da);
-            *reinterpret_cast<u32x4_t*>(dab + p.N + col) = pack8(db);
+            const u32x4_t aw = pack8(da), bw = pack8(db);
+            *reinterpret_cast<u32x4_t*>(dab + col) = aw;
+            *reinterpret_cast<u32x4_t*>(dab + p.N + col) = bw;
+            if (p.qc) {
+              uint8_t* qrow = p.qc + (long long)row * (2 * p.N);
+              uint8_t* srow = p.qs + (long long)row * (p.N >> 4);
+              quant8_xchg(aw, qrow + col, srow + (col >> 5), cl == 0);
+              quant8_xchg(bw, qrow + p.N + col, srow + ((p.N + col) >> 5), cl == 0);
+            }
           } else {
             if constexpr (RK) {
               if (p.kparts > 1) {   // fp32 partial of K part t.part
@@ -1079,11 +1102,16 @@ hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream
     }
   }
   if (ragged_k) return launch_mx<MX_EPI_STORE, true>(a, blocks, s);
+  hipError_t e;
   switch (epi) {
-    case MX_EPI_SWIGLU: return launch_mx<MX_EPI_SWIGLU, false>(a, blocks, s);
-    case MX_EPI_SWIGLU_BWD: return launch_mx<MX_EPI_SWIGLU_BWD, false>(a, blocks, s);
+    case MX_EPI_SWIGLU: e = launch_mx<MX_EPI_SWIGLU, false>(a, blocks, s); break;
+    case MX_EPI_SWIGLU_BWD: e = launch_mx<MX_EPI_SWIGLU_BWD, false>(a, blocks, s); break;
     default: return launch_mx<MX_EPI_STORE, false>(a, blocks, s);
   }
+  if (e != hipSuccess || !a.qc) return e;
+  // The 128x128 kernel does not quantize in its epilogue: quantize the stored rows afterwards.
+  const int K = epi == MX_EPI_SWIGLU ? a.N : 2 * a.N;
+  return launch_mx_quant_rows(epi == MX_EPI_SWIGLU ? a.out2 : a.out0, a.M, K, K, a.qc, a.qs, s);
 }
 
 }  // namespace moe

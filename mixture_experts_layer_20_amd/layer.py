@@ -342,11 +342,11 @@ class MoELayer:
             q("q_x", t["x"], M, d, m.xq)
             self._stage(self._pfx(i, "gate_up_fwd"), L.moe_mx_gemm_rows, m.xq[0], m.xq[1], m.w1q[0], m.w1q[1], d,
                         f * d, m.w3q[0], m.w3q[1], 0, m.offsets, G, M, f, d, L.MOE_MX_EPI_SWIGLU,
-                        t["a"] if bw else None, t["b"] if bw else None, t["h"], None, None, m.ws, m.ws.numel())
-            q("q_h", t["h"], M, f, m.hq)
+                        t["a"] if bw else None, t["b"] if bw else None, t["h"], None, None, m.hq[0], m.hq[1],
+                        m.ws, m.ws.numel())   # H also comes out quantized (rows along f)
             self._stage(self._pfx(i, "down_fwd"), L.moe_mx_gemm_rows, m.hq[0], m.hq[1], m.w2q[0], m.w2q[1], f,
                         d * f, None, None, 0, m.offsets, G, M, d, f, L.MOE_MX_EPI_STORE, t["y"], None, None, None,
-                        None, m.ws, m.ws.numel())
+                        None, None, None, m.ws, m.ws.numel())
 
     def _mx_dgrad(self, dout):
         d = self.cfg.d
@@ -357,11 +357,10 @@ class MoELayer:
             q("q_dy", t["dy"], M, d, m.dyq)
             self._stage(self._pfx(i, "down_bwd"), L.moe_mx_gemm_rows, m.dyq[0], m.dyq[1], m.w2t[0], m.w2t[1], G * d,
                         d, None, None, 0, m.offsets, G, M, f, d, L.MOE_MX_EPI_SWIGLU_BWD, t["dab"], None, None,
-                        t["a"], t["b"], m.ws, m.ws.numel())
-            q("q_dab", t["dab"], M, 2 * f, m.dabq)
+                        t["a"], t["b"], m.dabq[0], m.dabq[1], m.ws, m.ws.numel())   # [dA | dB] also quantized
             self._stage(self._pfx(i, "gate_up_dgrad"), L.moe_mx_gemm_rows, m.dabq[0], m.dabq[1], m.w1t[0],
                         m.w1t[1], G * f, f, m.w3t[0], m.w3t[1], f, m.offsets, G, M, d, 2 * f, L.MOE_MX_EPI_STORE,
-                        t["dx"], None, None, None, None, m.ws, m.ws.numel())
+                        t["dx"], None, None, None, None, None, None, m.ws, m.ws.numel())
 
     def _mx_wgrad(self, dout):
         d = self.cfg.d

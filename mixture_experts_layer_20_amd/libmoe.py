@@ -84,7 +84,7 @@ _SIGS = {
     "moe_mx_quantize_cols": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _I64, _I32, _P, _P, _I64, _P, _P]),
     "moe_mx_gemm_workspace_size": (_SZ, [_I32]),
     "moe_mx_gemm_rows": (_I32, [_P, _P, _P, _P, _I64, _I64, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _I32, _P, _P,
-                                _P, _P, _P, _P, _SZ, _P]),
+                                _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mx_gemm_k_workspace_size": (_SZ, [_I32, _I64, _I64]),
     "moe_mx_gemm_k": (_I32, [_P, _P, _I64, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "moe_status_string": (_c.c_char_p, [_I32]),
@@ -316,10 +316,12 @@ def moe_mx_gemm_workspace_size(G) -> int:
 
 
 def moe_mx_gemm_rows(a_codes, a_scales, b_codes, b_scales, b_row_stride, b_group_stride, b2_codes, b2_scales, b2_k,
-                     offsets, G, M, N, K, epilogue, out0, out1, out2, aux0, aux1, ws, ws_bytes, stream=None):
+                     offsets, G, M, N, K, epilogue, out0, out1, out2, aux0, aux1, q_codes, q_scales, ws, ws_bytes,
+                     stream=None):
     _call("moe_mx_gemm_rows", _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), b_row_stride,
           b_group_stride, _ptr(b2_codes), _ptr(b2_scales), b2_k, _ptr(offsets), G, M, N, K, epilogue, _ptr(out0),
-          _ptr(out1), _ptr(out2), _ptr(aux0), _ptr(aux1), _ptr(ws), ws_bytes, _stream(stream))
+          _ptr(out1), _ptr(out2), _ptr(aux0), _ptr(aux1), _ptr(q_codes), _ptr(q_scales), _ptr(ws), ws_bytes,
+          _stream(stream))
 
 
 def moe_mx_gemm_k_workspace_size(G, M, N) -> int:

@@ -139,7 +139,7 @@ def test_mxfp8_argument_checks(lib):
     g = L.moe_mx_gemm_rows
     up = lambda epi: FAKE if epi == L.MOE_MX_EPI_SWIGLU else None    # second B source: SwiGLU up rows
     base = lambda N, K, epi, w: (FAKE, FAKE, FAKE, FAKE, K, N * K, up(epi), up(epi), 0, FAKE, 8, 512, N, K, epi, FAKE,
-                                 FAKE, FAKE, FAKE, FAKE, FAKE, w)
+                                 FAKE, FAKE, FAKE, FAKE, None, None, FAKE, w)
     _expect(L.MOE_ERR_UNSUPPORTED, g, *base(256, 192, L.MOE_MX_EPI_STORE, ws))
     _expect(L.MOE_ERR_UNSUPPORTED, g, *base(192, 256, L.MOE_MX_EPI_STORE, ws))
     _expect(L.MOE_ERR_INVALID_VALUE, g, *base(256, 256, 7, ws))
@@ -156,6 +156,9 @@ def test_mxfp8_argument_checks(lib):
     _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
     args[8] = 128
     args[7] = None             # codes without scales
+    _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
+    args = list(base(256, 256, L.MOE_MX_EPI_STORE, ws))
+    args[20] = args[21] = FAKE  # quantized outputs come from the SwiGLU epilogues only
     _expect(L.MOE_ERR_INVALID_VALUE, g, *args)
     gk = L.moe_mx_gemm_k
     W = 1 << 30   # a large enough workspace size

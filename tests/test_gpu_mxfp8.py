@@ -125,6 +125,16 @@ def ragged_offsets(rng, M, G):
     return np.concatenate([[0], cuts, [M]]).astype(np.int64)
 
 
+def quantize_rows_gpu_t(t):
+    """Stand-alone row quantization of a bf16 device tensor (codes, scales)."""
+    R, K = t.shape
+    codes = torch.empty((R, K), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=DEV)
+    L.moe_mx_quantize_rows(t, R, K, K, codes, scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
 def quantize_rows_gpu(x):
     R, K = x.shape
     codes = torch.empty((R, K), dtype=torch.uint8, device=DEV)
@@ -148,7 +158,7 @@ def test_gemm_rows_store(M, N, K, G):
     out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
     ws = torch.empty(L.moe_mx_gemm_workspace_size(G), dtype=torch.uint8, device=DEV)
     L.moe_mx_gemm_rows(ac, as_, bc, bs, K, N * K, None, None, 0, i32(offs), G, M, N, K, L.MOE_MX_EPI_STORE, out,
-                       None, None, None, None, ws, ws.numel())
+                       None, None, None, None, None, None, ws, ws.numel())
     torch.cuda.synchronize()
     qa = MX.mx_quantize_rows(a)
     qb = [MX.mx_quantize_rows(b[g]) for g in range(G)]
@@ -172,8 +182,10 @@ def test_gemm_rows_swiglu_and_backward():
     H = torch.empty_like(A)
     ws = torch.empty(L.moe_mx_gemm_workspace_size(G), dtype=torch.uint8, device=DEV)
     # gate rows at the start of each group's [2f, d] block, up rows f rows further (second source)
+    hq = torch.empty((M, f), dtype=torch.uint8, device=DEV)
+    hs = torch.empty((M, f // 32), dtype=torch.uint8, device=DEV)
     L.moe_mx_gemm_rows(xc, xs, wc, wsc, d, 2 * f * d, wc[f:], wsc[f:], 0, i32(offs), G, M, f, d,
-                       L.MOE_MX_EPI_SWIGLU, A, B, H, None, None, ws, ws.numel())
+                       L.MOE_MX_EPI_SWIGLU, A, B, H, None, None, hq, hs, ws, ws.numel())
     torch.cuda.synchronize()
     qx = MX.mx_quantize_rows(x)
     q1 = [MX.mx_quantize_rows(w1[g]) for g in range(G)]
@@ -184,6 +196,10 @@ def test_gemm_rows_swiglu_and_backward():
     assert_close("A", tnp(A), G1, TOL)
     assert_close("B", tnp(B), G3, TOL)
     assert_close("H", tnp(H), Href, TOL)
+    # The fused quantization of H equals the stand-alone quantizer on the stored H (rows in groups).
+    rq, rs = quantize_rows_gpu_t(H)
+    rows = np.arange(M)[(np.arange(M) >= offs[0]) & (np.arange(M) < offs[-1])]
+    assert np.array_equal(u8(hq)[rows], u8(rq)[rows]) and np.array_equal(u8(hs)[rows], u8(rs)[rows]), "fused H codes"
 
     # Backward through the down projection: dH = dY W2 (contraction over d), SwiGLU backward
     # against the stashed A and B.
@@ -194,8 +210,10 @@ def test_gemm_rows_swiglu_and_backward():
     a_in = as_dtype_values(2.0 * rng.standard_normal((M, f)), "bf16")     # stashed gate/up values
     b_in = as_dtype_values(rng.standard_normal((M, f)), "bf16")
     dab = torch.empty((M, 2 * f), dtype=torch.bfloat16, device=DEV)
+    dq = torch.empty((M, 2 * f), dtype=torch.uint8, device=DEV)
+    dsq = torch.empty((M, 2 * f // 32), dtype=torch.uint8, device=DEV)
     L.moe_mx_gemm_rows(dyc, dys, w2c, w2s, d, f * d, None, None, 0, i32(offs), G, M, f, d, L.MOE_MX_EPI_SWIGLU_BWD,
-                       dab, None, None, dev_tensor(a_in, "bf16"), dev_tensor(b_in, "bf16"), ws, ws.numel())
+                       dab, None, None, dev_tensor(a_in, "bf16"), dev_tensor(b_in, "bf16"), dq, dsq, ws, ws.numel())
     torch.cuda.synchronize()
     qdy = MX.mx_quantize_rows(dy)
     q2 = [MX.mx_quantize_rows(w2t[g]) for g in range(G)]
@@ -207,6 +225,9 @@ def test_gemm_rows_swiglu_and_backward():
     got = tnp(dab)
     assert_close("dA", got[:, :f], dA, TOL)
     assert_close("dB", got[:, f:], dB, TOL)
+    rq, rs = quantize_rows_gpu_t(dab)
+    assert np.array_equal(u8(dq), u8(rq)) and np.array_equal(u8(dsq), u8(rs)), "fused [dA|dB] codes"
+
 
 
 @pytest.mark.parametrize("R,Mw,N,G,split", [(1000, 256, 128, 7, 128), (300, 128, 256, 3, 128),
@@ -265,7 +286,7 @@ def test_gemm_rows_k_split():
     for n_out in (N, N // 2):      # N = 256: pipelined kernel; the 128-column half view: 128x128 kernel
         out = torch.empty((M, n_out), dtype=torch.bfloat16, device=DEV)
         L.moe_mx_gemm_rows(ac, as_, c1, s1, K1, N * K1, c2, s2, K1, i32(offs), G, M, n_out, K1 + K2,
-                           L.MOE_MX_EPI_STORE, out, None, None, None, None, ws, ws.numel())
+                           L.MOE_MX_EPI_STORE, out, None, None, None, None, None, None, ws, ws.numel())
         torch.cuda.synchronize()
         bb = np.concatenate([b1, b2], axis=2)[:, :n_out]
         qa = MX.mx_quantize_rows(a)

@@ -45,10 +45,11 @@ def short_name(name: str) -> str:
     m = re.search(r"grouped_gemm_bf16<(\d), [^>]*Cfg<(\d+), (\d+), (\d), (\d)>", name)
     if m:
         return f"grouped_gemm_bf16[{MODES[int(m.group(1))]}, {m.group(2)}x{m.group(3)}, {int(m.group(4)) * int(m.group(5))} waves]"
-    m = re.search(r"(mx_gemm_pipe_kernel|mx_gemm_kernel)<(\d), (true|false)>", name)
+    m = re.search(r"(mx_gemm_pipe_kernel|mx_gemm_kernel)<(\d), (true|false)(?:, (\d+))?>", name)
     if m:
         epi = "wgrad" if m.group(3) == "true" else ("store", "swiglu", "swiglu_bwd")[int(m.group(2))]
-        return f"{m.group(1).replace('_kernel', '')}[{epi}]"
+        sw = f", {m.group(4)}-byte scales" if m.group(4) else ""
+        return f"{m.group(1).replace('_kernel', '')}[{epi}{sw}]"
     m = re.search(r"(grouped_gemm_pipe|grouped_gemm_bf16_dma|splitk_reduce)<(\d)>", name)
     if m:
         return f"{m.group(1)}[{MODES[int(m.group(2))]}]"

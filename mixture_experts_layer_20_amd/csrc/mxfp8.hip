@@ -502,8 +502,17 @@ template <int SW> struct ScaleRing {
   static constexpr int STEPS = SW / 2;               // K steps per load
   static constexpr int SLOT = 2 * PB * SW;
   static constexpr int SLOTS = SW == 4 ? 3 : 2;      // a slot is reloaded only after its last read
-  static constexpr int LDS = PNST * PSTAGE + SLOTS * SLOT;
+  static constexpr int PREF = PNST * PSTAGE + SLOTS * SLOT;   // group tile prefix (ragged rows): 1025 ints
+  static constexpr int LDS = PREF + 4 * 1032;
 };
+
+// One LDS dword read with its own wait (a compiler-generated LDS read would first wait for every
+// direct load in flight).
+__device__ __forceinline__ int lds_i32(uint32_t addr) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -579,20 +588,21 @@ __device__ __forceinline__ int ufirst(int v) { return __builtin_amdgcn_readfirst
 // Tile Lt of the launch (tile order: group by group, row tiles, column tiles fastest); false past the
 // last tile.
 template <bool RK>
-__device__ __forceinline__ bool pipe_tile(const MxGemmArgs& p, int Lt, int NT, PTile& t) {
+__device__ __forceinline__ bool pipe_tile(const MxGemmArgs& p, int Lt, int NT, uint32_t pref, PTile& t) {
   t.nt = Lt % NT;
   if constexpr (!RK) {
+    // pref: LDS address of the group tile prefix (pref[g] = row tiles of groups before g)
     const int mt = Lt / NT;
-    if (mt >= ufirst(p.tile_prefix[p.G])) return false;
+    if (mt >= ufirst(lds_i32(pref + 4 * p.G))) return false;
     int lo = 0, hi = p.G;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (ufirst(p.tile_prefix[mid]) <= mt) lo = mid; else hi = mid;
+      if (ufirst(lds_i32(pref + 4 * mid)) <= mt) lo = mid; else hi = mid;
     }
     t.g = lo;
     const int r0 = min(max(ufirst(p.offsets[lo]), 0), p.M);
     const int r1 = min(max(ufirst(p.offsets[lo + 1]), r0), p.M);
-    t.m0 = r0 + (mt - ufirst(p.tile_prefix[lo])) * PB;
+    t.m0 = r0 + (mt - ufirst(lds_i32(pref + 4 * lo))) * PB;
     t.m_end = r1;
     t.kb0 = 0;
     t.nk = p.K / PK;
@@ -840,9 +850,41 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
   const int wm = wave & 1, wn = wave >> 1, li = lane & 31, h = lane >> 5;
   constexpr int OC = EPI == MX_EPI_SWIGLU ? 128 : PB;   // output columns per tile
   const int NT = p.N / OC;
+  // Ragged rows: the group tile prefix, computed by every workgroup into LDS before any direct
+  // load is issued (G <= 1024; a Hillis-Steele scan over 1024 entries, two per thread).
+  int* pref_lds = reinterpret_cast<int*>(plds + SR::PREF);
+  const uint32_t pref = lds_off(pref_lds);
+  if constexpr (!RK) {
+    int* scan = pref_lds + 1;   // scan[g] = row tiles of groups 0..g
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int g = tid + 512 * q;
+      int v = 0;
+      if (g < p.G) {
+        const int r0 = min(max(p.offsets[g], 0), p.M);
+        const int r1 = min(max(p.offsets[g + 1], r0), p.M);
+        v = (r1 - r0 + PB - 1) / PB;
+      }
+      scan[g] = v;
+    }
+    if (tid == 0) pref_lds[0] = 0;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      int add[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int g = tid + 512 * q;
+        add[q] = g >= o ? scan[g - o] : 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) scan[tid + 512 * q] += add[q];
+      __syncthreads();
+    }
+  }
   // Tiles to share out: ragged rows count the row tiles the groups really have (the launch size
   // assumes the worst case; an even split of that would leave the XCDs at its end idle).
-  const int U = RK ? p.tiles : ufirst(p.tile_prefix[p.G]) * NT;
+  const int U = RK ? p.tiles : ufirst(pref_lds[p.G]) * NT;
 
   const int nb = gridDim.x, b = blockIdx.x;
   int first, stride, last;   // this workgroup's tiles: first, first + stride, ... < last
@@ -873,7 +915,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
   auto pseek = [&]() {   // move to the first tile at or after pl with steps to load
     pvalid = false;
     while (pl < last) {
-      if (!pipe_tile<RK>(p, pl, NT, pt)) { pl = last; break; }
+      if (!pipe_tile<RK>(p, pl, NT, pref, pt)) { pl = last; break; }
       if (pt.nk > 0) {
         pipe_sources<EPI, RK>(p, pt, split, wave, lane, L);
         pvalid = true;
@@ -910,7 +952,7 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_pipe_kernel(MxGemmArgs p) {
   bool after_epi = false;
   for (int Lt = first; Lt < last; Lt += stride) {
     PTile t;
-    if (!pipe_tile<RK>(p, Lt, NT, t)) break;
+    if (!pipe_tile<RK>(p, Lt, NT, pref, t)) break;
     f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1074,10 +1116,12 @@ hipError_t launch_mx_gemm(int epi, bool ragged_k, const MxGemmArgs& a, hipStream
   const long long NT = a.N / OC;
   long long tiles;
   if (!ragged_k) {
-    hipLaunchKernelGGL(mx_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.G, 0LL, (long long)a.M, TM, 1,
-                       a.tile_prefix);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!pipe) {   // the pipelined kernel computes its tile prefix itself
+      hipLaunchKernelGGL(mx_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.G, 0LL, (long long)a.M, TM, 1,
+                         a.tile_prefix);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     tiles = ((long long)(a.M + TM - 1) / TM + a.G) * NT;
   } else {
     tiles = (long long)a.G * (a.M / TM) * NT;

@@ -111,10 +111,14 @@ struct SegGeo {
   uint32_t offs, pref;
 };
 
-// The tiles of one XCD: n of them; list position i < n1 is tile total0 + lo1 + i (set 1), the
-// others are lo0 + (i - n1) (set 0 numbering, which set 1 continues).
+// The tiles of one XCD: n list positions; position i < n1 is tile total0 + lo1 + i (set 1), the
+// others are lo0 + (i - n1) (set 0 numbering, which set 1 continues).  Positions from q on are
+// half tiles (ragged M only): q + 2h + s is row half s of tile position q + h.  When the XCD's
+// last round of tiles would keep at most half of its workgroups busy, those tiles are dealt as
+// halves, so every workgroup ends with at most one half tile instead of some running a whole
+// extra tile while the others wait.
 struct Deal {
-  int n, n1, lo0, lo1, total0;
+  int n, n1, lo0, lo1, total0, q;
 };
 __device__ __forceinline__ int tile_at(const Deal& dl, int i) {
   return i < dl.n1 ? dl.total0 + dl.lo1 + i : dl.lo0 + (i - dl.n1);
@@ -191,6 +195,20 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
     t.k_end = min(r1, t.k_begin + chunk);
   }
   t.nk = (t.k_end - t.k_begin + BKS - 1) / BKS;
+  return t;
+}
+
+// The tile at list position i of an XCD's deal.  A half with no rows (the second half of a tile
+// of at most 128 rows) has nk = 0 and is skipped.
+template <int MODE>
+__device__ __forceinline__ Tile deal_tile(const GemmArgs& p, const SegGeo (&geo)[2], const Deal& dl, int i) {
+  if (Traits<MODE>::raggedK || i < dl.q) return decode_tile<MODE>(p, geo, tile_at(dl, i));
+  const int h = (i - dl.q) >> 1, s = (i - dl.q) & 1;
+  Tile t = decode_tile<MODE>(p, geo, tile_at(dl, dl.q + h));
+  t.m0 += s * (BM / 2);
+  t.m_end = min(t.m_end, t.m0 + BM / 2);
+  t.half = true;
+  if (t.m0 >= t.m_end) t.nk = 0;
   return t;
 }
 
@@ -917,7 +935,7 @@ __device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const S
     return;
   }
   for (int i = pr.i + nbx; i < dl.n; i += nbx) {
-    const Tile t = decode_tile<MODE>(p, geo, tile_at(dl, i));
+    const Tile t = deal_tile<MODE>(p, geo, dl, i);
     if (t.nk > 0) {
       pr.t = t;
       pr.i = i;
@@ -1043,12 +1061,21 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     dl.lo1 = min(geo[1].total, xcd * per1);
     dl.n1 = min(geo[1].total, (xcd + 1) * per1) - dl.lo1;
     dl.n = dl.n1 + min(geo[0].total, (xcd + 1) * per0) - dl.lo0;
+    dl.q = dl.n;
   } else {
     const int total = geo[0].total + geo[1].total, per = (total + 7) >> 3;
     dl.lo0 = min(total, xcd * per);
     dl.lo1 = 0;
     dl.n1 = 0;
     dl.n = min(total, (xcd + 1) * per) - dl.lo0;
+    dl.q = dl.n;
+    if constexpr (!TR::raggedK) {
+      const int rem = dl.n % nbx;
+      if (rem > 0 && 2 * rem <= nbx) {
+        dl.q = dl.n - rem;
+        dl.n += rem;
+      }
+    }
   }
 
   // Consumer: the tile being multiplied (the first one with work; empty ones get zeros).
@@ -1056,9 +1083,9 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
   Tile ct;
   for (;; ic += nbx) {
     if (ic >= dl.n) return;
-    ct = decode_tile<MODE>(p, geo, tile_at(dl, ic));
+    ct = deal_tile<MODE>(p, geo, dl, ic);
     if (ct.nk > 0) break;
-    zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
+    if constexpr (TR::raggedK) zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
   }
 
   // Prologue: stages 0..3 into slots 0..3, wait for stage 0, read substep 0 of stage 0.
@@ -1110,12 +1137,12 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     }
     bool more = false;
     for (ic += nbx; ic < dl.n; ic += nbx) {
-      ct = decode_tile<MODE>(p, geo, tile_at(dl, ic));
+      ct = deal_tile<MODE>(p, geo, dl, ic);
       if (ct.nk > 0) {
         more = true;
         break;
       }
-      zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
+      if constexpr (TR::raggedK) zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
     }
     if (!more) break;
   }

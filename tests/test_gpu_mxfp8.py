@@ -301,6 +301,11 @@ LAYER_CASES = {
     # name: (routing, T, d, E, k, f, fs)
     "learned_f256": ("learned", 256, 256, 8, 2, 256, 256),
     "random_f128": ("random", 300, 256, 5, 3, 128, 128),
+    # few tokens over many experts: most experts get no rows, one gets most of them
+    "learned_sparse_k1": ("learned", 48, 256, 32, 1, 128, 128),
+    "learned_sparse_k2": ("learned", 40, 256, 16, 2, 128, 128),
+    "learned_single_token": ("learned", 1, 128, 4, 1, 128, 128),
+    "random_top8_e256": ("random", 200, 128, 256, 8, 128, 128),
 }
 
 
@@ -331,6 +336,10 @@ def test_mx_layer_matches_oracle(case):
     # device's fp32-versus-float64 difference; single products are held to 4e-3 above.
     for name, (got, ref) in checks.items():
         assert_close(name, tnp(got), ref, 5e-2)
+    counts = np.bincount(np.asarray(fwd["topk_idx"]).reshape(-1), minlength=E)
+    for e in np.nonzero(counts == 0)[0]:
+        for key in ("dw1", "dw3", "dw2"):
+            assert bool((b[key][int(e)] == 0).all()), f"empty expert {e}: {key} is not zero"
 
 
 @pytest.mark.parametrize("name", ["tiny64e_random", "tiny64e_learned_skew"])

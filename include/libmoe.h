@@ -14,6 +14,10 @@
  *   Memory      All tensor pointers are DEVICE pointers owned by the caller.  The library keeps
  *               no pointer after a call returns and allocates no device memory: scratch space is
  *               the caller's workspace, sized by the matching *_workspace_size function.
+ *               Every device pointer (tensors, index arrays, workspaces) must be 16-byte
+ *               aligned: the kernels use 16-byte vector and direct-to-LDS accesses from each base
+ *               (hipMalloc and PyTorch allocations are 256-byte aligned); a misaligned pointer
+ *               returns MOE_ERR_INVALID_VALUE.
  *   Layout      Row-major, contiguous.  Weights are [out_features, in_features]:
  *                 w_router [E, d]; w1, w3 [G, f, d]; w2 [G, d, f].
  *   Types       dt = MOE_F32: every activation and weight is float.  dt = MOE_BF16: activations,

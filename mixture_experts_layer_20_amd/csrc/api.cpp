@@ -5,7 +5,9 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "common.h"
@@ -36,6 +38,20 @@ constexpr int64_t kMaxInt = 0x7fffffff;
   do {                                       \
     if (!(cond)) return fail(st, __VA_ARGS__); \
   } while (0)
+
+// Device tensors, index arrays and workspaces are accessed with vector loads and stores of up to
+// 16 bytes (the GEMMs also with 16-byte direct-to-LDS loads) at offsets from each base pointer
+// that are multiples of the access size, so every device pointer must be 16-byte aligned (hipMalloc
+// and PyTorch allocations are 256-byte aligned).  NULL passes.
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  return true;
+}
+
+#define CHECK_ALIGN16(...)                                                   \
+  CHECK(aligned16({__VA_ARGS__}), MOE_ERR_INVALID_VALUE,                    \
+        "device pointers must be 16-byte aligned (" #__VA_ARGS__ ")")
 
 moe_status_t check_dtype(moe_dtype_t dt) {
   CHECK(dt == MOE_F32 || dt == MOE_BF16, MOE_ERR_INVALID_VALUE, "dt must be MOE_F32 or MOE_BF16");
@@ -75,6 +91,9 @@ inline hipStream_t S(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); 
 
 moe_status_t run_gemm(int mode, const moe::GemmArgs& a, moe_dtype_t dt, moe_stream_t s,
                       const char* what) {
+  CHECK_ALIGN16(a.a, a.b0, a.b1, a.aux0, a.aux1, a.out0, a.out1, a.out2, a.offsets, a.tile_prefix);
+  if (a.nseg == 2) CHECK_ALIGN16(a.s1.a, a.s1.b0, a.s1.b1, a.s1.aux0, a.s1.aux1, a.s1.out0, a.s1.out1, a.s1.out2,
+                                 a.s1.offsets);
   return hip_check(moe::launch_grouped_gemm(mode, a, dt == MOE_BF16, S(s)), what);
 }
 
@@ -124,6 +143,7 @@ moe_status_t moe_route(const void* x, const void* w_router, const float* bias, f
   CHECK(w_router || !bias, MOE_ERR_INVALID_VALUE, "bias given without a learned router");
   if (T == 0) return MOE_OK;
   CHECK(logits && topk_idx && topk_gate, MOE_ERR_INVALID_VALUE, "logits/topk_idx/topk_gate is NULL");
+  CHECK_ALIGN16(x, w_router, bias, logits, topk_idx, topk_gate);
   if (w_router) {
     st = hip_check(moe::launch_router_logits(x, w_router, bias, logits, (int)T, (int)d, E,
                                              dt == MOE_BF16, S(stream)),
@@ -156,6 +176,7 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int6
   const size_t need = moe::permute_ws_bytes(T, E, k);
   CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
         ws ? ws_bytes : (size_t)0);
+  CHECK_ALIGN16(x, topk_idx, counts, offsets, dest_pos, src_row, x_perm, ws);
   return hip_check(moe::launch_permute(x, topk_idx, (int)T, (int)d, E, k, dt == MOE_BF16, counts,
                                        offsets, dest_pos, src_row, x_perm, ws, S(stream)),
                    "permute");
@@ -378,6 +399,7 @@ moe_status_t moe_combine(const void* y_perm, const float* topk_gate, const int32
   CHECK(d % 8 == 0, MOE_ERR_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
   if (T == 0) return MOE_OK;
   CHECK(y_perm && topk_gate && dest_pos && out, MOE_ERR_INVALID_VALUE, "y_perm/topk_gate/dest_pos/out is NULL");
+  CHECK_ALIGN16(y_perm, topk_gate, dest_pos, shared_out, out);
   return hip_check(moe::launch_combine(y_perm, topk_gate, dest_pos, shared_out, (int)T, (int)d, k,
                                        dt == MOE_BF16, out, S(stream)),
                    "combine");
@@ -394,6 +416,7 @@ moe_status_t moe_combine_bwd(const void* dout, const void* y_perm, const float* 
   if (T == 0) return MOE_OK;
   CHECK(dout && topk_gate && dest_pos && dy_perm, MOE_ERR_INVALID_VALUE, "dout/topk_gate/dest_pos/dy_perm is NULL");
   CHECK(!dgate || y_perm, MOE_ERR_INVALID_VALUE, "y_perm is NULL while dgate is requested");
+  CHECK_ALIGN16(dout, y_perm, topk_gate, dest_pos, dy_perm, dgate);
   return hip_check(moe::launch_combine_bwd(dout, y_perm, topk_gate, dest_pos, (int)T, (int)d, k,
                                            dt == MOE_BF16, dy_perm, dgate, S(stream)),
                    "combine backward");
@@ -409,6 +432,7 @@ moe_status_t moe_permute_bwd(const void* dx_perm, const int32_t* dest_pos, const
   CHECK(d % 8 == 0, MOE_ERR_UNSUPPORTED, "d must be a multiple of 8 (got %lld)", (long long)d);
   if (T == 0) return MOE_OK;
   CHECK(dx_perm && dest_pos && dx, MOE_ERR_INVALID_VALUE, "dx_perm/dest_pos/dx is NULL");
+  CHECK_ALIGN16(dx_perm, dest_pos, dx_add0, dx_add1, dx);
   return hip_check(moe::launch_permute_bwd(dx_perm, dest_pos, dx_add0, dx_add1, (int)T, (int)d, k,
                                            dt == MOE_BF16, dx, S(stream)),
                    "permute backward");
@@ -436,6 +460,7 @@ moe_status_t moe_route_bwd(const float* dgate, const float* topk_gate, const int
   const size_t need = moe::route_bwd_ws_bytes(T, d, E, k);
   CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
         ws ? ws_bytes : (size_t)0);
+  CHECK_ALIGN16(dgate, topk_gate, topk_idx, offsets, src_row, x, w_router, dw_router, dx_router, ws);
   return hip_check(moe::launch_route_bwd(dgate, topk_gate, topk_idx, offsets, src_row, x, w_router,
                                          (int)T, (int)d, E, k, dt == MOE_BF16, dw_router, dx_router,
                                          ws, S(stream)),
@@ -458,6 +483,7 @@ moe_status_t moe_router_aux(const float* logits, const int32_t* counts, int64_t 
   const size_t need = moe::router_aux_ws_bytes(T, E);
   CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
         ws ? ws_bytes : (size_t)0);
+  CHECK_ALIGN16(logits, counts, loss, prob_mean, load_frac, ws);
   return hip_check(moe::launch_router_aux(logits, counts, (int)T, E, k, weight, loss, prob_mean, load_frac, ws,
                                           S(stream)),
                    "router statistics");
@@ -481,6 +507,7 @@ moe_status_t moe_router_aux_bwd(const float* logits, const float* load_frac, con
   const size_t need = moe::router_aux_bwd_ws_bytes(T, d, E);
   CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
         ws ? ws_bytes : (size_t)0);
+  CHECK_ALIGN16(logits, load_frac, x, w_router, dw_router, dx_router, ws);
   return hip_check(moe::launch_router_aux_bwd(logits, load_frac, x, w_router, (int)T, (int)d, E, weight,
                                               dt == MOE_BF16, dw_router, dx_router, ws, S(stream)),
                    "router load-balancing backward");
@@ -500,6 +527,7 @@ moe_status_t moe_mx_quantize_rows(const void* x, int64_t R, int64_t K, int64_t l
   CHECK(K <= kMaxInt && R <= kMaxInt, MOE_ERR_UNSUPPORTED, "R and K must fit in int32");
   if (R == 0) return MOE_OK;
   CHECK(x && codes && scales, MOE_ERR_INVALID_VALUE, "x/codes/scales is NULL");
+  CHECK_ALIGN16(x, codes, scales);
   return hip_check(moe::launch_mx_quant_rows(x, R, (int)K, ldx, codes, scales, S(stream)), "MXFP8 row quantization");
 }
 
@@ -533,6 +561,7 @@ moe_status_t moe_mx_quantize_cols(const void* x, int64_t R, int64_t N, int64_t l
   CHECK(ldc >= need, MOE_ERR_INVALID_VALUE, "ldc must be >= %lld (got %lld)", (long long)need, (long long)ldc);
   CHECK(kbase && (ldc == 0 || (codes && scales)), MOE_ERR_INVALID_VALUE, "kbase/codes/scales is NULL");
   CHECK(R == 0 || x, MOE_ERR_INVALID_VALUE, "x is NULL");
+  CHECK_ALIGN16(x, offsets, codes, scales, kbase);
   return hip_check(moe::launch_mx_quant_cols(x, R, (int)N, ldx, offsets, G, group_rows, kpad, codes, scales, ldc,
                                              kbase, S(stream)),
                    "MXFP8 column quantization");
@@ -582,6 +611,7 @@ moe_status_t moe_mx_gemm_rows(const uint8_t* a_codes, const uint8_t* a_scales, c
   CHECK(ws && ws_bytes >= need, MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
         ws ? ws_bytes : (size_t)0);
   if (M == 0) return MOE_OK;
+  CHECK_ALIGN16(a_codes, a_scales, b_codes, b_scales, b2_codes, b2_scales, offsets, out0, out1, out2, aux0, aux1, q_codes, q_scales, ws);
   moe::MxGemmArgs a{};
   a.a = a_codes;
   a.as = a_scales;
@@ -633,6 +663,7 @@ moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int6
   const size_t need = moe::mx_k_workspace_bytes(G, (int)M, (int)N);
   CHECK(need == 0 || (ws && ws_bytes >= need), MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
         ws ? ws_bytes : (size_t)0);
+  CHECK_ALIGN16(a_codes, a_scales, b_codes, b_scales, kbase, out0, out1, ws);
   moe::MxGemmArgs a{};
   a.a = a_codes;
   a.as = a_scales;

@@ -170,3 +170,22 @@ def test_mxfp8_argument_checks(lib):
     assert need > 0 and L.moe_mx_gemm_k_workspace_size(1024, 2048, 2048) == 0
     _expect(L.MOE_ERR_WORKSPACE, gk, FAKE, FAKE, 512, FAKE, FAKE, 512, FAKE, 1, 256, 256, 256, FAKE, None, FAKE,
             need - 1)
+
+
+def test_misaligned_pointers_are_rejected(lib):
+    """Every device pointer must be 16-byte aligned; a misaligned one is refused before any launch."""
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_route, FAKE + 2, FAKE, None, FAKE, 8, 16, 4, 2, 1, L.MOE_BF16, FAKE,
+            FAKE)
+    assert "16-byte aligned" in L.last_error()
+    ws = L.moe_grouped_mlp_fwd_workspace_size(512, 8, 256, 128)
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_expert_down_fwd, FAKE + 8, FAKE, 8, 512, 256, 128, FAKE, L.MOE_BF16,
+            FAKE, FAKE, ws)
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_expert_down_fwd, FAKE, FAKE, 8, 512, 256, 128, FAKE, L.MOE_BF16,
+            FAKE + 4, FAKE, ws)
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_combine, FAKE, FAKE, FAKE, None, 10, 16, 2, L.MOE_BF16, FAKE + 4)
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_mx_quantize_rows, FAKE, 4, 64, 64, FAKE + 8, FAKE)
+    mws = L.moe_mx_gemm_workspace_size(8)
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_mx_gemm_rows, FAKE + 1, FAKE, FAKE, FAKE, 256, 256 * 256, None, None, 0,
+            FAKE, 8, 512, 256, 256, L.MOE_MX_EPI_STORE, FAKE, None, None, None, None, None, None, FAKE, mws)
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_mx_gemm_k, FAKE, FAKE, 512, FAKE + 16 + 4, FAKE, 512, FAKE, 8, 256, 256,
+            256, FAKE, None, FAKE, 1 << 30)

@@ -342,7 +342,7 @@ def test_mx_layer_matches_oracle(case):
             assert bool((b[key][int(e)] == 0).all()), f"empty expert {e}: {key} is not zero"
 
 
-@pytest.mark.parametrize("name", ["tiny64e_random", "tiny64e_learned_skew"])
+@pytest.mark.parametrize("name", ["tiny64e_random", "tiny64e_learned_skew", "e128_2seq", "large_e128"])
 def test_mx_layer_full_size_sampled_experts(name):
     """The MXFP8 layer at the full Tiny-64E shape (the bench's launch configuration).  Routing and
     dispatch are bit-exact over the whole batch; an expert's products depend only on its own rows,

@@ -127,10 +127,10 @@ __global__ __launch_bounds__(1024) void mx_prefix_kernel(const int32_t* __restri
 }
 
 // ---- Column quantization: 128 padded rows of one group x 512 columns per workgroup ----------
-// Each thread quantizes two columns over four 32-row blocks and writes each column's 128 codes as
-// one 128-byte run and its four scale bytes as one dword.  A thread only reads and writes its own
-// LDS rows, so no barrier is needed.  Groups are padded to a multiple of 128
-// rows, so a 128-row chunk never spans two groups.
+// Each thread quantizes two columns over four 32-row blocks into LDS ([column][128 codes]) and
+// writes their four scale bytes as one dword; after a barrier the workgroup writes the 512 code
+// runs of 128 bytes, eight lanes per run, so one store instruction covers eight whole runs.
+// Groups are padded to a multiple of 128 rows, so a 128-row chunk never spans two groups.
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __restrict__ x, long long R, int N,
                                                             long long ldx, const int32_t* __restrict__ offsets,
                                                             int G, long long group_rows,
@@ -192,14 +192,17 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const bf16_t* __rest
       dst[1] = w[1];
     }
   }
-  if (!active) return;
+  if (active) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(&stage[lc + c][0]);
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + (long long)(n + c) * ldc + k0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dst[q] = src[q];
-    *reinterpret_cast<uint32_t*>(scales + (long long)(n + c) * (ldc >> 5) + (k0 >> 5)) = sc[c];
+    for (int c = 0; c < 2; ++c)
+      *reinterpret_cast<uint32_t*>(scales + (long long)(n + c) * (ldc >> 5) + (k0 >> 5)) = sc[c];
+  }
+  __syncthreads();
+  const int n0 = blockIdx.y * 512, runs = min(512, N - n0), part = threadIdx.x & 7;
+#pragma unroll 4
+  for (int run = threadIdx.x >> 3; run < runs; run += 32) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage[run][16 * part]);
+    *reinterpret_cast<u32x4_t*>(codes + (long long)(n0 + run) * ldc + k0 + 16 * part) = v;
   }
 }
 

@@ -756,6 +756,61 @@ template <int EPI, bool RK>
 __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& t, const f32x16_t (&acc)[4][2],
                                               int wm, int wn, int lane) {
   const int cl = xcol(lane), rl = lane & 15;
+  if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
+    // The A/B stash of a 32-row block is loaded, all of it, before the block's first store: the
+    // stores through out0 and qc may alias the stash as far as the compiler knows, so a load
+    // written after one would wait for it and then for a whole memory round trip.  (Loading the
+    // next block's stash as well, before these stores, needs more registers than are left.)
+    // Rows past the group are clamped on load and dropped on store.
+    u32x4_t sa[1][2][2], sb[1][2][2];   // [buffer][column block][16-row piece]
+    auto load_blk = [&](int i, int buf) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) {
+          const int row = min(t.m0 + wm * 128 + i * 32 + rl + 16 * pc, t.m_end - 1);
+          const long long o = (long long)row * p.N + t.nt * PB + wn * 64 + c * 32 + cl;
+          sa[buf][c][pc] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(p.aux0) + o);
+          sb[buf][c][pc] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(p.aux1) + o);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      load_blk(i, 0);
+      const int rbase = t.m0 + wm * 128 + i * 32 + rl;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float x[2][8];
+        xchg_block(acc[i][c], x[0], x[1]);
+        const int col = t.nt * PB + wn * 64 + c * 32 + cl;
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) {
+          const int row = rbase + 16 * pc;
+          if (row >= t.m_end) continue;
+          float a[8], bb[8], da[8], db[8];
+          unpack8(sa[0][c][pc], a);
+          unpack8(sb[0][c][pc], bb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sg = sigmoid_f32(a[e]);
+            da[e] = x[pc][e] * bb[e] * sg * (1.0f + a[e] * (1.0f - sg));
+            db[e] = x[pc][e] * a[e] * sg;
+          }
+          bf16_t* dab = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * (2 * p.N);
+          const u32x4_t aw = pack8(da), bw = pack8(db);
+          *reinterpret_cast<u32x4_t*>(dab + col) = aw;
+          *reinterpret_cast<u32x4_t*>(dab + p.N + col) = bw;
+          if (p.qc) {
+            uint8_t* qrow = p.qc + (long long)row * (2 * p.N);
+            uint8_t* srow = p.qs + (long long)row * (p.N >> 4);
+            quant8_xchg(aw, qrow + col, srow + (col >> 5), cl == 0);
+            quant8_xchg(bw, qrow + p.N + col, srow + ((p.N + col) >> 5), cl == 0);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rbase = t.m0 + wm * 128 + i * 32 + rl;   // + 16 for the second piece
@@ -788,28 +843,7 @@ __device__ __forceinline__ void pipe_epilogue(const MxGemmArgs& p, const PTile& 
         for (int pc = 0; pc < 2; ++pc) {
           const int row = rbase + 16 * pc;
           if (!RK && row >= t.m_end) continue;
-          if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
-            const long long o = (long long)row * p.N + col;
-            float a[8], bb[8], da[8], db[8];
-            unpack8(*reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(p.aux0) + o), a);
-            unpack8(*reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(p.aux1) + o), bb);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float sg = sigmoid_f32(a[e]);
-              da[e] = x[pc][e] * bb[e] * sg * (1.0f + a[e] * (1.0f - sg));
-              db[e] = x[pc][e] * a[e] * sg;
-            }
-            bf16_t* dab = reinterpret_cast<bf16_t*>(p.out0) + (long long)row * (2 * p.N);
-            const u32x4_t aw = pack8(da), bw = pack8(db);
-            *reinterpret_cast<u32x4_t*>(dab + col) = aw;
-            *reinterpret_cast<u32x4_t*>(dab + p.N + col) = bw;
-            if (p.qc) {
-              uint8_t* qrow = p.qc + (long long)row * (2 * p.N);
-              uint8_t* srow = p.qs + (long long)row * (p.N >> 4);
-              quant8_xchg(aw, qrow + col, srow + (col >> 5), cl == 0);
-              quant8_xchg(bw, qrow + p.N + col, srow + ((p.N + col) >> 5), cl == 0);
-            }
-          } else {
+          {
             if constexpr (RK) {
               if (p.kparts > 1) {   // fp32 partial of K part t.part
                 float* dst = p.partial + (((long long)t.part * p.G + t.g) * p.M + row) * p.N + col;

@@ -22,11 +22,12 @@
 //    step, between the phases.  LDS reads are inline assembly with explicit lgkmcnt waits and the
 //    ring is governed by explicit vmcnt waits (the compiler's own waits would drain every load in
 //    flight before each LDS access).
-//  * Epilogue straight from the accumulators: 4x4 DPP quad transposes give each lane 4
-//    consecutive columns of one row, the mode's elementwise math (SwiGLU, SwiGLU backward) is
-//    applied and 8-byte bf16 stores go out.
+//  * Epilogue straight from the accumulators: a v_permlane32_swap gives each lane 8 consecutive
+//    columns of one row, the mode's elementwise math (SwiGLU, SwiGLU backward, whose A/B stash is
+//    loaded in the same layout two blocks ahead) is applied and 16-byte bf16 stores go out.
 //  * Persistent grid, per-expert tile prefix computed in-kernel, tiles dealt so each XCD walks one
-//    contiguous run (workgroup b runs on XCD b % 8).
+//    contiguous run (workgroup b runs on XCD b % 8); an XCD's last round of tiles, when it would
+//    keep at most half of its workgroups busy, is dealt as 128-row half tiles.
 #include "common.h"
 #include "gemm_common.h"
 

@@ -15,11 +15,24 @@
 // from lane i + 32b.  Products of E4M3 values and power-of-two scales are exact in fp32, and are
 // accumulated in fp32.
 //
-// GEMM design: one workgroup = one 128x128 output tile (4 waves, 2x2, 64x64 each), K consumed 128
-// bytes (= 128 elements) per step through a double-buffered LDS tile (16 KiB per operand and
-// buffer) with 128-byte row segments, 16-byte chunks XOR-swizzled by (row >> 1) & 7 so a
-// ds_read_b128 over 16 rows hits 16 distinct bank groups.  The B operand is the instruction's first
-// operand, so each lane's accumulators hold 4 consecutive output columns of one row.
+// Main GEMM (mx_gemm_pipe_kernel): persistent, one workgroup per CU, 256x256 output tiles, 8 waves
+// (two per SIMD, 128x64 each), K consumed 64 bytes per step.  Operand codes stream through a ring
+// of four 32 KiB LDS stages filled by direct-to-LDS loads; the stream runs across tile boundaries,
+// so the next tile's first stages load during an epilogue.  Scale bytes land in their own small
+// LDS ring (one dword per row per two K steps, or 16 bytes per eight where sizes allow).  Each XCD
+// takes a contiguous run of the real tile count (read from the group tile prefix the workgroup
+// computes in LDS), dealt round-robin to its workgroups.  Weight gradients (ragged K) run over each
+// group's padded column range and, when there are few output tiles, split K into parts with fp32
+// partials summed in part order.  Epilogues exchange accumulator lanes so each lane stores 16
+// contiguous bytes: plain store, SwiGLU (also writing the MXFP8 rows of H) and SwiGLU backward
+// (also writing the MXFP8 rows of [dA | dB]).
+//
+// Fallback GEMM (mx_gemm_kernel, shapes the main one does not take): one workgroup = one 128x128
+// output tile (4 waves, 2x2, 64x64 each), K consumed 128 bytes (= 128 elements) per step through a
+// double-buffered LDS tile (16 KiB per operand and buffer) with 128-byte row segments, 16-byte
+// chunks XOR-swizzled by (row >> 1) & 7 so a ds_read_b128 over 16 rows hits 16 distinct bank
+// groups.  In both, the B operand is the instruction's first operand, so each lane's accumulators
+// hold 4 consecutive output columns of one row.
 #include "common.h"
 #include "mxfp8.h"
 

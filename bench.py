@@ -6,7 +6,7 @@ the Olmo-core DDP MoE examples, "Production throughput runs").  A step is one fu
 path: route -> permute -> grouped SwiGLU experts + shared expert -> combine -> combine backward ->
 expert and shared dgrad/wgrad -> permute backward (+ router backward for learned routing).
 
-Prints one JSON line.  `--gpus N` with N > 1 is not supported: this build runs on one GPU.
+Prints one JSON line.  `--gpus N` with N > 1 is not supported: libmoe runs on one GPU.
 """
 from __future__ import annotations
 
@@ -121,7 +121,7 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs one GPU's share of the layer only; --gpus {a.gpus} is not supported "
-              "(no multi-GPU path in this build).", file=sys.stderr)
+              "(libmoe has no multi-GPU path).", file=sys.stderr)
         return 2
 
     import torch

@@ -10,7 +10,7 @@ What the layer computes, and where the pages state it:
     random (Olmo-core DDP MoE examples, "Production throughput runs" and its operating-point table);
   * tokens move to experts that stay resident; the experts do not move (Olmo-core 3 Opens Large
     MoE Training, "Enhanced Key Takeaways" and "Technical Deep Dive").
-The pages give no formulas. Readings taken where they are silent (all listed in the design doc):
+The pages give no formulas. Readings taken where they are silent:
   router logits are fp32, summed in index order one rounding per step, then + bias; selection is
   the k largest logits, ties to the lowest expert index, -0 equal to +0; gates are a softmax over
   the k chosen logits; the expert MLP is SwiGLU, silu(x W1^T) * (x W3^T) then W2^T, no biases; the

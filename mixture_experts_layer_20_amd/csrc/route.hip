@@ -139,8 +139,18 @@ __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, cons
   }
 }
 
+// Selection order of two (logit, expert) pairs: is (v, e) before (bv, bi)?  A larger logit comes
+// first, equal logits (-0 == +0) by lower expert index, and a NaN after every number (NaNs among
+// themselves by index), so every selected index is a real expert even when logits are NaN.
+__device__ __forceinline__ bool select_before(float v, int e, float bv, int bi) {
+  const bool vn = v != v, bn = bv != bv;
+  if (vn != bn) return bn;
+  if (!vn && v != bv) return v > bv;
+  return e < bi;
+}
+
 // Top-k and gates: one wavefront per token, each lane holding up to 4 logits (E <= 256).
-// k rounds of a wave-wide arg-max under the order (larger logit first, then lower index).
+// k rounds of a wave-wide arg-max under select_before.
 __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int T, int E, int k,
                                                         int renormalize, int32_t* topk_idx,
                                                         float* topk_gate) {
@@ -160,12 +170,13 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j >= k) break;
-    float bv = -INFINITY;
+    // (NaN, past every index): any untaken expert comes before it
+    float bv = __builtin_nanf("");
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      if (!taken[i] && (v[i] > bv || (v[i] == bv && e < bi))) {
+      if (!taken[i] && select_before(v[i], e, bv, bi)) {
         bv = v[i];
         bi = e;
       }
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int
     for (int off = 32; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off, 64);
       const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
+      if (select_before(ov, oi, bv, bi)) {
         bv = ov;
         bi = oi;
       }

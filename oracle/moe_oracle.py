@@ -72,6 +72,8 @@ def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     """Indices of the k largest logits per token, largest first, equal values by lower index.
 
     A stable sort of the negated logits is exactly that order (IEEE comparison, so -0 == +0).
+    numpy's sort places NaN after every number, so a NaN logit ranks below -inf and NaNs rank among
+    themselves by index: every selected index is a real expert whatever the logits hold.
     """
     order = np.argsort(-np.asarray(logits), axis=1, kind="stable")
     return np.ascontiguousarray(order[:, :k]).astype(np.int32)

@@ -75,6 +75,26 @@ def test_random_route_ties(renormalize, kind, E, k):
     assert_close("gates", tnp(gate), O.gate_weights(Lg, ref_idx, renormalize=bool(renormalize)), 1e-6)
 
 
+@pytest.mark.parametrize("E,k", [(64, 4), (256, 8), (8, 8), (5, 2)])
+def test_route_with_nan_logits_selects_real_experts(E, k):
+    """NaN logits rank after every number and among themselves by index (the oracle's order): every
+    index stays in [0, E).  Only the router runs; nothing downstream reads the indices."""
+    log(f"route NaN logits E={E} k={k}")
+    T = 600
+    rng = np.random.default_rng(E + 3 * k)
+    Lg = rng.choice(np.array([np.nan, -np.inf, np.inf, -1.0, 0.0, 2.5], np.float32), size=(T, E))
+    Lg[: T // 4] = rng.standard_normal((T // 4, E)).astype(np.float32)
+    Lg[T // 4] = np.nan                                  # a whole token of NaN logits
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    L.moe_route(None, None, None, f32(Lg), T, 64, E, k, 1, L.MOE_BF16, idx, gate)
+    torch.cuda.synchronize()
+    got = tnp(idx)
+    assert got.min() >= 0 and got.max() < E
+    assert np.array_equal(got, O.select_topk(Lg, k))
+    assert list(got[T // 4]) == list(range(k))
+
+
 # ---------------------------------------------------------------------------------------- permute
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -33,6 +33,28 @@ def test_topk_matches_brute_force(k, kind):
         assert list(got[t]) == brute_topk(L[t], k), (t, L[t])
 
 
+def brute_topk_nan(row, k):
+    # The rule for non-finite logits: NaN after every number (-inf included), NaNs by index.
+    key = lambda e: (1, 0.0, e) if np.isnan(row[e]) else (0, -float(row[e]), e)
+    return sorted(range(len(row)), key=key)[:k]
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_topk_orders_nan_after_every_number(k):
+    rng = np.random.default_rng(7 + k)
+    T, E = 200, 8
+    L = rng.choice(np.array([np.nan, -np.inf, np.inf, -1.0, 0.0, -0.0, 2.0], np.float32), size=(T, E))
+    L[0] = np.nan                                   # a token whose logits are all NaN
+    L[1, :] = np.nan
+    L[1, 5] = -np.inf                               # one number among NaNs comes first
+    got = O.select_topk(L, k)
+    assert got.min() >= 0 and got.max() < E
+    for t in range(T):
+        assert list(got[t]) == brute_topk_nan(L[t], k), (t, L[t])
+    assert list(got[0]) == list(range(k))
+    assert got[1][0] == 5
+
+
 def test_topk_all_permutations_tiny():
     # Every ordering of 4 logits with one tie, all k.
     for perm in itertools.permutations([0.5, 2.0, 2.0, -1.0]):

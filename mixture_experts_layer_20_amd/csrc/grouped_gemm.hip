@@ -875,11 +875,10 @@ template <int MODE>
 hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float* partial, hipStream_t s) {
   typedef Traits<MODE> TR;
   if (bf16) {
-    // The pipelined 256x256 kernel wherever it applies: weight gradients, and ragged-M stages
-    // whose groups average at least 384 rows (LIBMOE_PIPE=0 disables it).
+    // The pipelined 256x256 kernel wherever it applies (LIBMOE_PIPE=0 disables it).
     static const char* pipe_env = getenv("LIBMOE_PIPE");
     const bool pipe_on = !(pipe_env && pipe_env[0] == '0');
-    if (pipe_on && pipe_supports(MODE, p) && (TR::raggedK || (p.G > 0 && p.M / p.G >= 384))) {
+    if (pipe_on && pipe_supports(MODE, p)) {
       int ksplit = 1;
       if constexpr (TR::raggedK) {
         const int Mw = mode_Mw(MODE, p.d, p.f), N = mode_N(MODE, p.d, p.f);
@@ -987,7 +986,7 @@ bool merge_sets(int mode, const GemmArgs& p) {
   // its tiles are about as long as set 0's (see launch_wgrad_sets).
   if (mode == GEMM_DOWN_WGRAD || mode == GEMM_UP_WGRAD)
     return (long long)p.G * (mode_Mw(mode, p.d, p.f) / 256) * (mode_N(mode, p.d, p.f) / 256) >= 2LL * num_cus();
-  return p.G > 0 && p.M / p.G >= 384 && p.s1.G > 0 && p.s1.M / p.s1.G >= 384;
+  return true;
 }
 
 // Set 1 of p as a single-set problem.

@@ -1050,32 +1050,33 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     }
   }
   // Tiles are dealt so each XCD (workgroup b runs on XCD b % 8) walks one contiguous run of the
-  // tile order.  Weight gradients of two sets: each XCD gets a run of each set, the longer set-1
-  // tiles (split shared-expert reductions) first.
+  // tile order.  Two sets: each XCD gets a run of each set, set 1 first.  The sets' tiles differ in
+  // length (the shared expert's K is its own d_ff in the down and gate/up data-gradient products,
+  // and its weight-gradient reduction is split into chunks), so one run over both sets would leave
+  // the XCDs that draw set 1 with more work; set 1's tiles are the longer ones where they differ.
   const int xcd = blockIdx.x & 7;
   const int nbx = gridDim.x >> 3;
   Deal dl;
   dl.total0 = geo[0].total;
-  if (TR::raggedK && two) {
+  if (two) {
     const int per0 = (geo[0].total + 7) >> 3, per1 = (geo[1].total + 7) >> 3;
     dl.lo0 = min(geo[0].total, xcd * per0);
     dl.lo1 = min(geo[1].total, xcd * per1);
     dl.n1 = min(geo[1].total, (xcd + 1) * per1) - dl.lo1;
     dl.n = dl.n1 + min(geo[0].total, (xcd + 1) * per0) - dl.lo0;
-    dl.q = dl.n;
   } else {
-    const int total = geo[0].total + geo[1].total, per = (total + 7) >> 3;
+    const int total = geo[0].total, per = (total + 7) >> 3;
     dl.lo0 = min(total, xcd * per);
     dl.lo1 = 0;
     dl.n1 = 0;
     dl.n = min(total, (xcd + 1) * per) - dl.lo0;
-    dl.q = dl.n;
-    if constexpr (!TR::raggedK) {
-      const int rem = dl.n % nbx;
-      if (rem > 0 && 2 * rem <= nbx) {
-        dl.q = dl.n - rem;
-        dl.n += rem;
-      }
+  }
+  dl.q = dl.n;
+  if constexpr (!TR::raggedK) {
+    const int rem = dl.n % nbx;
+    if (rem > 0 && 2 * rem <= nbx) {
+      dl.q = dl.n - rem;
+      dl.n += rem;
     }
   }
 

@@ -1,10 +1,20 @@
 """Benchmark: one GPU's MoE layer, forward+backward, on device-resident synthetic inputs.
 
-Default workload: one 8192-token sequence, d_model 2048, 64 experts, top-4 random routing, expert
-and shared-expert d_ff 1024, bf16 storage with fp32 accumulation (the Tiny-64E operating point of
-the Olmo-core DDP MoE examples, "Production throughput runs").  A step is one full pass of the
-path: route -> permute -> grouped SwiGLU experts + shared expert -> combine -> combine backward ->
-expert and shared dgrad/wgrad -> permute backward (+ router backward for learned routing).
+Default workload `large_e128`: one 8192-token sequence, d_model 4096, 128 experts, top-4 learned
+softmax router, expert d_ff 2048 plus one shared expert of d_ff 4096, bf16 storage with fp32
+accumulation -- the 128-expert operating point of the Olmo-core DDP MoE examples ("Production
+throughput runs": sequence 8192, top-4, one shared expert) and the largest workload that runs
+here.  A step is one full pass of the path: route -> permute -> grouped SwiGLU experts + shared
+expert -> combine -> combine backward -> router backward -> expert and shared dgrad/wgrad ->
+permute backward.
+
+Timing: W untimed warm-up steps, then K timed steps, each preceded by a write of a 512 MiB
+scratch buffer that evicts the L2 caches and the 256 MiB last-level cache, with HIP events on the
+launch stream around every step (not around the flush); `ms_per_step` is the median of those K
+step times and `value` the tokens per second it gives.  A second loop of K steps without flushes
+gives the warm-cache numbers.  Per-call times come from a separate pass with events around every
+library call, so the timed steps carry no per-call events.  Practical ceilings measured in the same
+process: a device-to-device copy (bandwidth) and a square bf16 matrix product (matrix units).
 
 Prints one JSON line.  `--gpus N` with N > 1 is not supported: libmoe runs on one GPU.
 """
@@ -13,6 +23,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -94,14 +105,133 @@ def cpu_baseline(cfg, inp, sample_tokens, min_seconds=10.0, max_runs=4):
                       f"{runs} run(s), {total:.1f} s total"}
 
 
+def cpu_small_configs():
+    """The oracle on the tiny fp32 workload (median of 5, all cores and one thread) and on a
+    512-token sample of the Tiny-64E workload with one thread: fixed small reference points."""
+    from threadpoolctl import threadpool_limits
+    from mixture_experts_layer_20_amd import inputs as I
+    from oracle import moe_oracle as O
+    out = {}
+    c0 = I.CONFIGS["tiny_fp32"]
+    v0 = I.values(I.make_inputs(c0))
+    for label, limit in (("all_cores", None), ("one_thread", 1)):
+        times = []
+        with threadpool_limits(limits=limit):
+            for _ in range(5):
+                t0 = time.perf_counter()
+                O.run_layer(c0, v0)
+                times.append(time.perf_counter() - t0)
+        out[f"tiny_fp32_{label}"] = {"tokens_per_s": c0.T / statistics.median(times),
+                                     "median_s": statistics.median(times), "runs": 5}
+    c1 = I.CONFIGS["tiny64e_random"]
+    v1 = I.values(I.make_inputs(c1))
+    n = 512
+    sub = dict(v1)
+    for key in ("x", "logits", "dout"):
+        sub[key] = v1[key][:n]
+    with threadpool_limits(limits=1):
+        O.run_layer(c1.with_(T=n), sub)
+        t0 = time.perf_counter()
+        O.run_layer(c1.with_(T=n), sub)
+        dt = time.perf_counter() - t0
+    out["tiny64e_random_one_thread"] = {"tokens_per_s": n / dt, "seconds": dt,
+                                        "sample": f"first {n} of {c1.T} tokens, forward+backward"}
+    return out
+
+
+def pct(xs, q):
+    """q-th percentile (linear interpolation) of a non-empty list."""
+    s = sorted(xs)
+    i = (len(s) - 1) * q / 100.0
+    lo = int(i)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (i - lo)
+
+
+def timed_steps(lay, steps, flush):
+    """K steps with events around each (flush before each when given); per-step ms and wall s."""
+    import torch
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if flush is not None:
+            flush.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        lay.step()
+        e.record()
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [s.elapsed_time(e) for s, e in evs], wall
+
+
+def ceilings(dev):
+    """Practical ceilings on this GPU: device copy bandwidth (torch copy of 2 GiB) and a square
+    bf16 matrix product (torch.matmul, 8192^3), each the best of 10 event-timed runs."""
+    import torch
+    out = {}
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(12):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize()
+        best = min(best, s.elapsed_time(e))
+    out["device_copy_GBps"] = 2 * n / (best * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    best = float("inf")
+    for _ in range(12):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        torch.matmul(a, b)
+        e.record()
+        torch.cuda.synchronize()
+        best = min(best, s.elapsed_time(e))
+    out["torch_matmul_bf16_8192_TFLOPs"] = 2 * m ** 3 / (best * 1e-3) / 1e12
+    # the same product through libmoe's grouped GEMM (one group of 8192 rows, the down stage)
+    from mixture_experts_layer_20_amd import libmoe as L
+    offs = torch.tensor([0, m], dtype=torch.int32, device=dev)
+    ws = torch.empty(max(256, L.moe_grouped_mlp_fwd_workspace_size(m, 1, m, m)), dtype=torch.uint8, device=dev)
+    y = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    best = float("inf")
+    for _ in range(12):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        L.moe_expert_down_fwd(a, offs, 1, m, m, m, b, L.MOE_BF16, y, ws, ws.numel())
+        e.record()
+        torch.cuda.synchronize()
+        best = min(best, s.elapsed_time(e))
+    out["libmoe_grouped_gemm_bf16_8192_TFLOPs"] = 2 * m ** 3 / (best * 1e-3) / 1e12
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="tiny64e_random")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_e128")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="MiB of scratch written before each timed step to evict the caches (0: none)")
+    ap.add_argument("--stage-steps", type=int, default=10,
+                    help="steps of the separate pass with events around every library call")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the workload the oracle runs for cpu_baseline (0: a size that takes "
+                         "about 10-30 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--cpu-small-configs", action="store_true",
+                    help="also time the oracle on the tiny fp32 workload and a Tiny-64E sample, with one "
+                         "thread and all cores")
     ap.add_argument("--lbl", type=float, default=0.0,
                     help="weight of the router's load-balancing loss (learned-routing workloads; 0: off)")
     ap.add_argument("--recompute", action="store_true",
@@ -138,7 +268,8 @@ def main(argv=None) -> int:
     inp = I.make_inputs(cfg)
     dev = torch.device("cuda:0")
     mx = a.precision == "mxfp8"
-    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=not (a.no_merge or mx), recompute=a.recompute,
+    merged = not (a.no_merge or mx)
+    lay = LY.MoELayer(cfg, LY.upload_inputs(inp, dev), merge_shared=merged, recompute=a.recompute,
                       lbl_weight=a.lbl, precision=a.precision, mx_cached_weights=a.mx_cached_weights)
     if a.copy_probe_mb > 0:
         src = torch.empty(a.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
@@ -146,33 +277,35 @@ def main(argv=None) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    flush = torch.empty(a.flush_mb << 20, dtype=torch.uint8, device=dev) if a.flush_mb > 0 else None
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(a.warmup):
         lay.step()
     torch.cuda.synchronize()
-    lay.events = {}
     print("[bench] timing", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
+    cold, cold_wall = timed_steps(lay, a.steps, flush)
+    warm, warm_wall = timed_steps(lay, a.steps, None)
+    ms_per_step = statistics.median(cold)
+
+    # Separate pass: events around every library call, on the launch stream.
+    print("[bench] per-call pass", file=sys.stderr, flush=True)
+    lay.events = {}
+    for _ in range(a.stage_steps):
         lay.step()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / a.steps
-
-    # Per-call device durations from the events recorded on the launch stream.
     stages = {}
     for name, pairs in lay.events.items():
         ms = [s.elapsed_time(e) for s, e in pairs]
         stages[name] = sum(ms) / len(ms)
-    flops = stage_flops(cfg, merged=not (a.no_merge or mx), recompute=a.recompute)
+    lay.events = None
+    flops = stage_flops(cfg, merged=merged, recompute=a.recompute)
     peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     gemm_ms = sum(stages[s] for s in flops if s in stages)
     gemm_flop = sum(flops.values())
     stage_tflops = {s: flops[s] / (stages[s] * 1e-3) / 1e12 for s in flops if s in stages}
-    # The dominant GEMM kernel: the longest stage that is one kernel launch (a weight-gradient
-    # stage is the GEMM plus its split-reduction pass).
-    dom = max((s for s in GEMM_STAGES if s in stages and (mx or "wgrad" not in s)), key=lambda s: stages[s])
+    # The dominant kernel: the longest GEMM stage, weight gradients included.  Each stage is one
+    # grouped-GEMM launch (a weight gradient whose reduction is split adds its reduce launch).
+    dom = max((s for s in flops if s in stages), key=lambda s: stages[s])
     achieved = stage_tflops[dom]
     traffic = None
     if os.path.exists(a.traffic_json):
@@ -185,7 +318,7 @@ def main(argv=None) -> int:
             traffic = None
     line = {
         "metric": METRIC,
-        "value": cfg.T * a.steps / elapsed,
+        "value": cfg.T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -203,6 +336,11 @@ def main(argv=None) -> int:
                    "mx_weights": ("quantized once (optimizer-step cadence)" if a.mx_cached_weights
                                   else "quantized every pass") if mx else None,
                    "lbl_weight": a.lbl if cfg.routing == "learned" else 0.0},
+        "step_ms": {"median": ms_per_step, "p10": pct(cold, 10), "p90": pct(cold, 90),
+                    "mean": statistics.fmean(cold), "caches_flushed_mb": a.flush_mb,
+                    "wall_s_incl_flushes": cold_wall,
+                    "warm_median": statistics.median(warm), "warm_p10": pct(warm, 10), "warm_p90": pct(warm, 90),
+                    "warm_wall_ms_per_step": warm_wall * 1e3 / a.steps},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "grouped_gemm": {"tflops": gemm_flop / (gemm_ms * 1e-3) / 1e12,
@@ -218,9 +356,17 @@ def main(argv=None) -> int:
         # MXFP8 quantization passes (activations each product, weights in both orientations).
         qs = {k: v for k, v in stages.items() if k.startswith("q_") or k.startswith("shared_q_")}
         line["mxfp8_quantize_ms"] = sum(qs.values())
+    del lay, flush
+    torch.cuda.empty_cache()
+    if not a.no_ceilings:
+        print("[bench] ceilings", file=sys.stderr, flush=True)
+        line["ceilings"] = ceilings(dev)
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, a.cpu_sample_tokens)
+        n = a.cpu_sample_tokens or (512 if cfg.d * cfg.f * cfg.E > (1 << 28) else 8192)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, n)
+        if a.cpu_small_configs:
+            line["cpu_baseline"]["small_configs"] = cpu_small_configs()
     print(json.dumps(line), flush=True)
     return 0
 

@@ -74,7 +74,9 @@ typedef void* moe_stream_t; /* hipStream_t */
  *                                       logits ordered by lower expert index (-0 equals +0)
  *   topk_gate  [T, k] float  OUTPUT    renormalize=1: softmax over the k chosen logits;
  *                                       renormalize=0: full softmax probability over all E
- * NaN or infinite logits are not supported (the selection is then unspecified). */
+ * A NaN logit ranks after every number (-inf included) and NaNs among themselves by lower index,
+ * so every topk_idx value is in [0, E) whatever the logits hold; the gates of a token with a NaN
+ * or infinite logit are unspecified. */
 moe_status_t moe_route(const void* x, const void* w_router, const float* bias, float* logits,
                        int64_t T, int64_t d, int32_t E, int32_t k, int32_t renormalize,
                        moe_dtype_t dt, int32_t* topk_idx, float* topk_gate, moe_stream_t stream);
@@ -122,6 +124,9 @@ moe_status_t moe_grouped_mlp_fwd(const void* x_in, const int32_t* offsets, int32
                                  void* h, void* y, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* Backward of moe_grouped_mlp_fwd (all four steps below, dAB kept in the workspace).
+ * Source: the same expert kernels trained end to end ("Olmo-core DDP MoE examples", "Production
+ * throughput runs": every operating point is a training run, so each expert product has its data
+ * and weight gradient; "Interpreting the eight-layer DDP vs FSDP comparison": sparse expert kernels).
  *   dy [M, d], x_in [M, d], a, b, h [M, f]                INPUT  (dt)
  *   dx_in [M, d]                                          OUTPUT (dt)
  *   dw1, dw3 [G, f, d]; dw2 [G, d, f]                     OUTPUT (dt); a group with no rows
@@ -232,7 +237,9 @@ moe_status_t moe_combine(const void* y_perm, const float* topk_gate, const int32
 /* ------------------------------------------------------------------------------------------ */
 /* Backward                                                                                    */
 
-/* Backward of moe_combine:
+/* Backward of moe_combine: the gradient of its gate-weighted sum of the k routed outputs plus the
+ * shared output.  Source: "Olmo-core DDP MoE examples", "Production throughput runs" (top-k routed
+ * experts plus one shared expert, trained; learned routing, whose gates receive this gradient).
  *   dy_perm[dest_pos[t*k+j]] = topk_gate[t,j] * dout[t]                 OUTPUT [T*k, d] (dt)
  *   dgate[t,j] = <dout[t], y_perm[dest_pos[t*k+j]]> (fp32)              OUTPUT [T, k] or NULL
  * (the shared expert's output gradient is dout itself). */
@@ -240,7 +247,10 @@ moe_status_t moe_combine_bwd(const void* dout, const void* y_perm, const float* 
                              const int32_t* dest_pos, int64_t T, int64_t d, int32_t k,
                              moe_dtype_t dt, void* dy_perm, float* dgate, moe_stream_t stream);
 
-/* Backward of the row gather plus the other contributions to dx:
+/* Backward of the row gather plus the other contributions to dx.  Source: "Olmo-core 3 Opens Large
+ * MoE Training", "Technical Deep Dive" (tokens travel to resident experts, so their gradients
+ * travel back to the tokens); the shared expert and the learned router also read x ("Olmo-core DDP
+ * MoE examples", "Production throughput runs"), whence the two addends.
  *   dx[t] = sum_j dx_perm[dest_pos[t*k+j]] + dx_add0[t] + dx_add1[t]   (fp32 sum)
  *   dx_perm [T*k, d] (dt) INPUT; dx_add0, dx_add1 [T, d] (dt) INPUT or NULL; dx [T, d] OUTPUT */
 moe_status_t moe_permute_bwd(const void* dx_perm, const int32_t* dest_pos, const void* dx_add0,
@@ -380,6 +390,34 @@ moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int6
 
 /* ------------------------------------------------------------------------------------------ */
 /* Utilities                                                                                   */
+
+/* The calls that take a workspace, for moe_workspace_bytes. */
+typedef enum {
+  MOE_OP_ROUTE = 0,           /* none */
+  MOE_OP_PERMUTE = 1,         /* moe_permute */
+  MOE_OP_GROUPED_MLP_FWD = 2, /* moe_grouped_mlp_fwd and the single-set forward stages, routed experts */
+  MOE_OP_GROUPED_MLP_BWD = 3, /* moe_grouped_mlp_bwd (routed experts) */
+  MOE_OP_COMBINE = 4,         /* none */
+  MOE_OP_COMBINE_BWD = 5,     /* none */
+  MOE_OP_PERMUTE_BWD = 6,     /* none */
+  MOE_OP_ROUTE_BWD = 7,       /* moe_route_bwd */
+  MOE_OP_EXPERT_STAGE = 8,    /* moe_expert_stage, any stage, over the routed set and (fs > 0) the
+                                 shared expert as a second set */
+  MOE_OP_ROUTER_AUX = 9,      /* moe_router_aux */
+  MOE_OP_ROUTER_AUX_BWD = 10, /* moe_router_aux_bwd */
+  MOE_OP_MX_GEMM_ROWS = 11,   /* moe_mx_gemm_rows over the routed experts (and the shared expert) */
+  MOE_OP_MX_GEMM_K = 12       /* moe_mx_gemm_k, both weight-gradient products of each set */
+} moe_op_t;
+
+/* Device workspace bytes that call `op` needs in a layer of T tokens of width d, each routed to
+ * k of E experts of hidden width f, plus a shared expert of hidden width fs (0: none) that sees
+ * every token: the routed experts are G = E groups over M = T*k rows, the shared expert one group
+ * over T rows.  Equal to the matching *_workspace_size query (the largest one where the call runs
+ * on both sets); a workspace of this size serves every call of that kind in such a layer.  Returns
+ * 0 for a call that needs none, and 0 with the reason in moe_last_error() for an unknown op or
+ * sizes outside the ranges the calls accept.  Some sizes depend on the compute units of the current
+ * device: query with the device current that will run the call. */
+size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int64_t f, int64_t fs);
 
 const char* moe_status_string(moe_status_t status);
 /* Detail of the last error returned on the calling thread ("" if none). */

@@ -683,4 +683,49 @@ moe_status_t moe_mx_gemm_k(const uint8_t* a_codes, const uint8_t* a_scales, int6
   return hip_check(moe::launch_mx_gemm(MOE_MX_EPI_STORE, true, a, S(stream)), "MXFP8 grouped GEMM (K)");
 }
 
+// ---------------------------------------------------------------------------------------------
+
+size_t moe_workspace_bytes(int32_t op, int64_t T, int64_t d, int32_t E, int32_t k, int64_t f, int64_t fs) {
+  g_err.clear();
+  if (check_tokens(T, d, E, k) != MOE_OK) return 0;
+  if (f <= 0 || fs < 0) {
+    fail(MOE_ERR_INVALID_VALUE, "f must be > 0 and fs >= 0 (got f=%lld, fs=%lld)", (long long)f, (long long)fs);
+    return 0;
+  }
+  const int64_t Tk = T * k;
+  // The routed experts and (fs > 0) the shared expert as expert sets, sizes only.
+  moe_expert_set_t sets[2] = {};
+  sets[0].G = E;
+  sets[0].M = Tk;
+  sets[0].f = f;
+  sets[1].G = 1;
+  sets[1].M = T;
+  sets[1].f = fs;
+  const int nsets = fs > 0 ? 2 : 1;
+  switch (op) {
+    case MOE_OP_ROUTE:
+    case MOE_OP_COMBINE:
+    case MOE_OP_COMBINE_BWD:
+    case MOE_OP_PERMUTE_BWD: return 0;
+    case MOE_OP_PERMUTE: return moe_permute_workspace_size(T, E, k);
+    case MOE_OP_GROUPED_MLP_FWD: return moe_grouped_mlp_fwd_workspace_size(Tk, E, d, f);
+    case MOE_OP_GROUPED_MLP_BWD: return moe_grouped_mlp_bwd_workspace_size(Tk, E, d, f);
+    case MOE_OP_ROUTE_BWD: return moe_route_bwd_workspace_size(T, d, E, k);
+    case MOE_OP_EXPERT_STAGE: return moe_expert_stage_workspace_size(sets, nsets, d);
+    case MOE_OP_ROUTER_AUX: return moe_router_aux_workspace_size(T, E);
+    case MOE_OP_ROUTER_AUX_BWD: return moe_router_aux_bwd_workspace_size(T, d, E);
+    case MOE_OP_MX_GEMM_ROWS: return moe_mx_gemm_workspace_size(E);
+    case MOE_OP_MX_GEMM_K: {
+      size_t need = std::max(moe_mx_gemm_k_workspace_size(E, d, f), moe_mx_gemm_k_workspace_size(E, 2 * f, d));
+      if (fs > 0)
+        need = std::max(need, std::max(moe_mx_gemm_k_workspace_size(1, d, fs),
+                                       moe_mx_gemm_k_workspace_size(1, 2 * fs, d)));
+      return need;
+    }
+    default:
+      fail(MOE_ERR_INVALID_VALUE, "unknown op %d", op);
+      return 0;
+  }
+}
+
 }  // extern "C"

@@ -27,6 +27,20 @@ MOE_STAGE_GATE_UP_DGRAD = 3
 MOE_STAGE_DOWN_WGRAD = 4
 MOE_STAGE_GATE_UP_WGRAD = 5
 
+MOE_OP_ROUTE = 0
+MOE_OP_PERMUTE = 1
+MOE_OP_GROUPED_MLP_FWD = 2
+MOE_OP_GROUPED_MLP_BWD = 3
+MOE_OP_COMBINE = 4
+MOE_OP_COMBINE_BWD = 5
+MOE_OP_PERMUTE_BWD = 6
+MOE_OP_ROUTE_BWD = 7
+MOE_OP_EXPERT_STAGE = 8
+MOE_OP_ROUTER_AUX = 9
+MOE_OP_ROUTER_AUX_BWD = 10
+MOE_OP_MX_GEMM_ROWS = 11
+MOE_OP_MX_GEMM_K = 12
+
 MOE_MX_EPI_STORE = 0
 MOE_MX_EPI_SWIGLU = 1
 MOE_MX_EPI_SWIGLU_BWD = 2
@@ -87,6 +101,7 @@ _SIGS = {
                                 _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mx_gemm_k_workspace_size": (_SZ, [_I32, _I64, _I64]),
     "moe_mx_gemm_k": (_I32, [_P, _P, _I64, _P, _P, _I64, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "moe_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I32, _I32, _I64, _I64]),
     "moe_status_string": (_c.c_char_p, [_I32]),
     "moe_last_error": (_c.c_char_p, []),
     "moe_version": (_c.c_char_p, []),
@@ -164,6 +179,10 @@ def dtype_code(t: torch.Tensor) -> int:
 def moe_route(x, w_router, bias, logits, T, d, E, k, renormalize, dt, topk_idx, topk_gate, stream=None):
     _call("moe_route", _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits), T, d, E, k, renormalize, dt,
           _ptr(topk_idx), _ptr(topk_gate), _stream(stream))
+
+
+def moe_workspace_bytes(op, T, d, E, k, f, fs=0) -> int:
+    return lib().moe_workspace_bytes(op, T, d, E, k, f, fs)
 
 
 def moe_permute_workspace_size(T, E, k) -> int:

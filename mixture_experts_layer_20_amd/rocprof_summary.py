@@ -6,17 +6,19 @@ Inputs (all written by rocprofv3 with --output-format csv):
   <pmc dir>/run_counter_collection.csv                      from  --pmc WRITE_SIZE  (one pass)
   <pmc dir>/run_counter_collection.csv                      from  --pmc <other counters>
                                                             (optional, --pmc, repeatable)
-The bench run must include `--copy-probe-mb N`: one plain device copy of N MiB whose counter
+The bench runs must include `--copy-probe-mb N`: one plain device copy of N MiB whose counter
 readings calibrate FETCH_SIZE / WRITE_SIZE (KiB per dispatch) to bytes.
 
-Each GEMM stage of a layer step is one launch covering the routed experts and the shared expert
-(--sets-per-stage 1, the default), or two launches, routed then shared (--sets-per-stage 2, a
-bench run with --no-merge); dispatches are labelled by that order.
+Every kernel of the layer is attributed to the library call (stage) that launches it.  Each grouped
+GEMM stage is one launch over the routed experts and the shared expert (a split weight-gradient
+reduction adds a reduce launch).  Per stage: launch durations from the trace, HBM bytes per launch
+from the counters, and the algorithmic work (FLOPs of the GEMM stages, bytes of the
+bandwidth-bound ones) of the workload.
 
 Usage:
-  python -m mixture_experts_layer_20_amd.rocprof_summary --trace T --fetch F --write W \
-      --workload tiny64e_random --copy-mb 256 --command "<the rocprofv3 commands>" \
-      --out profiles/<name>.md [--traffic-json profiles/traffic.json]
+  python -m mixture_experts_layer_20_amd.rocprof_summary --trace T [--fetch F --write W] \
+      --workload large_e128 --copy-mb 256 --command "<the rocprofv3 commands>" \
+      --out profiles/<name>.md [--traffic-json profiles/traffic.json] [--pmc P ...]
 """
 from __future__ import annotations
 
@@ -27,12 +29,28 @@ import hashlib
 import json
 import os
 import re
+import sys
 
 MODES = ["gate_up_fwd", "down_fwd", "down_bwd", "gate_up_dgrad", "down_wgrad", "gate_up_wgrad"]
 PKG = os.path.dirname(os.path.abspath(__file__))
-
+ROOT = os.path.dirname(PKG)
 
 GEMM_SOURCES = ("common.h", "gemm_common.h", "grouped_gemm.hip", "grouped_gemm_pipe.hip")
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+SIMDS = 1024   # 256 CUs x 4
+
+# kernel name pattern -> stage (library call) that launches it; first match wins
+STAGE_OF = [
+    (r"router_logits|topk_gate", "route"),
+    (r"local_rank|scan_lds|scan_kernel|scatter_gather|rank_scan", "permute"),
+    (r"combine_bwd_kernel", "combine_bwd"),
+    (r"combine_kernel", "combine"),
+    (r"route_dl|route_dx|route_dw|seg_prefix", "route_bwd"),
+    (r"permute_bwd_kernel", "permute_bwd"),
+    (r"aux_", "router_aux"),
+    (r"mx_", "mxfp8"),
+]
 
 
 def kernel_source_sha() -> str:
@@ -43,6 +61,21 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def gemm_mode(name: str) -> str | None:
+    m = re.search(r"(?:grouped_gemm_(?:bf16|bf16_dma|pipe|f32)|splitk_reduce)<(\d)[,>]", name)
+    return MODES[int(m.group(1))] if m else None
+
+
+def stage_of(name: str) -> str | None:
+    mode = gemm_mode(name)
+    if mode:
+        return mode
+    for pat, st in STAGE_OF:
+        if re.search(pat, name):
+            return st
+    return None
+
+
 def short_name(name: str) -> str:
     m = re.search(r"grouped_gemm_bf16<(\d), [^>]*Cfg<(\d+), (\d+), (\d), (\d)>", name)
     if m:
@@ -51,34 +84,13 @@ def short_name(name: str) -> str:
     if m:
         epi = "wgrad" if m.group(3) == "true" else ("store", "swiglu", "swiglu_bwd")[int(m.group(2))]
         sw = f", {m.group(4)}-byte scales" if m.group(4) else ""
-        return f"{m.group(1).replace('_kernel', '')}[{epi}{sw}]"
+        return f"{m.group(1)}[{epi}{sw}]"
     m = re.search(r"(grouped_gemm_pipe|grouped_gemm_bf16_dma|splitk_reduce)<(\d)>", name)
     if m:
         return f"{m.group(1)}[{MODES[int(m.group(2))]}]"
     n = re.sub(r"void |moe::|\(anonymous namespace\)::", "", name)
     n = re.sub(r"\(.*", "", n)
     return n.strip()
-
-
-def gemm_mode(name: str) -> str | None:
-    m = re.search(r"grouped_gemm_(?:bf16|bf16_dma|pipe|f32)<(\d)[,>]", name)
-    return MODES[int(m.group(1))] if m else None
-
-
-def labelled_dispatches(rows, name_key, id_key, sets_per_stage=1):
-    """Label GEMM dispatches by expert set: 'routed+shared' (one launch per stage) or
-    'routed'/'shared' by their order within a step."""
-    seen = collections.Counter()
-    out = []
-    for r in sorted(rows, key=lambda r: int(r[id_key])):
-        n = r[name_key]
-        mode = gemm_mode(n)
-        label = None
-        if mode:
-            label = "routed+shared" if sets_per_stage == 1 else ("routed", "shared")[seen[n] % 2]
-            seen[n] += 1
-        out.append((r, mode, label))
-    return out
 
 
 def copy_scale(pmc_csv: str, counter: str, copy_mb: int) -> float | None:
@@ -89,44 +101,53 @@ def copy_scale(pmc_csv: str, counter: str, copy_mb: int) -> float | None:
     return copy_mb * 1024.0 / (sum(vals) / len(vals))
 
 
-def per_stage_counter(pmc_csv: str, counter: str, sets_per_stage: int):
-    rows = [r for r in csv.DictReader(open(pmc_csv)) if r["Counter_Name"] == counter]
+def per_kernel_counter(pmc_csv: str, counter: str):
+    """Mean of a counter per launch of each kernel (short name)."""
     acc = collections.defaultdict(list)
-    for r, mode, label in labelled_dispatches(rows, "Kernel_Name", "Dispatch_Id", sets_per_stage):
-        if mode:
-            acc[(mode, label)].append(float(r["Counter_Value"]))
+    for r in csv.DictReader(open(pmc_csv)):
+        if r["Counter_Name"] == counter:
+            acc[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-SIMDS = 1024   # 256 CUs x 4
+def algorithmic(workload: str):
+    """FLOPs of each GEMM stage and bytes of each bandwidth-bound stage of one step (bench.py's
+    formulas, imported so the two cannot drift apart)."""
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench
+    from mixture_experts_layer_20_amd import inputs as I
+    cfg = I.CONFIGS[workload]
+    return bench.stage_flops(cfg), bench.stage_bytes(cfg)
 
 
-def counter_section(dirs, durs, sets_per_stage):
-    """Per-stage means of every counter of the extra passes, plus the L2 hit rate and the MFMA
-    busy cycles per SIMD per second of the stage."""
+def counter_section(dirs, kdur):
+    """Mean per launch of every counter of the extra passes, per kernel, plus the L2 hit rate and
+    the MFMA busy cycles per SIMD per second of the launch."""
     vals = collections.defaultdict(dict)
     names = []
     for d in dirs:
         path = os.path.join(d, "run_counter_collection.csv")
         for c in sorted({r["Counter_Name"] for r in csv.DictReader(open(path))}):
             names.append(c)
-            for key, v in per_stage_counter(path, c, sets_per_stage).items():
-                vals[key][c] = v
-    out = ["", "## Grouped GEMM stages: cache and issue counters (mean per launch)", "",
-           "| stage | expert set | " + " | ".join(names) + " | L2 hit % | MFMA busy G cycles/s per SIMD |",
-           "|---|---|" + "---:|" * (len(names) + 2)]
-    for key in sorted(vals, key=lambda k: (MODES.index(k[0]), k[1])):
-        v = vals[key]
-        dur = sum(durs[key]) / len(durs[key]) * 1e-6 if durs.get(key) else float("nan")
+            for k, v in per_kernel_counter(path, c).items():
+                vals[k][c] = v
+    out = ["", "## Cache and issue counters (mean per launch)", "",
+           "| kernel | " + " | ".join(names) + " | L2 hit % | MFMA busy G cycles/s per SIMD |",
+           "|---|" + "---:|" * (len(names) + 2)]
+    for k in sorted(vals, key=lambda k: -kdur.get(k, 0.0)):
+        v = vals[k]
+        dur = kdur.get(k, float("nan")) * 1e-6
         hit = miss = float("nan")
         if "TCC_HIT_sum" in v and "TCC_MISS_sum" in v:
             hit, miss = v["TCC_HIT_sum"], v["TCC_MISS_sum"]
         rate = v.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / SIMDS / dur / 1e9
-        out.append(f"| {key[0]} | {key[1]} | " + " | ".join(f"{v.get(c, float('nan')):.4g}" for c in names)
-                   + f" | {100.0 * hit / (hit + miss):.1f} | {rate:.3f} |")
+        hitp = 100.0 * hit / (hit + miss) if hit + miss > 0 else float("nan")
+        out.append(f"| {k} | " + " | ".join(f"{v.get(c, float('nan')):.4g}" for c in names)
+                   + f" | {hitp:.1f} | {rate:.3f} |")
     out += ["", "L2 hit % = TCC_HIT / (TCC_HIT + TCC_MISS). MFMA busy rate = SQ_VALU_MFMA_BUSY_CYCLES per SIMD "
-            f"({SIMDS} SIMDs) over the stage's trace duration: divided by the shader clock it is the share of "
-            "time the matrix unit was busy (0.35 of 2.4 GHz, 0.41 of 2.06 GHz for 0.85)."]
+            f"({SIMDS} SIMDs) over the launch's trace duration: divided by the shader clock it is the share of "
+            "time the matrix unit was busy."]
     return out
 
 
@@ -140,62 +161,97 @@ def main(argv=None) -> int:
     ap.add_argument("--command", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json")
-    ap.add_argument("--sets-per-stage", type=int, choices=(1, 2), default=1)
     ap.add_argument("--pmc", action="append", default=[],
                     help="a further counter pass (cache and issue counters), repeatable")
     a = ap.parse_args(argv)
 
     stats = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_stats.csv"))))
     trace = list(csv.DictReader(open(os.path.join(a.trace, "run_kernel_trace.csv"))))
-    # per-stage durations from the trace
-    durs = collections.defaultdict(list)
-    for r, mode, label in labelled_dispatches(trace, "Kernel_Name", "Dispatch_Id", a.sets_per_stage):
-        if mode:
-            durs[(mode, label)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    if not (a.fetch and a.write):
-        lines = [f"# rocprofv3 summary: kernels of one layer step, workload {a.workload}", "",
-                 "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", "",
-                 "## Kernel statistics (--kernel-trace --stats)", "",
-                 "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
-        for r in stats:
-            lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                         f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-        open(a.out, "w").write("\n".join(lines) + "\n")
-        print("\n".join(lines))
-        return 0
-    fcsv = os.path.join(a.fetch, "run_counter_collection.csv")
-    wcsv = os.path.join(a.write, "run_counter_collection.csv")
-    fs = copy_scale(fcsv, "FETCH_SIZE", a.copy_mb)
-    ws = copy_scale(wcsv, "WRITE_SIZE", a.copy_mb)
-    fetch = per_stage_counter(fcsv, "FETCH_SIZE", a.sets_per_stage)
-    write = per_stage_counter(wcsv, "WRITE_SIZE", a.sets_per_stage)
+    kd = collections.defaultdict(list)      # short kernel name -> launch durations (us)
+    kstage = {}
+    for r in trace:
+        n = short_name(r["Kernel_Name"])
+        kd[n].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        kstage[n] = stage_of(r["Kernel_Name"])
+    kdur = {k: sum(v) / len(v) for k, v in kd.items()}
+    flops, hbm_bytes = algorithmic(a.workload)
 
-    lines = [f"# rocprofv3 summary: grouped GEMM and other kernels, workload {a.workload}", "",
+    lines = [f"# rocprofv3 summary: kernels of the layer step, workload {a.workload}", "",
              "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", "",
              f"grouped-GEMM sources ({', '.join(GEMM_SOURCES)}) sha256[:16] = {kernel_source_sha()}", "",
              "## Kernel statistics (--kernel-trace --stats)", "",
-             "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+             "| kernel | stage | calls | avg us | total us | % |", "|---|---|---:|---:|---:|---:|"]
     for r in stats:
-        lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        n = short_name(r["Name"])
+        lines.append(f"| {n} | {kstage.get(n) or '-'} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-    lines += ["", "## Grouped GEMM stages: duration and HBM traffic per launch", "",
-              f"Counter calibration with a plain {a.copy_mb} MiB device copy: FETCH_SIZE x{fs:.3f}, "
-              f"WRITE_SIZE x{ws:.3f} (KiB per dispatch -> bytes = KiB x 1024 x factor).", "",
-              "| stage | expert set | avg us (trace) | HBM read MB | HBM write MB |",
-              "|---|---|---:|---:|---:|"]
+
+    # The GEMM launches: the grouped GEMM kernel of each stage (its split reduce listed apart).
+    gemm_k = {k: s for k, s in kstage.items() if s in MODES and not k.startswith("splitk_reduce")}
+    lines += ["", "## Grouped GEMM launches (one per stage: routed experts + shared expert)", "",
+              "| stage | kernel | avg us | algorithmic TFLOP | TFLOP/s | of 2.5 PFLOP/s bf16 |",
+              "|---|---|---:|---:|---:|---:|"]
+    best = None
+    for k, s in sorted(gemm_k.items(), key=lambda kv: MODES.index(kv[1])):
+        if s not in flops:
+            continue
+        rate = flops[s] / (kdur[k] * 1e-6) / 1e12
+        lines.append(f"| {s} | {k} | {kdur[k]:.1f} | {flops[s] / 1e12:.3f} | {rate:.1f} | {rate / PEAK_BF16_TFLOPS:.3f} |")
+        if best is None or kdur[k] > kdur[best[0]]:
+            best = (k, s, rate)
+    if best:
+        lines += ["", f"Dominant kernel (longest launch): {best[0]} ({best[1]}), {kdur[best[0]]:.1f} us, "
+                      f"{best[2]:.1f} TFLOP/s = {best[2] / PEAK_BF16_TFLOPS:.3f} of the bf16 peak."]
+
     traffic = {}
-    for key in sorted(durs, key=lambda k: (MODES.index(k[0]), k[1])):
-        d = sum(durs[key]) / len(durs[key])
-        rd = fetch.get(key, float("nan")) * 1024 * (fs or 1)
-        wr = write.get(key, float("nan")) * 1024 * (ws or 1)
-        lines.append(f"| {key[0]} | {key[1]} | {d:.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
-        stage = "shared_" + key[0] if key[1] == "shared" else key[0]
-        traffic[stage] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
-                          "avg_us_trace": d, "kernel_source_sha": kernel_source_sha()}
+    if a.fetch and a.write:
+        fcsv = os.path.join(a.fetch, "run_counter_collection.csv")
+        wcsv = os.path.join(a.write, "run_counter_collection.csv")
+        fs = copy_scale(fcsv, "FETCH_SIZE", a.copy_mb)
+        ws = copy_scale(wcsv, "WRITE_SIZE", a.copy_mb)
+        fetch = per_kernel_counter(fcsv, "FETCH_SIZE")
+        write = per_kernel_counter(wcsv, "WRITE_SIZE")
+        lines += ["", "## HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "",
+                  f"Calibration with a plain {a.copy_mb} MiB device copy: FETCH_SIZE x{fs:.3f}, "
+                  f"WRITE_SIZE x{ws:.3f} (KiB per dispatch -> bytes = KiB x 1024 x factor).", "",
+                  "| kernel | stage | avg us | read MB | write MB | GB/s (counters) | of 8 TB/s |",
+                  "|---|---|---:|---:|---:|---:|---:|"]
+        per_stage = collections.defaultdict(lambda: [0.0, 0.0, 0.0])   # us, read, write per step-call
+        for k in sorted(kdur, key=lambda k: -kdur[k]):
+            st = kstage.get(k)
+            if st is None or k not in fetch:
+                continue
+            rd = fetch[k] * 1024 * (fs or 1)
+            wr = write.get(k, float("nan")) * 1024 * (ws or 1)
+            gbs = (rd + wr) / (kdur[k] * 1e-6) / 1e9
+            lines.append(f"| {k} | {st} | {kdur[k]:.1f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {gbs:.0f} | "
+                         f"{gbs / PEAK_HBM_GBS:.3f} |")
+            if st in hbm_bytes or st in MODES:
+                # launches per call of the stage: GEMM stages and the data-movement calls launch
+                # each of their kernels once per call
+                ps = per_stage[st]
+                ps[0] += kdur[k]
+                ps[1] += rd
+                ps[2] += wr
+        lines += ["", "## Bandwidth-bound stages: counters against the algorithmic bytes", "",
+                  "| stage | kernels us | counter MB | algorithmic MB | ratio | GB/s (algorithmic) | of 8 TB/s |",
+                  "|---|---:|---:|---:|---:|---:|---:|"]
+        for st in ("permute", "combine", "combine_bwd", "permute_bwd"):
+            if st in per_stage and st in hbm_bytes:
+                us, rd, wr = per_stage[st]
+                alg = hbm_bytes[st]
+                gbs = alg / (us * 1e-6) / 1e9
+                lines.append(f"| {st} | {us:.1f} | {(rd + wr) / 1e6:.1f} | {alg / 1e6:.1f} | {(rd + wr) / alg:.2f} | "
+                             f"{gbs:.0f} | {gbs / PEAK_HBM_GBS:.3f} |")
+        for k, s in gemm_k.items():
+            rd = fetch.get(k, 0.0) * 1024 * (fs or 1)
+            wr = write.get(k, 0.0) * 1024 * (ws or 1)
+            traffic[s] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                          "avg_us_trace": kdur[k], "kernel_source_sha": kernel_source_sha()}
     if a.pmc:
-        lines += counter_section(a.pmc, durs, a.sets_per_stage)
+        lines += counter_section(a.pmc, kdur)
     open(a.out, "w").write("\n".join(lines) + "\n")
-    if a.traffic_json:
+    if a.traffic_json and traffic:
         allt = json.load(open(a.traffic_json)) if os.path.exists(a.traffic_json) else {}
         allt[a.workload] = traffic
         json.dump(allt, open(a.traffic_json, "w"), indent=1, sort_keys=True)

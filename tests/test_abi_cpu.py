@@ -189,3 +189,35 @@ def test_misaligned_pointers_are_rejected(lib):
             FAKE, 8, 512, 256, 256, L.MOE_MX_EPI_STORE, FAKE, None, None, None, None, None, None, FAKE, mws)
     _expect(L.MOE_ERR_INVALID_VALUE, L.moe_mx_gemm_k, FAKE, FAKE, 512, FAKE + 16 + 4, FAKE, 512, FAKE, 8, 256, 256,
             256, FAKE, None, FAKE, 1 << 30)
+
+
+def test_workspace_bytes_equals_each_calls_own_query(lib):
+    T, d, E, k, f, fs = 512, 256, 8, 2, 128, 256
+    Tk = T * k
+    sets = [L.expert_set(None, E, Tk, f), L.expert_set(None, 1, T, fs)]
+    want = {
+        L.MOE_OP_ROUTE: 0, L.MOE_OP_COMBINE: 0, L.MOE_OP_COMBINE_BWD: 0, L.MOE_OP_PERMUTE_BWD: 0,
+        L.MOE_OP_PERMUTE: L.moe_permute_workspace_size(T, E, k),
+        L.MOE_OP_GROUPED_MLP_FWD: L.moe_grouped_mlp_fwd_workspace_size(Tk, E, d, f),
+        L.MOE_OP_GROUPED_MLP_BWD: L.moe_grouped_mlp_bwd_workspace_size(Tk, E, d, f),
+        L.MOE_OP_ROUTE_BWD: L.moe_route_bwd_workspace_size(T, d, E, k),
+        L.MOE_OP_EXPERT_STAGE: L.moe_expert_stage_workspace_size(sets, d),
+        L.MOE_OP_ROUTER_AUX: L.moe_router_aux_workspace_size(T, E),
+        L.MOE_OP_ROUTER_AUX_BWD: L.moe_router_aux_bwd_workspace_size(T, d, E),
+        L.MOE_OP_MX_GEMM_ROWS: L.moe_mx_gemm_workspace_size(E),
+        L.MOE_OP_MX_GEMM_K: max(L.moe_mx_gemm_k_workspace_size(E, d, f), L.moe_mx_gemm_k_workspace_size(E, 2 * f, d),
+                                L.moe_mx_gemm_k_workspace_size(1, d, fs), L.moe_mx_gemm_k_workspace_size(1, 2 * fs, d)),
+    }
+    for op, n in want.items():
+        assert L.moe_workspace_bytes(op, T, d, E, k, f, fs) == n, op
+    for op in (L.MOE_OP_PERMUTE, L.MOE_OP_GROUPED_MLP_BWD, L.MOE_OP_ROUTE_BWD, L.MOE_OP_EXPERT_STAGE):
+        assert want[op] > 0, op
+    # without a shared expert the stage query covers the routed set alone
+    assert L.moe_workspace_bytes(L.MOE_OP_EXPERT_STAGE, T, d, E, k, f, 0) == \
+        L.moe_expert_stage_workspace_size(sets[:1], d)
+    # unknown op and invalid sizes: 0, with the reason
+    assert L.moe_workspace_bytes(99, T, d, E, k, f, fs) == 0
+    assert b"unknown op" in lib.moe_last_error()
+    assert L.moe_workspace_bytes(L.MOE_OP_PERMUTE, T, d, E, 0, f, fs) == 0
+    assert L.moe_workspace_bytes(L.MOE_OP_PERMUTE, T, d, E, k, 0, fs) == 0
+    assert L.moe_workspace_bytes(L.MOE_OP_PERMUTE, T, d, E, k, f, -1) == 0

@@ -4,30 +4,35 @@
 // Tokens are moved to experts that stay resident ("Olmo-core 3 Opens Large MoE Training",
 // "Technical Deep Dive"); each expert's rows form one ragged group of the grouped GEMM.
 //
-// Design (one workgroup = 256x256 output tile, 4 waves in a 2x2 grid, 128x128 per wave):
-//  * K is consumed 32 at a time ("K step") through a ring of four 32 KiB LDS stages that global
-//    loads fill directly (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l).  The
-//    loads form one continuous stream over all tiles of the workgroup: the stage four steps
-//    ahead is issued as soon as a slot frees up, also across tile boundaries, so the next tile's
-//    first stages are in flight during the current tile's epilogue.
-//  * An operand that is K-contiguous in memory is kept [row][32 k] in LDS (64-byte rows, 16-byte
-//    chunks XOR-swizzled) and read with ds_read_b128.  An operand that is K-strided (weights in
-//    dgrad, activations in wgrad) is kept [32 k][256 rows] (512-byte rows, 64-byte windows
-//    XOR-swizzled by k) and read with ds_read_b64_tr_b16, which hands each lane 4 consecutive k
-//    of one column: two such reads form a 32x32x16 MFMA operand.  No transposition pass.
-//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators (256 per lane, in AGPRs).
-//  * One wave per SIMD, so the wave's own instruction order decides how well the matrix core is
-//    fed: each K step is two phases of 16 MFMAs, and every LDS fragment read and every global
-//    load is placed between two MFMAs (scheduling barriers pin the order).  One s_barrier per K
-//    step, between the phases.  LDS reads are inline assembly with explicit lgkmcnt waits and the
-//    ring is governed by explicit vmcnt waits (the compiler's own waits would drain every load in
-//    flight before each LDS access).
+// Design (one workgroup = 256x256 output tile, 8 waves in a 2x4 grid, 128x64 per wave):
+//  * K is consumed 64 at a time ("K step") through two 64 KiB LDS stages that global loads fill
+//    directly (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l).  The loads form one
+//    continuous stream over all tiles of the workgroup: a stage is refilled with the stage two steps
+//    ahead as soon as every wave has read it, also across tile boundaries, so the next tile's first
+//    stages are in flight during the current tile's epilogue.
+//  * The vector memory path of a CU keeps a limited number of cache-line requests in flight, so the
+//    operand stream runs at (lines in flight x bytes per request) / latency.  A K-contiguous operand
+//    row of a 64-deep stage is 128 bytes, one whole line per request (a 32-deep stage requested half
+//    lines and streamed at half the rate).  Such an operand is kept [row][64 k] in LDS (128-byte
+//    rows, 16-byte chunks XOR-swizzled) and read with ds_read_b128.  An operand that is K-strided
+//    (weights in dgrad, activations in wgrad) is kept [64 k][256 rows] (512-byte rows, 64-byte
+//    windows XOR-swizzled by k) and read with ds_read_b64_tr_b16, which hands each lane 4 consecutive
+//    k of one column: two such reads form a 32x32x16 MFMA operand.  No transposition pass.
+//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators (128 per lane, in AGPRs).
+//  * Two waves per SIMD (one per row half), so one can feed the matrix core while the other waits
+//    on a load issue, a fragment read or the barrier.  A K step is four phases of 8 MFMAs (one per
+//    16-deep substep); every LDS fragment read and every global load is placed between two MFMAs
+//    (scheduling barriers pin the order).  One s_barrier per K step, before the last phase, which
+//    issues the stage loads.  LDS reads are inline assembly with explicit lgkmcnt waits and the ring
+//    is governed by explicit vmcnt waits (the compiler's own waits would drain every load in flight
+//    before each LDS access).
 //  * Epilogue straight from the accumulators: a v_permlane32_swap gives each lane 8 consecutive
 //    columns of one row, the mode's elementwise math (SwiGLU, SwiGLU backward, whose A/B stash is
-//    loaded in the same layout two blocks ahead) is applied and 16-byte bf16 stores go out.
+//    loaded in the same layout a block ahead) is applied and 16-byte bf16 stores go out.
 //  * Persistent grid, per-expert tile prefix computed in-kernel, tiles dealt so each XCD walks one
-//    contiguous run (workgroup b runs on XCD b % 8); an XCD's last round of tiles, when it would
-//    keep at most half of its workgroups busy, is dealt as 128-row half tiles.
+//    contiguous run of each expert set (workgroup b runs on XCD b % 8); an XCD's last round of
+//    tiles, when it would keep at most half of its workgroups busy, is dealt as 128-row half tiles,
+//    whose second row half of waves issues its loads but no MFMAs.
 #include "common.h"
 #include "gemm_common.h"
 
@@ -38,12 +43,18 @@ namespace {
 
 using namespace gemm;
 
-constexpr int BM = 256, BN = 256, BKS = 32, NSTAGE = 4, NTH = 256, WGM = 2, WGN = 2, MI = 4, NI = 4;
-constexpr int OPB = 256 * BKS * 2;         // one operand tile of one stage: 16 KiB
-constexpr int STAGE = 2 * OPB;             // 32 KiB
+constexpr int BM = 256, BN = 256, BKS = 64, NSTAGE = 2;
+constexpr int NW = 8, NTH = 64 * NW;  // two waves per SIMD
+constexpr int WGN = 4;                // wave w: row half wm = w / WGN, column quarter wn = w % WGN
+constexpr int MI = 4, NI = 2;         // 32x32 blocks per wave: 128 rows x 64 columns
+constexpr int LPW = 64 / NW;          // direct loads (1 KiB each) per wave per 64 KiB stage
+constexpr int LPO = LPW / 2;          // of them per operand
+constexpr int OPB = 256 * BKS * 2;         // one operand tile of one stage: 32 KiB
+constexpr int STAGE = 2 * OPB;             // 64 KiB
 constexpr int LDS_BYTES = NSTAGE * STAGE;  // 128 KiB
 constexpr int PMAXG = 1024;   // groups of the first set
 constexpr int PMAXG1 = 64;    // groups of the second set (the shared expert: 1)
+constexpr int WG_NB = 8;      // tile columns per block of the weight-gradient tile order
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -67,18 +78,19 @@ __device__ __forceinline__ int lds_load_i32(uint32_t addr) {
   return v;
 }
 
-// ---- K-contiguous operand: [256 rows][32 k], 64-byte rows; chunk swizzle (row >> 2) & 3 makes
-// 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int kc_swz(int row) { return (row >> 2) & 3; }
+// ---- K-contiguous operand: [256 rows][64 k], 128-byte rows (each 128-byte row segment is one
+// whole cache line of the source, loaded by 8 lanes of one instruction); chunk swizzle
+// (row >> 1) & 7 makes 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kc_swz(int row) { return (row >> 1) & 7; }
 
-// ---- K-strided operand: [32 k][256 columns], 512-byte rows; 64-byte window w of row k is stored
+// ---- K-strided operand: [64 k][256 columns], 512-byte rows; 64-byte window w of row k is stored
 // at window w ^ (k & 3) (within its 256-byte half), so the 4 k-rows of one transposed read hit
 // distinct bank groups.
 __device__ __forceinline__ int mc_phys_chunk(int k, int chunk) { return chunk ^ ((k & 3) << 2); }
 
 // ---- Tiles -------------------------------------------------------------------------------
 // Output tile: set seg, group g, rows [m0, min(m0 + 256, m_end)), tile column nt, K range
-// [k_begin, k_end) in nk steps of 32 (split: K chunk index of a split weight gradient; ks: the
+// [k_begin, k_end) in nk steps of 64 (split: K chunk index of a split weight gradient; ks: the
 // split count).  half: at most 128 rows remain (ragged M only), multiplied as a 128x256 tile.
 struct Tile {
   int seg, g, m0, m_end, nt, k_begin, k_end, nk, split, ks;
@@ -181,10 +193,20 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
     t.k_begin = 0;
     t.k_end = mode_K(MODE, p.d, p.f);
   } else {
-    t.nt = L % NT;
-    int r = L / NT;
-    const int mt = r % MT;
-    r /= MT;
+    int r = L / (MT * NT);
+    const int idx = L - r * (MT * NT);
+    // Inside one (group, split): blocks of WG_NB tile columns, walked row tile by row tile, so an
+    // XCD's round of workgroups covers a compact block of the expert's gradient and the next round
+    // reuses its column operand (wide gradients: 16 tile columns at d = 4096).
+    int mt;
+    if (NT > WG_NB && NT % WG_NB == 0) {
+      const int jb = idx / (MT * WG_NB), rem = idx - jb * (MT * WG_NB);
+      mt = rem / WG_NB;
+      t.nt = jb * WG_NB + (rem - mt * WG_NB);
+    } else {
+      t.nt = idx % NT;
+      mt = idx / NT;
+    }
     t.split = r % ksplit;
     t.g = r / ksplit;
     t.m0 = mt * BM;
@@ -214,19 +236,19 @@ __device__ __forceinline__ Tile deal_tile(const GemmArgs& p, const SegGeo (&geo)
 }
 
 // ---- Direct loads ------------------------------------------------------------------------
-// Load IDX (0..3: operand A, 4..7: operand B) of the stage starting at k0 of tile t: 16 bytes per
-// lane into LDS slot q = (wave * 4 + j) * 64 + lane of the operand tile.
-// KC: slot q = (row q/4, physical chunk q%4).  MC: slot q = (k q/32, physical chunk q%32).
+// Load IDX (below LPO: operand A, else operand B) of the stage starting at k0 of tile t: 16 bytes
+// per lane into LDS slot q = (wave * LPO + j) * 64 + lane of the operand tile.
+// KC: slot q = (row q/8, physical chunk q%8).  MC: slot q = (k q/32, physical chunk q%32).
 template <int MODE, int IDX>
 __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const Tile& t, int k0, int wave, int lane) {
-  constexpr bool A_OP = IDX < 4;
-  constexpr int j = IDX & 3;
+  constexpr bool A_OP = IDX < LPO;
+  constexpr int j = IDX % LPO;
   constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
-  const int q = (wave * 4 + j) * 64 + lane;
+  const int q = (wave * LPO + j) * 64 + lane;
   const bf16_t* src;
   if constexpr (kc) {
-    const int row = q >> 2;
-    const int kk = k0 + (((q & 3) ^ kc_swz(row)) << 3);
+    const int row = q >> 3;
+    const int kk = k0 + (((q & 7) ^ kc_swz(row)) << 3);
     if constexpr (A_OP) {
       src = a_ptr_kc<MODE, bf16_t>(p, min(t.m0 + row, t.m_end - 1), kk);
     } else {
@@ -243,8 +265,8 @@ __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const
       src = reinterpret_cast<const bf16_t*>(g_zero_rows);
     }
   }
-  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * 4 + j) * 1024), 16,
-                                   0, 0);
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * LPO + j) * 1024),
+                                   16, 0, 0);
 }
 
 // Loads inside the K loop: source = wave-uniform stage base + per-lane 32-bit byte offset.  The
@@ -252,12 +274,12 @@ __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const
 // carry k0 and the tile position.
 template <int MODE>
 __device__ __forceinline__ uint32_t load_offset(const GemmArgs& p, const Tile& t, int idx, int wave, int lane) {
-  const bool a_op = idx < 4;
-  const int q = (wave * 4 + (idx & 3)) * 64 + lane;
+  const bool a_op = idx < LPO;
+  const int q = (wave * LPO + idx % LPO) * 64 + lane;
   const bool kc = a_op ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
   if (kc) {
-    const int row = q >> 2;
-    const uint32_t c16 = (uint32_t)(((q & 3) ^ kc_swz(row)) << 4);
+    const int row = q >> 3;
+    const uint32_t c16 = (uint32_t)(((q & 7) ^ kc_swz(row)) << 4);
     if (a_op) {
       const int K = mode_K(MODE, p.d, p.f);
       return (uint32_t)(min(t.m0 + row, t.m_end - 1) - t.m0) * (uint32_t)K * 2u + c16;
@@ -274,6 +296,33 @@ __device__ __forceinline__ uint32_t load_offset(const GemmArgs& p, const Tile& t
   return ((uint32_t)kr * stride + col) * 2u;
 }
 
+// Per-lane byte offsets of a wave's loads from the stage bases.  Only the K-contiguous A operand
+// (rows clamped at the group end) needs one per load; load j of any other operand is its first
+// load's offset plus j times a wave-uniform step, with the swizzle change of odd j applied as an
+// XOR (issue_fast).
+struct LoadOffs {
+  uint32_t a[LPO];
+  uint32_t b;
+  uint32_t sa, sb;   // steps (bytes) between consecutive loads of A (not K-contiguous) and of B
+};
+
+// Step between consecutive loads of a wave (load j covers 8 K-contiguous rows, or 2 K rows of a
+// K-strided operand, after load j - 1).
+template <int MODE, bool A_OP>
+__device__ __forceinline__ uint32_t load_step(const GemmArgs& p) {
+  constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
+  uint32_t ld;   // elements per row (KC) or per K row (MC) of the operand
+  if constexpr (A_OP) {
+    if constexpr (kc) ld = mode_K(MODE, p.d, p.f);
+    else ld = MODE == GEMM_DOWN_WGRAD ? p.d : 2 * p.f;
+  } else if constexpr (kc) {
+    ld = MODE == GEMM_UP_FWD ? p.d : p.f;
+  } else {
+    ld = (MODE == GEMM_DOWN_BWD || MODE == GEMM_DOWN_WGRAD) ? p.f : p.d;
+  }
+  return kc ? 16u * ld : 4u * ld;
+}
+
 // Wave-uniform byte bases of operands A and B for the stage starting at k0.
 template <int MODE>
 __device__ __forceinline__ void stage_bases(const GemmArgs& p, const Tile& t, int k0, int wave, const char*& sa,
@@ -283,7 +332,9 @@ __device__ __forceinline__ void stage_bases(const GemmArgs& p, const Tile& t, in
   const size_t d = p.d, f = p.f, g = t.g;
   if constexpr (MODE == GEMM_UP_FWD) {
     sa = a + ((size_t)t.m0 * d + k0) * 2;
-    sb = reinterpret_cast<const char*>(wave < 2 ? p.b0 : p.b1) + ((g * f + (size_t)t.nt * (BN / 2)) * d + k0) * 2;
+    // B tile rows 0..127 are W1 (gate) rows, 128..255 the same W3 (up) rows; wave w loads rows
+    // 16 * LPO * w .. + 16 * LPO - 1
+    sb = reinterpret_cast<const char*>(wave < NW / 2 ? p.b0 : p.b1) + ((g * f + (size_t)t.nt * (BN / 2)) * d + k0) * 2;
   } else if constexpr (MODE == GEMM_DOWN_FWD) {
     sa = a + ((size_t)t.m0 * f + k0) * 2;
     sb = b0 + ((g * d + (size_t)t.nt * BN) * f + k0) * 2;
@@ -305,17 +356,26 @@ __device__ __forceinline__ void stage_bases(const GemmArgs& p, const Tile& t, in
 }
 
 template <int MODE, int IDX>
-__device__ __forceinline__ void issue_fast(char* stage, const char* sa, const char* sb, const uint32_t (&voff)[8],
+__device__ __forceinline__ void issue_fast(char* stage, const char* sa, const char* sb, const LoadOffs& lo,
                                            int k_left, int wave, int lane) {
-  constexpr bool A_OP = IDX < 4;
-  const char* src = (A_OP ? sa : sb) + voff[IDX];
+  constexpr bool A_OP = IDX < LPO;
+  constexpr int J = IDX % LPO;
+  // Load J is 8 K-contiguous rows (2 K rows) after load 0, which moves the row swizzle by 4
+  // chunks (the window swizzle by 8 chunks) for odd J: a 64-byte (128-byte) XOR on top of the step.
+  constexpr bool KC = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
+  constexpr uint32_t FLIP = (J & 1) ? (KC ? 64u : 128u) : 0u;
+  uint32_t off;
+  if constexpr (A_OP && Traits<MODE>::a_kcontig) off = lo.a[J];
+  else if constexpr (A_OP) off = (lo.a[0] + (uint32_t)J * lo.sa) ^ FLIP;
+  else off = (lo.b + (uint32_t)J * lo.sb) ^ FLIP;
+  const char* src = (A_OP ? sa : sb) + off;
   if constexpr (Traits<MODE>::raggedK) {
-    // K-strided operands: lane reads K row (wave * 4 + j) * 2 + lane / 32 of the stage; rows past
-    // the group's end read zeros.
-    const int kr = (wave * 4 + (IDX & 3)) * 2 + (lane >> 5);
+    // K-strided operands: lane reads K row (wave * LPO + j) * 2 + lane / 32 of the stage; rows
+    // past the group's end read zeros.
+    const int kr = (wave * LPO + IDX % LPO) * 2 + (lane >> 5);
     if (kr >= k_left) src = reinterpret_cast<const char*>(g_zero_rows);
   }
-  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * 4 + (IDX & 3)) * 1024),
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * LPO + IDX % LPO) * 1024),
                                    16, 0, 0);
 }
 
@@ -327,44 +387,38 @@ struct StageSrc {
 };
 
 // ---- Fragments ---------------------------------------------------------------------------
-// Tile shapes.  Full tiles: 256x256, waves in a 2x2 grid of 128x128 (4x4 MFMA blocks each).  Half
-// tiles (the last rows of a group when at most 128 remain): 128x256, waves side by side, 128x64
-// each (4x2 blocks); the load stream is the same, the MFMA work halves.  Wave w = wm + 2*wn.
-template <bool HALF> constexpr int nblk_b() { return HALF ? 2 : 4; }
+// Every tile is multiplied as 256x256: eight waves in a 2x4 grid, wave w = 4*wm + wn owning rows
+// wm*128.. and 64 columns (4x2 MFMA blocks).  The two waves of a SIMD (w and w + 4, one per row
+// half) take turns on its matrix core, so one of them can issue MFMAs while the other waits on a
+// load issue, a fragment read or the barrier.  A tile with at most 128 rows (the last rows of a
+// group) keeps the same load stream; the waves of the second row half skip its MFMAs.
 
 // Row (A) / column (B) of the wave's MFMA block i inside the 256-wide operand tile.
-template <int MODE, bool A_OP, bool HALF>
+template <int MODE, bool A_OP>
 __device__ __forceinline__ int block_row(int wm, int wn, int i) {
-  if constexpr (A_OP) {
-    return (HALF ? 0 : wm * 128) + 32 * i;
-  } else if constexpr (HALF) {
-    const int w = wm + WGM * wn;
-    // gate/up: the wave's 32 gate (W1) columns in block 0, the same up (W3) columns in block 1
-    if constexpr (MODE == GEMM_UP_FWD) return i == 0 ? w * 32 : 128 + w * 32;
-    else return w * 64 + 32 * i;
-  } else if constexpr (MODE == GEMM_UP_FWD) {
-    // gate (W1) columns in blocks 0,1 and the same up (W3) columns in blocks 2,3
-    return (i < 2) ? wn * 64 + 32 * i : 128 + wn * 64 + 32 * (i - 2);
-  } else {
-    return wn * 128 + 32 * i;
-  }
+  if constexpr (A_OP) return wm * 128 + 32 * i;
+  // gate/up: the wave's 32 gate (W1) columns in block 0, the same up (W3) columns in block 1
+  else if constexpr (MODE == GEMM_UP_FWD) return i == 0 ? wn * 32 : 128 + wn * 32;
+  else return wn * 64 + 32 * i;
 }
 
 // Per-lane LDS offset (within a stage, operand base included) of the first fragment read of each
 // 16-deep substep; the other blocks follow from it:
-//  KC: block i is a constant offset away (its rows are 32*i or, for the gate/up B tile, the listed
-//      rows further; the swizzle repeats every 16 rows), applied as the instruction's offset field.
+//  KC: block i is a constant offset away (its rows are 32*i or, for the gate/up B tile, 128 rows
+//      further; the swizzle repeats every 16 rows), applied as the instruction's offset field.
+//  The substep s (0..3) picks the 16-deep quarter of the stage's 64 k.
 //  MC: block i is 32 columns = 4 chunks further; with the window swizzle that is an XOR of i into
-//      address bits 6-7.  The second transposed read of a block is 4 k-rows = 2048 bytes further.
-template <int MODE, bool A_OP, bool HALF>
+//      address bits 6-7 (block 0 starts at a multiple of 64 columns).  The second transposed read
+//      of a block is 4 k-rows = 2048 bytes further.
+template <int MODE, bool A_OP>
 __device__ __forceinline__ uint32_t frag_base(int s, int wm, int wn, int lane) {
   constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
   const uint32_t base = A_OP ? 0 : OPB;
-  const int rb = block_row<MODE, A_OP, HALF>(wm, wn, 0);
+  const int rb = block_row<MODE, A_OP>(wm, wn, 0);
   if constexpr (kc) {
     const int row = rb + (lane & 31);
     const int chunk = s * 2 + (lane >> 5);
-    return base + row * 64 + ((chunk ^ kc_swz(row)) << 4);
+    return base + row * 128 + ((chunk ^ kc_swz(row)) << 4);
   } else {
     // 16-lane block b = lane/16 covers columns rb + 16*(b&1) + [0,16) and k-rows
     // s*16 + (b>>1)*8 + [0,8); lane j = 4c + q of the block points at k-row c, columns +4q..+4q+3.
@@ -376,34 +430,38 @@ __device__ __forceinline__ uint32_t frag_base(int s, int wm, int wn, int lane) {
 }
 
 // Offset of block i relative to block 0 (KC operands), in bytes.
-template <int MODE, bool A_OP, bool HALF>
+template <int MODE, bool A_OP>
 constexpr int kc_block_off(int i) {
-  if (A_OP) return 2048 * i;
-  if (MODE == GEMM_UP_FWD) return HALF ? 8192 * i : (i < 2 ? 2048 * i : 8192 + 2048 * (i - 2));
-  return 2048 * i;
+  if (!A_OP && MODE == GEMM_UP_FWD) return 16384 * i;
+  return 4096 * i;
 }
 
-// Fragments of one 16-deep substep, read one instruction at a time (IDX).  KC: one read per
-// block.  MC: two reads per block (4 k each), kept apart until packed for the MFMA.
-template <bool KC>
+// Fragments of one 16-deep substep for NB blocks, read one instruction at a time (IDX).  KC: one
+// read per block.  MC: two reads per block (4 k each), kept apart until packed for the MFMA.
+template <bool KC, int NB>
 struct Frag;
-template <>
-struct Frag<true> {
+template <int NB>
+struct Frag<true, NB> {
   static constexpr int PER_BLOCK = 1;
-  bf16x8_t v[4];
-  template <int MODE, bool A_OP, bool HALF, int IDX>
+  bf16x8_t v[NB];
+  template <int MODE, bool A_OP, int IDX>
   __device__ __forceinline__ void read_one(uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1 offset:%2"
                  : "=v"(v[IDX])
-                 : "v"(addr), "i"(kc_block_off<MODE, A_OP, HALF>(IDX)));
+                 : "v"(addr), "i"(kc_block_off<MODE, A_OP>(IDX)));
   }
   __device__ __forceinline__ bf16x8_t get(int i) const { return v[i]; }
+  // after an lgkmcnt wait: the values are in-out operands here, so no use moves above the wait
+  __device__ __forceinline__ void landed() {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) asm volatile("" : "+v"(v[i]));
+  }
 };
-template <>
-struct Frag<false> {
+template <int NB>
+struct Frag<false, NB> {
   static constexpr int PER_BLOCK = 2;
-  u32x2_t h[2][4];
-  template <int MODE, bool A_OP, bool HALF, int IDX>
+  u32x2_t h[2][NB];
+  template <int MODE, bool A_OP, int IDX>
   __device__ __forceinline__ void read_one(uint32_t addr) {
     constexpr int i = IDX >> 1, r = IDX & 1;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(h[r][i]) : "v"(addr ^ (uint32_t)(i << 6)), "i"(r * 2048));
@@ -412,106 +470,109 @@ struct Frag<false> {
     const u32x4_t u = {h[0][i].x, h[0][i].y, h[1][i].x, h[1][i].y};
     return __builtin_bit_cast(bf16x8_t, u);
   }
+  __device__ __forceinline__ void landed() {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) asm volatile("" : "+v"(h[0][i]), "+v"(h[1][i]));
+  }
 };
 
-// Wait until every LDS read is done; the fragments are in-out operands so no use of them can be
-// scheduled before the wait.
-__device__ __forceinline__ void frag_wait(Frag<true>& a, Frag<true>& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.v[0]), "+v"(a.v[1]), "+v"(a.v[2]), "+v"(a.v[3]), "+v"(b.v[0]),
-               "+v"(b.v[1]), "+v"(b.v[2]), "+v"(b.v[3]));
-}
-__device__ __forceinline__ void frag_wait(Frag<true>& a, Frag<false>& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.v[0]), "+v"(a.v[1]), "+v"(a.v[2]), "+v"(a.v[3]), "+v"(b.h[0][0]),
-               "+v"(b.h[0][1]), "+v"(b.h[0][2]), "+v"(b.h[0][3]), "+v"(b.h[1][0]), "+v"(b.h[1][1]),
-               "+v"(b.h[1][2]), "+v"(b.h[1][3]));
-}
-__device__ __forceinline__ void frag_wait(Frag<false>& a, Frag<false>& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a.h[0][0]), "+v"(a.h[0][1]), "+v"(a.h[0][2]), "+v"(a.h[0][3]),
-               "+v"(a.h[1][0]), "+v"(a.h[1][1]), "+v"(a.h[1][2]), "+v"(a.h[1][3]), "+v"(b.h[0][0]),
-               "+v"(b.h[0][1]), "+v"(b.h[0][2]), "+v"(b.h[0][3]), "+v"(b.h[1][0]), "+v"(b.h[1][1]),
-               "+v"(b.h[1][2]), "+v"(b.h[1][3]));
+template <int MODE>
+using FragA = Frag<Traits<MODE>::a_kcontig, MI>;
+template <int MODE>
+using FragB = Frag<Traits<MODE>::b_kcontig, NI>;
+
+// Wait until every LDS read is done; then the fragments count as written (no use of them can be
+// scheduled before the wait).
+template <int MODE>
+__device__ __forceinline__ void frag_wait(FragA<MODE>& a, FragB<MODE>& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  a.landed();
+  b.landed();
 }
 
 // ---- K step phases -------------------------------------------------------------------------
-// Slot Q of a phase: MFMA Q (block row Q/NB, block column Q%NB), then the memory instructions that
+// Slot Q of a phase: MFMA Q (block row Q/NI, block column Q%NI), then the memory instructions that
 // belong to the slot.  The scheduling barriers keep this order: the matrix core always has the
-// next MFMA queued while the wave issues a read or a load.
-template <int MODE>
-using FragA = Frag<Traits<MODE>::a_kcontig>;
-template <int MODE>
-using FragB = Frag<Traits<MODE>::b_kcontig>;
+// next MFMA queued while the wave issues a read or a load.  ACT = false: a wave of the idle row
+// half of a 128-row tile, which issues only the loads.
 
-// MFMAs per phase and fragment reads per substep of a shape.
-template <bool HALF> constexpr int nslots() { return MI * nblk_b<HALF>(); }
-template <int MODE, bool HALF>
+// MFMAs per phase and fragment reads per substep.
+constexpr int NS = MI * NI;
+template <int MODE>
 constexpr int nreads_a() { return MI * FragA<MODE>::PER_BLOCK; }
-template <int MODE, bool HALF>
-constexpr int nreads_b() { return nblk_b<HALF>() * FragB<MODE>::PER_BLOCK; }
+template <int MODE>
+constexpr int nreads_b() { return NI * FragB<MODE>::PER_BLOCK; }
 
 // The B fragment goes in as the MFMA's first operand: the accumulator block is then the
 // transpose of the output block, so each lane ends up with consecutive output columns of one row.
-template <int MODE, bool HALF, int Q>
+template <int MODE, int Q>
 __device__ __forceinline__ void mfma_slot(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a, const FragB<MODE>& b) {
-  constexpr int NB = nblk_b<HALF>();
-  constexpr int i = Q / NB, j = Q % NB;
+  constexpr int i = Q / NI, j = Q % NI;
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b.get(j), a.get(i), acc[i][j], 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Fragment read R of a substep (A's reads first, then B's).
-template <int MODE, bool HALF, int R>
+template <int MODE, int R>
 __device__ __forceinline__ void read_slot(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
-  constexpr int NRA = nreads_a<MODE, HALF>(), NRB = nreads_b<MODE, HALF>();
-  if constexpr (R < NRA) a.template read_one<MODE, true, HALF, R>(ra);
-  else if constexpr (R < NRA + NRB) b.template read_one<MODE, false, HALF, R - NRA>(rb);
+  constexpr int NRA = nreads_a<MODE>(), NRB = nreads_b<MODE>();
+  if constexpr (R < NRA) a.template read_one<MODE, true, R>(ra);
+  else if constexpr (R < NRA + NRB) b.template read_one<MODE, false, R - NRA>(rb);
 }
 
-// Phase 0 of a K step: MFMAs on substep 0 (a0, b0); reads of substep 1 (a1, b1) of the same
-// stage at ra/rb.
-template <int MODE, bool HALF, int Q>
-__device__ __forceinline__ void phase0(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a0, const FragB<MODE>& b0,
-                                       FragA<MODE>& a1, FragB<MODE>& b1, uint32_t ra, uint32_t rb) {
-  constexpr int NS = nslots<HALF>(), NR = nreads_a<MODE, HALF>() + nreads_b<MODE, HALF>();
-  if constexpr (Q < NS) {
-    mfma_slot<MODE, HALF, Q>(acc, a0, b0);
-    // reads spread over the slots (two per slot where there are more reads than slots)
-    read_slot<MODE, HALF, Q>(a1, b1, ra, rb);
-    if constexpr (NR > NS) read_slot<MODE, HALF, Q + NS>(a1, b1, ra, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    phase0<MODE, HALF, Q + 1>(acc, a0, b0, a1, b1, ra, rb);
+// Reads spread over the slots: ceil(reads / slots) per slot.
+template <int MODE>
+constexpr int reads_per_slot() { return (nreads_a<MODE>() + nreads_b<MODE>() + NS - 1) / NS; }
+template <int MODE, int Q, int I>
+__device__ __forceinline__ void slot_reads(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
+  if constexpr (I < reads_per_slot<MODE>()) {
+    read_slot<MODE, Q + I * NS>(a, b, ra, rb);
+    slot_reads<MODE, Q, I + 1>(a, b, ra, rb);
   }
 }
 
-// Phase 1: MFMAs on substep 1 (a1, b1); reads of substep 0 (a0, b0) of the next stage at ra/rb;
-// the 8 loads of the stage four steps ahead into this step's slot, spread over the phase.
-template <int MODE, bool HALF, int Q>
-__device__ __forceinline__ void phase1(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a1, const FragB<MODE>& b1,
-                                       FragA<MODE>& a0, FragB<MODE>& b0, uint32_t ra, uint32_t rb, char* stage,
-                                       const StageSrc& ss, const uint32_t (&voff)[8], int wave, int lane) {
-  constexpr int NS = nslots<HALF>(), NR = nreads_a<MODE, HALF>() + nreads_b<MODE, HALF>();
+// Direct loads of slot Q: the LPW loads of a stage are spread evenly over the NS slots of a phase
+// (a burst of direct loads stalls the issuing wave).
+template <int MODE, int Q, int I>
+__device__ __forceinline__ void slot_loads(char* stage, const StageSrc& ss, const LoadOffs& voff, int wave,
+                                           int lane) {
+  constexpr int PER = (LPW + NS - 1) / NS, EVERY = NS > LPW ? NS / LPW : 1;
+  if constexpr (I < PER && Q % EVERY == 0 && (Q / EVERY) * PER + I < LPW) {
+    issue_fast<MODE, (Q / EVERY) * PER + I>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
+    slot_loads<MODE, Q, I + 1>(stage, ss, voff, wave, lane);
+  }
+}
+
+// One phase of a K step: the MFMAs of the current substep (fragments ac, bc); the reads of the
+// next substep into an, bn at ra/rb; with LOADS, the loads of the stage two steps ahead into this
+// step's slot.
+template <int MODE, bool ACT, bool LOADS, int Q>
+__device__ __forceinline__ void phase(f32x16_t (&acc)[MI][NI], const FragA<MODE>& ac, const FragB<MODE>& bc,
+                                      FragA<MODE>& an, FragB<MODE>& bn, uint32_t ra, uint32_t rb, char* stage,
+                                      const StageSrc& ss, const LoadOffs& voff, int wave, int lane) {
   if constexpr (Q < NS) {
-    mfma_slot<MODE, HALF, Q>(acc, a1, b1);
-    read_slot<MODE, HALF, Q>(a0, b0, ra, rb);
-    if constexpr (NR > NS) read_slot<MODE, HALF, Q + NS>(a0, b0, ra, rb);
-    // one load every NS/8 slots: a burst of direct loads stalls the issuing wave
-    if constexpr (Q % (NS / 8) == 0) issue_fast<MODE, Q / (NS / 8)>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
+    if constexpr (ACT) {
+      mfma_slot<MODE, Q>(acc, ac, bc);
+      slot_reads<MODE, Q, 0>(an, bn, ra, rb);
+    }
+    if constexpr (LOADS) slot_loads<MODE, Q, 0>(stage, ss, voff, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
-    phase1<MODE, HALF, Q + 1>(acc, a1, b1, a0, b0, ra, rb, stage, ss, voff, wave, lane);
+    phase<MODE, ACT, LOADS, Q + 1>(acc, ac, bc, an, bn, ra, rb, stage, ss, voff, wave, lane);
   }
 }
 
 // All reads of one substep's fragments (prologue, start of a tile).
-template <int MODE, bool HALF, int R>
+template <int MODE, int R>
 __device__ __forceinline__ void read_all(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
-  if constexpr (R < nreads_a<MODE, HALF>() + nreads_b<MODE, HALF>()) {
-    read_slot<MODE, HALF, R>(a, b, ra, rb);
-    read_all<MODE, HALF, R + 1>(a, b, ra, rb);
+  if constexpr (R < nreads_a<MODE>() + nreads_b<MODE>()) {
+    read_slot<MODE, R>(a, b, ra, rb);
+    read_all<MODE, R + 1>(a, b, ra, rb);
   }
 }
 
 template <int MODE, int IDX>
 __device__ __forceinline__ void issue_all(const GemmArgs& p, char* stage, const Tile& t, int k0, int wave, int lane) {
-  if constexpr (IDX < 8) {
+  if constexpr (IDX < LPW) {
     issue_load<MODE, IDX>(p, stage, t, k0, wave, lane);
     issue_all<MODE, IDX + 1>(p, stage, t, k0, wave, lane);
   }
@@ -687,8 +748,8 @@ __device__ __forceinline__ void store_block(const GemmArgs& p, const OutWins& o,
   }
 }
 
-// Store instructions every epilogue issues at least (per wave, half tiles; the optional
-// pre-activation stashes of the gate/up GEMM not counted).
+// Store instructions every epilogue issues at least (per wave; the optional pre-activation stashes
+// of the gate/up GEMM not counted).
 template <int MODE>
 constexpr int epilogue_stores() {
   return MODE == GEMM_UP_FWD ? 8 : (MODE == GEMM_DOWN_BWD ? 32 : 16);
@@ -740,15 +801,15 @@ __device__ __forceinline__ void wait_aux(AuxBlock& x) {
   asm volatile("s_waitcnt vmcnt(%4)" : "+v"(x.a0), "+v"(x.a1), "+v"(x.b0), "+v"(x.b1) : "n"(N) : "memory");
 }
 
-// Output blocks per wave row of a shape (the gate/up GEMM pairs a gate block with an up block).
-template <int MODE, bool HALF>
-constexpr int out_nj() { return MODE == GEMM_UP_FWD ? nblk_b<HALF>() / 2 : nblk_b<HALF>(); }
+// Output blocks per wave row (the gate/up GEMM pairs a gate block with an up block).
+template <int MODE>
+constexpr int out_nj() { return MODE == GEMM_UP_FWD ? NI / 2 : NI; }
 
 // Window row and column of accumulator block IDX.
-template <int MODE, bool HALF, int IDX>
-constexpr int block_r() { return (IDX / out_nj<MODE, HALF>()) * 32; }
-template <int MODE, bool HALF, int IDX>
-constexpr int block_c() { return (IDX % out_nj<MODE, HALF>()) * 32; }
+template <int MODE, int IDX>
+constexpr int block_r() { return (IDX / out_nj<MODE>()) * 32; }
+template <int MODE, int IDX>
+constexpr int block_c() { return (IDX % out_nj<MODE>()) * 32; }
 
 template <int MODE>
 __device__ __forceinline__ void epilogue_block(const GemmArgs& p, const OutWins& o, const f32x16_t& c,
@@ -765,7 +826,7 @@ __device__ __forceinline__ void epilogue_block(const GemmArgs& p, const OutWins&
 }
 
 // Blocks whose pre-activations are in flight ahead of the block being stored.
-constexpr int AUX_AHEAD = 2;
+constexpr int AUX_AHEAD = 1;
 
 // Memory instructions issued after the pre-activation loads of block IDX and before the wait for
 // them: the stores of the AUX_AHEAD blocks before it and the loads of the AUX_AHEAD blocks after
@@ -778,54 +839,57 @@ constexpr int aux_younger() {
 // Blocks IDX.. of the wave's accumulators, unrolled at compile time (the loop unroller gives up on
 // the larger epilogues, and a run-time block index would put the accumulators in scratch memory).
 // The down-projection dgrad keeps the pre-activation loads AUX_AHEAD blocks ahead of their use.
-template <int MODE, bool HALF, int IDX>
+template <int MODE, int IDX>
 __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& o, const f32x16_t (&acc)[MI][NI],
                                               int row0, int col0, int m_end, int lane,
                                               AuxBlock (&aux)[AUX_AHEAD + 1], int ksplit) {
-  constexpr int NJ = out_nj<MODE, HALF>();
+  constexpr int NJ = out_nj<MODE>();
   constexpr int NB = MI * NJ;
   constexpr int NA = AUX_AHEAD + 1;
   if constexpr (IDX < NB) {
     if constexpr (MODE == GEMM_DOWN_BWD) {
       if constexpr (IDX + AUX_AHEAD < NB)
-        load_aux(p, row0 + block_r<MODE, HALF, IDX + AUX_AHEAD>(), m_end,
-                 col0 + block_c<MODE, HALF, IDX + AUX_AHEAD>(), aux[(IDX + AUX_AHEAD) % NA], lane);
+        load_aux(p, row0 + block_r<MODE, IDX + AUX_AHEAD>(), m_end, col0 + block_c<MODE, IDX + AUX_AHEAD>(),
+                 aux[(IDX + AUX_AHEAD) % NA], lane);
       wait_aux<aux_younger<IDX, NB>()>(aux[IDX % NA]);
     }
     constexpr int mi = IDX / NJ, ni = IDX % NJ;
     constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NJ : ni;
-    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, HALF, IDX>(), block_c<MODE, HALF, IDX>(),
-                         aux[IDX % NA], ksplit, lane);
-    epilogue_from<MODE, HALF, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
+    epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, IDX>(), block_c<MODE, IDX>(), aux[IDX % NA],
+                         ksplit, lane);
+    epilogue_from<MODE, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
   }
 }
 
 // Pre-activation loads of blocks IDX..AUX_AHEAD-1, issued in block order before the first store.
-template <int MODE, bool HALF, int IDX>
+template <int MODE, int IDX>
 __device__ __forceinline__ void aux_prologue(const GemmArgs& p, int row0, int col0, int m_end,
                                              AuxBlock (&aux)[AUX_AHEAD + 1], int lane) {
-  if constexpr (IDX < AUX_AHEAD && IDX < MI * out_nj<MODE, HALF>()) {
-    load_aux(p, row0 + block_r<MODE, HALF, IDX>(), m_end, col0 + block_c<MODE, HALF, IDX>(), aux[IDX], lane);
-    aux_prologue<MODE, HALF, IDX + 1>(p, row0, col0, m_end, aux, lane);
+  if constexpr (IDX < AUX_AHEAD && IDX < MI * out_nj<MODE>()) {
+    load_aux(p, row0 + block_r<MODE, IDX>(), m_end, col0 + block_c<MODE, IDX>(), aux[IDX], lane);
+    aux_prologue<MODE, IDX + 1>(p, row0, col0, m_end, aux, lane);
   }
 }
 
-template <int MODE, bool HALF>
+// The wave's output block of a tile: rows wm*128.. and its 64 columns (32 H columns for the gate/up
+// GEMM).  The idle row half of a 128-row tile runs it too: its window holds no rows, so every store
+// is dropped, and it issues the same number of memory instructions as the others.
+template <int MODE>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], const Tile& t,
                                               int wm, int wn, int lane, float* partial) {
   // The accumulator reads are opaque to the hazard checker: leave the last MFMA's write-back
   // (at most 18 wait states) behind before the first of them.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-  const int w = wm + WGM * wn;
-  const int row0 = t.m0 + (HALF ? 0 : wm * 128);
-  int col0;
-  if constexpr (HALF) col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + w * 32 : t.nt * BN + w * 64;
-  else col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 64 : t.nt * BN + wn * 128;
+  // The lane index through a volatile move: the per-lane addressing below is then computed here,
+  // not hoisted out of the tile loop into registers the K loop would have to keep (or spill).
+  asm volatile("v_mov_b32 %0, %0" : "+v"(lane));
+  const int row0 = t.m0 + wm * 128;
+  const int col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 32 : t.nt * BN + wn * 64;
   const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
   const int ksplit = t.ks;
   AuxBlock aux[AUX_AHEAD + 1];
-  if constexpr (MODE == GEMM_DOWN_BWD) aux_prologue<MODE, HALF, 0>(p, row0, col0, t.m_end, aux, lane);
-  epilogue_from<MODE, HALF, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
+  if constexpr (MODE == GEMM_DOWN_BWD) aux_prologue<MODE, 0>(p, row0, col0, t.m_end, aux, lane);
+  epilogue_from<MODE, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
 }
 
 // Output of a tile with an empty K range (a weight gradient of an expert without tokens): zeros.
@@ -834,7 +898,7 @@ __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int 
                                           float* partial) {
   const float z[2][8] = {};
   const AuxBlock zx = {};
-  const int row0 = t.m0 + wm * 128, col0 = t.nt * BN + wn * 128;
+  const int row0 = t.m0 + wm * 128, col0 = t.nt * BN + wn * 64;
   const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
   const int ksplit = t.ks;
 #pragma unroll 1
@@ -885,11 +949,11 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 
 // Producer of the load stream: the tile and K step of the next stage to load.  Once the stream
 // runs out it keeps reloading the last stage (valid memory, into slots nobody reads again), so
-// every K step issues exactly 8 loads per wave and the vmcnt arithmetic stays fixed.
+// every K step issues exactly LPW loads per wave and the vmcnt arithmetic stays fixed.
 struct Producer {
   Tile t;
   int i, k;        // this XCD's tile list position, K step
-  uint32_t voff[8];
+  LoadOffs lo;     // per-lane load offsets
   StageSrc ss;     // sources of stage k
   long long da, db;  // byte step of the sources from one K step to the next
 };
@@ -910,8 +974,12 @@ __device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs
 template <int MODE>
 __device__ __forceinline__ void set_offsets(Producer& pr, const GemmArgs& p, int wave, int lane) {
   const GemmArgs q = seg_args(p, pr.t.seg);
+  constexpr bool kca = Traits<MODE>::a_kcontig;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) pr.voff[i] = load_offset<MODE>(q, pr.t, i, wave, lane);
+  for (int i = 0; i < (kca ? LPO : 1); ++i) pr.lo.a[i] = load_offset<MODE>(q, pr.t, i, wave, lane);
+  pr.lo.b = load_offset<MODE>(q, pr.t, LPO, wave, lane);
+  pr.lo.sa = (uint32_t)uniform((int)load_step<MODE, true>(q));
+  pr.lo.sb = (uint32_t)uniform((int)load_step<MODE, false>(q));
   pr.ss = stage_src<MODE>(pr, p, wave);
   const long long d = q.d, f = q.f, kc = 2 * BKS;
   if constexpr (MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD) { pr.da = kc; pr.db = kc; }
@@ -948,57 +1016,67 @@ __device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const S
   pr.i = dl.n;
 }
 
-// Per-lane fragment read bases of one tile shape (substeps 0 and 1, both operands).
+// Per-lane fragment read bases of substep 0, both operands.  Substep s of a slot at sb:
+//  KC: the logical chunk is 2s + lane/32 and the swizzle XORs bits 4-6 of the address only, so the
+//      address is (base + sb) XOR 32s (sb and base's row part leave bits 5-6 clear);
+//  MC: the window swizzle depends on k mod 4, the same in every substep, so it is base + sb + 8192s.
 struct FragBases {
-  uint32_t a0, a1, b0, b1;
+  uint32_t a, b;
 };
-template <int MODE, bool HALF>
+template <int MODE>
 __device__ __forceinline__ FragBases frag_bases(uint32_t lds0, int wm, int wn, int lane) {
   FragBases f;
-  f.a0 = lds0 + frag_base<MODE, true, HALF>(0, wm, wn, lane);
-  f.a1 = lds0 + frag_base<MODE, true, HALF>(1, wm, wn, lane);
-  f.b0 = lds0 + frag_base<MODE, false, HALF>(0, wm, wn, lane);
-  f.b1 = lds0 + frag_base<MODE, false, HALF>(1, wm, wn, lane);
+  f.a = lds0 + frag_base<MODE, true>(0, wm, wn, lane);
+  f.b = lds0 + frag_base<MODE, false>(0, wm, wn, lane);
   return f;
 }
+template <int MODE, bool A_OP, int S>
+__device__ __forceinline__ uint32_t sub_addr(uint32_t base, uint32_t sb) {
+  constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
+  if constexpr (kc) return (base + sb) ^ (uint32_t)(32 * S);
+  else return base + sb + (uint32_t)(8192 * S);
+}
 
-// One output tile of shape HALF: its K steps j, j+1, ... and its epilogue.  On entry a0/b0 hold
-// substep 0 of stage j read for this shape; on return, substep 0 of the next stage (the next
-// tile's first) read for this shape.
-template <int MODE, bool HALF>
+// One output tile: its K steps j, j+1, ... and its epilogue.  ACT: on entry a0/b0 hold substep 0
+// of stage j.  !ACT (the idle row half of a 128-row tile): the wave issues its share of the load
+// stream and the epilogue's memory instructions only, and reads no fragments.
+//
+// A K step (stage j, slot j & 1): four phases of 16-deep substeps whose fragments alternate
+// between the register sets 0 and 1; the fourth phase reads substep 0 of stage j + 1 from the other
+// slot and loads stage j + 2 into this one, which every wave has finished reading by then.
+template <int MODE, bool ACT>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& ct, const FragBases& fb, FragA<MODE>& a0,
                                          FragB<MODE>& b0, FragA<MODE>& a1, FragB<MODE>& b1, int& j,
                                          int& since_epi, Producer& pr, const SegGeo (&geo)[2], const Deal& dl,
                                          int nbx, int wm, int wn, int wave, int lane, char* lds, float* partial) {
-  // K steps since the last epilogue.  Its stores are younger than the stage each of the next three
-  // K steps waits for, and at least epilogue_stores() of them were issued, so those steps may
-  // leave that many more operations outstanding.
-  constexpr int VM_AFTER_EPI = 16 + epilogue_stores<MODE>() < 62 ? 16 + epilogue_stores<MODE>() : 62;
   f32x16_t acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < nblk_b<HALF>(); ++jj)
+    for (int jj = 0; jj < NI; ++jj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
   for (int kc = 0; kc < ct.nk; ++kc, ++j) {
-    // Phase 0: substep 0 of stage j; read substep 1.
-    const uint32_t sb = (j & 3) * STAGE;
-    phase0<MODE, HALF, 0>(acc, a0, b0, a1, b1, fb.a1 + sb, fb.b1 + sb);
-    frag_wait(a1, b1);
-    // Stage j+1 has landed once only the loads of stages j+2, j+3 (and any stores issued after
-    // them) are outstanding; the barrier makes every wave's part visible and frees slot j & 3.
-    if (since_epi < 3) wait_vm<VM_AFTER_EPI>();
-    else wait_vm<16>();
+    const uint32_t sb = (j & 1) * STAGE;
+    phase<MODE, ACT, false, 0>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 1>(fb.a, sb), sub_addr<MODE, false, 1>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
+    if constexpr (ACT) frag_wait<MODE>(a1, b1);
+    phase<MODE, ACT, false, 0>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 2>(fb.a, sb), sub_addr<MODE, false, 2>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
+    if constexpr (ACT) frag_wait<MODE>(a0, b0);
+    phase<MODE, ACT, false, 0>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 3>(fb.a, sb), sub_addr<MODE, false, 3>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
+    if constexpr (ACT) frag_wait<MODE>(a1, b1);
+    // Stage j+1 has landed once nothing issued before the last epilogue's stores is outstanding
+    // (the first step after an epilogue; at least epilogue_stores() of them follow the stage's
+    // loads), or nothing at all; the barrier makes every wave's part visible and frees slot j & 1.
+    if (since_epi == 0) wait_vm<epilogue_stores<MODE>()>();
+    else wait_vm<0>();
     barrier();
-    // Phase 1: substep 1 of stage j; read substep 0 of stage j+1; load stage j+4 into slot j & 3.
-    const uint32_t sn = ((j + 1) & 3) * STAGE;
-    phase1<MODE, HALF, 0>(acc, a1, b1, a0, b0, fb.a0 + sn, fb.b0 + sn, lds + sb, pr.ss, pr.voff, wave, lane);
+    const uint32_t sn = ((j + 1) & 1) * STAGE;
+    phase<MODE, ACT, true, 0>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 0>(fb.a, sn), sub_addr<MODE, false, 0>(fb.b, sn), lds + sb, pr.ss, pr.lo, wave, lane);
     advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
-    frag_wait(a0, b0);
+    if constexpr (ACT) frag_wait<MODE>(a0, b0);
     ++since_epi;
   }
-  epilogue_tile<MODE, HALF>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
+  epilogue_tile<MODE>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
   since_epi = 0;
 }
 
@@ -1014,10 +1092,11 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6), lane = tid & 63;
-  const int wm = wave % WGM, wn = wave / WGM;
+  // the two waves of a SIMD (w, w + 4) take the two row halves
+  const int wm = wave / WGN, wn = wave % WGN;
   const uint32_t lds0 = lds_addr_of(lds);
 
-  const FragBases full = frag_bases<MODE, false>(lds0, wm, wn, lane);
+  const FragBases fb = frag_bases<MODE>(lds0, wm, wn, lane);
 
   // Per set: clamped group offsets (the clamping of group_rows), tile geometry and, for ragged M,
   // the per-group tile prefix.  Set 1 (if any) follows set 0 in the tile order.
@@ -1090,7 +1169,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     if constexpr (TR::raggedK) zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
   }
 
-  // Prologue: stages 0..3 into slots 0..3, wait for stage 0, read substep 0 of stage 0.
+  // Prologue: stages 0 and 1 into slots 0 and 1, wait for stage 0.
   Producer pr;
   pr.t = ct;
   pr.i = ic;
@@ -1101,41 +1180,23 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     issue_all<MODE, 0>(seg_args(p, pr.t.seg), lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
     advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
   }
-  wait_vm<24>();
+  wait_vm<(NSTAGE - 1) * LPW>();
   barrier();
   FragA<MODE> a0, a1;
   FragB<MODE> b0, b1;
   int j = 0, since_epi = 3;
-  if constexpr (TR::raggedK) {
-    read_all<MODE, false, 0>(a0, b0, full.a0, full.b0);
-    frag_wait(a0, b0);
-  }
-  // Ragged M: half tiles have their own fragment bases; after a tile, the substep-0 fragments of
-  // the next stage were read for that tile's shape and are read again when the shape changes.
-  const FragBases hb = frag_bases<MODE, true>(lds0, wm, wn, lane);
-  bool fr_half = !ct.half;
   for (;;) {
-    if constexpr (TR::raggedK) {
-      run_tile<MODE, false>(p, ct, full, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
+    if (!TR::raggedK && ct.half && wm == 1) {
+      run_tile<MODE, false>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
                             partial);
-    } else if (ct.half) {
-      if (!fr_half) {
-        const uint32_t sb = (j & 3) * STAGE;
-        read_all<MODE, true, 0>(a0, b0, hb.a0 + sb, hb.b0 + sb);
-        frag_wait(a0, b0);
-      }
-      run_tile<MODE, true>(p, ct, hb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
-                           partial);
-      fr_half = true;
     } else {
-      if (fr_half) {
-        const uint32_t sb = (j & 3) * STAGE;
-        read_all<MODE, false, 0>(a0, b0, full.a0 + sb, full.b0 + sb);
-        frag_wait(a0, b0);
-      }
-      run_tile<MODE, false>(p, ct, full, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
-                            partial);
-      fr_half = false;
+      // Substep 0 of the tile's first stage, read here rather than kept in registers through the
+      // previous epilogue: its slot is refilled only after this wave's next barrier.
+      const uint32_t sb = (j & 1) * STAGE;
+      read_all<MODE, 0>(a0, b0, sub_addr<MODE, true, 0>(fb.a, sb), sub_addr<MODE, false, 0>(fb.b, sb));
+      frag_wait<MODE>(a0, b0);
+      run_tile<MODE, true>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
+                           partial);
     }
     bool more = false;
     for (ic += nbx; ic < dl.n; ic += nbx) {

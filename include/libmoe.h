@@ -13,7 +13,8 @@
  * Conventions shared by every call
  *   Memory      All tensor pointers are DEVICE pointers owned by the caller.  The library keeps
  *               no pointer after a call returns and allocates no device memory: scratch space is
- *               the caller's workspace, sized by the matching *_workspace_size function.
+ *               the caller's workspace, sized by the matching *_workspace_size function (or, for
+ *               moe_permute_noalloc, a fixed device array the library holds per GPU).
  *               Every device pointer (tensors, index arrays, workspaces) must be 16-byte
  *               aligned: the kernels use 16-byte vector and direct-to-LDS accesses from each base
  *               (hipMalloc and PyTorch allocations are 256-byte aligned); a misaligned pointer
@@ -98,6 +99,20 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int6
                          int32_t k, moe_dtype_t dt, int32_t* counts, int32_t* offsets,
                          int32_t* dest_pos, int32_t* src_row, void* x_perm, void* ws,
                          size_t ws_bytes, moe_stream_t stream);
+
+/* moe_permute for callers that cannot allocate device memory or pass a workspace: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and checks as moe_permute without ws/ws_bytes; no call allocates or frees anything.  Its scratch
+ * is a fixed array in device memory that the library holds on every GPU it runs on until the
+ * process ends: moe_permute_noalloc_max_scratch() bytes (4 MiB).  Sizes whose moe_permute
+ * workspace (moe_permute_workspace_size(T, E, k)) exceeds that return MOE_ERR_UNSUPPORTED; with
+ * E = 256 this allows T*k up to about 690,000.  All calls on one GPU share that GPU's array, which
+ * keeps the last call's contents: calls that may overlap on one GPU (different streams, no ordering
+ * between them) race on it and give undefined results; calls ordered on one stream are safe. */
+size_t moe_permute_noalloc_max_scratch(void);
+moe_status_t moe_permute_noalloc(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E,
+                                 int32_t k, moe_dtype_t dt, int32_t* counts, int32_t* offsets,
+                                 int32_t* dest_pos, int32_t* src_row, void* x_perm, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------------------------ */
 /* Grouped SwiGLU expert MLP.  G groups (experts) over M rows; group g owns rows                */

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -110,6 +111,38 @@ moe::GemmArgs base_args(const int32_t* offsets, int32_t G, int64_t M, int64_t d,
   return a;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Scratch for the entry point that allocates nothing (moe_permute_noalloc): a file-scope device
+// array that each GPU holds from the library's load until the process ends.  In host code the
+// array's name only stands in for the symbol; its device address, different on every GPU, comes
+// from hipGetSymbolAddress, taken once per device with that device current, and only that address
+// is ever handed to a kernel.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that device).
+moe_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  CHECK(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "device %d is beyond the %d devices supported", dev,
+        kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +213,35 @@ moe_status_t moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int6
   return hip_check(moe::launch_permute(x, topk_idx, (int)T, (int)d, E, k, dt == MOE_BF16, counts,
                                        offsets, dest_pos, src_row, x_perm, ws, S(stream)),
                    "permute");
+}
+
+size_t moe_permute_noalloc_max_scratch(void) { return kScratchBytes; }
+
+moe_status_t moe_permute_noalloc(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E, int32_t k,
+                                 moe_dtype_t dt, int32_t* counts, int32_t* offsets, int32_t* dest_pos,
+                                 int32_t* src_row, void* x_perm, moe_stream_t stream) {
+  g_err.clear();
+  moe_status_t st = check_dtype(dt);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(T, d, E, k)) != MOE_OK) return st;
+  CHECK(counts && offsets, MOE_ERR_INVALID_VALUE, "counts/offsets is NULL");
+  CHECK(T == 0 || (topk_idx && dest_pos && src_row), MOE_ERR_INVALID_VALUE,
+        "topk_idx/dest_pos/src_row is NULL");
+  CHECK(!x_perm || x || T == 0, MOE_ERR_INVALID_VALUE, "x is NULL while x_perm is requested");
+  CHECK(!x_perm || d % 8 == 0, MOE_ERR_UNSUPPORTED, "the row gather needs d %% 8 == 0 (got %lld)",
+        (long long)d);
+  const size_t need = moe::permute_ws_bytes(T, E, k);
+  CHECK(need <= kScratchBytes, MOE_ERR_UNSUPPORTED,
+        "T*k = %lld with E = %d needs %zu bytes of scratch; moe_permute_noalloc holds %zu (use moe_permute)",
+        (long long)(T * k), E, need, kScratchBytes);
+  CHECK_ALIGN16(x, topk_idx, counts, offsets, dest_pos, src_row, x_perm);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MOE_OK) return st;
+  // Every scratch element the kernels read they first write in the same call (chunk counts,
+  // chunk bases, local ranks), so nothing needs clearing.
+  return hip_check(moe::launch_permute(x, topk_idx, (int)T, (int)d, E, k, dt == MOE_BF16, counts,
+                                       offsets, dest_pos, src_row, x_perm, ws, S(stream)),
+                   "permute (no allocation)");
 }
 
 // ---------------------------------------------------------------------------------------------

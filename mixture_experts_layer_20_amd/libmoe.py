@@ -68,6 +68,8 @@ _SIGS = {
     "moe_route": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "moe_permute_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "moe_permute": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_noalloc_max_scratch": (_SZ, []),
+    "moe_permute_noalloc": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_mlp_fwd_workspace_size": (_SZ, [_I64, _I32, _I64, _I64]),
     "moe_grouped_mlp_bwd_workspace_size": (_SZ, [_I64, _I32, _I64, _I64]),
     "moe_grouped_mlp_fwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _P, _P, _P, _P,
@@ -193,6 +195,15 @@ def moe_permute(x, topk_idx, T, d, E, k, dt, counts, offsets, dest_pos, src_row,
                 stream=None):
     _call("moe_permute", _ptr(x), _ptr(topk_idx), T, d, E, k, dt, _ptr(counts), _ptr(offsets),
           _ptr(dest_pos), _ptr(src_row), _ptr(x_perm), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def moe_permute_noalloc_max_scratch() -> int:
+    return lib().moe_permute_noalloc_max_scratch()
+
+
+def moe_permute_noalloc(x, topk_idx, T, d, E, k, dt, counts, offsets, dest_pos, src_row, x_perm, stream=None):
+    _call("moe_permute_noalloc", _ptr(x), _ptr(topk_idx), T, d, E, k, dt, _ptr(counts), _ptr(offsets),
+          _ptr(dest_pos), _ptr(src_row), _ptr(x_perm), _stream(stream))
 
 
 def moe_grouped_mlp_fwd_workspace_size(M, G, d, f) -> int:

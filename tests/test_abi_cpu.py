@@ -221,3 +221,15 @@ def test_workspace_bytes_equals_each_calls_own_query(lib):
     assert L.moe_workspace_bytes(L.MOE_OP_PERMUTE, T, d, E, 0, f, fs) == 0
     assert L.moe_workspace_bytes(L.MOE_OP_PERMUTE, T, d, E, k, 0, fs) == 0
     assert L.moe_workspace_bytes(L.MOE_OP_PERMUTE, T, d, E, k, f, -1) == 0
+
+
+def test_permute_noalloc_refuses_sizes_beyond_its_scratch(lib):
+    cap = L.moe_permute_noalloc_max_scratch()
+    assert cap == 4 << 20
+    T, E, k = 200_000, 256, 4
+    assert L.moe_permute_workspace_size(T, E, k) > cap
+    _expect(L.MOE_ERR_UNSUPPORTED, L.moe_permute_noalloc, FAKE, FAKE, T, 16, E, k, L.MOE_BF16, FAKE, FAKE, FAKE,
+            FAKE, FAKE)
+    assert b"moe_permute_noalloc holds" in lib.moe_last_error()
+    _expect(L.MOE_ERR_INVALID_VALUE, L.moe_permute_noalloc, FAKE, FAKE, 100, 16, 8, 2, L.MOE_BF16, None, FAKE,
+            FAKE, FAKE, FAKE)

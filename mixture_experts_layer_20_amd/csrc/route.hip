@@ -63,19 +63,15 @@ __device__ __forceinline__ void logits_step(const float* xrow, const float* wrow
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (BF16) {
-        acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
-      } else {
-        const float prod = a[i] * b[j];
-        acc[i][j] = acc[i][j] + prod;
-      }
+      const float prod = a[i] * b[j];
+      acc[i][j] = acc[i][j] + prod;
     }
 }
 
-// Logits: one thread owns 2 tokens x 4 experts and walks the features in increasing order.
-// bf16 inputs: the product of two bf16 values is exact in fp32, so a fused multiply-add rounds
-// exactly like the separate product and sum.  fp32 inputs: separate multiply and add.  The next
-// 128-feature tile is loaded into registers while the current one is multiplied.
+// Logits on the vector ALU (fp32 inputs, and bf16 rows whose length is not a multiple of 8): one
+// thread owns 2 tokens x 4 experts and walks the features in increasing order, each product and
+// each sum rounded separately.  The next 128-feature tile is loaded into registers while the
+// current one is multiplied.
 template <bool BF16>
 __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, const void* wv,
                                                             const float* bias, float* logits,
@@ -135,6 +131,144 @@ __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, cons
       float v = acc[i][j];
       if (bias) v = v + bias[e];
       logits[(size_t)t * E + e] = v;
+    }
+  }
+}
+
+// Logits of bf16 inputs on the matrix core.  v_mfma_f32_16x16x1_4b_f32 adds one product per output
+// per instruction (K = 1), rounding each step to nearest like an FMA, and a product of two bf16
+// values is exact in fp32 (while it is not below the normal range, see below), so a chain of them
+// over k = 0, 1, ... is the canonical sequential sum bit for bit at twice the rate of unpacked fp32
+// FMAs.  A dependent chain issues every 32 cycles (measured), so each wave runs one: 16 tokens
+// (operand A, the same in the instruction's four 16x16 blocks) by 64 experts (operand B, one per
+// lane, block b = experts 16b..16b+15).  Output register r of lane l is block r/4, token row
+// 4*(l/16) + r%4, expert column l%16.  The four waves of a block share their 64 expert rows: each
+// 64-k slice of them is staged once in LDS (coalesced 128-byte row segments, 16-byte chunks
+// swizzled by row, double-buffered, one barrier per slice); token rows are read directly in
+// chunks of 8 k through a ring of RM_RING chunks in flight.  Rows past T or E are clamped to row 0
+// and their results not stored.
+//
+// The matrix core rounds a subnormal partial sum differently from IEEE fp32, and a product below
+// fp32's normal range is not exact.  Neither can arise when every nonzero input has magnitude
+// >= 2^-50: every product (at most 16 significant bits) is then a multiple of 2^-114, and so is
+// every partial sum, which is therefore zero or at least 2^-114.  Each lane keeps the minimum over
+// the values it loads of |v| - 1 (as 16-bit integers, so zero wraps to the top); a block that saw
+// a nonzero |v| below 2^-50 recomputes its outputs on the vector ALU in the canonical order.
+typedef float f32x16_r __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+constexpr uint16_t RM_TINY = 77 << 7;   // bf16 magnitude bits of 2^-50
+constexpr int RM_TOK = 16, RM_EXP = 64, RM_WAVES = 4, RM_RING = 8, RM_KB = 64;
+
+// Packed running minimum of |v| - 1 over the 8 bf16 values of a load.
+__device__ __forceinline__ u16x2_t tiny_scan(u16x2_t mn, const uint4& v) {
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u16x2_t a = __builtin_bit_cast(u16x2_t, w4[i] & 0x7fff7fffu);
+    const u16x2_t one = {1, 1};
+    mn = __builtin_elementwise_min(mn, a - one);
+  }
+  return mn;
+}
+__device__ __forceinline__ bool tiny_seen(u16x2_t mn) { return mn.x < RM_TINY - 1 || mn.y < RM_TINY - 1; }
+
+__global__ __launch_bounds__(64 * RM_WAVES) void router_logits_mfma_kernel(const bf16_t* x, const bf16_t* w,
+                                                                        const float* bias, float* logits, int T,
+                                                                        int d, int E) {
+  // [buffer][expert row][8 chunks of 16 bytes], chunk c of row r stored at c ^ ((r >> 1) & 7): 16
+  // consecutive rows read at one chunk hit 16 distinct 16-byte bank groups
+  __shared__ uint4 wsm[2][RM_EXP * 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tw = (blockIdx.x * RM_WAVES + wave) * RM_TOK, e0 = blockIdx.y * RM_EXP;
+  const bool active = tw < T;   // wave-uniform; an inactive wave still stages and meets the barriers
+  const int t = active ? min(tw + (lane & 15), T - 1) : 0;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * d);
+  const int nch = d >> 3, nkb = (d + RM_KB - 1) / RM_KB;
+  // staging: thread i copies chunks 2*(i%4), 2*(i%4)+1 of expert row i/4 of a 64-k slice
+  const int sr = tid >> 2, sc = (tid & 3) * 2;
+  const uint4* wsrc = reinterpret_cast<const uint4*>(w + (size_t)min(e0 + sr, E - 1) * d);
+  u16x2_t mn = {0xffff, 0xffff};
+  uint4 st[2];
+  // Loads are never skipped by a branch (indices clamped, values past the row zeroed by a select):
+  // a load under a condition makes the compiler wait for every load in flight before the next use.
+  auto stage_load = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = kb * 8 + sc + q;
+      const uint4 v = wsrc[min(c, nch - 1)];
+      st[q] = c < nch ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      mn = tiny_scan(mn, st[q]);
+      wsm[buf][sr * 8 + ((sc + q) ^ ((sr >> 1) & 7))] = st[q];
+    }
+  };
+  stage_load(0);
+  stage_store(0);
+  stage_load(min(1, nkb - 1));
+  uint4 xa[RM_RING];
+#pragma unroll
+  for (int r = 0; r < RM_RING; ++r) xa[r] = xr[min(r, nch - 1)];
+  __syncthreads();
+  f32x16_r acc = {};
+  // chunk r of slice kb: the staged expert values and the token values of k = 8c..8c+7
+  auto chunk = [&](int buf, int r, int c, bool mfma) {
+    const uint4 xv = xa[r];
+    const uint4 wv = wsm[buf][lane * 8 + (r ^ ((lane >> 1) & 7))];
+    mn = tiny_scan(mn, xv);
+    xa[r] = xr[min(c + RM_RING, nch - 1)];
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    if (mfma) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // k = 8c + 2i, then 8c + 2i + 1
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(__uint_as_float(xw[i] << 16), __uint_as_float(ww[i] << 16), acc,
+                                                   0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(__uint_as_float(xw[i] & 0xffff0000u),
+                                                   __uint_as_float(ww[i] & 0xffff0000u), acc, 0, 0, 0);
+      }
+    }
+  };
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if ((kb + 1) * 8 <= nch) {
+#pragma unroll
+      for (int r = 0; r < RM_RING; ++r) chunk(buf, r, kb * 8 + r, active);
+    } else {   // the last, partial slice
+      for (int r = 0; r < RM_RING; ++r) chunk(buf, r, kb * 8 + r, active && kb * 8 + r < nch);
+    }
+    // slice kb+1 into the other buffer (last read in slice kb-1, before the previous barrier)
+    if (kb + 1 < nkb) stage_store(buf ^ 1);
+    stage_load(min(kb + 2, nkb - 1));
+    __syncthreads();
+  }
+  const bool tiny = __syncthreads_or(tiny_seen(mn)) != 0;
+  if (!active) return;
+  if (tiny) {
+    // canonical order on the vector ALU: each product rounded, then the sum (contraction is off)
+#pragma unroll 1
+    for (int r = 0; r < 16; ++r) {
+      const int tt = min(tw + 4 * (lane >> 4) + (r & 3), T - 1), ee = min(e0 + 16 * (r >> 2) + (lane & 15), E - 1);
+      const bf16_t* xt = x + (size_t)tt * d;
+      const bf16_t* we = w + (size_t)ee * d;
+      float s = 0.0f;
+      for (int kk = 0; kk < d; ++kk) {
+        const float prod = bf16_to_f32(xt[kk]) * bf16_to_f32(we[kk]);
+        s = s + prod;
+      }
+      acc[r] = s;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int tt = tw + 4 * (lane >> 4) + (r & 3), ee = e0 + 16 * (r >> 2) + (lane & 15);
+    if (tt < T && ee < E) {
+      float v = acc[r];
+      if (bias) v = v + bias[ee];
+      logits[(size_t)tt * E + ee] = v;
     }
   }
 }
@@ -444,6 +578,12 @@ inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 hipError_t launch_router_logits(const void* x, const void* w, const float* bias, float* logits,
                                 int T, int d, int E, bool bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (bf16 && d % 8 == 0) {
+    hipLaunchKernelGGL(router_logits_mfma_kernel, dim3(ceil_div(T, RM_TOK * RM_WAVES), ceil_div(E, RM_EXP)),
+                       dim3(64 * RM_WAVES), 0, s, reinterpret_cast<const bf16_t*>(x),
+                       reinterpret_cast<const bf16_t*>(w), bias, logits, T, d, E);
+    return hipGetLastError();
+  }
   dim3 grid(ceil_div(T, RT), ceil_div(E, RE));
   if (bf16) hipLaunchKernelGGL(router_logits_kernel<true>, grid, dim3(RTH), 0, s, x, w, bias, logits, T, d, E);
   else hipLaunchKernelGGL(router_logits_kernel<false>, grid, dim3(RTH), 0, s, x, w, bias, logits, T, d, E);

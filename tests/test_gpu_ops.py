@@ -53,6 +53,27 @@ def test_learned_route_bit_exact(dtype, T, d, E, k, bias):
     assert_close("gates", tnp(gate), O.gate_weights(ref_logits, ref_idx), 1e-6)
 
 
+@pytest.mark.parametrize("scale", [2.0 ** -60, 2.0 ** 50])
+def test_learned_route_bit_exact_at_extreme_magnitudes(scale):
+    """Products below fp32's normal range (about 2^-130, kept as subnormals by the canonical order)
+    and large ones: the logits stay bit-exact."""
+    log(f"route learned bf16 extreme magnitudes scale={scale}")
+    T, d, E, k = 256, 512, 64, 4
+    rng = np.random.default_rng(11)
+    x = as_dtype_values(scale * rng.standard_normal((T, d)), "bf16")
+    w = as_dtype_values((2.0 ** -72 if scale < 1 else 2.0 ** -10) * rng.standard_normal((E, d)), "bf16")
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gate = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    L.moe_route(dev_tensor(x, "bf16"), dev_tensor(w, "bf16"), None, logits, T, d, E, k, 1, L.MOE_BF16, idx, gate)
+    torch.cuda.synchronize()
+    ref = O.canonical_router_logits(x, w)
+    if scale < 1:
+        assert np.abs(ref).max() < 2.0 ** -120 and np.count_nonzero(ref) > 0   # subnormal range, not zero
+    assert np.array_equal(tnp(logits).view(np.uint32), ref.view(np.uint32)), "logits not bit-exact"
+    assert np.array_equal(tnp(idx), O.select_topk(ref, k))
+
+
 @pytest.mark.parametrize("renormalize", [1, 0])
 @pytest.mark.parametrize("kind", ["gauss", "integer_ties", "signed_zero"])
 @pytest.mark.parametrize("E,k", [(64, 4), (256, 8), (8, 8), (130, 3)])

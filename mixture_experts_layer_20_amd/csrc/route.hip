@@ -139,114 +139,157 @@ __global__ __launch_bounds__(RTH) void router_logits_kernel(const void* xv, cons
 // per instruction (K = 1), rounding each step to nearest like an FMA, and a product of two bf16
 // values is exact in fp32 (while it is not below the normal range, see below), so a chain of them
 // over k = 0, 1, ... is the canonical sequential sum bit for bit at twice the rate of unpacked fp32
-// FMAs.  A dependent chain issues every 32 cycles (measured), so each wave runs one: 16 tokens
-// (operand A, the same in the instruction's four 16x16 blocks) by 64 experts (operand B, one per
-// lane, block b = experts 16b..16b+15).  Output register r of lane l is block r/4, token row
-// 4*(l/16) + r%4, expert column l%16.  The four waves of a block share their 64 expert rows: each
-// 64-k slice of them is staged once in LDS (coalesced 128-byte row segments, 16-byte chunks
-// swizzled by row, double-buffered, one barrier per slice); token rows are read directly in
-// chunks of 8 k through a ring of RM_RING chunks in flight.  Rows past T or E are clamped to row 0
-// and their results not stored.
+// FMAs.  The instruction issues every 32 cycles, dependent or not (measured), so one wave per SIMD
+// runs one chain: 16 tokens (operand A, the same in the instruction's four 16x16 blocks) by 64
+// experts (operand B, one per lane, block b = experts 16b..16b+15).  Output register r of lane l is
+// block r/4, token row 4*(l/16) + r%4, expert column l%16.
+//
+// A vector-ALU instruction of the wave that runs the chain waits for the matrix core (measured:
+// each one adds about 7 cycles to the chain), while one from another wave on the same SIMD runs
+// beside it.  So a workgroup is 4 chain waves (64 tokens by 64 experts) and 4 staging waves.  The
+// staging waves load 128-k slices of the token and expert rows (whole 256-byte row segments per
+// instruction, one slice ahead), widen the bf16 values to fp32 and store them in LDS (rows padded
+// by 16 bytes so 16 rows read at one offset hit distinct banks), double buffered, one barrier per
+// slice.  A chain wave only reads its fp32 operands from LDS, the next 8 k while the current 8
+// products run, and issues matrix-core instructions.  Chunks past d are staged as zeros: a product
+// 0 * 0 = +0 leaves every partial sum unchanged (the canonical sum starts at +0 and so is never
+// -0).  Rows past T or E are clamped to the last row and their results not stored.
 //
 // The matrix core rounds a subnormal partial sum differently from IEEE fp32, and a product below
 // fp32's normal range is not exact.  Neither can arise when every nonzero input has magnitude
 // >= 2^-50: every product (at most 16 significant bits) is then a multiple of 2^-114, and so is
-// every partial sum, which is therefore zero or at least 2^-114.  Each lane keeps the minimum over
-// the values it loads of |v| - 1 (as 16-bit integers, so zero wraps to the top); a block that saw
-// a nonzero |v| below 2^-50 recomputes its outputs on the vector ALU in the canonical order.
+// every partial sum, which is therefore zero or at least 2^-114.  The staging threads keep the
+// minimum over the values they stage of 2|v| - 1 (16-bit integers, so zero wraps to the top); a
+// workgroup that saw a nonzero |v| below 2^-50 recomputes its outputs on the vector ALU in the
+// canonical order.
 typedef float f32x16_r __attribute__((ext_vector_type(16)));
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 constexpr uint16_t RM_TINY = 77 << 7;   // bf16 magnitude bits of 2^-50
-constexpr int RM_TOK = 16, RM_EXP = 64, RM_WAVES = 4, RM_RING = 8, RM_KB = 64;
+constexpr int RM_TOK = 16, RM_EXP = 64, RM_CW = 4;   // tokens per chain, experts, chain waves
+constexpr int RM_ROWS = RM_TOK * RM_CW;              // token rows of a workgroup (= staging rows)
+constexpr int RM_CH = 16;                            // chunks of 8 k per slice
+constexpr int RM_PITCH = RM_CH * 8 + 4;              // floats per staged row (16-byte pad)
+constexpr int RM_BUF = RM_ROWS * RM_PITCH;           // floats per staged operand slice
+constexpr int RM_LDS = 4 * RM_BUF * 4;               // bytes: 2 buffers x (tokens, experts)
+constexpr int RM_NTH = 64 * 2 * RM_CW;
+static_assert(RM_ROWS == RM_EXP && RM_ROWS * RM_CH == 4 * 64 * RM_CW, "staging map: 4 rows per thread");
+static_assert(RM_LDS > (160 << 10) / 2, "one workgroup per compute unit");
 
-// Packed running minimum of |v| - 1 over the 8 bf16 values of a load.
+// Packed running minimum of 2|v| - 1 over the 8 bf16 values of a chunk.
 __device__ __forceinline__ u16x2_t tiny_scan(u16x2_t mn, const uint4& v) {
   const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u16x2_t a = __builtin_bit_cast(u16x2_t, w4[i] & 0x7fff7fffu);
-    const u16x2_t one = {1, 1};
-    mn = __builtin_elementwise_min(mn, a - one);
+    const u16x2_t two = {2, 2}, mone = {0xffff, 0xffff};
+    mn = __builtin_elementwise_min(mn, __builtin_bit_cast(u16x2_t, w4[i]) * two + mone);
   }
   return mn;
 }
-__device__ __forceinline__ bool tiny_seen(u16x2_t mn) { return mn.x < RM_TINY - 1 || mn.y < RM_TINY - 1; }
+__device__ __forceinline__ bool tiny_seen(u16x2_t mn) {
+  return mn.x < 2 * RM_TINY - 1 || mn.y < 2 * RM_TINY - 1;
+}
+__device__ __forceinline__ void widen_store(float* dst, const uint4& v) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                                                  __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+  reinterpret_cast<float4*>(dst)[1] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                                                  __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+}
 
-__global__ __launch_bounds__(64 * RM_WAVES) void router_logits_mfma_kernel(const bf16_t* x, const bf16_t* w,
-                                                                        const float* bias, float* logits, int T,
-                                                                        int d, int E) {
-  // [buffer][expert row][8 chunks of 16 bytes], chunk c of row r stored at c ^ ((r >> 1) & 7): 16
-  // consecutive rows read at one chunk hit 16 distinct 16-byte bank groups
-  __shared__ uint4 wsm[2][RM_EXP * 8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tw = (blockIdx.x * RM_WAVES + wave) * RM_TOK, e0 = blockIdx.y * RM_EXP;
-  const bool active = tw < T;   // wave-uniform; an inactive wave still stages and meets the barriers
-  const int t = active ? min(tw + (lane & 15), T - 1) : 0;
-  const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * d);
-  const int nch = d >> 3, nkb = (d + RM_KB - 1) / RM_KB;
-  // staging: thread i copies chunks 2*(i%4), 2*(i%4)+1 of expert row i/4 of a 64-k slice
-  const int sr = tid >> 2, sc = (tid & 3) * 2;
-  const uint4* wsrc = reinterpret_cast<const uint4*>(w + (size_t)min(e0 + sr, E - 1) * d);
+__global__ __launch_bounds__(RM_NTH) void router_logits_mfma_kernel(const bf16_t* x, const bf16_t* w,
+                                                                   const float* bias, float* logits, int T,
+                                                                   int d, int E) {
+  extern __shared__ __attribute__((aligned(16))) float rlds[];   // [buffer][tokens | experts][row][RM_PITCH]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * RM_ROWS, e0 = blockIdx.y * RM_EXP;
+  const int nch = d >> 3, nkb = (nch + RM_CH - 1) / RM_CH;
   u16x2_t mn = {0xffff, 0xffff};
-  uint4 st[2];
-  // Loads are never skipped by a branch (indices clamped, values past the row zeroed by a select):
-  // a load under a condition makes the compiler wait for every load in flight before the next use.
-  auto stage_load = [&](int kb) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int c = kb * 8 + sc + q;
-      const uint4 v = wsrc[min(c, nch - 1)];
-      st[q] = c < nch ? v : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      mn = tiny_scan(mn, st[q]);
-      wsm[buf][sr * 8 + ((sc + q) ^ ((sr >> 1) & 7))] = st[q];
-    }
-  };
-  stage_load(0);
-  stage_store(0);
-  stage_load(min(1, nkb - 1));
-  uint4 xa[RM_RING];
-#pragma unroll
-  for (int r = 0; r < RM_RING; ++r) xa[r] = xr[min(r, nch - 1)];
-  __syncthreads();
   f32x16_r acc = {};
-  // chunk r of slice kb: the staged expert values and the token values of k = 8c..8c+7
-  auto chunk = [&](int buf, int r, int c, bool mfma) {
-    const uint4 xv = xa[r];
-    const uint4 wv = wsm[buf][lane * 8 + (r ^ ((lane >> 1) & 7))];
-    mn = tiny_scan(mn, xv);
-    xa[r] = xr[min(c + RM_RING, nch - 1)];
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-    if (mfma) {
+  if (wave >= RM_CW) {
+    // staging: thread i copies chunk i % 16 of rows i / 16 + 16 q, q = 0..3 (a row is 16 threads)
+    const int st = tid - 64 * RM_CW, sr = st >> 4, sc = st & 15;
+    const uint4* xsrc[4];
+    const uint4* wsrc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {   // k = 8c + 2i, then 8c + 2i + 1
-        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(__uint_as_float(xw[i] << 16), __uint_as_float(ww[i] << 16), acc,
-                                                   0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(__uint_as_float(xw[i] & 0xffff0000u),
-                                                   __uint_as_float(ww[i] & 0xffff0000u), acc, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      xsrc[q] = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + sr + 16 * q, T - 1) * d);
+      wsrc[q] = reinterpret_cast<const uint4*>(w + (size_t)min(e0 + sr + 16 * q, E - 1) * d);
+    }
+    uint4 sx[4], sw[4];
+    // Global loads are never under a branch (the chunk index is clamped and the value zeroed when
+    // staged): a load under a condition makes the compiler wait for every load in flight.
+    auto stage_load = [&](int kb) {
+      const int c = min(kb * RM_CH + sc, nch - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sx[q] = xsrc[q][c];
+        sw[q] = wsrc[q][c];
       }
-    }
-  };
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if ((kb + 1) * 8 <= nch) {
+    };
+    auto stage_store = [&](int buf, int kb) {
+      if ((kb + 1) * RM_CH > nch) {   // the last, partial slice: chunks past d become zeros
+        const uint32_t keep = kb * RM_CH + sc < nch ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int r = 0; r < RM_RING; ++r) chunk(buf, r, kb * 8 + r, active);
-    } else {   // the last, partial slice
-      for (int r = 0; r < RM_RING; ++r) chunk(buf, r, kb * 8 + r, active && kb * 8 + r < nch);
-    }
-    // slice kb+1 into the other buffer (last read in slice kb-1, before the previous barrier)
-    if (kb + 1 < nkb) stage_store(buf ^ 1);
-    stage_load(min(kb + 2, nkb - 1));
+        for (int q = 0; q < 4; ++q) {
+          sx[q] = make_uint4(sx[q].x & keep, sx[q].y & keep, sx[q].z & keep, sx[q].w & keep);
+          sw[q] = make_uint4(sw[q].x & keep, sw[q].y & keep, sw[q].z & keep, sw[q].w & keep);
+        }
+      }
+      float* xd = rlds + (2 * buf) * RM_BUF + sr * RM_PITCH + sc * 8;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 vx = sx[q], vw = sw[q];
+        mn = tiny_scan(tiny_scan(mn, vx), vw);
+        widen_store(xd + 16 * q * RM_PITCH, vx);
+        widen_store(xd + RM_BUF + 16 * q * RM_PITCH, vw);
+      }
+    };
+    stage_load(0);
+    stage_store(0, 0);
+    stage_load(min(1, nkb - 1));
     __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+      // slice kb+1 into the other buffer (last read in slice kb-1, before the previous barrier)
+      if (kb + 1 < nkb) stage_store((kb + 1) & 1, kb + 1);
+      stage_load(min(kb + 2, nkb - 1));
+      __syncthreads();
+    }
+  } else {
+    // chain wave: token row wave*16 + lane%16 (operand A), expert row lane (operand B)
+    const float4* xr = reinterpret_cast<const float4*>(rlds + (wave * RM_TOK + (lane & 15)) * RM_PITCH);
+    const float4* wr = reinterpret_cast<const float4*>(rlds + RM_BUF + lane * RM_PITCH);
+    constexpr int BUF4 = 2 * RM_BUF / 4;   // float4s from one buffer to the next
+    __syncthreads();
+    float4 xn0 = xr[0], xn1 = xr[1], wn0 = wr[0], wn1 = wr[1];
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int o = (kb & 1) * BUF4;
+#pragma unroll
+      for (int r = 0; r < RM_CH; ++r) {
+        const float4 x0 = xn0, x1 = xn1, w0 = wn0, w1 = wn1;
+        if (r + 1 < RM_CH) {
+          xn0 = xr[o + 2 * r + 2];
+          xn1 = xr[o + 2 * r + 3];
+          wn0 = wr[o + 2 * r + 2];
+          wn1 = wr[o + 2 * r + 3];
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keeps the reads ahead of this chunk's products
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const float ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x1f32(xs[i], ws[i], acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      const int on = ((kb + 1) & 1) * BUF4;
+      xn0 = xr[on];
+      xn1 = xr[on + 1];
+      wn0 = wr[on];
+      wn1 = wr[on + 1];
+    }
   }
   const bool tiny = __syncthreads_or(tiny_seen(mn)) != 0;
-  if (!active) return;
+  const int tw = t0 + wave * RM_TOK;
+  if (wave >= RM_CW || tw >= T) return;
   if (tiny) {
     // canonical order on the vector ALU: each product rounded, then the sum (contraction is off)
 #pragma unroll 1
@@ -579,9 +622,12 @@ hipError_t launch_router_logits(const void* x, const void* w, const float* bias,
                                 int T, int d, int E, bool bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (bf16 && d % 8 == 0) {
-    hipLaunchKernelGGL(router_logits_mfma_kernel, dim3(ceil_div(T, RM_TOK * RM_WAVES), ceil_div(E, RM_EXP)),
-                       dim3(64 * RM_WAVES), 0, s, reinterpret_cast<const bf16_t*>(x),
-                       reinterpret_cast<const bf16_t*>(w), bias, logits, T, d, E);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(router_logits_mfma_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, RM_LDS);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(router_logits_mfma_kernel, dim3(ceil_div(T, RM_ROWS), ceil_div(E, RM_EXP)), dim3(RM_NTH),
+                       RM_LDS, s, reinterpret_cast<const bf16_t*>(x), reinterpret_cast<const bf16_t*>(w), bias,
+                       logits, T, d, E);
     return hipGetLastError();
   }
   dim3 grid(ceil_div(T, RT), ceil_div(E, RE));

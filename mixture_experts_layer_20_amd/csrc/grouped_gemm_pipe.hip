@@ -47,11 +47,27 @@ constexpr int BM = 256, BN = 256, BKS = 64, NSTAGE = 2;
 constexpr int NW = 8, NTH = 64 * NW;  // two waves per SIMD
 constexpr int WGN = 4;                // wave w: row half wm = w / WGN, column quarter wn = w % WGN
 constexpr int MI = 4, NI = 2;         // 32x32 blocks per wave: 128 rows x 64 columns
-constexpr int LPW = 64 / NW;          // direct loads (1 KiB each) per wave per 64 KiB stage
-constexpr int LPO = LPW / 2;          // of them per operand
-constexpr int OPB = 256 * BKS * 2;         // one operand tile of one stage: 32 KiB
-constexpr int STAGE = 2 * OPB;             // 64 KiB
-constexpr int LDS_BYTES = NSTAGE * STAGE;  // 128 KiB
+constexpr int MIX = 5, BMX = 320;     // a tile of 257..BMX rows (modes with row capacity BMX): 160 x 64
+constexpr int LPB = 4;                // direct loads (1 KiB each) per wave per stage of operand B
+constexpr int OPB = 256 * BKS * 2;    // operand B tile of one stage: 32 KiB
+
+// Modes whose tiles hold up to BMX rows (operand A K-contiguous, registers to spare): an expert of
+// 257..320 rows is one tile rather than a full tile and a remainder tile that streams the same
+// weights again.  The others hold up to BM rows.
+template <int MODE>
+constexpr bool has_x() { return MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD; }
+template <int MODE>
+constexpr int rows_a() { return has_x<MODE>() ? BMX : BM; }          // operand A rows per stage
+template <int MODE>
+constexpr int opa() { return rows_a<MODE>() * BKS * 2; }             // operand A bytes per stage
+template <int MODE>
+constexpr int lpa() { return opa<MODE>() / 1024 / NW; }              // its direct loads per wave
+template <int MODE>
+constexpr int lpw() { return lpa<MODE>() + LPB; }                    // direct loads per wave per stage
+template <int MODE>
+constexpr int stage_bytes() { return opa<MODE>() + OPB; }
+template <int MODE>
+constexpr int mi_max() { return has_x<MODE>() ? MIX : MI; }
 constexpr int PMAXG = 1024;   // groups of the first set
 constexpr int PMAXG1 = 64;    // groups of the second set (the shared expert: 1)
 constexpr int WG_NB = 8;      // tile columns per block of the weight-gradient tile order
@@ -89,12 +105,13 @@ __device__ __forceinline__ int kc_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mc_phys_chunk(int k, int chunk) { return chunk ^ ((k & 3) << 2); }
 
 // ---- Tiles -------------------------------------------------------------------------------
-// Output tile: set seg, group g, rows [m0, min(m0 + 256, m_end)), tile column nt, K range
-// [k_begin, k_end) in nk steps of 64 (split: K chunk index of a split weight gradient; ks: the
-// split count).  half: at most 128 rows remain (ragged M only), multiplied as a 128x256 tile.
+// Output tile: set seg, group g, rows [m0, m_end), tile column nt, K range [k_begin, k_end) in nk
+// steps of 64 (split: K chunk index of a split weight gradient; ks: the split count).  half: at
+// most 128 rows (ragged M only), multiplied as a 128x256 tile.  x: more than 256 rows (at most
+// BMX), multiplied as a 320x256 tile, 160 rows per wave.
 struct Tile {
   int seg, g, m0, m_end, nt, k_begin, k_end, nk, split, ks;
-  bool half;
+  bool half, x;
 };
 
 // The arguments of one set of groups (set 1: the second set of a merged launch), in the layout
@@ -154,6 +171,20 @@ __device__ __forceinline__ void group_rows_lds(uint32_t offs, int g, int& lo, in
   hi = max(lo, uniform(lds_load_i32(offs + 4 * (g + 1))));
 }
 
+// Rows per tile of a group of R rows (ragged M) and the group's tiles: ceil(R / BMX) tiles of
+// equal height where the mode has row capacity BMX (so no tile is a short remainder that streams
+// the weights again), else 256-row tiles and a remainder.
+template <int MODE>
+__device__ __forceinline__ int group_tiles(int R) {
+  return has_x<MODE>() ? (R + BMX - 1) / BMX : (R + BM - 1) / BM;
+}
+template <int MODE>
+__device__ __forceinline__ int tile_rows(int R) {
+  if constexpr (!has_x<MODE>()) return BM;
+  const int n = max(1, group_tiles<MODE>(R));
+  return (R + n - 1) / n;
+}
+
 template <int MODE>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&geo)[2], int L) {
   Tile t;
@@ -166,6 +197,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
   const uint32_t pref = t.seg ? geo[1].pref : geo[0].pref, offs = t.seg ? geo[1].offs : geo[0].offs;
   t.split = 0;
   t.half = false;
+  t.x = false;
   if constexpr (!Traits<MODE>::raggedK) {
     // Tile order: group by group; inside a group, bands of `band` row tiles, and inside a band
     // column by column.  A band spans about as many tiles as an XCD runs at once, so the tiles
@@ -187,9 +219,11 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
     const int mt = b * MB + (r - t.nt * mb);
     int r0, r1;
     group_rows_lds(offs, t.g, r0, r1);
-    t.m0 = r0 + mt * BM;
-    t.m_end = r1;
-    t.half = r1 - t.m0 <= BM / 2;
+    const int rpt = tile_rows<MODE>(r1 - r0);
+    t.m0 = r0 + mt * rpt;
+    t.m_end = min(r1, t.m0 + rpt);
+    t.half = t.m_end - t.m0 <= BM / 2;
+    t.x = t.m_end - t.m0 > BM;
     t.k_begin = 0;
     t.k_end = mode_K(MODE, p.d, p.f);
   } else {
@@ -228,23 +262,27 @@ __device__ __forceinline__ Tile deal_tile(const GemmArgs& p, const SegGeo (&geo)
   if (Traits<MODE>::raggedK || i < dl.q) return decode_tile<MODE>(p, geo, tile_at(dl, i));
   const int h = (i - dl.q) >> 1, s = (i - dl.q) & 1;
   Tile t = decode_tile<MODE>(p, geo, tile_at(dl, dl.q + h));
-  t.m0 += s * (BM / 2);
-  t.m_end = min(t.m_end, t.m0 + BM / 2);
-  t.half = true;
+  const int hb = t.x ? BMX / 2 : BM / 2;   // a tile of more than 256 rows: two of at most 160
+  t.m0 += s * hb;
+  t.m_end = min(t.m_end, t.m0 + hb);
+  t.half = t.m_end - t.m0 <= BM / 2;
+  t.x = false;
   if (t.m0 >= t.m_end) t.nk = 0;
   return t;
 }
 
 // ---- Direct loads ------------------------------------------------------------------------
-// Load IDX (below LPO: operand A, else operand B) of the stage starting at k0 of tile t: 16 bytes
-// per lane into LDS slot q = (wave * LPO + j) * 64 + lane of the operand tile.
+// Load IDX (below lpa: operand A, else operand B) of the stage starting at k0 of tile t: 16 bytes
+// per lane into LDS slot q = (wave * lp + j) * 64 + lane of the operand tile (lp: the operand's
+// loads per wave).
 // KC: slot q = (row q/8, physical chunk q%8).  MC: slot q = (k q/32, physical chunk q%32).
 template <int MODE, int IDX>
 __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const Tile& t, int k0, int wave, int lane) {
-  constexpr bool A_OP = IDX < LPO;
-  constexpr int j = IDX % LPO;
+  constexpr bool A_OP = IDX < lpa<MODE>();
+  constexpr int LP = A_OP ? lpa<MODE>() : LPB;
+  constexpr int j = A_OP ? IDX : IDX - lpa<MODE>();
   constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
-  const int q = (wave * LPO + j) * 64 + lane;
+  const int q = (wave * LP + j) * 64 + lane;
   const bf16_t* src;
   if constexpr (kc) {
     const int row = q >> 3;
@@ -265,7 +303,7 @@ __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const
       src = reinterpret_cast<const bf16_t*>(g_zero_rows);
     }
   }
-  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * LPO + j) * 1024),
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : opa<MODE>()) + (wave * LP + j) * 1024),
                                    16, 0, 0);
 }
 
@@ -274,8 +312,8 @@ __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const
 // carry k0 and the tile position.
 template <int MODE>
 __device__ __forceinline__ uint32_t load_offset(const GemmArgs& p, const Tile& t, int idx, int wave, int lane) {
-  const bool a_op = idx < LPO;
-  const int q = (wave * LPO + idx % LPO) * 64 + lane;
+  const bool a_op = idx < lpa<MODE>();
+  const int q = (a_op ? wave * lpa<MODE>() + idx : wave * LPB + idx - lpa<MODE>()) * 64 + lane;
   const bool kc = a_op ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
   if (kc) {
     const int row = q >> 3;
@@ -301,7 +339,7 @@ __device__ __forceinline__ uint32_t load_offset(const GemmArgs& p, const Tile& t
 // load's offset plus j times a wave-uniform step, with the swizzle change of odd j applied as an
 // XOR (issue_fast).
 struct LoadOffs {
-  uint32_t a[LPO];
+  uint32_t a[MIX];   // lpa loads (at most 5)
   uint32_t b;
   uint32_t sa, sb;   // steps (bytes) between consecutive loads of A (not K-contiguous) and of B
 };
@@ -333,7 +371,7 @@ __device__ __forceinline__ void stage_bases(const GemmArgs& p, const Tile& t, in
   if constexpr (MODE == GEMM_UP_FWD) {
     sa = a + ((size_t)t.m0 * d + k0) * 2;
     // B tile rows 0..127 are W1 (gate) rows, 128..255 the same W3 (up) rows; wave w loads rows
-    // 16 * LPO * w .. + 16 * LPO - 1
+    // 8 * LPB * w .. + 8 * LPB - 1
     sb = reinterpret_cast<const char*>(wave < NW / 2 ? p.b0 : p.b1) + ((g * f + (size_t)t.nt * (BN / 2)) * d + k0) * 2;
   } else if constexpr (MODE == GEMM_DOWN_FWD) {
     sa = a + ((size_t)t.m0 * f + k0) * 2;
@@ -358,8 +396,9 @@ __device__ __forceinline__ void stage_bases(const GemmArgs& p, const Tile& t, in
 template <int MODE, int IDX>
 __device__ __forceinline__ void issue_fast(char* stage, const char* sa, const char* sb, const LoadOffs& lo,
                                            int k_left, int wave, int lane) {
-  constexpr bool A_OP = IDX < LPO;
-  constexpr int J = IDX % LPO;
+  constexpr bool A_OP = IDX < lpa<MODE>();
+  constexpr int LP = A_OP ? lpa<MODE>() : LPB;
+  constexpr int J = A_OP ? IDX : IDX - lpa<MODE>();
   // Load J is 8 K-contiguous rows (2 K rows) after load 0, which moves the row swizzle by 4
   // chunks (the window swizzle by 8 chunks) for odd J: a 64-byte (128-byte) XOR on top of the step.
   constexpr bool KC = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
@@ -370,12 +409,12 @@ __device__ __forceinline__ void issue_fast(char* stage, const char* sa, const ch
   else off = (lo.b + (uint32_t)J * lo.sb) ^ FLIP;
   const char* src = (A_OP ? sa : sb) + off;
   if constexpr (Traits<MODE>::raggedK) {
-    // K-strided operands: lane reads K row (wave * LPO + j) * 2 + lane / 32 of the stage; rows
+    // K-strided operands: lane reads K row (wave * LP + J) * 2 + lane / 32 of the stage; rows
     // past the group's end read zeros.
-    const int kr = (wave * LPO + IDX % LPO) * 2 + (lane >> 5);
+    const int kr = (wave * LP + J) * 2 + (lane >> 5);
     if (kr >= k_left) src = reinterpret_cast<const char*>(g_zero_rows);
   }
-  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : OPB) + (wave * LPO + IDX % LPO) * 1024),
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : opa<MODE>()) + (wave * LP + J) * 1024),
                                    16, 0, 0);
 }
 
@@ -393,10 +432,11 @@ struct StageSrc {
 // load issue, a fragment read or the barrier.  A tile with at most 128 rows (the last rows of a
 // group) keeps the same load stream; the waves of the second row half skip its MFMAs.
 
-// Row (A) / column (B) of the wave's MFMA block i inside the 256-wide operand tile.
+// Row (A) / column (B) of the wave's MFMA block i inside the operand tile (M blocks per wave row:
+// the wave's rows are wm * 32M ..).
 template <int MODE, bool A_OP>
-__device__ __forceinline__ int block_row(int wm, int wn, int i) {
-  if constexpr (A_OP) return wm * 128 + 32 * i;
+__device__ __forceinline__ int block_row(int wm, int wn, int i, int M = MI) {
+  if constexpr (A_OP) return wm * 32 * M + 32 * i;
   // gate/up: the wave's 32 gate (W1) columns in block 0, the same up (W3) columns in block 1
   else if constexpr (MODE == GEMM_UP_FWD) return i == 0 ? wn * 32 : 128 + wn * 32;
   else return wn * 64 + 32 * i;
@@ -411,10 +451,10 @@ __device__ __forceinline__ int block_row(int wm, int wn, int i) {
 //      address bits 6-7 (block 0 starts at a multiple of 64 columns).  The second transposed read
 //      of a block is 4 k-rows = 2048 bytes further.
 template <int MODE, bool A_OP>
-__device__ __forceinline__ uint32_t frag_base(int s, int wm, int wn, int lane) {
+__device__ __forceinline__ uint32_t frag_base(int s, int wm, int wn, int lane, int M = MI) {
   constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
-  const uint32_t base = A_OP ? 0 : OPB;
-  const int rb = block_row<MODE, A_OP>(wm, wn, 0);
+  const uint32_t base = A_OP ? 0 : opa<MODE>();
+  const int rb = block_row<MODE, A_OP>(wm, wn, 0, M);
   if constexpr (kc) {
     const int row = rb + (lane & 31);
     const int chunk = s * 2 + (lane >> 5);
@@ -477,7 +517,7 @@ struct Frag<false, NB> {
 };
 
 template <int MODE>
-using FragA = Frag<Traits<MODE>::a_kcontig, MI>;
+using FragA = Frag<Traits<MODE>::a_kcontig, mi_max<MODE>()>;
 template <int MODE>
 using FragB = Frag<Traits<MODE>::b_kcontig, NI>;
 
@@ -496,83 +536,85 @@ __device__ __forceinline__ void frag_wait(FragA<MODE>& a, FragB<MODE>& b) {
 // next MFMA queued while the wave issues a read or a load.  ACT = false: a wave of the idle row
 // half of a 128-row tile, which issues only the loads.
 
-// MFMAs per phase and fragment reads per substep.
-constexpr int NS = MI * NI;
-template <int MODE>
-constexpr int nreads_a() { return MI * FragA<MODE>::PER_BLOCK; }
+// MFMAs per phase and fragment reads per substep of a tile with M blocks per wave row.
+template <int M>
+constexpr int n_slots() { return M * NI; }
+template <int MODE, int M>
+constexpr int nreads_a() { return M * FragA<MODE>::PER_BLOCK; }
 template <int MODE>
 constexpr int nreads_b() { return NI * FragB<MODE>::PER_BLOCK; }
 
 // The B fragment goes in as the MFMA's first operand: the accumulator block is then the
 // transpose of the output block, so each lane ends up with consecutive output columns of one row.
-template <int MODE, int Q>
-__device__ __forceinline__ void mfma_slot(f32x16_t (&acc)[MI][NI], const FragA<MODE>& a, const FragB<MODE>& b) {
+template <int MODE, int Q, int M>
+__device__ __forceinline__ void mfma_slot(f32x16_t (&acc)[M][NI], const FragA<MODE>& a, const FragB<MODE>& b) {
   constexpr int i = Q / NI, j = Q % NI;
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b.get(j), a.get(i), acc[i][j], 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Fragment read R of a substep (A's reads first, then B's).
-template <int MODE, int R>
+template <int MODE, int R, int M>
 __device__ __forceinline__ void read_slot(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
-  constexpr int NRA = nreads_a<MODE>(), NRB = nreads_b<MODE>();
+  constexpr int NRA = nreads_a<MODE, M>(), NRB = nreads_b<MODE>();
   if constexpr (R < NRA) a.template read_one<MODE, true, R>(ra);
   else if constexpr (R < NRA + NRB) b.template read_one<MODE, false, R - NRA>(rb);
 }
 
 // Reads spread over the slots: ceil(reads / slots) per slot.
-template <int MODE>
-constexpr int reads_per_slot() { return (nreads_a<MODE>() + nreads_b<MODE>() + NS - 1) / NS; }
-template <int MODE, int Q, int I>
+template <int MODE, int M>
+constexpr int reads_per_slot() { return (nreads_a<MODE, M>() + nreads_b<MODE>() + n_slots<M>() - 1) / n_slots<M>(); }
+template <int MODE, int Q, int I, int M>
 __device__ __forceinline__ void slot_reads(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
-  if constexpr (I < reads_per_slot<MODE>()) {
-    read_slot<MODE, Q + I * NS>(a, b, ra, rb);
-    slot_reads<MODE, Q, I + 1>(a, b, ra, rb);
+  if constexpr (I < reads_per_slot<MODE, M>()) {
+    read_slot<MODE, Q + I * n_slots<M>(), M>(a, b, ra, rb);
+    slot_reads<MODE, Q, I + 1, M>(a, b, ra, rb);
   }
 }
 
-// Direct loads of slot Q: the LPW loads of a stage are spread evenly over the NS slots of a phase
+// Direct loads of slot Q: the lpw loads of a stage are spread evenly over the slots of a phase
 // (a burst of direct loads stalls the issuing wave).
-template <int MODE, int Q, int I>
+template <int MODE, int Q, int I, int M>
 __device__ __forceinline__ void slot_loads(char* stage, const StageSrc& ss, const LoadOffs& voff, int wave,
                                            int lane) {
+  constexpr int NS = n_slots<M>(), LPW = lpw<MODE>();
   constexpr int PER = (LPW + NS - 1) / NS, EVERY = NS > LPW ? NS / LPW : 1;
   if constexpr (I < PER && Q % EVERY == 0 && (Q / EVERY) * PER + I < LPW) {
     issue_fast<MODE, (Q / EVERY) * PER + I>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
-    slot_loads<MODE, Q, I + 1>(stage, ss, voff, wave, lane);
+    slot_loads<MODE, Q, I + 1, M>(stage, ss, voff, wave, lane);
   }
 }
 
 // One phase of a K step: the MFMAs of the current substep (fragments ac, bc); the reads of the
 // next substep into an, bn at ra/rb; with LOADS, the loads of the stage two steps ahead into this
 // step's slot.
-template <int MODE, bool ACT, bool LOADS, int Q>
-__device__ __forceinline__ void phase(f32x16_t (&acc)[MI][NI], const FragA<MODE>& ac, const FragB<MODE>& bc,
+template <int MODE, bool ACT, bool LOADS, int Q, int M>
+__device__ __forceinline__ void phase(f32x16_t (&acc)[M][NI], const FragA<MODE>& ac, const FragB<MODE>& bc,
                                       FragA<MODE>& an, FragB<MODE>& bn, uint32_t ra, uint32_t rb, char* stage,
                                       const StageSrc& ss, const LoadOffs& voff, int wave, int lane) {
-  if constexpr (Q < NS) {
+  if constexpr (Q < n_slots<M>()) {
     if constexpr (ACT) {
-      mfma_slot<MODE, Q>(acc, ac, bc);
-      slot_reads<MODE, Q, 0>(an, bn, ra, rb);
+      mfma_slot<MODE, Q, M>(acc, ac, bc);
+      slot_reads<MODE, Q, 0, M>(an, bn, ra, rb);
     }
-    if constexpr (LOADS) slot_loads<MODE, Q, 0>(stage, ss, voff, wave, lane);
+    if constexpr (LOADS) slot_loads<MODE, Q, 0, M>(stage, ss, voff, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
-    phase<MODE, ACT, LOADS, Q + 1>(acc, ac, bc, an, bn, ra, rb, stage, ss, voff, wave, lane);
+    phase<MODE, ACT, LOADS, Q + 1, M>(acc, ac, bc, an, bn, ra, rb, stage, ss, voff, wave, lane);
   }
 }
 
 // All reads of one substep's fragments (prologue, start of a tile).
-template <int MODE, int R>
+template <int MODE, int R, int M>
 __device__ __forceinline__ void read_all(FragA<MODE>& a, FragB<MODE>& b, uint32_t ra, uint32_t rb) {
-  if constexpr (R < nreads_a<MODE>() + nreads_b<MODE>()) {
-    read_slot<MODE, R>(a, b, ra, rb);
-    read_all<MODE, R + 1>(a, b, ra, rb);
+  if constexpr (R < nreads_a<MODE, M>() + nreads_b<MODE>()) {
+    read_slot<MODE, R, M>(a, b, ra, rb);
+    read_all<MODE, R + 1, M>(a, b, ra, rb);
   }
 }
 
 template <int MODE, int IDX>
 __device__ __forceinline__ void issue_all(const GemmArgs& p, char* stage, const Tile& t, int k0, int wave, int lane) {
-  if constexpr (IDX < LPW) {
+  if constexpr (IDX < lpw<MODE>()) {
     issue_load<MODE, IDX>(p, stage, t, k0, wave, lane);
     issue_all<MODE, IDX + 1>(p, stage, t, k0, wave, lane);
   }
@@ -618,15 +660,16 @@ __device__ __forceinline__ u32x4_t pack8_bf16(const float (&x)[8]) {
   const u32x4_t w = {a.x, a.y, b.x, b.y};
   return w;
 }
-// The output windows of one wave's 128x128 block of a tile.
+// The output windows of one wave's block of a tile (wrows rows).
 struct OutWins {
   OutWin w[3];
 };
 
 template <int MODE>
-__device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, int row0, int col0, float* partial) {
+__device__ __forceinline__ OutWins out_wins(const GemmArgs& p, const Tile& t, int row0, int col0, float* partial,
+                                            int wrows = 128) {
   OutWins o;
-  const int rows = min(128, t.m_end - row0);
+  const int rows = min(wrows, t.m_end - row0);
   const size_t d = p.d, f = p.f;
   if constexpr (MODE == GEMM_UP_FWD) {
     const size_t e = (size_t)row0 * f + col0;
@@ -772,8 +815,11 @@ constexpr int epilogue_stores() {
 // leaves lane l with columns 16H + 8*(l/32) + 0..7.
 __device__ __forceinline__ void block_half(const f32x16_t& c, int h, float (&x)[8]) {
   float lo[4], hi[4];
-  MOE_AGPR_READ4(c, 8 * h, lo);
-  MOE_AGPR_READ4(c, 8 * h + 4, hi);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = c[8 * h + e];
+    hi[e] = c[8 * h + 4 + e];
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo[e]), __float_as_uint(hi[e]), false, false);
@@ -839,12 +885,12 @@ constexpr int aux_younger() {
 // Blocks IDX.. of the wave's accumulators, unrolled at compile time (the loop unroller gives up on
 // the larger epilogues, and a run-time block index would put the accumulators in scratch memory).
 // The down-projection dgrad keeps the pre-activation loads AUX_AHEAD blocks ahead of their use.
-template <int MODE, int IDX>
-__device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& o, const f32x16_t (&acc)[MI][NI],
+template <int MODE, int IDX, int M>
+__device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& o, const f32x16_t (&acc)[M][NI],
                                               int row0, int col0, int m_end, int lane,
                                               AuxBlock (&aux)[AUX_AHEAD + 1], int ksplit) {
   constexpr int NJ = out_nj<MODE>();
-  constexpr int NB = MI * NJ;
+  constexpr int NB = M * NJ;
   constexpr int NA = AUX_AHEAD + 1;
   if constexpr (IDX < NB) {
     if constexpr (MODE == GEMM_DOWN_BWD) {
@@ -857,7 +903,7 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& 
     constexpr int nu = (MODE == GEMM_UP_FWD) ? ni + NJ : ni;
     epilogue_block<MODE>(p, o, acc[mi][ni], acc[mi][nu], block_r<MODE, IDX>(), block_c<MODE, IDX>(), aux[IDX % NA],
                          ksplit, lane);
-    epilogue_from<MODE, IDX + 1>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
+    epilogue_from<MODE, IDX + 1, M>(p, o, acc, row0, col0, m_end, lane, aux, ksplit);
   }
 }
 
@@ -871,11 +917,11 @@ __device__ __forceinline__ void aux_prologue(const GemmArgs& p, int row0, int co
   }
 }
 
-// The wave's output block of a tile: rows wm*128.. and its 64 columns (32 H columns for the gate/up
+// The wave's output block of a tile: rows wm*32M.. and its 64 columns (32 H columns for the gate/up
 // GEMM).  The idle row half of a 128-row tile runs it too: its window holds no rows, so every store
 // is dropped, and it issues the same number of memory instructions as the others.
-template <int MODE>
-__device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[MI][NI], const Tile& t,
+template <int MODE, int M>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[M][NI], const Tile& t,
                                               int wm, int wn, int lane, float* partial) {
   // The accumulator reads are opaque to the hazard checker: leave the last MFMA's write-back
   // (at most 18 wait states) behind before the first of them.
@@ -883,13 +929,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
   // The lane index through a volatile move: the per-lane addressing below is then computed here,
   // not hoisted out of the tile loop into registers the K loop would have to keep (or spill).
   asm volatile("v_mov_b32 %0, %0" : "+v"(lane));
-  const int row0 = t.m0 + wm * 128;
+  const int row0 = t.m0 + wm * 32 * M;
   const int col0 = (MODE == GEMM_UP_FWD) ? t.nt * (BN / 2) + wn * 32 : t.nt * BN + wn * 64;
-  const OutWins o = out_wins<MODE>(p, t, row0, col0, partial);
+  const OutWins o = out_wins<MODE>(p, t, row0, col0, partial, 32 * M);
   const int ksplit = t.ks;
   AuxBlock aux[AUX_AHEAD + 1];
   if constexpr (MODE == GEMM_DOWN_BWD) aux_prologue<MODE, 0>(p, row0, col0, t.m_end, aux, lane);
-  epilogue_from<MODE, 0>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
+  epilogue_from<MODE, 0, M>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
 }
 
 // Output of a tile with an empty K range (a weight gradient of an expert without tokens): zeros.
@@ -907,8 +953,9 @@ __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int 
     for (int ni = 0; ni < NI; ++ni) store_block<MODE>(p, o, mi * 32, ni * 32, z, z, zx, ksplit, lane);
 }
 
-// Per-group tile prefix (ragged-M modes): pref[g] = 256-row tiles of the groups before g, from
-// the clamped offsets in offs.
+// Per-group tile prefix (ragged-M modes): pref[g] = tiles (group_tiles) of the groups before g,
+// from the clamped offsets in offs.
+template <int MODE>
 __device__ __forceinline__ void tile_prefix_lds(int G, const int* offs, int* pref, int* scratch) {
   const int tid = threadIdx.x;
   if (tid == 0) scratch[NTH] = 0;
@@ -918,7 +965,7 @@ __device__ __forceinline__ void tile_prefix_lds(int G, const int* offs, int* pre
     int c = 0;
     if (g < G) {
       const int lo = offs[g], hi = max(lo, offs[g + 1]);
-      c = (hi - lo + BM - 1) / BM;
+      c = group_tiles<MODE>(hi - lo);
     }
     scratch[tid] = c;
     __syncthreads();
@@ -949,7 +996,7 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 
 // Producer of the load stream: the tile and K step of the next stage to load.  Once the stream
 // runs out it keeps reloading the last stage (valid memory, into slots nobody reads again), so
-// every K step issues exactly LPW loads per wave and the vmcnt arithmetic stays fixed.
+// every K step issues exactly lpw loads per wave and the vmcnt arithmetic stays fixed.
 struct Producer {
   Tile t;
   int i, k;        // this XCD's tile list position, K step
@@ -976,8 +1023,8 @@ __device__ __forceinline__ void set_offsets(Producer& pr, const GemmArgs& p, int
   const GemmArgs q = seg_args(p, pr.t.seg);
   constexpr bool kca = Traits<MODE>::a_kcontig;
 #pragma unroll
-  for (int i = 0; i < (kca ? LPO : 1); ++i) pr.lo.a[i] = load_offset<MODE>(q, pr.t, i, wave, lane);
-  pr.lo.b = load_offset<MODE>(q, pr.t, LPO, wave, lane);
+  for (int i = 0; i < (kca ? lpa<MODE>() : 1); ++i) pr.lo.a[i] = load_offset<MODE>(q, pr.t, i, wave, lane);
+  pr.lo.b = load_offset<MODE>(q, pr.t, lpa<MODE>(), wave, lane);
   pr.lo.sa = (uint32_t)uniform((int)load_step<MODE, true>(q));
   pr.lo.sb = (uint32_t)uniform((int)load_step<MODE, false>(q));
   pr.ss = stage_src<MODE>(pr, p, wave);
@@ -1021,12 +1068,13 @@ __device__ __forceinline__ void advance(Producer& pr, const GemmArgs& p, const S
 //      address is (base + sb) XOR 32s (sb and base's row part leave bits 5-6 clear);
 //  MC: the window swizzle depends on k mod 4, the same in every substep, so it is base + sb + 8192s.
 struct FragBases {
-  uint32_t a, b;
+  uint32_t a, ax, b;   // ax: operand A of a tile of more than 256 rows (160 rows per wave)
 };
 template <int MODE>
 __device__ __forceinline__ FragBases frag_bases(uint32_t lds0, int wm, int wn, int lane) {
   FragBases f;
   f.a = lds0 + frag_base<MODE, true>(0, wm, wn, lane);
+  f.ax = lds0 + frag_base<MODE, true>(0, wm, wn, lane, MIX);
   f.b = lds0 + frag_base<MODE, false>(0, wm, wn, lane);
   return f;
 }
@@ -1037,32 +1085,35 @@ __device__ __forceinline__ uint32_t sub_addr(uint32_t base, uint32_t sb) {
   else return base + sb + (uint32_t)(8192 * S);
 }
 
-// One output tile: its K steps j, j+1, ... and its epilogue.  ACT: on entry a0/b0 hold substep 0
-// of stage j.  !ACT (the idle row half of a 128-row tile): the wave issues its share of the load
-// stream and the epilogue's memory instructions only, and reads no fragments.
+// One output tile: its K steps j, j+1, ... and its epilogue.  M blocks per wave row (MI, or MIX
+// for a tile of more than 256 rows).  ACT: on entry a0/b0 hold substep 0 of stage j.  !ACT (the
+// idle row half of a 128-row tile): the wave issues its share of the load stream and the
+// epilogue's memory instructions only, and reads no fragments.
 //
 // A K step (stage j, slot j & 1): four phases of 16-deep substeps whose fragments alternate
 // between the register sets 0 and 1; the fourth phase reads substep 0 of stage j + 1 from the other
 // slot and loads stage j + 2 into this one, which every wave has finished reading by then.
-template <int MODE, bool ACT>
+template <int MODE, bool ACT, int M>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& ct, const FragBases& fb, FragA<MODE>& a0,
                                          FragB<MODE>& b0, FragA<MODE>& a1, FragB<MODE>& b1, int& j,
                                          int& since_epi, Producer& pr, const SegGeo (&geo)[2], const Deal& dl,
                                          int nbx, int wm, int wn, int wave, int lane, char* lds, float* partial) {
-  f32x16_t acc[MI][NI];
+  constexpr uint32_t STAGE = stage_bytes<MODE>();
+  const uint32_t fa = M == MIX ? fb.ax : fb.a;
+  f32x16_t acc[M][NI];
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < M; ++i)
 #pragma unroll
     for (int jj = 0; jj < NI; ++jj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
   for (int kc = 0; kc < ct.nk; ++kc, ++j) {
     const uint32_t sb = (j & 1) * STAGE;
-    phase<MODE, ACT, false, 0>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 1>(fb.a, sb), sub_addr<MODE, false, 1>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
+    phase<MODE, ACT, false, 0, M>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 1>(fa, sb), sub_addr<MODE, false, 1>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
     if constexpr (ACT) frag_wait<MODE>(a1, b1);
-    phase<MODE, ACT, false, 0>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 2>(fb.a, sb), sub_addr<MODE, false, 2>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
+    phase<MODE, ACT, false, 0, M>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 2>(fa, sb), sub_addr<MODE, false, 2>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
     if constexpr (ACT) frag_wait<MODE>(a0, b0);
-    phase<MODE, ACT, false, 0>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 3>(fb.a, sb), sub_addr<MODE, false, 3>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
+    phase<MODE, ACT, false, 0, M>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 3>(fa, sb), sub_addr<MODE, false, 3>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
     if constexpr (ACT) frag_wait<MODE>(a1, b1);
     // Stage j+1 has landed once nothing issued before the last epilogue's stores is outstanding
     // (the first step after an epilogue; at least epilogue_stores() of them follow the stage's
@@ -1071,19 +1122,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& ct, cons
     else wait_vm<0>();
     barrier();
     const uint32_t sn = ((j + 1) & 1) * STAGE;
-    phase<MODE, ACT, true, 0>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 0>(fb.a, sn), sub_addr<MODE, false, 0>(fb.b, sn), lds + sb, pr.ss, pr.lo, wave, lane);
+    phase<MODE, ACT, true, 0, M>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 0>(fa, sn), sub_addr<MODE, false, 0>(fb.b, sn), lds + sb, pr.ss, pr.lo, wave, lane);
     advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
     if constexpr (ACT) frag_wait<MODE>(a0, b0);
     ++since_epi;
   }
-  epilogue_tile<MODE>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
+  epilogue_tile<MODE, M>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
   since_epi = 0;
 }
 
 template <int MODE>
 __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int ksplit, float* partial) {
   typedef Traits<MODE> TR;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  constexpr int STAGE = stage_bytes<MODE>();
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];
   __shared__ int pref_s[PMAXG + 1];
   __shared__ int offs_s[PMAXG + 1];
   __shared__ int pref1_s[PMAXG1 + 1];
@@ -1122,7 +1174,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     } else if constexpr (!TR::raggedK) {
       int* offs_tab = sg ? offs1_s : offs_s;
       int* pref_tab = sg ? pref1_s : pref_s;
-      tile_prefix_lds(G, offs_tab, pref_tab, scan_scratch);
+      tile_prefix_lds<MODE>(G, offs_tab, pref_tab, scan_scratch);
       geo[sg].total = pref_tab[G] * geo[sg].NT;
     } else {
       geo[sg].total = G * geo[sg].ks * geo[sg].MT * geo[sg].NT;
@@ -1180,23 +1232,29 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     issue_all<MODE, 0>(seg_args(p, pr.t.seg), lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
     advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
   }
-  wait_vm<(NSTAGE - 1) * LPW>();
+  wait_vm<(NSTAGE - 1) * lpw<MODE>()>();
   barrier();
   FragA<MODE> a0, a1;
   FragB<MODE> b0, b1;
   int j = 0, since_epi = 3;
   for (;;) {
+    // Substep 0 of the tile's first stage is read here rather than kept in registers through the
+    // previous epilogue (its slot is refilled only after this wave's next barrier, and the previous
+    // tile may have had the other row layout).
+    const uint32_t sb = (j & 1) * STAGE;
     if (!TR::raggedK && ct.half && wm == 1) {
-      run_tile<MODE, false>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
-                            partial);
-    } else {
-      // Substep 0 of the tile's first stage, read here rather than kept in registers through the
-      // previous epilogue: its slot is refilled only after this wave's next barrier.
-      const uint32_t sb = (j & 1) * STAGE;
-      read_all<MODE, 0>(a0, b0, sub_addr<MODE, true, 0>(fb.a, sb), sub_addr<MODE, false, 0>(fb.b, sb));
+      run_tile<MODE, false, MI>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
+                                partial);
+    } else if (has_x<MODE>() && ct.x) {
+      read_all<MODE, 0, mi_max<MODE>()>(a0, b0, sub_addr<MODE, true, 0>(fb.ax, sb), sub_addr<MODE, false, 0>(fb.b, sb));
       frag_wait<MODE>(a0, b0);
-      run_tile<MODE, true>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
-                           partial);
+      run_tile<MODE, true, mi_max<MODE>()>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave,
+                                           lane, lds, partial);
+    } else {
+      read_all<MODE, 0, MI>(a0, b0, sub_addr<MODE, true, 0>(fb.a, sb), sub_addr<MODE, false, 0>(fb.b, sb));
+      frag_wait<MODE>(a0, b0);
+      run_tile<MODE, true, MI>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
+                               partial);
     }
     bool more = false;
     for (ic += nbx; ic < dl.n; ic += nbx) {

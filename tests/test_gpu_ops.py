@@ -209,6 +209,19 @@ def test_grouped_mlp_tile_tails(f):
     check_grouped_mlp("bf16", off, 256, f, (5,), 11)
 
 
+# Group sizes around the 320-row tile capacity of the forward and data-gradient products (one
+# tile up to 320 rows, then equal tiles of at most 320): 257..320-row tiles, 321 as two tiles of 161,
+# 577 and 641 as two and three tiles, and short groups beside them.
+X_SIZES = [300, 257, 320, 321, 0, 577, 640, 641, 960, 100, 1]
+
+
+@pytest.mark.parametrize("f", [256, 512])
+def test_grouped_mlp_320_row_tiles(f):
+    off = np.concatenate([[0], np.cumsum(X_SIZES)]).astype(np.int32)
+    log(f"grouped mlp 320-row tiles bf16 sizes={X_SIZES} f={f}")
+    check_grouped_mlp("bf16", off, 256, f, (4,), 13)
+
+
 def check_grouped_mlp(dtype, off, d, f, empties, seed):
     G, M = len(off) - 1, int(off[-1])
     P = mlp_problem(M, G, d, f, dtype, seed)

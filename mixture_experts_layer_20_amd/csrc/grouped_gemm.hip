@@ -6,18 +6,18 @@
 // Deep Dive").  Forward and dgrad GEMMs are ragged in M (rows), weight gradients are ragged in K
 // (the reduction runs over the expert's rows; an expert with no rows gets zeros).
 //
-// bf16 path: 128x128x64 workgroup tiles, 4 waves of 64x64, v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation, double-buffered LDS with one barrier per K step.  LDS tiles are always stored
-// K-contiguous ([row][k], 128-byte rows, 16-byte chunks XOR-swizzled by row) so the MFMA operand
-// reads are single 16-byte loads; operands that are K-strided in memory (weights in dgrad,
-// activations in wgrad) are transposed in registers on their way into LDS.
+// bf16 path: the pipelined 256x256 kernel (grouped_gemm_pipe.hip) for every problem whose output
+// columns are a multiple of 256; otherwise (d or f an odd multiple of 128) the kernel here:
+// 128x128x64 workgroup tiles, 4 waves of 64x64, v_mfma_f32_32x32x16_bf16 with fp32 accumulation,
+// double-buffered LDS with one barrier per K step.  Its LDS tiles are always stored K-contiguous
+// ([row][k], 128-byte rows, 16-byte chunks XOR-swizzled by row) so the MFMA operand reads are
+// single 16-byte loads; operands that are K-strided in memory (weights in dgrad, activations in
+// wgrad) are transposed in registers on their way into LDS.
 // fp32 path: a plain LDS-tiled FMA kernel with the same tile schedule and epilogues.
 #include "common.h"
 #include "gemm_common.h"
 
 #include <algorithm>
-#include <cstdio>
-#include <cstdlib>
 
 namespace moe {
 namespace {
@@ -421,233 +421,6 @@ __global__ __launch_bounds__(C::NTH, 1) void grouped_gemm_bf16(GemmArgs p, int N
   }
 }
 
-// --------------------------------------------------------------------------------------------
-// Pipelined kernel for the modes whose two operands are K-contiguous (gate/up and down forward).
-//
-// 256x256 output tiles, 8 waves of 128x64, K consumed 32 at a time through a ring of four LDS
-// stages that the global loads fill directly (global_load_lds_dwordx4: lane l's 16 bytes land at
-// M0 + 16*l), so three stages of loads are in flight while one is multiplied and no registers are
-// spent on staging.  Each stage is its own LDS object and the loop is unrolled over the ring, so
-// the compiler's wait tracking sees which stage an LDS read touches; waits are explicit
-// s_waitcnt with a barrier (no fence: a fence would drain every load in flight).
-
-namespace dmak {
-constexpr int BM = 256, BN = 256, BKS = 32, S = 4, NTH = 512;
-constexpr int ROWB = BKS * 2;              // bytes per LDS row (32 bf16)
-constexpr int STAGE = (BM + BN) * ROWB;    // 32 KiB per stage
-typedef Cfg<256, 256, 2, 4> Geo;           // wave geometry: 2 x 4 waves, MI = 4, NI = 2
-}  // namespace dmak
-
-typedef __attribute__((address_space(1))) void gvoid_t;
-typedef __attribute__((address_space(3))) void lvoid_t;
-
-// 16-byte chunk swizzle for 64-byte LDS rows: 16 consecutive rows read at one logical chunk hit 16
-// distinct 16-byte bank groups of the 64-bank LDS.
-__host__ __device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
-
-// s_waitcnt with lgkmcnt = 0, expcnt untouched, vmcnt = N (N < 16).
-#define MOE_WAIT_VM_LGKM0(N) __builtin_amdgcn_s_waitcnt(0x0070 | (N))
-
-// Issue one stage: A and B tiles, 1024 16-byte slots each, two instructions per wave per operand.
-// Slot q of a tile is (row q/4, physical chunk q%4); the lane fetches the logical chunk that the
-// swizzle places there.  A rows past the expert's end re-read its last row (never stored).
-template <int MODE>
-__device__ __forceinline__ void dma_issue(const GemmArgs& p, char* st, int g, int m0, int m_end, int nt,
-                                          int k0, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = (wave * 2 + j) * 64 + lane;
-    const int row = q >> 2, logical = (q & 3) ^ swz64(row);
-    const int m = min(m0 + row, m_end - 1);
-    __builtin_amdgcn_global_load_lds((gvoid_t*)a_ptr_kc<MODE, bf16_t>(p, m, k0 + logical * 8),
-                                     (lvoid_t*)(st + (wave * 2 + j) * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = (wave * 2 + j) * 64 + lane;
-    const int row = q >> 2, logical = (q & 3) ^ swz64(row);
-    __builtin_amdgcn_global_load_lds((gvoid_t*)b_ptr_kc<MODE, bf16_t, dmak::BN>(p, g, nt, row, k0 + logical * 8),
-                                     (lvoid_t*)(st + dmak::BM * dmak::ROWB + (wave * 2 + j) * 1024), 16, 0, 0);
-  }
-}
-
-// LDS byte address of a pointer into shared memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)ptr);
-}
-
-// 16-byte LDS read issued as inline assembly.  The compiler's own wait insertion would otherwise
-// drain every direct-to-LDS load in flight before the read (it cannot tell which stage a read
-// touches), so these reads are invisible to it and are fenced by lds_wait below instead.
-__device__ __forceinline__ bf16x8_t lds_read16(uint32_t addr) {
-  bf16x8_t v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
-  return v;
-}
-
-// Wait for all LDS reads of this wave; the fragments are in-out operands so that no use of them
-// can be scheduled before the wait.
-__device__ __forceinline__ void lds_wait(bf16x8_t (&af)[4], bf16x8_t (&bf)[2]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]), "+v"(bf[1]));
-}
-
-// Per-lane LDS byte offsets (within a stage) of the fragments of the two 16-deep substeps.
-struct DmaFragOffsets {
-  uint32_t a[2][4];   // [substep][mi]
-  uint32_t b[2][2];   // [substep][ni]
-};
-
-template <int MODE>
-__device__ __forceinline__ DmaFragOffsets dma_frag_offsets(int wm, int wn, int lane) {
-  using namespace dmak;
-  DmaFragOffsets o;
-#pragma unroll
-  for (int s = 0; s < BKS / 16; ++s) {
-    const int chunk = s * 2 + (lane >> 5);
-#pragma unroll
-    for (int mi = 0; mi < Geo::MI; ++mi) {
-      const int row = wm * (BM / Geo::WGM) + mi * 32 + (lane & 31);
-      o.a[s][mi] = row * ROWB + ((chunk ^ swz64(row)) << 4);
-    }
-#pragma unroll
-    for (int ni = 0; ni < Geo::NI; ++ni) {
-      const int row = wave_nrow<MODE, Geo>(wn, ni) + (lane & 31);
-      o.b[s][ni] = BM * ROWB + row * ROWB + ((chunk ^ swz64(row)) << 4);
-    }
-  }
-  return o;
-}
-
-// One stage of MFMAs: two 16-deep substeps, 4 A and 2 B fragments each; the reads of the second
-// substep are issued before the first substep's MFMAs.
-__device__ __forceinline__ void dma_compute(uint32_t base, const DmaFragOffsets& o,
-                                            f32x16_t (&acc)[dmak::Geo::MI][dmak::Geo::NI]) {
-  using namespace dmak;
-  bf16x8_t af[2][4], bfr[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) af[0][mi] = lds_read16(base + o.a[0][mi]);
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni) bfr[0][ni] = lds_read16(base + o.b[0][ni]);
-  lds_wait(af[0], bfr[0]);
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) af[1][mi] = lds_read16(base + o.a[1][mi]);
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni) bfr[1][ni] = lds_read16(base + o.b[1][ni]);
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][mi], bfr[0][ni], acc[mi][ni], 0, 0, 0);
-  lds_wait(af[1], bfr[1]);
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][mi], bfr[1][ni], acc[mi][ni], 0, 0, 0);
-}
-
-// Wait until stage k has landed (this wave's loads; the barrier makes every wave's visible and
-// certifies that all waves finished the stage that is about to be refilled).
-__device__ __forceinline__ void dma_wait_stage(int k, int nk) {
-  const int later = nk - 1 - k;     // stages issued after k that may stay in flight (4 loads each)
-  if (later >= 2) MOE_WAIT_VM_LGKM0(8);
-  else if (later == 1) MOE_WAIT_VM_LGKM0(4);
-  else MOE_WAIT_VM_LGKM0(0);
-  asm volatile("s_barrier" ::: "memory");
-}
-
-template <int MODE>
-__global__ __launch_bounds__(dmak::NTH, 1) void grouped_gemm_bf16_dma(GemmArgs p, int NT) {
-  using namespace dmak;
-  typedef Geo C;
-  __shared__ __attribute__((aligned(16))) char st0[STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[STAGE];
-  __shared__ __attribute__((aligned(16))) char st2[STAGE];
-  __shared__ __attribute__((aligned(16))) char st3[STAGE];
-  __shared__ int pref[MAXG + 1];
-  __shared__ int scan_scratch[NTH + 1];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave % C::WGM, wn = wave / C::WGM;
-
-  block_tile_prefix<BM, NTH>(p, pref, scan_scratch);
-  const int total = pref[p.G] * NT;
-  const int per = (total + 7) >> 3;
-  const int xcd = blockIdx.x & 7;
-  const int nbx = gridDim.x >> 3;
-  const int L_end = min(total, (xcd + 1) * per);
-  const int nk = mode_K(MODE, p.d, p.f) / BKS;
-  const DmaFragOffsets fo = dma_frag_offsets<MODE>(wm, wn, lane);
-  const uint32_t sb0 = lds_addr(st0), sb1 = lds_addr(st1), sb2 = lds_addr(st2), sb3 = lds_addr(st3);
-
-  for (int L = xcd * per + (blockIdx.x >> 3); L < L_end; L += nbx) {
-    const int mt = L / NT;
-    const int nt = L - mt * NT;
-    int lo = 0, hi = p.G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pref[mid] <= mt) lo = mid; else hi = mid;
-    }
-    const int g = lo;
-    int r0, r1;
-    group_rows(p.offsets, g, p.M, r0, r1);
-    const int m0 = r0 + (mt - pref[g]) * BM;
-    const int m_end = r1;
-
-    f32x16_t acc[C::MI][C::NI];
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    MOE_WAIT_VM_LGKM0(0);   // the previous tile's stores count in vmcnt too
-    dma_issue<MODE>(p, st0, g, m0, m_end, nt, 0, wave, lane);
-    if (nk > 1) dma_issue<MODE>(p, st1, g, m0, m_end, nt, BKS, wave, lane);
-    if (nk > 2) dma_issue<MODE>(p, st2, g, m0, m_end, nt, 2 * BKS, wave, lane);
-    for (int kt = 0; kt < nk; kt += S) {
-#define MOE_DMA_STEP(I, CUR, NXT)                                                     \
-      if (kt + I < nk) {                                                                \
-        dma_wait_stage(kt + I, nk);                                                     \
-        if (kt + I + 3 < nk) dma_issue<MODE>(p, NXT, g, m0, m_end, nt, (kt + I + 3) * BKS, wave, lane); \
-        dma_compute(CUR, fo, acc);                                                      \
-      }
-      MOE_DMA_STEP(0, sb0, st3)
-      MOE_DMA_STEP(1, sb1, st0)
-      MOE_DMA_STEP(2, sb2, st1)
-      MOE_DMA_STEP(3, sb3, st2)
-#undef MOE_DMA_STEP
-    }
-    MOE_WAIT_VM_LGKM0(0);
-    asm volatile("s_barrier" ::: "memory");   // every wave is done with the ring before it refills
-
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * (BM / C::WGM) + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m >= m_end) continue;
-        if constexpr (MODE == GEMM_UP_FWD) {
-#pragma unroll
-          for (int ni = 0; ni < C::NI / 2; ++ni) {
-            const int n = nt * (BN / 2) + wave_nrow<MODE, C>(wn, ni) + (lane & 31);
-            epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][ni][v], acc[mi][ni + C::NI / 2][v]);
-          }
-        } else {
-#pragma unroll
-          for (int ni = 0; ni < C::NI; ++ni) {
-            const int n = nt * BN + wave_nrow<MODE, C>(wn, ni) + (lane & 31);
-            epilogue<MODE, bf16_t>(p, g, m, n, acc[mi][ni][v], 0.0f);
-          }
-        }
-      }
-    }
-  }
-}
-
 // Sum of the split-K partials in split order, written as bf16 weight gradients (dW2, or dW1/dW3
 // by gradient row).  Each thread sums 8 consecutive columns (16-byte loads, one 16-byte store).
 template <int MODE>
@@ -846,39 +619,15 @@ hipError_t launch_bf16(const GemmArgs& p, size_t partial_bytes, float* partial, 
   return e;
 }
 
-template <int MODE>
-hipError_t launch_bf16_dma(const GemmArgs& p, hipStream_t s) {
-  auto kern = grouped_gemm_bf16_dma<MODE>;
-  static int blocks_per_cu = 0;
-  if (blocks_per_cu == 0) {
-    int nb = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, dmak::NTH, 0);
-    if (e != hipSuccess) return e;
-    blocks_per_cu = nb > 0 ? nb : 1;
-  }
-  if (p.M == 0) return hipSuccess;
-  if (p.G > MAXG) return hipErrorInvalidValue;
-  const int NT = mode_N(MODE, p.d, p.f) / dmak::BN;
-  const long long tiles = ((long long)ceil_div(p.M, dmak::BM) + p.G) * NT;
-  long long grid = std::min<long long>(tiles, (long long)num_cus() * blocks_per_cu);
-  grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(dmak::NTH), 0, s, p, NT);
-  return hipGetLastError();
-}
-
 typedef Cfg<128, 128, 2, 2> T128x128;   // 4 waves of 64x64
-typedef Cfg<128, 256, 2, 4> T128x256;   // 8 waves of 64x64
-typedef Cfg<256, 128, 4, 2> T256x128;   // 8 waves of 64x64
-typedef Cfg<256, 256, 2, 4> T256x256;   // 8 waves of 128x64
 
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float* partial, hipStream_t s) {
   typedef Traits<MODE> TR;
   if (bf16) {
-    // The pipelined 256x256 kernel wherever it applies (LIBMOE_PIPE=0 disables it).
-    static const char* pipe_env = getenv("LIBMOE_PIPE");
-    const bool pipe_on = !(pipe_env && pipe_env[0] == '0');
-    if (pipe_on && pipe_supports(MODE, p)) {
+    // The pipelined 256x256 kernel wherever its shape rules hold (output columns a multiple of 256),
+    // else the 128x128 register-staged kernel (d and f are multiples of 128).
+    if (pipe_supports(MODE, p)) {
       int ksplit = 1;
       if constexpr (TR::raggedK) {
         const int Mw = mode_Mw(MODE, p.d, p.f), N = mode_N(MODE, p.d, p.f);
@@ -891,32 +640,6 @@ hipError_t launch_mode(const GemmArgs& p, bool bf16, size_t partial_bytes, float
                          s, p, partial, ksplit);
       return hipGetLastError();
     }
-    // Tile shape (LIBMOE_TILE=<BM>x<BN> overrides it for tuning sweeps; a shape that does not
-    // divide the problem falls back to the default).
-    const int N = mode_N(MODE, p.d, p.f);
-    const int Mw = TR::raggedK ? mode_Mw(MODE, p.d, p.f) : 256;
-    // Default: 256x256 (8 waves of 128x64) where it divides; groups averaging under 384 rows
-    // use 128x128 (4 waves, two workgroups per CU) to bound the ragged-tail waste.
-    int bm = 128, bn = 128;
-    if (N % 256 == 0 && Mw % 256 == 0 && (TR::raggedK || (p.G > 0 && p.M / p.G >= 384))) bm = bn = 256;
-    static const char* ov = getenv("LIBMOE_TILE");
-    if (ov) {
-      int obm = 0, obn = 0;
-      if (sscanf(ov, "%dx%d", &obm, &obn) == 2 && (obm == 128 || obm == 256) && (obn == 128 || obn == 256) &&
-          N % obn == 0 && Mw % obm == 0) {
-        bm = obm;
-        bn = obn;
-      }
-    }
-    if constexpr (MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD) {
-      // Both operands K-contiguous: the direct-to-LDS pipelined kernel (LIBMOE_DMA=0 disables it).
-      static const char* dma = getenv("LIBMOE_DMA");
-      if (bm == 256 && bn == 256 && mode_K(MODE, p.d, p.f) % dmak::BKS == 0 && !(dma && dma[0] == '0'))
-        return launch_bf16_dma<MODE>(p, s);
-    }
-    if (bm == 256 && bn == 256) return launch_bf16<MODE, T256x256>(p, partial_bytes, partial, s);
-    if (bm == 256) return launch_bf16<MODE, T256x128>(p, partial_bytes, partial, s);
-    if (bn == 256) return launch_bf16<MODE, T128x256>(p, partial_bytes, partial, s);
     return launch_bf16<MODE, T128x128>(p, partial_bytes, partial, s);
   }
   const int NT = mode_N(MODE, p.d, p.f) / FBN;
@@ -975,13 +698,7 @@ namespace {
 // Whether the two sets of p go into one launch of the pipelined kernel: it must cover both, and
 // each must be a shape the single-set launcher would give it.
 bool merge_sets(int mode, const GemmArgs& p) {
-  static const char* pipe_env = getenv("LIBMOE_PIPE");
-  if (pipe_env && pipe_env[0] == '0') return false;
   if (!pipe_supports(mode, p)) return false;
-  // LIBMOE_MERGE=0: never merge; =2: merge whenever the kernel takes both sets (tests, sweeps).
-  const char* m = getenv("LIBMOE_MERGE");
-  if (m && m[0] == '0') return false;
-  if (m && m[0] == '2') return true;
   // Weight gradients: set 0 must fill the chip without a split; set 1's row reduction is split so
   // its tiles are about as long as set 0's (see launch_wgrad_sets).
   if (mode == GEMM_DOWN_WGRAD || mode == GEMM_UP_WGRAD)

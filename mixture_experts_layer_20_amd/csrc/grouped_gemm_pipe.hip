@@ -70,7 +70,7 @@ template <int MODE>
 constexpr int mi_max() { return has_x<MODE>() ? MIX : MI; }
 constexpr int PMAXG = 1024;   // groups of the first set
 constexpr int PMAXG1 = 64;    // groups of the second set (the shared expert: 1)
-constexpr int WG_NB = 8;      // tile columns per block of the weight-gradient tile order
+constexpr int WG_NB = 4;      // tile columns per block of the weight-gradient tile order
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -907,6 +907,49 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& 
   }
 }
 
+// Rows of 128 bytes: blocks (mi, 0) and (mi, 1) stored together.  After swap16 each block has r0
+// (rows 0..15) and r1 (rows 16..31), lane l holding row l % 16 and 16 bytes at xcol_bf16(l).  A
+// rotation by 8 lanes inside each 16-lane row (DPP row_ror:8) of block 1's pieces and a select on
+// lane bit 3 give A (rows 0..7: block 0 where bit 3 is clear, block 1 where it is set) and B (rows
+// 8..15): 8 lanes and 128 contiguous bytes (a whole cache line) per row, in as many store
+// instructions as two blocks stored apart.
+__device__ __forceinline__ void st_rows128(const OutWin& w, int br, const float (&x0)[2][8], const float (&x1)[2][8],
+                                           int lane) {
+  u32x4_t a[2], c[2];
+  swap16(pack8_bf16(x0[0]), pack8_bf16(x0[1]), a[0], a[1]);
+  swap16(pack8_bf16(x1[0]), pack8_bf16(x1[1]), c[0], c[1]);
+  const bool hi8 = (lane & 8) != 0;
+  const int rl = br + (lane & 7);
+  const int cx = xcol_bf16(lane);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    u32x4_t A, B;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)c[q][e], 0x128, 0xf, 0xf, false);
+      A[e] = hi8 ? t : a[q][e];
+      B[e] = hi8 ? a[q][e] : t;
+    }
+    const int r = rl + 16 * q;
+    __builtin_amdgcn_raw_buffer_store_b128(A, w.r, (int)(r * w.row_bytes) + (cx + (hi8 ? 32 : 0)) * 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(B, w.r, (int)((r + 8) * w.row_bytes) + (cx + (hi8 ? 0 : 32)) * 2, 0, 0);
+  }
+}
+// The epilogue of the modes with one bf16 output and no elementwise math (down projection, gate/up
+// data gradient, unsplit weight gradients), block row MIDX.. of the wave.
+template <int MIDX, int M>
+__device__ __forceinline__ void epilogue_rows128(const OutWins& o, const f32x16_t (&acc)[M][NI], int lane) {
+  if constexpr (MIDX < M) {
+    float v0[2][8], v1[2][8];
+    block_half(acc[MIDX][0], 0, v0[0]);
+    block_half(acc[MIDX][0], 1, v0[1]);
+    block_half(acc[MIDX][1], 0, v1[0]);
+    block_half(acc[MIDX][1], 1, v1[1]);
+    st_rows128(o.w[0], MIDX * 32, v0, v1, lane);
+    epilogue_rows128<MIDX + 1, M>(o, acc, lane);
+  }
+}
+
 // Pre-activation loads of blocks IDX..AUX_AHEAD-1, issued in block order before the first store.
 template <int MODE, int IDX>
 __device__ __forceinline__ void aux_prologue(const GemmArgs& p, int row0, int col0, int m_end,
@@ -935,6 +978,12 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
   const int ksplit = t.ks;
   AuxBlock aux[AUX_AHEAD + 1];
   if constexpr (MODE == GEMM_DOWN_BWD) aux_prologue<MODE, 0>(p, row0, col0, t.m_end, aux, lane);
+  if constexpr (MODE != GEMM_UP_FWD && MODE != GEMM_DOWN_BWD) {
+    if (ksplit == 1) {   // same store count as the per-block path (two per block)
+      epilogue_rows128<0, M>(o, acc, lane);
+      return;
+    }
+  }
   epilogue_from<MODE, 0, M>(p, o, acc, row0, col0, t.m_end, lane, aux, ksplit);
 }
 

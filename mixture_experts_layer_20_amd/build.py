@@ -68,12 +68,53 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     return LIB_PATH
 
 
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB_PATH = os.path.join(ASAN_DIR, "libmoe_asan.so")
+# Host AddressSanitizer for the C-ABI layer only: the flag applies to the host pass, never to device code.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that a process loading the ASan build must preload."""
+    llvm = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(llvm)) if os.path.isdir(llvm) else []:
+        cand = os.path.join(llvm, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return cand
+    raise RuntimeError("clang AddressSanitizer runtime not found under " + llvm)
+
+
+def build_asan(verbose: bool = False) -> str:
+    """Debug build: api.cpp (argument checks, workspace layout, scratch set-up) with host ASan,
+    linked with the regular objects of the other sources, at _build/asan/libmoe_asan.so."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, s + ".o")) for s in SOURCES):
+        build(verbose=verbose)
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    obj = os.path.join(ASAN_DIR, "api.cpp.o")
+    cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, "-O1", "-g", *ASAN_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+           os.path.join(CSRC, "api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling api.cpp with ASan failed:\n{r.stderr}")
+    objs = [obj] + [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s != "api.cpp"]
+    r = subprocess.run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", ASAN_LIB_PATH, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking the ASan build failed:\n{r.stderr}")
+    if verbose:
+        print(ASAN_LIB_PATH)
+    return ASAN_LIB_PATH
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--asan", action="store_true", help="also build the host-ASan debug library")
     a = ap.parse_args(argv)
     print(build(a.jobs, a.verbose))
+    if a.asan:
+        print(build_asan(a.verbose))
     return 0
 
 

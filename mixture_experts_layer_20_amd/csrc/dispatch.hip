@@ -175,6 +175,112 @@ __global__ __launch_bounds__(256) void scatter_gather_kernel(const T* x, const i
   }
 }
 
+// Passes 2 and 3 in one launch, for problems whose chunk counts fit in LDS (nch * E <= FUSED_LDS).
+// Each block takes GT consecutive tokens: it issues the loads of their rows first, then derives
+// from all chunk counts the first row of each (chunk, expert) pair for the (at most two) chunks
+// its assignments fall in (the scan of pass 2, recomputed per block from 32 KiB of counts), writes
+// dest_pos and src_row, and stores each row at its k destinations.  Block 0 also writes counts and
+// offsets.
+typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));   // native vector: stays in registers
+constexpr int GT = 8;              // tokens per block of the fused pass
+constexpr int FUSED_LDS = 8192;    // chunk counts (ints) staged per block
+constexpr int FUSED_MAXV = 2;      // 16-byte row pieces per thread and token (d * esize <= 8 KiB)
+template <typename T>
+__global__ __launch_bounds__(256) void scan_gather_kernel(const T* x, const int32_t* topk_idx,
+                                                          const int32_t* local_rank,
+                                                          const int32_t* chunk_counts, int nch, int T_, int d,
+                                                          int E, int k, int32_t* counts, int32_t* offsets,
+                                                          int32_t* dest_pos, int32_t* src_row, T* x_perm) {
+  __shared__ __attribute__((aligned(16))) int cc[FUSED_LDS];
+  __shared__ int tot[256];
+  __shared__ int base_s[2][256];
+  __shared__ int dst_s[GT * 8];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * GT, nt = min(GT, T_ - t0);
+  const int Tk = T_ * k;
+  constexpr int V = 16 / sizeof(T);
+  const int nv = x_perm ? d / V : 0;
+  // 1. the block's rows into registers (independent of everything below).  Loads are unconditional
+  // (token and piece indices clamped) so the row array stays in registers.
+  v4u32_t row[GT][FUSED_MAXV];
+  const int nvl = max(nv, 1);
+#pragma unroll
+  for (int i = 0; i < GT; ++i)
+#pragma unroll
+    for (int q = 0; q < FUSED_MAXV; ++q) {
+      const v4u32_t* src = reinterpret_cast<const v4u32_t*>(x + (size_t)(t0 + min(i, nt - 1)) * d);
+      row[i][q] = src[min(tid + q * 256, nvl - 1)];
+    }
+  // 2. counts -> per-expert totals -> offsets; first rows of the block's chunks
+  // counts: 16-byte loads, all of a round issued before any is stored (one wait per round)
+  const int n = nch * E, n4 = n / 4;
+  const int4* cc4 = reinterpret_cast<const int4*>(chunk_counts);
+  for (int b = 0; b < n4; b += 4 * 256) {
+    int4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = cc4[min(b + u * 256 + tid, n4 - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (b + u * 256 + tid < n4) reinterpret_cast<int4*>(cc)[b + u * 256 + tid] = v[u];
+  }
+  for (int i = 4 * n4 + tid; i < n; i += 256) cc[i] = chunk_counts[i];
+  __syncthreads();
+  const int c0 = (t0 * k) / CHUNK;
+  int total = 0, below0 = 0, below1 = 0;
+  if (tid < E) {
+    for (int c = 0; c < nch; ++c) {
+      const int v = cc[c * E + tid];
+      if (c < c0) below0 += v;
+      if (c < c0 + 1) below1 += v;
+      total += v;
+    }
+  }
+  tot[tid] = total;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? tot[tid - off] : 0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int excl = tot[tid] - total;
+    base_s[0][tid] = excl + below0;
+    base_s[1][tid] = excl + below1;
+    if (blockIdx.x == 0) {
+      counts[tid] = total;
+      offsets[tid] = excl;
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) offsets[E] = Tk;
+  __syncthreads();
+  // 3. destinations of the block's assignments
+  if (tid < nt * k) {
+    // An expert index outside [0, E) (not produced by moe_route) gives an unspecified permutation,
+    // but every access stays inside the buffers.
+    const int a = t0 * k + tid;
+    const int e = min(max(topk_idx[a], 0), E - 1);
+    const int dst = min(max(base_s[a / CHUNK - c0][e] + local_rank[a], 0), Tk - 1);
+    dest_pos[a] = dst;
+    src_row[dst] = a;
+    dst_s[tid] = dst;
+  }
+  if (x_perm == nullptr) return;
+  __syncthreads();
+  // 4. each row to its k destinations
+  for (int j = 0; j < k; ++j) {   // slot-major: the row array is indexed at compile time
+#pragma unroll
+    for (int i = 0; i < GT; ++i) {
+      if (i < nt) {
+        v4u32_t* dst = reinterpret_cast<v4u32_t*>(x_perm + (size_t)dst_s[i * k + j] * d);
+#pragma unroll
+        for (int q = 0; q < FUSED_MAXV; ++q)
+          if (tid + q * 256 < nv) dst[tid + q * 256] = row[i][q];
+      }
+    }
+  }
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 8 consecutive elements as fp32.  NT: a stream nothing later in the layer pass reads again (a
@@ -275,6 +381,19 @@ hipError_t launch_permute(const void* x, const int32_t* topk_idx, int T, int d, 
   if (Tk > 0)
     hipLaunchKernelGGL(local_rank_kernel, dim3(nch), dim3(CH_THREADS), 0, s, topk_idx, Tk, E, nbits,
                        local_rank, chunk_counts);
+  const size_t esz = bf16 ? 2 : 4;
+  if (Tk > 0 && (long long)nch * E <= FUSED_LDS && E <= 256 && k <= 8 && (d * esz) % 16 == 0 &&
+      d * esz <= (size_t)FUSED_MAXV * 256 * 16) {
+    if (bf16)
+      hipLaunchKernelGGL(scan_gather_kernel<bf16_t>, dim3(ceil_div(T, GT)), dim3(256), 0, s,
+                         reinterpret_cast<const bf16_t*>(x), topk_idx, local_rank, chunk_counts, nch, T, d, E, k,
+                         counts, offsets, dest_pos, src_row, reinterpret_cast<bf16_t*>(x_perm));
+    else
+      hipLaunchKernelGGL(scan_gather_kernel<float>, dim3(ceil_div(T, GT)), dim3(256), 0, s,
+                         reinterpret_cast<const float*>(x), topk_idx, local_rank, chunk_counts, nch, T, d, E, k,
+                         counts, offsets, dest_pos, src_row, reinterpret_cast<float*>(x_perm));
+    return hipGetLastError();
+  }
   if ((long long)nch * E <= SCAN_LDS && E <= SCAN_THREADS)
     hipLaunchKernelGGL(scan_lds_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, chunk_counts, nch, E, Tk, counts,
                        offsets, chunk_base);

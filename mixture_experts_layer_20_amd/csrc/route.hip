@@ -440,6 +440,39 @@ __global__ __launch_bounds__(256) void route_dx_kernel(const float* dl, const in
   }
 }
 
+// The same for d a multiple of 8: each thread 8 consecutive columns of one token (16-byte loads of
+// the expert rows, which stay in L2, and one 16-byte store), DXCOLS columns per block.
+constexpr int DXCOLS = 2048;
+template <typename T>
+__global__ __launch_bounds__(256) void route_dx8_kernel(const float* dl, const int32_t* idx, const T* w, int d,
+                                                        int k, T* dx) {
+  const int t = blockIdx.x;
+  const int c = blockIdx.y * DXCOLS + threadIdx.x * 8;
+  if (c >= d) return;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const size_t a = (size_t)t * k + j;
+    const float g = dl[a];
+    float wv[8];
+    row8<std::is_same<T, bf16_t>::value>(w, (size_t)idx[a] * d, c, d, true, wv);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += g * wv[q];
+  }
+  T* out = dx + (size_t)t * d + c;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = (uint32_t)from_f32<bf16_t>(acc[2 * i]) | ((uint32_t)from_f32<bf16_t>(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(out) = make_uint4(u[0], u[1], u[2], u[3]);
+  } else {
+    reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
 constexpr int SEG = 64;      // permuted rows per partial sum of the router weight gradient
 constexpr int DWCOLS = 1024; // columns per block (any d)
 constexpr int DWCOLS8 = 2048; // columns per block, 8 per thread (d a multiple of 8)
@@ -666,7 +699,15 @@ hipError_t launch_route_bwd(const float* dgate, const float* gate, const int32_t
 
   if (T > 0) {
     hipLaunchKernelGGL(route_dl_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, dgate, gate, T, k, dl);
-    if (bf16)
+    if (d % 8 == 0) {
+      const dim3 g((unsigned)T, ceil_div(d, DXCOLS));
+      if (bf16)
+        hipLaunchKernelGGL(route_dx8_kernel<bf16_t>, g, dim3(256), 0, s, dl, topk_idx,
+                           reinterpret_cast<const bf16_t*>(w), d, k, reinterpret_cast<bf16_t*>(dx_router));
+      else
+        hipLaunchKernelGGL(route_dx8_kernel<float>, g, dim3(256), 0, s, dl, topk_idx,
+                           reinterpret_cast<const float*>(w), d, k, reinterpret_cast<float*>(dx_router));
+    } else if (bf16)
       hipLaunchKernelGGL(route_dx_kernel<bf16_t>, dim3(T), dim3(256), 0, s, dl, topk_idx,
                          reinterpret_cast<const bf16_t*>(w), d, k, reinterpret_cast<bf16_t*>(dx_router));
     else

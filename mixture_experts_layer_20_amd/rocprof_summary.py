@@ -43,7 +43,7 @@ SIMDS = 1024   # 256 CUs x 4
 # kernel name pattern -> stage (library call) that launches it; first match wins
 STAGE_OF = [
     (r"router_logits|topk_gate", "route"),
-    (r"local_rank|scan_lds|scan_kernel|scatter_gather|rank_scan", "permute"),
+    (r"local_rank|scan_lds|scan_kernel|scatter_gather|scan_gather|rank_scan", "permute"),
     (r"combine_bwd_kernel", "combine_bwd"),
     (r"combine_kernel", "combine"),
     (r"route_dl|route_dx|route_dw|seg_prefix", "route_bwd"),

@@ -51,11 +51,11 @@ constexpr int MIX = 5, BMX = 320;     // a tile of 257..BMX rows (modes with row
 constexpr int LPB = 4;                // direct loads (1 KiB each) per wave per stage of operand B
 constexpr int OPB = 256 * BKS * 2;    // operand B tile of one stage: 32 KiB
 
-// Modes whose tiles hold up to BMX rows (operand A K-contiguous, registers to spare): an expert of
-// 257..320 rows is one tile rather than a full tile and a remainder tile that streams the same
-// weights again.  The others hold up to BM rows.
+// Modes whose tiles hold up to BMX rows (operand A K-contiguous): an expert of 257..320 rows is one
+// tile rather than a full tile and a remainder tile that streams the same weights again.  The
+// weight gradients hold up to BM rows.
 template <int MODE>
-constexpr bool has_x() { return MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD; }
+constexpr bool has_x() { return MODE == GEMM_UP_FWD || MODE == GEMM_DOWN_FWD || MODE == GEMM_UP_DGRAD || MODE == GEMM_DOWN_BWD; }
 template <int MODE>
 constexpr int rows_a() { return has_x<MODE>() ? BMX : BM; }          // operand A rows per stage
 template <int MODE>
@@ -68,6 +68,20 @@ template <int MODE>
 constexpr int stage_bytes() { return opa<MODE>() + OPB; }
 template <int MODE>
 constexpr int mi_max() { return has_x<MODE>() ? MIX : MI; }
+// Operand A loads per wave that a tile of at most BM rows needs; the others (rows BM..BMX-1 of a
+// BMX-row stage) are issued only for tiles of more than BM rows.
+constexpr int LPA_BM = BM * BKS * 2 / 1024 / NW;
+template <int MODE>
+constexpr int lpa_skip() { return lpa<MODE>() - LPA_BM; }
+// 1 KiB slot of a stage's operand tile that load j of a wave fills.  K-contiguous operand A is
+// slot-major over the waves (load j of wave w: slot j * NW + w), so loads j >= LPA_BM are exactly
+// the rows past BM; every other operand is wave-major (slot w * lp + j), which keeps the loads of
+// one wave LP consecutive slots apart by a fixed step.
+template <int MODE, bool A_OP>
+__device__ __forceinline__ int load_slot(int wave, int j) {
+  if constexpr (A_OP && Traits<MODE>::a_kcontig) return j * NW + wave;
+  else return wave * (A_OP ? lpa<MODE>() : LPB) + j;
+}
 constexpr int PMAXG = 1024;   // groups of the first set
 constexpr int PMAXG1 = 64;    // groups of the second set (the shared expert: 1)
 constexpr int WG_NB = 4;      // tile columns per block of the weight-gradient tile order
@@ -173,14 +187,18 @@ __device__ __forceinline__ void group_rows_lds(uint32_t offs, int g, int& lo, in
 
 // Rows per tile of a group of R rows (ragged M) and the group's tiles: ceil(R / BMX) tiles of
 // equal height where the mode has row capacity BMX (so no tile is a short remainder that streams
-// the weights again), else 256-row tiles and a remainder.
+// the weights again), else 256-row tiles and a remainder.  The SwiGLU-backward product (down_bwd)
+// takes a BMX-row tile only for a group that it holds whole: its 320-row tile spills registers at
+// tile boundaries, which costs more than a remainder tile once a group has two or more tiles.
 template <int MODE>
 __device__ __forceinline__ int group_tiles(int R) {
+  if constexpr (MODE == GEMM_DOWN_BWD) return R <= BMX ? (R > 0) : (R + BM - 1) / BM;
   return has_x<MODE>() ? (R + BMX - 1) / BMX : (R + BM - 1) / BM;
 }
 template <int MODE>
 __device__ __forceinline__ int tile_rows(int R) {
   if constexpr (!has_x<MODE>()) return BM;
+  if constexpr (MODE == GEMM_DOWN_BWD) return R <= BMX ? BMX : BM;
   const int n = max(1, group_tiles<MODE>(R));
   return (R + n - 1) / n;
 }
@@ -279,10 +297,12 @@ __device__ __forceinline__ Tile deal_tile(const GemmArgs& p, const SegGeo (&geo)
 template <int MODE, int IDX>
 __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const Tile& t, int k0, int wave, int lane) {
   constexpr bool A_OP = IDX < lpa<MODE>();
-  constexpr int LP = A_OP ? lpa<MODE>() : LPB;
   constexpr int j = A_OP ? IDX : IDX - lpa<MODE>();
   constexpr bool kc = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
-  const int q = (wave * LP + j) * 64 + lane;
+  if constexpr (A_OP && j >= LPA_BM) {
+    if (!t.x) return;   // as in issue_fast
+  }
+  const int q = load_slot<MODE, A_OP>(wave, j) * 64 + lane;
   const bf16_t* src;
   if constexpr (kc) {
     const int row = q >> 3;
@@ -303,7 +323,7 @@ __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const
       src = reinterpret_cast<const bf16_t*>(g_zero_rows);
     }
   }
-  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : opa<MODE>()) + (wave * LP + j) * 1024),
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : opa<MODE>()) + load_slot<MODE, A_OP>(wave, j) * 1024),
                                    16, 0, 0);
 }
 
@@ -313,7 +333,7 @@ __device__ __forceinline__ void issue_load(const GemmArgs& p, char* stage, const
 template <int MODE>
 __device__ __forceinline__ uint32_t load_offset(const GemmArgs& p, const Tile& t, int idx, int wave, int lane) {
   const bool a_op = idx < lpa<MODE>();
-  const int q = (a_op ? wave * lpa<MODE>() + idx : wave * LPB + idx - lpa<MODE>()) * 64 + lane;
+  const int q = (a_op ? load_slot<MODE, true>(wave, idx) : load_slot<MODE, false>(wave, idx - lpa<MODE>())) * 64 + lane;
   const bool kc = a_op ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
   if (kc) {
     const int row = q >> 3;
@@ -395,10 +415,12 @@ __device__ __forceinline__ void stage_bases(const GemmArgs& p, const Tile& t, in
 
 template <int MODE, int IDX>
 __device__ __forceinline__ void issue_fast(char* stage, const char* sa, const char* sb, const LoadOffs& lo,
-                                           int k_left, int wave, int lane) {
+                                           int k_left, bool x, int wave, int lane) {
   constexpr bool A_OP = IDX < lpa<MODE>();
-  constexpr int LP = A_OP ? lpa<MODE>() : LPB;
   constexpr int J = A_OP ? IDX : IDX - lpa<MODE>();
+  if constexpr (A_OP && J >= LPA_BM) {
+    if (!x) return;   // wave-uniform: rows past BM of a tile that has none
+  }
   // Load J is 8 K-contiguous rows (2 K rows) after load 0, which moves the row swizzle by 4
   // chunks (the window swizzle by 8 chunks) for odd J: a 64-byte (128-byte) XOR on top of the step.
   constexpr bool KC = A_OP ? Traits<MODE>::a_kcontig : Traits<MODE>::b_kcontig;
@@ -409,12 +431,12 @@ __device__ __forceinline__ void issue_fast(char* stage, const char* sa, const ch
   else off = (lo.b + (uint32_t)J * lo.sb) ^ FLIP;
   const char* src = (A_OP ? sa : sb) + off;
   if constexpr (Traits<MODE>::raggedK) {
-    // K-strided operands: lane reads K row (wave * LP + J) * 2 + lane / 32 of the stage; rows
-    // past the group's end read zeros.
-    const int kr = (wave * LP + J) * 2 + (lane >> 5);
+    // K-strided operands: lane reads K row (load slot) * 2 + lane / 32 of the stage; rows past
+    // the group's end read zeros.
+    const int kr = load_slot<MODE, A_OP>(wave, J) * 2 + (lane >> 5);
     if (kr >= k_left) src = reinterpret_cast<const char*>(g_zero_rows);
   }
-  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : opa<MODE>()) + (wave * LP + J) * 1024),
+  __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(stage + (A_OP ? 0 : opa<MODE>()) + load_slot<MODE, A_OP>(wave, J) * 1024),
                                    16, 0, 0);
 }
 
@@ -423,6 +445,7 @@ struct StageSrc {
   const char* sa;
   const char* sb;
   int k_left;
+  bool x;   // the stage belongs to a tile of more than BM rows (all lpa operand A loads)
 };
 
 // ---- Fragments ---------------------------------------------------------------------------
@@ -580,7 +603,7 @@ __device__ __forceinline__ void slot_loads(char* stage, const StageSrc& ss, cons
   constexpr int NS = n_slots<M>(), LPW = lpw<MODE>();
   constexpr int PER = (LPW + NS - 1) / NS, EVERY = NS > LPW ? NS / LPW : 1;
   if constexpr (I < PER && Q % EVERY == 0 && (Q / EVERY) * PER + I < LPW) {
-    issue_fast<MODE, (Q / EVERY) * PER + I>(stage, ss.sa, ss.sb, voff, ss.k_left, wave, lane);
+    issue_fast<MODE, (Q / EVERY) * PER + I>(stage, ss.sa, ss.sb, voff, ss.k_left, ss.x, wave, lane);
     slot_loads<MODE, Q, I + 1, M>(stage, ss, voff, wave, lane);
   }
 }
@@ -1044,8 +1067,9 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Producer of the load stream: the tile and K step of the next stage to load.  Once the stream
-// runs out it keeps reloading the last stage (valid memory, into slots nobody reads again), so
-// every K step issues exactly lpw loads per wave and the vmcnt arithmetic stays fixed.
+// runs out it keeps reloading the last stage (valid memory, into slots nobody reads again).  The
+// K loop's waits (everything, or everything but the last epilogue's stores) do not depend on how
+// many loads a stage has, so a stage of a tile of at most BM rows skips the A loads past row BM.
 struct Producer {
   Tile t;
   int i, k;        // this XCD's tile list position, K step
@@ -1059,6 +1083,7 @@ __device__ __forceinline__ StageSrc stage_src(const Producer& pr, const GemmArgs
   StageSrc ss;
   const int k0 = pr.t.k_begin + pr.k * BKS;
   ss.k_left = pr.t.k_end - k0;
+  ss.x = pr.t.x;
   stage_bases<MODE>(seg_args(p, pr.t.seg), pr.t, k0, wave, ss.sa, ss.sb);
   ss.sa = uniform_ptr(ss.sa);
   ss.sb = uniform_ptr(ss.sb);
@@ -1281,7 +1306,8 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     issue_all<MODE, 0>(seg_args(p, pr.t.seg), lds + s * STAGE, pr.t, pr.t.k_begin + pr.k * BKS, wave, lane);
     advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
   }
-  wait_vm<(NSTAGE - 1) * lpw<MODE>()>();
+  // stage 0 landed: at most stage 1's loads outstanding (one fewer per skipped A load)
+  wait_vm<(NSTAGE - 1) * (lpw<MODE>() - lpa_skip<MODE>())>();
   barrier();
   FragA<MODE> a0, a1;
   FragB<MODE> b0, b1;

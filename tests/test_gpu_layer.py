@@ -151,10 +151,16 @@ def test_full_size_layer_sampled(name):
     assert_close("dx[sample]", tnp(b["dx"][tt]), sb["dx"], tol)
     if cfg.routing == "learned":
         assert_close("dgate[sample]", tnp(b["dgate"][tt]), sb["dgates"], tol)
-    # Weight gradients of two experts: the busiest and the least busy non-empty one.
+    # Weight gradients of the busiest, the least busy non-empty and the median-load expert, and of
+    # one expert of 257..320 rows if there is one (a single 320-row tile in the forward products).
     counts = R["counts"]
     nz = np.nonzero(counts)[0]
-    for e in {int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])}:
+    pick = {int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])]),
+            int(nz[np.argsort(counts[nz])[len(nz) // 2]])}
+    mid = np.nonzero((counts > 256) & (counts <= 320))[0]
+    if len(mid):
+        pick.add(int(mid[0]))
+    for e in sorted(pick):
         dW1, dW3, dW2 = expert_weight_grads(cfg, vals, R, e, None)
         assert_close(f"dw1[{e}]", tnp(b["dw1"][e]), dW1, tol)
         assert_close(f"dw3[{e}]", tnp(b["dw3"][e]), dW3, tol)

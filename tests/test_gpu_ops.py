@@ -222,6 +222,30 @@ def test_grouped_mlp_320_row_tiles(f):
     check_grouped_mlp("bf16", off, 256, f, (4,), 13)
 
 
+@pytest.mark.parametrize("sizes", [X_SIZES, TAIL_SIZES])
+def test_down_bwd_dab_matches_oracle(sizes):
+    """The SwiGLU-backward product's own output [dA | dB] (the combined backward call keeps it in
+    its workspace), on groups around the 256- and 320-row tile boundaries."""
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    G, M, d, f = len(sizes), int(off[-1]), 256, 256
+    log(f"down_bwd dA/dB sizes={sizes}")
+    P = mlp_problem(M, G, d, f, "bf16", 17)
+    dev = {k: dev_tensor(v, "bf16") for k, v in P.items()}
+    offs = i32(off)
+    A, B, H, _ = O.grouped_swiglu_forward(P["X"], off, P["w1"], P["w3"], P["w2"])
+    A, B = as_dtype_values(A, "bf16"), as_dtype_values(B, "bf16")   # the stashes as stored
+    _, _, _, _, rdA, rdB = O.grouped_swiglu_backward(P["dY"], P["X"], A, B, H, off, P["w1"], P["w3"], P["w2"])
+    a, b = dev_tensor(A, "bf16"), dev_tensor(B, "bf16")
+    dab = empty((M, 2 * f), "bf16")
+    wsn = L.moe_grouped_mlp_bwd_workspace_size(M, G, d, f)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=DEV)
+    L.moe_expert_down_bwd(dev["dY"], a, b, offs, G, M, d, f, dev["w2"], L.MOE_BF16, dab, ws, wsn)
+    torch.cuda.synchronize()
+    got = tnp(dab)
+    assert_close("dA", got[:, :f], rdA, TOL["bf16"])
+    assert_close("dB", got[:, f:], rdB, TOL["bf16"])
+
+
 def check_grouped_mlp(dtype, off, d, f, empties, seed):
     G, M = len(off) - 1, int(off[-1])
     P = mlp_problem(M, G, d, f, dtype, seed)
@@ -338,12 +362,15 @@ def test_two_expert_sets(dtype, shared_f):
     tol = TOL[dtype]
     for i, (P, off, (M, G, f)) in enumerate(zip(probs, offs, shapes)):
         A, B, H, Y = O.grouped_swiglu_forward(P["X"], off, P["w1"], P["w3"], P["w2"])
-        rdx, rdw1, rdw3, rdw2, _, _ = O.grouped_swiglu_backward(P["dY"], P["X"], A, B, H, off, P["w1"], P["w3"],
-                                                                P["w2"])
+        rdx, rdw1, rdw3, rdw2, rdA, rdB = O.grouped_swiglu_backward(P["dY"], P["X"], A, B, H, off, P["w1"],
+                                                                    P["w3"], P["w2"])
         got = results[0][i]
         for name, ref in (("a", A), ("b", B), ("h", H), ("y", Y), ("dx", rdx), ("dw1", rdw1), ("dw3", rdw3),
                           ("dw2", rdw2)):
             assert_close(f"set{i}.{name}", tnp(got[name]), ref, tol)
+        dab = tnp(got["dab"])
+        assert_close(f"set{i}.dA", dab[:, :f], rdA, tol)
+        assert_close(f"set{i}.dB", dab[:, f:], rdB, tol)
         for name in ("a", "b", "h", "y", "dab", "dx"):
             assert torch.equal(got[name], results[1][i][name]), f"set{i}.{name}: merged != per-set"
 

@@ -935,9 +935,13 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& 
 // rotation by 8 lanes inside each 16-lane row (DPP row_ror:8) of block 1's pieces and a select on
 // lane bit 3 give A (rows 0..7: block 0 where bit 3 is clear, block 1 where it is set) and B (rows
 // 8..15): 8 lanes and 128 contiguous bytes (a whole cache line) per row, in as many store
-// instructions as two blocks stored apart.
+// instructions as two blocks stored apart.  NT: a nontemporal store (weight gradients, which nothing
+// in the layer pass reads again: with normal stores the 4 MB of gradient lines an XCD writes per
+// round of tiles evicted the operand panels from L2, and the panels were fetched again).
+template <bool NT>
 __device__ __forceinline__ void st_rows128(const OutWin& w, int br, const float (&x0)[2][8], const float (&x1)[2][8],
                                            int lane) {
+  constexpr int AUX = NT ? 2 : 0;   // cache policy bits of the buffer store: nt
   u32x4_t a[2], c[2];
   swap16(pack8_bf16(x0[0]), pack8_bf16(x0[1]), a[0], a[1]);
   swap16(pack8_bf16(x1[0]), pack8_bf16(x1[1]), c[0], c[1]);
@@ -954,13 +958,13 @@ __device__ __forceinline__ void st_rows128(const OutWin& w, int br, const float 
       B[e] = hi8 ? a[q][e] : t;
     }
     const int r = rl + 16 * q;
-    __builtin_amdgcn_raw_buffer_store_b128(A, w.r, (int)(r * w.row_bytes) + (cx + (hi8 ? 32 : 0)) * 2, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(B, w.r, (int)((r + 8) * w.row_bytes) + (cx + (hi8 ? 0 : 32)) * 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(A, w.r, (int)(r * w.row_bytes) + (cx + (hi8 ? 32 : 0)) * 2, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(B, w.r, (int)((r + 8) * w.row_bytes) + (cx + (hi8 ? 0 : 32)) * 2, 0, AUX);
   }
 }
 // The epilogue of the modes with one bf16 output and no elementwise math (down projection, gate/up
 // data gradient, unsplit weight gradients), block row MIDX.. of the wave.
-template <int MIDX, int M>
+template <int MIDX, int M, bool NT>
 __device__ __forceinline__ void epilogue_rows128(const OutWins& o, const f32x16_t (&acc)[M][NI], int lane) {
   if constexpr (MIDX < M) {
     float v0[2][8], v1[2][8];
@@ -968,8 +972,8 @@ __device__ __forceinline__ void epilogue_rows128(const OutWins& o, const f32x16_
     block_half(acc[MIDX][0], 1, v0[1]);
     block_half(acc[MIDX][1], 0, v1[0]);
     block_half(acc[MIDX][1], 1, v1[1]);
-    st_rows128(o.w[0], MIDX * 32, v0, v1, lane);
-    epilogue_rows128<MIDX + 1, M>(o, acc, lane);
+    st_rows128<NT>(o.w[0], MIDX * 32, v0, v1, lane);
+    epilogue_rows128<MIDX + 1, M, NT>(o, acc, lane);
   }
 }
 
@@ -1003,7 +1007,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
   if constexpr (MODE == GEMM_DOWN_BWD) aux_prologue<MODE, 0>(p, row0, col0, t.m_end, aux, lane);
   if constexpr (MODE != GEMM_UP_FWD && MODE != GEMM_DOWN_BWD) {
     if (ksplit == 1) {   // same store count as the per-block path (two per block)
-      epilogue_rows128<0, M>(o, acc, lane);
+      epilogue_rows128<0, M, Traits<MODE>::raggedK>(o, acc, lane);
       return;
     }
   }

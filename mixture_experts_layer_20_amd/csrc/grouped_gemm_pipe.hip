@@ -217,10 +217,10 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
   t.half = false;
   t.x = false;
   if constexpr (!Traits<MODE>::raggedK) {
-    // Tile order: group by group; inside a group, bands of `band` row tiles, and inside a band
-    // column by column.  A band spans about as many tiles as an XCD runs at once, so the tiles
-    // that read one weight tile run together, and a band cut by that window re-reads activation
-    // rows rather than a whole expert's weights.
+    // Tile order: group by group; inside a group, bands of `band` (4) row tiles, and inside a band
+    // column by column.  An XCD's round of 32 tiles then covers 4 row tiles by 8 column tiles of a
+    // large group (the shared expert), which reads the fewest distinct operand panels per round
+    // (4 + 8); the row tiles that read one weight tile run together.
     int lo = 0, hi = p.G;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -1246,7 +1246,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     geo[sg].NT = mode_N(MODE, p.d, f) / BN;
     geo[sg].MT = TR::raggedK ? mode_Mw(MODE, p.d, f) / BM : 0;
     geo[sg].ks = sg ? max(1, p.s1.ksplit) : ksplit;
-    geo[sg].band = max(1, (int)(gridDim.x >> 3) / geo[sg].NT);
+    geo[sg].band = 4;
     if (sg == 1 && !two) {
       geo[sg].total = 0;
     } else if constexpr (!TR::raggedK) {

@@ -4,7 +4,8 @@
 // Tokens are moved to experts that stay resident ("Olmo-core 3 Opens Large MoE Training",
 // "Technical Deep Dive"); each expert's rows form one ragged group of the grouped GEMM.
 //
-// Design (one workgroup = 256x256 output tile, 8 waves in a 2x4 grid, 128x64 per wave):
+// Design (one workgroup = 256x256 output tile, 8 waves in a 2x4 grid, 128x64 per wave; a group of
+// 257..320 rows in the forward and data-gradient products takes one 320x256 tile, 160x64 per wave):
 //  * K is consumed 64 at a time ("K step") through two 64 KiB LDS stages that global loads fill
 //    directly (global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16*l).  The loads form one
 //    continuous stream over all tiles of the workgroup: a stage is refilled with the stage two steps
@@ -18,7 +19,7 @@
 //    (weights in dgrad, activations in wgrad) is kept [64 k][256 rows] (512-byte rows, 64-byte
 //    windows XOR-swizzled by k) and read with ds_read_b64_tr_b16, which hands each lane 4 consecutive
 //    k of one column: two such reads form a 32x32x16 MFMA operand.  No transposition pass.
-//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators (128 per lane, in AGPRs).
+//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators (128 per lane, 160 in a 320-row tile).
 //  * Two waves per SIMD (one per row half), so one can feed the matrix core while the other waits
 //    on a load issue, a fragment read or the barrier.  A K step is four phases of 8 MFMAs (one per
 //    16-deep substep); every LDS fragment read and every global load is placed between two MFMAs
@@ -28,7 +29,10 @@
 //    before each LDS access).
 //  * Epilogue straight from the accumulators: a v_permlane32_swap gives each lane 8 consecutive
 //    columns of one row, the mode's elementwise math (SwiGLU, SwiGLU backward, whose A/B stash is
-//    loaded in the same layout a block ahead) is applied and 16-byte bf16 stores go out.
+//    loaded in the same layout a block ahead) is applied and 16-byte bf16 stores go out, as whole
+//    128-byte rows where the mode has one output.  Weight gradients are stored nontemporally, and
+//    three quarters of a weight-gradient tile's stores are issued during the next tile's first K
+//    step, between its MFMAs.
 //  * Persistent grid, per-expert tile prefix computed in-kernel, tiles dealt so each XCD walks one
 //    contiguous run of each expert set (workgroup b runs on XCD b % 8); an XCD's last round of
 //    tiles, when it would keep at most half of its workgroups busy, is dealt as 128-row half tiles,
@@ -608,21 +612,61 @@ __device__ __forceinline__ void slot_loads(char* stage, const StageSrc& ss, cons
   }
 }
 
+// Deferred epilogue stores of the unsplit weight gradients.  A weight-gradient tile has a short K
+// loop (the expert's rows, 4 K steps at 256 rows), and its epilogue writes as many bytes as the
+// loop loads from L2; issued all at once, the stores hold the matrix cores idle.  So the epilogue
+// stores block row 0 of the wave and keeps block rows 1..3 (DEFER store instructions) as packed
+// bf16 rows, which the first K step of the wave's next tile issues between its MFMAs, four per
+// phase in the first three phases.  The K loop's wait arithmetic is unchanged: the step's wait
+// comes after them, and an epilogue plus the deferred stores still issue epilogue_stores().
+constexpr int DEFER_ROWS = 3;
+constexpr int DEFER = 4 * DEFER_ROWS;
+struct Pending {
+  u32x4_t v[DEFER];
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t row_bytes;
+  int offa, offb;   // per-lane byte offsets of the A and B rows of a pair (row 0 of the window)
+};
+struct NoPending {};
+template <int MODE>
+using PendingOf = typename std::conditional<Traits<MODE>::raggedK, Pending, NoPending>::type;
+// Deferred store I: block row MI - DEFER_ROWS + I / 4, row half q, the pair's A (rows 0..7) or B
+// (rows 8..15) store of st_rows128.
+template <int I>
+__device__ __forceinline__ void pending_store(const Pending& pd) {
+  constexpr int mi = MI - DEFER_ROWS + I / 4, q = (I / 2) % 2;
+  constexpr bool isb = I % 2;
+  const int off = (isb ? pd.offb : pd.offa) + (int)((mi * 32 + 16 * q + (isb ? 8 : 0)) * pd.row_bytes);
+  __builtin_amdgcn_raw_buffer_store_b128(pd.v[I], pd.r, off, 0, 2);
+}
+
+template <int I>
+__device__ __forceinline__ void flush_pending(const Pending& pd) {
+  if constexpr (I < DEFER) {
+    pending_store<I>(pd);
+    flush_pending<I + 1>(pd);
+  }
+}
+
 // One phase of a K step: the MFMAs of the current substep (fragments ac, bc); the reads of the
 // next substep into an, bn at ra/rb; with LOADS, the loads of the stage two steps ahead into this
-// step's slot.
-template <int MODE, bool ACT, bool LOADS, int Q, int M>
+// step's slot; with PS >= 0, the deferred stores of phase PS of a tile's first K step.
+template <int MODE, bool ACT, bool LOADS, int Q, int M, int PS = -1>
 __device__ __forceinline__ void phase(f32x16_t (&acc)[M][NI], const FragA<MODE>& ac, const FragB<MODE>& bc,
                                       FragA<MODE>& an, FragB<MODE>& bn, uint32_t ra, uint32_t rb, char* stage,
-                                      const StageSrc& ss, const LoadOffs& voff, int wave, int lane) {
+                                      const StageSrc& ss, const LoadOffs& voff, int wave, int lane,
+                                      const PendingOf<MODE>* pd = nullptr) {
   if constexpr (Q < n_slots<M>()) {
     if constexpr (ACT) {
       mfma_slot<MODE, Q, M>(acc, ac, bc);
       slot_reads<MODE, Q, 0, M>(an, bn, ra, rb);
     }
     if constexpr (LOADS) slot_loads<MODE, Q, 0, M>(stage, ss, voff, wave, lane);
+    constexpr int SPP = (DEFER + 2) / 3, EVERY = n_slots<M>() / SPP;   // deferred stores per phase
+    if constexpr (PS >= 0 && Q % EVERY == EVERY - 1 && PS * SPP + Q / EVERY < DEFER)
+      pending_store<PS * SPP + Q / EVERY>(*pd);
     __builtin_amdgcn_sched_barrier(0);
-    phase<MODE, ACT, LOADS, Q + 1, M>(acc, ac, bc, an, bn, ra, rb, stage, ss, voff, wave, lane);
+    phase<MODE, ACT, LOADS, Q + 1, M, PS>(acc, ac, bc, an, bn, ra, rb, stage, ss, voff, wave, lane, pd);
   }
 }
 
@@ -815,7 +859,8 @@ __device__ __forceinline__ void store_block(const GemmArgs& p, const OutWins& o,
 }
 
 // Store instructions every epilogue issues at least (per wave; the optional pre-activation stashes
-// of the gate/up GEMM not counted).
+// of the gate/up GEMM not counted; an unsplit weight-gradient epilogue with the deferred stores the
+// next tile's first K step issues before its wait).
 template <int MODE>
 constexpr int epilogue_stores() {
   return MODE == GEMM_UP_FWD ? 8 : (MODE == GEMM_DOWN_BWD ? 32 : 16);
@@ -938,43 +983,76 @@ __device__ __forceinline__ void epilogue_from(const GemmArgs& p, const OutWins& 
 // instructions as two blocks stored apart.  NT: a nontemporal store (weight gradients, which nothing
 // in the layer pass reads again: with normal stores the 4 MB of gradient lines an XCD writes per
 // round of tiles evicted the operand panels from L2, and the panels were fetched again).
+__device__ __forceinline__ void rows128_data(const float (&x0)[2][8], const float (&x1)[2][8], int lane,
+                                             u32x4_t (&A)[2], u32x4_t (&B)[2]) {
+  u32x4_t a[2], c[2];
+  swap16(pack8_bf16(x0[0]), pack8_bf16(x0[1]), a[0], a[1]);
+  swap16(pack8_bf16(x1[0]), pack8_bf16(x1[1]), c[0], c[1]);
+  const bool hi8 = (lane & 8) != 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)c[q][e], 0x128, 0xf, 0xf, false);
+      A[q][e] = hi8 ? t : a[q][e];
+      B[q][e] = hi8 ? a[q][e] : t;
+    }
+  }
+}
 template <bool NT>
 __device__ __forceinline__ void st_rows128(const OutWin& w, int br, const float (&x0)[2][8], const float (&x1)[2][8],
                                            int lane) {
   constexpr int AUX = NT ? 2 : 0;   // cache policy bits of the buffer store: nt
-  u32x4_t a[2], c[2];
-  swap16(pack8_bf16(x0[0]), pack8_bf16(x0[1]), a[0], a[1]);
-  swap16(pack8_bf16(x1[0]), pack8_bf16(x1[1]), c[0], c[1]);
+  u32x4_t A[2], B[2];
+  rows128_data(x0, x1, lane, A, B);
   const bool hi8 = (lane & 8) != 0;
   const int rl = br + (lane & 7);
   const int cx = xcol_bf16(lane);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    u32x4_t A, B;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)c[q][e], 0x128, 0xf, 0xf, false);
-      A[e] = hi8 ? t : a[q][e];
-      B[e] = hi8 ? a[q][e] : t;
-    }
     const int r = rl + 16 * q;
-    __builtin_amdgcn_raw_buffer_store_b128(A, w.r, (int)(r * w.row_bytes) + (cx + (hi8 ? 32 : 0)) * 2, 0, AUX);
-    __builtin_amdgcn_raw_buffer_store_b128(B, w.r, (int)((r + 8) * w.row_bytes) + (cx + (hi8 ? 0 : 32)) * 2, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(A[q], w.r, (int)(r * w.row_bytes) + (cx + (hi8 ? 32 : 0)) * 2, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(B[q], w.r, (int)((r + 8) * w.row_bytes) + (cx + (hi8 ? 0 : 32)) * 2, 0, AUX);
   }
 }
 // The epilogue of the modes with one bf16 output and no elementwise math (down projection, gate/up
 // data gradient, unsplit weight gradients), block row MIDX.. of the wave.
-template <int MIDX, int M, bool NT>
+template <int MIDX, int M, bool NT, int END = M>
 __device__ __forceinline__ void epilogue_rows128(const OutWins& o, const f32x16_t (&acc)[M][NI], int lane) {
-  if constexpr (MIDX < M) {
+  if constexpr (MIDX < END) {
     float v0[2][8], v1[2][8];
     block_half(acc[MIDX][0], 0, v0[0]);
     block_half(acc[MIDX][0], 1, v0[1]);
     block_half(acc[MIDX][1], 0, v1[0]);
     block_half(acc[MIDX][1], 1, v1[1]);
     st_rows128<NT>(o.w[0], MIDX * 32, v0, v1, lane);
-    epilogue_rows128<MIDX + 1, M, NT>(o, acc, lane);
+    epilogue_rows128<MIDX + 1, M, NT, END>(o, acc, lane);
   }
+}
+// The last DEFER_ROWS block rows of a wave's unsplit weight gradient, packed for pending_store.
+template <int M>
+__device__ __forceinline__ void defer_rows(const OutWin& w, const f32x16_t (&acc)[M][NI], int lane, Pending& pd) {
+#pragma unroll
+  for (int mi = M - DEFER_ROWS; mi < M; ++mi) {
+    float v0[2][8], v1[2][8];
+    block_half(acc[mi][0], 0, v0[0]);
+    block_half(acc[mi][0], 1, v0[1]);
+    block_half(acc[mi][1], 0, v1[0]);
+    block_half(acc[mi][1], 1, v1[1]);
+    u32x4_t A[2], B[2];
+    rows128_data(v0, v1, lane, A, B);
+    const int i = 4 * (mi - (M - DEFER_ROWS));
+    pd.v[i + 0] = A[0];
+    pd.v[i + 1] = B[0];
+    pd.v[i + 2] = A[1];
+    pd.v[i + 3] = B[1];
+  }
+  const bool hi8 = (lane & 8) != 0;
+  const int cx = xcol_bf16(lane);
+  pd.r = w.r;
+  pd.row_bytes = w.row_bytes;
+  pd.offa = (int)((lane & 7) * w.row_bytes) + (cx + (hi8 ? 32 : 0)) * 2;
+  pd.offb = (int)((lane & 7) * w.row_bytes) + (cx + (hi8 ? 0 : 32)) * 2;
 }
 
 // Pre-activation loads of blocks IDX..AUX_AHEAD-1, issued in block order before the first store.
@@ -992,7 +1070,7 @@ __device__ __forceinline__ void aux_prologue(const GemmArgs& p, int row0, int co
 // is dropped, and it issues the same number of memory instructions as the others.
 template <int MODE, int M>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t (&acc)[M][NI], const Tile& t,
-                                              int wm, int wn, int lane, float* partial) {
+                                              int wm, int wn, int lane, float* partial, PendingOf<MODE>& pd, bool& pd_on) {
   // The accumulator reads are opaque to the hazard checker: leave the last MFMA's write-back
   // (at most 18 wait states) behind before the first of them.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
@@ -1005,6 +1083,14 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& p, const f32x16_t 
   const int ksplit = t.ks;
   AuxBlock aux[AUX_AHEAD + 1];
   if constexpr (MODE == GEMM_DOWN_BWD) aux_prologue<MODE, 0>(p, row0, col0, t.m_end, aux, lane);
+  if constexpr (Traits<MODE>::raggedK && M == MI) {
+    if (ksplit == 1) {   // block rows past MI - DEFER_ROWS go out in the next tile's first K step
+      epilogue_rows128<0, M, true, M - DEFER_ROWS>(o, acc, lane);
+      defer_rows<M>(o.w[0], acc, lane, pd);
+      pd_on = true;
+      return;
+    }
+  }
   if constexpr (MODE != GEMM_UP_FWD && MODE != GEMM_DOWN_BWD) {
     if (ksplit == 1) {   // same store count as the per-block path (two per block)
       epilogue_rows128<0, M, Traits<MODE>::raggedK>(o, acc, lane);
@@ -1163,20 +1249,46 @@ __device__ __forceinline__ uint32_t sub_addr(uint32_t base, uint32_t sb) {
   else return base + sb + (uint32_t)(8192 * S);
 }
 
+// One K step (stage j, slot j & 1): four phases of 16-deep substeps whose fragments alternate
+// between the register sets 0 and 1; the fourth phase reads substep 0 of stage j + 1 from the other
+// slot and loads stage j + 2 into this one, which every wave has finished reading by then.  PD: the
+// first three phases also issue the previous tile's deferred stores.
+template <int MODE, bool ACT, int M, bool PD>
+__device__ __forceinline__ void kstep(const GemmArgs& p, f32x16_t (&acc)[M][NI], uint32_t fa, const FragBases& fb,
+                                      FragA<MODE>& a0, FragB<MODE>& b0, FragA<MODE>& a1, FragB<MODE>& b1, int j,
+                                      int since_epi, Producer& pr, const SegGeo (&geo)[2], const Deal& dl, int nbx,
+                                      int wave, int lane, char* lds, const PendingOf<MODE>& pd) {
+  constexpr uint32_t STAGE = stage_bytes<MODE>();
+  const uint32_t sb = (j & 1) * STAGE;
+  phase<MODE, ACT, false, 0, M, PD ? 0 : -1>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 1>(fa, sb), sub_addr<MODE, false, 1>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane, &pd);
+  if constexpr (ACT) frag_wait<MODE>(a1, b1);
+  phase<MODE, ACT, false, 0, M, PD ? 1 : -1>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 2>(fa, sb), sub_addr<MODE, false, 2>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane, &pd);
+  if constexpr (ACT) frag_wait<MODE>(a0, b0);
+  phase<MODE, ACT, false, 0, M, PD ? 2 : -1>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 3>(fa, sb), sub_addr<MODE, false, 3>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane, &pd);
+  if constexpr (ACT) frag_wait<MODE>(a1, b1);
+  // Stage j+1 has landed once nothing issued before the last epilogue's stores is outstanding
+  // (the first step after an epilogue; at least epilogue_stores() of them follow the stage's
+  // loads), or nothing at all; the barrier makes every wave's part visible and frees slot j & 1.
+  if (since_epi == 0) wait_vm<epilogue_stores<MODE>()>();
+  else wait_vm<0>();
+  barrier();
+  const uint32_t sn = ((j + 1) & 1) * STAGE;
+  phase<MODE, ACT, true, 0, M>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 0>(fa, sn), sub_addr<MODE, false, 0>(fb.b, sn), lds + sb, pr.ss, pr.lo, wave, lane);
+  advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
+  if constexpr (ACT) frag_wait<MODE>(a0, b0);
+}
+
 // One output tile: its K steps j, j+1, ... and its epilogue.  M blocks per wave row (MI, or MIX
 // for a tile of more than 256 rows).  ACT: on entry a0/b0 hold substep 0 of stage j.  !ACT (the
 // idle row half of a 128-row tile): the wave issues its share of the load stream and the
-// epilogue's memory instructions only, and reads no fragments.
-//
-// A K step (stage j, slot j & 1): four phases of 16-deep substeps whose fragments alternate
-// between the register sets 0 and 1; the fourth phase reads substep 0 of stage j + 1 from the other
-// slot and loads stage j + 2 into this one, which every wave has finished reading by then.
+// epilogue's memory instructions only, and reads no fragments.  pd_on: pd holds the previous
+// tile's deferred stores.
 template <int MODE, bool ACT, int M>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& ct, const FragBases& fb, FragA<MODE>& a0,
                                          FragB<MODE>& b0, FragA<MODE>& a1, FragB<MODE>& b1, int& j,
                                          int& since_epi, Producer& pr, const SegGeo (&geo)[2], const Deal& dl,
-                                         int nbx, int wm, int wn, int wave, int lane, char* lds, float* partial) {
-  constexpr uint32_t STAGE = stage_bytes<MODE>();
+                                         int nbx, int wm, int wn, int wave, int lane, char* lds, float* partial,
+                                         PendingOf<MODE>& pd, bool& pd_on) {
   const uint32_t fa = M == MIX ? fb.ax : fb.a;
   f32x16_t acc[M][NI];
 #pragma unroll
@@ -1185,27 +1297,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const Tile& ct, cons
     for (int jj = 0; jj < NI; ++jj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
-  for (int kc = 0; kc < ct.nk; ++kc, ++j) {
-    const uint32_t sb = (j & 1) * STAGE;
-    phase<MODE, ACT, false, 0, M>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 1>(fa, sb), sub_addr<MODE, false, 1>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
-    if constexpr (ACT) frag_wait<MODE>(a1, b1);
-    phase<MODE, ACT, false, 0, M>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 2>(fa, sb), sub_addr<MODE, false, 2>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
-    if constexpr (ACT) frag_wait<MODE>(a0, b0);
-    phase<MODE, ACT, false, 0, M>(acc, a0, b0, a1, b1, sub_addr<MODE, true, 3>(fa, sb), sub_addr<MODE, false, 3>(fb.b, sb), nullptr, pr.ss, pr.lo, wave, lane);
-    if constexpr (ACT) frag_wait<MODE>(a1, b1);
-    // Stage j+1 has landed once nothing issued before the last epilogue's stores is outstanding
-    // (the first step after an epilogue; at least epilogue_stores() of them follow the stage's
-    // loads), or nothing at all; the barrier makes every wave's part visible and frees slot j & 1.
-    if (since_epi == 0) wait_vm<epilogue_stores<MODE>()>();
-    else wait_vm<0>();
-    barrier();
-    const uint32_t sn = ((j + 1) & 1) * STAGE;
-    phase<MODE, ACT, true, 0, M>(acc, a1, b1, a0, b0, sub_addr<MODE, true, 0>(fa, sn), sub_addr<MODE, false, 0>(fb.b, sn), lds + sb, pr.ss, pr.lo, wave, lane);
-    advance<MODE>(pr, p, geo, dl, nbx, wave, lane);
-    if constexpr (ACT) frag_wait<MODE>(a0, b0);
+  int kc = 0;
+  if constexpr (Traits<MODE>::raggedK && M == MI && ACT) {
+    if (pd_on) {
+      kstep<MODE, ACT, M, true>(p, acc, fa, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wave, lane, lds, pd);
+      pd_on = false;
+      ++kc, ++j, ++since_epi;
+    }
+  }
+  for (; kc < ct.nk; ++kc, ++j) {
+    kstep<MODE, ACT, M, false>(p, acc, fa, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wave, lane, lds, pd);
     ++since_epi;
   }
-  epilogue_tile<MODE, M>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial);
+  epilogue_tile<MODE, M>(seg_args(p, ct.seg), acc, ct, wm, wn, lane, partial, pd, pd_on);
   since_epi = 0;
 }
 
@@ -1316,6 +1420,8 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
   FragA<MODE> a0, a1;
   FragB<MODE> b0, b1;
   int j = 0, since_epi = 3;
+  PendingOf<MODE> pd;
+  bool pd_on = false;
   for (;;) {
     // Substep 0 of the tile's first stage is read here rather than kept in registers through the
     // previous epilogue (its slot is refilled only after this wave's next barrier, and the previous
@@ -1323,17 +1429,17 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     const uint32_t sb = (j & 1) * STAGE;
     if (!TR::raggedK && ct.half && wm == 1) {
       run_tile<MODE, false, MI>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
-                                partial);
+                                partial, pd, pd_on);
     } else if (has_x<MODE>() && ct.x) {
       read_all<MODE, 0, mi_max<MODE>()>(a0, b0, sub_addr<MODE, true, 0>(fb.ax, sb), sub_addr<MODE, false, 0>(fb.b, sb));
       frag_wait<MODE>(a0, b0);
       run_tile<MODE, true, mi_max<MODE>()>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave,
-                                           lane, lds, partial);
+                                           lane, lds, partial, pd, pd_on);
     } else {
       read_all<MODE, 0, MI>(a0, b0, sub_addr<MODE, true, 0>(fb.a, sb), sub_addr<MODE, false, 0>(fb.b, sb));
       frag_wait<MODE>(a0, b0);
       run_tile<MODE, true, MI>(p, ct, fb, a0, b0, a1, b1, j, since_epi, pr, geo, dl, nbx, wm, wn, wave, lane, lds,
-                               partial);
+                               partial, pd, pd_on);
     }
     bool more = false;
     for (ic += nbx; ic < dl.n; ic += nbx) {
@@ -1345,6 +1451,9 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
       if constexpr (TR::raggedK) zero_tile<MODE>(seg_args(p, ct.seg), ct, wm, wn, lane, partial);
     }
     if (!more) break;
+  }
+  if constexpr (Traits<MODE>::raggedK) {
+    if (pd_on) flush_pending<0>(pd);   // the last tile's deferred stores
   }
   // No direct-to-LDS load may still be writing when the workgroup's LDS is released.
   wait_vm<0>();

@@ -402,145 +402,134 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int
 // ------------------------------------------------------------------------------------------
 // Router backward (gates = softmax over the chosen logits).
 
-// dl[t*k+j] = g_j (dg_j - sum_i g_i dg_i): the logit gradient of the chosen experts.  Evaluated
-// as g_j * sum_i g_i (dg_j - dg_i), equal because the gates sum to one; this form has no
-// cancellation between large terms when one gate is close to 1 and the others are tiny.
-__global__ void route_dl_kernel(const float* dgate, const float* gate, int T, int k, float* dl) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  float g[8], dg[8];
+// The logit gradients of a token's K (>= k) chosen experts: dl_j = g_j (dg_j - sum_i g_i dg_i),
+// evaluated as g_j * sum_i g_i (dg_j - dg_i), equal because the gates sum to one; this form has no
+// cancellation between large terms when one gate is close to 1 and the others are tiny.  Entries
+// j >= k are 0.  Every kernel below takes its dl from here, so all of them see the same values.
+template <int K>
+__device__ __forceinline__ void token_logit_grads(const float* gate, const float* dgate, size_t t, int k,
+                                                  float (&dl)[K]) {
+  float g[K], dg[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    g[j] = j < k ? gate[(size_t)t * k + j] : 0.0f;
-    dg[j] = j < k ? dgate[(size_t)t * k + j] : 0.0f;
+  for (int i = 0; i < K; ++i) {   // loads at a clamped index, never under a condition
+    const size_t a = t * k + (i < k ? i : k - 1);
+    g[i] = i < k ? gate[a] : 0.0f;
+    dg[i] = i < k ? dgate[a] : 0.0f;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
+  for (int j = 0; j < K; ++j) {
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < K; ++i)
       if (i < k) s += g[i] * (dg[j] - dg[i]);
-    dl[(size_t)t * k + j] = g[j] * s;
+    dl[j] = j < k ? g[j] * s : 0.0f;
   }
 }
+// The logit gradient of assignment a = t*k + j.
+__device__ __forceinline__ float assignment_logit_grad(const float* gate, const float* dgate, int a, int k) {
+  float dl[8];
+  token_logit_grads<8>(gate, dgate, (size_t)(a / k), k, dl);
+  const int j = a % k;
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i == j) r = dl[i];
+  return r;
+}
 
-// dx_router[t] = sum_j dl[t,j] * w_router[idx[t,j]], one block per token.
+// dx_router[t] = sum_j dl[t,j] * w_router[idx[t,j]], one block per token (any d).
 template <typename T>
-__global__ __launch_bounds__(256) void route_dx_kernel(const float* dl, const int32_t* idx,
+__global__ __launch_bounds__(256) void route_dx_kernel(const float* dgate, const float* gate, const int32_t* idx,
                                                        const T* w, int d, int k, T* dx) {
   const int t = blockIdx.x;
+  float dl[8];
+  token_logit_grads<8>(gate, dgate, (size_t)t, k, dl);
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
     float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const size_t a = (size_t)t * k + j;
-      acc += dl[a] * to_f32<T>(w[(size_t)idx[a] * d + c]);
-    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) acc += dl[j] * to_f32<T>(w[(size_t)idx[(size_t)t * k + j] * d + c]);
     dx[(size_t)t * d + c] = from_f32<T>(acc);
   }
 }
 
-// The same for d a multiple of 8: each thread 8 consecutive columns of one token (16-byte loads of
-// the expert rows, which stay in L2, and one 16-byte store), DXCOLS columns per block.
-constexpr int DXCOLS = 2048;
-template <typename T>
-__global__ __launch_bounds__(256) void route_dx8_kernel(const float* dl, const int32_t* idx, const T* w, int d,
-                                                        int k, T* dx) {
-  const int t = blockIdx.x;
-  const int c = blockIdx.y * DXCOLS + threadIdx.x * 8;
-  if (c >= d) return;
-  float acc[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const size_t a = (size_t)t * k + j;
-    const float g = dl[a];
-    float wv[8];
-    row8<std::is_same<T, bf16_t>::value>(w, (size_t)idx[a] * d, c, d, true, wv);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += g * wv[q];
+constexpr int SEG = 64;        // permuted rows per partial sum of the router weight gradient
+constexpr int DWCOLS = 1024;   // columns per block (any d)
+constexpr int DWCOLS8 = 2048;  // columns per block, 8 per thread (d a multiple of 8)
+constexpr int DXCOLS = 2048;   // dx_router columns per block, 8 per thread (d a multiple of 8)
+constexpr int DXL = 16;        // 16-byte expert-row loads in flight per thread in a dx_router block
+// Tokens per dx_router block for K expert rows per token (T: element type of the rows).
+template <typename T, int K>
+constexpr int dx_tokens() { return DXL / (K * (sizeof(T) == 2 ? 1 : 2)) > 0 ? DXL / (K * (sizeof(T) == 2 ? 1 : 2)) : 1; }
+
+// pre[e] = SEG-row segments of the experts before e, pre[E] = all of them, in LDS, computed by the
+// block itself (blockDim 256, E <= 256) from the clamped offsets.
+__device__ __forceinline__ void seg_prefix_lds(const int32_t* offsets, int E, int Tk, int* pre) {
+  const int tid = threadIdx.x;
+  int c = 0;
+  if (tid < E) {
+    int lo = offsets[tid], hi = offsets[tid + 1];
+    lo = lo < 0 ? 0 : (lo > Tk ? Tk : lo);
+    hi = hi < lo ? lo : (hi > Tk ? Tk : hi);
+    c = (hi - lo + SEG - 1) / SEG;
   }
-  T* out = dx + (size_t)t * d + c;
-  if constexpr (std::is_same<T, bf16_t>::value) {
-    uint32_t u[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      u[i] = (uint32_t)from_f32<bf16_t>(acc[2 * i]) | ((uint32_t)from_f32<bf16_t>(acc[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(out) = make_uint4(u[0], u[1], u[2], u[3]);
-  } else {
-    reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  pre[tid + 1] = c;
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? pre[tid + 1 - off] : 0;
+    __syncthreads();
+    pre[tid + 1] += v;
+    __syncthreads();
   }
 }
 
-constexpr int SEG = 64;      // permuted rows per partial sum of the router weight gradient
-constexpr int DWCOLS = 1024; // columns per block (any d)
-constexpr int DWCOLS8 = 2048; // columns per block, 8 per thread (d a multiple of 8)
-
-// Segment prefix: number of SEG-row segments before each expert.
-__global__ void seg_prefix_kernel(const int32_t* offsets, int E, int Tk, int32_t* prefix) {
-  __shared__ int s[256];
-  __shared__ int carry_s;
-  const int tid = threadIdx.x;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < E; base += 256) {
-    const int e = base + tid;
-    int c = 0;
-    if (e < E) {
-      int lo = offsets[e], hi = offsets[e + 1];
-      lo = lo < 0 ? 0 : (lo > Tk ? Tk : lo);
-      hi = hi < lo ? lo : (hi > Tk ? Tk : hi);
-      c = (hi - lo + SEG - 1) / SEG;
-    }
-    s[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int v = tid >= off ? s[tid - off] : 0;
-      __syncthreads();
-      s[tid] += v;
-      __syncthreads();
-    }
-    const int carry = carry_s;
-    if (e < E) prefix[e] = carry + s[tid] - c;
-    __syncthreads();
-    if (tid == 255) carry_s = carry + s[255];
-    __syncthreads();
+// The segment of a partial-sum block: its expert e and permuted rows [p0, p1); false past the last.
+__device__ __forceinline__ bool find_segment(const int* pre, const int32_t* offsets, int E, int Tk, int seg, int& e,
+                                             int& p0, int& p1) {
+  if (seg >= pre[E]) return false;
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= seg) lo = mid; else hi = mid;
   }
-  if (tid == 0) prefix[E] = carry_s;
+  e = lo;
+  int r0 = offsets[e], r1 = offsets[e + 1];
+  r0 = r0 < 0 ? 0 : (r0 > Tk ? Tk : r0);
+  r1 = r1 < r0 ? r0 : (r1 > Tk ? Tk : r1);
+  p0 = r0 + (seg - pre[e]) * SEG;
+  p1 = p0 + SEG < r1 ? p0 + SEG : r1;
+  return true;
+}
+
+// The segment's token rows and logit gradients, staged in LDS in permuted-row order.
+__device__ __forceinline__ void stage_segment(const float* dgate, const float* gate, const int32_t* src_row, int k,
+                                              int Tk, int p0, int n, int* tok_s, float* w_s) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    int a = src_row[p0 + i];
+    a = a < 0 ? 0 : (a >= Tk ? Tk - 1 : a);   // a valid row even for a corrupt plan
+    tok_s[i] = a / k;
+    w_s[i] = assignment_logit_grad(gate, dgate, a, k);
+  }
+  __syncthreads();
 }
 
 // Partial dW_router rows: segment s of expert e sums dl(a) * x[a / k] over its rows in order.
 template <typename T>
-__global__ __launch_bounds__(256) void route_dw_partial_kernel(const float* dl, const int32_t* src_row,
-                                                               const int32_t* offsets,
-                                                               const int32_t* seg_prefix,
-                                                               const T* x, int E, int Tk, int d,
-                                                               int k, float* partial) {
-  const int seg = blockIdx.x;
-  if (seg >= seg_prefix[E]) return;
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (seg_prefix[mid] <= seg) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  int r0 = offsets[e], r1 = offsets[e + 1];
-  r0 = r0 < 0 ? 0 : (r0 > Tk ? Tk : r0);
-  r1 = r1 < r0 ? r0 : (r1 > Tk ? Tk : r1);
-  const int p0 = r0 + (seg - seg_prefix[e]) * SEG;
-  const int p1 = p0 + SEG < r1 ? p0 + SEG : r1;
-  const int cbase = blockIdx.y * DWCOLS;
-  // Stage the segment's token rows and weights, then stream the rows in order.
+__global__ __launch_bounds__(256) void route_dw_partial_kernel(const float* dgate, const float* gate,
+                                                               const int32_t* src_row, const int32_t* offsets,
+                                                               const T* x, int E, int Tk, int d, int k,
+                                                               float* partial) {
+  __shared__ int pre[257];
   __shared__ int tok_s[SEG];
   __shared__ float w_s[SEG];
+  seg_prefix_lds(offsets, E, Tk, pre);
+  const int seg = blockIdx.x;
+  int e, p0, p1;
+  if (!find_segment(pre, offsets, E, Tk, seg, e, p0, p1)) return;
+  const int cbase = blockIdx.y * DWCOLS;
   const int n = p1 - p0;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int a = src_row[p0 + i];
-    tok_s[i] = a / k;
-    w_s[i] = dl[a];
-  }
-  __syncthreads();
+  stage_segment(dgate, gate, src_row, k, Tk, p0, n, tok_s, w_s);
   constexpr int NC = DWCOLS / 256;
   float acc[NC];
 #pragma unroll
@@ -560,9 +549,9 @@ __global__ __launch_bounds__(256) void route_dw_partial_kernel(const float* dl, 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (r0 + u < n) {
-        const float w = w_s[r0 + u];
+        const float wgt = w_s[r0 + u];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) acc[i] += w * xv[u][i];
+        for (int i = 0; i < NC; ++i) acc[i] += wgt * xv[u][i];
       }
     }
   }
@@ -573,72 +562,138 @@ __global__ __launch_bounds__(256) void route_dw_partial_kernel(const float* dl, 
   }
 }
 
-// The same with 8 consecutive columns per thread and 16-byte loads of the token rows (d a
-// multiple of 8); rows are accumulated in the same order.
-template <typename T>
-__global__ __launch_bounds__(256) void route_dw_partial8_kernel(const float* dl, const int32_t* src_row,
-                                                                const int32_t* offsets,
-                                                                const int32_t* seg_prefix,
-                                                                const T* x, int E, int Tk, int d,
-                                                                int k, float* partial) {
-  const int seg = blockIdx.x;
-  if (seg >= seg_prefix[E]) return;
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (seg_prefix[mid] <= seg) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  int r0 = offsets[e], r1 = offsets[e + 1];
-  r0 = r0 < 0 ? 0 : (r0 > Tk ? Tk : r0);
-  r1 = r1 < r0 ? r0 : (r1 > Tk ? Tk : r1);
-  const int p0 = r0 + (seg - seg_prefix[e]) * SEG;
-  const int p1 = p0 + SEG < r1 ? p0 + SEG : r1;
-  __shared__ int tok_s[SEG];
-  __shared__ float w_s[SEG];
-  const int n = p1 - p0;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int a = src_row[p0 + i];
-    tok_s[i] = a / k;
-    w_s[i] = dl[a];
-  }
-  __syncthreads();
-  const int c = blockIdx.y * DWCOLS8 + threadIdx.x * 8;
-  if (c >= d) return;
-  float acc[8];
+// 8 columns of one expert row as floats, from 16-byte loads already issued (RW of them: 1 for bf16,
+// 2 for fp32).
+template <typename T, int RW>
+__device__ __forceinline__ void unpack8(const uint4 (&u)[RW], float (&v)[8]) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    const uint32_t wd[4] = {u[0].x, u[0].y, u[0].z, u[0].w};
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-  for (int rr = 0; rr < n; rr += 8) {
-    float xv[8][8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (rr + u < n) {
-        row8<std::is_same<T, bf16_t>::value>(x, (size_t)tok_s[rr + u] * d, c, d, true, xv[u]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xv[u][q] = 0.0f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(wd[i] << 16);
+      v[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
     }
+  } else {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (rr + u < n) {
-        const float w = w_s[rr + u];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] += w * xv[u][q];
-      }
+    for (int r = 0; r < 2; ++r) {
+      v[4 * r + 0] = __uint_as_float(u[r].x);
+      v[4 * r + 1] = __uint_as_float(u[r].y);
+      v[4 * r + 2] = __uint_as_float(u[r].z);
+      v[4 * r + 3] = __uint_as_float(u[r].w);
     }
   }
-  float* out = partial + (size_t)seg * d + c;
-  reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-// dW_router[e] = sum of the expert's segment partials, in segment order (zeros if none).
-__global__ __launch_bounds__(256) void route_dw_reduce_kernel(const float* partial,
-                                                              const int32_t* seg_prefix, int d,
-                                                              float* dw) {
+// The router backward for d a multiple of 8, in one launch: blocks [0, ndw) form the dW_router
+// partial sums (block b: segment b / ncw, 2048 columns b % ncw, 8 per thread), the rest dx_router
+// (dx_tokens tokens per block, 2048 columns, 8 per thread).  The two kinds share no data; one launch
+// lets the latency-bound dx_router blocks run beside the bandwidth-bound partial sums.  A dx_router
+// thread issues all DXL expert-row loads of its tokens before it multiplies (a block per token kept
+// too few bytes in flight per CU); rows j >= k of a token (K > k) load a valid row and are skipped.
+template <typename T, int K>
+__global__ __launch_bounds__(256) void route_bwd8_kernel(const float* dgate, const float* gate, const int32_t* idx,
+                                                         const int32_t* src_row, const int32_t* offsets, const T* x,
+                                                         const T* w, int Tn, int d, int E, int k, int ndw, int ncw,
+                                                         float* partial, T* dx) {
+  constexpr int RW = sizeof(T) == 2 ? 1 : 2;   // 16-byte loads per 8 columns
+  const int Tk = Tn * k;
+  if ((int)blockIdx.x < ndw) {
+    __shared__ int pre[257];
+    __shared__ int tok_s[SEG];
+    __shared__ float w_s[SEG];
+    seg_prefix_lds(offsets, E, Tk, pre);
+    const int seg = blockIdx.x / ncw;
+    int e, p0, p1;
+    if (!find_segment(pre, offsets, E, Tk, seg, e, p0, p1)) return;
+    const int n = p1 - p0;
+    stage_segment(dgate, gate, src_row, k, Tk, p0, n, tok_s, w_s);
+    const int c = (blockIdx.x % ncw) * DWCOLS8 + threadIdx.x * 8;
+    if (c >= d) return;
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int rr = 0; rr < n; rr += 8) {
+      uint4 raw[8][RW];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {   // rows past the segment load its first row (never used)
+        const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)tok_s[rr + u < n ? rr + u : 0] * d + c);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) raw[u][r] = src[r];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (rr + u < n) {
+          float xv[8];
+          unpack8<T, RW>(raw[u], xv);
+          const float wgt = w_s[rr + u];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] += wgt * xv[q];
+        }
+      }
+    }
+    float* out = partial + (size_t)seg * d + c;
+    reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    return;
+  }
+  constexpr int NT = dx_tokens<T, K>();
+  const int ncx = (d + DXCOLS - 1) / DXCOLS;
+  const int b = blockIdx.x - ndw, tb = b / ncx;
+  const int c = (b % ncx) * DXCOLS + threadIdx.x * 8;
+  if (c >= d) return;
+  float dl[NT][K];
+  uint4 raw[NT][K][RW];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int t = min(tb * NT + tt, Tn - 1);
+    token_logit_grads<K>(gate, dgate, (size_t)t, k, dl[tt]);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int e = idx[(size_t)t * k + (j < k ? j : k - 1)];
+      e = e < 0 ? 0 : (e >= E ? E - 1 : e);   // a valid row even for a corrupt selection
+      const uint4* src = reinterpret_cast<const uint4*>(w + (size_t)e * d + c);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) raw[tt][j][r] = src[r];
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int t = tb * NT + tt;
+    if (t >= Tn) break;
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (j < k) {
+        float wv[8];
+        unpack8<T, RW>(raw[tt][j], wv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += dl[tt][j] * wv[q];
+      }
+    }
+    T* out = dx + (size_t)t * d + c;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        u[i] = (uint32_t)from_f32<bf16_t>(acc[2 * i]) | ((uint32_t)from_f32<bf16_t>(acc[2 * i + 1]) << 16);
+      *reinterpret_cast<uint4*>(out) = make_uint4(u[0], u[1], u[2], u[3]);
+    } else {
+      reinterpret_cast<float4*>(out)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      reinterpret_cast<float4*>(out)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+// dW_router[e] = sum of the expert's segment partials, in segment order (zeros if none).  Segments
+// past nseg (the partial sums that exist) are never read.
+__global__ __launch_bounds__(256) void route_dw_reduce_kernel(const float* partial, const int32_t* offsets, int E,
+                                                              int Tk, int d, int nseg, float* dw) {
+  __shared__ int pre[257];
+  seg_prefix_lds(offsets, E, Tk, pre);
   const int e = blockIdx.x;
-  const int s0 = seg_prefix[e], s1 = seg_prefix[e + 1];
+  const int s0 = min(pre[e], nseg), s1 = min(pre[e + 1], nseg);
   for (int c = blockIdx.y * DWCOLS + threadIdx.x; c < d && c < (blockIdx.y + 1) * DWCOLS; c += 256) {
     float acc = 0.0f;
 #pragma unroll 16
@@ -681,8 +736,34 @@ static inline long long max_segments(long long Tk, int E) { return (Tk + SEG - 1
 
 size_t route_bwd_ws_bytes(long long T, long long d, int E, int k) {
   const long long Tk = T * k;
-  return align256((size_t)Tk * sizeof(float)) + align256((size_t)(E + 1) * sizeof(int32_t)) +
-         align256((size_t)max_segments(Tk, E) * d * sizeof(float));
+  return align256((size_t)max_segments(Tk, E) * d * sizeof(float));
+}
+
+template <typename T>
+static void launch_route_bwd8(const float* dgate, const float* gate, const int32_t* idx, const int32_t* src_row,
+                              const int32_t* offsets, const T* x, const T* w, int Tn, int d, int E, int k,
+                              float* partial, T* dx, hipStream_t s) {
+  const int ncw = ceil_div(d, DWCOLS8), ncx = ceil_div(d, DXCOLS);
+  const int ndw = (int)max_segments((long long)Tn * k, E) * ncw;
+  auto grid = [&](int nt) { return dim3((unsigned)(ndw + ceil_div(Tn, nt) * ncx)); };
+  switch (k) {
+    case 1:
+      hipLaunchKernelGGL((route_bwd8_kernel<T, 1>), grid(dx_tokens<T, 1>()), dim3(256), 0, s, dgate, gate, idx, src_row, offsets, x,
+                         w, Tn, d, E, k, ndw, ncw, partial, dx);
+      break;
+    case 2:
+      hipLaunchKernelGGL((route_bwd8_kernel<T, 2>), grid(dx_tokens<T, 2>()), dim3(256), 0, s, dgate, gate, idx, src_row, offsets, x,
+                         w, Tn, d, E, k, ndw, ncw, partial, dx);
+      break;
+    case 3:
+    case 4:
+      hipLaunchKernelGGL((route_bwd8_kernel<T, 4>), grid(dx_tokens<T, 4>()), dim3(256), 0, s, dgate, gate, idx, src_row, offsets, x,
+                         w, Tn, d, E, k, ndw, ncw, partial, dx);
+      break;
+    default:
+      hipLaunchKernelGGL((route_bwd8_kernel<T, 8>), grid(dx_tokens<T, 8>()), dim3(256), 0, s, dgate, gate, idx, src_row, offsets, x,
+                         w, Tn, d, E, k, ndw, ncw, partial, dx);
+  }
 }
 
 hipError_t launch_route_bwd(const float* dgate, const float* gate, const int32_t* topk_idx,
@@ -690,51 +771,32 @@ hipError_t launch_route_bwd(const float* dgate, const float* gate, const int32_t
                             const void* w, int T, int d, int E, int k, bool bf16, float* dw,
                             void* dx_router, void* ws, hipStream_t s) {
   const int Tk = T * k;
-  char* p = reinterpret_cast<char*>(ws);
-  float* dl = reinterpret_cast<float*>(p);
-  p += align256((size_t)Tk * sizeof(float));
-  int32_t* seg_prefix = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)(E + 1) * sizeof(int32_t));
-  float* partial = reinterpret_cast<float*>(p);
-
-  if (T > 0) {
-    hipLaunchKernelGGL(route_dl_kernel, dim3(ceil_div(T, 256)), dim3(256), 0, s, dgate, gate, T, k, dl);
-    if (d % 8 == 0) {
-      const dim3 g((unsigned)T, ceil_div(d, DXCOLS));
-      if (bf16)
-        hipLaunchKernelGGL(route_dx8_kernel<bf16_t>, g, dim3(256), 0, s, dl, topk_idx,
-                           reinterpret_cast<const bf16_t*>(w), d, k, reinterpret_cast<bf16_t*>(dx_router));
-      else
-        hipLaunchKernelGGL(route_dx8_kernel<float>, g, dim3(256), 0, s, dl, topk_idx,
-                           reinterpret_cast<const float*>(w), d, k, reinterpret_cast<float*>(dx_router));
-    } else if (bf16)
-      hipLaunchKernelGGL(route_dx_kernel<bf16_t>, dim3(T), dim3(256), 0, s, dl, topk_idx,
-                         reinterpret_cast<const bf16_t*>(w), d, k, reinterpret_cast<bf16_t*>(dx_router));
-    else
-      hipLaunchKernelGGL(route_dx_kernel<float>, dim3(T), dim3(256), 0, s, dl, topk_idx,
-                         reinterpret_cast<const float*>(w), d, k, reinterpret_cast<float*>(dx_router));
-  }
-  hipLaunchKernelGGL(seg_prefix_kernel, dim3(1), dim3(256), 0, s, offsets, E, Tk, seg_prefix);
-  const int ncb = ceil_div(d, DWCOLS);
-  const long long nseg = max_segments(Tk, E);
-  if (d % 8 == 0) {
-    const dim3 g((unsigned)nseg, ceil_div(d, DWCOLS8));
+  float* partial = reinterpret_cast<float*>(ws);
+  if (T > 0 && d % 8 == 0) {
     if (bf16)
-      hipLaunchKernelGGL(route_dw_partial8_kernel<bf16_t>, g, dim3(256), 0, s, dl, src_row, offsets, seg_prefix,
-                         reinterpret_cast<const bf16_t*>(x), E, Tk, d, k, partial);
+      launch_route_bwd8<bf16_t>(dgate, gate, topk_idx, src_row, offsets, reinterpret_cast<const bf16_t*>(x),
+                                reinterpret_cast<const bf16_t*>(w), T, d, E, k, partial,
+                                reinterpret_cast<bf16_t*>(dx_router), s);
     else
-      hipLaunchKernelGGL(route_dw_partial8_kernel<float>, g, dim3(256), 0, s, dl, src_row, offsets, seg_prefix,
+      launch_route_bwd8<float>(dgate, gate, topk_idx, src_row, offsets, reinterpret_cast<const float*>(x),
+                               reinterpret_cast<const float*>(w), T, d, E, k, partial,
+                               reinterpret_cast<float*>(dx_router), s);
+  } else if (T > 0) {
+    const dim3 gdw((unsigned)max_segments(Tk, E), ceil_div(d, DWCOLS));
+    if (bf16) {
+      hipLaunchKernelGGL(route_dx_kernel<bf16_t>, dim3(T), dim3(256), 0, s, dgate, gate, topk_idx,
+                         reinterpret_cast<const bf16_t*>(w), d, k, reinterpret_cast<bf16_t*>(dx_router));
+      hipLaunchKernelGGL(route_dw_partial_kernel<bf16_t>, gdw, dim3(256), 0, s, dgate, gate, src_row, offsets,
+                         reinterpret_cast<const bf16_t*>(x), E, Tk, d, k, partial);
+    } else {
+      hipLaunchKernelGGL(route_dx_kernel<float>, dim3(T), dim3(256), 0, s, dgate, gate, topk_idx,
+                         reinterpret_cast<const float*>(w), d, k, reinterpret_cast<float*>(dx_router));
+      hipLaunchKernelGGL(route_dw_partial_kernel<float>, gdw, dim3(256), 0, s, dgate, gate, src_row, offsets,
                          reinterpret_cast<const float*>(x), E, Tk, d, k, partial);
-  } else if (bf16) {
-    hipLaunchKernelGGL(route_dw_partial_kernel<bf16_t>, dim3((unsigned)nseg, ncb), dim3(256), 0, s, dl,
-                       src_row, offsets, seg_prefix, reinterpret_cast<const bf16_t*>(x), E, Tk, d, k,
-                       partial);
-  } else {
-    hipLaunchKernelGGL(route_dw_partial_kernel<float>, dim3((unsigned)nseg, ncb), dim3(256), 0, s, dl,
-                       src_row, offsets, seg_prefix, reinterpret_cast<const float*>(x), E, Tk, d, k,
-                       partial);
+    }
   }
-  hipLaunchKernelGGL(route_dw_reduce_kernel, dim3(E, ncb), dim3(256), 0, s, partial, seg_prefix, d, dw);
+  hipLaunchKernelGGL(route_dw_reduce_kernel, dim3(E, ceil_div(d, DWCOLS)), dim3(256), 0, s, partial, offsets, E, Tk, d,
+                     (int)max_segments(Tk, E), dw);
   return hipGetLastError();
 }
 

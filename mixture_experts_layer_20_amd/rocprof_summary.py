@@ -47,7 +47,7 @@ STAGE_OF = [
     (r"local_rank|scan_lds|scan_kernel|scatter_gather|scan_gather|rank_scan", "permute"),
     (r"combine_bwd_kernel", "combine_bwd"),
     (r"combine_kernel", "combine"),
-    (r"route_dl|route_dx|route_dw|seg_prefix", "route_bwd"),
+    (r"route_bwd|route_dx|route_dw", "route_bwd"),
     (r"permute_bwd_kernel", "permute_bwd"),
     (r"aux_", "router_aux"),
     (r"mx_", "mxfp8"),

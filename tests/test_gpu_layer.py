@@ -76,6 +76,39 @@ def test_layer_is_bitwise_deterministic():
             assert torch.equal(v, lay.bufs[k]), k
 
 
+def test_layer_step_replays_as_hip_graph():
+    """The whole step captured once as a HIP graph (nothing in the path allocates, clears memory or
+    synchronizes): every replay, with eager steps in between, reproduces the eager step bit for bit,
+    also after its outputs were overwritten."""
+    cfg = SMALL["bf16_learned_skew"]
+    inp = I.make_inputs(cfg)
+    lay = run_layer_gpu(cfg, inp)
+    keys = [k for k in lay.bufs.t if not k.startswith("ws") and k != "shared_offsets"]
+    ref = {k: lay.bufs[k].clone() for k in keys}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lay.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lay.step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in keys:
+            lay.bufs[k].fill_(float("nan") if lay.bufs[k].is_floating_point() else -1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(lay.bufs[k], ref[k]), f"replay {rep}: {k}"
+        lay.step()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(lay.bufs[k], ref[k]), f"eager step after replay {rep}: {k}"
+
+
 @pytest.mark.parametrize("name", ["fp32_fwd_bwd_learned_bias", "bf16_random_ragged", "bf16_learned_skew"])
 def test_recompute_layer_matches_oracle(name):
     """Per-layer recompute variant (no A/B stash in the forward, gate/up GEMM rerun in the backward)

@@ -1147,6 +1147,72 @@ __device__ __forceinline__ void tile_prefix_lds(int G, const int* offs, int* pre
   __syncthreads();
 }
 
+// Weight gradients: a tile's cost in K steps, plus WG_TILE_COST for its epilogue and the
+// pipeline's turn at a tile boundary (a tile of chunk rows of one split of a group of R rows).
+constexpr int WG_TILE_COST = 5;
+__device__ __forceinline__ int wg_tile_cost(int R, int ks) {
+  const int chunk = (R + ks - 1) / ks;
+  return (chunk + BKS - 1) / BKS + WG_TILE_COST;
+}
+
+// cpref[g] = summed cost of the tiles of the groups before g, cpref[G] the total (every group has
+// tpg tiles, all of one cost), from the clamped offsets in offs.  A group's share is capped so the
+// total stays below 2^30 (only groups far beyond any memory size reach the cap).
+__device__ __forceinline__ void cost_prefix_lds(int G, int ks, int tpg, const int* offs, int* cpref,
+                                                int* scratch) {
+  const int tid = threadIdx.x;
+  const long long cap = (1LL << 30) / (G + 1);
+  if (tid == 0) scratch[NTH] = 0;
+  __syncthreads();
+  for (int base = 0; base < G; base += NTH) {
+    const int g = base + tid;
+    int c = 0;
+    if (g < G) {
+      const int lo = offs[g], hi = max(lo, offs[g + 1]);
+      c = (int)min(cap, (long long)tpg * wg_tile_cost(hi - lo, ks));
+    }
+    scratch[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < NTH; off <<= 1) {
+      const int v = tid >= off ? scratch[tid - off] : 0;
+      __syncthreads();
+      scratch[tid] += v;
+      __syncthreads();
+    }
+    const int carry = scratch[NTH];
+    if (g < G) cpref[g] = carry + scratch[tid] - c;
+    __syncthreads();
+    if (tid == NTH - 1) scratch[NTH] = carry + scratch[NTH - 1];
+    __syncthreads();
+  }
+  if (tid == 0) cpref[G] = scratch[NTH];
+  __syncthreads();
+}
+
+// Summed cost of the tiles before tile i (i <= G * tpg).
+__device__ __forceinline__ int cost_before(const int* cpref, const int* offs, int tpg, int ks, int i) {
+  const int g = i / tpg, r = i - g * tpg;
+  if (r == 0) return cpref[g];
+  const int lo = offs[g], hi = max(lo, offs[g + 1]);
+  return cpref[g] + r * wg_tile_cost(hi - lo, ks);
+}
+
+// First tile of XCD x under a cost-balanced cut: the first tile whose preceding cost reaches x/8
+// of the total.
+__device__ __forceinline__ int cost_cut(const int* cpref, const int* offs, int G, int tpg, int ks, int x) {
+  if (x >= 8) return G * tpg;
+  const int target = (int)((long long)x * cpref[G] / 8);
+  int lo = 0, hi = G;   // largest g with cpref[g] <= target
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cpref[mid] <= target) lo = mid; else hi = mid;
+  }
+  const int glo = offs[lo], ghi = max(glo, offs[lo + 1]);
+  const int tc = wg_tile_cost(ghi - glo, ks);
+  const int j = (target - cpref[lo] + tc - 1) / tc;
+  return lo * tpg + min(j, tpg);
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0): everything but the N newest loads or stores is done.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
 template <int N>
@@ -1367,23 +1433,45 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
   // length (the shared expert's K is its own d_ff in the down and gate/up data-gradient products,
   // and its weight-gradient reduction is split into chunks), so one run over both sets would leave
   // the XCDs that draw set 1 with more work; set 1's tiles are the longer ones where they differ.
+  //
+  // Weight gradients of skewed routing: set 0's tiles differ in cost with their group's rows, and
+  // equal tile counts per XCD can leave one XCD with far more K steps than another.  When the
+  // costliest XCD of the equal-count cut would carry more than 1.15x the mean, set 0 is cut by
+  // cost instead (a cut may then fall inside a group, whose operand panels two XCDs then read;
+  // with balanced routing the equal-count cut is kept for that reason).
   const int xcd = blockIdx.x & 7;
   const int nbx = gridDim.x >> 3;
+  const int total0 = geo[0].total, per0 = (total0 + 7) >> 3;
+  bool by_cost = false;
+  if constexpr (TR::raggedK) {
+    const int tpg = geo[0].ks * geo[0].MT * geo[0].NT;
+    if (total0 > 0) {
+      cost_prefix_lds(p.G, geo[0].ks, tpg, offs_s, pref_s, scan_scratch);
+      int worst = 0;
+      for (int x = 0; x < 8; ++x)
+        worst = max(worst, cost_before(pref_s, offs_s, tpg, geo[0].ks, min(total0, (x + 1) * per0)) -
+                               cost_before(pref_s, offs_s, tpg, geo[0].ks, min(total0, x * per0)));
+      by_cost = (long long)worst * 800 > (long long)pref_s[p.G] * 115;
+    }
+  }
+  auto cut0 = [&](int x) {
+    if constexpr (TR::raggedK) {
+      if (by_cost) return cost_cut(pref_s, offs_s, p.G, geo[0].ks * geo[0].MT * geo[0].NT, geo[0].ks, x);
+    }
+    return min(total0, x * per0);
+  };
   Deal dl;
-  dl.total0 = geo[0].total;
+  dl.total0 = total0;
+  dl.lo0 = cut0(xcd);
   if (two) {
-    const int per0 = (geo[0].total + 7) >> 3, per1 = (geo[1].total + 7) >> 3;
-    dl.lo0 = min(geo[0].total, xcd * per0);
+    const int per1 = (geo[1].total + 7) >> 3;
     dl.lo1 = min(geo[1].total, xcd * per1);
     dl.n1 = min(geo[1].total, (xcd + 1) * per1) - dl.lo1;
-    dl.n = dl.n1 + min(geo[0].total, (xcd + 1) * per0) - dl.lo0;
   } else {
-    const int total = geo[0].total, per = (total + 7) >> 3;
-    dl.lo0 = min(total, xcd * per);
     dl.lo1 = 0;
     dl.n1 = 0;
-    dl.n = min(total, (xcd + 1) * per) - dl.lo0;
   }
+  dl.n = dl.n1 + cut0(xcd + 1) - dl.lo0;
   dl.q = dl.n;
   if constexpr (!TR::raggedK) {
     const int rem = dl.n % nbx;

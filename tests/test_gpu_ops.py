@@ -434,7 +434,11 @@ def test_combine_and_backward(dtype, T, d, E, k, shared):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T,d,E,k,skew", [(600, 256, 16, 4, 0.0), (2000, 128, 64, 4, 4.0),
-                                           (40, 384, 256, 8, 0.0), (9, 16, 4, 1, 0.0)])
+                                           (40, 384, 256, 8, 0.0), (9, 16, 4, 1, 0.0),
+                                           # the full-size launch shape (2 column blocks), a partial
+                                           # column block with k = 3 and 2, and k = 8 of 8
+                                           (1000, 4096, 128, 4, 0.0), (333, 2056, 60, 3, 2.0),
+                                           (150, 2056, 32, 2, 0.0), (257, 4104, 8, 8, 0.0)])
 def test_route_backward(dtype, T, d, E, k, skew):
     log(f"route bwd {dtype} T={T} d={d} E={E} k={k}")
     rng = np.random.default_rng(T + d)

@@ -152,11 +152,30 @@ __device__ __forceinline__ GemmArgs seg_args(const GemmArgs& p, int seg) {
   return q;
 }
 
+// Division of non-negative 31-bit integers by a divisor fixed for the whole launch, as a multiply
+// and a shift (the round-up method of Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (mulhi(m, n) + n) >> l.  The tile decode runs once or twice per tile in every wave, and a
+// weight-gradient tile is only a few K steps long.
+struct FastDiv {
+  uint32_t m, l;
+};
+__device__ __forceinline__ FastDiv make_fastdiv(uint32_t d) {   // d >= 1
+  const uint32_t l = d > 1 ? 32u - (uint32_t)__clz((int)(d - 1)) : 0u;
+  const uint64_t m = ((((uint64_t)1 << l) - d) << 32) / d + 1;
+  return FastDiv{(uint32_t)m, l};
+}
+__device__ __forceinline__ int fdiv(int n, uint32_t m, uint32_t l) {
+  return (int)(((uint64_t)__umulhi((uint32_t)n, m) + (uint32_t)n) >> l);
+}
+
 // Tile geometry of one set: tile columns, weight-gradient row tiles, split, tiles, the row-tile
-// band of the tile order, and the LDS tables (clamped group offsets, per-group tile prefix).
+// band of the tile order, the LDS tables (clamped group offsets, per-group tile prefix) and, for
+// the weight-gradient decode, divisions by MT * NT, MT * WG_NB, NT and the split.
 struct SegGeo {
   int NT, MT, ks, total, band;
   uint32_t offs, pref;
+  FastDiv fd_mn, fd_mb, fd_nt, fd_ks;
 };
 
 // The tiles of one XCD: n list positions; position i < n1 is tile total0 + lo1 + i (set 1), the
@@ -249,27 +268,32 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
     t.k_begin = 0;
     t.k_end = mode_K(MODE, p.d, p.f);
   } else {
-    int r = L / (MT * NT);
+    const SegGeo& g0 = geo[0];
+    const SegGeo& g1 = geo[1];
+    const uint32_t mn_m = t.seg ? g1.fd_mn.m : g0.fd_mn.m, mn_l = t.seg ? g1.fd_mn.l : g0.fd_mn.l;
+    const uint32_t ks_m = t.seg ? g1.fd_ks.m : g0.fd_ks.m, ks_l = t.seg ? g1.fd_ks.l : g0.fd_ks.l;
+    const int r = fdiv(L, mn_m, mn_l);
     const int idx = L - r * (MT * NT);
     // Inside one (group, split): blocks of WG_NB tile columns, walked row tile by row tile, so an
     // XCD's round of workgroups covers a compact block of the expert's gradient and the next round
     // reuses its column operand (wide gradients: 16 tile columns at d = 4096).
     int mt;
     if (NT > WG_NB && NT % WG_NB == 0) {
-      const int jb = idx / (MT * WG_NB), rem = idx - jb * (MT * WG_NB);
+      const int jb = fdiv(idx, t.seg ? g1.fd_mb.m : g0.fd_mb.m, t.seg ? g1.fd_mb.l : g0.fd_mb.l);
+      const int rem = idx - jb * (MT * WG_NB);
       mt = rem / WG_NB;
       t.nt = jb * WG_NB + (rem - mt * WG_NB);
     } else {
-      t.nt = idx % NT;
-      mt = idx / NT;
+      mt = fdiv(idx, t.seg ? g1.fd_nt.m : g0.fd_nt.m, t.seg ? g1.fd_nt.l : g0.fd_nt.l);
+      t.nt = idx - mt * NT;
     }
-    t.split = r % ksplit;
-    t.g = r / ksplit;
+    t.g = fdiv(r, ks_m, ks_l);
+    t.split = r - t.g * ksplit;
     t.m0 = mt * BM;
     t.m_end = t.m0 + BM;
     int r0, r1;
     group_rows_lds(offs, t.g, r0, r1);
-    const int chunk = ((r1 - r0 + ksplit - 1) / ksplit + BKS - 1) / BKS * BKS;
+    const int chunk = (fdiv(r1 - r0 + ksplit - 1, ks_m, ks_l) + BKS - 1) / BKS * BKS;
     t.k_begin = min(r1, r0 + t.split * chunk);
     t.k_end = min(r1, t.k_begin + chunk);
   }
@@ -1417,6 +1441,10 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     geo[sg].MT = TR::raggedK ? mode_Mw(MODE, p.d, f) / BM : 0;
     geo[sg].ks = sg ? max(1, p.s1.ksplit) : ksplit;
     geo[sg].band = 4;
+    geo[sg].fd_mn = make_fastdiv((uint32_t)max(1, geo[sg].MT * geo[sg].NT));
+    geo[sg].fd_mb = make_fastdiv((uint32_t)max(1, geo[sg].MT * WG_NB));
+    geo[sg].fd_nt = make_fastdiv((uint32_t)max(1, geo[sg].NT));
+    geo[sg].fd_ks = make_fastdiv((uint32_t)max(1, geo[sg].ks));
     if (sg == 1 && !two) {
       geo[sg].total = 0;
     } else if constexpr (!TR::raggedK) {

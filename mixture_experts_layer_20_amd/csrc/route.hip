@@ -326,6 +326,40 @@ __device__ __forceinline__ bool select_before(float v, int e, float bv, int bi) 
   return e < bi;
 }
 
+// The better of (bv, bi) and the pair held by the lane that DPP control CTRL names.
+template <int CTRL>
+__device__ __forceinline__ void best_dpp(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xf, 0xf, false);
+  if (select_before(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+// The first pair under select_before over the whole wavefront, in every lane: inside each quad
+// (quad_perm 1,0,3,2 and 2,3,0,1), inside each 16-lane row (row_ror 4 and 8: each lane then holds
+// its row's first pair), then across the four rows from lanes 0, 16, 32, 48 (v_readlane, no LDS
+// round trip).  select_before is a total order, so any reduction order gives the same pair.
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+  best_dpp<0xB1>(bv, bi);
+  best_dpp<0x4E>(bv, bi);
+  best_dpp<0x124>(bv, bi);
+  best_dpp<0x128>(bv, bi);
+  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+    const int oi = __builtin_amdgcn_readlane(bi, 16 * r);
+    if (select_before(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+  bv = v;
+  bi = i;
+}
+
 // Top-k and gates: one wavefront per token, each lane holding up to 4 logits (E <= 256).
 // k rounds of a wave-wide arg-max under select_before.
 __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int T, int E, int k,
@@ -358,15 +392,7 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int
         bi = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (select_before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_best(bv, bi);
     selv[j] = bv;
     seli[j] = bi;
 #pragma unroll

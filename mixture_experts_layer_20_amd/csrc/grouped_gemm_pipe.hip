@@ -637,8 +637,8 @@ __device__ __forceinline__ void slot_loads(char* stage, const StageSrc& ss, cons
 }
 
 // Deferred epilogue stores of the unsplit weight gradients.  A weight-gradient tile has a short K
-// loop (the expert's rows, 4 K steps at 256 rows), and its epilogue writes as many bytes as the
-// loop loads from L2; issued all at once, the stores hold the matrix cores idle.  So the epilogue
+// loop (the expert's rows, 4 K steps at 256 rows), and its epilogue writes half as many bytes as
+// the loop loads from L2; issued all at once, the stores hold the matrix cores idle.  So the epilogue
 // stores block row 0 of the wave and keeps block rows 1..3 (DEFER store instructions) as packed
 // bf16 rows, which the first K step of the wave's next tile issues between its MFMAs, four per
 // phase in the first three phases.  The K loop's wait arithmetic is unchanged: the step's wait

@@ -438,7 +438,8 @@ def test_combine_and_backward(dtype, T, d, E, k, shared):
                                            # the full-size launch shape (2 column blocks), a partial
                                            # column block with k = 3 and 2, and k = 8 of 8
                                            (1000, 4096, 128, 4, 0.0), (333, 2056, 60, 3, 2.0),
-                                           (150, 2056, 32, 2, 0.0), (257, 4104, 8, 8, 0.0)])
+                                           (150, 2056, 32, 2, 0.0), (257, 4104, 8, 8, 0.0),
+                                           (0, 64, 8, 2, 0.0)])   # no tokens: dW_router is all zeros
 def test_route_backward(dtype, T, d, E, k, skew):
     log(f"route bwd {dtype} T={T} d={d} E={E} k={k}")
     rng = np.random.default_rng(T + d)

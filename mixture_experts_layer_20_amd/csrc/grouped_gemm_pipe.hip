@@ -174,6 +174,7 @@ __device__ __forceinline__ int fdiv(int n, uint32_t m, uint32_t l) {
 // the weight-gradient decode, divisions by MT * NT, MT * WG_NB, NT and the split.
 struct SegGeo {
   int NT, MT, ks, total, band;
+  bool rows256;   // the set's groups take 256-row tiles (and a remainder) even where 320-row ones fit
   uint32_t offs, pref;
   FastDiv fd_mn, fd_mb, fd_nt, fd_ks;
 };
@@ -214,14 +215,15 @@ __device__ __forceinline__ void group_rows_lds(uint32_t offs, int g, int& lo, in
 // takes a BMX-row tile only for a group that it holds whole: its 320-row tile spills registers at
 // tile boundaries, which costs more than a remainder tile once a group has two or more tiles.
 template <int MODE>
-__device__ __forceinline__ int group_tiles(int R) {
+__device__ __forceinline__ int group_tiles(int R, bool rows256 = false) {
   if constexpr (MODE == GEMM_DOWN_BWD) return R <= BMX ? (R > 0) : (R + BM - 1) / BM;
-  return has_x<MODE>() ? (R + BMX - 1) / BMX : (R + BM - 1) / BM;
+  return has_x<MODE>() && !rows256 ? (R + BMX - 1) / BMX : (R + BM - 1) / BM;
 }
 template <int MODE>
-__device__ __forceinline__ int tile_rows(int R) {
+__device__ __forceinline__ int tile_rows(int R, bool rows256 = false) {
   if constexpr (!has_x<MODE>()) return BM;
   if constexpr (MODE == GEMM_DOWN_BWD) return R <= BMX ? BMX : BM;
+  if (rows256) return BM;
   const int n = max(1, group_tiles<MODE>(R));
   return (R + n - 1) / n;
 }
@@ -260,7 +262,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& p0, const SegGeo (&g
     const int mt = b * MB + (r - t.nt * mb);
     int r0, r1;
     group_rows_lds(offs, t.g, r0, r1);
-    const int rpt = tile_rows<MODE>(r1 - r0);
+    const int rpt = tile_rows<MODE>(r1 - r0, t.seg ? geo[1].rows256 : geo[0].rows256);
     t.m0 = r0 + mt * rpt;
     t.m_end = min(r1, t.m0 + rpt);
     t.half = t.m_end - t.m0 <= BM / 2;
@@ -1142,7 +1144,7 @@ __device__ __forceinline__ void zero_tile(const GemmArgs& p, const Tile& t, int 
 // Per-group tile prefix (ragged-M modes): pref[g] = tiles (group_tiles) of the groups before g,
 // from the clamped offsets in offs.
 template <int MODE>
-__device__ __forceinline__ void tile_prefix_lds(int G, const int* offs, int* pref, int* scratch) {
+__device__ __forceinline__ void tile_prefix_lds(int G, const int* offs, int* pref, int* scratch, bool rows256) {
   const int tid = threadIdx.x;
   if (tid == 0) scratch[NTH] = 0;
   __syncthreads();
@@ -1151,7 +1153,7 @@ __device__ __forceinline__ void tile_prefix_lds(int G, const int* offs, int* pre
     int c = 0;
     if (g < G) {
       const int lo = offs[g], hi = max(lo, offs[g + 1]);
-      c = group_tiles<MODE>(hi - lo);
+      c = group_tiles<MODE>(hi - lo, rows256);
     }
     scratch[tid] = c;
     __syncthreads();
@@ -1441,6 +1443,24 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     geo[sg].MT = TR::raggedK ? mode_Mw(MODE, p.d, f) / BM : 0;
     geo[sg].ks = sg ? max(1, p.s1.ksplit) : ksplit;
     geo[sg].band = 4;
+    // The second set's groups (the shared expert: T rows in one group) take 256-row tiles where
+    // its tiles are the longer ones (its K is its own d_ff, larger than the routed experts') and
+    // 256-row tiles deal them to each XCD's workgroups in whole rounds while 320-row ones do not:
+    // it is dealt first, and a partial round of its long tiles leaves some workgroups carrying one
+    // more than the others for the whole stage.
+    geo[sg].rows256 = false;
+    if constexpr (has_x<MODE>() && MODE != GEMM_DOWN_BWD) {
+      if (sg == 1 && two && mode_K(MODE, p.d, p.s1.f) > mode_K(MODE, p.d, p.f)) {
+        int n256 = 0, nx = 0;
+        for (int g = 0; g < G; ++g) {
+          const int lo = offs1_s[g], R = max(lo, offs1_s[g + 1]) - lo;
+          n256 += group_tiles<MODE>(R, true);
+          nx += group_tiles<MODE>(R, false);
+        }
+        const int round = 8 * (int)(gridDim.x >> 3);
+        geo[sg].rows256 = (n256 * geo[sg].NT) % round == 0 && (nx * geo[sg].NT) % round != 0;
+      }
+    }
     geo[sg].fd_mn = make_fastdiv((uint32_t)max(1, geo[sg].MT * geo[sg].NT));
     geo[sg].fd_mb = make_fastdiv((uint32_t)max(1, geo[sg].MT * WG_NB));
     geo[sg].fd_nt = make_fastdiv((uint32_t)max(1, geo[sg].NT));
@@ -1450,7 +1470,7 @@ __global__ __launch_bounds__(NTH, 1) void grouped_gemm_pipe(GemmArgs p, int kspl
     } else if constexpr (!TR::raggedK) {
       int* offs_tab = sg ? offs1_s : offs_s;
       int* pref_tab = sg ? pref1_s : pref_s;
-      tile_prefix_lds<MODE>(G, offs_tab, pref_tab, scan_scratch);
+      tile_prefix_lds<MODE>(G, offs_tab, pref_tab, scan_scratch, geo[sg].rows256);
       geo[sg].total = pref_tab[G] * geo[sg].NT;
     } else {
       geo[sg].total = G * geo[sg].ks * geo[sg].MT * geo[sg].NT;

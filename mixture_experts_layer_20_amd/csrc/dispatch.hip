@@ -29,12 +29,19 @@ __global__ __launch_bounds__(CH_THREADS) void local_rank_kernel(const int32_t* t
   __syncthreads();
   const int base = blockIdx.x * CHUNK + w * (CHUNK / 4);
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int ev[CH_PER_THREAD], rk[CH_PER_THREAD];
+  int ev[CH_PER_THREAD], rk[CH_PER_THREAD], ld[CH_PER_THREAD];
+  // All of the thread's expert ids first: the wave barriers below would otherwise keep each step's
+  // load behind the previous step's counter update (one memory latency per step).
+#pragma unroll
+  for (int it = 0; it < CH_PER_THREAD; ++it) {
+    const int a = base + it * 64 + lane;
+    ld[it] = topk_idx[min(a, Tk - 1)];   // unconditional (clamped), so the loads stay in flight together
+  }
 #pragma unroll
   for (int it = 0; it < CH_PER_THREAD; ++it) {
     const int a = base + it * 64 + lane;
     const bool valid = a < Tk;
-    const int e = valid ? topk_idx[a] : 0;
+    const int e = ld[it];
     unsigned long long peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -287,6 +294,19 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // nontemporal access, which does not displace reused data from the caches).
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16_t> {
+  typedef u32x4_t Raw;
+  template <bool NT = false>
+  __device__ static Raw load_raw(const bf16_t* p) {
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+    return NT ? __builtin_nontemporal_load(q) : *q;
+  }
+  __device__ static void unpack(const Raw& w, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
   template <bool NT = false>
   __device__ static void load(const bf16_t* p, float (&v)[8]) {
     const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
@@ -307,6 +327,20 @@ template <> struct Vec8<bf16_t> {
   }
 };
 template <> struct Vec8<float> {
+  struct Raw {
+    float4 a, b;
+  };
+  template <bool NT = false>
+  __device__ static Raw load_raw(const float* p) {
+    Raw r;
+    r.a = reinterpret_cast<const float4*>(p)[0];
+    r.b = reinterpret_cast<const float4*>(p)[1];
+    return r;
+  }
+  __device__ static void unpack(const Raw& r, float (&v)[8]) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  }
   template <bool NT = false>
   __device__ static void load(const float* p, float (&v)[8]) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
@@ -352,6 +386,55 @@ __global__ __launch_bounds__(256) void permute_bwd_kernel(const T* dx_perm, cons
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
     Vec8<T>::template store<true>(dx + (size_t)t * d + c, acc);
+  }
+}
+
+// The same for a fixed k: the k gathered segments and the addends of an iteration are all requested
+// before any is used (k + 2 loads in flight together); same sums in the same order.
+template <typename T, int K>
+__global__ __launch_bounds__(256) void permute_bwd_k_kernel(const T* dx_perm, const int32_t* dest_pos,
+                                                            const T* add0, const T* add1, int d, T* dx) {
+  const int t = blockIdx.x;
+  int rows[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) rows[j] = dest_pos[(size_t)t * K + j];
+  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+    typename Vec8<T>::Raw raw[K], r0, r1;
+#pragma unroll
+    for (int j = 0; j < K; ++j) raw[j] = Vec8<T>::template load_raw<true>(dx_perm + (size_t)rows[j] * d + c);
+    if (add0) r0 = Vec8<T>::template load_raw<true>(add0 + (size_t)t * d + c);
+    if (add1) r1 = Vec8<T>::template load_raw<true>(add1 + (size_t)t * d + c);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      Vec8<T>::unpack(raw[j], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (add0) {
+      Vec8<T>::unpack(r0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (add1) {
+      Vec8<T>::unpack(r1, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    Vec8<T>::template store<true>(dx + (size_t)t * d + c, acc);
+  }
+}
+
+template <typename T>
+void launch_permute_bwd_t(const T* dx_perm, const int32_t* dest_pos, const T* add0, const T* add1, int T_, int d,
+                          int k, T* dx, hipStream_t s) {
+  switch (k) {
+    case 1: hipLaunchKernelGGL((permute_bwd_k_kernel<T, 1>), dim3(T_), dim3(256), 0, s, dx_perm, dest_pos, add0, add1, d, dx); break;
+    case 2: hipLaunchKernelGGL((permute_bwd_k_kernel<T, 2>), dim3(T_), dim3(256), 0, s, dx_perm, dest_pos, add0, add1, d, dx); break;
+    case 4: hipLaunchKernelGGL((permute_bwd_k_kernel<T, 4>), dim3(T_), dim3(256), 0, s, dx_perm, dest_pos, add0, add1, d, dx); break;
+    case 8: hipLaunchKernelGGL((permute_bwd_k_kernel<T, 8>), dim3(T_), dim3(256), 0, s, dx_perm, dest_pos, add0, add1, d, dx); break;
+    default: hipLaunchKernelGGL(permute_bwd_kernel<T>, dim3(T_), dim3(256), 0, s, dx_perm, dest_pos, add0, add1, d, k, dx);
   }
 }
 
@@ -418,15 +501,13 @@ hipError_t launch_permute_bwd(const void* dx_perm, const int32_t* dest_pos, cons
                               hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (bf16)
-    hipLaunchKernelGGL(permute_bwd_kernel<bf16_t>, dim3(T), dim3(256), 0, s,
-                       reinterpret_cast<const bf16_t*>(dx_perm), dest_pos,
-                       reinterpret_cast<const bf16_t*>(add0), reinterpret_cast<const bf16_t*>(add1), d,
-                       k, reinterpret_cast<bf16_t*>(dx));
+    launch_permute_bwd_t<bf16_t>(reinterpret_cast<const bf16_t*>(dx_perm), dest_pos,
+                                 reinterpret_cast<const bf16_t*>(add0), reinterpret_cast<const bf16_t*>(add1), T, d, k,
+                                 reinterpret_cast<bf16_t*>(dx), s);
   else
-    hipLaunchKernelGGL(permute_bwd_kernel<float>, dim3(T), dim3(256), 0, s,
-                       reinterpret_cast<const float*>(dx_perm), dest_pos,
-                       reinterpret_cast<const float*>(add0), reinterpret_cast<const float*>(add1), d, k,
-                       reinterpret_cast<float*>(dx));
+    launch_permute_bwd_t<float>(reinterpret_cast<const float*>(dx_perm), dest_pos,
+                                reinterpret_cast<const float*>(add0), reinterpret_cast<const float*>(add1), T, d, k,
+                                reinterpret_cast<float*>(dx), s);
   return hipGetLastError();
 }
 

@@ -45,10 +45,10 @@ SIMDS = 1024   # 256 CUs x 4
 STAGE_OF = [
     (r"router_logits|topk_gate", "route"),
     (r"local_rank|scan_lds|scan_kernel|scatter_gather|scan_gather|rank_scan", "permute"),
-    (r"combine_bwd_kernel", "combine_bwd"),
-    (r"combine_kernel", "combine"),
+    (r"combine_bwd(_k)?_kernel", "combine_bwd"),
+    (r"combine(_k)?_kernel", "combine"),
     (r"route_bwd|route_dx|route_dw", "route_bwd"),
-    (r"permute_bwd_kernel", "permute_bwd"),
+    (r"permute_bwd(_k)?_kernel", "permute_bwd"),
     (r"aux_", "router_aux"),
     (r"mx_", "mxfp8"),
 ]

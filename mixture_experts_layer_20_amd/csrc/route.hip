@@ -316,112 +316,92 @@ __global__ __launch_bounds__(RM_NTH) void router_logits_mfma_kernel(const bf16_t
   }
 }
 
-// Selection order of two (logit, expert) pairs: is (v, e) before (bv, bi)?  A larger logit comes
-// first, equal logits (-0 == +0) by lower expert index, and a NaN after every number (NaNs among
-// themselves by index), so every selected index is a real expert even when logits are NaN.
-__device__ __forceinline__ bool select_before(float v, int e, float bv, int bi) {
-  const bool vn = v != v, bn = bv != bv;
-  if (vn != bn) return bn;
-  if (!vn && v != bv) return v > bv;
-  return e < bi;
+// Selection key of a (logit, expert) pair: a larger key is selected first.  The high word orders
+// the logits (the sign-magnitude bits mapped to a monotone unsigned code, -0 taken as +0 so equal
+// logits tie), a NaN gets code 0, below every number (whose codes are at least 0x007fffff); the
+// low word is ~e, so equal codes go to the lower expert index.  Keys of distinct experts differ,
+// and every real key exceeds 0, the key of an empty or already taken slot.
+__device__ __forceinline__ uint64_t select_key(float v, int e) {
+  uint32_t b = __float_as_uint(v);
+  b = b == 0x80000000u ? 0u : b;
+  const uint32_t flip = (uint32_t)((int32_t)b >> 31) | 0x80000000u;   // ~b below zero, b | sign above
+  const uint32_t code = (b & 0x7fffffffu) > 0x7f800000u ? 0u : b ^ flip;
+  return ((uint64_t)code << 32) | (uint32_t)~e;
 }
+// The logit a key was made from (a NaN for code 0; +0 for -0).
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t code = (uint32_t)(key >> 32);
+  if (code == 0u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(code & 0x80000000u ? code & 0x7fffffffu : ~code);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
 
-// The better of (bv, bi) and the pair held by the lane that DPP control CTRL names.
+// The larger of key and the key of the lane that DPP control CTRL names (within a 16-lane row).
 template <int CTRL>
-__device__ __forceinline__ void best_dpp(float& bv, int& bi) {
-  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xf, 0xf, false));
-  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xf, 0xf, false);
-  if (select_before(ov, oi, bv, bi)) {
-    bv = ov;
-    bi = oi;
-  }
-}
-// The first pair under select_before over the whole wavefront, in every lane: inside each quad
-// (quad_perm 1,0,3,2 and 2,3,0,1), inside each 16-lane row (row_ror 4 and 8: each lane then holds
-// its row's first pair), then across the four rows from lanes 0, 16, 32, 48 (v_readlane, no LDS
-// round trip).  select_before is a total order, so any reduction order gives the same pair.
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-  best_dpp<0xB1>(bv, bi);
-  best_dpp<0x4E>(bv, bi);
-  best_dpp<0x124>(bv, bi);
-  best_dpp<0x128>(bv, bi);
-  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-  int i = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
-    const int oi = __builtin_amdgcn_readlane(bi, 16 * r);
-    if (select_before(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-  bv = v;
-  bi = i;
+__device__ __forceinline__ uint64_t max_dpp(uint64_t key) {
+  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)key, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(key >> 32), CTRL, 0xf, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > key ? o : key;
 }
 
-// Top-k and gates: one wavefront per token, each lane holding up to 4 logits (E <= 256).
-// k rounds of a wave-wide arg-max under select_before.
+// Top-k and gates: L lanes per token (16 or 32), S logits per lane (lane j of a token holds experts
+// j, j + L, ..., j + (S-1) L), so L * S >= E.  Round r takes the largest key of the token (the
+// lane's best slot, then a maximum over the token's lanes: quad swaps and row rotations by DPP,
+// and one exchange across rows for L = 32), clears that slot, and lane r keeps it.
+template <int L, int S>
 __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int T, int E, int k,
                                                         int renormalize, int32_t* topk_idx,
                                                         float* topk_gate) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float v[4];
-  bool taken[4];
+  const int gl = blockIdx.x * 256 + threadIdx.x;
+  const int t = gl / L, j = gl % L;
+  if (__builtin_amdgcn_readfirstlane(t) >= T) return;   // the wave's first token is past T
+  const int tc = min(t, T - 1);
+  float v[S];
+  uint64_t key[S];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    taken[i] = e >= E;
-    v[i] = taken[i] ? 0.0f : logits[(size_t)t * E + e];
+  for (int s = 0; s < S; ++s) {   // unconditional loads (clamped expert), so all are in flight together
+    const int e = j + s * L;
+    v[s] = logits[(size_t)tc * E + min(e, E - 1)];
+    key[s] = e < E ? select_key(v[s], e) : 0ull;
   }
-  float selv[8];
-  int seli[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    // (NaN, past every index): any untaken expert comes before it
-    float bv = __builtin_nanf("");
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (!taken[i] && select_before(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_best(bv, bi);
-    selv[j] = bv;
-    seli[j] = bi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == bi) taken[i] = true;
-  }
-  // Gates.  selv[0] is the largest logit of the token.
+  uint64_t top = 0, mine = 0;
   float denom = 0.0f;
-  if (renormalize) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) denom += expf(selv[j] - selv[0]);
-  } else {
+  for (int r = 0; r < 8; ++r) {
+    if (r >= k) break;
+    uint64_t best = key[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) best = key[s] > best ? key[s] : best;
+    best = max_dpp<0xB1>(best);    // quad_perm 1,0,3,2
+    best = max_dpp<0x4E>(best);    // quad_perm 2,3,0,1
+    best = max_dpp<0x124>(best);   // row_ror 4
+    best = max_dpp<0x128>(best);   // row_ror 8: every lane of the row holds the row's best
+    if constexpr (L == 32) {
+      const uint32_t lo = __shfl_xor((int)(uint32_t)best, 16, 64);
+      const uint32_t hi = __shfl_xor((int)(uint32_t)(best >> 32), 16, 64);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      best = o > best ? o : best;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) key[s] = key[s] == best ? 0ull : key[s];
+    if (r == 0) top = best;
+    if (j == r) mine = best;
+    if (renormalize) denom += expf(key_logit(best) - key_logit(top));
+  }
+  const float vmax = key_logit(top);   // the token's largest logit
+  if (!renormalize) {
     float part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) part += expf(v[i] - selv[0]);
+    for (int s = 0; s < S; ++s)
+      if (j + s * L < E) part += expf(v[s] - vmax);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    for (int off = L / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
     denom = part;
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        topk_idx[(size_t)t * k + j] = seli[j];
-        topk_gate[(size_t)t * k + j] = expf(selv[j] - selv[0]) / denom;
-      }
-    }
+  if (t < T && j < k) {
+    topk_idx[(size_t)t * k + j] = key_expert(mine);
+    topk_gate[(size_t)t * k + j] = expf(key_logit(mine) - vmax) / denom;
   }
 }
 
@@ -753,8 +733,15 @@ hipError_t launch_router_logits(const void* x, const void* w, const float* bias,
 hipError_t launch_topk_gate(const float* logits, int T, int E, int k, int renormalize,
                             int32_t* topk_idx, float* topk_gate, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_gate_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s, logits, T, E, k,
-                     renormalize, topk_idx, topk_gate);
+  if (E <= 64)
+    hipLaunchKernelGGL((topk_gate_kernel<16, 4>), dim3(ceil_div(T, 16)), dim3(256), 0, s, logits, T, E, k,
+                       renormalize, topk_idx, topk_gate);
+  else if (E <= 128)
+    hipLaunchKernelGGL((topk_gate_kernel<16, 8>), dim3(ceil_div(T, 16)), dim3(256), 0, s, logits, T, E, k,
+                       renormalize, topk_idx, topk_gate);
+  else
+    hipLaunchKernelGGL((topk_gate_kernel<32, 8>), dim3(ceil_div(T, 8)), dim3(256), 0, s, logits, T, E, k,
+                       renormalize, topk_idx, topk_gate);
   return hipGetLastError();
 }
 

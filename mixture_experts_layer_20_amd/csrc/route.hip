@@ -693,7 +693,9 @@ __global__ __launch_bounds__(256) void route_bwd8_kernel(const float* dgate, con
 }
 
 // dW_router[e] = sum of the expert's segment partials, in segment order (zeros if none).  Segments
-// past nseg (the partial sums that exist) are never read.
+// past nseg (the partial sums that exist) are never read.  The form for d a multiple of 4 takes four
+// columns per thread in 16-byte loads, one column quad per thread, so all of a thread's segment
+// loads are in flight together; the other form strides over the block's columns.
 __global__ __launch_bounds__(256) void route_dw_reduce_kernel(const float* partial, const int32_t* offsets, int E,
                                                               int Tk, int d, int nseg, float* dw) {
   __shared__ int pre[257];
@@ -743,6 +745,25 @@ hipError_t launch_topk_gate(const float* logits, int T, int E, int k, int renorm
     hipLaunchKernelGGL((topk_gate_kernel<32, 8>), dim3(ceil_div(T, 8)), dim3(256), 0, s, logits, T, E, k,
                        renormalize, topk_idx, topk_gate);
   return hipGetLastError();
+}
+__global__ __launch_bounds__(256) void route_dw_reduce4_kernel(const float* partial, const int32_t* offsets, int E,
+                                                               int Tk, int d, int nseg, float* dw) {
+  __shared__ int pre[257];
+  seg_prefix_lds(offsets, E, Tk, pre);
+  const int e = blockIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= d) return;
+  const int s0 = min(pre[e], nseg), s1 = min(pre[e + 1], nseg);
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 8
+  for (int s = s0; s < s1; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(partial + (size_t)s * d + c);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(dw + (size_t)e * d + c) = acc;
 }
 
 static inline long long max_segments(long long Tk, int E) { return (Tk + SEG - 1) / SEG + E; }
@@ -808,8 +829,12 @@ hipError_t launch_route_bwd(const float* dgate, const float* gate, const int32_t
                          reinterpret_cast<const float*>(x), E, Tk, d, k, partial);
     }
   }
-  hipLaunchKernelGGL(route_dw_reduce_kernel, dim3(E, ceil_div(d, DWCOLS)), dim3(256), 0, s, partial, offsets, E, Tk, d,
-                     (int)max_segments(Tk, E), dw);
+  if (d % 4 == 0)
+    hipLaunchKernelGGL(route_dw_reduce4_kernel, dim3(E, ceil_div(d, 1024)), dim3(256), 0, s, partial, offsets, E, Tk,
+                       d, (int)max_segments(Tk, E), dw);
+  else
+    hipLaunchKernelGGL(route_dw_reduce_kernel, dim3(E, ceil_div(d, DWCOLS)), dim3(256), 0, s, partial, offsets, E, Tk,
+                       d, (int)max_segments(Tk, E), dw);
   return hipGetLastError();
 }
 

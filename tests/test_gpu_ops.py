@@ -439,6 +439,9 @@ def test_combine_and_backward(dtype, T, d, E, k, shared):
                                            # column block with k = 3 and 2, and k = 8 of 8
                                            (1000, 4096, 128, 4, 0.0), (333, 2056, 60, 3, 2.0),
                                            (150, 2056, 32, 2, 0.0), (257, 4104, 8, 8, 0.0),
+                                           # d % 8 = 4 (four-column reduce, per-column partial sums),
+                                           # d % 4 = 2 over two column blocks (one-column reduce)
+                                           (200, 260, 16, 2, 0.0), (300, 1030, 16, 4, 1.0),
                                            (0, 64, 8, 2, 0.0)])   # no tokens: dW_router is all zeros
 def test_route_backward(dtype, T, d, E, k, skew):
     log(f"route bwd {dtype} T={T} d={d} E={E} k={k}")

@@ -353,8 +353,8 @@ template <int L, int S>
 __global__ __launch_bounds__(256) void topk_gate_kernel(const float* logits, int T, int E, int k,
                                                         int renormalize, int32_t* topk_idx,
                                                         float* topk_gate) {
-  const int gl = blockIdx.x * 256 + threadIdx.x;
-  const int t = gl / L, j = gl % L;
+  const long long gl = (long long)blockIdx.x * 256 + threadIdx.x;   // T * L may exceed 2^31
+  const int t = (int)(gl / L), j = (int)(gl % L);
   if (__builtin_amdgcn_readfirstlane(t) >= T) return;   // the wave's first token is past T
   const int tc = min(t, T - 1);
   float v[S];

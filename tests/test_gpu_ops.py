@@ -76,7 +76,7 @@ def test_learned_route_bit_exact_at_extreme_magnitudes(scale):
 
 @pytest.mark.parametrize("renormalize", [1, 0])
 @pytest.mark.parametrize("kind", ["gauss", "integer_ties", "signed_zero"])
-@pytest.mark.parametrize("E,k", [(64, 4), (256, 8), (8, 8), (130, 3)])
+@pytest.mark.parametrize("E,k", [(64, 4), (256, 8), (8, 8), (130, 3), (128, 4), (100, 6)])
 def test_random_route_ties(renormalize, kind, E, k):
     log(f"route random {kind} E={E} k={k} renorm={renormalize}")
     T = 1000
@@ -96,7 +96,7 @@ def test_random_route_ties(renormalize, kind, E, k):
     assert_close("gates", tnp(gate), O.gate_weights(Lg, ref_idx, renormalize=bool(renormalize)), 1e-6)
 
 
-@pytest.mark.parametrize("E,k", [(64, 4), (256, 8), (8, 8), (5, 2)])
+@pytest.mark.parametrize("E,k", [(64, 4), (256, 8), (8, 8), (5, 2), (128, 8)])
 def test_route_with_nan_logits_selects_real_experts(E, k):
     """NaN logits rank after every number and among themselves by index (the oracle's order): every
     index stays in [0, E).  Only the router runs; nothing downstream reads the indices."""
